@@ -1,0 +1,42 @@
+"""bit_moe_amd: the 2-bit routed-expert MoE FFN layer on MI355X (gfx950).
+
+Python binding over libbitmoe.so (see include/bitmoe.h).  PyTorch provides
+device memory and streams only; every step of the layer runs in the
+library's HIP kernels.
+"""
+from ._lib import (BF16, BitMoEError, DECODE, F32, Layer, PREFILL, SYMBOLS, bucket, dequant_iq2x,
+                   dequant_q2k, ffn_decode, ffn_prefill, lib, pack_bf16, pack_iq2x, pack_q2k, route,
+                   route_workspace_bytes, set_timing_events, strerror, topk, version,
+                   workspace_bytes)
+
+
+def layer_from_canonical(H, I, E, k, router_bits, gate, up, down, grid, shared=None, device="cuda"):
+    """Upload canonical weights (numpy/torch uint8 blocks, bf16 bit arrays) to
+    the GPU and convert the quantised and shared tensors to the tiled layout
+    with the library's pack entry points."""
+    import numpy as np
+    import torch
+
+    def dev(a, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a)) if isinstance(a, np.ndarray) else a
+        if dtype is not None:
+            t = t.view(dtype)
+        return t.to(device).contiguous()
+
+    router = dev(router_bits, torch.bfloat16) if router_bits is not None else \
+        torch.zeros((E, H), dtype=torch.bfloat16, device=device)
+    gq = pack_iq2x(dev(gate).reshape(-1), E, I, H)
+    uq = pack_iq2x(dev(up).reshape(-1), E, I, H)
+    dq = pack_q2k(dev(down).reshape(-1), E, H, I)
+    g = dev(grid).reshape(-1)
+    sh = None
+    if shared is not None:
+        sg, su, sd = (dev(a, torch.bfloat16) for a in shared)
+        sh = (pack_bf16(sg), pack_bf16(su), pack_bf16(sd))
+    return Layer(H, I, E, k, router, gq, uq, dq, g, sh)
+
+
+__all__ = ["BF16", "BitMoEError", "DECODE", "F32", "Layer", "PREFILL", "SYMBOLS", "bucket",
+           "dequant_iq2x", "dequant_q2k", "ffn_decode", "ffn_prefill", "layer_from_canonical", "lib",
+           "pack_bf16", "pack_iq2x", "pack_q2k", "route", "route_workspace_bytes", "set_timing_events", "strerror", "topk",
+           "version", "workspace_bytes"]

@@ -1,0 +1,210 @@
+// Standalone dequantisation of canonical IQ2X / Q2K blocks, and the load-time
+// canonical -> tiled layout transforms.
+//
+// Formats: the routed experts' IQ2_XXS-style up/gate blocks and Q2_K down
+// blocks (page "ds4 : analyse pratique pour un usage documente", section
+// "Support de modeles et choix de quantification"), in GGML's byte order
+// (page "antirez/ds4 - Moteur local d'inference DeepSeek V4 Flash pour
+// Metal", section "Remerciements a llama.cpp et GGML").
+//
+// Exactness: an IQ2X value d*(0.5+s)/4*g has at most 11+5+3 significant bits,
+// so every product below is exact in fp32 whatever the evaluation order.  A
+// Q2K value is one fp32 rounding of (d*scale)*q - dmin*min, both products
+// exact; fmaf gives that single rounding.
+#include "common.h"
+
+namespace {
+
+using namespace bm;
+
+// One thread per (block, group of 32 weights).
+template <int OUT_BF16>
+__global__ void __launch_bounds__(256)
+k_dequant_iq2x(const uint8_t *__restrict__ blocks, const uint8_t *__restrict__ grid,
+               int64_t nblocks, void *__restrict__ out) {
+    __shared__ uint32_t sgrid32[256 * 2];
+    const uint8_t *sgrid = reinterpret_cast<const uint8_t *>(sgrid32);
+    for (int i = threadIdx.x; i < 256 * 2; i += blockDim.x)
+        sgrid32[i] = reinterpret_cast<const uint32_t *>(grid)[i];
+    __syncthreads();
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= nblocks * 8) return;
+    int64_t b = gid >> 3;
+    int g = (int)(gid & 7);
+    const uint16_t *blk = reinterpret_cast<const uint16_t *>(blocks + 66 * b);
+    float d = fp16_to_f32(blk[0]);
+    const uint16_t *grp = blk + 1 + 4 * g;               // 8 bytes, 2-byte aligned
+    uint32_t idxw = (uint32_t)grp[0] | ((uint32_t)grp[1] << 16);
+    uint32_t a = (uint32_t)grp[2] | ((uint32_t)grp[3] << 16);
+    float db = d * fmaf((float)(a >> 28), 0.25f, 0.125f);  // d*(0.5+s)/4, exact
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        uint32_t s7 = (a >> (7 * j)) & 0x7Fu;
+        uint32_t sig = s7 | ((uint32_t)(__popc(s7) & 1) << 7);
+        const uint8_t *row = sgrid + 8 * ((idxw >> (8 * j)) & 0xFFu);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            float m = db * (float)row[i];
+            v[8 * j + i] = ((sig >> i) & 1u) ? -m : m;
+        }
+    }
+    if (OUT_BF16) {
+        uint4 *o = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + 256 * b + 32 * g);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            uint32_t w[4];
+#pragma unroll
+            for (int p = 0; p < 4; p++)
+                w[p] = f32_to_bf16_rne(v[8 * q + 2 * p]) | (f32_to_bf16_rne(v[8 * q + 2 * p + 1]) << 16);
+            o[q] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else {
+        float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(out) + 256 * b + 32 * g);
+#pragma unroll
+        for (int q = 0; q < 8; q++) o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+}
+
+// One thread per (block, sub-block of 16 weights).
+template <int OUT_BF16>
+__global__ void __launch_bounds__(256)
+k_dequant_q2k(const uint8_t *__restrict__ blocks, int64_t nblocks, void *__restrict__ out) {
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= nblocks * 16) return;
+    int64_t b = gid >> 4;
+    int sb = (int)(gid & 15);
+    const uint8_t *blk = blocks + 84 * b;
+    const uint32_t *w32 = reinterpret_cast<const uint32_t *>(blk);
+    uint32_t dd = w32[20];                                  // bytes 80..83
+    float d = fp16_to_f32(dd & 0xFFFFu), dmin = fp16_to_f32(dd >> 16);
+    uint32_t scb = blk[sb];
+    float dsc = d * (float)(scb & 15u);                     // exact
+    float dm = dmin * (float)(scb >> 4);                    // exact
+    int h = sb >> 3, j = (sb & 7) >> 1, l0 = 16 * (sb & 1);
+    const uint32_t *q32 = reinterpret_cast<const uint32_t *>(blk + 16 + 32 * h + l0);
+    float v[16];
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        uint32_t q = (q32[w] >> (2 * j)) & 0x03030303u;
+#pragma unroll
+        for (int i = 0; i < 4; i++) v[4 * w + i] = fmaf(dsc, (float)((q >> (8 * i)) & 3u), -dm);
+    }
+    if (OUT_BF16) {
+        uint4 *o = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + 256 * b + 16 * sb);
+#pragma unroll
+        for (int q = 0; q < 2; q++) {
+            uint32_t w[4];
+#pragma unroll
+            for (int p = 0; p < 4; p++)
+                w[p] = f32_to_bf16_rne(v[8 * q + 2 * p]) | (f32_to_bf16_rne(v[8 * q + 2 * p + 1]) << 16);
+            o[q] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else {
+        float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(out) + 256 * b + 16 * sb);
+#pragma unroll
+        for (int q = 0; q < 4; q++) o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+    }
+}
+
+// canonical IQ2X -> tiled; one thread per block
+__global__ void __launch_bounds__(256)
+k_pack_iq2x(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int E, int N, int nb) {
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t per_e = (int64_t)N * nb;
+    if (gid >= per_e * E) return;
+    int64_t e = gid / per_e, rem = gid % per_e;
+    int n = (int)(rem / nb), kb = (int)(rem % nb);
+    int P = n >> 6, r = n & 63;
+    const uint16_t *s = reinterpret_cast<const uint16_t *>(src + 66 * gid);
+    uint8_t *slab = dst + e * per_e * 66;
+    int64_t pk = (int64_t)P * nb + kb;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            w[q] = (uint32_t)s[1 + 8 * c + 2 * q] | ((uint32_t)s[2 + 8 * c + 2 * q] << 16);
+        reinterpret_cast<uint4 *>(slab)[(pk * 4 + c) * 64 + r] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    reinterpret_cast<uint16_t *>(slab + 64 * per_e)[pk * 64 + r] = s[0];
+}
+
+// canonical Q2K -> tiled; one thread per block
+__global__ void __launch_bounds__(256)
+k_pack_q2k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int E, int N, int nb) {
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t per_e = (int64_t)N * nb;
+    if (gid >= per_e * E) return;
+    int64_t e = gid / per_e, rem = gid % per_e;
+    int n = (int)(rem / nb), kb = (int)(rem % nb);
+    int P = n >> 6, r = n & 63;
+    const uint32_t *s = reinterpret_cast<const uint32_t *>(src + 84 * gid);
+    uint8_t *slab = dst + e * per_e * 84;
+    int64_t pk = (int64_t)P * nb + kb;
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+        reinterpret_cast<uint4 *>(slab)[(pk * 4 + c) * 64 + r] =
+            make_uint4(s[4 + 4 * c], s[5 + 4 * c], s[6 + 4 * c], s[7 + 4 * c]);
+    reinterpret_cast<uint4 *>(slab + 64 * per_e)[pk * 64 + r] = make_uint4(s[0], s[1], s[2], s[3]);
+    reinterpret_cast<uint32_t *>(slab + 80 * per_e)[pk * 64 + r] = s[20];
+}
+
+// row-major bf16 [N][K] -> tiled; one thread per 8-value piece
+__global__ void __launch_bounds__(256)
+k_pack_bf16(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int N, int K8) {
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (int64_t)N * K8) return;
+    int n = (int)(gid / K8), c = (int)(gid % K8);
+    dst[((int64_t)(n >> 6) * K8 + c) * 64 + (n & 63)] = src[gid];
+}
+
+inline unsigned grid_for(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
+
+}  // namespace
+
+namespace bm_host {
+
+int launch_dequant_iq2x(const void *blocks, const void *grid, int64_t nblocks, void *out,
+                        int out_dtype, hipStream_t s) {
+    unsigned g = grid_for(nblocks * 8, 256);
+    if (out_dtype == BITMOE_BF16)
+        k_dequant_iq2x<1><<<g, 256, 0, s>>>((const uint8_t *)blocks, (const uint8_t *)grid, nblocks, out);
+    else
+        k_dequant_iq2x<0><<<g, 256, 0, s>>>((const uint8_t *)blocks, (const uint8_t *)grid, nblocks, out);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
+
+int launch_dequant_q2k(const void *blocks, int64_t nblocks, void *out, int out_dtype, hipStream_t s) {
+    unsigned g = grid_for(nblocks * 16, 256);
+    if (out_dtype == BITMOE_BF16)
+        k_dequant_q2k<1><<<g, 256, 0, s>>>((const uint8_t *)blocks, nblocks, out);
+    else
+        k_dequant_q2k<0><<<g, 256, 0, s>>>((const uint8_t *)blocks, nblocks, out);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
+
+int launch_pack_iq2x(const void *src, void *dst, int E, int N, int K, hipStream_t s) {
+    int64_t n = (int64_t)E * N * (K / 256);
+    k_pack_iq2x<<<grid_for(n, 256), 256, 0, s>>>((const uint8_t *)src, (uint8_t *)dst, E, N, K / 256);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
+
+int launch_pack_q2k(const void *src, void *dst, int E, int N, int K, hipStream_t s) {
+    int64_t n = (int64_t)E * N * (K / 256);
+    k_pack_q2k<<<grid_for(n, 256), 256, 0, s>>>((const uint8_t *)src, (uint8_t *)dst, E, N, K / 256);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
+
+int launch_pack_bf16(const void *src, void *dst, int N, int K, hipStream_t s) {
+    int64_t n = (int64_t)N * (K / 8);
+    k_pack_bf16<<<grid_for(n, 256), 256, 0, s>>>((const uint4 *)src, (uint4 *)dst, N, K / 8);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
+
+}  // namespace bm_host

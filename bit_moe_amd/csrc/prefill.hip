@@ -1,0 +1,352 @@
+// Prefill FFN: grouped GEMMs over the bucketed (token, expert) pairs with the
+// routed weights dequantised to bf16 tiles in LDS feeding bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Prefill is compute-bound
+// (page "Faire tenir un MoE de 284B dans un portable de 128 Go", section "Un
+// pre-remplissage a 790 t/s revele le veritable goulot d'etranglement"), so
+// the dense contraction goes to the matrix cores.
+//
+// Work list: the bucketing pass emits tiles (expert e, first row r0) of up to
+// BM rows of expert e's bucket; grid.y walks the tiles, grid.x the N tiles.
+//  gate/up: A = gathered activation rows (bf16), B = [gate rows | up rows]
+//           of the N tile, epilogue h = silu(g) * u (bf16, bucket order).
+//  down:    A = h rows of the tile (contiguous), B = Q2K rows, epilogue
+//           writes o[pair][n] (fp32); k_combine applies the routing weights.
+#include "common.h"
+
+namespace {
+
+using namespace bm;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 64;        // rows per tile (matches the bucket tile list)
+constexpr int BK = 128;       // K per LDS stage (half a superblock)
+constexpr int LDK = BK + 8;   // padded LDS row stride in bf16 elements
+
+struct PrefillArgs {
+    int H, I, k, T;
+    const uint8_t *gate, *up, *down, *grid;
+    const int32_t *counts, *offsets, *perm, *tiles, *n_tiles;
+};
+
+// --- B-tile dequantisation into LDS (bf16 = RNE of the exact fp32 value) ---
+
+// 32 weights of IQ2X group g of block (n, kb) of one expert's tiled slab.
+BM_DEV void iq2x_group_to_lds(const uint8_t *slab, int N, int nb, int n, int kb, int g,
+                              const uint2 *sgrid, uint16_t *dst) {
+    const int P = n >> 6, r = n & 63;
+    const int64_t pk = (int64_t)P * nb + kb;
+    const uint2 gw = reinterpret_cast<const uint2 *>(slab)[((pk * 4 + (g >> 1)) * 64 + r) * 2 + (g & 1)];
+    const float d = fp16_to_f32(reinterpret_cast<const uint16_t *>(slab + (int64_t)N * nb * 64)[pk * 64 + r]);
+    const float db = d * fmaf((float)(gw.y >> 28), 0.25f, 0.125f);
+    uint32_t out[16];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        uint32_t s7 = (gw.y >> (7 * j)) & 0x7Fu;
+        uint32_t sig = s7 | ((uint32_t)(__popc(s7) & 1) << 7);
+        uint2 row = sgrid[(gw.x >> (8 * j)) & 0xFFu];
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+            uint32_t m0 = ((i < 4 ? row.x : row.y) >> (8 * (i & 3))) & 0xFFu;
+            uint32_t m1 = ((i < 4 ? row.x : row.y) >> (8 * ((i + 1) & 3))) & 0xFFu;
+            uint32_t b0 = f32_to_bf16_rne(db * (float)m0) | (((sig >> i) & 1u) << 15);
+            uint32_t b1 = f32_to_bf16_rne(db * (float)m1) | (((sig >> (i + 1)) & 1u) << 15);
+            out[4 * j + i / 2] = b0 | (b1 << 16);
+        }
+    }
+    uint4 *o = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+    for (int q = 0; q < 4; q++) o[q] = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+}
+
+// 16 weights of Q2K sub-block b of block (n, kb).
+BM_DEV void q2k_sub_to_lds(const uint8_t *slab, int N, int nb, int n, int kb, int b, uint16_t *dst) {
+    const int P = n >> 6, r = n & 63;
+    const int64_t pk = (int64_t)P * nb + kb;
+    const int64_t S = (int64_t)N * nb;
+    const int hh = b >> 3, j = (b & 7) >> 1, c = 2 * hh + (b & 1);
+    const uint4 qv = reinterpret_cast<const uint4 *>(slab)[(pk * 4 + c) * 64 + r];
+    const uint32_t scb = slab[S * 64 + (pk * 64 + r) * 16 + b];
+    const uint32_t dd = reinterpret_cast<const uint32_t *>(slab + S * 80)[pk * 64 + r];
+    const float dsc = fp16_to_f32(dd & 0xFFFFu) * (float)(scb & 15u);
+    const float dm = fp16_to_f32(dd >> 16) * (float)(scb >> 4);
+    uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+    uint32_t out[8];
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        uint32_t q = (qw[w] >> (2 * j)) & 0x03030303u;
+        uint32_t v0 = f32_to_bf16_rne(fmaf(dsc, (float)(q & 0xFFu), -dm));
+        uint32_t v1 = f32_to_bf16_rne(fmaf(dsc, (float)((q >> 8) & 0xFFu), -dm));
+        uint32_t v2 = f32_to_bf16_rne(fmaf(dsc, (float)((q >> 16) & 0xFFu), -dm));
+        uint32_t v3 = f32_to_bf16_rne(fmaf(dsc, (float)(q >> 24), -dm));
+        out[2 * w] = v0 | (v1 << 16);
+        out[2 * w + 1] = v2 | (v3 << 16);
+    }
+    uint4 *o = reinterpret_cast<uint4 *>(dst);
+    o[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    o[1] = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+// MFMA over one BK stage: wave computes 4 M-blocks x NB N-blocks.
+template <int NB>
+BM_DEV void mfma_stage(const uint16_t *sa, const uint16_t *sb, const int (&bcol)[NB],
+                       f32x4 (&acc)[4][NB]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+        const int kof = kk + 8 * (lane >> 4);
+        bf16x8 fb[NB];
+#pragma unroll
+        for (int j = 0; j < NB; j++)
+            fb[j] = *reinterpret_cast<const bf16x8 *>(sb + (bcol[j] + (lane & 15)) * LDK + kof);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sa + (16 * i + (lane & 15)) * LDK + kof);
+#pragma unroll
+            for (int j = 0; j < NB; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gate/up.  grid = (I/64, max_tiles), 256 threads.  N tile: h columns
+// n0..n0+63; B rows 0-63 = gate rows n0.., 64-127 = up rows n0..
+// ---------------------------------------------------------------------------
+template <int XBF16>
+__global__ void __launch_bounds__(256)
+k_prefill_gateup(int H, int I, int k, const uint8_t *__restrict__ gate,
+                 const uint8_t *__restrict__ up, const uint8_t *__restrict__ grid,
+                 const void *__restrict__ x, const int32_t *__restrict__ counts,
+                 const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
+                 const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
+                 uint16_t *__restrict__ h) {
+    __shared__ __attribute__((aligned(16))) uint16_t sa[BM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t sb[128 * LDK];
+    __shared__ uint2 sgrid[256];
+    __shared__ int stok[BM];
+    const int tile = blockIdx.y;
+    if (tile >= *n_tiles) return;
+    const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
+    const int off = offsets[e], rows = min(BM, counts[e] - r0);
+    const int n0 = blockIdx.x * 64;
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int i = tid; i < 256; i += 256) sgrid[i] = reinterpret_cast<const uint2 *>(grid)[i];
+    if (tid < BM) stok[tid] = perm[off + r0 + min(tid, rows - 1)] / k;
+    const int nb = H / kQK;
+    const int64_t slab = (int64_t)I * nb * 66;
+    const uint8_t *G = gate + e * slab, *U = up + e * slab;
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int bcol[2] = {16 * wv, 64 + 16 * wv};
+    __syncthreads();
+    for (int k0 = 0; k0 < H; k0 += BK) {
+        // A: 64 rows x 128 K -> 1024 pieces of 8 values, 4 per thread
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            int piece = tid + 256 * p, r = piece >> 4, c = (piece & 15) * 8;
+            const int t = stok[r];
+            uint4 v;
+            if (XBF16) {
+                v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)t * H + k0 + c);
+            } else {
+                const float4 *xp = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)t * H + k0 + c);
+                float4 a = xp[0], b = xp[1];
+                v = make_uint4(f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16),
+                               f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16),
+                               f32_to_bf16_rne(b.x) | (f32_to_bf16_rne(b.y) << 16),
+                               f32_to_bf16_rne(b.z) | (f32_to_bf16_rne(b.w) << 16));
+            }
+            *reinterpret_cast<uint4 *>(sa + r * LDK + c) = v;
+        }
+        // B: 128 rows x 4 groups = 512 (row, group) units, 2 per thread
+        const int kb = k0 / kQK, g0 = (k0 % kQK) / 32;
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+            int u = tid + 256 * p, row = u >> 2, gg = u & 3;
+            const uint8_t *S = row < 64 ? G : U;
+            iq2x_group_to_lds(S, I, nb, n0 + (row & 63), kb, g0 + gg, sgrid, sb + row * LDK + 32 * gg);
+        }
+        __syncthreads();
+        mfma_stage<2>(sa, sb, bcol, acc);
+        __syncthreads();
+    }
+    // epilogue: lane holds rows 4*(lane/16)+q of each M block, column lane%16
+    const int n = n0 + 16 * wv + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            int m = 16 * i + 4 * (lane >> 4) + q;
+            if (m < rows) {
+                float hv = silu(acc[i][0][q]) * acc[i][1][q];
+                h[(int64_t)(off + r0 + m) * I + n] = (uint16_t)f32_to_bf16_rne(hv);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// down.  grid = (H/64, max_tiles), 256 threads.  A = h rows (bucket order).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+k_prefill_down(int H, int I, const uint8_t *__restrict__ down, const uint16_t *__restrict__ h,
+               const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
+               const int32_t *__restrict__ perm, const int32_t *__restrict__ tiles,
+               const int32_t *__restrict__ n_tiles, float *__restrict__ o) {
+    __shared__ __attribute__((aligned(16))) uint16_t sa[BM * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t sb[64 * LDK];
+    const int tile = blockIdx.y;
+    if (tile >= *n_tiles) return;
+    const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
+    const int off = offsets[e], rows = min(BM, counts[e] - r0);
+    const int n0 = blockIdx.x * 64;
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nb = I / kQK;
+    const uint8_t *D = down + (int64_t)e * H * nb * 84;
+    f32x4 acc[4][1];
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int bcol[1] = {16 * wv};
+    for (int k0 = 0; k0 < I; k0 += BK) {
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            int piece = tid + 256 * p, r = piece >> 4, c = (piece & 15) * 8;
+            int row = off + r0 + min(r, rows - 1);
+            *reinterpret_cast<uint4 *>(sa + r * LDK + c) =
+                *reinterpret_cast<const uint4 *>(h + (int64_t)row * I + k0 + c);
+        }
+        // B: 64 rows x 8 sub-blocks (128 K) = 512 units, 2 per thread
+        const int kb = k0 / kQK, b0 = (k0 % kQK) / 16;
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+            int u = tid + 256 * p, row = u >> 3, sbk = u & 7;
+            q2k_sub_to_lds(D, H, nb, n0 + row, kb, b0 + sbk, sb + row * LDK + 16 * sbk);
+        }
+        __syncthreads();
+        mfma_stage<1>(sa, sb, bcol, acc);
+        __syncthreads();
+    }
+    const int n = n0 + 16 * wv + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            int m = 16 * i + 4 * (lane >> 4) + q;
+            if (m < rows) o[(int64_t)perm[off + r0 + m] * H + n] = acc[i][0][q];
+        }
+}
+
+// Shared expert for prefill-mode calls: dense bf16 FFN per token, one
+// workgroup per (token, 64-row panel); simple and only used when a shared
+// expert is supplied to the prefill entry point.
+template <int XBF16>
+__global__ void __launch_bounds__(64)
+k_shared_gateup_rows(int H, int I, const uint4 *__restrict__ sg, const uint4 *__restrict__ su,
+                     const void *__restrict__ x, float *__restrict__ hs) {
+    const int P = blockIdx.x, t = blockIdx.y, lane = lane_id(), K8 = H / 8;
+    float g = 0.f, u = 0.f;
+    for (int c = 0; c < K8; c++) {
+        uint4 gw = sg[((int64_t)P * K8 + c) * 64 + lane], uw = su[((int64_t)P * K8 + c) * 64 + lane];
+        float xv[8];
+        if (XBF16) {
+            uint4 xb = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)t * H + 8 * c);
+            uint32_t xw[4] = {xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) { xv[2 * q] = bf16_lo(xw[q]); xv[2 * q + 1] = bf16_hi(xw[q]); }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; q++) xv[q] = static_cast<const float *>(x)[(int64_t)t * H + 8 * c + q];
+        }
+        uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w}, uu[4] = {uw.x, uw.y, uw.z, uw.w};
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            g = fmaf(bf16_lo(gg[q]), xv[2 * q], g); g = fmaf(bf16_hi(gg[q]), xv[2 * q + 1], g);
+            u = fmaf(bf16_lo(uu[q]), xv[2 * q], u); u = fmaf(bf16_hi(uu[q]), xv[2 * q + 1], u);
+        }
+    }
+    hs[(int64_t)t * I + P * 64 + lane] = silu(g) * u;
+}
+
+__global__ void __launch_bounds__(64)
+k_shared_down_rows(int H, int I, const uint4 *__restrict__ sd, const float *__restrict__ hs,
+                   float *__restrict__ os) {
+    const int P = blockIdx.x, t = blockIdx.y, lane = lane_id(), K8 = I / 8;
+    float acc = 0.f;
+    for (int c = 0; c < K8; c++) {
+        uint4 wv = sd[((int64_t)P * K8 + c) * 64 + lane];
+        uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+        const float *hp = hs + (int64_t)t * I + 8 * c;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            acc = fmaf(bf16_lo(ww[q]), hp[2 * q], acc);
+            acc = fmaf(bf16_hi(ww[q]), hp[2 * q + 1], acc);
+        }
+    }
+    os[(int64_t)t * H + P * 64 + lane] = acc;
+}
+
+__global__ void __launch_bounds__(256)
+k_combine_p(const float *__restrict__ o, const float *__restrict__ w, const float *__restrict__ os,
+            float *__restrict__ y, int T, int H, int k) {
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)T * H) return;
+    int t = (int)(i / H), n = (int)(i % H);
+    float s = 0.f;
+    for (int j = 0; j < k; j++) s = fmaf(w[t * k + j], o[((int64_t)t * k + j) * H + n], s);
+    if (os) s += os[i];
+    y[i] = s;
+}
+
+}  // namespace
+
+namespace bm_host {
+
+int prefill_tile_rows() { return BM; }
+
+int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T, const int32_t *ids,
+                       const float *w, float *y, const Buckets &b, int max_tiles, uint16_t *xb,
+                       uint16_t *h, float *o, float *hs, float *os, hipStream_t s) {
+    (void)ids; (void)xb;
+    const int H = L->H, I = L->I, k = L->k;
+    dim3 g1(I / 64, max_tiles);
+    timing_begin(s);
+    if (x_dtype == BITMOE_BF16)
+        k_prefill_gateup<1><<<g1, 256, 0, s>>>(H, I, k, (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q,
+                                               (const uint8_t *)L->grid, x, b.counts, b.offsets, b.perm,
+                                               b.tiles, b.n_tiles, h);
+    else
+        k_prefill_gateup<0><<<g1, 256, 0, s>>>(H, I, k, (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q,
+                                               (const uint8_t *)L->grid, x, b.counts, b.offsets, b.perm,
+                                               b.tiles, b.n_tiles, h);
+    BM_LAUNCH_CHECK();
+    timing_end(s);
+    dim3 g2(H / 64, max_tiles);
+    k_prefill_down<<<g2, 256, 0, s>>>(H, I, (const uint8_t *)L->down_q, h, b.counts, b.offsets, b.perm,
+                                      b.tiles, b.n_tiles, o);
+    BM_LAUNCH_CHECK();
+    const bool shared = L->shared_gate != nullptr;
+    if (shared) {
+        dim3 gs1(I / 64, T), gs2(H / 64, T);
+        if (x_dtype == BITMOE_BF16)
+            k_shared_gateup_rows<1><<<gs1, 64, 0, s>>>(H, I, (const uint4 *)L->shared_gate,
+                                                       (const uint4 *)L->shared_up, x, hs);
+        else
+            k_shared_gateup_rows<0><<<gs1, 64, 0, s>>>(H, I, (const uint4 *)L->shared_gate,
+                                                       (const uint4 *)L->shared_up, x, hs);
+        BM_LAUNCH_CHECK();
+        k_shared_down_rows<<<gs2, 64, 0, s>>>(H, I, (const uint4 *)L->shared_down, hs, os);
+        BM_LAUNCH_CHECK();
+    }
+    int64_t n = (int64_t)T * H;
+    k_combine_p<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(o, w, shared ? os : nullptr, y, T, H, k);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
+
+}  // namespace bm_host

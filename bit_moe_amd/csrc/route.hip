@@ -1,0 +1,236 @@
+// Routing: router logits (bf16 router weights, fp32 accumulation), top-k with
+// ties to the lower expert index, and the softmax renormalised over the k
+// selected experts.  The router is one of the unquantised parts of the
+// layer (page "ds4 : analyse pratique pour un usage documente", section
+// "Support de modeles et choix de quantification"); it chooses a few experts
+// per token (page "Un modele de 284 milliards de parametres tourne desormais
+// sur un Mac de 128 Go. Qui y perd ?", section "Comment un modele de 284
+// milliards de parametres tient sur une seule machine").
+#include "common.h"
+
+namespace {
+
+using namespace bm;
+
+constexpr int kRouterKC = 128;   // K columns per split of the small-T router
+
+// ---------------------------------------------------------------------------
+// Small-T router: one lane per expert row, K split over blockIdx.x.  Each
+// lane streams 16-byte pieces of its own row; the activations are the same
+// for all lanes, so they come in through scalar loads.  Writes partial sums
+// part[ks][t][e]; the top-k kernel adds the splits in a fixed order.
+// ---------------------------------------------------------------------------
+template <int XBF16, int NT>
+BM_DEV void router_tokens(const uint4 *__restrict__ wrow, const void *__restrict__ x, int H,
+                          int t0, int nt, int k0, float *__restrict__ part, int T, int E, int e,
+                          bool valid, int ks) {
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < kRouterKC / 8; c++) {
+        uint4 wv = valid ? wrow[c] : make_uint4(0, 0, 0, 0);
+        int k = k0 + 8 * c;
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            int tt = t0 + (t < nt ? t : 0);
+            if (XBF16) {
+                const uint4 xv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)tt * H + k);
+                float a = acc[t];
+                a = dot2_bf16(wv.x, xv.x, a);
+                a = dot2_bf16(wv.y, xv.y, a);
+                a = dot2_bf16(wv.z, xv.z, a);
+                a = dot2_bf16(wv.w, xv.w, a);
+                acc[t] = a;
+            } else {
+                const float4 *xp = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)tt * H + k);
+                float4 x0 = xp[0], x1 = xp[1];
+                float a = acc[t];
+                a = fmaf(bf16_lo(wv.x), x0.x, a); a = fmaf(bf16_hi(wv.x), x0.y, a);
+                a = fmaf(bf16_lo(wv.y), x0.z, a); a = fmaf(bf16_hi(wv.y), x0.w, a);
+                a = fmaf(bf16_lo(wv.z), x1.x, a); a = fmaf(bf16_hi(wv.z), x1.y, a);
+                a = fmaf(bf16_lo(wv.w), x1.z, a); a = fmaf(bf16_hi(wv.w), x1.w, a);
+                acc[t] = a;
+            }
+        }
+    }
+    if (valid) {
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+            if (t < nt) part[((int64_t)ks * T + t0 + t) * E + e] = acc[t];
+    }
+}
+
+template <int XBF16>
+__global__ void __launch_bounds__(64)
+k_router_gemv(const uint16_t *__restrict__ wr, const void *__restrict__ x, int T, int H, int E,
+              float *__restrict__ part) {
+    int ks = blockIdx.x;
+    int e = blockIdx.y * 64 + (int)threadIdx.x;
+    bool valid = e < E;
+    int k0 = ks * kRouterKC;
+    const uint4 *wrow = reinterpret_cast<const uint4 *>(wr + (int64_t)(valid ? e : 0) * H + k0);
+    for (int t0 = 0; t0 < T; t0 += 8) {
+        int nt = min(8, T - t0);
+        if (nt == 1)
+            router_tokens<XBF16, 1>(wrow, x, H, t0, 1, k0, part, T, E, e, valid, ks);
+        else
+            router_tokens<XBF16, 8>(wrow, x, H, t0, nt, k0, part, T, E, e, valid, ks);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Large-T router (bf16 activations): logits = X[T][H] . W[E][H]^T on bf16
+// MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation.  64x64 output tile
+// per workgroup, 4 waves of 32x32, K staged through LDS 64 columns at a time.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256)
+k_router_mfma(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, int T, int H, int E,
+              float *__restrict__ C) {
+    constexpr int BK = 64, LD = BK + 8;   // padded row stride (bf16 elements)
+    __shared__ __attribute__((aligned(16))) uint16_t sa[64 * LD];
+    __shared__ __attribute__((aligned(16))) uint16_t sb[64 * LD];
+    int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+    int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < H; k0 += BK) {
+        // 64 rows x 64 cols = 512 pieces of 8 bf16 per operand; 2 per thread
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+            int piece = tid + 256 * p, r = piece >> 3, c = (piece & 7) * 8;
+            int ra = min(m0 + r, T - 1), rb = min(n0 + r, E - 1);
+            uint4 va = *reinterpret_cast<const uint4 *>(X + (int64_t)ra * H + k0 + c);
+            uint4 vb = *reinterpret_cast<const uint4 *>(W + (int64_t)rb * H + k0 + c);
+            *reinterpret_cast<uint4 *>(sa + r * LD + c) = va;
+            *reinterpret_cast<uint4 *>(sb + r * LD + c) = vb;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 32) {
+            bf16x8 fa[2], fb[2];
+            int kof = kk + 8 * (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                fa[i] = *reinterpret_cast<const bf16x8 *>(sa + (wm + 16 * i + (lane & 15)) * LD + kof);
+                fb[i] = *reinterpret_cast<const bf16x8 *>(sb + (wn + 16 * i + (lane & 15)) * LD + kof);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            int n = n0 + wn + 16 * j + (lane & 15);
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                int m = m0 + wm + 16 * i + 4 * (lane >> 4) + q;
+                if (m < T && n < E) C[(int64_t)m * E + n] = acc[i][j][q];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k: one wave per token.  Sums the KS partial logits in split order,
+// selects k by repeated wave argmax (larger value, then lower index), and
+// writes w = softmax over the selected logits.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+k_topk(const float *__restrict__ part, int KS, int T, int E, int k, float *__restrict__ logits,
+       int32_t *__restrict__ ids, float *__restrict__ wout) {
+    int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    int lane = threadIdx.x & 63;
+    if (t >= T) return;
+    constexpr int MAXV = 16;                 // E <= 1024
+    float v[MAXV];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < MAXV; i++) {
+        int e = lane + 64 * i;
+        float s = 0.f;
+        if (e < E) {
+            for (int ks = 0; ks < KS; ks++) s += part[((int64_t)ks * T + t) * E + e];
+            if (logits) logits[(int64_t)t * E + e] = s;
+        }
+        v[i] = s;
+    }
+    float sel[16];
+    int sid[16];
+    for (int j = 0; j < k; j++) {
+        float bv = 0.f;
+        int be = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < MAXV; i++) {
+            int e = lane + 64 * i;
+            bool ok = e < E && !((taken >> i) & 1u);
+            if (ok && (be == 0x7FFFFFFF || v[i] > bv)) { bv = v[i]; be = e; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            float ov = __shfl_xor(bv, o, 64);
+            int oe = __shfl_xor(be, o, 64);
+            bool better = (oe != 0x7FFFFFFF) &&
+                          (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be));
+            if (better) { bv = ov; be = oe; }
+        }
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        sel[j] = bv;
+        sid[j] = be;
+    }
+    if (lane == 0) {
+        float z = 0.f, ex[16];
+        for (int j = 0; j < k; j++) { ex[j] = __expf(sel[j] - sel[0]); z += ex[j]; }
+        float inv = 1.0f / z;
+        for (int j = 0; j < k; j++) {
+            ids[(int64_t)t * k + j] = sid[j];
+            wout[(int64_t)t * k + j] = ex[j] * inv;
+        }
+    }
+}
+
+}  // namespace
+
+namespace bm_host {
+
+int router_splits(int H) { return H / kRouterKC; }
+
+int launch_router_gemv(const bitmoe_layer *L, const void *x, int x_dtype, int T, float *part,
+                       hipStream_t s) {
+    dim3 g(router_splits(L->H), (L->E + 63) / 64);
+    if (x_dtype == BITMOE_BF16)
+        k_router_gemv<1><<<g, 64, 0, s>>>((const uint16_t *)L->router_w, x, T, L->H, L->E, part);
+    else
+        k_router_gemv<0><<<g, 64, 0, s>>>((const uint16_t *)L->router_w, x, T, L->H, L->E, part);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
+
+int launch_router_mfma(const bitmoe_layer *L, const void *x, int T, float *logits, hipStream_t s) {
+    dim3 g((T + 63) / 64, (L->E + 63) / 64);
+    k_router_mfma<<<g, 256, 0, s>>>((const uint16_t *)x, (const uint16_t *)L->router_w, T, L->H,
+                                    L->E, logits);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
+
+int launch_topk(const float *part, int KS, int T, int E, int k, float *logits, int32_t *ids,
+                float *w, hipStream_t s) {
+    k_topk<<<(T + 3) / 4, 256, 0, s>>>(part, KS, T, E, k, logits, ids, w);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
+
+}  // namespace bm_host

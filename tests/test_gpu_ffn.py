@@ -1,0 +1,192 @@
+"""GPU parity: the MoE FFN (decode and prefill entry points) against the
+oracle, max|err| <= 2e-2 * rms(oracle output) with fp32 accumulation.
+
+The FFN tests feed both sides the same ids and weights (the oracle's
+routing, as float32), so the FFN is checked on its own; an end-to-end test
+routes on the GPU as well.  Full-size prefill chunks are compared on a
+sample of tokens the oracle computes one by one (hottest and coldest
+experts included)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _gpu import (assert_close_rms, device_layer, near_tie_tokens, require_gpu, say, synth_layer,
+                  torch, x_to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _routing(w, x):
+    """ids int32 [T,k] and weights as float32 (what the GPU receives)."""
+    L = synth_layer(w)
+    if w.routing == "zipf":
+        ids, wt = oracle.topk(synth.zipf_logits(w, T=x.shape[0]).astype(np.float64), w.k)
+    else:
+        ids, wt = oracle.route(x, L.router(), w.k)
+    return ids.astype(np.int32), wt.astype(np.float32)
+
+
+def _gpu_ffn(w, x, ids, wt, mode):
+    import bit_moe_amd as bm
+    lay = device_layer(w)
+    fn = bm.ffn_decode if mode == "decode" else bm.ffn_prefill
+    y = fn(lay, x_to_device(x), torch.from_numpy(ids).cuda(), torch.from_numpy(wt).cuda())
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _oracle_rows(w, x, ids, wt, rows):
+    L = synth_layer(w)
+    return oracle.layer_ffn(L, x[rows], ids[rows], wt[rows].astype(np.float64))
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_tiny_layer_all_tokens(mode):
+    require_gpu()
+    w = synth.WORKLOADS["tiny"]
+    x, _ = synth.make_tokens(w)
+    ids, wt = _routing(w, x)
+    y = _gpu_ffn(w, x, ids, wt, mode)
+    ref = _oracle_rows(w, x, ids, wt, np.arange(w.T))
+    assert_close_rms(y, ref, what=f"tiny/{mode}")
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_tiny_shapes_with_shared_and_ragged_tokens(mode):
+    """Shared expert present, T not a multiple of any tile, bf16 and fp32."""
+    require_gpu()
+    for xd, T in (("bf16", 37), ("f32", 5)):
+        w = synth.WORKLOADS["tiny"].with_(name=f"tiny_sh_{xd}", T=T, shared=True, x_dtype=xd, seed=21)
+        x, _ = synth.make_tokens(w)
+        ids, wt = _routing(w, x)
+        y = _gpu_ffn(w, x, ids, wt, mode)
+        ref = _oracle_rows(w, x, ids, wt, np.arange(T))
+        assert_close_rms(y, ref, what=f"tiny-shared/{xd}/{mode}/T={T}")
+
+
+def test_decode_b1_full():
+    require_gpu()
+    w = synth.WORKLOADS["decode_b1"]
+    x, _ = synth.make_tokens(w)
+    ids, wt = _routing(w, x)
+    say(f"[ffn] decode_b1 ids={ids.tolist()}")
+    y = _gpu_ffn(w, x, ids, wt, "decode")
+    ref = _oracle_rows(w, x, ids, wt, np.arange(1))
+    assert_close_rms(y, ref, what="decode_b1")
+
+
+def test_decode_b16_zipf_full():
+    require_gpu()
+    w = synth.WORKLOADS["decode_b16_zipf"]
+    x, _ = synth.make_tokens(w)
+    ids, wt = _routing(w, x)
+    say(f"[ffn] decode_b16_zipf distinct experts={len(np.unique(ids))}")
+    y = _gpu_ffn(w, x, ids, wt, "decode")
+    ref = _oracle_rows(w, x, ids, wt, np.arange(w.T))
+    assert_close_rms(y, ref, what="decode_b16_zipf")
+
+
+def _sample_rows(ids, n_random, seed):
+    """Random tokens plus tokens routed to the hottest and coldest experts."""
+    rng = np.random.default_rng(seed)
+    T = ids.shape[0]
+    c = np.bincount(ids.ravel())
+    hot, cold = int(np.argmax(c)), int(np.argmin(np.where(c > 0, c, c.max() + 1)))
+    t_hot = np.nonzero((ids == hot).any(axis=1))[0]
+    t_cold = np.nonzero((ids == cold).any(axis=1))[0]
+    rows = set(rng.choice(T, size=n_random, replace=False).tolist())
+    rows |= {int(t_hot[0]), int(t_hot[-1]), int(t_cold[0]), 0, T - 1}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["prefill_2k", "prefill_8k_zipf"])
+def test_prefill_full_size_sampled(name):
+    require_gpu()
+    w = synth.WORKLOADS[name]
+    x, _ = synth.make_tokens(w)
+    ids, wt = _routing(w, x)
+    c = np.bincount(ids.ravel(), minlength=w.E)
+    say(f"[ffn] {name} rows/expert max={c.max()} min={c.min()} active={np.count_nonzero(c)}")
+    y = _gpu_ffn(w, x, ids, wt, "prefill")
+    rows = _sample_rows(ids, 6, 1)
+    ref = _oracle_rows(w, x, ids, wt, rows)
+    assert_close_rms(y[rows], ref, what=f"{name} rows {rows.tolist()}")
+    assert np.all(np.isfinite(y))
+
+
+def test_decode_and_prefill_agree_and_batch_rows_match_single_tokens():
+    require_gpu()
+    w = synth.WORKLOADS["decode_b16_zipf"]
+    x, _ = synth.make_tokens(w)
+    ids, wt = _routing(w, x)
+    yd = _gpu_ffn(w, x, ids, wt, "decode")
+    yp = _gpu_ffn(w, x, ids, wt, "prefill")
+    assert_close_rms(yp, yd.astype(np.float64), what="prefill vs decode")
+    for t in (0, 7, 15):
+        y1 = _gpu_ffn(w, x[t:t + 1], ids[t:t + 1], wt[t:t + 1], "decode")
+        np.testing.assert_array_equal(y1[0], yd[t])
+
+
+def test_deterministic_repeat():
+    require_gpu()
+    w = synth.WORKLOADS["decode_b16_zipf"]
+    x, _ = synth.make_tokens(w)
+    ids, wt = _routing(w, x)
+    for mode in ("decode", "prefill"):
+        a = _gpu_ffn(w, x, ids, wt, mode)
+        b = _gpu_ffn(w, x, ids, wt, mode)
+        np.testing.assert_array_equal(a, b)
+
+
+def test_zero_activation_gives_zero():
+    require_gpu()
+    w = synth.WORKLOADS["decode_b16_zipf"]
+    x = np.zeros((4, w.H), dtype=np.uint16)
+    ids = np.array([[0, 1, 2, 3, 4, 5, 6, 7]] * 4, dtype=np.int32)
+    wt = np.full((4, 8), 0.125, dtype=np.float32)
+    for mode in ("decode", "prefill"):
+        assert np.all(_gpu_ffn(w, x, ids, wt, mode) == 0.0)
+
+
+def test_hot_expert_many_tiles_and_unused_experts():
+    """Every token picks the same k experts: one expert bucket spans many
+    row tiles, all other experts are empty."""
+    require_gpu()
+    w = synth.WORKLOADS["tiny"].with_(name="tiny_hot", T=300, x_dtype="bf16", seed=5)
+    x, _ = synth.make_tokens(w)
+    ids = np.tile(np.array([6, 1], dtype=np.int32), (w.T, 1))
+    wt = np.tile(np.array([0.7, 0.3], dtype=np.float32), (w.T, 1))
+    ref = _oracle_rows(w, x, ids, wt, np.arange(w.T))
+    for mode in ("decode", "prefill"):
+        assert_close_rms(_gpu_ffn(w, x, ids, wt, mode), ref, what=f"hot/{mode}")
+
+
+def test_single_expert_single_slot():
+    require_gpu()
+    w = synth.WORKLOADS["tiny"].with_(name="tiny_k1", k=1, T=3, seed=8)
+    x, _ = synth.make_tokens(w)
+    ids = np.array([[3], [3], [0]], dtype=np.int32)
+    wt = np.ones((3, 1), dtype=np.float32)
+    ref = _oracle_rows(w, x, ids, wt, np.arange(3))
+    for mode in ("decode", "prefill"):
+        assert_close_rms(_gpu_ffn(w, x, ids, wt, mode), ref, what=f"k1/{mode}")
+
+
+def test_end_to_end_route_then_ffn():
+    require_gpu()
+    import bit_moe_amd as bm
+    w = synth.WORKLOADS["decode_b1"].with_(T=4, name="decode_b4")
+    x, _ = synth.make_tokens(w)
+    lay = device_layer(synth.WORKLOADS["decode_b1"])
+    L = synth_layer(synth.WORKLOADS["decode_b1"])
+    xd = x_to_device(x)
+    gid, gw = bm.route(lay, xd)
+    y = bm.ffn_decode(lay, xd, gid, gw)
+    torch.cuda.synchronize()
+    lg = oracle.router_logits(x, L.router())
+    assert len(near_tie_tokens(lg, w.k)) == 0
+    rid, rw = oracle.topk(lg, w.k)
+    np.testing.assert_array_equal(gid.cpu().numpy(), rid)
+    ref = oracle.layer_ffn(L, x, rid, rw)
+    assert_close_rms(y.cpu().numpy(), ref, what="route+decode")
