@@ -84,6 +84,10 @@ def time_dominant(step, n):
     import torch
     import bit_moe_amd as bm
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for s, e in evs:            # torch creates the HIP events on first record
+        s.record()
+        e.record()
+    torch.cuda.synchronize()
     for i, (s, e) in enumerate(evs):
         bm.set_timing_events(s, e)
         step(i)

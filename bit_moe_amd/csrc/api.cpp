@@ -95,7 +95,7 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
 
 size_t route_ws_bytes(const bitmoe_layer *L, int T, int x_dtype) {
     if (T >= kMfmaRouterMinT && x_dtype == BITMOE_BF16) return up256((size_t)T * L->E * 4);
-    return up256((size_t)bm_host::router_splits(L->H) * std::min(T, 8) * L->E * 4);
+    return up256((size_t)std::min(T, bm_host::router_tokens_per_launch()) * L->E * 4);
 }
 
 int check_ws(void *ws, size_t have, size_t need) {
@@ -176,16 +176,16 @@ int moe_route(const bitmoe_layer *L, const void *x, int x_dtype, int T, float *l
         if ((rc = bm_host::launch_router_mfma(L, x, T, lg, s))) return rc;
         return bm_host::launch_topk(lg, 1, T, L->E, L->k, nullptr, ids, w, s);
     }
-    // split-K GEMV over token batches of at most 8 rows
-    const int KS = bm_host::router_splits(L->H);
+    // one wave per expert row, token batches of router_tokens_per_launch()
+    const int NT = bm_host::router_tokens_per_launch();
     const size_t xs = x_dtype == BITMOE_BF16 ? 2 : 4;
-    for (int t0 = 0; t0 < T; t0 += 8) {
-        int nt = std::min(8, T - t0);
+    for (int t0 = 0; t0 < T; t0 += NT) {
+        int nt = std::min(NT, T - t0);
         const char *xb = static_cast<const char *>(x) + (size_t)t0 * L->H * xs;
-        if ((rc = bm_host::launch_router_gemv(L, xb, x_dtype, nt, part, s))) return rc;
-        if ((rc = bm_host::launch_topk(part, KS, nt, L->E, L->k,
-                                       logits ? logits + (size_t)t0 * L->E : nullptr,
-                                       ids + (size_t)t0 * L->k, w + (size_t)t0 * L->k, s)))
+        float *lg = logits ? logits + (size_t)t0 * L->E : part;
+        if ((rc = bm_host::launch_router_gemv(L, xb, x_dtype, nt, lg, s))) return rc;
+        if ((rc = bm_host::launch_topk(lg, 1, nt, L->E, L->k, nullptr, ids + (size_t)t0 * L->k,
+                                       w + (size_t)t0 * L->k, s)))
             return rc;
     }
     return BITMOE_OK;

@@ -64,10 +64,10 @@ int launch_pack_iq2x(const void *src, void *dst, int E, int N, int K, hipStream_
 int launch_pack_q2k(const void *src, void *dst, int E, int N, int K, hipStream_t s);
 int launch_pack_bf16(const void *src, void *dst, int N, int K, hipStream_t s);
 
-// router logits: partial sums over KS K-splits, part [KS][T][E] fp32
-int router_splits(int H);
+// router logits [T][E] fp32 for at most router_tokens_per_launch() tokens
+int router_tokens_per_launch();
 int launch_router_gemv(const bitmoe_layer *L, const void *x, int x_dtype, int T,
-                       float *part, hipStream_t s);
+                       float *logits, hipStream_t s);
 int launch_router_mfma(const bitmoe_layer *L, const void *x, int T, float *logits,
                        hipStream_t s);
 int launch_topk(const float *part, int KS, int T, int E, int k, float *logits,

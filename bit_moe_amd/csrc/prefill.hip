@@ -32,14 +32,16 @@ struct PrefillArgs {
 
 // --- B-tile dequantisation into LDS (bf16 = RNE of the exact fp32 value) ---
 
-// 32 weights of IQ2X group g of block (n, kb) of one expert's tiled slab.
-BM_DEV void iq2x_group_to_lds(const uint8_t *slab, int N, int nb, int n, int kb, int g,
-                              const uint2 *sgrid, uint16_t *dst) {
+// 32 weights of IQ2X group g of block (n, kb) of one expert's tiled slab,
+// without the superblock scale: +-(2s+1)*grid[idx][i].  With codebook
+// magnitudes in {1,3,5,7} these are odd integers <= 217, exact in bf16; the
+// factor d/8 is applied to the fp32 partial sums of each superblock.
+BM_DEV void iq2x_group_int_to_lds(const uint8_t *slab, int nb, int n, int kb, int g,
+                                  const uint2 *sgrid, uint16_t *dst) {
     const int P = n >> 6, r = n & 63;
     const int64_t pk = (int64_t)P * nb + kb;
     const uint2 gw = reinterpret_cast<const uint2 *>(slab)[((pk * 4 + (g >> 1)) * 64 + r) * 2 + (g & 1)];
-    const float d = fp16_to_f32(reinterpret_cast<const uint16_t *>(slab + (int64_t)N * nb * 64)[pk * 64 + r]);
-    const float db = d * fmaf((float)(gw.y >> 28), 0.25f, 0.125f);
+    const float s2 = (float)(2u * (gw.y >> 28) + 1u);
     uint32_t out[16];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -50,8 +52,8 @@ BM_DEV void iq2x_group_to_lds(const uint8_t *slab, int N, int nb, int n, int kb,
         for (int i = 0; i < 8; i += 2) {
             uint32_t m0 = ((i < 4 ? row.x : row.y) >> (8 * (i & 3))) & 0xFFu;
             uint32_t m1 = ((i < 4 ? row.x : row.y) >> (8 * ((i + 1) & 3))) & 0xFFu;
-            uint32_t b0 = f32_to_bf16_rne(db * (float)m0) | (((sig >> i) & 1u) << 15);
-            uint32_t b1 = f32_to_bf16_rne(db * (float)m1) | (((sig >> (i + 1)) & 1u) << 15);
+            uint32_t b0 = f32_to_bf16_rne(s2 * (float)m0) | (((sig >> i) & 1u) << 15);
+            uint32_t b1 = f32_to_bf16_rne(s2 * (float)m1) | (((sig >> (i + 1)) & 1u) << 15);
             out[4 * j + i / 2] = b0 | (b1 << 16);
         }
     }
@@ -60,26 +62,25 @@ BM_DEV void iq2x_group_to_lds(const uint8_t *slab, int N, int nb, int n, int kb,
     for (int q = 0; q < 4; q++) o[q] = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
 }
 
-// 16 weights of Q2K sub-block b of block (n, kb).
-BM_DEV void q2k_sub_to_lds(const uint8_t *slab, int N, int nb, int n, int kb, int b, uint16_t *dst) {
+// 16 weights of Q2K sub-block b of block (n, kb) without d and the min:
+// scale*q, integers 0..45, exact in bf16.  The kernel applies d and the
+// -dmin*min*sum(h) term to the fp32 partial sums of each superblock.
+BM_DEV void q2k_sub_int_to_lds(const uint8_t *slab, int N, int nb, int n, int kb, int b, uint16_t *dst) {
     const int P = n >> 6, r = n & 63;
     const int64_t pk = (int64_t)P * nb + kb;
     const int64_t S = (int64_t)N * nb;
     const int hh = b >> 3, j = (b & 7) >> 1, c = 2 * hh + (b & 1);
     const uint4 qv = reinterpret_cast<const uint4 *>(slab)[(pk * 4 + c) * 64 + r];
-    const uint32_t scb = slab[S * 64 + (pk * 64 + r) * 16 + b];
-    const uint32_t dd = reinterpret_cast<const uint32_t *>(slab + S * 80)[pk * 64 + r];
-    const float dsc = fp16_to_f32(dd & 0xFFFFu) * (float)(scb & 15u);
-    const float dm = fp16_to_f32(dd >> 16) * (float)(scb >> 4);
+    const float sc = (float)(slab[S * 64 + (pk * 64 + r) * 16 + b] & 15u);
     uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
     uint32_t out[8];
 #pragma unroll
     for (int w = 0; w < 4; w++) {
         uint32_t q = (qw[w] >> (2 * j)) & 0x03030303u;
-        uint32_t v0 = f32_to_bf16_rne(fmaf(dsc, (float)(q & 0xFFu), -dm));
-        uint32_t v1 = f32_to_bf16_rne(fmaf(dsc, (float)((q >> 8) & 0xFFu), -dm));
-        uint32_t v2 = f32_to_bf16_rne(fmaf(dsc, (float)((q >> 16) & 0xFFu), -dm));
-        uint32_t v3 = f32_to_bf16_rne(fmaf(dsc, (float)(q >> 24), -dm));
+        uint32_t v0 = __float_as_uint(sc * (float)(q & 0xFFu)) >> 16;
+        uint32_t v1 = __float_as_uint(sc * (float)((q >> 8) & 0xFFu)) >> 16;
+        uint32_t v2 = __float_as_uint(sc * (float)((q >> 16) & 0xFFu)) >> 16;
+        uint32_t v3 = __float_as_uint(sc * (float)(q >> 24)) >> 16;
         out[2 * w] = v0 | (v1 << 16);
         out[2 * w + 1] = v2 | (v3 << 16);
     }
@@ -138,46 +139,64 @@ k_prefill_gateup(int H, int I, int k, const uint8_t *__restrict__ gate,
     const int nb = H / kQK;
     const int64_t slab = (int64_t)I * nb * 66;
     const uint8_t *G = gate + e * slab, *U = up + e * slab;
-    f32x4 acc[4][2];
+    const uint16_t *Gd = reinterpret_cast<const uint16_t *>(G + (int64_t)I * nb * 64);
+    const uint16_t *Ud = reinterpret_cast<const uint16_t *>(U + (int64_t)I * nb * 64);
+    const int ncol = n0 + 16 * wv + (lane & 15);          // this lane's output column
+    const int64_t dbase = (int64_t)(ncol >> 6) * nb * 64 + (ncol & 63);
+    f32x4 acc[4][2], part[4][2];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int bcol[2] = {16 * wv, 64 + 16 * wv};
     __syncthreads();
-    for (int k0 = 0; k0 < H; k0 += BK) {
-        // A: 64 rows x 128 K -> 1024 pieces of 8 values, 4 per thread
+    for (int kb = 0; kb < nb; kb++) {
 #pragma unroll
-        for (int p = 0; p < 4; p++) {
-            int piece = tid + 256 * p, r = piece >> 4, c = (piece & 15) * 8;
-            const int t = stok[r];
-            uint4 v;
-            if (XBF16) {
-                v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)t * H + k0 + c);
-            } else {
-                const float4 *xp = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)t * H + k0 + c);
-                float4 a = xp[0], b = xp[1];
-                v = make_uint4(f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16),
-                               f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16),
-                               f32_to_bf16_rne(b.x) | (f32_to_bf16_rne(b.y) << 16),
-                               f32_to_bf16_rne(b.z) | (f32_to_bf16_rne(b.w) << 16));
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int half = 0; half < 2; half++) {
+            const int k0 = kb * kQK + half * BK;
+            // A: 64 rows x 128 K -> 1024 pieces of 8 values, 4 per thread
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                int piece = tid + 256 * p, r = piece >> 4, c = (piece & 15) * 8;
+                const int t = stok[r];
+                uint4 v;
+                if (XBF16) {
+                    v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)t * H + k0 + c);
+                } else {
+                    const float4 *xp = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)t * H + k0 + c);
+                    float4 a = xp[0], b = xp[1];
+                    v = make_uint4(f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16),
+                                   f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16),
+                                   f32_to_bf16_rne(b.x) | (f32_to_bf16_rne(b.y) << 16),
+                                   f32_to_bf16_rne(b.z) | (f32_to_bf16_rne(b.w) << 16));
+                }
+                *reinterpret_cast<uint4 *>(sa + r * LDK + c) = v;
             }
-            *reinterpret_cast<uint4 *>(sa + r * LDK + c) = v;
-        }
-        // B: 128 rows x 4 groups = 512 (row, group) units, 2 per thread
-        const int kb = k0 / kQK, g0 = (k0 % kQK) / 32;
+            // B: 128 rows x 4 groups = 512 (row, group) units, 2 per thread
 #pragma unroll
-        for (int p = 0; p < 2; p++) {
-            int u = tid + 256 * p, row = u >> 2, gg = u & 3;
-            const uint8_t *S = row < 64 ? G : U;
-            iq2x_group_to_lds(S, I, nb, n0 + (row & 63), kb, g0 + gg, sgrid, sb + row * LDK + 32 * gg);
+            for (int p = 0; p < 2; p++) {
+                int u = tid + 256 * p, row = u >> 2, gg = u & 3;
+                const uint8_t *S = row < 64 ? G : U;
+                iq2x_group_int_to_lds(S, nb, n0 + (row & 63), kb, 4 * half + gg, sgrid, sb + row * LDK + 32 * gg);
+            }
+            __syncthreads();
+            mfma_stage<2>(sa, sb, bcol, part);
+            __syncthreads();
         }
-        __syncthreads();
-        mfma_stage<2>(sa, sb, bcol, acc);
-        __syncthreads();
+        const float dg = 0.125f * fp16_to_f32(Gd[dbase + (int64_t)kb * 64]);
+        const float du = 0.125f * fp16_to_f32(Ud[dbase + (int64_t)kb * 64]);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                acc[i][0][q] = fmaf(dg, part[i][0][q], acc[i][0][q]);
+                acc[i][1][q] = fmaf(du, part[i][1][q], acc[i][1][q]);
+            }
     }
     // epilogue: lane holds rows 4*(lane/16)+q of each M block, column lane%16
-    const int n = n0 + 16 * wv + (lane & 15);
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -185,14 +204,20 @@ k_prefill_gateup(int H, int I, int k, const uint8_t *__restrict__ gate,
             int m = 16 * i + 4 * (lane >> 4) + q;
             if (m < rows) {
                 float hv = silu(acc[i][0][q]) * acc[i][1][q];
-                h[(int64_t)(off + r0 + m) * I + n] = (uint16_t)f32_to_bf16_rne(hv);
+                h[(int64_t)(off + r0 + m) * I + ncol] = (uint16_t)f32_to_bf16_rne(hv);
             }
         }
 }
 
 // ---------------------------------------------------------------------------
 // down.  grid = (H/64, max_tiles), 256 threads.  A = h rows (bucket order).
+// Per superblock: P = h . (scale*q) on MFMA, Pmin = Hsum . min on one more
+// MFMA whose K slots hold the 16 sub-block sums of h split into bf16 high
+// and low parts (so the min term keeps ~16 bits), then
+// C += d * P - dmin * Pmin in fp32.
 // ---------------------------------------------------------------------------
+constexpr int HS_LD = 40;     // padded row stride of the sub-block sums (bf16)
+
 __global__ void __launch_bounds__(256)
 k_prefill_down(int H, int I, const uint8_t *__restrict__ down, const uint16_t *__restrict__ h,
                const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
@@ -200,6 +225,7 @@ k_prefill_down(int H, int I, const uint8_t *__restrict__ down, const uint16_t *_
                const int32_t *__restrict__ n_tiles, float *__restrict__ o) {
     __shared__ __attribute__((aligned(16))) uint16_t sa[BM * LDK];
     __shared__ __attribute__((aligned(16))) uint16_t sb[64 * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t hs[BM * HS_LD];
     const int tile = blockIdx.y;
     if (tile >= *n_tiles) return;
     const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
@@ -208,37 +234,79 @@ k_prefill_down(int H, int I, const uint8_t *__restrict__ down, const uint16_t *_
     const int tid = threadIdx.x, lane = lane_id();
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nb = I / kQK;
-    const uint8_t *D = down + (int64_t)e * H * nb * 84;
-    f32x4 acc[4][1];
+    const int64_t S = (int64_t)H * nb;
+    const uint8_t *D = down + (int64_t)e * S * 84;
+    const int ncol = n0 + 16 * wv + (lane & 15);           // this lane's output column
+    const int64_t pbase = (int64_t)(ncol >> 6) * nb * 64 + (ncol & 63);
+    f32x4 acc[4][1], part[4][1];
 #pragma unroll
     for (int i = 0; i < 4; i++) acc[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int bcol[1] = {16 * wv};
-    for (int k0 = 0; k0 < I; k0 += BK) {
+    for (int kb = 0; kb < nb; kb++) {
 #pragma unroll
-        for (int p = 0; p < 4; p++) {
-            int piece = tid + 256 * p, r = piece >> 4, c = (piece & 15) * 8;
-            int row = off + r0 + min(r, rows - 1);
-            *reinterpret_cast<uint4 *>(sa + r * LDK + c) =
-                *reinterpret_cast<const uint4 *>(h + (int64_t)row * I + k0 + c);
-        }
-        // B: 64 rows x 8 sub-blocks (128 K) = 512 units, 2 per thread
-        const int kb = k0 / kQK, b0 = (k0 % kQK) / 16;
+        for (int i = 0; i < 4; i++) part[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int half = 0; half < 2; half++) {
+            const int k0 = kb * kQK + half * BK;
 #pragma unroll
-        for (int p = 0; p < 2; p++) {
-            int u = tid + 256 * p, row = u >> 3, sbk = u & 7;
-            q2k_sub_to_lds(D, H, nb, n0 + row, kb, b0 + sbk, sb + row * LDK + 16 * sbk);
+            for (int p = 0; p < 4; p++) {
+                int piece = tid + 256 * p, r = piece >> 4, c = (piece & 15) * 8;
+                int row = off + r0 + min(r, rows - 1);
+                *reinterpret_cast<uint4 *>(sa + r * LDK + c) =
+                    *reinterpret_cast<const uint4 *>(h + (int64_t)row * I + k0 + c);
+            }
+            // B: 64 rows x 8 sub-blocks (128 K) = 512 units, 2 per thread
+#pragma unroll
+            for (int p = 0; p < 2; p++) {
+                int u = tid + 256 * p, row = u >> 3, sbk = u & 7;
+                q2k_sub_int_to_lds(D, H, nb, n0 + row, kb, 8 * half + sbk, sb + row * LDK + 16 * sbk);
+            }
+            __syncthreads();
+            // sums of 16 h values per (row, sub-block), split hi + lo
+#pragma unroll
+            for (int p = 0; p < 2; p++) {
+                int u = tid + 256 * p, row = u >> 3, j = u & 7;
+                const uint4 *src = reinterpret_cast<const uint4 *>(sa + row * LDK + 16 * j);
+                uint4 a = src[0], b = src[1];
+                uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                float sum = 0.f;
+#pragma unroll
+                for (int q = 0; q < 8; q++) sum += bf16_lo(w8[q]) + bf16_hi(w8[q]);
+                uint32_t hi = f32_to_bf16_rne(sum);
+                uint32_t lo = f32_to_bf16_rne(sum - bf16_to_f32(hi));
+                hs[row * HS_LD + 8 * half + j] = (uint16_t)hi;
+                hs[row * HS_LD + 16 + 8 * half + j] = (uint16_t)lo;
+            }
+            mfma_stage<1>(sa, sb, bcol, part);
+            __syncthreads();
         }
-        __syncthreads();
-        mfma_stage<1>(sa, sb, bcol, acc);
-        __syncthreads();
+        // min term: K slots = [Hsum_hi 0..15 | Hsum_lo 0..15] x [min 0..15 | min 0..15]
+        const int64_t pk = pbase + (int64_t)kb * 64;
+        const int kg = lane >> 4;
+        const uint2 scb = *reinterpret_cast<const uint2 *>(D + S * 64 + pk * 16 + 8 * (kg & 1));
+        uint32_t mw[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            uint32_t word = q < 2 ? scb.x : scb.y;
+            uint32_t m0 = (word >> (16 * (q & 1) + 4)) & 15u, m1 = (word >> (16 * (q & 1) + 12)) & 15u;
+            mw[q] = (__float_as_uint((float)m0) >> 16) | (__float_as_uint((float)m1) & 0xFFFF0000u);
+        }
+        const bf16x8 fbm = __builtin_bit_cast(bf16x8, make_uint4(mw[0], mw[1], mw[2], mw[3]));
+        const uint32_t dd = reinterpret_cast<const uint32_t *>(D + S * 80)[pk];
+        const float d = fp16_to_f32(dd & 0xFFFFu), dmin = fp16_to_f32(dd >> 16);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const bf16x8 fam = *reinterpret_cast<const bf16x8 *>(hs + (16 * i + (lane & 15)) * HS_LD + 8 * kg);
+            const f32x4 pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fam, fbm, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; q++) acc[i][0][q] = fmaf(d, part[i][0][q], fmaf(-dmin, pm[q], acc[i][0][q]));
+        }
     }
-    const int n = n0 + 16 * wv + (lane & 15);
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             int m = 16 * i + 4 * (lane >> 4) + q;
-            if (m < rows) o[(int64_t)perm[off + r0 + m] * H + n] = acc[i][0][q];
+            if (m < rows) o[(int64_t)perm[off + r0 + m] * H + ncol] = acc[i][0][q];
         }
 }
 

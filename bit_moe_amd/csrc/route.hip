@@ -12,28 +12,30 @@ namespace {
 
 using namespace bm;
 
-constexpr int kRouterKC = 128;   // K columns per split of the small-T router
+constexpr int kRouterNT = 16;   // tokens per launch of the small-T router
 
 // ---------------------------------------------------------------------------
-// Small-T router: one lane per expert row, K split over blockIdx.x.  Each
-// lane streams 16-byte pieces of its own row; the activations are the same
-// for all lanes, so they come in through scalar loads.  Writes partial sums
-// part[ks][t][e]; the top-k kernel adds the splits in a fixed order.
+// Small-T router: one wave per expert row, lanes across K (16-byte pieces,
+// each wave reads its row once in 1 KiB coalesced steps), a wave reduction
+// per token.  Each logit is produced by exactly one wave, in a fixed order,
+// so results are reproducible run to run.
 // ---------------------------------------------------------------------------
 template <int XBF16, int NT>
-BM_DEV void router_tokens(const uint4 *__restrict__ wrow, const void *__restrict__ x, int H,
-                          int t0, int nt, int k0, float *__restrict__ part, int T, int E, int e,
-                          bool valid, int ks) {
+BM_DEV void router_row(const uint4 *__restrict__ wrow, const void *__restrict__ x, int H, int T,
+                       int E, int e, float *__restrict__ logits) {
+    const int lane = lane_id();
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] = 0.f;
-#pragma unroll 4
-    for (int c = 0; c < kRouterKC / 8; c++) {
-        uint4 wv = valid ? wrow[c] : make_uint4(0, 0, 0, 0);
-        int k = k0 + 8 * c;
+    const int steps = (H + 511) / 512;          // H is a multiple of 256
+#pragma unroll 2
+    for (int s = 0; s < steps; s++) {
+        const int k = 512 * s + 8 * lane;
+        if (k >= H) break;                       // only in a half-width last step
+        const uint4 wv = wrow[64 * s + lane];
 #pragma unroll
         for (int t = 0; t < NT; t++) {
-            int tt = t0 + (t < nt ? t : 0);
+            const int tt = t < T ? t : 0;
             if (XBF16) {
                 const uint4 xv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)tt * H + k);
                 float a = acc[t];
@@ -44,7 +46,7 @@ BM_DEV void router_tokens(const uint4 *__restrict__ wrow, const void *__restrict
                 acc[t] = a;
             } else {
                 const float4 *xp = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)tt * H + k);
-                float4 x0 = xp[0], x1 = xp[1];
+                const float4 x0 = xp[0], x1 = xp[1];
                 float a = acc[t];
                 a = fmaf(bf16_lo(wv.x), x0.x, a); a = fmaf(bf16_hi(wv.x), x0.y, a);
                 a = fmaf(bf16_lo(wv.y), x0.z, a); a = fmaf(bf16_hi(wv.y), x0.w, a);
@@ -54,29 +56,26 @@ BM_DEV void router_tokens(const uint4 *__restrict__ wrow, const void *__restrict
             }
         }
     }
-    if (valid) {
 #pragma unroll
-        for (int t = 0; t < NT; t++)
-            if (t < nt) part[((int64_t)ks * T + t0 + t) * E + e] = acc[t];
+    for (int t = 0; t < NT; t++) {
+        const float v = wave_sum(acc[t]);
+        if (lane == 0 && t < T) logits[(int64_t)t * E + e] = v;
     }
 }
 
 template <int XBF16>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 k_router_gemv(const uint16_t *__restrict__ wr, const void *__restrict__ x, int T, int H, int E,
-              float *__restrict__ part) {
-    int ks = blockIdx.x;
-    int e = blockIdx.y * 64 + (int)threadIdx.x;
-    bool valid = e < E;
-    int k0 = ks * kRouterKC;
-    const uint4 *wrow = reinterpret_cast<const uint4 *>(wr + (int64_t)(valid ? e : 0) * H + k0);
-    for (int t0 = 0; t0 < T; t0 += 8) {
-        int nt = min(8, T - t0);
-        if (nt == 1)
-            router_tokens<XBF16, 1>(wrow, x, H, t0, 1, k0, part, T, E, e, valid, ks);
-        else
-            router_tokens<XBF16, 8>(wrow, x, H, t0, nt, k0, part, T, E, e, valid, ks);
-    }
+              float *__restrict__ logits) {
+    const int e = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (e >= E) return;
+    const uint4 *wrow = reinterpret_cast<const uint4 *>(wr + (int64_t)e * H);
+    if (T == 1)
+        router_row<XBF16, 1>(wrow, x, H, T, E, e, logits);
+    else if (T <= 4)
+        router_row<XBF16, 4>(wrow, x, H, T, E, e, logits);
+    else
+        router_row<XBF16, kRouterNT>(wrow, x, H, T, E, e, logits);
 }
 
 // ---------------------------------------------------------------------------
@@ -205,15 +204,15 @@ k_topk(const float *__restrict__ part, int KS, int T, int E, int k, float *__res
 
 namespace bm_host {
 
-int router_splits(int H) { return H / kRouterKC; }
+int router_tokens_per_launch() { return kRouterNT; }
 
-int launch_router_gemv(const bitmoe_layer *L, const void *x, int x_dtype, int T, float *part,
+int launch_router_gemv(const bitmoe_layer *L, const void *x, int x_dtype, int T, float *logits,
                        hipStream_t s) {
-    dim3 g(router_splits(L->H), (L->E + 63) / 64);
+    dim3 g((L->E + 3) / 4);
     if (x_dtype == BITMOE_BF16)
-        k_router_gemv<1><<<g, 64, 0, s>>>((const uint16_t *)L->router_w, x, T, L->H, L->E, part);
+        k_router_gemv<1><<<g, 256, 0, s>>>((const uint16_t *)L->router_w, x, T, L->H, L->E, logits);
     else
-        k_router_gemv<0><<<g, 64, 0, s>>>((const uint16_t *)L->router_w, x, T, L->H, L->E, part);
+        k_router_gemv<0><<<g, 256, 0, s>>>((const uint16_t *)L->router_w, x, T, L->H, L->E, logits);
     BM_LAUNCH_CHECK();
     return BITMOE_OK;
 }
