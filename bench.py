@@ -107,19 +107,18 @@ def decode_b1(args, L, lays):
     ids = torch.empty((1, w.k), dtype=torch.int32, device="cuda")
     wt = torch.empty((1, w.k), dtype=torch.float32, device="cuda")
     y = torch.empty((1, w.H), dtype=torch.float32, device="cuda")
-    rws = torch.empty(max(256, bm.route_workspace_bytes(lays[0], 1, bm.BF16)), dtype=torch.uint8, device="cuda")
     ws = torch.empty(bm.workspace_bytes(lays[0], 1, bm.DECODE), dtype=torch.uint8, device="cuda")
 
     def step(i):
         lay, x = lays[i % len(lays)], xs[i % R]
-        bm.route(lay, x, ids=ids, w=wt, ws=rws)
-        bm.ffn_decode(lay, x, ids, wt, y=y, ws=ws)
+        bm.forward_decode(lay, x, ids=ids, w=wt, y=y, ws=ws)
 
     ms = time_steps(step, args.warmup, args.steps)
     gu_ms = time_dominant(step, min(args.steps, 100))
+    # the timed launch streams the routed gate/up blocks and the shared down
     routed = w.k * (2 * w.I * (w.H // 256) * 66)
-    shared = 2 * w.I * w.H * 2
-    gu_bytes = routed + shared
+    shared_down = w.I * w.H * 2
+    gu_bytes = routed + shared_down
     step_bytes = w.k * (2 * w.I * (w.H // 256) * 66 + w.H * (w.I // 256) * 84) + 3 * w.I * w.H * 2 + w.E * w.H * 2
     return dict(ms=ms, gu_ms=gu_ms, gu_bytes=gu_bytes, step_bytes=step_bytes)
 
@@ -234,7 +233,7 @@ def main():
                    "tokens_per_step": 1, "layer_copies_rotated": args.copies,
                    "step_hbm_bytes": r["step_bytes"],
                    "step_hbm_GBps": r["step_bytes"] / (r["ms"] * 1e-3) / 1e9},
-        "roofline": {"bound": "hbm", "kernel": "k_decode_gateup",
+        "roofline": {"bound": "hbm", "kernel": "k_dec_gateup",
                      "achieved": gu_bw / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": gu_bw / HBM_PEAK, "traffic": None,
                      "kernel_us": r["gu_ms"] * 1e3, "algorithmic_bytes": r["gu_bytes"]},

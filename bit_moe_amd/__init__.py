@@ -5,7 +5,7 @@ device memory and streams only; every step of the layer runs in the
 library's HIP kernels.
 """
 from ._lib import (BF16, BitMoEError, DECODE, F32, Layer, PREFILL, SYMBOLS, bucket, dequant_iq2x,
-                   dequant_q2k, ffn_decode, ffn_prefill, lib, pack_bf16, pack_iq2x, pack_q2k, route,
+                   dequant_q2k, ffn_decode, ffn_prefill, forward_decode, lib, pack_bf16, pack_iq2x, pack_q2k, route,
                    route_workspace_bytes, set_timing_events, strerror, topk, version,
                    workspace_bytes)
 
@@ -37,6 +37,6 @@ def layer_from_canonical(H, I, E, k, router_bits, gate, up, down, grid, shared=N
 
 
 __all__ = ["BF16", "BitMoEError", "DECODE", "F32", "Layer", "PREFILL", "SYMBOLS", "bucket",
-           "dequant_iq2x", "dequant_q2k", "ffn_decode", "ffn_prefill", "layer_from_canonical", "lib",
+           "dequant_iq2x", "dequant_q2k", "ffn_decode", "ffn_prefill", "forward_decode", "layer_from_canonical", "lib",
            "pack_bf16", "pack_iq2x", "pack_q2k", "route", "route_workspace_bytes", "set_timing_events", "strerror", "topk",
            "version", "workspace_bytes"]

@@ -21,7 +21,7 @@ EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = -1, -2, -3, -4
 # every symbol declared in include/bitmoe.h
 SYMBOLS = [
     "moe_route_workspace_bytes", "moe_route", "moe_topk", "moe_bucket_workspace_bytes",
-    "moe_bucket", "moe_workspace_bytes", "moe_ffn_decode", "moe_ffn_prefill",
+    "moe_bucket", "moe_workspace_bytes", "moe_ffn_decode", "moe_forward_decode", "moe_ffn_prefill",
     "moe_dequant_iq2x", "moe_dequant_q2k", "moe_pack_iq2x", "moe_pack_q2k", "moe_pack_bf16",
     "moe_set_timing_events", "moe_strerror", "moe_version",
 ]
@@ -62,6 +62,7 @@ def lib() -> C.CDLL:
         "moe_workspace_bytes": ([LP, I, I], SZ),
         "moe_ffn_decode": ([LP, P, I, I, P, P, P, P, SZ, P], I),
         "moe_ffn_prefill": ([LP, P, I, I, P, P, P, P, SZ, P], I),
+        "moe_forward_decode": ([LP, P, I, I, P, P, P, P, SZ, P], I),
         "moe_dequant_iq2x": ([P, P, I64, P, I, P], I),
         "moe_dequant_q2k": ([P, I64, P, I, P], I),
         "moe_pack_iq2x": ([P, P, I, I, I, P], I),
@@ -229,6 +230,25 @@ def _ffn(fn, name, mode, layer: Layer, x, ids, w, y=None, ws=None, stream=None):
 
 def ffn_decode(layer, x, ids, w, y=None, ws=None, stream=None):
     return _ffn(lib().moe_ffn_decode, "moe_ffn_decode", DECODE, layer, x, ids, w, y, ws, stream)
+
+
+def forward_decode(layer, x, ids=None, w=None, y=None, ws=None, stream=None):
+    """Routing + decode FFN in one call. Returns (y, ids, w)."""
+    torch = _torch()
+    T = x.shape[0]
+    dev = x.device
+    if ids is None:
+        ids = torch.empty((T, layer.k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, layer.k), dtype=torch.float32, device=dev)
+    if y is None:
+        y = torch.empty((T, layer.H), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(workspace_bytes(layer, T, DECODE), dev)
+    _dev_check(x, ids, w, y, ws)
+    _check(lib().moe_forward_decode(layer.ref, _ptr(x), _x_dtype(x), T, _ptr(ids), _ptr(w), _ptr(y),
+                                    _ptr(ws), ws.numel(), _stream(stream)), "moe_forward_decode")
+    return y, ids, w
 
 
 def ffn_prefill(layer, x, ids, w, y=None, ws=None, stream=None):

@@ -15,6 +15,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kMaxT = 1 << 20;           // tokens per call
 constexpr int kMfmaRouterMinT = 64;      // bf16 activations: MFMA router from here on
+constexpr int kFusedRouterMaxT = 16;     // decode: router rows fused into the first launch
 
 inline size_t up256(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
@@ -56,8 +57,11 @@ struct Carve {
 struct FfnWs {
     bm_host::Buckets b{};
     int max_tiles = 0;
-    float *h = nullptr, *hsum = nullptr, *o = nullptr, *hs = nullptr, *os = nullptr;
+    // prefill
+    float *o = nullptr, *hs = nullptr, *os = nullptr;
     uint16_t *hb = nullptr;
+    // decode
+    bm_host::DecodeBufs d{};
     size_t bytes = 0;
 };
 
@@ -79,15 +83,25 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
         f.b.n_tiles = c.take<int32_t>(1);
         f.hb = c.take<uint16_t>(n * L->I);
         f.o = c.take<float>(n * L->H);
+        if (shared) {
+            f.hs = c.take<float>((int64_t)T * L->I);
+            f.os = c.take<float>((int64_t)T * L->H);
+        }
     } else {
         f.b.tile_rows = 1;
-        f.h = c.take<float>(n * L->I);
-        f.hsum = c.take<float>(n * (L->I / 16));
-        f.o = c.take<float>(n * L->H);
-    }
-    if (shared) {
-        f.hs = c.take<float>((int64_t)T * L->I);
-        f.os = c.take<float>((int64_t)T * L->H);
+        const bm_host::DecodePlan p = bm_host::decode_plan(L, T, false);
+        bm_host::DecodeBufs &d = f.d;
+        d.logits = c.take<float>((int64_t)T * L->E);
+        d.h = c.take<uint16_t>(2 * n * L->I);
+        d.hsum = c.take<float>(n * (L->I / 16));
+        d.o = c.take<float>(n * L->H);
+        d.tab = c.take<uint4>(4096 + 4);
+        if (shared) {
+            d.sgp = c.take<float>((int64_t)p.kc_sg * 2 * T * L->I);
+            d.hs = c.take<uint16_t>(2 * (int64_t)T * L->I);
+            d.osp = c.take<float>((int64_t)p.kc_sd * T * L->H);
+        }
+        d.bk = f.b;
     }
     f.bytes = c.off;
     return f;
@@ -174,7 +188,7 @@ int moe_route(const bitmoe_layer *L, const void *x, int x_dtype, int T, float *l
     if (T >= kMfmaRouterMinT && x_dtype == BITMOE_BF16) {
         float *lg = logits ? logits : part;
         if ((rc = bm_host::launch_router_mfma(L, x, T, lg, s))) return rc;
-        return bm_host::launch_topk(lg, 1, T, L->E, L->k, nullptr, ids, w, s);
+        return bm_host::launch_topk(lg, T, L->E, L->k, ids, w, s);
     }
     // one wave per expert row, token batches of router_tokens_per_launch()
     const int NT = bm_host::router_tokens_per_launch();
@@ -184,7 +198,7 @@ int moe_route(const bitmoe_layer *L, const void *x, int x_dtype, int T, float *l
         const char *xb = static_cast<const char *>(x) + (size_t)t0 * L->H * xs;
         float *lg = logits ? logits + (size_t)t0 * L->E : part;
         if ((rc = bm_host::launch_router_gemv(L, xb, x_dtype, nt, lg, s))) return rc;
-        if ((rc = bm_host::launch_topk(lg, 1, nt, L->E, L->k, nullptr, ids + (size_t)t0 * L->k,
+        if ((rc = bm_host::launch_topk(lg, nt, L->E, L->k, ids + (size_t)t0 * L->k,
                                        w + (size_t)t0 * L->k, s)))
             return rc;
     }
@@ -197,7 +211,7 @@ int moe_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w, v
     if (T > kMaxT) return BITMOE_EUNSUPPORTED;
     if (T == 0) return BITMOE_OK;
     if (!logits || !ids || !w) return BITMOE_EINVAL;
-    return bm_host::launch_topk(logits, 1, T, E, k, nullptr, ids, w, as_stream(stream));
+    return bm_host::launch_topk(logits, T, E, k, ids, w, as_stream(stream));
 }
 
 size_t moe_bucket_workspace_bytes(int T, int k, int E) {
@@ -232,9 +246,32 @@ int moe_ffn_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, con
     FfnWs f;
     int rc = ffn_common(L, x, x_dtype, T, ids, w, y, ws, ws_bytes, BITMOE_DECODE, &f);
     if (rc || T == 0) return rc;
+    bm_host::DecodeBufs b = f.d;
+    b.ids = const_cast<int32_t *>(ids);
+    b.w = const_cast<float *>(w);
+    b.y = y;
+    return bm_host::launch_decode(L, x, x_dtype, T, bm_host::decode_plan(L, T, false), b,
+                                  as_stream(stream));
+}
+
+int moe_forward_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, int32_t *ids,
+                       float *w, float *y, void *ws, size_t ws_bytes, void *stream) {
+    if (L && !L->router_w) return BITMOE_EINVAL;
+    FfnWs f;
+    int rc = ffn_common(L, x, x_dtype, T, ids, w, y, ws, ws_bytes, BITMOE_DECODE, &f);
+    if (rc || T == 0) return rc;
     hipStream_t s = as_stream(stream);
-    if ((rc = bm_host::launch_bucket(ids, T, L->k, L->E, f.b, s))) return rc;
-    return bm_host::launch_decode_ffn(L, x, x_dtype, T, ids, w, y, f.b, f.h, f.hsum, f.o, f.hs, f.os, s);
+    bm_host::DecodeBufs b = f.d;
+    b.ids = ids;
+    b.w = w;
+    b.y = y;
+    const bool fused = T <= kFusedRouterMaxT;
+    if (!fused) {
+        // the decode workspace's logits area is large enough for the router
+        rc = moe_route(L, x, x_dtype, T, nullptr, ids, w, b.logits, up256((size_t)T * L->E * 4), stream);
+        if (rc) return rc;
+    }
+    return bm_host::launch_decode(L, x, x_dtype, T, bm_host::decode_plan(L, T, fused), b, s);
 }
 
 int moe_ffn_prefill(const bitmoe_layer *L, const void *x, int x_dtype, int T, const int32_t *ids,

@@ -8,112 +8,11 @@
 // rank is the popcount of the lower lanes in that match set.  Per-wave counts
 // go to LDS so each lane also knows how many earlier waves (and, through the
 // histogram pass, earlier blocks) hit its expert.
-#include "common.h"
+#include "device_util.h"
 
 namespace {
 
 using namespace bm;
-
-constexpr int kBT = 1024;           // threads per bucketing block = pairs per chunk
-constexpr int kBW = kBT / 64;       // waves per block
-
-BM_DEV int key_bits(int E) {        // bits needed for keys 0..E (E = "no pair")
-    int b = 1;
-    while ((1 << b) <= E) b++;
-    return b;
-}
-
-// Exclusive scan over the block; returns the prefix of v, sets *total.
-BM_DEV int block_exscan(int v, int *swave, int *total) {
-    int lane = lane_id(), w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) swave[w] = x;
-    __syncthreads();
-    if (w == 0) {
-        int s = lane < nw ? swave[lane] : 0, c = s;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            int y = __shfl_up(c, o, 64);
-            if (lane >= o) c += y;
-        }
-        if (lane < nw) swave[lane] = c - s;
-        if (lane == nw - 1) swave[kBW] = c;
-    }
-    __syncthreads();
-    int r = x - v + swave[w];
-    *total = swave[kBW];
-    __syncthreads();
-    return r;
-}
-
-// Match set and rank of this lane's key among the lanes of its wave.
-BM_DEV void wave_match(int key, int kbits, uint64_t &match, int &rank) {
-    uint64_t m = __ballot(1);
-    for (int b = 0; b < kbits; b++) {
-        int bit = (key >> b) & 1;
-        uint64_t bb = __ballot(bit);
-        m &= bit ? bb : ~bb;
-    }
-    uint64_t lt = (1ull << lane_id()) - 1ull;
-    match = m;
-    rank = __popcll(m & lt);
-}
-
-// Stable scatter of one chunk of kBT pairs starting at p0.  base[e] holds the
-// first perm slot of expert e for this chunk; wcnt is [kBW][E] LDS, zeroed.
-BM_DEV void scatter_chunk(const int32_t *__restrict__ ids, int n, int E, int p0, const int *base,
-                          int *wcnt, int32_t *__restrict__ perm, int kbits) {
-    int tid = threadIdx.x, w = tid >> 6;
-    int p = p0 + tid;
-    int key = p < n ? ids[p] : E;
-    uint64_t match;
-    int rank;
-    wave_match(key, kbits, match, rank);
-    if (key < E && rank == 0) wcnt[w * E + key] = __popcll(match);
-    __syncthreads();
-    if (key < E) {
-        int pos = base[key] + rank;
-        for (int v = 0; v < w; v++) pos += wcnt[v * E + key];
-        perm[pos] = p;
-    }
-}
-
-// Active list (ascending experts with pairs) and the row-tile list.
-BM_DEV void active_and_tiles(const int *scount, int E, int32_t *__restrict__ active,
-                             int32_t *__restrict__ n_active, int32_t *__restrict__ tiles,
-                             int32_t *__restrict__ n_tiles, int tile_rows, int *swave) {
-    int tid = threadIdx.x;
-    for (int e0 = 0, abase = 0, tbase = 0; e0 < E; e0 += kBT) {
-        int e = e0 + tid;
-        int c = e < E ? scount[e] : 0;
-        int tot;
-        int a = block_exscan(c > 0 ? 1 : 0, swave, &tot);
-        if (e < E) {
-            active[e] = -1;
-        }
-        __syncthreads();
-        if (e < E && c > 0) active[abase + a] = e;
-        abase += tot;
-        if (tiles) {
-            int nt = (c + tile_rows - 1) / tile_rows, ttot;
-            int t0 = block_exscan(nt, swave, &ttot);
-            for (int i = 0; i < nt; i++) {
-                tiles[2 * (tbase + t0 + i)] = e;
-                tiles[2 * (tbase + t0 + i) + 1] = i * tile_rows;
-            }
-            tbase += ttot;
-        }
-        if (e0 + kBT >= E && tid == 0) {
-            *n_active = abase;
-            if (n_tiles) *n_tiles = tbase;
-        }
-    }
-}
 
 // ---- single-block path (small T*k) -----------------------------------------
 __global__ void __launch_bounds__(kBT)
@@ -122,43 +21,9 @@ k_bucket_small(const int32_t *__restrict__ ids, int n, int E, int32_t *__restric
                int32_t *__restrict__ active, int32_t *__restrict__ n_active,
                int32_t *__restrict__ tiles, int32_t *__restrict__ n_tiles, int tile_rows) {
     extern __shared__ int smem[];
-    int *scount = smem;               // [E]
-    int *sbase = scount + E;          // [E]
-    int *wcnt = sbase + E;            // [kBW][E]
     __shared__ int swave[kBW + 1];
-    int tid = threadIdx.x;
-    for (int e = tid; e < E; e += kBT) scount[e] = 0;
-    for (int i = tid; i < kBW * E; i += kBT) wcnt[i] = 0;
-    __syncthreads();
-    for (int p = tid; p < n; p += kBT) atomicAdd(&scount[ids[p]], 1);
-    __syncthreads();
-    // offsets = exclusive scan of counts (E <= 1024 = kBT)
-    {
-        int c = tid < E ? scount[tid] : 0, tot;
-        int o = block_exscan(c, swave, &tot);
-        if (tid < E) {
-            counts[tid] = c;
-            offsets[tid] = o;
-            sbase[tid] = o;
-        }
-        if (tid == 0) offsets[E] = tot;
-    }
-    __syncthreads();
-    active_and_tiles(scount, E, active, n_active, tiles, n_tiles, tile_rows, swave);
-    int kbits = key_bits(E);
-    for (int p0 = 0; p0 < n; p0 += kBT) {
-        scatter_chunk(ids, n, E, p0, sbase, wcnt, perm, kbits);
-        __syncthreads();
-        for (int e = tid; e < E; e += kBT) {
-            int s = 0;
-            for (int v = 0; v < kBW; v++) {
-                s += wcnt[v * E + e];
-                wcnt[v * E + e] = 0;
-            }
-            sbase[e] += s;
-        }
-        __syncthreads();
-    }
+    bucket_block(ids, n, E, counts, offsets, perm, active, n_active, tiles, n_tiles, tile_rows, smem,
+                 swave);
 }
 
 // ---- multi-block path -------------------------------------------------------

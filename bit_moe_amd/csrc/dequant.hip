@@ -107,6 +107,21 @@ k_dequant_q2k(const uint8_t *__restrict__ blocks, int64_t nblocks, void *__restr
     }
 }
 
+// One canonical IQ2X group (4 index bytes, u32 signs/scale) -> the four
+// 16-bit fields of the tiled layout (see common.h), packed in two words.
+BM_DEV uint2 iq2x_group_fields(uint32_t idxw, uint32_t a) {
+    const uint32_t s = a >> 28;
+    uint32_t F[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint32_t s7 = (a >> (7 * j)) & 0x7Fu;
+        const uint32_t par = __popc(s7 & 15u) & 1u;
+        F[j] = (((idxw >> (8 * j)) & 0xFFu) << 8) | ((s7 & 7u) << 4) | (par << 7) |
+               (((s7 >> 4) & 7u) << 1) | ((s >> j) & 1u);
+    }
+    return make_uint2(F[0] | (F[1] << 16), F[2] | (F[3] << 16));
+}
+
 // canonical IQ2X -> tiled; one thread per block
 __global__ void __launch_bounds__(256)
 k_pack_iq2x(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int E, int N, int nb) {
@@ -121,11 +136,15 @@ k_pack_iq2x(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int E, i
     int64_t pk = (int64_t)P * nb + kb;
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-        uint32_t w[4];
+        uint2 f[2];
 #pragma unroll
-        for (int q = 0; q < 4; q++)
-            w[q] = (uint32_t)s[1 + 8 * c + 2 * q] | ((uint32_t)s[2 + 8 * c + 2 * q] << 16);
-        reinterpret_cast<uint4 *>(slab)[(pk * 4 + c) * 64 + r] = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int h = 0; h < 2; h++) {
+            const int g = 2 * c + h;                         // group; its 8 bytes at 2 + 8g
+            uint32_t idxw = (uint32_t)s[1 + 4 * g] | ((uint32_t)s[2 + 4 * g] << 16);
+            uint32_t a = (uint32_t)s[3 + 4 * g] | ((uint32_t)s[4 + 4 * g] << 16);
+            f[h] = iq2x_group_fields(idxw, a);
+        }
+        reinterpret_cast<uint4 *>(slab)[(pk * 4 + c) * 64 + r] = make_uint4(f[0].x, f[0].y, f[1].x, f[1].y);
     }
     reinterpret_cast<uint16_t *>(slab + 64 * per_e)[pk * 64 + r] = s[0];
 }

@@ -41,13 +41,13 @@ BM_DEV void iq2x_group_int_to_lds(const uint8_t *slab, int nb, int n, int kb, in
     const int P = n >> 6, r = n & 63;
     const int64_t pk = (int64_t)P * nb + kb;
     const uint2 gw = reinterpret_cast<const uint2 *>(slab)[((pk * 4 + (g >> 1)) * 64 + r) * 2 + (g & 1)];
-    const float s2 = (float)(2u * (gw.y >> 28) + 1u);
+    const float s2 = (float)(2u * iq2x_scale(gw.x, gw.y) + 1u);
     uint32_t out[16];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        uint32_t s7 = (gw.y >> (7 * j)) & 0x7Fu;
-        uint32_t sig = s7 | ((uint32_t)(__popc(s7) & 1) << 7);
-        uint2 row = sgrid[(gw.x >> (8 * j)) & 0xFFu];
+        const uint32_t F = ((j < 2 ? gw.x : gw.y) >> (16 * (j & 1))) & 0xFFFFu;
+        const uint32_t sig = iq2x_signs(F);
+        const uint2 row = sgrid[F >> 8];
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
             uint32_t m0 = ((i < 4 ? row.x : row.y) >> (8 * (i & 3))) & 0xFFu;

@@ -6,7 +6,7 @@
 // per token (page "Un modele de 284 milliards de parametres tourne desormais
 // sur un Mac de 128 Go. Qui y perd ?", section "Comment un modele de 284
 // milliards de parametres tient sur une seule machine").
-#include "common.h"
+#include "device_util.h"
 
 namespace {
 
@@ -20,49 +20,6 @@ constexpr int kRouterNT = 16;   // tokens per launch of the small-T router
 // per token.  Each logit is produced by exactly one wave, in a fixed order,
 // so results are reproducible run to run.
 // ---------------------------------------------------------------------------
-template <int XBF16, int NT>
-BM_DEV void router_row(const uint4 *__restrict__ wrow, const void *__restrict__ x, int H, int T,
-                       int E, int e, float *__restrict__ logits) {
-    const int lane = lane_id();
-    float acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; t++) acc[t] = 0.f;
-    const int steps = (H + 511) / 512;          // H is a multiple of 256
-#pragma unroll 2
-    for (int s = 0; s < steps; s++) {
-        const int k = 512 * s + 8 * lane;
-        if (k >= H) break;                       // only in a half-width last step
-        const uint4 wv = wrow[64 * s + lane];
-#pragma unroll
-        for (int t = 0; t < NT; t++) {
-            const int tt = t < T ? t : 0;
-            if (XBF16) {
-                const uint4 xv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)tt * H + k);
-                float a = acc[t];
-                a = dot2_bf16(wv.x, xv.x, a);
-                a = dot2_bf16(wv.y, xv.y, a);
-                a = dot2_bf16(wv.z, xv.z, a);
-                a = dot2_bf16(wv.w, xv.w, a);
-                acc[t] = a;
-            } else {
-                const float4 *xp = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)tt * H + k);
-                const float4 x0 = xp[0], x1 = xp[1];
-                float a = acc[t];
-                a = fmaf(bf16_lo(wv.x), x0.x, a); a = fmaf(bf16_hi(wv.x), x0.y, a);
-                a = fmaf(bf16_lo(wv.y), x0.z, a); a = fmaf(bf16_hi(wv.y), x0.w, a);
-                a = fmaf(bf16_lo(wv.z), x1.x, a); a = fmaf(bf16_hi(wv.z), x1.y, a);
-                a = fmaf(bf16_lo(wv.w), x1.z, a); a = fmaf(bf16_hi(wv.w), x1.w, a);
-                acc[t] = a;
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
-        const float v = wave_sum(acc[t]);
-        if (lane == 0 && t < T) logits[(int64_t)t * E + e] = v;
-    }
-}
-
 template <int XBF16>
 __global__ void __launch_bounds__(256)
 k_router_gemv(const uint16_t *__restrict__ wr, const void *__restrict__ x, int T, int H, int E,
@@ -143,61 +100,14 @@ k_router_mfma(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, in
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave per token.  Sums the KS partial logits in split order,
-// selects k by repeated wave argmax (larger value, then lower index), and
-// writes w = softmax over the selected logits.
+// Top-k: one wave per token over the final logits.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
-k_topk(const float *__restrict__ part, int KS, int T, int E, int k, float *__restrict__ logits,
-       int32_t *__restrict__ ids, float *__restrict__ wout) {
-    int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    int lane = threadIdx.x & 63;
+k_topk(const float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ ids,
+       float *__restrict__ wout) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    constexpr int MAXV = 16;                 // E <= 1024
-    float v[MAXV];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < MAXV; i++) {
-        int e = lane + 64 * i;
-        float s = 0.f;
-        if (e < E) {
-            for (int ks = 0; ks < KS; ks++) s += part[((int64_t)ks * T + t) * E + e];
-            if (logits) logits[(int64_t)t * E + e] = s;
-        }
-        v[i] = s;
-    }
-    float sel[16];
-    int sid[16];
-    for (int j = 0; j < k; j++) {
-        float bv = 0.f;
-        int be = 0x7FFFFFFF;
-#pragma unroll
-        for (int i = 0; i < MAXV; i++) {
-            int e = lane + 64 * i;
-            bool ok = e < E && !((taken >> i) & 1u);
-            if (ok && (be == 0x7FFFFFFF || v[i] > bv)) { bv = v[i]; be = e; }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            float ov = __shfl_xor(bv, o, 64);
-            int oe = __shfl_xor(be, o, 64);
-            bool better = (oe != 0x7FFFFFFF) &&
-                          (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be));
-            if (better) { bv = ov; be = oe; }
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        sel[j] = bv;
-        sid[j] = be;
-    }
-    if (lane == 0) {
-        float z = 0.f, ex[16];
-        for (int j = 0; j < k; j++) { ex[j] = __expf(sel[j] - sel[0]); z += ex[j]; }
-        float inv = 1.0f / z;
-        for (int j = 0; j < k; j++) {
-            ids[(int64_t)t * k + j] = sid[j];
-            wout[(int64_t)t * k + j] = ex[j] * inv;
-        }
-    }
+    topk_wave(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, wout + (int64_t)t * k);
 }
 
 }  // namespace
@@ -225,9 +135,8 @@ int launch_router_mfma(const bitmoe_layer *L, const void *x, int T, float *logit
     return BITMOE_OK;
 }
 
-int launch_topk(const float *part, int KS, int T, int E, int k, float *logits, int32_t *ids,
-                float *w, hipStream_t s) {
-    k_topk<<<(T + 3) / 4, 256, 0, s>>>(part, KS, T, E, k, logits, ids, w);
+int launch_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w, hipStream_t s) {
+    k_topk<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, ids, w);
     BM_LAUNCH_CHECK();
     return BITMOE_OK;
 }

@@ -51,13 +51,20 @@
  *   n*(K/256) + kb; experts are stacked on a leading axis [E].
  *
  *  TILED layout (what the FFN entry points read; moe_pack_* produces it).
- *   Same bytes, regrouped into 64-row panels so that 64 lanes reading one
- *   16-byte piece of 64 consecutive rows issue one contiguous 1 KiB access.
+ *   The same information in the same number of bytes, regrouped into 64-row
+ *   panels so that 64 lanes reading one 16-byte piece of 64 consecutive rows
+ *   issue one contiguous 1 KiB access.
  *   Per expert the slab has exactly the canonical size, with nb = K/256,
  *   P = n/64, r = n%64:
  *   IQ2X slab (N*nb*66 bytes):
- *     [0, 64*N*nb):           qs piece c (bytes 2+16c..17+16c of block (n,kb))
- *                             at ((P*nb + kb)*4 + c)*64 + r, 16 bytes each
+ *     [0, 64*N*nb):           piece c (groups 2c, 2c+1 of block (n,kb)) at
+ *                             ((P*nb + kb)*4 + c)*64 + r, 16 bytes each; each
+ *                             group re-encoded (bijectively, same 8 bytes) as
+ *                             four little-endian 16-bit fields, one per run j
+ *                             of 8 weights: bit 0 bit j of the group scale s;
+ *                             bits 1-3 signs of weights 4,5,6; bits 4-6 signs
+ *                             of weights 0,1,2; bit 7 parity of the signs of
+ *                             weights 0..3; bits 8-15 the codebook index
  *     [64*N*nb, 66*N*nb):     d of block (n,kb) at (P*nb + kb)*64 + r, 2 bytes
  *   Q2K slab (N*nb*84 bytes):
  *     [0, 64*N*nb):           qs piece c (bytes 16+16c..31+16c) as above
@@ -159,6 +166,18 @@ int moe_ffn_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T,
 int moe_ffn_prefill(const bitmoe_layer *L, const void *x, int x_dtype, int T,
                     const int32_t *ids, const float *w, float *y, void *ws,
                     size_t ws_bytes, void *stream);
+
+/*
+ * The whole layer for a decode batch: moe_route followed by moe_ffn_decode
+ * in one call.  For T <= 16 the router rows, the shared expert and the
+ * bookkeeping share launches with the expert GEMVs (four launches in all).
+ * ids int32 [T][k] and w float32 [T][k] receive the routing (same values as
+ * moe_route); y float32 [T][H] as moe_ffn_decode.  Needs L->router_w.
+ * ws: at least moe_workspace_bytes(L, T, BITMOE_DECODE) bytes.
+ */
+int moe_forward_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T,
+                       int32_t *ids, float *w, float *y, void *ws,
+                       size_t ws_bytes, void *stream);
 
 /*
  * Standalone dequantisation of CANONICAL blocks: nblocks blocks ->

@@ -190,3 +190,23 @@ def test_end_to_end_route_then_ffn():
     np.testing.assert_array_equal(gid.cpu().numpy(), rid)
     ref = oracle.layer_ffn(L, x, rid, rw)
     assert_close_rms(y.cpu().numpy(), ref, what="route+decode")
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 20])
+def test_forward_decode_routes_and_matches_oracle(T):
+    """moe_forward_decode (router fused into the first launch for T <= 16,
+    separate routing above) against oracle routing + FFN."""
+    require_gpu()
+    import bit_moe_amd as bm
+    w0 = synth.WORKLOADS["decode_b1"]
+    w = w0.with_(T=T, name=f"fwd{T}")
+    L = synth_layer(w0)
+    x, _ = synth.make_tokens(w, accept=lambda t, r: oracle.margin_ok(r, L.router(), w.k, 1e-4))
+    lay = device_layer(w0)
+    y, gid, gw = bm.forward_decode(lay, x_to_device(x))
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(x, L.router(), w.k)
+    np.testing.assert_array_equal(gid.cpu().numpy(), rid)
+    np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=1e-5)
+    ref = oracle.layer_ffn(L, x, rid, gw.cpu().numpy().astype(np.float64))
+    assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode T={T}")
