@@ -115,10 +115,8 @@ def decode_b1(args, L, lays):
 
     ms = time_steps(step, args.warmup, args.steps)
     gu_ms = time_dominant(step, min(args.steps, 100))
-    # the timed launch streams the routed gate/up blocks and the shared down
-    routed = w.k * (2 * w.I * (w.H // 256) * 66)
-    shared_down = w.I * w.H * 2
-    gu_bytes = routed + shared_down
+    # the timed launch streams the routed gate/up blocks of the k experts
+    gu_bytes = w.k * (2 * w.I * (w.H // 256) * 66)
     step_bytes = w.k * (2 * w.I * (w.H // 256) * 66 + w.H * (w.I // 256) * 84) + 3 * w.I * w.H * 2 + w.E * w.H * 2
     return dict(ms=ms, gu_ms=gu_ms, gu_bytes=gu_bytes, step_bytes=step_bytes)
 

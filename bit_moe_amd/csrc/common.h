@@ -50,89 +50,129 @@ BM_DEV float wave_sum(float v) {
 
 BM_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// ---- tiled IQ2X group fields ---------------------------------------------
-// A tiled IQ2X group is four little-endian 16-bit fields F_j (run j of 8
-// weights): bits 8-15 the codebook index; bits 4-6 the signs of weights
-// 0,1,2 and bit 7 the parity of the signs of weights 0..3; bits 1-3 the
-// signs of weights 4,5,6; bit 0 bit j of the 4-bit group scale.  The sign
-// of weight 3 is bit7 ^ bits 4..6 and that of weight 7 (even parity over
-// the 8) is bit7 ^ bits 1..3.  It is a bijective re-encoding of the
-// canonical 8 bytes.
-//
-// Decode tables (LDS): a 64 KiB main table of 16-byte entries, one per
-// (index, F bits 4-7): the 8 magnitudes as bf16 with the signs of weights
-// 0..3 applied and weight 7 signed by the parity bit; and an 8-entry mask
-// table (F bits 1-3) that flips the signs of weights 4..7.
-constexpr int kIq2xMainEntries = 4096;            // uint4 entries
-constexpr int kIq2xMaskBytes = 64;                // after the main table
-BM_DEV uint32_t iq2x_main_off(uint32_t F) { return F & 0xFFF0u; }
-BM_DEV uint32_t iq2x_mask_off(uint32_t F) { return (F << 2) & 0x38u; }
-// 4-bit group scale from the two words W0 = F0 | F1 << 16, W1 = F2 | F3 << 16
-BM_DEV uint32_t iq2x_scale(uint32_t W0, uint32_t W1) {
-    return (W0 & 1u) | ((W0 >> 15) & 2u) | ((W1 & 1u) << 2) | ((W1 >> 13) & 8u);
+// ---- hand-over between workgroups of one launch -------------------------
+// Data read by other workgroups of the same launch is written with
+// device-scope (write-through) stores and read with device-scope loads; a
+// workgroup waits for its stores to complete before it signals them.
+BM_DEV void st_dev(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+BM_DEV void st_dev(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+BM_DEV float ld_dev(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+BM_DEV uint32_t ld_dev(const uint32_t *p) {
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+BM_DEV void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---- tiled IQ2X group words ----------------------------------------------
+// A tiled IQ2X group (32 weights, four runs of 8) is two little-endian
+// 32-bit words, W0 for runs 0,1 and W1 for runs 2,3.  Bits 0-1 of W0 are
+// bits 0-1 of the 4-bit group scale, bits 0-1 of W1 its bits 2-3.  The
+// first run of a word is the 15-bit field R at bits 2-16, the second at
+// bits 17-31; within R: bits 0-2 the signs of weights 0,1,2, bit 3 the
+// parity of the signs of weights 0..3, bits 4-11 the codebook index and
+// bits 12-14 the signs of weights 4,5,6.  The sign of weight 3 is
+// bit 3 ^ bits 0..2, that of weight 7 (even parity over the 8) is
+// bit 3 ^ bits 12..14.  It is a bijective re-encoding of the canonical
+// 8 bytes of the group.
+//
+// Decode tables (LDS, 2 x 4096 dwords): table 1 at index R & 0xFFF holds
+// weights 0..3 of the run, table 2 at index R >> 3 weights 4..7, each
+// weight as one byte: the low byte of bf16(24 + w), w = +-magnitude (the
+// high byte of every such bf16 is 0x41 for magnitudes 0..7).  The
+// byte offsets of both lookups are a shift and a mask of the word.
+constexpr int kIq2xTabDwords = 4096;              // per table
+constexpr int kIq2xBias = 24;
+constexpr uint32_t kIq2xHiBytes = 0x41414141u;
+BM_DEV uint32_t iq2x_run(uint32_t W, int second) { return second ? W >> 17 : (W >> 2) & 0x7FFFu; }
+BM_DEV uint32_t iq2x_scale(uint32_t W0, uint32_t W1) { return (W0 & 3u) | ((W1 & 3u) << 2); }
+BM_DEV uint32_t iq2x_run_idx(uint32_t R) { return (R >> 4) & 0xFFu; }
 // signs of the 8 weights of a run (bit i = weight i negative)
-BM_DEV uint32_t iq2x_signs(uint32_t F) {
-    const uint32_t lo3 = (F >> 4) & 7u, hi3 = (F >> 1) & 7u, p = (F >> 7) & 1u;
+BM_DEV uint32_t iq2x_run_signs(uint32_t R) {
+    const uint32_t lo3 = R & 7u, hi3 = (R >> 12) & 7u, p = (R >> 3) & 1u;
     const uint32_t s3 = p ^ (__popc(lo3) & 1u), s7 = p ^ (__popc(hi3) & 1u);
     return lo3 | (s3 << 3) | (hi3 << 4) | (s7 << 7);
 }
-// main table entry e: index e >> 4, F bits 4-7 = e & 15
-BM_DEV uint4 iq2x_main_entry(const uint8_t *__restrict__ grid, int e) {
-    const int idx = e >> 4;
-    const uint32_t q = e & 15, p = q >> 3;
-    const uint32_t lo3 = q & 7u;
-    const uint32_t signs = lo3 | ((p ^ (__popc(lo3) & 1u)) << 3) | (p << 7);
-    const uint2 m8 = *reinterpret_cast<const uint2 *>(grid + 8 * idx);
-    uint32_t v[8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const uint32_t m = ((i < 4 ? m8.x : m8.y) >> (8 * (i & 3))) & 0xFFu;
-        v[i] = (__float_as_uint((float)m) >> 16) | (((signs >> i) & 1u) << 15);   // exact
+// byte offsets into the tables of the two runs of word W
+BM_DEV uint32_t iq2x_off1(uint32_t W, int second) { return second ? (W >> 15) & 0x3FFCu : W & 0x3FFCu; }
+BM_DEV uint32_t iq2x_off2(uint32_t W, int second) {
+    return 4u * kIq2xTabDwords + (second ? (W >> 18) & 0x3FFCu : (W >> 3) & 0x3FFCu);
+}
+// low byte of bf16(24 + (neg ? -m : m)), m in 0..7: 24 +- m lies in [16, 32)
+BM_DEV uint32_t iq2x_biased_byte(uint32_t m, uint32_t neg) {
+    const uint32_t v = neg ? 8u - m : 8u + m;      // (24 +- m) - 16, in 1..15
+    return 0x80u | (v << 3);
+}
+// table entry i of table `which` (0: weights 0..3, 1: weights 4..7)
+BM_DEV uint32_t iq2x_tab_entry(const uint8_t *__restrict__ grid, int which, uint32_t i) {
+    uint32_t idx, sg;
+    if (which == 0) {             // i = idx << 4 | parity03 << 3 | signs 0..2
+        idx = i >> 4;
+        const uint32_t lo3 = i & 7u, p = (i >> 3) & 1u;
+        sg = lo3 | ((p ^ (__popc(lo3) & 1u)) << 3);
+    } else {                      // i = signs 4..6 << 9 | idx << 1 | parity03
+        idx = (i >> 1) & 0xFFu;
+        const uint32_t hi3 = (i >> 9) & 7u, p = i & 1u;
+        sg = hi3 | ((p ^ (__popc(hi3) & 1u)) << 3);
     }
-    return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+    const uint32_t m4 = *reinterpret_cast<const uint32_t *>(grid + 8 * idx + 4 * which);
+    uint32_t e = 0;
+#pragma unroll
+    for (int b = 0; b < 4; b++) e |= iq2x_biased_byte((m4 >> (8 * b)) & 0xFFu, (sg >> b) & 1u) << (8 * b);
+    return e;
 }
-// mask table entry m (F bits 1-3): sign flips of weights 4,5 / 6,7
-BM_DEV uint2 iq2x_mask_entry(int m) {
-    const uint32_t b4 = m & 1, b5 = (m >> 1) & 1, b6 = (m >> 2) & 1;
-    return make_uint2((b4 << 15) | (b5 << 31), (b6 << 15) | ((b4 ^ b5 ^ b6) << 31));
-}
+// the two bf16 pairs (24 + w0, 24 + w1), (24 + w2, 24 + w3) of a table entry
+BM_DEV uint32_t iq2x_pair_lo(uint32_t e) { return __builtin_amdgcn_perm(kIq2xHiBytes, e, 0x04010400u); }
+BM_DEV uint32_t iq2x_pair_hi(uint32_t e) { return __builtin_amdgcn_perm(kIq2xHiBytes, e, 0x04030402u); }
 
 // ---- small-T router row: one wave per expert row, lanes across K ---------
+// The row is read in chunks (up to 8 loads of 16 bytes per lane, all in
+// flight together), so one row costs about one memory round trip per chunk.
+template <int XBF16, int NT>
+BM_DEV float router_dot8(uint4 wv, const void *__restrict__ x, int H, int tt, int k, float a) {
+    if (XBF16) {
+        const uint4 xv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)tt * H + k);
+        a = dot2_bf16(wv.x, xv.x, a);
+        a = dot2_bf16(wv.y, xv.y, a);
+        a = dot2_bf16(wv.z, xv.z, a);
+        a = dot2_bf16(wv.w, xv.w, a);
+    } else {
+        const float4 *xp = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)tt * H + k);
+        const float4 x0 = xp[0], x1 = xp[1];
+        a = fmaf(bf16_lo(wv.x), x0.x, a); a = fmaf(bf16_hi(wv.x), x0.y, a);
+        a = fmaf(bf16_lo(wv.y), x0.z, a); a = fmaf(bf16_hi(wv.y), x0.w, a);
+        a = fmaf(bf16_lo(wv.z), x1.x, a); a = fmaf(bf16_hi(wv.z), x1.y, a);
+        a = fmaf(bf16_lo(wv.w), x1.z, a); a = fmaf(bf16_hi(wv.w), x1.w, a);
+    }
+    return a;
+}
+
 template <int XBF16, int NT>
 BM_DEV void router_row(const uint4 *__restrict__ wrow, const void *__restrict__ x, int H, int T,
                        int E, int e, float *__restrict__ logits) {
+    constexpr int CH = NT == 1 ? 8 : NT <= 4 ? 4 : 2;
     const int lane = lane_id();
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] = 0.f;
     const int steps = (H + 511) / 512;          // H is a multiple of 256
-#pragma unroll 2
-    for (int s = 0; s < steps; s++) {
-        const int k = 512 * s + 8 * lane;
-        if (k >= H) break;                       // only in a half-width last step
-        const uint4 wv = wrow[64 * s + lane];
+    for (int s0 = 0; s0 < steps; s0 += CH) {
+        uint4 wv[CH];
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
-            const int tt = t < T ? t : 0;
-            if (XBF16) {
-                const uint4 xv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)tt * H + k);
-                float a = acc[t];
-                a = dot2_bf16(wv.x, xv.x, a);
-                a = dot2_bf16(wv.y, xv.y, a);
-                a = dot2_bf16(wv.z, xv.z, a);
-                a = dot2_bf16(wv.w, xv.w, a);
-                acc[t] = a;
-            } else {
-                const float4 *xp = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)tt * H + k);
-                const float4 x0 = xp[0], x1 = xp[1];
-                float a = acc[t];
-                a = fmaf(bf16_lo(wv.x), x0.x, a); a = fmaf(bf16_hi(wv.x), x0.y, a);
-                a = fmaf(bf16_lo(wv.y), x0.z, a); a = fmaf(bf16_hi(wv.y), x0.w, a);
-                a = fmaf(bf16_lo(wv.z), x1.x, a); a = fmaf(bf16_hi(wv.z), x1.y, a);
-                a = fmaf(bf16_lo(wv.w), x1.z, a); a = fmaf(bf16_hi(wv.w), x1.w, a);
-                acc[t] = a;
-            }
+        for (int i = 0; i < CH; i++) {
+            // steps past the row, and the idle half-wave of a half-width
+            // last step, re-read the row's first piece and are not used
+            const int s = s0 + i, k = 512 * s + 8 * lane;
+            wv[i] = wrow[(s < steps && k < H) ? 64 * s + lane : lane];
+        }
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            const int s = s0 + i, k = 512 * s + 8 * lane;
+            if (s >= steps || k >= H) continue;
+#pragma unroll
+            for (int t = 0; t < NT; t++) acc[t] = router_dot8<XBF16, NT>(wv[i], x, H, t < T ? t : 0, k, acc[t]);
         }
     }
 #pragma unroll
@@ -179,13 +219,14 @@ struct Buckets {
 size_t bucket_scratch_bytes(int T, int k, int E);
 int launch_bucket(const int32_t *ids, int T, int k, int E, const Buckets &b, hipStream_t s);
 
-// decode FFN (four launches, see decode.hip)
+// decode FFN (three launches for decode batches, see decode.hip)
 struct DecodePlan {
     int slots = 0;          // workgroup rows reserved for active experts
     int n_rwg = 0;          // router workgroups in the front launch (0: ids given)
     int kc_sg = 0;          // K chunks of the shared gate/up
     int kc_sd = 0;          // K chunks of the shared down
-    bool bucket_in_mid = true;
+    bool small = false;     // T*k <= 128: routing / bucketing inside the gate/up workgroups
+    bool need_mid = true;   // top-k and/or bucketing in a launch of their own
 };
 struct DecodeBufs {
     float *logits;          // [T][E] (router in the front launch)
@@ -193,12 +234,13 @@ struct DecodeBufs {
     float *w;               // [T][k]
     Buckets bk;
     float *sgp;             // [kc_sg][2][T][I] shared gate/up partial sums
-    uint16_t *hs;           // [2][T][I] shared h as bf16 hi, lo
     uint16_t *h;            // [2][T*k][I] routed h as bf16 hi, lo (bucket order, quads [0,2,1,3])
     float *hsum;            // [T*k][I/16]
     float *o;               // [T*k][H] routed down outputs, pair order
     float *osp;             // [kc_sd][T][H] shared down partial sums
-    uint4 *tab;             // IQ2X decode tables (64 KiB + 64 B)
+    int32_t *ycount;        // [H/64] finished down workgroups per panel
+    uint4 *tab;             // IQ2X decode tables (2 x 16 KiB)
+    float *xs;              // [T][H/32] activation sums over groups of 32
     float *y;               // [T][H]
 };
 DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router);

@@ -9,17 +9,17 @@
 // veritable goulot d'etranglement"): each active expert's blocks are read
 // from HBM once per call and decoded in registers.
 //
-// Launches, each balanced so that every wave streams a similar number of
-// bytes:
-//   front  : codebook table, router rows (optional) || shared-expert
-//            gate/up, split over K
-//   mid    : top-k (optional) and bucketing (one workgroup)
+// Launches (T <= 128/k: three; larger batches add a routing/bucketing
+// launch, experts chosen by several tokens a second gate/up and down):
+//   front  : decode tables, activation sums, router rows; the workgroup
+//            that finds every router workgroup done tops-k and buckets the
+//            batch (or buckets the given ids); clears the combine counters
+//            || shared-expert gate/up partial sums per (panel, K chunk)
 //   gateup : routed gate/up + SwiGLU per (active expert, 64-row panel)
-//            || shared h = silu(sum of gate partials) * (sum of up partials)
-//            (experts chosen by several tokens: a second launch)
-//   down   : routed down per (active expert, 64-row panel) || shared down,
-//            split over K
-//   combine: y = sum of the k weighted slots + shared partials, in a fixed
+//   down   : routed down per (active expert, 64-row panel) || shared down
+//            per (panel, K chunk), its h built from the gate/up partials;
+//            the last workgroup to finish a panel combines it,
+//            y = sum of the k weighted slots + shared partials, in a fixed
 //            order, so results are reproducible run to run.
 //
 // Mapping: lane r of every wave owns row P*64 + r of a panel (tiled layout),
@@ -37,8 +37,15 @@ using namespace bm;
 constexpr int kW = 8;              // waves per workgroup
 constexpr int kWG = 16;            // waves per routed gate/up workgroup
 constexpr int kNT = 4;             // tokens per pass over the weights
-constexpr int kTabU4 = kIq2xMainEntries + kIq2xMaskBytes / 16;   // decode tables, uint4 units
-constexpr int kTabWG = (kTabU4 + kW * 64 - 1) / (kW * 64);      // front workgroups that build them
+constexpr int kMaxChunks = 8;      // K chunks of the shared expert, at most
+constexpr int kMaxExperts = 1024;
+constexpr int kSharedChunkCols = 512;   // I columns of one shared-down K chunk, at most
+constexpr int kTabDw = 2 * kIq2xTabDwords;                     // decode tables, dwords (32 KiB)
+constexpr int kTabWG = kTabDw / (kW * 64);                       // front workgroups that build them
+// 16-byte pieces per load batch of a gate/up wave (fewer when several
+// tokens share the pass, to bound register use)
+template <int NT>
+constexpr int pieces_per_batch() { return NT == 1 ? 2 : 1; }
 
 // ---- per-token dot products --------------------------------------------------
 
@@ -68,41 +75,66 @@ BM_DEV const void *xrow(const void *x, int t, int H, int k) {
                  : (const void *)(static_cast<const float *>(x) + (int64_t)t * H + k);
 }
 
-// One IQ2X superblock of this lane's row: four 16-byte pieces (8 groups of
-// four 16-bit fields) and the fp16 d; dotted with NT activation rows.
-// Per run of 8 weights: one 16-byte main-table read (weights 0..7, signs of
-// 0..3 and the parity sign of 7 applied) and one read of the 64-byte mask
-// table (all lanes hit 8 addresses: broadcast, no bank conflicts).
+// One group's activations (32 values per token) and their sums, held in
+// scalar registers when the activations are bf16.
 template <int XBF16, int NT>
-BM_DEV void iq2x_superblock(const uint4 (&q)[4], float d, const char *tab, const void *x,
-                            const int (&tok)[NT], int H, int k0, float (&acc)[NT]) {
+struct XGroup {
+    uint4 v[XBF16 ? NT : 1][4];
+    float s[NT];
+};
+
+template <int XBF16, int NT>
+BM_DEV void load_xgroup(XGroup<XBF16, NT> &g, const void *__restrict__ x, const float *__restrict__ xs,
+                        const int (&tok)[NT], int H, int gg) {
+    const int G = H / 32;
 #pragma unroll
-    for (int g = 0; g < 8; g++) {
-        const uint32_t W0 = (g & 1) ? q[g >> 1].z : q[g >> 1].x;
-        const uint32_t W1 = (g & 1) ? q[g >> 1].w : q[g >> 1].y;
-        const float scale = d * fmaf((float)iq2x_scale(W0, W1), 0.25f, 0.125f);   // d*(0.5+s)/4
-        uint4 v[4];
-        uint2 m[4];
+    for (int t = 0; t < NT; t++) {
+        g.s[t] = xs[(int64_t)tok[t] * G + gg];
+        if (XBF16) {
+            const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)tok[t] * H + 32 * gg);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint32_t F = ((j < 2 ? W0 : W1) >> (16 * (j & 1))) & 0xFFFFu;
-            v[j] = *reinterpret_cast<const uint4 *>(tab + iq2x_main_off(F));
-            m[j] = *reinterpret_cast<const uint2 *>(tab + 16 * kIq2xMainEntries + iq2x_mask_off(F));
+            for (int q = 0; q < 4; q++) g.v[t][q] = p[q];
         }
-        float part[NT];
-#pragma unroll
-        for (int t = 0; t < NT; t++) part[t] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const uint2 lo = make_uint2(v[j].x, v[j].y);
-            const uint2 hi = make_uint2(v[j].z ^ m[j].x, v[j].w ^ m[j].y);
-#pragma unroll
-            for (int t = 0; t < NT; t++)
-                part[t] = dot8<XBF16>(lo, hi, xrow<XBF16>(x, tok[t], H, k0 + 32 * g + 8 * j), part[t]);
-        }
-#pragma unroll
-        for (int t = 0; t < NT; t++) acc[t] = fmaf(scale, part[t], acc[t]);
     }
+}
+
+// One IQ2X group (32 weights, words W0, W1) of this lane's row dotted with
+// NT activation rows.  Each run of 8 weights is two 4-byte table reads and
+// four byte permutes giving bf16 pairs of 24 + w; the bias is removed per
+// group with the activation sums (24 * sum of the group's activations).
+template <int XBF16, int NT>
+BM_DEV void iq2x_group(uint32_t W0, uint32_t W1, float dq8, const char *tab, const XGroup<XBF16, NT> &xg,
+                       const void *x, const int (&tok)[NT], int H, int gg, float (&acc)[NT]) {
+    const float scale = dq8 * (float)(2u * iq2x_scale(W0, W1) + 1u);   // d*(0.5+s)/4
+    uint32_t e1[4], e2[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const uint32_t W = r < 2 ? W0 : W1;
+        e1[r] = *reinterpret_cast<const uint32_t *>(tab + iq2x_off1(W, r & 1));
+        e2[r] = *reinterpret_cast<const uint32_t *>(tab + iq2x_off2(W, r & 1));
+    }
+    float part[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) part[t] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const uint2 lo = make_uint2(iq2x_pair_lo(e1[r]), iq2x_pair_hi(e1[r]));
+        const uint2 hi = make_uint2(iq2x_pair_lo(e2[r]), iq2x_pair_hi(e2[r]));
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            if (XBF16) {
+                const uint4 xv = xg.v[t][r];
+                part[t] = dot2_bf16(lo.x, xv.x, part[t]);
+                part[t] = dot2_bf16(lo.y, xv.y, part[t]);
+                part[t] = dot2_bf16(hi.x, xv.z, part[t]);
+                part[t] = dot2_bf16(hi.y, xv.w, part[t]);
+            } else {
+                part[t] = dot8<0>(lo, hi, xrow<0>(x, tok[t], H, 32 * gg + 8 * r), part[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = fmaf(scale, fmaf(-(float)kIq2xBias, xg.s[t], part[t]), acc[t]);
 }
 
 // Even split of [0, n) over `parts`; returns [lo, hi) of part `i`.
@@ -111,12 +143,9 @@ BM_DEV void split_range(int n, int parts, int i, int &lo, int &hi) {
     hi = (int)((int64_t)n * (i + 1) / parts);
 }
 
-// ---------------------------------------------------------------------------
-// front: router rows || shared gate/up partial sums over K chunk c.
-// grid = n_rwg + (I/64)*kc_sg workgroups of kW waves.
-// sgp layout [kc_sg][2][T][I] (gate, up).
-// ---------------------------------------------------------------------------
-template <int XBF16, int NT>
+// Shared-expert gate/up partial sums of panel P over K pieces [c0, c1) for
+// tokens t0..t0+NT-1, by NW waves; sgp layout [kc_sg][2][T][I].
+template <int XBF16, int NT, int NW>
 BM_DEV void shared_gateup_pass(int H, int I, int T, int t0, int P, int c0, int c1,
                                const uint4 *__restrict__ sg, const uint4 *__restrict__ su,
                                const void *__restrict__ x, float *__restrict__ gp,
@@ -130,7 +159,7 @@ BM_DEV void shared_gateup_pass(int H, int I, int T, int t0, int P, int c0, int c
 #pragma unroll
     for (int t = 0; t < NT; t++) ag[t] = au[t] = 0.f;
     int w0, w1;
-    split_range(c1 - c0, kW, wv, w0, w1);
+    split_range(c1 - c0, NW, wv, w0, w1);
 #pragma unroll 4
     for (int c = c0 + w0; c < c0 + w1; c++) {
         const int64_t pc = ((int64_t)P * K8 + c) * 64 + lane;
@@ -151,7 +180,7 @@ BM_DEV void shared_gateup_pass(int H, int I, int T, int t0, int P, int c0, int c
     if (wv < NT && t0 + wv < T) {
         float g = 0.f, u = 0.f;
 #pragma unroll
-        for (int v = 0; v < kW; v++) {
+        for (int v = 0; v < NW; v++) {
             g += red[((v * kNT + wv) * 2 + 0) * 64 + lane];
             u += red[((v * kNT + wv) * 2 + 1) * 64 + lane];
         }
@@ -161,28 +190,55 @@ BM_DEV void shared_gateup_pass(int H, int I, int T, int t0, int P, int c0, int c
     __syncthreads();
 }
 
+// Workgroup roles, in blockIdx order: decode tables | activation sums |
+// router rows (n_rwg) | shared-expert gate/up partial sums per (panel,
+// K chunk).
 template <int XBF16>
 __global__ void __launch_bounds__(kW * 64)
-k_dec_front(int H, int I, int E, int T, int n_rwg, int kc_sg, const uint16_t *__restrict__ wr,
-            const void *__restrict__ x, const uint4 *__restrict__ sg, const uint4 *__restrict__ su,
-            const uint8_t *__restrict__ grid, uint4 *__restrict__ gtab, float *__restrict__ logits,
-            float *__restrict__ sgp) {
+k_dec_front(int H, int I, int E, int T, int n_xwg, int n_rwg, int kc_sg, const uint16_t *__restrict__ wr,
+            const void *__restrict__ x, const uint8_t *__restrict__ grid, uint32_t *__restrict__ gtab,
+            float *__restrict__ xs, float *__restrict__ logits, int32_t *__restrict__ ycount,
+            const uint4 *__restrict__ sg, const uint4 *__restrict__ su, float *__restrict__ sgp) {
     __shared__ float red[kW * kNT * 2 * 64];
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int b = blockIdx.x;
     if (b < kTabWG) {          // the decode tables, once per call
         const int i = b * kW * 64 + threadIdx.x;
-        if (i < kIq2xMainEntries) {
-            gtab[i] = iq2x_main_entry(grid, i);
-        } else if (i < kTabU4) {
-            const int m = 2 * (i - kIq2xMainEntries);
-            const uint2 a = iq2x_mask_entry(m), c = iq2x_mask_entry(m + 1);
-            gtab[i] = make_uint4(a.x, a.y, c.x, c.y);
-        }
+        gtab[i] = iq2x_tab_entry(grid, i >= kIq2xTabDwords, i & (kIq2xTabDwords - 1));
+        if (b == 0)            // the down launch's per-panel combine counters
+            for (int p = threadIdx.x; p < H / 64; p += kW * 64) ycount[p] = 0;
         return;
     }
     b -= kTabWG;
+    if (b < n_xwg) {           // activation sums over groups of 32, fixed order
+        const int G = H / 32;
+        const int64_t i = (int64_t)b * kW * 64 + threadIdx.x;
+        if (i >= (int64_t)T * G) return;
+        const int t = (int)(i / G), g = (int)(i - (int64_t)t * G);
+        float sum = 0.f;
+        if (XBF16) {
+            const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)t * H + 32 * g);
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const uint4 v = p[q];
+                const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) sum += bf16_lo(wd[j]) + bf16_hi(wd[j]);
+            }
+        } else {
+            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)t * H + 32 * g);
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                const float4 v = p[q];
+                sum += v.x + v.y + v.z + v.w;
+            }
+        }
+        xs[i] = sum;
+        return;
+    }
+    b -= n_xwg;
     if (b < n_rwg) {
-        const int e = b * kW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int e = b * kW + wv;
         if (e >= E) return;
         const uint4 *wrow = reinterpret_cast<const uint4 *>(wr + (int64_t)e * H);
         if (T == 1)
@@ -193,16 +249,18 @@ k_dec_front(int H, int I, int E, int T, int n_rwg, int kc_sg, const uint16_t *__
             router_row<XBF16, 16>(wrow, x, H, T, E, e, logits);
         return;
     }
-    const int bs = b - n_rwg, P = bs / kc_sg, c = bs % kc_sg;
+    b -= n_rwg;
+    // shared gate/up: panel P of the I rows, K chunk c
+    const int P = b / kc_sg, c = b % kc_sg;
     int c0, c1;
     split_range(H / 8, kc_sg, c, c0, c1);
     float *gp = sgp + (int64_t)(c * 2 + 0) * T * I;
     float *up_ = sgp + (int64_t)(c * 2 + 1) * T * I;
     for (int t0 = 0; t0 < T; t0 += kNT) {
         if (T - t0 == 1)
-            shared_gateup_pass<XBF16, 1>(H, I, T, t0, P, c0, c1, sg, su, x, gp, up_, red);
+            shared_gateup_pass<XBF16, 1, kW>(H, I, T, t0, P, c0, c1, sg, su, x, gp, up_, red);
         else
-            shared_gateup_pass<XBF16, kNT>(H, I, T, t0, P, c0, c1, sg, su, x, gp, up_, red);
+            shared_gateup_pass<XBF16, kNT, kW>(H, I, T, t0, P, c0, c1, sg, su, x, gp, up_, red);
     }
 }
 
@@ -223,9 +281,15 @@ k_dec_mid(int E, int k, int T, const float *__restrict__ logits, int32_t *__rest
         __threadfence_block();
         __syncthreads();
     }
-    if (do_bucket)
-        bucket_block(ids, T * k, E, counts, offsets, perm, active, n_active, nullptr, nullptr, 1, smem,
-                     swave);
+    if (!do_bucket) return;
+    const int n = T * k;
+    if (n <= kWaveBucketMax) {        // decode batches: one wave, no block scans
+        if (wv == 0) bucket_wave_rank(ids, n, E, perm, smem);
+        __syncthreads();
+        if (wv == 0) bucket_wave_lists(n, smem, counts, offsets, active, n_active);
+        return;
+    }
+    bucket_block(ids, n, E, counts, offsets, perm, active, n_active, nullptr, nullptr, 1, smem, swave);
 }
 
 // ---------------------------------------------------------------------------
@@ -237,53 +301,77 @@ struct Tok {
 };
 
 template <int XBF16, int NT>
-BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P, const char *tab,
+BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P, uint4 *tabl,
+                               const uint4 *__restrict__ gtab, bool copy_tab,
                                const uint8_t *__restrict__ gate, const uint8_t *__restrict__ up,
-                               const void *__restrict__ x, const int32_t *__restrict__ perm,
+                               const void *__restrict__ x, const float *__restrict__ xs,
+                               const int32_t *perm,
                                uint16_t *__restrict__ h, int64_t hrows, float *__restrict__ hsum,
                                float *red) {
     const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int tok[NT];
 #pragma unroll
-    for (int t = 0; t < NT; t++) tok[t] = perm[tk.off + min(t0 + t, tk.cnt - 1)] / k;
+    for (int t = 0; t < NT; t++)
+        tok[t] = __builtin_amdgcn_readfirstlane(perm[tk.off + min(t0 + t, tk.cnt - 1)] / k);
     float ag[NT], au[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) ag[t] = au[t] = 0.f;
     const int nb = H / kQK;
     const int64_t slab = (int64_t)I * nb * 66;
     const uint8_t *G = gate + tk.e * slab, *U = up + tk.e * slab;
-    const uint4 *gq = reinterpret_cast<const uint4 *>(G);
-    const uint4 *uq = reinterpret_cast<const uint4 *>(U);
-    const uint16_t *gd = reinterpret_cast<const uint16_t *>(G + (int64_t)I * nb * 64);
-    const uint16_t *ud = reinterpret_cast<const uint16_t *>(U + (int64_t)I * nb * 64);
-    int kb0, kb1;
-    split_range(nb, kWG, wv, kb0, kb1);
-    // software pipeline: the next superblock's 8 pieces are in flight while
-    // the current one is decoded
-    uint4 g4[4], u4[4], ng[4], nu[4];
-    uint32_t gdw = 0, udw = 0, ngd = 0, nud = 0;
-    auto load = [&](int kb, uint4 (&a)[4], uint4 (&bq)[4], uint32_t &da, uint32_t &db) {
-        const int64_t pk = (int64_t)P * nb + kb;
+    const uint4 *gq = reinterpret_cast<const uint4 *>(G) + (int64_t)P * nb * 4 * 64 + lane;
+    const uint4 *uq = reinterpret_cast<const uint4 *>(U) + (int64_t)P * nb * 4 * 64 + lane;
+    const uint16_t *gd = reinterpret_cast<const uint16_t *>(G + (int64_t)I * nb * 64) + (int64_t)P * nb * 64 + lane;
+    const uint16_t *ud = reinterpret_cast<const uint16_t *>(U + (int64_t)I * nb * 64) + (int64_t)P * nb * 64 + lane;
+    // this wave's share of the panel's 16-byte pieces (two groups each), in
+    // batches of kPB; the next batch is in flight while one is decoded
+    int p0, p1;
+    split_range(4 * nb, kWG, wv, p0, p1);
+    constexpr int kPB = pieces_per_batch<NT>();
+    uint4 g4[kPB], u4[kPB], ng[kPB], nu[kPB];
+    uint32_t gdw[kPB], udw[kPB], ngd[kPB], nud[kPB];
+    auto load = [&](int pb, uint4 (&a4)[kPB], uint4 (&b4)[kPB], uint32_t (&da)[kPB], uint32_t (&db)[kPB]) {
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            a[c] = gq[(pk * 4 + c) * 64 + lane];
-            bq[c] = uq[(pk * 4 + c) * 64 + lane];
+        for (int i = 0; i < kPB; i++) {
+            const int pc = min(pb + i, p1 - 1);      // a short last batch re-reads its last piece
+            a4[i] = gq[(int64_t)pc * 64];
+            b4[i] = uq[(int64_t)pc * 64];
+            da[i] = gd[(int64_t)(pc >> 2) * 64];
+            db[i] = ud[(int64_t)(pc >> 2) * 64];
         }
-        da = gd[pk * 64 + lane];
-        db = ud[pk * 64 + lane];
     };
-    if (kb0 < kb1) load(kb0, g4, u4, gdw, udw);
-    for (int kb = kb0; kb < kb1; kb++) {
-        if (kb + 1 < kb1) load(kb + 1, ng, nu, ngd, nud);
-        iq2x_superblock<XBF16, NT>(g4, fp16_to_f32(gdw), tab, x, tok, H, kb * kQK, ag);
-        iq2x_superblock<XBF16, NT>(u4, fp16_to_f32(udw), tab, x, tok, H, kb * kQK, au);
+    if (p0 < p1) load(p0, g4, u4, gdw, udw);
+    if (copy_tab) {            // the decode tables, while the first batch is in flight
+        for (int i = threadIdx.x; i < kTabDw / 4; i += blockDim.x) tabl[i] = gtab[i];
+        __syncthreads();
+    }
+    const char *tab = reinterpret_cast<const char *>(tabl);
+    // activations of the current group, the next one in flight
+    XGroup<XBF16, NT> xa, xb;
+    if (p0 < p1) load_xgroup<XBF16, NT>(xa, x, xs, tok, H, 2 * p0);
+    for (int pb = p0; pb < p1; pb += kPB) {
+        if (pb + kPB < p1) load(pb + kPB, ng, nu, ngd, nud);
+        const int n = min(kPB, p1 - pb);
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            g4[c] = ng[c];
-            u4[c] = nu[c];
+        for (int i = 0; i < kPB; i++) {
+            if (i < n) {
+                const int gg = 2 * (pb + i);
+                const float dg = 0.125f * fp16_to_f32(gdw[i]), du = 0.125f * fp16_to_f32(udw[i]);
+                load_xgroup<XBF16, NT>(xb, x, xs, tok, H, gg + 1);
+                iq2x_group<XBF16, NT>(g4[i].x, g4[i].y, dg, tab, xa, x, tok, H, gg, ag);
+                iq2x_group<XBF16, NT>(u4[i].x, u4[i].y, du, tab, xa, x, tok, H, gg, au);
+                load_xgroup<XBF16, NT>(xa, x, xs, tok, H, pb + i + 1 < p1 ? gg + 2 : gg);
+                iq2x_group<XBF16, NT>(g4[i].z, g4[i].w, dg, tab, xb, x, tok, H, gg + 1, ag);
+                iq2x_group<XBF16, NT>(u4[i].z, u4[i].w, du, tab, xb, x, tok, H, gg + 1, au);
+            }
         }
-        gdw = ngd;
-        udw = nud;
+#pragma unroll
+        for (int i = 0; i < kPB; i++) {
+            g4[i] = ng[i];
+            u4[i] = nu[i];
+            gdw[i] = ngd[i];
+            udw[i] = nud[i];
+        }
     }
 #pragma unroll
     for (int t = 0; t < NT; t++) {
@@ -328,93 +416,95 @@ BM_DEV float dot8_hilo(uint4 wq, uint4 hh, uint4 hl, float acc) {
     return acc;
 }
 
-template <int NT>
-BM_DEV void shared_down_pass(int H, int I, int T, int t0, int P, int c0, int c1,
-                             const uint4 *__restrict__ sd, const uint16_t *__restrict__ hs,
-                             float *__restrict__ osp, float *red) {
-    const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int K8 = I / 8;
-    const int64_t lo_off = (int64_t)T * I;
-    float acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; t++) acc[t] = 0.f;
-    int w0, w1;
-    split_range(c1 - c0, kW, wv, w0, w1);
-#pragma unroll 4
-    for (int c = c0 + w0; c < c0 + w1; c++) {
-        const uint4 wq = sd[((int64_t)P * K8 + c) * 64 + lane];
-#pragma unroll
-        for (int t = 0; t < NT; t++) {
-            const uint16_t *hp = hs + (int64_t)min(t0 + t, T - 1) * I + 8 * c;
-            acc[t] = dot8_hilo(wq, *reinterpret_cast<const uint4 *>(hp),
-                               *reinterpret_cast<const uint4 *>(hp + lo_off), acc[t]);
+// Routing of a small batch (T*k <= 128) inside a workgroup: top-k of the
+// router logits (mode 1) or the given ids (mode 2), then the one-wave
+// bucketing, all in LDS; workgroup 0 also writes the results out for the
+// launches that follow.  Counts and offsets are kept for the active experts
+// only.
+struct SmallRoute {
+    int counts[kMaxExperts], offsets[kMaxExperts];
+    int perm[kWaveBucketMax], active[kWaveBucketMax], ids[kWaveBucketMax], sk[kWaveBucketMax];
+    int n_active;
+};
+
+BM_DEV void route_in_wg(int mode, int E, int k, int T, const float *__restrict__ logits, int32_t *ids,
+                        float *w, const bm_host::Buckets &bk, SmallRoute &r) {
+    const int wv = threadIdx.x >> 6, n = T * k;
+    const bool out = blockIdx.x == 0;
+    if (mode == 1) {
+        for (int t = wv; t < T; t += kWG)
+            topk_wave(logits + (int64_t)t * E, E, k, out ? ids + (int64_t)t * k : nullptr,
+                      out ? w + (int64_t)t * k : nullptr, r.ids + t * k);
+    } else {
+        for (int p = threadIdx.x; p < n; p += blockDim.x) r.ids[p] = ids[p];
+    }
+    __syncthreads();
+    if (wv == 0) bucket_wave_rank(r.ids, n, E, r.perm, r.sk);
+    __syncthreads();
+    if (wv == 0) bucket_wave_lists(n, r.sk, r.counts, r.offsets, r.active, &r.n_active);
+    __syncthreads();
+    if (out) {
+        for (int p = threadIdx.x; p < n; p += blockDim.x) bk.perm[p] = r.perm[p];
+        for (int a = threadIdx.x; a < r.n_active; a += blockDim.x) {
+            const int e = r.active[a];
+            bk.active[a] = e;
+            bk.counts[e] = r.counts[e];
+            bk.offsets[e] = r.offsets[e];
         }
+        if (threadIdx.x == 0) *bk.n_active = r.n_active;
     }
-#pragma unroll
-    for (int t = 0; t < NT; t++) red[(wv * kNT + t) * 64 + lane] = acc[t];
-    __syncthreads();
-    if (wv < NT && t0 + wv < T) {
-        float s = 0.f;
-#pragma unroll
-        for (int v = 0; v < kW; v++) s += red[(v * kNT + wv) * 64 + lane];
-        osp[(int64_t)(t0 + wv) * H + P * 64 + lane] = s;
-    }
-    __syncthreads();
 }
 
-// MULTI = 0 takes the experts chosen by exactly one token (and the shared
-// h); MULTI = 1 the experts with several tokens (passes of kNT tokens).
-// Keeping the two apart keeps each kernel's register use low.
+// MULTI = 0 takes the experts chosen by exactly one token, MULTI = 1 the
+// experts with several tokens (passes of kNT tokens); keeping the two apart
+// keeps each kernel's register use low.  route_mode: 0 the bucketing is in
+// bk already, 1/2 route_in_wg (MULTI = 0 only).
 template <int XBF16, int MULTI>
 __global__ void __launch_bounds__(kWG * 64)
-k_dec_gateup(int H, int I, int k, int T, int n_gwg, int kc_sg, const uint8_t *__restrict__ gate,
+k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const uint8_t *__restrict__ gate,
              const uint8_t *__restrict__ up, const uint4 *__restrict__ gtab,
-             const void *__restrict__ x, const int32_t *__restrict__ counts,
-             const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
-             const int32_t *__restrict__ active, const int32_t *__restrict__ n_active,
-             const float *__restrict__ sgp, uint16_t *__restrict__ hs, uint16_t *__restrict__ h,
-             float *__restrict__ hsum) {
+             const void *__restrict__ x, const float *__restrict__ xs, const float *__restrict__ logits,
+             int32_t *ids, float *w, bm_host::Buckets bk, uint16_t *__restrict__ h, float *__restrict__ hsum) {
     const int64_t hrows = (int64_t)T * k;
-    __shared__ uint4 tab[kTabU4];
+    __shared__ uint4 tab[kTabDw / 4];
     __shared__ float red[kWG * (MULTI ? kNT : 1) * 2 * 64];
+    __shared__ SmallRoute sr;
+    const int32_t *counts = bk.counts, *offsets = bk.offsets, *perm = bk.perm, *active = bk.active;
+    int na;
+    if (!MULTI && route_mode) {
+        route_in_wg(route_mode, E, k, T, logits, ids, w, bk, sr);
+        counts = sr.counts;
+        offsets = sr.offsets;
+        perm = sr.perm;
+        active = sr.active;
+        na = sr.n_active;
+    } else {
+        na = *bk.n_active;
+    }
     const int b = blockIdx.x;
     if (b < n_gwg) {
         const int panels = I / 64, slot = b / panels, P = b % panels;
-        if (slot >= *n_active) return;
+        if (slot >= na) return;
         Tok tk;
         tk.e = active[slot];
         tk.off = offsets[tk.e];
         tk.cnt = counts[tk.e];
         if ((tk.cnt > 1) != (MULTI != 0)) return;
-        for (int i = threadIdx.x; i < kTabU4; i += blockDim.x) tab[i] = gtab[i];
-        __syncthreads();
-        const char *tb = reinterpret_cast<const char *>(tab);
         if (!MULTI) {
-            routed_gateup_pass<XBF16, 1>(H, I, k, tk, 0, P, tb, gate, up, x, perm, h, hrows, hsum, red);
+            routed_gateup_pass<XBF16, 1>(H, I, k, tk, 0, P, tab, gtab, true, gate, up, x, xs, perm, h, hrows,
+                                         hsum, red);
             return;
         }
         for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
             if (tk.cnt - t0 == 1)
-                routed_gateup_pass<XBF16, 1>(H, I, k, tk, t0, P, tb, gate, up, x, perm, h, hrows, hsum, red);
+                routed_gateup_pass<XBF16, 1>(H, I, k, tk, t0, P, tab, gtab, t0 == 0, gate, up, x, xs, perm, h,
+                                             hrows, hsum, red);
             else
-                routed_gateup_pass<XBF16, kNT>(H, I, k, tk, t0, P, tb, gate, up, x, perm, h, hrows, hsum, red);
+                routed_gateup_pass<XBF16, kNT>(H, I, k, tk, t0, P, tab, gtab, t0 == 0, gate, up, x, xs, perm,
+                                               h, hrows, hsum, red);
         }
         return;
     }
-    if (MULTI) return;
-    // shared h = silu(sum of gate partials) * (sum of up partials), fixed order
-    const int64_t n = (int64_t)T * I;
-    const int64_t i = (int64_t)(b - n_gwg) * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    float g = 0.f, u = 0.f;
-    for (int c = 0; c < kc_sg; c++) {
-        g += sgp[(int64_t)(2 * c) * n + i];
-        u += sgp[(int64_t)(2 * c + 1) * n + i];
-    }
-    const float hv = silu(g) * u;
-    const uint32_t hi = f32_to_bf16_rne(hv);
-    hs[i] = (uint16_t)hi;
-    hs[n + i] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
 }
 
 // ---------------------------------------------------------------------------
@@ -490,71 +580,176 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
         }
     }
 #pragma unroll
-    for (int t = 0; t < NT; t++) red[(wv * kNT + t) * 64 + lane] = acc[t];
+    for (int t = 0; t < NT; t++) red[(wv * NT + t) * 64 + lane] = acc[t];
     __syncthreads();
     if (wv < NT && t0 + wv < tk.cnt) {
         float s = 0.f;
 #pragma unroll
-        for (int v = 0; v < kW; v++) s += red[(v * kNT + wv) * 64 + lane];
-        o[(int64_t)perm[tk.off + t0 + wv] * H + P * 64 + lane] = s;
+        for (int v = 0; v < kW; v++) s += red[(v * NT + wv) * 64 + lane];
+        st_dev(&o[(int64_t)perm[tk.off + t0 + wv] * H + P * 64 + lane], s);
     }
     __syncthreads();
 }
 
-__global__ void __launch_bounds__(kW * 64)
-k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const uint8_t *__restrict__ down,
+// Shared h for tokens t0..t0+NT-1 on the I columns [8 c0, 8 c1) of this
+// workgroup's K chunk: silu(sum of the gate partials) * (sum of the up
+// partials), summed in a fixed order, as bf16 hi + lo in LDS
+// (hl[t][hi, lo][8 (c1 - c0)]).
+template <int NT>
+BM_DEV void shared_h_chunk(int I, int T, int t0, int c0, int c1, int kc_sg, const float *__restrict__ sgp,
+                           uint16_t *hl) {
+    const int n = 8 * (c1 - c0);
+    const uint32_t TI = (uint32_t)T * (uint32_t)I;        // 32-bit offsets: one register per load
+    for (int i = threadIdx.x; i < NT * n; i += blockDim.x) {
+        const int t = i / n, j = i - t * n;
+        const uint32_t col = (uint32_t)min(t0 + t, T - 1) * (uint32_t)I + 8 * c0 + j;
+        float gv[kMaxChunks], uv[kMaxChunks];
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; c++) {
+            const uint32_t cc = (uint32_t)min(c, kc_sg - 1);
+            gv[c] = sgp[2 * cc * TI + col];
+            uv[c] = sgp[(2 * cc + 1) * TI + col];
+        }
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; c++)
+            if (c < kc_sg) {
+                g += gv[c];
+                u += uv[c];
+            }
+        const float hv = silu(g) * u;
+        const uint32_t hi = f32_to_bf16_rne(hv);
+        hl[(t * 2 + 0) * n + j] = (uint16_t)hi;
+        hl[(t * 2 + 1) * n + j] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
+    }
+    __syncthreads();
+}
+
+// Shared down of panel P over the K pieces [c0, c1) with h from LDS.
+template <int NT>
+BM_DEV void shared_down_pass(int H, int I, int T, int t0, int P, int c0, int c1,
+                             const uint4 *__restrict__ sd, const uint16_t *hl, float *__restrict__ osp,
+                             float *red) {
+    const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int K8 = I / 8, n = 8 * (c1 - c0);
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = 0.f;
+    int w0, w1;
+    split_range(c1 - c0, kW, wv, w0, w1);
+#pragma unroll 4
+    for (int c = c0 + w0; c < c0 + w1; c++) {
+        const uint4 wq = sd[((int64_t)P * K8 + c) * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            const uint16_t *hp = hl + (t * 2) * n + 8 * (c - c0);
+            acc[t] = dot8_hilo(wq, *reinterpret_cast<const uint4 *>(hp),
+                               *reinterpret_cast<const uint4 *>(hp + n), acc[t]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++) red[(wv * NT + t) * 64 + lane] = acc[t];
+    __syncthreads();
+    if (wv < NT && t0 + wv < T) {
+        float s = 0.f;
+#pragma unroll
+        for (int v = 0; v < kW; v++) s += red[(v * NT + wv) * 64 + lane];
+        st_dev(&osp[(int64_t)(t0 + wv) * H + P * 64 + lane], s);
+    }
+    __syncthreads();
+}
+
+// y for the 64 outputs of panel P: sum over the k slots of w * o, plus the
+// shared partials, in a fixed order (device-scope loads of this launch's
+// results).
+BM_DEV void combine_panel(int H, int k, int T, int kc_sd, int P, const float *o, const float *w,
+                          const float *osp, float *y) {
+    const int wv = threadIdx.x >> 6, n = P * 64 + lane_id();
+    for (int t = wv; t < T; t += kW) {
+        // every load issued before the first is used (k <= 16, kc_sd <= 4)
+        float ov[16], sv[kMaxChunks];
+#pragma unroll
+        for (int j = 0; j < 16; j++) ov[j] = ld_dev(&o[((uint32_t)t * k + min(j, k - 1)) * (uint32_t)H + n]);
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; c++)
+            sv[c] = kc_sd ? ld_dev(&osp[((uint32_t)min(c, kc_sd - 1) * T + t) * (uint32_t)H + n]) : 0.f;
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; j++)
+            if (j < k) s = fmaf(w[t * k + j], ov[j], s);
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; c++)
+            if (c < kc_sd) s += sv[c];
+        y[(int64_t)t * H + n] = s;
+    }
+}
+
+// After a workgroup's outputs for panel P are stored (device scope): count
+// it in the panel's counter (cleared by the front launch); the workgroup
+// that brings the count to all contributors (the active experts and the
+// shared chunks) combines the panel.
+BM_DEV void count_and_combine(int H, int k, int T, int kc_sd, int P, int n_contrib, int32_t *ycount,
+                              const float *o, const float *w, const float *osp, float *y, int *sdo) {
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *sdo = __hip_atomic_fetch_add(&ycount[P], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_contrib - 1;
+    __syncthreads();
+    if (*sdo) combine_panel(H, k, T, kc_sd, P, o, w, osp, y);
+}
+
+// MULTI = 0: experts chosen by one token, and the shared down; MULTI = 1:
+// experts chosen by several tokens (launched only when T > 1).
+template <int MULTI>
+__global__ void __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 8)))
+k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sg, int kc_sd, const uint8_t *__restrict__ down,
            const uint4 *__restrict__ sd, const int32_t *__restrict__ counts,
            const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
            const int32_t *__restrict__ active, const int32_t *__restrict__ n_active,
-           const uint16_t *__restrict__ h, const float *__restrict__ hsum,
-           const uint16_t *__restrict__ hs, float *__restrict__ osp, float *__restrict__ o) {
+           const uint16_t *__restrict__ h, const float *__restrict__ hsum, const float *__restrict__ sgp,
+           const float *__restrict__ w, int32_t *__restrict__ ycount, float *__restrict__ osp,
+           float *__restrict__ o, float *__restrict__ y) {
     const int64_t hrows = (int64_t)T * k;
     __shared__ float red[kW * kNT * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t hl[kNT * 2 * kSharedChunkCols];
+    __shared__ int sdo;
     const int panels = H / 64;
     const int na = *n_active;
-    int P;
     if ((int)blockIdx.x < n_dwg) {
-        const int slot = blockIdx.x / panels;
-        P = blockIdx.x % panels;
+        const int slot = blockIdx.x / panels, P = blockIdx.x % panels;
         if (slot >= na) return;
         Tok tk;
         tk.e = active[slot];
         tk.off = offsets[tk.e];
         tk.cnt = counts[tk.e];
-        for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
-            if (tk.cnt - t0 == 1)
-                routed_down_pass<1>(H, I, tk, t0, P, down, perm, h, hrows, hsum, o, red);
-            else
-                routed_down_pass<kNT>(H, I, tk, t0, P, down, perm, h, hrows, hsum, o, red);
+        if ((tk.cnt > 1) != (MULTI != 0)) return;
+        if (!MULTI) {
+            routed_down_pass<1>(H, I, tk, 0, P, down, perm, h, hrows, hsum, o, red);
+        } else {
+            for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
+                if (tk.cnt - t0 == 1)
+                    routed_down_pass<1>(H, I, tk, t0, P, down, perm, h, hrows, hsum, o, red);
+                else
+                    routed_down_pass<kNT>(H, I, tk, t0, P, down, perm, h, hrows, hsum, o, red);
+            }
         }
-    } else {
-        const int bs = blockIdx.x - n_dwg, c = bs % kc_sd;
-        P = bs / kc_sd;
+        count_and_combine(H, k, T, kc_sd, P, na + kc_sd, ycount, o, w, osp, y, &sdo);
+    } else if (!MULTI) {
+        const int bs = blockIdx.x - n_dwg, c = bs % kc_sd, P = bs / kc_sd;
         int c0, c1;
         split_range(I / 8, kc_sd, c, c0, c1);
         float *op = osp + (int64_t)c * T * H;
         for (int t0 = 0; t0 < T; t0 += kNT) {
-            if (T - t0 == 1)
-                shared_down_pass<1>(H, I, T, t0, P, c0, c1, sd, hs, op, red);
-            else
-                shared_down_pass<kNT>(H, I, T, t0, P, c0, c1, sd, hs, op, red);
+            if (T - t0 == 1) {
+                shared_h_chunk<1>(I, T, t0, c0, c1, kc_sg, sgp, hl);
+                shared_down_pass<1>(H, I, T, t0, P, c0, c1, sd, hl, op, red);
+            } else {
+                shared_h_chunk<kNT>(I, T, t0, c0, c1, kc_sg, sgp, hl);
+                shared_down_pass<kNT>(H, I, T, t0, P, c0, c1, sd, hl, op, red);
+            }
         }
+        count_and_combine(H, k, T, kc_sd, P, na + kc_sd, ycount, o, w, osp, y, &sdo);
     }
-}
-
-// y[t][n] = sum_j w[t][j] * o[t*k+j][n] (+ shared partials), fixed order.
-__global__ void __launch_bounds__(256)
-k_dec_combine(int H, int k, int T, int kc_sd, const float *__restrict__ o,
-              const float *__restrict__ w, const float *__restrict__ osp, float *__restrict__ y) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)T * H) return;
-    const int t = (int)(i / H);
-    const int n = (int)(i - (int64_t)t * H);
-    float s = 0.f;
-    for (int j = 0; j < k; j++) s = fmaf(w[t * k + j], o[((int64_t)t * k + j) * H + n], s);
-    if (osp)
-        for (int c = 0; c < kc_sd; c++) s += osp[((int64_t)c * T + t) * H + n];
-    y[i] = s;
 }
 
 }  // namespace
@@ -567,92 +762,78 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     p.slots = (int)std::min<int64_t>(L->E, (int64_t)T * L->k);
     p.n_rwg = with_router ? (L->E + kW - 1) / kW : 0;
     p.kc_sg = shared ? 8 : 0;
-    p.kc_sd = shared ? 4 : 0;
-    p.bucket_in_mid = (int64_t)T * L->k <= 4096;
+    p.kc_sd = shared ? std::max(1, (L->I + kSharedChunkCols - 1) / kSharedChunkCols) : 0;
+    p.small = (int64_t)T * L->k <= kWaveBucketMax;
+    p.need_mid = !p.small;
     return p;
 }
 
-size_t decode_mid_lds(int E) { return (size_t)(2 + kBW) * E * sizeof(int); }
+size_t decode_mid_lds(int E) {
+    return (size_t)std::max<int64_t>((int64_t)(2 + kBW) * E, kWaveBucketMax) * sizeof(int);
+}
 
 int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, const DecodePlan &p,
                   const DecodeBufs &b, hipStream_t s) {
     const int H = L->H, I = L->I, E = L->E, k = L->k;
     const bool shared = L->shared_gate != nullptr;
-    // front
-    const int n_front = kTabWG + p.n_rwg + (shared ? (I / 64) * p.kc_sg : 0);
+    const bool bf = x_dtype == BITMOE_BF16;
+    if (p.kc_sd > kMaxChunks || p.kc_sg > kMaxChunks) return BITMOE_EUNSUPPORTED;
+    // front: tables, activation sums, router rows, shared gate/up
+    const int n_xwg = (int)(((int64_t)T * (H / 32) + kW * 64 - 1) / (kW * 64));
+    const int n_front = kTabWG + n_xwg + p.n_rwg + (shared ? (I / 64) * p.kc_sg : 0);
     {
-        if (x_dtype == BITMOE_BF16)
-            k_dec_front<1><<<n_front, kW * 64, 0, s>>>(H, I, E, T, p.n_rwg, p.kc_sg,
-                                                       (const uint16_t *)L->router_w, x,
-                                                       (const uint4 *)L->shared_gate,
-                                                       (const uint4 *)L->shared_up, (const uint8_t *)L->grid,
-                                                       b.tab, b.logits, b.sgp);
-        else
-            k_dec_front<0><<<n_front, kW * 64, 0, s>>>(H, I, E, T, p.n_rwg, p.kc_sg,
-                                                       (const uint16_t *)L->router_w, x,
-                                                       (const uint4 *)L->shared_gate,
-                                                       (const uint4 *)L->shared_up, (const uint8_t *)L->grid,
-                                                       b.tab, b.logits, b.sgp);
+        auto kf = bf ? k_dec_front<1> : k_dec_front<0>;
+        kf<<<n_front, kW * 64, 0, s>>>(H, I, E, T, n_xwg, p.n_rwg, p.kc_sg, (const uint16_t *)L->router_w, x,
+                                       (const uint8_t *)L->grid, reinterpret_cast<uint32_t *>(b.tab), b.xs,
+                                       b.logits, b.ycount, (const uint4 *)L->shared_gate,
+                                       (const uint4 *)L->shared_up, b.sgp);
         BM_LAUNCH_CHECK();
     }
-    // mid
-    const size_t sh = decode_mid_lds(E);
-    if (sh > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_dec_mid),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
-    k_dec_mid<<<1, kBT, sh, s>>>(E, k, T, p.n_rwg ? b.logits : nullptr, b.ids, b.w,
-                                 p.bucket_in_mid ? 1 : 0, b.bk.counts, b.bk.offsets, b.bk.perm,
-                                 b.bk.active, b.bk.n_active);
-    BM_LAUNCH_CHECK();
-    if (!p.bucket_in_mid) {
-        int rc = launch_bucket(b.ids, T, k, E, b.bk, s);
-        if (rc) return rc;
+    // mid: top-k and bucketing of batches above 128 pairs
+    if (p.need_mid) {
+        const int64_t n = (int64_t)T * k;
+        const bool in_mid = n <= 4096;
+        const size_t sh = decode_mid_lds(E);
+        if (sh > 64 * 1024)
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_dec_mid),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+        k_dec_mid<<<1, kBT, sh, s>>>(E, k, T, p.n_rwg ? b.logits : nullptr, b.ids, b.w, in_mid ? 1 : 0,
+                                     b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active, b.bk.n_active);
+        BM_LAUNCH_CHECK();
+        if (!in_mid) {
+            int rc = launch_bucket(b.ids, T, k, E, b.bk, s);
+            if (rc) return rc;
+        }
     }
-    // gateup (+ shared h)
+    // routed gate/up; experts chosen by several tokens in a second launch
     const int n_gwg = p.slots * (I / 64);
-    const int n_fin = shared ? (int)(((int64_t)T * I + kWG * 64 - 1) / (kWG * 64)) : 0;
     timing_begin(s);
-    if (x_dtype == BITMOE_BF16)
-        k_dec_gateup<1, 0><<<n_gwg + n_fin, kWG * 64, 0, s>>>(H, I, k, T, n_gwg, p.kc_sg,
-                                                              (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q,
-                                                              (const uint4 *)b.tab, x, b.bk.counts, b.bk.offsets,
-                                                              b.bk.perm, b.bk.active, b.bk.n_active, b.sgp, b.hs,
-                                                              b.h, b.hsum);
-    else
-        k_dec_gateup<0, 0><<<n_gwg + n_fin, kWG * 64, 0, s>>>(H, I, k, T, n_gwg, p.kc_sg,
-                                                              (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q,
-                                                              (const uint4 *)b.tab, x, b.bk.counts, b.bk.offsets,
-                                                              b.bk.perm, b.bk.active, b.bk.n_active, b.sgp, b.hs,
-                                                              b.h, b.hsum);
-    BM_LAUNCH_CHECK();
-    if (T > 1) {   // experts chosen by several tokens
-        if (x_dtype == BITMOE_BF16)
-            k_dec_gateup<1, 1><<<n_gwg, kWG * 64, 0, s>>>(H, I, k, T, n_gwg, p.kc_sg,
-                                                          (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q,
-                                                          (const uint4 *)b.tab, x, b.bk.counts, b.bk.offsets,
-                                                          b.bk.perm, b.bk.active, b.bk.n_active, b.sgp, b.hs,
-                                                          b.h, b.hsum);
-        else
-            k_dec_gateup<0, 1><<<n_gwg, kWG * 64, 0, s>>>(H, I, k, T, n_gwg, p.kc_sg,
-                                                          (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q,
-                                                          (const uint4 *)b.tab, x, b.bk.counts, b.bk.offsets,
-                                                          b.bk.perm, b.bk.active, b.bk.n_active, b.sgp, b.hs,
-                                                          b.h, b.hsum);
+    const int route_mode = p.small ? (p.n_rwg ? 1 : 2) : 0;
+    for (int multi = 0; multi < (T > 1 ? 2 : 1); multi++) {
+        auto kg = multi ? (bf ? k_dec_gateup<1, 1> : k_dec_gateup<0, 1>)
+                        : (bf ? k_dec_gateup<1, 0> : k_dec_gateup<0, 0>);
+        kg<<<n_gwg, kWG * 64, 0, s>>>(H, I, E, k, T, n_gwg, multi ? 0 : route_mode, (const uint8_t *)L->gate_q,
+                                      (const uint8_t *)L->up_q, (const uint4 *)b.tab, x, b.xs, b.logits, b.ids,
+                                      b.w, b.bk, b.h, b.hsum);
+        BM_LAUNCH_CHECK();
     }
-    BM_LAUNCH_CHECK();
     timing_end(s);
-    // down (+ shared down), then the combine
+    // down || shared down; the last workgroup to finish a panel combines it
     const int n_dwg = p.slots * (H / 64);
     const int n_sd = shared ? (H / 64) * p.kc_sd : 0;
-    k_dec_down<<<n_dwg + n_sd, kW * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, (const uint8_t *)L->down_q,
+    k_dec_down<0><<<n_dwg + n_sd, kW * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sg, p.kc_sd,
+                                                   (const uint8_t *)L->down_q, (const uint4 *)L->shared_down,
+                                                   b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active,
+                                                   b.bk.n_active, b.h, b.hsum, b.sgp, b.w, b.ycount,
+                                                   shared ? b.osp : nullptr, b.o, b.y);
+    BM_LAUNCH_CHECK();
+    if (T > 1) {
+        k_dec_down<1><<<n_dwg, kW * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sg, p.kc_sd, (const uint8_t *)L->down_q,
                                                 (const uint4 *)L->shared_down, b.bk.counts, b.bk.offsets,
-                                                b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum, b.hs,
-                                                shared ? b.osp : nullptr, b.o);
-    BM_LAUNCH_CHECK();
-    const int64_t ny = (int64_t)T * H;
-    k_dec_combine<<<(unsigned)((ny + 255) / 256), 256, 0, s>>>(H, k, T, p.kc_sd, b.o, b.w,
-                                                               shared ? b.osp : nullptr, b.y);
-    BM_LAUNCH_CHECK();
+                                                b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum, b.sgp, b.w,
+                                                b.ycount, shared ? b.osp : nullptr, b.o, b.y);
+        BM_LAUNCH_CHECK();
+    }
     return BITMOE_OK;
 }
 

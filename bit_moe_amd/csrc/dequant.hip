@@ -107,19 +107,18 @@ k_dequant_q2k(const uint8_t *__restrict__ blocks, int64_t nblocks, void *__restr
     }
 }
 
-// One canonical IQ2X group (4 index bytes, u32 signs/scale) -> the four
-// 16-bit fields of the tiled layout (see common.h), packed in two words.
+// One canonical IQ2X group (4 index bytes, u32 signs/scale) -> the two
+// words of the tiled layout (see common.h).
+BM_DEV uint32_t iq2x_run_field(uint32_t idx, uint32_t s7) {
+    const uint32_t p03 = __popc(s7 & 15u) & 1u;
+    return (s7 & 7u) | (p03 << 3) | (idx << 4) | (((s7 >> 4) & 7u) << 12);
+}
 BM_DEV uint2 iq2x_group_fields(uint32_t idxw, uint32_t a) {
     const uint32_t s = a >> 28;
-    uint32_t F[4];
+    uint32_t R[4];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const uint32_t s7 = (a >> (7 * j)) & 0x7Fu;
-        const uint32_t par = __popc(s7 & 15u) & 1u;
-        F[j] = (((idxw >> (8 * j)) & 0xFFu) << 8) | ((s7 & 7u) << 4) | (par << 7) |
-               (((s7 >> 4) & 7u) << 1) | ((s >> j) & 1u);
-    }
-    return make_uint2(F[0] | (F[1] << 16), F[2] | (F[3] << 16));
+    for (int j = 0; j < 4; j++) R[j] = iq2x_run_field((idxw >> (8 * j)) & 0xFFu, (a >> (7 * j)) & 0x7Fu);
+    return make_uint2((s & 3u) | (R[0] << 2) | (R[1] << 17), (s >> 2) | (R[2] << 2) | (R[3] << 17));
 }
 
 // canonical IQ2X -> tiled; one thread per block

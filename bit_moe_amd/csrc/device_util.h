@@ -7,41 +7,61 @@
 
 namespace bm {
 
-// Top-k of one token's logits by one wavefront: repeated wave argmax
-// (larger value, then lower index), then softmax over the k selected.
-// Lane 0 writes ids[0..k) and w[0..k).  E <= 1024, k <= 16.
+// Wave-wide max through DPP row shifts and row broadcasts (no LDS round
+// trips); lanes without a source lane keep their own value.
+template <int CTRL, int ROWS>
+BM_DEV float dpp_max(float v) {
+    const int o = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF, false);
+    return fmaxf(v, __int_as_float(o));
+}
+BM_DEV float wave_max_f32(float v) {
+    v = dpp_max<0x111, 0xF>(v);   // row_shr:1
+    v = dpp_max<0x112, 0xF>(v);   // row_shr:2
+    v = dpp_max<0x114, 0xF>(v);   // row_shr:4
+    v = dpp_max<0x118, 0xF>(v);   // row_shr:8: lane 15 of each row holds the row max
+    v = dpp_max<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+    v = dpp_max<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3: lane 63 holds the max
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Top-k of one token's logits by one wavefront: k rounds of wave max, the
+// lowest index holding it (ballots), then the softmax over the k selected.
+// Lane 0 writes ids[0..k) and w[0..k) (either may be null) and, if given,
+// the ids to sids[0..k) as well.  E <= 1024, k <= 16.  (NaN logits:
+// the result is unspecified but every id is distinct and in range.)
 BM_DEV void topk_wave(const float *__restrict__ lrow, int E, int k, int32_t *__restrict__ ids,
-                      float *__restrict__ wout) {
+                      float *__restrict__ wout, int *sids = nullptr) {
     const int lane = lane_id();
     constexpr int MAXV = 16;
+    const int nv = (E + 63) >> 6;
     float v[MAXV];
-    uint32_t taken = 0;
+    uint32_t live = 0;        // bit i: element lane + 64 i exists and is not taken
 #pragma unroll
     for (int i = 0; i < MAXV; i++) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? lrow[e] : 0.f;
+        const int ec = e < E ? e : E - 1;        // every load issued, the extra ones masked
+        v[i] = lrow[ec];
+        if (e < E) live |= 1u << i;
     }
     float sel[16];
     int sid[16];
     for (int j = 0; j < k; j++) {
-        float bv = 0.f;
-        int be = 0x7FFFFFFF;
+        float bv = -__builtin_inff();
 #pragma unroll
-        for (int i = 0; i < MAXV; i++) {
-            const int e = lane + 64 * i;
-            const bool ok = e < E && !((taken >> i) & 1u);
-            if (ok && (be == 0x7FFFFFFF || v[i] > bv)) { bv = v[i]; be = e; }
+        for (int i = 0; i < MAXV; i++)
+            if ((live >> i) & 1u) bv = fmaxf(bv, v[i]);
+        const float m = wave_max_f32(bv);
+        int be = -1;
+        for (int i = 0; i < nv && be < 0; i++) {
+            const uint64_t b = __ballot(((live >> i) & 1u) && v[i] == m);
+            if (b) be = 64 * i + (int)__builtin_ctzll(b);
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oe = __shfl_xor(be, o, 64);
-            const bool better = (oe != 0x7FFFFFFF) &&
-                                (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be));
-            if (better) { bv = ov; be = oe; }
+        for (int i = 0; i < nv && be < 0; i++) {      // only reached with NaN logits
+            const uint64_t b = __ballot((live >> i) & 1u);
+            if (b) be = 64 * i + (int)__builtin_ctzll(b);
         }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        sel[j] = bv;
+        if ((be & 63) == lane) live &= ~(1u << (be >> 6));
+        sel[j] = m;
         sid[j] = be;
     }
     if (lane == 0) {
@@ -49,8 +69,9 @@ BM_DEV void topk_wave(const float *__restrict__ lrow, int E, int k, int32_t *__r
         for (int j = 0; j < k; j++) { ex[j] = __expf(sel[j] - sel[0]); z += ex[j]; }
         const float inv = 1.0f / z;
         for (int j = 0; j < k; j++) {
-            ids[j] = sid[j];
-            wout[j] = ex[j] * inv;
+            if (ids) ids[j] = sid[j];
+            if (wout) wout[j] = ex[j] * inv;
+            if (sids) sids[j] = sid[j];
         }
     }
 }
@@ -156,6 +177,83 @@ BM_DEV void active_and_tiles(const int *scount, int E, int32_t *__restrict__ act
     }
 }
 
+
+// ---- small-batch bucketing by one wavefront (n <= 128 pairs) -------------
+// Stage 1: the stable rank of every pair among all pairs (key = expert id,
+// ties by pair index) from ballots over the key bits, most significant
+// first; perm[rank] = pair, and the keys in sorted order into LDS sk[].
+// Stage 2 (after a block barrier): the ascending active list, and counts
+// and offsets of the active experts only (other entries are not written).
+constexpr int kWaveBucketMax = 128;
+
+BM_DEV void bucket_wave_rank(const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ perm,
+                             int *sk) {
+    const int lane = lane_id();
+    const int kb = key_bits(E);
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int M = n > 64 ? 2 : 1;
+    int key[2];
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        const int p = lane + 64 * m;
+        key[m] = p < n ? ids[p] : E;
+    }
+    for (int m = 0; m < M; m++) {
+        int rank = 0;
+        for (int m2 = 0; m2 < M; m2++) {
+            uint64_t eq = ~0ull;
+            int less = 0;
+            for (int b = kb - 1; b >= 0; b--) {
+                const uint64_t B = __ballot((key[m2] >> b) & 1);
+                if ((key[m] >> b) & 1) {
+                    less += __popcll(eq & ~B);
+                    eq &= B;
+                } else {
+                    eq &= ~B;
+                }
+            }
+            rank += less + (m2 < m ? __popcll(eq) : m2 == m ? __popcll(eq & below) : 0);
+        }
+        const int p = lane + 64 * m;
+        if (p < n) {
+            perm[rank] = p;
+            sk[rank] = key[m];
+        }
+    }
+}
+
+BM_DEV void bucket_wave_lists(int n, const int *sk, int32_t *__restrict__ counts,
+                              int32_t *__restrict__ offsets, int32_t *__restrict__ active,
+                              int32_t *__restrict__ n_active) {
+    const int lane = lane_id();
+    const uint64_t below = (1ull << lane) - 1ull;
+    bool lead[2];
+    int key[2];
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        const int r = lane + 64 * m;
+        key[m] = r < n ? sk[r] : -1;
+        lead[m] = r < n && (r == 0 || sk[r - 1] != key[m]);
+    }
+    const uint64_t L0 = __ballot(lead[0]), L1 = __ballot(lead[1]);
+    const int na = __popcll(L0) + __popcll(L1);
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        if (!lead[m]) continue;
+        const int r = lane + 64 * m;
+        const int slot = m == 0 ? __popcll(L0 & below) : __popcll(L0) + __popcll(L1 & below);
+        // next leader after r, else n
+        int next = n;
+        const uint64_t a0 = m == 0 ? (L0 & ~(below | (1ull << lane))) : 0ull;
+        const uint64_t a1 = m == 0 ? L1 : (L1 & ~(below | (1ull << lane)));
+        if (a0) next = (int)__builtin_ctzll(a0);
+        else if (a1) next = 64 + (int)__builtin_ctzll(a1);
+        active[slot] = key[m];
+        offsets[key[m]] = r;
+        counts[key[m]] = next - r;
+    }
+    if (lane == 0) *n_active = na;
+}
 
 // Single-workgroup bucketing of n <= a few thousand pairs (kBT threads):
 // counts, offsets, stable perm, active list [, row tiles].  smem must hold

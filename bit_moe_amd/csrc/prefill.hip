@@ -45,9 +45,9 @@ BM_DEV void iq2x_group_int_to_lds(const uint8_t *slab, int nb, int n, int kb, in
     uint32_t out[16];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const uint32_t F = ((j < 2 ? gw.x : gw.y) >> (16 * (j & 1))) & 0xFFFFu;
-        const uint32_t sig = iq2x_signs(F);
-        const uint2 row = sgrid[F >> 8];
+        const uint32_t R = iq2x_run(j < 2 ? gw.x : gw.y, j & 1);
+        const uint32_t sig = iq2x_run_signs(R);
+        const uint2 row = sgrid[iq2x_run_idx(R)];
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
             uint32_t m0 = ((i < 4 ? row.x : row.y) >> (8 * (i & 3))) & 0xFFu;

@@ -17,13 +17,16 @@ def _tiled_iq2x_numpy(canon, N, K):
     idx = grp[:, :, :, :4].astype(np.uint32)
     a = grp[:, :, :, 4:8].copy().view("<u4")[..., 0]
     s = a >> 28
-    fields = np.zeros((N, nb, 8, 4), dtype=np.uint32)
+    runs = np.zeros((N, nb, 8, 4), dtype=np.uint32)
     for j in range(4):
         s7 = (a >> (7 * j)) & 0x7F
         lo4 = s7 & 15
         par = (np.unpackbits(lo4.astype(np.uint8)[..., None], axis=-1).sum(-1) & 1).astype(np.uint32)
-        fields[..., j] = (idx[..., j] << 8) | ((s7 & 7) << 4) | (par << 7) | (((s7 >> 4) & 7) << 1) | ((s >> j) & 1)
-    qs = fields.astype("<u2").view(np.uint8).reshape(N, nb, 4, 16)      # 4 pieces of 16 bytes
+        runs[..., j] = (s7 & 7) | (par << 3) | (idx[..., j] << 4) | (((s7 >> 4) & 7) << 12)
+    words = np.zeros((N, nb, 8, 2), dtype=np.uint32)
+    words[..., 0] = (s & 3) | (runs[..., 0] << 2) | (runs[..., 1] << 17)
+    words[..., 1] = (s >> 2) | (runs[..., 2] << 2) | (runs[..., 3] << 17)
+    qs = words.astype("<u4").view(np.uint8).reshape(N, nb, 4, 16)       # 4 pieces of 16 bytes
     qs = qs.reshape(N // 64, 64, nb, 4, 16).transpose(0, 2, 3, 1, 4)     # [P][kb][c][r][16]
     dd = d.reshape(N // 64, 64, nb, 2).transpose(0, 2, 1, 3)             # [P][kb][r][2]
     return np.concatenate([qs.reshape(-1), dd.reshape(-1)])
