@@ -2,9 +2,9 @@
 """Throughput of the 2-bit routed-expert MoE layer on one MI355X.
 
 One step = one pass of the whole hot path over one batch held in HBM:
-router logits + top-k/renormalise (moe_route), then moe_ffn_decode
-(bucketing, fused IQ2X gate/up dequant-GEMV + SwiGLU, fused Q2K down
-dequant-GEMV, gate-weighted combine, bf16 shared expert).
+moe_forward_decode (router logits, top-k + renormalised softmax, bucketing,
+fused IQ2X gate/up dequant-GEMV + SwiGLU, fused Q2K down dequant-GEMV,
+gate-weighted combine, bf16 shared expert).
 
 Workload of the headline line: one decode token at DeepSeek-V4-Flash MoE
 shapes (H 7168, I 2048, 256 routed experts, top-8, one bf16 shared expert),
@@ -35,7 +35,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=8, help="layer copies rotated to defeat MALL")
     ap.add_argument("--prefill-steps", type=int, default=10)
-    ap.add_argument("--cpu-tokens", type=int, default=8, help="oracle sample size (tokens)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample size (seconds)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy of known size (counter calibration)")
+    ap.add_argument("--summarize-kernels", metavar="TRACE_DIR",
+                    help="print per-kernel durations of a rocprofv3 --kernel-trace run")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="print the per-kernel HBM traffic summary of four rocprofv3 --pmc runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the b16 and prefill lines")
     return ap.parse_args()
@@ -79,8 +85,8 @@ def time_steps(step, warmup, steps):
 
 
 def time_dominant(step, n):
-    """Average duration of the gate/up kernel, from HIP events the library
-    records around that launch on its stream."""
+    """Average duration of the gate/up kernel, from the HIP events that its
+    dispatch takes at kernel start and end (moe_set_timing_events)."""
     import torch
     import bit_moe_amd as bm
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
@@ -179,26 +185,140 @@ def prefill_2k(args, lays):
     return dict(ms=ms, flops=flops, gu_ms=gu_ms, gu_flops=gu_flops)
 
 
-def cpu_baseline(n_tokens):
+def cpu_baseline(target_s=15.0, max_tokens=400):
+    """The oracle (plain fp64 C, all host threads) on the decode workload,
+    one token at a time until about target_s seconds of oracle time: routing
+    and the layer per token.  Expert slabs are generated (untimed) before the
+    token that first uses them."""
     import numpy as np
     import oracle
     import synth
     w = synth.WORKLOADS["decode_b1"]
     L = synth.make_layer(w)
-    x, _ = synth.make_tokens(w.with_(T=n_tokens))
-    L.shared()
-    t0 = time.time()
-    for t in range(n_tokens):
-        ids, wt = oracle.route(x[t:t + 1], L.router(), w.k)
-        oracle.layer_ffn(L, x[t:t + 1], ids, wt)
-    dt = time.time() - t0
-    return dict(value=n_tokens / dt, unit="tokens/s", cores=oracle.max_threads(), kind="oracle",
-                sample=f"{n_tokens} decode tokens (route + 8 routed experts + shared expert each) "
-                       f"of the same 1-token workload, fp64, {dt:.1f}s")
+    x, _ = synth.make_tokens(w.with_(T=max_tokens))
+    grid, router, shared = L.grid(), L.router(), L.shared()
+    gate, up, down = {}, {}, {}
+    spent, n = 0.0, 0
+    while n < max_tokens and (spent < target_s or n < 4):
+        xt = x[n:n + 1]
+        t0 = time.perf_counter()
+        ids, wt = oracle.route(xt, router, w.k)
+        spent += time.perf_counter() - t0
+        for e in (int(v) for v in np.unique(ids)):
+            if e not in gate:
+                gate[e], up[e], down[e] = L.gate(e), L.up(e), L.down(e)
+        t0 = time.perf_counter()
+        oracle.moe_ffn(w.H, w.I, w.E, w.k, grid, gate, up, down, shared, xt, ids, wt)
+        spent += time.perf_counter() - t0
+        n += 1
+    return dict(value=n / spent, unit="tokens/s", cores=oracle.max_threads(), kind="oracle",
+                sample=f"{n} decode tokens of the batch-1 workload (routing + 8 routed experts + "
+                       f"shared expert each, fp64), {spent:.1f} s of oracle time")
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling the FETCH_SIZE and
+    WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def _pmc_per_kernel(dirname, counter):
+    """{kernel name: average counter value per dispatch} from a rocprofv3
+    --pmc output directory (sqlite database)."""
+    import glob
+    import sqlite3
+    out = {}
+    for db in glob.glob(os.path.join(dirname, "**", "*.db"), recursive=True):
+        c = sqlite3.connect(db)
+        q = ("select kernel_name, value from counters_collection where counter_name = ?")
+        acc = {}
+        for name, v in c.execute(q, (counter,)):
+            acc.setdefault(name, []).append(v)
+        for name, vs in acc.items():
+            out[name] = sum(vs) / len(vs)
+    return out
+
+
+def source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode.hip", "common.h", "device_util.h"):
+        with open(os.path.join(ROOT, "bit_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def summarize_traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes):
+    """Text summary: HBM bytes per dispatch of each decode kernel, the
+    counters scaled by what they read for the plain copy."""
+    fetch, write = _pmc_per_kernel(fetch_dir, "FETCH_SIZE"), _pmc_per_kernel(write_dir, "WRITE_SIZE")
+    cf = max(v for k, v in _pmc_per_kernel(cfetch_dir, "FETCH_SIZE").items() if "copyBuffer" in k)
+    cw = max(v for k, v in _pmc_per_kernel(cwrite_dir, "WRITE_SIZE").items() if "copyBuffer" in k)
+    f_scale, w_scale = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    lines = [f"source_digest {source_digest()}",
+             f"copy_calibration bytes {copy_bytes} FETCH_SIZE_KiB {cf:.1f} WRITE_SIZE_KiB {cw:.1f} "
+             f"fetch_scale {f_scale:.4f} write_scale {w_scale:.4f}"]
+    for k in sorted(fetch):
+        if "k_dec" not in k:
+            continue
+        fb, wb = fetch[k] * 1024.0 * f_scale, write.get(k, 0.0) * 1024.0 * w_scale
+        name = k[k.index("k_dec"):].split("(")[0].replace(" ", "")
+        lines.append(f"kernel {name} fetch_bytes {fb:.0f} write_bytes {wb:.0f} "
+                     f"traffic_bytes {fb + wb:.0f}")
+    return "\n".join(lines)
+
+
+def summarize_kernels(trace_dir):
+    """Per-kernel launch count and average / min / max duration (us) from a
+    rocprofv3 --kernel-trace output directory, grouped by name and grid."""
+    import glob
+    import sqlite3
+    rows = {}
+    for db in glob.glob(os.path.join(trace_dir, "**", "*.db"), recursive=True):
+        c = sqlite3.connect(db)
+        for name, gx, n, avg, mn, mx in c.execute(
+                "select name, grid_x, count(*), avg(end - start), min(end - start), max(end - start) "
+                "from kernels group by name, grid_x"):
+            rows[(name, gx)] = (n, avg / 1e3, mn / 1e3, mx / 1e3)
+    out = [f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'grid':>10}  kernel"]
+    for (name, gx), (n, avg, mn, mx) in sorted(rows.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        short = name[name.index("k_"):].split("(")[0] if "k_" in name else name.split("(")[0]
+        out.append(f"{n:6d} {avg:10.2f} {mn:10.2f} {mx:10.2f} {gx:10d}  {short}")
+    return "\n".join(out)
+
+
+def traffic_from_profile(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when the decode sources have changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", "traffic_k_dec_decode_b1.txt")
+    if not os.path.exists(p):
+        return None
+    lines = open(p).read().splitlines()
+    dig = [l.split()[1] for l in lines if l.startswith("source_digest")]
+    if not dig or dig[0] != source_digest():
+        return None
+    for l in lines:
+        f = l.split()
+        if f and f[0] == "kernel" and f[1] == kernel:
+            return float(f[f.index("traffic_bytes") + 1])
+    return None
 
 
 def main():
     args = parse()
+    if args.summarize_kernels:
+        print(summarize_kernels(args.summarize_kernels))
+        return
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic, copy_bytes=1 << 30))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               f"multi-GPU path. Run with --gpus 1.", file=sys.stderr)
@@ -208,13 +328,16 @@ def main():
     import synth
     bm.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     w = synth.WORKLOADS["decode_b1"]
     L, lays = build_layer(w, args.copies)
     r = decode_b1(args, L, lays)
     log(f"[bench] decode_b1 {r['ms'] * 1e3:.1f} us/step, gate/up {r['gu_ms'] * 1e3:.1f} us")
     gu_bw = r["gu_bytes"] / (r["gu_ms"] * 1e-3)
     out = {
-        "metric": "MoE-layer tokens/s (decode, batch 1)",
+        "metric": "MoE-layer tokens/s: decode HBM GB/s (%peak) + prefill MFMA TFLOP/s (%peak)",
         "value": 1.0 / (r["ms"] * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -233,7 +356,7 @@ def main():
                    "step_hbm_GBps": r["step_bytes"] / (r["ms"] * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "kernel": "k_dec_gateup",
                      "achieved": gu_bw / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": gu_bw / HBM_PEAK, "traffic": None,
+                     "frac": gu_bw / HBM_PEAK, "traffic": traffic_from_profile("k_dec_gateup<1,0>"),
                      "kernel_us": r["gu_ms"] * 1e3, "algorithmic_bytes": r["gu_bytes"]},
     }
     if not args.no_extra:
@@ -255,7 +378,7 @@ def main():
                              "gateup_mfma_frac": pf["gu_flops"] / (pf["gu_ms"] * 1e-3) / BF16_PEAK}
         log(f"[bench] prefill_2k {pf['ms']:.2f} ms/step")
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
         log(f"[bench] cpu baseline {out['cpu_baseline']['value']:.3f} tokens/s")
     print(json.dumps(out), flush=True)
 

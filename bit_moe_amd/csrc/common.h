@@ -254,17 +254,11 @@ int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T,
                        const Buckets &b, int max_tiles, uint16_t *xb, uint16_t *h,
                        float *o, float *hs, float *os, hipStream_t s);
 
-// events recorded around the gate/up launch (moe_set_timing_events)
+// events taken at the start and end of the gate/up launch (moe_set_timing_events)
 struct TimingEvents {
     hipEvent_t start = nullptr, stop = nullptr;
 };
 TimingEvents &timing_events();
-inline void timing_begin(hipStream_t s) {
-    if (timing_events().start) (void)hipEventRecord(timing_events().start, s);
-}
-inline void timing_end(hipStream_t s) {
-    if (timing_events().stop) (void)hipEventRecord(timing_events().stop, s);
-}
 
 }  // namespace bm_host
 

@@ -26,6 +26,8 @@
 // so one 16-byte load by 64 lanes is one contiguous 1 KiB access; the waves
 // of a workgroup split K and meet once in LDS.  Activations are identical
 // for all lanes and arrive through wave-uniform (scalar) loads.
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 #include "device_util.h"
@@ -471,8 +473,16 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
     __shared__ SmallRoute sr;
     const int32_t *counts = bk.counts, *offsets = bk.offsets, *perm = bk.perm, *active = bk.active;
     int na;
+    bool copy_tab = true;
     if (!MULTI && route_mode) {
+        // the decode tables are fetched while the batch is routed
+        static_assert(kTabDw / 4 == 2 * kWG * 64, "two table pieces per thread");
+        const uint4 ta = gtab[threadIdx.x], tb = gtab[threadIdx.x + kWG * 64];
         route_in_wg(route_mode, E, k, T, logits, ids, w, bk, sr);
+        tab[threadIdx.x] = ta;
+        tab[threadIdx.x + kWG * 64] = tb;
+        __syncthreads();
+        copy_tab = false;
         counts = sr.counts;
         offsets = sr.offsets;
         perm = sr.perm;
@@ -491,7 +501,7 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
         tk.cnt = counts[tk.e];
         if ((tk.cnt > 1) != (MULTI != 0)) return;
         if (!MULTI) {
-            routed_gateup_pass<XBF16, 1>(H, I, k, tk, 0, P, tab, gtab, true, gate, up, x, xs, perm, h, hrows,
+            routed_gateup_pass<XBF16, 1>(H, I, k, tk, 0, P, tab, gtab, copy_tab, gate, up, x, xs, perm, h, hrows,
                                          hsum, red);
             return;
         }
@@ -807,17 +817,19 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     }
     // routed gate/up; experts chosen by several tokens in a second launch
     const int n_gwg = p.slots * (I / 64);
-    timing_begin(s);
     const int route_mode = p.small ? (p.n_rwg ? 1 : 2) : 0;
     for (int multi = 0; multi < (T > 1 ? 2 : 1); multi++) {
         auto kg = multi ? (bf ? k_dec_gateup<1, 1> : k_dec_gateup<0, 1>)
                         : (bf ? k_dec_gateup<1, 0> : k_dec_gateup<0, 0>);
-        kg<<<n_gwg, kWG * 64, 0, s>>>(H, I, E, k, T, n_gwg, multi ? 0 : route_mode, (const uint8_t *)L->gate_q,
-                                      (const uint8_t *)L->up_q, (const uint4 *)b.tab, x, b.xs, b.logits, b.ids,
-                                      b.w, b.bk, b.h, b.hsum);
+        // the timing events, when set, are taken by the dispatch itself
+        // around the first gate/up launch
+        const TimingEvents ev = multi ? TimingEvents{} : timing_events();
+        hipExtLaunchKernelGGL(kg, dim3(n_gwg), dim3(kWG * 64), 0, s, ev.start, ev.stop, 0, H, I, E, k, T, n_gwg,
+                              multi ? 0 : route_mode, (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q,
+                              (const uint4 *)b.tab, x, (const float *)b.xs, (const float *)b.logits, b.ids, b.w,
+                              b.bk, b.h, b.hsum);
         BM_LAUNCH_CHECK();
     }
-    timing_end(s);
     // down || shared down; the last workgroup to finish a panel combines it
     const int n_dwg = p.slots * (H / 64);
     const int n_sd = shared ? (H / 64) * p.kc_sd : 0;

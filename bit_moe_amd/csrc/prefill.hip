@@ -11,6 +11,8 @@
 //           of the N tile, epilogue h = silu(g) * u (bf16, bucket order).
 //  down:    A = h rows of the tile (contiguous), B = Q2K rows, epilogue
 //           writes o[pair][n] (fp32); k_combine applies the routing weights.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace {
@@ -383,17 +385,16 @@ int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T,
     (void)ids; (void)xb;
     const int H = L->H, I = L->I, k = L->k;
     dim3 g1(I / 64, max_tiles);
-    timing_begin(s);
-    if (x_dtype == BITMOE_BF16)
-        k_prefill_gateup<1><<<g1, 256, 0, s>>>(H, I, k, (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q,
-                                               (const uint8_t *)L->grid, x, b.counts, b.offsets, b.perm,
-                                               b.tiles, b.n_tiles, h);
-    else
-        k_prefill_gateup<0><<<g1, 256, 0, s>>>(H, I, k, (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q,
-                                               (const uint8_t *)L->grid, x, b.counts, b.offsets, b.perm,
-                                               b.tiles, b.n_tiles, h);
-    BM_LAUNCH_CHECK();
-    timing_end(s);
+    {
+        // the timing events, when set, are taken by the dispatch itself
+        const TimingEvents ev = timing_events();
+        auto kg = x_dtype == BITMOE_BF16 ? k_prefill_gateup<1> : k_prefill_gateup<0>;
+        hipExtLaunchKernelGGL(kg, g1, dim3(256), 0, s, ev.start, ev.stop, 0, H, I, k, (const uint8_t *)L->gate_q,
+                              (const uint8_t *)L->up_q, (const uint8_t *)L->grid, x, (const int32_t *)b.counts,
+                              (const int32_t *)b.offsets, (const int32_t *)b.perm, (const int32_t *)b.tiles,
+                              (const int32_t *)b.n_tiles, h);
+        BM_LAUNCH_CHECK();
+    }
     dim3 g2(H / 64, max_tiles);
     k_prefill_down<<<g2, 256, 0, s>>>(H, I, (const uint8_t *)L->down_q, h, b.counts, b.offsets, b.perm,
                                       b.tiles, b.n_tiles, o);

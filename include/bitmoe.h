@@ -60,11 +60,15 @@
  *     [0, 64*N*nb):           piece c (groups 2c, 2c+1 of block (n,kb)) at
  *                             ((P*nb + kb)*4 + c)*64 + r, 16 bytes each; each
  *                             group re-encoded (bijectively, same 8 bytes) as
- *                             four little-endian 16-bit fields, one per run j
- *                             of 8 weights: bit 0 bit j of the group scale s;
- *                             bits 1-3 signs of weights 4,5,6; bits 4-6 signs
- *                             of weights 0,1,2; bit 7 parity of the signs of
- *                             weights 0..3; bits 8-15 the codebook index
+ *                             two little-endian words, W0 for runs 0,1 and W1
+ *                             for runs 2,3 (a run is 8 weights): bits 0-1 of
+ *                             W0 / W1 are bits 0-1 / 2-3 of the group scale s;
+ *                             the first run of a word is the 15-bit field R
+ *                             at bits 2-16, the second at bits 17-31.  In R:
+ *                             bits 0-2 the signs of weights 0,1,2, bit 3 the
+ *                             parity of the signs of weights 0..3, bits 4-11
+ *                             the codebook index, bits 12-14 the signs of
+ *                             weights 4,5,6 (weight 7: even parity of the 8)
  *     [64*N*nb, 66*N*nb):     d of block (n,kb) at (P*nb + kb)*64 + r, 2 bytes
  *   Q2K slab (N*nb*84 bytes):
  *     [0, 64*N*nb):           qs piece c (bytes 16+16c..31+16c) as above
@@ -105,7 +109,10 @@ typedef struct bitmoe_layer {
     const void *gate_q;        /* TILED IQ2X, E slabs of I*(H/256)*66 bytes */
     const void *up_q;          /* TILED IQ2X, same shape as gate_q */
     const void *down_q;        /* TILED Q2K, E slabs of H*(I/256)*84 bytes */
-    const void *grid;          /* uint8 [256][8] codebook magnitudes */
+    const void *grid;          /* uint8 [256][8] codebook magnitudes; the FFN
+                                  entry points require values 0..7 (the
+                                  format's codebook is {1,3,5,7}); the
+                                  dequant entry point takes any byte */
     const void *shared_gate;   /* TILED bf16 [I][H], or NULL: no shared expert */
     const void *shared_up;     /* TILED bf16 [I][H] (NULL iff shared_gate is) */
     const void *shared_down;   /* TILED bf16 [H][I] (NULL iff shared_gate is) */
@@ -169,8 +176,9 @@ int moe_ffn_prefill(const bitmoe_layer *L, const void *x, int x_dtype, int T,
 
 /*
  * The whole layer for a decode batch: moe_route followed by moe_ffn_decode
- * in one call.  For T <= 16 the router rows, the shared expert and the
- * bookkeeping share launches with the expert GEMVs (four launches in all).
+ * in one call.  For T <= 16 and T*k <= 128 the router rows, the shared expert
+ * and the bookkeeping share launches with the expert GEMVs (three launches
+ * in all; more for larger batches).
  * ids int32 [T][k] and w float32 [T][k] receive the routing (same values as
  * moe_route); y float32 [T][H] as moe_ffn_decode.  Needs L->router_w.
  * ws: at least moe_workspace_bytes(L, T, BITMOE_DECODE) bytes.
@@ -201,11 +209,13 @@ int moe_pack_bf16(const void *src, void *dst, int N, int K, void *stream);
 
 /*
  * Measurement hook.  When start and stop are both hipEvent_t handles (passed
- * as void*), every later moe_ffn_decode / moe_ffn_prefill call made from the
- * calling thread records `start` on its stream just before launching the
- * gate/up projection kernel (the kernel that moves most of the bytes) and
- * `stop` just after it, so hipEventElapsedTime gives that kernel's duration.
- * Pass NULL, NULL to turn it off.  The setting is per host thread.
+ * as void*), every later decode or prefill FFN call made from the calling
+ * thread launches its routed gate/up projection kernel with hipExtLaunchKernel
+ * and these events, which the dispatch itself takes when the kernel starts
+ * and when it ends, so hipEventElapsedTime gives that kernel's duration
+ * (for a decode batch with experts chosen by several tokens, the first of
+ * its two gate/up launches).  Pass NULL, NULL to turn it off.  The setting
+ * is per host thread.
  */
 int moe_set_timing_events(void *start, void *stop);
 
