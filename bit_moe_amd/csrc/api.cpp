@@ -92,14 +92,16 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
         const bm_host::DecodePlan p = bm_host::decode_plan(L, T, false);
         bm_host::DecodeBufs &d = f.d;
         d.logits = c.take<float>((int64_t)T * L->E);
-        d.h = c.take<uint16_t>(2 * n * L->I);
-        d.hsum = c.take<float>(n * (L->I / 16));
+        d.h = c.take<uint16_t>(n * L->I);
+        d.hsum2 = c.take<float2>(n * (L->I / 16));
+        d.hscale = c.take<float>(n * (L->I / 64));
         d.o = c.take<float>(n * L->H);
         d.ycount = c.take<int32_t>(L->H / 64);
         d.tab = c.take<uint4>(2 * 4096 / 4);
         d.xs = c.take<float>((int64_t)T * (L->H / 32));
         if (shared) {
             d.sgp = c.take<float>((int64_t)p.kc_sg * 2 * T * L->I);
+            d.hs = c.take<uint16_t>(2 * (int64_t)T * L->I);
             d.osp = c.take<float>((int64_t)p.kc_sd * T * L->H);
         }
         d.bk = f.b;

@@ -38,6 +38,12 @@ BM_DEV float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                            __builtin_bit_cast(bf16x2, b), acc, false);
 }
 
+// Packed fp16 pair dot product with fp32 accumulation (v_dot2_f32_f16).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+BM_DEV float dot2_f16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+}
+
 // ---- wave helpers -------------------------------------------------------
 
 BM_DEV int lane_id() { return __lane_id(); }
@@ -46,6 +52,19 @@ BM_DEV float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
     return v;
+}
+
+// Sum over each row of 16 lanes (DPP row shifts; out-of-row sources read 0),
+// complete in lane 15 of the row.
+template <int CTRL>
+BM_DEV float dpp_shr_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+BM_DEV float row16_sum(float v) {
+    v = dpp_shr_add<0x111>(v);
+    v = dpp_shr_add<0x112>(v);
+    v = dpp_shr_add<0x114>(v);
+    return dpp_shr_add<0x118>(v);
 }
 
 BM_DEV float silu(float z) { return z / (1.0f + __expf(-z)); }
@@ -126,6 +145,44 @@ BM_DEV uint32_t iq2x_tab_entry(const uint8_t *__restrict__ grid, int which, uint
 // the two bf16 pairs (24 + w0, 24 + w1), (24 + w2, 24 + w3) of a table entry
 BM_DEV uint32_t iq2x_pair_lo(uint32_t e) { return __builtin_amdgcn_perm(kIq2xHiBytes, e, 0x04010400u); }
 BM_DEV uint32_t iq2x_pair_hi(uint32_t e) { return __builtin_amdgcn_perm(kIq2xHiBytes, e, 0x04030402u); }
+
+// ---- tiled Q2K quant words -------------------------------------------------
+// A tiled Q2K sub-block (16 weights) is one little-endian word: the 2-bit
+// quants of the even-indexed weights 0,2,..,14 at bits 0-15 (weight 2p at
+// bits 2p), those of the odd-indexed ones at bits 16-31 (weight 2p+1 at
+// bits 16+2p).  Piece c (16 bytes) of a block holds sub-blocks 4c..4c+3.
+BM_DEV uint32_t q2k_word_quant(uint32_t W, int i) { return (W >> (16 * (i & 1) + (i & ~1))) & 3u; }
+// Weights 2p, 2p+1 of word W as the fp16 pair (B_p + q_2p, B_p + q_2p+1),
+// B_p = 2^(10 - 2s), s = p for p < 5, else p - 5 (taken from W >> 10): the
+// quants sit in the mantissa where one unit is 1, so only a mask and an OR
+// are needed.  W10 = W >> 10.
+template <int PAIR>
+BM_DEV uint32_t q2k_pair_f16(uint32_t W, uint32_t W10) {
+    constexpr int s = PAIR < 5 ? PAIR : PAIR - 5;
+    constexpr uint32_t base = (uint32_t)(25 - 2 * s) << 10;     // fp16 bits of 2^(10 - 2s)
+    return ((PAIR < 5 ? W : W10) & (0x00030003u << (2 * s))) | base | (base << 16);
+}
+// The 5 masks and 5 bases of q2k_pair_f16 held in registers, so that each
+// pair is one v_and_or_b32 (a three-operand op takes no two literals).
+struct Q2kPairConsts {
+    uint32_t mask[5], base[5];
+    BM_DEV Q2kPairConsts() {
+#pragma unroll
+        for (int s = 0; s < 5; s++) {
+            uint32_t m = 0x00030003u << (2 * s), b = ((uint32_t)(25 - 2 * s) << 10) * 0x10001u;
+            asm volatile("" : "+v"(m));
+            asm volatile("" : "+s"(b));
+            mask[s] = m;
+            base[s] = b;
+        }
+    }
+    template <int PAIR>
+    BM_DEV uint32_t pair(uint32_t W, uint32_t W10) const {
+        constexpr int s = PAIR < 5 ? PAIR : PAIR - 5;
+        return ((PAIR < 5 ? W : W10) & mask[s]) | base[s];
+    }
+};
+constexpr float q2k_pair_bias(int pair) { return (float)(1 << (10 - 2 * (pair < 5 ? pair : pair - 5))); }
 
 // ---- small-T router row: one wave per expert row, lanes across K ---------
 // The row is read in chunks (up to 8 loads of 16 bytes per lane, all in
@@ -234,8 +291,10 @@ struct DecodeBufs {
     float *w;               // [T][k]
     Buckets bk;
     float *sgp;             // [kc_sg][2][T][I] shared gate/up partial sums
-    uint16_t *h;            // [2][T*k][I] routed h as bf16 hi, lo (bucket order, quads [0,2,1,3])
-    float *hsum;            // [T*k][I/16]
+    uint16_t *hs;           // [2][T][I] shared h as bf16 hi, lo
+    uint16_t *h;            // [T*k][I] routed h as fp16, scaled per 64 columns (bucket order)
+    float2 *hsum2;          // [T*k][I/16] per 16 columns: {sum h, sum B_p h} of the scaled fp16 h
+    float *hscale;          // [T*k][I/64] the power of two that undoes the scaling
     float *o;               // [T*k][H] routed down outputs, pair order
     float *osp;             // [kc_sd][T][H] shared down partial sums
     int32_t *ycount;        // [H/64] finished down workgroups per panel

@@ -38,6 +38,8 @@ using namespace bm;
 
 constexpr int kW = 8;              // waves per workgroup
 constexpr int kWG = 16;            // waves per routed gate/up workgroup
+constexpr int kWD = 4;             // waves per down workgroup: every down workgroup of a decode
+                                   // batch is resident at once
 constexpr int kNT = 4;             // tokens per pass over the weights
 constexpr int kMaxChunks = 8;      // K chunks of the shared expert, at most
 constexpr int kMaxExperts = 1024;
@@ -308,8 +310,8 @@ BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P
                                const uint8_t *__restrict__ gate, const uint8_t *__restrict__ up,
                                const void *__restrict__ x, const float *__restrict__ xs,
                                const int32_t *perm,
-                               uint16_t *__restrict__ h, int64_t hrows, float *__restrict__ hsum,
-                               float *red) {
+                               uint16_t *__restrict__ h, float2 *__restrict__ hsum2,
+                               float *__restrict__ hscale, float *red) {
     const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int tok[NT];
 #pragma unroll
@@ -391,20 +393,21 @@ BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P
         const float hv = silu(g) * u;
         const int n = P * 64 + lane;
         const int64_t row = tk.off + t0 + wv;
-        // h as bf16 hi + lo (about 16 significant bits); within every aligned
-        // quad the order is [0, 2, 1, 3] so that the down kernel's bf16 pairs
-        // line up with pairs of 2-bit quants taken from bytes (0, 2), (1, 3)
-        const uint32_t hi = f32_to_bf16_rne(hv);
-        const uint32_t lo = f32_to_bf16_rne(hv - bf16_to_f32(hi));
-        const int pn = (n & ~3) | ((n & 1) << 1) | ((n >> 1) & 1);
-        h[row * I + pn] = (uint16_t)hi;
-        h[((int64_t)row + hrows) * I + pn] = (uint16_t)lo;
-        float s = bf16_to_f32(hi) + bf16_to_f32(lo);
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        s += __shfl_xor(s, 4, 64);
-        s += __shfl_xor(s, 8, 64);
-        if ((lane & 15) == 0) hsum[row * (I / 16) + (n >> 4)] = s;
+        // fp16 h scaled by 2^-e so that the panel's largest |h| lies in
+        // [2^14, 2^15): no overflow, full fp16 precision; 2^e is kept
+        const float amax = wave_max_f32(fabsf(hv));
+        int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 14 : 0;
+        e = max(-100, min(100, e));
+        const float inv = __uint_as_float((uint32_t)(127 - e) << 23), scl = __uint_as_float((uint32_t)(127 + e) << 23);
+        const _Float16 hf = (_Float16)(hv * inv);
+        h[row * I + n] = __builtin_bit_cast(uint16_t, hf);
+        // per 16 columns: sum of h and sum of B_p h, B_p the bias of the
+        // pair that column n % 16 falls in
+        const float v = (float)hf;
+        const int pp = (n & 15) >> 1;
+        const float hs = row16_sum(v), hb = row16_sum(q2k_pair_bias(pp) * v);
+        if ((lane & 15) == 15) hsum2[row * (I / 16) + (n >> 4)] = make_float2(hs, hb);
+        if (lane == 0) hscale[row * (I / 64) + P] = scl;
     }
     __syncthreads();
 }
@@ -466,8 +469,25 @@ __global__ void __launch_bounds__(kWG * 64)
 k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const uint8_t *__restrict__ gate,
              const uint8_t *__restrict__ up, const uint4 *__restrict__ gtab,
              const void *__restrict__ x, const float *__restrict__ xs, const float *__restrict__ logits,
-             int32_t *ids, float *w, bm_host::Buckets bk, uint16_t *__restrict__ h, float *__restrict__ hsum) {
-    const int64_t hrows = (int64_t)T * k;
+             int32_t *ids, float *w, bm_host::Buckets bk, uint16_t *__restrict__ h, float2 *__restrict__ hsum2,
+             float *__restrict__ hscale, int kc_sg, const float *__restrict__ sgp, uint16_t *__restrict__ hs) {
+    if (!MULTI && (int)blockIdx.x >= n_gwg) {
+        // shared h = silu(sum of the gate partials) * (sum of the up
+        // partials), in a fixed order, as bf16 hi + lo for the down launch
+        const int64_t n = (int64_t)T * I;
+        const int64_t i = (int64_t)(blockIdx.x - n_gwg) * blockDim.x + threadIdx.x;
+        if (i >= n) return;
+        float g = 0.f, u = 0.f;
+        for (int c = 0; c < kc_sg; c++) {
+            g += sgp[(int64_t)(2 * c) * n + i];
+            u += sgp[(int64_t)(2 * c + 1) * n + i];
+        }
+        const float hv = silu(g) * u;
+        const uint32_t hi = f32_to_bf16_rne(hv);
+        hs[i] = (uint16_t)hi;
+        hs[n + i] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
+        return;
+    }
     __shared__ uint4 tab[kTabDw / 4];
     __shared__ float red[kWG * (MULTI ? kNT : 1) * 2 * 64];
     __shared__ SmallRoute sr;
@@ -501,17 +521,17 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
         tk.cnt = counts[tk.e];
         if ((tk.cnt > 1) != (MULTI != 0)) return;
         if (!MULTI) {
-            routed_gateup_pass<XBF16, 1>(H, I, k, tk, 0, P, tab, gtab, copy_tab, gate, up, x, xs, perm, h, hrows,
-                                         hsum, red);
+            routed_gateup_pass<XBF16, 1>(H, I, k, tk, 0, P, tab, gtab, copy_tab, gate, up, x, xs, perm, h, hsum2,
+                                         hscale, red);
             return;
         }
         for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
             if (tk.cnt - t0 == 1)
                 routed_gateup_pass<XBF16, 1>(H, I, k, tk, t0, P, tab, gtab, t0 == 0, gate, up, x, xs, perm, h,
-                                             hrows, hsum, red);
+                                             hsum2, hscale, red);
             else
                 routed_gateup_pass<XBF16, kNT>(H, I, k, tk, t0, P, tab, gtab, t0 == 0, gate, up, x, xs, perm,
-                                               h, hrows, hsum, red);
+                                               h, hsum2, hscale, red);
         }
         return;
     }
@@ -521,11 +541,15 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
 // down: routed Q2K down per (slot, panel) || shared down split over K.
 // grid = slots*(H/64) + (H/64)*kc_sd.  o[pair][H] unweighted.
 // ---------------------------------------------------------------------------
+// Routed Q2K down of panel P for the pair rows of tokens t0..t0+NT-1 of
+// expert tk.  h arrives as fp16 scaled per 64 columns (hscale), with per-16
+// sums hs and bias-weighted sums hb (hsum2 = {hs, hb}); each sub-block is 8
+// fp16 dot products of (B_p + q) pairs, then sc*(S - hb) and m*hs.
 template <int NT>
 BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
                              const uint8_t *__restrict__ down, const int32_t *__restrict__ perm,
-                             const uint16_t *__restrict__ h, int64_t hrows,
-                             const float *__restrict__ hsum, float *__restrict__ o, float *red) {
+                             const uint16_t *__restrict__ h, const float2 *__restrict__ hsum2,
+                             const float *__restrict__ hscale, float *__restrict__ o, float *red) {
     const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int rows[NT];
 #pragma unroll
@@ -539,55 +563,66 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
     const uint4 *dq = reinterpret_cast<const uint4 *>(D);
     const uint4 *ds = reinterpret_cast<const uint4 *>(D + S * 64);
     const uint32_t *dd = reinterpret_cast<const uint32_t *>(D + S * 80);
+    const Q2kPairConsts qc;
     int kb0, kb1;
-    split_range(nb, kW, wv, kb0, kb1);
-    for (int kb = kb0; kb < kb1; kb++) {
+    split_range(nb, kWD, wv, kb0, kb1);
+    // the next superblock is in flight while one is decoded
+    uint4 q4[4], nq4[4], sc4 = make_uint4(0, 0, 0, 0), nsc4 = sc4;
+    uint32_t dm = 0, ndm = 0;
+    auto load = [&](int kb, uint4 (&q)[4], uint4 &sc, uint32_t &dmv) {
         const int64_t pk = (int64_t)P * nb + kb;
-        uint4 q4[4];
 #pragma unroll
-        for (int c = 0; c < 4; c++) q4[c] = dq[(pk * 4 + c) * 64 + lane];
-        const uint4 sc4 = ds[pk * 64 + lane];
-        const uint32_t dm = dd[pk * 64 + lane];
+        for (int c = 0; c < 4; c++) q[c] = dq[(pk * 4 + c) * 64 + lane];
+        sc = ds[pk * 64 + lane];
+        dmv = dd[pk * 64 + lane];
+    };
+    if (kb0 < kb1) load(kb0, q4, sc4, dm);
+    for (int kb = kb0; kb < kb1; kb++) {
+        if (kb + 1 < kb1) load(kb + 1, nq4, nsc4, ndm);
         const float d = fp16_to_f32(dm & 0xFFFFu), dmin = fp16_to_f32(dm >> 16);
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const int hh = c >> 1, l0 = 16 * (c & 1);
+        for (int c = 0; c < 4; c++) {                 // 64 columns: sub-blocks 4c..4c+3
             const uint32_t qw[4] = {q4[c].x, q4[c].y, q4[c].z, q4[c].w};
+            const uint32_t scw = c == 0 ? sc4.x : c == 1 ? sc4.y : c == 2 ? sc4.z : sc4.w;
+            const uint32_t scl = scw & 0x0F0F0F0Fu, mnb = (scw >> 4) & 0x0F0F0F0Fu;
+            const int col = kb * kQK + 64 * c;
+            float a1[NT], a2[NT];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int b = 8 * hh + 2 * j + (c & 1);
-                const uint32_t scw = (b < 4) ? sc4.x : (b < 8) ? sc4.y : (b < 12) ? sc4.z : sc4.w;
-                const uint32_t sb = (scw >> (8 * (b & 3))) & 0xFFu;
-                const float dsc = d * (float)(sb & 15u), dmm = dmin * (float)(sb >> 4);
-                const int kcol = kb * kQK + 128 * hh + 32 * j + l0;
-                // (128 + q) as bf16 pairs from quant bytes (0,2) and (1,3)
-                uint32_t qp[8];
+            for (int t = 0; t < NT; t++) a1[t] = a2[t] = 0.f;
 #pragma unroll
-                for (int w4 = 0; w4 < 4; w4++) {
-                    const uint32_t t4 = qw[w4] >> (2 * j);
-                    qp[2 * w4] = (t4 & 0x00030003u) | 0x43004300u;
-                    qp[2 * w4 + 1] = ((t4 >> 8) & 0x00030003u) | 0x43004300u;
-                }
+            for (int i = 0; i < 4; i++) {
+                const uint32_t W = qw[i], W10 = W >> 10;
+                const uint32_t pr[8] = {qc.pair<0>(W, W10), qc.pair<1>(W, W10), qc.pair<2>(W, W10),
+                                        qc.pair<3>(W, W10), qc.pair<4>(W, W10), qc.pair<5>(W, W10),
+                                        qc.pair<6>(W, W10), qc.pair<7>(W, W10)};
+                const float scf = (float)((scl >> (8 * i)) & 0xFFu), mf = (float)((mnb >> (8 * i)) & 0xFFu);
 #pragma unroll
                 for (int t = 0; t < NT; t++) {
-                    const uint4 *hp = reinterpret_cast<const uint4 *>(h + (int64_t)rows[t] * I + kcol);
-                    const uint4 *lp = reinterpret_cast<const uint4 *>(h + ((int64_t)rows[t] + hrows) * I + kcol);
-                    const uint4 a0 = hp[0], a1 = hp[1], b0 = lp[0], b1 = lp[1];
-                    float sacc = dot2_bf16(qp[0], a0.x, 0.f);
-                    sacc = dot2_bf16(qp[0], b0.x, sacc);
-                    sacc = dot2_bf16(qp[1], a0.y, sacc); sacc = dot2_bf16(qp[1], b0.y, sacc);
-                    sacc = dot2_bf16(qp[2], a0.z, sacc); sacc = dot2_bf16(qp[2], b0.z, sacc);
-                    sacc = dot2_bf16(qp[3], a0.w, sacc); sacc = dot2_bf16(qp[3], b0.w, sacc);
-                    sacc = dot2_bf16(qp[4], a1.x, sacc); sacc = dot2_bf16(qp[4], b1.x, sacc);
-                    sacc = dot2_bf16(qp[5], a1.y, sacc); sacc = dot2_bf16(qp[5], b1.y, sacc);
-                    sacc = dot2_bf16(qp[6], a1.z, sacc); sacc = dot2_bf16(qp[6], b1.z, sacc);
-                    sacc = dot2_bf16(qp[7], a1.w, sacc); sacc = dot2_bf16(qp[7], b1.w, sacc);
-                    // sum (128+q) h = 128 hsum + sum q h
-                    const float hsb = hsum[(int64_t)rows[t] * (I / 16) + (kcol >> 4)];
-                    acc[t] = fmaf(dsc, sacc, fmaf(-fmaf(128.f, dsc, dmm), hsb, acc[t]));
+                    const uint4 *hp = reinterpret_cast<const uint4 *>(h + (int64_t)rows[t] * I + col + 16 * i);
+                    const uint4 x0 = hp[0], x1 = hp[1];
+                    float sacc = dot2_f16(pr[0], x0.x, 0.f);
+                    sacc = dot2_f16(pr[1], x0.y, sacc);
+                    sacc = dot2_f16(pr[2], x0.z, sacc);
+                    sacc = dot2_f16(pr[3], x0.w, sacc);
+                    sacc = dot2_f16(pr[4], x1.x, sacc);
+                    sacc = dot2_f16(pr[5], x1.y, sacc);
+                    sacc = dot2_f16(pr[6], x1.z, sacc);
+                    sacc = dot2_f16(pr[7], x1.w, sacc);
+                    const float2 sb = hsum2[(int64_t)rows[t] * (I / 16) + (col >> 4) + i];   // {hs, hb}
+                    a1[t] = fmaf(scf, sacc - sb.y, a1[t]);
+                    a2[t] = fmaf(mf, sb.x, a2[t]);
                 }
             }
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                const float hsc = hscale[(int64_t)rows[t] * (I / 64) + (col >> 6)];
+                acc[t] = fmaf(hsc, fmaf(d, a1[t], -dmin * a2[t]), acc[t]);
+            }
         }
+#pragma unroll
+        for (int c = 0; c < 4; c++) q4[c] = nq4[c];
+        sc4 = nsc4;
+        dm = ndm;
     }
 #pragma unroll
     for (int t = 0; t < NT; t++) red[(wv * NT + t) * 64 + lane] = acc[t];
@@ -595,67 +630,51 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
     if (wv < NT && t0 + wv < tk.cnt) {
         float s = 0.f;
 #pragma unroll
-        for (int v = 0; v < kW; v++) s += red[(v * NT + wv) * 64 + lane];
+        for (int v = 0; v < kWD; v++) s += red[(v * NT + wv) * 64 + lane];
         st_dev(&o[(int64_t)perm[tk.off + t0 + wv] * H + P * 64 + lane], s);
     }
     __syncthreads();
 }
 
-// Shared h for tokens t0..t0+NT-1 on the I columns [8 c0, 8 c1) of this
-// workgroup's K chunk: silu(sum of the gate partials) * (sum of the up
-// partials), summed in a fixed order, as bf16 hi + lo in LDS
-// (hl[t][hi, lo][8 (c1 - c0)]).
-template <int NT>
-BM_DEV void shared_h_chunk(int I, int T, int t0, int c0, int c1, int kc_sg, const float *__restrict__ sgp,
-                           uint16_t *hl) {
-    const int n = 8 * (c1 - c0);
-    const uint32_t TI = (uint32_t)T * (uint32_t)I;        // 32-bit offsets: one register per load
-    for (int i = threadIdx.x; i < NT * n; i += blockDim.x) {
-        const int t = i / n, j = i - t * n;
-        const uint32_t col = (uint32_t)min(t0 + t, T - 1) * (uint32_t)I + 8 * c0 + j;
-        float gv[kMaxChunks], uv[kMaxChunks];
-#pragma unroll
-        for (int c = 0; c < kMaxChunks; c++) {
-            const uint32_t cc = (uint32_t)min(c, kc_sg - 1);
-            gv[c] = sgp[2 * cc * TI + col];
-            uv[c] = sgp[(2 * cc + 1) * TI + col];
-        }
-        float g = 0.f, u = 0.f;
-#pragma unroll
-        for (int c = 0; c < kMaxChunks; c++)
-            if (c < kc_sg) {
-                g += gv[c];
-                u += uv[c];
-            }
-        const float hv = silu(g) * u;
-        const uint32_t hi = f32_to_bf16_rne(hv);
-        hl[(t * 2 + 0) * n + j] = (uint16_t)hi;
-        hl[(t * 2 + 1) * n + j] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
-    }
-    __syncthreads();
-}
-
-// Shared down of panel P over the K pieces [c0, c1) with h from LDS.
+// Shared down of panel P over the K pieces [c0, c1); h as bf16 hi + lo
+// (hs[2][T][I]) through scalar loads.
 template <int NT>
 BM_DEV void shared_down_pass(int H, int I, int T, int t0, int P, int c0, int c1,
-                             const uint4 *__restrict__ sd, const uint16_t *hl, float *__restrict__ osp,
-                             float *red) {
+                             const uint4 *__restrict__ sd, const uint16_t *__restrict__ hs,
+                             float *__restrict__ osp, float *red) {
     const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int K8 = I / 8, n = 8 * (c1 - c0);
+    const int K8 = I / 8;
+    const int64_t lo_off = (int64_t)T * I;
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] = 0.f;
     int w0, w1;
-    split_range(c1 - c0, kW, wv, w0, w1);
-#pragma unroll 4
-    for (int c = c0 + w0; c < c0 + w1; c++) {
-        const uint4 wq = sd[((int64_t)P * K8 + c) * 64 + lane];
+    split_range(c1 - c0, kWD, wv, w0, w1);
+    // batches of 8 pieces, the next batch in flight while one is used
+    constexpr int B = 8;
+    uint4 cur[B], nxt[B];
+    const uint4 *base = sd + (int64_t)P * K8 * 64 + lane;
+    auto load = [&](int cb, uint4 (&v)[B]) {
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
-            const uint16_t *hp = hl + (t * 2) * n + 8 * (c - c0);
-            acc[t] = dot8_hilo(wq, *reinterpret_cast<const uint4 *>(hp),
-                               *reinterpret_cast<const uint4 *>(hp + n), acc[t]);
+        for (int i = 0; i < B; i++) v[i] = base[(int64_t)min(cb + i, c0 + w1 - 1) * 64];
+    };
+    if (w0 < w1) load(c0 + w0, cur);
+    for (int cb = c0 + w0; cb < c0 + w1; cb += B) {
+        if (cb + B < c0 + w1) load(cb + B, nxt);
+#pragma unroll
+        for (int i = 0; i < B; i++) {
+            const int c = cb + i;
+            if (c < c0 + w1) {
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    const uint16_t *hp = hs + (int64_t)min(t0 + t, T - 1) * I + 8 * c;
+                    acc[t] = dot8_hilo(cur[i], *reinterpret_cast<const uint4 *>(hp),
+                                       *reinterpret_cast<const uint4 *>(hp + lo_off), acc[t]);
+                }
+            }
         }
+#pragma unroll
+        for (int i = 0; i < B; i++) cur[i] = nxt[i];
     }
 #pragma unroll
     for (int t = 0; t < NT; t++) red[(wv * NT + t) * 64 + lane] = acc[t];
@@ -663,7 +682,7 @@ BM_DEV void shared_down_pass(int H, int I, int T, int t0, int P, int c0, int c1,
     if (wv < NT && t0 + wv < T) {
         float s = 0.f;
 #pragma unroll
-        for (int v = 0; v < kW; v++) s += red[(v * NT + wv) * 64 + lane];
+        for (int v = 0; v < kWD; v++) s += red[(v * NT + wv) * 64 + lane];
         st_dev(&osp[(int64_t)(t0 + wv) * H + P * 64 + lane], s);
     }
     __syncthreads();
@@ -675,7 +694,7 @@ BM_DEV void shared_down_pass(int H, int I, int T, int t0, int P, int c0, int c1,
 BM_DEV void combine_panel(int H, int k, int T, int kc_sd, int P, const float *o, const float *w,
                           const float *osp, float *y) {
     const int wv = threadIdx.x >> 6, n = P * 64 + lane_id();
-    for (int t = wv; t < T; t += kW) {
+    for (int t = wv; t < T; t += kWD) {
         // every load issued before the first is used (k <= 16, kc_sd <= 4)
         float ov[16], sv[kMaxChunks];
 #pragma unroll
@@ -711,17 +730,15 @@ BM_DEV void count_and_combine(int H, int k, int T, int kc_sd, int P, int n_contr
 // MULTI = 0: experts chosen by one token, and the shared down; MULTI = 1:
 // experts chosen by several tokens (launched only when T > 1).
 template <int MULTI>
-__global__ void __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 8)))
-k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sg, int kc_sd, const uint8_t *__restrict__ down,
+__global__ void __launch_bounds__(kWD * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 6)))
+k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const uint8_t *__restrict__ down,
            const uint4 *__restrict__ sd, const int32_t *__restrict__ counts,
            const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
            const int32_t *__restrict__ active, const int32_t *__restrict__ n_active,
-           const uint16_t *__restrict__ h, const float *__restrict__ hsum, const float *__restrict__ sgp,
-           const float *__restrict__ w, int32_t *__restrict__ ycount, float *__restrict__ osp,
-           float *__restrict__ o, float *__restrict__ y) {
-    const int64_t hrows = (int64_t)T * k;
-    __shared__ float red[kW * kNT * 64];
-    __shared__ __attribute__((aligned(16))) uint16_t hl[kNT * 2 * kSharedChunkCols];
+           const uint16_t *__restrict__ h, const float2 *__restrict__ hsum2, const float *__restrict__ hscale,
+           const uint16_t *__restrict__ hs, const float *__restrict__ w, int32_t *__restrict__ ycount,
+           float *__restrict__ osp, float *__restrict__ o, float *__restrict__ y) {
+    __shared__ float red[kWD * kNT * 64];
     __shared__ int sdo;
     const int panels = H / 64;
     const int na = *n_active;
@@ -734,13 +751,13 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sg, int kc_sd, const ui
         tk.cnt = counts[tk.e];
         if ((tk.cnt > 1) != (MULTI != 0)) return;
         if (!MULTI) {
-            routed_down_pass<1>(H, I, tk, 0, P, down, perm, h, hrows, hsum, o, red);
+            routed_down_pass<1>(H, I, tk, 0, P, down, perm, h, hsum2, hscale, o, red);
         } else {
             for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
                 if (tk.cnt - t0 == 1)
-                    routed_down_pass<1>(H, I, tk, t0, P, down, perm, h, hrows, hsum, o, red);
+                    routed_down_pass<1>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red);
                 else
-                    routed_down_pass<kNT>(H, I, tk, t0, P, down, perm, h, hrows, hsum, o, red);
+                    routed_down_pass<kNT>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red);
             }
         }
         count_and_combine(H, k, T, kc_sd, P, na + kc_sd, ycount, o, w, osp, y, &sdo);
@@ -750,13 +767,10 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sg, int kc_sd, const ui
         split_range(I / 8, kc_sd, c, c0, c1);
         float *op = osp + (int64_t)c * T * H;
         for (int t0 = 0; t0 < T; t0 += kNT) {
-            if (T - t0 == 1) {
-                shared_h_chunk<1>(I, T, t0, c0, c1, kc_sg, sgp, hl);
-                shared_down_pass<1>(H, I, T, t0, P, c0, c1, sd, hl, op, red);
-            } else {
-                shared_h_chunk<kNT>(I, T, t0, c0, c1, kc_sg, sgp, hl);
-                shared_down_pass<kNT>(H, I, T, t0, P, c0, c1, sd, hl, op, red);
-            }
+            if (T - t0 == 1)
+                shared_down_pass<1>(H, I, T, t0, P, c0, c1, sd, hs, op, red);
+            else
+                shared_down_pass<kNT>(H, I, T, t0, P, c0, c1, sd, hs, op, red);
         }
         count_and_combine(H, k, T, kc_sd, P, na + kc_sd, ycount, o, w, osp, y, &sdo);
     }
@@ -817,6 +831,7 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     }
     // routed gate/up; experts chosen by several tokens in a second launch
     const int n_gwg = p.slots * (I / 64);
+    const int n_fin = shared ? (int)(((int64_t)T * I + kWG * 64 - 1) / (kWG * 64)) : 0;
     const int route_mode = p.small ? (p.n_rwg ? 1 : 2) : 0;
     for (int multi = 0; multi < (T > 1 ? 2 : 1); multi++) {
         auto kg = multi ? (bf ? k_dec_gateup<1, 1> : k_dec_gateup<0, 1>)
@@ -824,26 +839,27 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
         // the timing events, when set, are taken by the dispatch itself
         // around the first gate/up launch
         const TimingEvents ev = multi ? TimingEvents{} : timing_events();
-        hipExtLaunchKernelGGL(kg, dim3(n_gwg), dim3(kWG * 64), 0, s, ev.start, ev.stop, 0, H, I, E, k, T, n_gwg,
-                              multi ? 0 : route_mode, (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q,
-                              (const uint4 *)b.tab, x, (const float *)b.xs, (const float *)b.logits, b.ids, b.w,
-                              b.bk, b.h, b.hsum);
+        hipExtLaunchKernelGGL(kg, dim3(n_gwg + (multi ? 0 : n_fin)), dim3(kWG * 64), 0, s, ev.start, ev.stop, 0,
+                              H, I, E, k, T, n_gwg, multi ? 0 : route_mode, (const uint8_t *)L->gate_q,
+                              (const uint8_t *)L->up_q, (const uint4 *)b.tab, x, (const float *)b.xs,
+                              (const float *)b.logits, b.ids, b.w, b.bk, b.h, b.hsum2, b.hscale, p.kc_sg,
+                              (const float *)b.sgp, b.hs);
         BM_LAUNCH_CHECK();
     }
     // down || shared down; the last workgroup to finish a panel combines it
     const int n_dwg = p.slots * (H / 64);
     const int n_sd = shared ? (H / 64) * p.kc_sd : 0;
-    k_dec_down<0><<<n_dwg + n_sd, kW * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sg, p.kc_sd,
+    k_dec_down<0><<<n_dwg + n_sd, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd,
                                                    (const uint8_t *)L->down_q, (const uint4 *)L->shared_down,
                                                    b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active,
-                                                   b.bk.n_active, b.h, b.hsum, b.sgp, b.w, b.ycount,
+                                                   b.bk.n_active, b.h, b.hsum2, b.hscale, b.hs, b.w, b.ycount,
                                                    shared ? b.osp : nullptr, b.o, b.y);
     BM_LAUNCH_CHECK();
     if (T > 1) {
-        k_dec_down<1><<<n_dwg, kW * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sg, p.kc_sd, (const uint8_t *)L->down_q,
+        k_dec_down<1><<<n_dwg, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, (const uint8_t *)L->down_q,
                                                 (const uint4 *)L->shared_down, b.bk.counts, b.bk.offsets,
-                                                b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum, b.sgp, b.w,
-                                                b.ycount, shared ? b.osp : nullptr, b.o, b.y);
+                                                b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum2, b.hscale, b.hs,
+                                                b.w, b.ycount, shared ? b.osp : nullptr, b.o, b.y);
         BM_LAUNCH_CHECK();
     }
     return BITMOE_OK;

@@ -158,12 +158,27 @@ k_pack_q2k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int E, in
     int n = (int)(rem / nb), kb = (int)(rem % nb);
     int P = n >> 6, r = n & 63;
     const uint32_t *s = reinterpret_cast<const uint32_t *>(src + 84 * gid);
+    const uint8_t *qs = src + 84 * gid + 16;
     uint8_t *slab = dst + e * per_e * 84;
     int64_t pk = (int64_t)P * nb + kb;
+    // sub-block b = 8h + 2j + lh holds weights l = 16 lh .. 16 lh + 15 of
+    // plane j of half h: q = (qs[32h + l] >> 2j) & 3
+    uint32_t W[16];
+#pragma unroll
+    for (int b = 0; b < 16; b++) {
+        const int h = b >> 3, j = (b >> 1) & 3, lh = b & 1;
+        uint32_t w = 0;
+#pragma unroll
+        for (int t = 0; t < 16; t++) {
+            const uint32_t q = (qs[32 * h + 16 * lh + t] >> (2 * j)) & 3u;
+            w |= q << (16 * (t & 1) + (t & ~1));
+        }
+        W[b] = w;
+    }
 #pragma unroll
     for (int c = 0; c < 4; c++)
         reinterpret_cast<uint4 *>(slab)[(pk * 4 + c) * 64 + r] =
-            make_uint4(s[4 + 4 * c], s[5 + 4 * c], s[6 + 4 * c], s[7 + 4 * c]);
+            make_uint4(W[4 * c], W[4 * c + 1], W[4 * c + 2], W[4 * c + 3]);
     reinterpret_cast<uint4 *>(slab + 64 * per_e)[pk * 64 + r] = make_uint4(s[0], s[1], s[2], s[3]);
     reinterpret_cast<uint32_t *>(slab + 80 * per_e)[pk * 64 + r] = s[20];
 }

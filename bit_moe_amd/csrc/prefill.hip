@@ -71,20 +71,14 @@ BM_DEV void q2k_sub_int_to_lds(const uint8_t *slab, int N, int nb, int n, int kb
     const int P = n >> 6, r = n & 63;
     const int64_t pk = (int64_t)P * nb + kb;
     const int64_t S = (int64_t)N * nb;
-    const int hh = b >> 3, j = (b & 7) >> 1, c = 2 * hh + (b & 1);
-    const uint4 qv = reinterpret_cast<const uint4 *>(slab)[(pk * 4 + c) * 64 + r];
+    const uint32_t W = reinterpret_cast<const uint32_t *>(slab)[((pk * 4 + (b >> 2)) * 64 + r) * 4 + (b & 3)];
     const float sc = (float)(slab[S * 64 + (pk * 64 + r) * 16 + b] & 15u);
-    uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
     uint32_t out[8];
 #pragma unroll
-    for (int w = 0; w < 4; w++) {
-        uint32_t q = (qw[w] >> (2 * j)) & 0x03030303u;
-        uint32_t v0 = __float_as_uint(sc * (float)(q & 0xFFu)) >> 16;
-        uint32_t v1 = __float_as_uint(sc * (float)((q >> 8) & 0xFFu)) >> 16;
-        uint32_t v2 = __float_as_uint(sc * (float)((q >> 16) & 0xFFu)) >> 16;
-        uint32_t v3 = __float_as_uint(sc * (float)(q >> 24)) >> 16;
-        out[2 * w] = v0 | (v1 << 16);
-        out[2 * w + 1] = v2 | (v3 << 16);
+    for (int p = 0; p < 8; p++) {
+        const uint32_t v0 = __float_as_uint(sc * (float)((W >> (2 * p)) & 3u)) >> 16;          // exact
+        const uint32_t v1 = __float_as_uint(sc * (float)((W >> (16 + 2 * p)) & 3u)) >> 16;
+        out[p] = v0 | (v1 << 16);
     }
     uint4 *o = reinterpret_cast<uint4 *>(dst);
     o[0] = make_uint4(out[0], out[1], out[2], out[3]);

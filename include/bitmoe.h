@@ -71,7 +71,11 @@
  *                             weights 4,5,6 (weight 7: even parity of the 8)
  *     [64*N*nb, 66*N*nb):     d of block (n,kb) at (P*nb + kb)*64 + r, 2 bytes
  *   Q2K slab (N*nb*84 bytes):
- *     [0, 64*N*nb):           qs piece c (bytes 16+16c..31+16c) as above
+ *     [0, 64*N*nb):           piece c at ((P*nb + kb)*4 + c)*64 + r, 16 bytes:
+ *                             the quants of sub-blocks 4c..4c+3 (weights
+ *                             64c..64c+63), one little-endian word each: the
+ *                             quant of weight 2p of the sub-block at bits 2p,
+ *                             that of weight 2p+1 at bits 16+2p
  *     [64*N*nb, 80*N*nb):     scales (bytes 0-15) at (P*nb + kb)*64 + r, 16 B
  *     [80*N*nb, 84*N*nb):     d, dmin (bytes 80-83) at (P*nb + kb)*64 + r, 4 B
  *   BF16 (shared expert) matrix [N][K] row-major -> tiled: the 8 values

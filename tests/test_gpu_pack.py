@@ -35,8 +35,16 @@ def _tiled_iq2x_numpy(canon, N, K):
 def _tiled_q2k_numpy(canon, N, K):
     nb = K // 256
     b = canon.reshape(N // 64, 64, nb, 84).transpose(0, 2, 1, 3)         # [P][kb][r][84]
-    qs = b[..., 16:80].reshape(N // 64, nb, 64, 4, 16).transpose(0, 1, 3, 2, 4)
-    return np.concatenate([qs.reshape(-1), b[..., 0:16].reshape(-1), b[..., 80:84].reshape(-1)])
+    qs = b[..., 16:80].astype(np.uint32)                                  # [P][kb][r][64]
+    # quant of weight i: (qs[32*(i//128) + i%32] >> 2*((i%128)//32)) & 3
+    i = np.arange(256)
+    q = (qs[..., 32 * (i // 128) + i % 32] >> (2 * ((i % 128) // 32))) & 3  # [P][kb][r][256]
+    q = q.reshape(q.shape[:-1] + (16, 16))                                # sub-block, weight t
+    t = np.arange(16)
+    words = (q << (16 * (t & 1) + (t & ~1))).sum(axis=-1).astype(np.uint32)   # [P][kb][r][16]
+    pieces = words.reshape(N // 64, nb, 64, 4, 4).transpose(0, 1, 3, 2, 4)    # [P][kb][c][r][4]
+    qs_t = np.ascontiguousarray(pieces.astype("<u4")).view(np.uint8)
+    return np.concatenate([qs_t.reshape(-1), b[..., 0:16].reshape(-1), b[..., 80:84].reshape(-1)])
 
 
 def test_pack_iq2x_and_q2k_match_documented_layout():
