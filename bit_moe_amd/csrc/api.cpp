@@ -58,8 +58,7 @@ struct FfnWs {
     bm_host::Buckets b{};
     int max_tiles = 0;
     // prefill
-    float *o = nullptr, *hs = nullptr, *os = nullptr;
-    uint16_t *hb = nullptr;
+    bm_host::PrefillBufs p{};
     // decode
     bm_host::DecodeBufs d{};
     size_t bytes = 0;
@@ -81,11 +80,14 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
         f.max_tiles = (int)((n + f.b.tile_rows - 1) / f.b.tile_rows + std::min<int64_t>(L->E, n));
         f.b.tiles = c.take<int32_t>(2 * std::max(f.max_tiles, 1));
         f.b.n_tiles = c.take<int32_t>(1);
-        f.hb = c.take<uint16_t>(n * L->I);
-        f.o = c.take<float>(n * L->H);
+        f.p.x16 = c.take<uint16_t>((int64_t)T * L->H);
+        f.p.xsc = c.take<float>(T);
+        f.p.h = c.take<uint16_t>(n * L->I);
+        f.p.hexp = c.take<int32_t>(n * (L->I / 256));
+        f.p.o = c.take<float>(n * L->H);
         if (shared) {
-            f.hs = c.take<float>((int64_t)T * L->I);
-            f.os = c.take<float>((int64_t)T * L->H);
+            f.p.hs = c.take<float>((int64_t)T * L->I);
+            f.p.os = c.take<float>((int64_t)T * L->H);
         }
     } else {
         f.b.tile_rows = 1;
@@ -284,8 +286,7 @@ int moe_ffn_prefill(const bitmoe_layer *L, const void *x, int x_dtype, int T, co
     if (rc || T == 0) return rc;
     hipStream_t s = as_stream(stream);
     if ((rc = bm_host::launch_bucket(ids, T, L->k, L->E, f.b, s))) return rc;
-    return bm_host::launch_prefill_ffn(L, x, x_dtype, T, ids, w, y, f.b, f.max_tiles, nullptr, f.hb, f.o,
-                                       f.hs, f.os, s);
+    return bm_host::launch_prefill_ffn(L, x, x_dtype, T, w, y, f.b, f.max_tiles, f.p, s);
 }
 
 int moe_dequant_iq2x(const void *blocks, const void *grid, int64_t nblocks, void *out, int out_dtype,

@@ -308,10 +308,17 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
 
 // prefill FFN
 int prefill_tile_rows();
-int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T,
-                       const int32_t *ids, const float *w, float *y,
-                       const Buckets &b, int max_tiles, uint16_t *xb, uint16_t *h,
-                       float *o, float *hs, float *os, hipStream_t s);
+// Prefill working buffers (all device memory, carved from the workspace).
+struct PrefillBufs {
+    uint16_t *x16;      // [T][H] fp16 activations, scaled per token by 1/xsc
+    float *xsc;         // [T] power-of-two token scales
+    uint16_t *h;        // [T*k][I] fp16 h rows in bucket order, scaled per 256 columns
+    int32_t *hexp;      // [T*k][I/256] exponents of those scales
+    float *o;           // [T*k][H] per-pair expert outputs
+    float *hs, *os;     // shared expert h [T][I] and output [T][H] (or null)
+};
+int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T, const float *w, float *y,
+                       const Buckets &b, int max_tiles, const PrefillBufs &pb, hipStream_t s);
 
 // events taken at the start and end of the gate/up launch (moe_set_timing_events)
 struct TimingEvents {

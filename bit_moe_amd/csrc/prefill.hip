@@ -1,16 +1,37 @@
-// Prefill FFN: grouped GEMMs over the bucketed (token, expert) pairs with the
-// routed weights dequantised to bf16 tiles in LDS feeding bf16 MFMA
-// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Prefill is compute-bound
-// (page "Faire tenir un MoE de 284B dans un portable de 128 Go", section "Un
-// pre-remplissage a 790 t/s revele le veritable goulot d'etranglement"), so
-// the dense contraction goes to the matrix cores.
+// Prefill FFN: grouped GEMMs over the bucketed (token, expert) rows on the
+// matrix cores.  Prefill is compute-bound (page "Faire tenir un MoE de 284B
+// dans un portable de 128 Go", section "Un pre-remplissage a 790 t/s revele
+// le veritable goulot d'etranglement"), so the contraction runs on
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation.
+//
+// Operands.  Activations enter as fp16 scaled by a power of two per token
+// (k_pf_xprep), so any bf16/fp32 range maps onto fp16's normal range; the
+// scale is undone in fp32 after the contraction.  Weights are dequantised
+// straight into MFMA operand registers, never to memory: each lane owns the
+// eight K slots of one codebook run (IQ2X) or of half a Q2K sub-block and
+// builds its fp16 operand with one packed fp16 op per weight pair (IQ2X:
+// w = c * (+-m), c = d/8 (2s+1) folded per group; Q2K: w = a q - b with
+// a = d sc, b = dmin m per sub-block).  The K order inside a stage is
+// permuted so that a lane's slots follow the packed layout; the activation
+// tile in LDS is read with the same permutation, so the products pair up.
+//
+// IQ2X runs decode through two LDS tables of ready-made fp16 pairs (2 x 4096
+// x 8 bytes): table 1 at R & 0xFFF gives weights 0..3 with their signs,
+// table 2 at R >> 3 weights 4..7 (R is the 15-bit run field of the tiled
+// words).  Two random 8-byte LDS reads per 8 weights.
 //
 // Work list: the bucketing pass emits tiles (expert e, first row r0) of up to
-// BM rows of expert e's bucket; grid.y walks the tiles, grid.x the N tiles.
-//  gate/up: A = gathered activation rows (bf16), B = [gate rows | up rows]
-//           of the N tile, epilogue h = silu(g) * u (bf16, bucket order).
-//  down:    A = h rows of the tile (contiguous), B = Q2K rows, epilogue
-//           writes o[pair][n] (fp32); k_combine applies the routing weights.
+// 96 rows of e's bucket; a tile runs ceil(rows/16) M-blocks (a compile-time
+// count chosen per tile).  Workgroups are numbered so that all N-tiles of one
+// M-tile land on the same XCD (round-robin dispatch), which keeps the
+// activation rows they share in that XCD's L2.
+//  gate/up: 8 waves x 32 h columns (gate and up blocks of the same columns
+//           in one lane), epilogue h = silu(g) u stored as fp16 with one
+//           power-of-two exponent per (row, 256 columns).
+//  down:    8 waves x 64 output columns, A = h rows rescaled per 256-column
+//           chunk to the row's largest exponent while staged into LDS;
+//           epilogue writes o[pair][n] (fp32); k_combine_p applies the
+//           routing weights.
 #include <hip/hip_ext.h>
 
 #include "common.h"
@@ -19,291 +40,512 @@ namespace {
 
 using namespace bm;
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 64;        // rows per tile (matches the bucket tile list)
-constexpr int BK = 128;       // K per LDS stage (half a superblock)
-constexpr int LDK = BK + 8;   // padded LDS row stride in bf16 elements
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfRows = 96;                   // rows per tile (6 M-blocks)
+constexpr int kPfHalf = 128;                  // K per LDS stage
+constexpr int kPfLda = kPfHalf + 8;           // padded LDS row (halfs): 272 B, conflict-free b128 reads
+constexpr int kPfGuCols = 256;                // h columns per gate/up workgroup
+constexpr int kPfDnCols = 512;                // output columns per down workgroup
+constexpr int kPfXcds = 8;
+constexpr int kPfTabBytes = 2 * 4096 * 8;
+constexpr int kPfABytes = kPfRows * kPfLda * 2;
+constexpr int kPfGuLds = kPfTabBytes + 2 * kPfABytes + kPfRows * (4 + 4 + 4) + kPfWaves * kPfRows * 4;
+constexpr int kPfDnLds = 2 * kPfABytes + kPfRows * (4 + 4);
 
-struct PrefillArgs {
-    int H, I, k, T;
-    const uint8_t *gate, *up, *down, *grid;
-    const int32_t *counts, *offsets, *perm, *tiles, *n_tiles;
-};
+BM_DEV uint32_t h2u(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+BM_DEV f16x2 u2h(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+BM_DEV uint32_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+BM_DEV uint32_t f16_pair(float f) { const uint32_t b = f16_bits(f); return b | (b << 16); }
+BM_DEV uint32_t pk_mul(uint32_t a, uint32_t b) { return h2u(u2h(a) * u2h(b)); }
 
-// --- B-tile dequantisation into LDS (bf16 = RNE of the exact fp32 value) ---
-
-// 32 weights of IQ2X group g of block (n, kb) of one expert's tiled slab,
-// without the superblock scale: +-(2s+1)*grid[idx][i].  With codebook
-// magnitudes in {1,3,5,7} these are odd integers <= 217, exact in bf16; the
-// factor d/8 is applied to the fp32 partial sums of each superblock.
-BM_DEV void iq2x_group_int_to_lds(const uint8_t *slab, int nb, int n, int kb, int g,
-                                  const uint2 *sgrid, uint16_t *dst) {
-    const int P = n >> 6, r = n & 63;
-    const int64_t pk = (int64_t)P * nb + kb;
-    const uint2 gw = reinterpret_cast<const uint2 *>(slab)[((pk * 4 + (g >> 1)) * 64 + r) * 2 + (g & 1)];
-    const float s2 = (float)(2u * iq2x_scale(gw.x, gw.y) + 1u);
-    uint32_t out[16];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const uint32_t R = iq2x_run(j < 2 ? gw.x : gw.y, j & 1);
-        const uint32_t sig = iq2x_run_signs(R);
-        const uint2 row = sgrid[iq2x_run_idx(R)];
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-            uint32_t m0 = ((i < 4 ? row.x : row.y) >> (8 * (i & 3))) & 0xFFu;
-            uint32_t m1 = ((i < 4 ? row.x : row.y) >> (8 * ((i + 1) & 3))) & 0xFFu;
-            uint32_t b0 = f32_to_bf16_rne(s2 * (float)m0) | (((sig >> i) & 1u) << 15);
-            uint32_t b1 = f32_to_bf16_rne(s2 * (float)m1) | (((sig >> (i + 1)) & 1u) << 15);
-            out[4 * j + i / 2] = b0 | (b1 << 16);
-        }
-    }
-    uint4 *o = reinterpret_cast<uint4 *>(dst);
-#pragma unroll
-    for (int q = 0; q < 4; q++) o[q] = make_uint4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+// Power-of-two exponent e with m * 2^-e in [2^14, 2^15) (0 for 0, inf, NaN).
+BM_DEV int pf_exponent(float m) {
+    const uint32_t u = __float_as_uint(m);
+    if (!(m > 0.f) || u >= 0x7F800000u) return 0;
+    const int ex = (int)(u >> 23) - 127;
+    return max(ex - 14, -100);
 }
 
-// 16 weights of Q2K sub-block b of block (n, kb) without d and the min:
-// scale*q, integers 0..45, exact in bf16.  The kernel applies d and the
-// -dmin*min*sum(h) term to the fp32 partial sums of each superblock.
-BM_DEV void q2k_sub_int_to_lds(const uint8_t *slab, int N, int nb, int n, int kb, int b, uint16_t *dst) {
-    const int P = n >> 6, r = n & 63;
-    const int64_t pk = (int64_t)P * nb + kb;
-    const int64_t S = (int64_t)N * nb;
-    const uint32_t W = reinterpret_cast<const uint32_t *>(slab)[((pk * 4 + (b >> 2)) * 64 + r) * 4 + (b & 3)];
-    const float sc = (float)(slab[S * 64 + (pk * 64 + r) * 16 + b] & 15u);
-    uint32_t out[8];
-#pragma unroll
-    for (int p = 0; p < 8; p++) {
-        const uint32_t v0 = __float_as_uint(sc * (float)((W >> (2 * p)) & 3u)) >> 16;          // exact
-        const uint32_t v1 = __float_as_uint(sc * (float)((W >> (16 + 2 * p)) & 3u)) >> 16;
-        out[p] = v0 | (v1 << 16);
-    }
-    uint4 *o = reinterpret_cast<uint4 *>(dst);
-    o[0] = make_uint4(out[0], out[1], out[2], out[3]);
-    o[1] = make_uint4(out[4], out[5], out[6], out[7]);
+// fp16 bits of 2^d, d <= 0 (subnormal below 2^-14, zero below 2^-24)
+BM_DEV uint32_t f16_pow2(int d) {
+    if (d >= -14) return (uint32_t)(15 + d) << 10;
+    if (d >= -24) return 1u << (d + 24);
+    return 0u;
 }
 
-// MFMA over one BK stage: wave computes 4 M-blocks x NB N-blocks.
-template <int NB>
-BM_DEV void mfma_stage(const uint16_t *sa, const uint16_t *sb, const int (&bcol)[NB],
-                       f32x4 (&acc)[4][NB]) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-        const int kof = kk + 8 * (lane >> 4);
-        bf16x8 fb[NB];
-#pragma unroll
-        for (int j = 0; j < NB; j++)
-            fb[j] = *reinterpret_cast<const bf16x8 *>(sb + (bcol[j] + (lane & 15)) * LDK + kof);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            bf16x8 fa = *reinterpret_cast<const bf16x8 *>(sa + (16 * i + (lane & 15)) * LDK + kof);
-#pragma unroll
-            for (int j = 0; j < NB; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
-        }
-    }
+// ---- workgroup -> (M-tile, N-tile), all N-tiles of an M-tile on one XCD ----
+struct PfSlot { int tile, ntile; };
+BM_DEV PfSlot pf_slot(int nN) {
+    const int b = blockIdx.x, xcd = b % kPfXcds, slot = b / kPfXcds;
+    return {(slot / nN) * kPfXcds + xcd, slot % nN};
 }
+int pf_grid(int max_tiles, int nN) { return (max_tiles + kPfXcds - 1) / kPfXcds * kPfXcds * nN; }
 
 // ---------------------------------------------------------------------------
-// gate/up.  grid = (I/64, max_tiles), 256 threads.  N tile: h columns
-// n0..n0+63; B rows 0-63 = gate rows n0.., 64-127 = up rows n0..
+// activations -> fp16, one power-of-two scale per token.  grid = T, 256 thr.
 // ---------------------------------------------------------------------------
 template <int XBF16>
 __global__ void __launch_bounds__(256)
-k_prefill_gateup(int H, int I, int k, const uint8_t *__restrict__ gate,
-                 const uint8_t *__restrict__ up, const uint8_t *__restrict__ grid,
-                 const void *__restrict__ x, const int32_t *__restrict__ counts,
-                 const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
-                 const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
-                 uint16_t *__restrict__ h) {
-    __shared__ __attribute__((aligned(16))) uint16_t sa[BM * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t sb[128 * LDK];
-    __shared__ uint2 sgrid[256];
-    __shared__ int stok[BM];
-    const int tile = blockIdx.y;
-    if (tile >= *n_tiles) return;
-    const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
-    const int off = offsets[e], rows = min(BM, counts[e] - r0);
-    const int n0 = blockIdx.x * 64;
-    const int tid = threadIdx.x, lane = lane_id();
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    for (int i = tid; i < 256; i += 256) sgrid[i] = reinterpret_cast<const uint2 *>(grid)[i];
-    if (tid < BM) stok[tid] = perm[off + r0 + min(tid, rows - 1)] / k;
-    const int nb = H / kQK;
-    const int64_t slab = (int64_t)I * nb * 66;
-    const uint8_t *G = gate + e * slab, *U = up + e * slab;
-    const uint16_t *Gd = reinterpret_cast<const uint16_t *>(G + (int64_t)I * nb * 64);
-    const uint16_t *Ud = reinterpret_cast<const uint16_t *>(U + (int64_t)I * nb * 64);
-    const int ncol = n0 + 16 * wv + (lane & 15);          // this lane's output column
-    const int64_t dbase = (int64_t)(ncol >> 6) * nb * 64 + (ncol & 63);
-    f32x4 acc[4][2], part[4][2];
+k_pf_xprep(int H, const void *__restrict__ x, uint16_t *__restrict__ x16, float *__restrict__ xsc) {
+    __shared__ float sm[4];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const int64_t row = (int64_t)t * H;
+    float m = 0.f;
+    for (int c = tid * 8; c < H; c += 256 * 8) {
+        float v[8];
+        if (XBF16) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + row + c);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int bcol[2] = {16 * wv, 64 + 16 * wv};
-    __syncthreads();
-    for (int kb = 0; kb < nb; kb++) {
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < 2; j++) part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int half = 0; half < 2; half++) {
-            const int k0 = kb * kQK + half * BK;
-            // A: 64 rows x 128 K -> 1024 pieces of 8 values, 4 per thread
-#pragma unroll
-            for (int p = 0; p < 4; p++) {
-                int piece = tid + 256 * p, r = piece >> 4, c = (piece & 15) * 8;
-                const int t = stok[r];
-                uint4 v;
-                if (XBF16) {
-                    v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)t * H + k0 + c);
-                } else {
-                    const float4 *xp = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)t * H + k0 + c);
-                    float4 a = xp[0], b = xp[1];
-                    v = make_uint4(f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16),
-                                   f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16),
-                                   f32_to_bf16_rne(b.x) | (f32_to_bf16_rne(b.y) << 16),
-                                   f32_to_bf16_rne(b.z) | (f32_to_bf16_rne(b.w) << 16));
-                }
-                *reinterpret_cast<uint4 *>(sa + r * LDK + c) = v;
-            }
-            // B: 128 rows x 4 groups = 512 (row, group) units, 2 per thread
-#pragma unroll
-            for (int p = 0; p < 2; p++) {
-                int u = tid + 256 * p, row = u >> 2, gg = u & 3;
-                const uint8_t *S = row < 64 ? G : U;
-                iq2x_group_int_to_lds(S, nb, n0 + (row & 63), kb, 4 * half + gg, sgrid, sb + row * LDK + 32 * gg);
-            }
-            __syncthreads();
-            mfma_stage<2>(sa, sb, bcol, part);
-            __syncthreads();
+            for (int i = 0; i < 4; i++) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
+        } else {
+            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + row + c);
+            const float4 a = p[0], b = p[1];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
         }
-        const float dg = 0.125f * fp16_to_f32(Gd[dbase + (int64_t)kb * 64]);
-        const float du = 0.125f * fp16_to_f32(Ud[dbase + (int64_t)kb * 64]);
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                acc[i][0][q] = fmaf(dg, part[i][0][q], acc[i][0][q]);
-                acc[i][1][q] = fmaf(du, part[i][1][q], acc[i][1][q]);
-            }
+        for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
     }
-    // epilogue: lane holds rows 4*(lane/16)+q of each M block, column lane%16
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    if ((tid & 63) == 0) sm[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+    const int e = pf_exponent(m);
+    if (tid == 0) xsc[t] = ldexpf(1.f, e);
+    for (int c = tid * 8; c < H; c += 256 * 8) {
+        float v[8];
+        if (XBF16) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + row + c);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
+        } else {
+            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + row + c);
+            const float4 a = p[0], b = p[1];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        }
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) o[i] = f16_bits(ldexpf(v[2 * i], -e)) | (f16_bits(ldexpf(v[2 * i + 1], -e)) << 16);
+        *reinterpret_cast<uint4 *>(x16 + row + c) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gate/up.  512 threads; wave w owns h columns hc0 + 32w .. +31: blocks 0,1
+// are the gate rows of those columns, blocks 2,3 the up rows.
+// ---------------------------------------------------------------------------
+
+// The LDS decode tables: fp16 pairs (+-m0, +-m1), (+-m2, +-m3) per entry.
+BM_DEV uint2 pf_tab_pairs(uint32_t m4, uint32_t sg) {
+    uint32_t h[4];
+#pragma unroll
+    for (int b = 0; b < 4; b++) h[b] = f16_bits((float)((m4 >> (8 * b)) & 0xFFu)) | (((sg >> b) & 1u) << 15);
+    return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+}
+BM_DEV void pf_build_tables(const uint8_t *__restrict__ grid, uint2 *t1, uint2 *t2) {
+    for (int i = threadIdx.x; i < 4096; i += kPfThreads) {
+        // table 1, i = idx << 4 | parity(signs 0..3) << 3 | signs 0..2
+        const uint32_t idx1 = i >> 4, lo3 = i & 7u, p1 = (i >> 3) & 1u;
+        const uint32_t sg1 = lo3 | ((p1 ^ (__popc(lo3) & 1u)) << 3);
+        t1[i] = pf_tab_pairs(*reinterpret_cast<const uint32_t *>(grid + 8 * idx1), sg1);
+        // table 2, i = signs 4..6 << 9 | idx << 1 | parity(signs 0..3)
+        const uint32_t idx2 = (i >> 1) & 0xFFu, hi3 = (i >> 9) & 7u, p2 = i & 1u;
+        const uint32_t sg2 = hi3 | ((p2 ^ (__popc(hi3) & 1u)) << 3);
+        t2[i] = pf_tab_pairs(*reinterpret_cast<const uint32_t *>(grid + 8 * idx2 + 4), sg2);
+    }
+}
+
+// fp16 operand of run `second` of word W (8 weights, K order), times c2
+BM_DEV f16x8 pf_iq2x_run(const uint8_t *lds, uint32_t W, int second, uint32_t c2) {
+    const uint32_t o1 = second ? (W >> 14) & 0x7FF8u : (W << 1) & 0x7FF8u;
+    const uint32_t o2 = second ? (W >> 17) & 0x7FF8u : (W >> 2) & 0x7FF8u;
+    const uint2 e1 = *reinterpret_cast<const uint2 *>(lds + o1);
+    const uint2 e2 = *reinterpret_cast<const uint2 *>(lds + 32768 + o2);
+    const uint4 v = make_uint4(pk_mul(c2, e1.x), pk_mul(c2, e1.y), pk_mul(c2, e2.x), pk_mul(c2, e2.y));
+    return __builtin_bit_cast(f16x8, v);
+}
+
+struct PfTile {
+    int e, r0, off, rows;
+};
+BM_DEV PfTile pf_tile(int tile, const int32_t *tiles, const int32_t *counts, const int32_t *offsets) {
+    PfTile t;
+    t.e = tiles[2 * tile];
+    t.r0 = tiles[2 * tile + 1];
+    t.off = offsets[t.e];
+    t.rows = min(kPfRows, counts[t.e] - t.r0);
+    return t;
+}
+
+struct GuArgs {
+    int H, I, k;
+    const uint8_t *gate, *up, *grid;
+    const uint16_t *x16;
+    const float *xsc;
+    const int32_t *counts, *offsets, *perm, *tiles, *n_tiles;
+    uint16_t *h;
+    int32_t *hexp;
+};
+
+// Stage rows 0..16*MB-1 of activation half (kb, hf) into LDS buffer `dst`:
+// 16 loads of 16 bytes per row, up to 3 per thread.
+template <int MB>
+BM_DEV void gu_stage_load(const GuArgs &a, const int *stok, int kb, int hf, uint4 (&r)[3]) {
+    const int k0 = kb * kQK + hf * kPfHalf;
+#pragma unroll
+    for (int p = 0; p < 3; p++) {
+        const int u = threadIdx.x + kPfThreads * p, row = u >> 4, c = u & 15;
+        if (row < 16 * MB) r[p] = *reinterpret_cast<const uint4 *>(a.x16 + (int64_t)stok[row] * a.H + k0 + 8 * c);
+    }
+}
+template <int MB>
+BM_DEV void stage_store(uint16_t *dst, const uint4 (&r)[3]) {
+#pragma unroll
+    for (int p = 0; p < 3; p++) {
+        const int u = threadIdx.x + kPfThreads * p, row = u >> 4, c = u & 15;
+        if (row < 16 * MB) *reinterpret_cast<uint4 *>(dst + row * kPfLda + 8 * c) = r[p];
+    }
+}
+
+template <int MB>
+BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
+    uint16_t *sa[2] = {reinterpret_cast<uint16_t *>(lds + kPfTabBytes),
+                       reinterpret_cast<uint16_t *>(lds + kPfTabBytes + kPfABytes)};
+    int *stok = reinterpret_cast<int *>(lds + kPfTabBytes + 2 * kPfABytes);
+    float *sxs = reinterpret_cast<float *>(stok + kPfRows);
+    int *sexp = reinterpret_cast<int *>(sxs + kPfRows);
+    float *smax = reinterpret_cast<float *>(sexp + kPfRows);
+    const int lane = lane_id(), n = lane & 15, kq = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nb = a.H / kQK;
+    const int64_t slab = (int64_t)a.I * nb * 66;
+    const uint8_t *src[2] = {a.gate + t.e * slab, a.up + t.e * slab};
+    // this lane's h column in blocks 0/2 and 1/3
+    const int hc = ntile * kPfGuCols + 32 * w + n;
+    // word and scale indices of block j at superblock 0, half 0
+    // (one expert's slab is below 4 GiB: 32-bit offsets)
+    uint32_t wbase[2], dbase[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int col = hc + 16 * j, P = col >> 6, r = col & 63;
+        wbase[j] = ((uint32_t)(P * nb * 4 * 64 + (kq >> 1) * 64 + r) * 2 + (kq & 1)) * 8;
+        dbase[j] = (uint32_t)(P * nb * 64 + r) * 2 + (uint32_t)a.I * nb * 64;
+    }
+    auto load_w = [&](int kb, int hf, uint2 (&wv)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            wv[j] = *reinterpret_cast<const uint2 *>(src[j >> 1] + wbase[j & 1] + kb * 4096 + hf * 2048);
+    };
+    auto load_d = [&](int kb, float (&dv)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            dv[j] = 0.125f * fp16_to_f32(*reinterpret_cast<const uint16_t *>(src[j >> 1] + dbase[j & 1] + kb * 128));
+    };
+    f32x4 acc[MB][4];
+#pragma unroll
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint2 wcur[4], wnxt[4];
+    float dcur[4], dnxt[4];
+    uint4 ar[3];
+    load_w(0, 0, wcur);
+    load_d(0, dcur);
+    gu_stage_load<MB>(a, stok, 0, 0, ar);
+    stage_store<MB>(sa[0], ar);
+    __syncthreads();
+    const int nsteps = 2 * nb;
+    for (int step = 0; step < nsteps; step++) {
+        const bool more = step + 1 < nsteps;
+        const int nkb = (step + 1) >> 1, nhf = (step + 1) & 1;
+        if (more) {
+            load_w(nkb, nhf, wnxt);
+            if (nhf == 0) load_d(nkb, dnxt);
+            gu_stage_load<MB>(a, stok, nkb, nhf, ar);
+        }
+        uint32_t c2[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) c2[j] = f16_pair(dcur[j] * (float)(2u * iq2x_scale(wcur[j].x, wcur[j].y) + 1u));
+        const uint16_t *A = sa[step & 1] + n * kPfLda + 32 * kq;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            f16x8 b[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) b[j] = pf_iq2x_run(lds, r < 2 ? wcur[j].x : wcur[j].y, r & 1, c2[j]);
+#pragma unroll
+            for (int i = 0; i < MB; i++) {
+                const f16x8 av = *reinterpret_cast<const f16x8 *>(A + 16 * i * kPfLda + 8 * r);
+#pragma unroll
+                for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[j], acc[i][j], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep each k-step's operands short-lived
+        }
+        if (more) stage_store<MB>(sa[(step + 1) & 1], ar);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; j++) wcur[j] = wnxt[j];
+        if (more && nhf == 0)
+#pragma unroll
+            for (int j = 0; j < 4; j++) dcur[j] = dnxt[j];
+    }
+    // epilogue: lane holds rows 16i + 4kq + q, columns hc (j=0) and hc+16 (j=1);
+    // h is computed twice (row maxima first, then the scaled stores)
+#pragma unroll
+    for (int i = 0; i < MB; i++)
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-            int m = 16 * i + 4 * (lane >> 4) + q;
-            if (m < rows) {
-                float hv = silu(acc[i][0][q]) * acc[i][1][q];
-                h[(int64_t)(off + r0 + m) * I + ncol] = (uint16_t)f32_to_bf16_rne(hv);
+            const int m = 16 * i + 4 * kq + q;
+            const float xs = sxs[m];
+            float mx = 0.f;
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                mx = fmaxf(mx, fabsf(silu(acc[i][j][q] * xs) * (acc[i][j + 2][q] * xs)));
+            mx = fmaxf(mx, __shfl_xor(mx, 1, kWave));
+            mx = fmaxf(mx, __shfl_xor(mx, 2, kWave));
+            mx = fmaxf(mx, __shfl_xor(mx, 4, kWave));
+            mx = fmaxf(mx, __shfl_xor(mx, 8, kWave));
+            if (n == 0) smax[w * kPfRows + m] = mx;
+        }
+    __syncthreads();
+    if (threadIdx.x < 16 * MB) {
+        float mx = 0.f;
+#pragma unroll
+        for (int v = 0; v < kPfWaves; v++) mx = fmaxf(mx, smax[v * kPfRows + threadIdx.x]);
+        const int e = pf_exponent(mx);
+        sexp[threadIdx.x] = e;
+        if ((int)threadIdx.x < t.rows)
+            a.hexp[(int64_t)(t.off + t.r0 + threadIdx.x) * (a.I / kPfGuCols) + ntile] = e;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int m = 16 * i + 4 * kq + q;
+            if (m < t.rows) {
+                const int e = sexp[m];
+                const float xs = sxs[m];
+                uint16_t *hp = a.h + (int64_t)(t.off + t.r0 + m) * a.I + hc;
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    hp[16 * j] = (uint16_t)f16_bits(ldexpf(silu(acc[i][j][q] * xs) * (acc[i][j + 2][q] * xs), -e));
             }
         }
 }
 
-// ---------------------------------------------------------------------------
-// down.  grid = (H/64, max_tiles), 256 threads.  A = h rows (bucket order).
-// Per superblock: P = h . (scale*q) on MFMA, Pmin = Hsum . min on one more
-// MFMA whose K slots hold the 16 sub-block sums of h split into bf16 high
-// and low parts (so the min term keeps ~16 bits), then
-// C += d * P - dmin * Pmin in fp32.
-// ---------------------------------------------------------------------------
-constexpr int HS_LD = 40;     // padded row stride of the sub-block sums (bf16)
+__global__ void __launch_bounds__(kPfThreads)
+k_pf_gateup(GuArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const PfSlot sl = pf_slot(a.I / kPfGuCols);
+    if (sl.tile >= *a.n_tiles) return;
+    const PfTile t = pf_tile(sl.tile, a.tiles, a.counts, a.offsets);
+    int *stok = reinterpret_cast<int *>(lds + kPfTabBytes + 2 * kPfABytes);
+    float *sxs = reinterpret_cast<float *>(stok + kPfRows);
+    if (threadIdx.x < kPfRows) {
+        const int tok = a.perm[t.off + t.r0 + min((int)threadIdx.x, t.rows - 1)] / a.k;
+        stok[threadIdx.x] = tok;
+        sxs[threadIdx.x] = a.xsc[tok];
+    }
+    pf_build_tables(a.grid, reinterpret_cast<uint2 *>(lds), reinterpret_cast<uint2 *>(lds + 32768));
+    __syncthreads();
+    switch ((t.rows + 15) >> 4) {
+        case 1: gu_tile<1>(a, lds, t, sl.ntile); break;
+        case 2: gu_tile<2>(a, lds, t, sl.ntile); break;
+        case 3: gu_tile<3>(a, lds, t, sl.ntile); break;
+        case 4: gu_tile<4>(a, lds, t, sl.ntile); break;
+        case 5: gu_tile<5>(a, lds, t, sl.ntile); break;
+        default: gu_tile<6>(a, lds, t, sl.ntile); break;
+    }
+}
 
-__global__ void __launch_bounds__(256)
-k_prefill_down(int H, int I, const uint8_t *__restrict__ down, const uint16_t *__restrict__ h,
-               const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,
-               const int32_t *__restrict__ perm, const int32_t *__restrict__ tiles,
-               const int32_t *__restrict__ n_tiles, float *__restrict__ o) {
-    __shared__ __attribute__((aligned(16))) uint16_t sa[BM * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t sb[64 * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t hs[BM * HS_LD];
-    const int tile = blockIdx.y;
-    if (tile >= *n_tiles) return;
-    const int e = tiles[2 * tile], r0 = tiles[2 * tile + 1];
-    const int off = offsets[e], rows = min(BM, counts[e] - r0);
-    const int n0 = blockIdx.x * 64;
-    const int tid = threadIdx.x, lane = lane_id();
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nb = I / kQK;
-    const int64_t S = (int64_t)H * nb;
-    const uint8_t *D = down + (int64_t)e * S * 84;
-    const int ncol = n0 + 16 * wv + (lane & 15);           // this lane's output column
-    const int64_t pbase = (int64_t)(ncol >> 6) * nb * 64 + (ncol & 63);
-    f32x4 acc[4][1], part[4][1];
+// ---------------------------------------------------------------------------
+// down.  512 threads; wave w owns output columns n0 + 64w .. +63 (4 blocks).
+// Lane kq of a half-superblock stage takes sub-blocks 8hf + 2kq, +1.
+// ---------------------------------------------------------------------------
+struct DnArgs {
+    int H, I;
+    const uint8_t *down;
+    const uint16_t *h;
+    const int32_t *hexp;
+    const int32_t *counts, *offsets, *perm, *tiles, *n_tiles;
+    float *o;
+};
+
+template <int MB>
+BM_DEV void dn_stage_load(const DnArgs &a, const PfTile &t, const int *semax, int kb, int hf,
+                          uint4 (&r)[3]) {
+    const int k0 = kb * kQK + hf * kPfHalf, nI = a.I / kPfGuCols;
 #pragma unroll
-    for (int i = 0; i < 4; i++) acc[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int bcol[1] = {16 * wv};
-    for (int kb = 0; kb < nb; kb++) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) part[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int half = 0; half < 2; half++) {
-            const int k0 = kb * kQK + half * BK;
-#pragma unroll
-            for (int p = 0; p < 4; p++) {
-                int piece = tid + 256 * p, r = piece >> 4, c = (piece & 15) * 8;
-                int row = off + r0 + min(r, rows - 1);
-                *reinterpret_cast<uint4 *>(sa + r * LDK + c) =
-                    *reinterpret_cast<const uint4 *>(h + (int64_t)row * I + k0 + c);
+    for (int p = 0; p < 3; p++) {
+        const int u = threadIdx.x + kPfThreads * p, row = u >> 4, c = u & 15;
+        if (row < 16 * MB) {
+            const int64_t gr = t.off + t.r0 + min(row, t.rows - 1);
+            uint4 v = *reinterpret_cast<const uint4 *>(a.h + gr * a.I + k0 + 8 * c);
+            const int d = a.hexp[gr * nI + kb] - semax[row];
+            if (d != 0) {
+                const uint32_t f = f16_pow2(d) * 0x10001u;
+                v = make_uint4(pk_mul(v.x, f), pk_mul(v.y, f), pk_mul(v.z, f), pk_mul(v.w, f));
             }
-            // B: 64 rows x 8 sub-blocks (128 K) = 512 units, 2 per thread
-#pragma unroll
-            for (int p = 0; p < 2; p++) {
-                int u = tid + 256 * p, row = u >> 3, sbk = u & 7;
-                q2k_sub_int_to_lds(D, H, nb, n0 + row, kb, 8 * half + sbk, sb + row * LDK + 16 * sbk);
-            }
-            __syncthreads();
-            // sums of 16 h values per (row, sub-block), split hi + lo
-#pragma unroll
-            for (int p = 0; p < 2; p++) {
-                int u = tid + 256 * p, row = u >> 3, j = u & 7;
-                const uint4 *src = reinterpret_cast<const uint4 *>(sa + row * LDK + 16 * j);
-                uint4 a = src[0], b = src[1];
-                uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-                float sum = 0.f;
-#pragma unroll
-                for (int q = 0; q < 8; q++) sum += bf16_lo(w8[q]) + bf16_hi(w8[q]);
-                uint32_t hi = f32_to_bf16_rne(sum);
-                uint32_t lo = f32_to_bf16_rne(sum - bf16_to_f32(hi));
-                hs[row * HS_LD + 8 * half + j] = (uint16_t)hi;
-                hs[row * HS_LD + 16 + 8 * half + j] = (uint16_t)lo;
-            }
-            mfma_stage<1>(sa, sb, bcol, part);
-            __syncthreads();
-        }
-        // min term: K slots = [Hsum_hi 0..15 | Hsum_lo 0..15] x [min 0..15 | min 0..15]
-        const int64_t pk = pbase + (int64_t)kb * 64;
-        const int kg = lane >> 4;
-        const uint2 scb = *reinterpret_cast<const uint2 *>(D + S * 64 + pk * 16 + 8 * (kg & 1));
-        uint32_t mw[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            uint32_t word = q < 2 ? scb.x : scb.y;
-            uint32_t m0 = (word >> (16 * (q & 1) + 4)) & 15u, m1 = (word >> (16 * (q & 1) + 12)) & 15u;
-            mw[q] = (__float_as_uint((float)m0) >> 16) | (__float_as_uint((float)m1) & 0xFFFF0000u);
-        }
-        const bf16x8 fbm = __builtin_bit_cast(bf16x8, make_uint4(mw[0], mw[1], mw[2], mw[3]));
-        const uint32_t dd = reinterpret_cast<const uint32_t *>(D + S * 80)[pk];
-        const float d = fp16_to_f32(dd & 0xFFFFu), dmin = fp16_to_f32(dd >> 16);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const bf16x8 fam = *reinterpret_cast<const bf16x8 *>(hs + (16 * i + (lane & 15)) * HS_LD + 8 * kg);
-            const f32x4 pm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fam, fbm, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-            for (int q = 0; q < 4; q++) acc[i][0][q] = fmaf(d, part[i][0][q], fmaf(-dmin, pm[q], acc[i][0][q]));
+            r[p] = v;
         }
     }
+}
+
+template <int MB>
+BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
+    uint16_t *sa[2] = {reinterpret_cast<uint16_t *>(lds), reinterpret_cast<uint16_t *>(lds + kPfABytes)};
+    int *semax = reinterpret_cast<int *>(lds + 2 * kPfABytes);
+    const int lane = lane_id(), n = lane & 15, kq = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nb = a.I / kQK;
+    const int64_t S = (int64_t)a.H * nb;
+    const uint8_t *D = a.down + (int64_t)t.e * S * 84;
+    const int c0 = ntile * kPfDnCols + 64 * w + n;
+    const bool active = ntile * kPfDnCols + 64 * w < a.H;     // wave-uniform
+    // byte offsets at superblock 0 (one expert's slab is below 4 GiB)
+    uint32_t qoff[4], soff[4], doff[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int j = 0; j < 4; j++) {
+        const int col = min(c0 + 16 * j, a.H - 1), P = col >> 6, r = col & 63;
+        const uint32_t pk64 = (uint32_t)(P * nb * 64 + r);           // (P nb + kb) 64 + r at kb = 0
+        qoff[j] = ((uint32_t)(P * nb * 256 + (kq >> 1) * 64 + r) * 2 + (kq & 1)) * 8;
+        soff[j] = (uint32_t)(S * 64) + pk64 * 16 + 2 * kq;
+        doff[j] = (uint32_t)(S * 80) + pk64 * 4;
+    }
+    auto load_w = [&](int kb, int hf, uint2 (&wv)[4], uint32_t (&sv)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            wv[j] = *reinterpret_cast<const uint2 *>(D + qoff[j] + kb * 4096 + hf * 2048);
+            sv[j] = *reinterpret_cast<const uint16_t *>(D + soff[j] + kb * 1024 + 8 * hf);
+        }
+    };
+    auto load_d = [&](int kb, uint32_t (&dv)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) dv[j] = *reinterpret_cast<const uint32_t *>(D + doff[j] + kb * 256);
+    };
+    const Q2kPairConsts pc;
+    uint32_t nbias[5];
+#pragma unroll
+    for (int s = 0; s < 5; s++) {
+        uint32_t v = f16_pair(-(float)(1 << (10 - 2 * s)));
+        asm volatile("" : "+s"(v));
+        nbias[s] = v;
+    }
+    f32x4 acc[MB][4];
+#pragma unroll
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint2 wcur[4], wnxt[4];
+    uint32_t scur[4], snxt[4], dcur[4], dnxt[4];
+    uint4 ar[3];
+    load_w(0, 0, wcur, scur);
+    load_d(0, dcur);
+    dn_stage_load<MB>(a, t, semax, 0, 0, ar);
+    stage_store<MB>(sa[0], ar);
+    __syncthreads();
+    const int nsteps = 2 * nb;
+    for (int step = 0; step < nsteps; step++) {
+        const bool more = step + 1 < nsteps;
+        const int nkb = (step + 1) >> 1, nhf = (step + 1) & 1;
+        if (more) {
+            load_w(nkb, nhf, wnxt, snxt);
+            if (nhf == 0) load_d(nkb, dnxt);
+            dn_stage_load<MB>(a, t, semax, nkb, nhf, ar);
+        }
+        if (active) {
+            const uint16_t *A = sa[step & 1] + n * kPfLda + 32 * kq;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                f16x8 b[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t W = r < 2 ? wcur[j].x : wcur[j].y, W10 = W >> 10;
+                    // (a, -b) of this sub-block: a = d sc, b = dmin m
+                    const uint32_t sb = (scur[j] >> (8 * (r >> 1))) & 0xFFu;
+                    const f16x2 av = u2h(f16_pair(fp16_to_f32(dcur[j] & 0xFFFFu) * (float)(sb & 15u)));
+                    const f16x2 bv = u2h(f16_pair(-fp16_to_f32(dcur[j] >> 16) * (float)(sb >> 4)));
+                    uint32_t qb[4];
+                    if ((r & 1) == 0) {
+                        qb[0] = pc.pair<0>(W, W10); qb[1] = pc.pair<1>(W, W10);
+                        qb[2] = pc.pair<2>(W, W10); qb[3] = pc.pair<3>(W, W10);
+                    } else {
+                        qb[0] = pc.pair<4>(W, W10); qb[1] = pc.pair<5>(W, W10);
+                        qb[2] = pc.pair<6>(W, W10); qb[3] = pc.pair<7>(W, W10);
+                    }
+                    uint4 v;
+                    uint32_t *vv = reinterpret_cast<uint32_t *>(&v);
+#pragma unroll
+                    for (int p = 0; p < 4; p++) {
+                        const int pr = ((r & 1) ? 4 : 0) + p, s = pr < 5 ? pr : pr - 5;
+                        const f16x2 q = u2h(qb[p]) + u2h(nbias[s]);          // exact quant
+                        vv[p] = h2u(__builtin_elementwise_fma(q, av, bv));   // a q - b
+                    }
+                    b[j] = __builtin_bit_cast(f16x8, v);
+                }
+#pragma unroll
+                for (int i = 0; i < MB; i++) {
+                    const f16x8 av = *reinterpret_cast<const f16x8 *>(A + 16 * i * kPfLda + 8 * r);
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[j], acc[i][j], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (more) stage_store<MB>(sa[(step + 1) & 1], ar);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; j++) { wcur[j] = wnxt[j]; scur[j] = snxt[j]; }
+        if (more && nhf == 0)
+#pragma unroll
+            for (int j = 0; j < 4; j++) dcur[j] = dnxt[j];
+    }
+    if (!active) return;
+#pragma unroll
+    for (int i = 0; i < MB; i++)
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-            int m = 16 * i + 4 * (lane >> 4) + q;
-            if (m < rows) o[(int64_t)perm[off + r0 + m] * H + ncol] = acc[i][0][q];
+            const int m = 16 * i + 4 * kq + q;
+            if (m < t.rows) {
+                const int e = semax[m];
+                float *op = a.o + (int64_t)a.perm[t.off + t.r0 + m] * a.H;
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    if (c0 + 16 * j < a.H) op[c0 + 16 * j] = ldexpf(acc[i][j][q], e);
+            }
         }
+}
+
+__global__ void __launch_bounds__(kPfThreads)
+k_pf_down(DnArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const PfSlot sl = pf_slot((a.H + kPfDnCols - 1) / kPfDnCols);
+    if (sl.tile >= *a.n_tiles) return;
+    const PfTile t = pf_tile(sl.tile, a.tiles, a.counts, a.offsets);
+    int *semax = reinterpret_cast<int *>(lds + 2 * kPfABytes);
+    if (threadIdx.x < kPfRows) {
+        const int nI = a.I / kPfGuCols;
+        const int64_t gr = t.off + t.r0 + min((int)threadIdx.x, t.rows - 1);
+        int e = -1 << 30;
+        for (int c = 0; c < nI; c++) e = max(e, a.hexp[gr * nI + c]);
+        semax[threadIdx.x] = e;
+    }
+    __syncthreads();
+    switch ((t.rows + 15) >> 4) {
+        case 1: dn_tile<1>(a, lds, t, sl.ntile); break;
+        case 2: dn_tile<2>(a, lds, t, sl.ntile); break;
+        case 3: dn_tile<3>(a, lds, t, sl.ntile); break;
+        case 4: dn_tile<4>(a, lds, t, sl.ntile); break;
+        case 5: dn_tile<5>(a, lds, t, sl.ntile); break;
+        default: dn_tile<6>(a, lds, t, sl.ntile); break;
+    }
 }
 
 // Shared expert for prefill-mode calls: dense bf16 FFN per token, one
@@ -371,43 +613,52 @@ k_combine_p(const float *__restrict__ o, const float *__restrict__ w, const floa
 
 namespace bm_host {
 
-int prefill_tile_rows() { return BM; }
+int prefill_tile_rows() { return kPfRows; }
 
-int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T, const int32_t *ids,
-                       const float *w, float *y, const Buckets &b, int max_tiles, uint16_t *xb,
-                       uint16_t *h, float *o, float *hs, float *os, hipStream_t s) {
-    (void)ids; (void)xb;
+int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T, const float *w, float *y,
+                       const Buckets &b, int max_tiles, const PrefillBufs &pb, hipStream_t s) {
     const int H = L->H, I = L->I, k = L->k;
-    dim3 g1(I / 64, max_tiles);
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_gateup),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kPfGuLds);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_down),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kPfDnLds);
+        attr = true;
+    }
+    if (x_dtype == BITMOE_BF16) k_pf_xprep<1><<<T, 256, 0, s>>>(H, x, pb.x16, pb.xsc);
+    else k_pf_xprep<0><<<T, 256, 0, s>>>(H, x, pb.x16, pb.xsc);
+    BM_LAUNCH_CHECK();
     {
+        GuArgs a{H, I, k, (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q, (const uint8_t *)L->grid,
+                 pb.x16, pb.xsc, b.counts, b.offsets, b.perm, b.tiles, b.n_tiles, pb.h, pb.hexp};
         // the timing events, when set, are taken by the dispatch itself
         const TimingEvents ev = timing_events();
-        auto kg = x_dtype == BITMOE_BF16 ? k_prefill_gateup<1> : k_prefill_gateup<0>;
-        hipExtLaunchKernelGGL(kg, g1, dim3(256), 0, s, ev.start, ev.stop, 0, H, I, k, (const uint8_t *)L->gate_q,
-                              (const uint8_t *)L->up_q, (const uint8_t *)L->grid, x, (const int32_t *)b.counts,
-                              (const int32_t *)b.offsets, (const int32_t *)b.perm, (const int32_t *)b.tiles,
-                              (const int32_t *)b.n_tiles, h);
+        hipExtLaunchKernelGGL(k_pf_gateup, dim3(pf_grid(max_tiles, I / kPfGuCols)), dim3(kPfThreads), kPfGuLds, s,
+                              ev.start, ev.stop, 0, a);
         BM_LAUNCH_CHECK();
     }
-    dim3 g2(H / 64, max_tiles);
-    k_prefill_down<<<g2, 256, 0, s>>>(H, I, (const uint8_t *)L->down_q, h, b.counts, b.offsets, b.perm,
-                                      b.tiles, b.n_tiles, o);
-    BM_LAUNCH_CHECK();
+    {
+        DnArgs a{H, I, (const uint8_t *)L->down_q, pb.h, pb.hexp, b.counts, b.offsets, b.perm, b.tiles,
+                 b.n_tiles, pb.o};
+        k_pf_down<<<pf_grid(max_tiles, (H + kPfDnCols - 1) / kPfDnCols), kPfThreads, kPfDnLds, s>>>(a);
+        BM_LAUNCH_CHECK();
+    }
     const bool shared = L->shared_gate != nullptr;
     if (shared) {
         dim3 gs1(I / 64, T), gs2(H / 64, T);
         if (x_dtype == BITMOE_BF16)
             k_shared_gateup_rows<1><<<gs1, 64, 0, s>>>(H, I, (const uint4 *)L->shared_gate,
-                                                       (const uint4 *)L->shared_up, x, hs);
+                                                       (const uint4 *)L->shared_up, x, pb.hs);
         else
             k_shared_gateup_rows<0><<<gs1, 64, 0, s>>>(H, I, (const uint4 *)L->shared_gate,
-                                                       (const uint4 *)L->shared_up, x, hs);
+                                                       (const uint4 *)L->shared_up, x, pb.hs);
         BM_LAUNCH_CHECK();
-        k_shared_down_rows<<<gs2, 64, 0, s>>>(H, I, (const uint4 *)L->shared_down, hs, os);
+        k_shared_down_rows<<<gs2, 64, 0, s>>>(H, I, (const uint4 *)L->shared_down, pb.hs, pb.os);
         BM_LAUNCH_CHECK();
     }
     int64_t n = (int64_t)T * H;
-    k_combine_p<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(o, w, shared ? os : nullptr, y, T, H, k);
+    k_combine_p<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(pb.o, w, shared ? pb.os : nullptr, y, T, H, k);
     BM_LAUNCH_CHECK();
     return BITMOE_OK;
 }
