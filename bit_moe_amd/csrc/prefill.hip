@@ -2,7 +2,9 @@
 // matrix cores.  Prefill is compute-bound (page "Faire tenir un MoE de 284B
 // dans un portable de 128 Go", section "Un pre-remplissage a 790 t/s revele
 // le veritable goulot d'etranglement"), so the contraction runs on
-// v_mfma_f32_16x16x32_f16 with fp32 accumulation.
+// v_mfma_f32_32x32x16_f16 with fp32 accumulation (on gfx950 the 32x32 shape
+// issues at the full matrix rate from one wave and leaves room for the
+// dequantisation VALU work between MFMAs; 16x16x32 reaches about 80%).
 //
 // Operands.  Activations enter as fp16 scaled by a power of two per token
 // (k_pf_xprep), so any bf16/fp32 range maps onto fp16's normal range; the
@@ -15,13 +17,16 @@
 // permuted so that a lane's slots follow the packed layout; the activation
 // tile in LDS is read with the same permutation, so the products pair up.
 //
-// IQ2X runs decode through two LDS tables of ready-made fp16 pairs (2 x 4096
-// x 8 bytes): table 1 at R & 0xFFF gives weights 0..3 with their signs,
-// table 2 at R >> 3 weights 4..7 (R is the 15-bit run field of the tiled
-// words).  Two random 8-byte LDS reads per 8 weights.
+// IQ2X runs decode through two LDS tables: the codebook row of the run's
+// index as 8 fp16 magnitudes, and the run's 7 stored sign bits (parity signs
+// included) as 4 XOR masks over the fp16 pairs.  Both are kept in 16 copies,
+// one per 16-byte slot of a 256-byte line, and lane l reads slot l & 15: on
+// gfx950 a 16-lane group whose slots are distinct is served without bank
+// conflicts whatever lines it touches, so the random lookups run at full
+// LDS rate (random 8-byte lookups into one copy lose about half to conflicts).
 //
 // Work list: the bucketing pass emits tiles (expert e, first row r0) of up to
-// 96 rows of e's bucket; a tile runs ceil(rows/16) M-blocks (a compile-time
+// 96 rows of e's bucket; a tile runs ceil(rows/32) row blocks (a compile-time
 // count chosen per tile).  Workgroups are numbered so that all N-tiles of one
 // M-tile land on the same XCD (round-robin dispatch), which keeps the
 // activation rows they share in that XCD's L2.
@@ -42,17 +47,25 @@ using namespace bm;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfRows = 96;                   // rows per tile (6 M-blocks)
+constexpr int kPfRows = 96;                   // rows per tile (3 blocks of 32)
 constexpr int kPfHalf = 128;                  // K per LDS stage
-constexpr int kPfLda = kPfHalf + 8;           // padded LDS row (halfs): 272 B, conflict-free b128 reads
+// Activation stage in LDS, chunk-major: 16-byte chunk c (8 K values) of row m
+// at (c * kPfRows + m) * 16.  An MFMA operand read (16 lanes = 16 rows of one
+// chunk) and a staging write (8 rows x 2 chunks per 16 lanes) then touch
+// contiguous 128-byte runs, which gfx950's LDS serves without bank conflicts
+// (row-strided layouts, padded or XOR-swizzled, cost 4 extra cycles per read).
 constexpr int kPfGuCols = 256;                // h columns per gate/up workgroup
 constexpr int kPfDnCols = 512;                // output columns per down workgroup
 constexpr int kPfXcds = 8;
-constexpr int kPfTabBytes = 2 * 4096 * 8;
-constexpr int kPfABytes = kPfRows * kPfLda * 2;
+constexpr int kPfMagBytes = 256 * 256;          // 256 codebook rows x 16 copies x 16 bytes
+constexpr int kPfSgnBytes = 128 * 256;          // 128 sign patterns x 16 copies x 16 bytes
+constexpr int kPfTabBytes = kPfMagBytes + kPfSgnBytes;
+constexpr int kPfABytes = kPfRows * kPfHalf * 2;
 constexpr int kPfGuLds = kPfTabBytes + 2 * kPfABytes + kPfRows * (4 + 4 + 4) + kPfWaves * kPfRows * 4;
 constexpr int kPfDnLds = 2 * kPfABytes + kPfRows * (4 + 4);
 
@@ -141,33 +154,52 @@ k_pf_xprep(int H, const void *__restrict__ x, uint16_t *__restrict__ x16, float 
 // are the gate rows of those columns, blocks 2,3 the up rows.
 // ---------------------------------------------------------------------------
 
-// The LDS decode tables: fp16 pairs (+-m0, +-m1), (+-m2, +-m3) per entry.
-BM_DEV uint2 pf_tab_pairs(uint32_t m4, uint32_t sg) {
-    uint32_t h[4];
+// The LDS decode tables.  Magnitudes: line i holds, 16 times, the fp16
+// pairs (m0, m1), (m2, m3), (m4, m5), (m6, m7) of codebook row i.  Signs: line
+// i (i = the run field's bits 0-3 | bits 12-14 << 4, i.e. signs 0..2, the
+// parity of signs 0..3, signs 4..6) holds, 16 times, the XOR masks that
+// negate weight 2p in the low and weight 2p+1 in the high half of pair p;
+// sign 3 = parity ^ signs 0..2, sign 7 = parity ^ signs 4..6 (even parity).
+BM_DEV void pf_build_tables(const uint8_t *__restrict__ grid, uint8_t *lds) {
+    const int t = threadIdx.x;
+    u32x4 v;
+    uint8_t *line;
+    if (t < 256) {
+        const uint2 g = *reinterpret_cast<const uint2 *>(grid + 8 * t);
+        const uint32_t m[2] = {g.x, g.y};
+        uint32_t h[8];
 #pragma unroll
-    for (int b = 0; b < 4; b++) h[b] = f16_bits((float)((m4 >> (8 * b)) & 0xFFu)) | (((sg >> b) & 1u) << 15);
-    return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-}
-BM_DEV void pf_build_tables(const uint8_t *__restrict__ grid, uint2 *t1, uint2 *t2) {
-    for (int i = threadIdx.x; i < 4096; i += kPfThreads) {
-        // table 1, i = idx << 4 | parity(signs 0..3) << 3 | signs 0..2
-        const uint32_t idx1 = i >> 4, lo3 = i & 7u, p1 = (i >> 3) & 1u;
-        const uint32_t sg1 = lo3 | ((p1 ^ (__popc(lo3) & 1u)) << 3);
-        t1[i] = pf_tab_pairs(*reinterpret_cast<const uint32_t *>(grid + 8 * idx1), sg1);
-        // table 2, i = signs 4..6 << 9 | idx << 1 | parity(signs 0..3)
-        const uint32_t idx2 = (i >> 1) & 0xFFu, hi3 = (i >> 9) & 7u, p2 = i & 1u;
-        const uint32_t sg2 = hi3 | ((p2 ^ (__popc(hi3) & 1u)) << 3);
-        t2[i] = pf_tab_pairs(*reinterpret_cast<const uint32_t *>(grid + 8 * idx2 + 4), sg2);
+        for (int b = 0; b < 8; b++) h[b] = f16_bits((float)((m[b >> 2] >> (8 * (b & 3))) & 0xFFu));
+        v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        line = lds + 256 * t;
+    } else if (t < 384) {
+        const uint32_t i = t - 256, lo3 = i & 7u, p = (i >> 3) & 1u, hi3 = (i >> 4) & 7u;
+        const uint32_t sg = lo3 | ((p ^ (__popc(lo3) & 1u)) << 3) | (hi3 << 4) | ((p ^ (__popc(hi3) & 1u)) << 7);
+        uint32_t mk[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) mk[q] = (((sg >> (2 * q)) & 1u) << 15) | (((sg >> (2 * q + 1)) & 1u) << 31);
+        v = u32x4{mk[0], mk[1], mk[2], mk[3]};
+        line = lds + kPfMagBytes + 256 * i;
+    } else {
+        return;
     }
+#pragma unroll
+    for (int c = 0; c < 16; c++) *reinterpret_cast<u32x4 *>(line + 16 * c) = v;
 }
 
-// fp16 operand of run `second` of word W (8 weights, K order), times c2
-BM_DEV f16x8 pf_iq2x_run(const uint8_t *lds, uint32_t W, int second, uint32_t c2) {
-    const uint32_t o1 = second ? (W >> 14) & 0x7FF8u : (W << 1) & 0x7FF8u;
-    const uint32_t o2 = second ? (W >> 17) & 0x7FF8u : (W >> 2) & 0x7FF8u;
-    const uint2 e1 = *reinterpret_cast<const uint2 *>(lds + o1);
-    const uint2 e2 = *reinterpret_cast<const uint2 *>(lds + 32768 + o2);
-    const uint4 v = make_uint4(pk_mul(c2, e1.x), pk_mul(c2, e1.y), pk_mul(c2, e2.x), pk_mul(c2, e2.y));
+// Table lookups of run `second` of word W (magnitudes, sign masks); slot16 =
+// 16 (lane & 15)
+struct RunLut { u32x4 m, g; };
+BM_DEV RunLut pf_iq2x_lookup(const uint8_t *lds, uint32_t W, int second, uint32_t slot16) {
+    const uint32_t idx = second ? (W >> 21) & 0xFFu : (W >> 6) & 0xFFu;
+    const uint32_t sig = second ? ((W >> 17) & 0xFu) | ((W >> 25) & 0x70u) : ((W >> 2) & 0xFu) | ((W >> 10) & 0x70u);
+    return {*reinterpret_cast<const u32x4 *>(lds + (idx << 8) + slot16),
+            *reinterpret_cast<const u32x4 *>(lds + kPfMagBytes + (sig << 8) + slot16)};
+}
+// fp16 operand (8 weights, K order) of a looked-up run, times the group's c2
+BM_DEV f16x8 pf_iq2x_build(const RunLut &l, uint32_t c2) {
+    const uint4 v = make_uint4(pk_mul(c2, l.m.x ^ l.g.x), pk_mul(c2, l.m.y ^ l.g.y), pk_mul(c2, l.m.z ^ l.g.z),
+                               pk_mul(c2, l.m.w ^ l.g.w));
     return __builtin_bit_cast(f16x8, v);
 }
 
@@ -193,127 +225,170 @@ struct GuArgs {
     int32_t *hexp;
 };
 
-// Stage rows 0..16*MB-1 of activation half (kb, hf) into LDS buffer `dst`:
-// 16 loads of 16 bytes per row, up to 3 per thread.
-template <int MB>
-BM_DEV void gu_stage_load(const GuArgs &a, const int *stok, int kb, int hf, uint4 (&r)[3]) {
+// Activation stages (gate/up: x16 rows, down: h rows) go global -> registers
+// -> LDS, chunk-major with R rows: 16-byte chunk c (8 K values) of row m at
+// (c R + m) * 16.  R rows x 16 chunks = R/32 loads of 16 bytes per thread,
+// each group of 64 lanes taking 8 rows x 8 chunks (a 16-lane group then
+// writes two contiguous 128-byte runs).  Operand reads (32 rows of one chunk
+// per half-wave) touch contiguous 256-byte runs: no bank conflicts.
+struct StageIdx { int row, c; };
+BM_DEV StageIdx stage_idx(int p) {
+    const int u = threadIdx.x + kPfThreads * p, q = u >> 6, l = u & 63;
+    return {8 * (q >> 1) + (l & 7), 8 * (q & 1) + (l >> 3)};
+}
+template <int R>
+BM_DEV void stage_store(uint8_t *dst, const u32x4 (&r)[R / 32]) {
+#pragma unroll
+    for (int p = 0; p < R / 32; p++) {
+        const StageIdx x = stage_idx(p);
+        *reinterpret_cast<u32x4 *>(dst + (x.c * R + x.row) * 16) = r[p];
+    }
+}
+template <int R>
+BM_DEV void gu_stage_load(const GuArgs &a, const int *stok, int kb, int hf, u32x4 (&r)[R / 32]) {
     const int k0 = kb * kQK + hf * kPfHalf;
 #pragma unroll
-    for (int p = 0; p < 3; p++) {
-        const int u = threadIdx.x + kPfThreads * p, row = u >> 4, c = u & 15;
-        if (row < 16 * MB) r[p] = *reinterpret_cast<const uint4 *>(a.x16 + (int64_t)stok[row] * a.H + k0 + 8 * c);
+    for (int p = 0; p < R / 32; p++) {
+        const StageIdx x = stage_idx(p);
+        r[p] = *reinterpret_cast<const u32x4 *>(a.x16 + (int64_t)stok[x.row] * a.H + k0 + 8 * x.c);
     }
 }
-template <int MB>
-BM_DEV void stage_store(uint16_t *dst, const uint4 (&r)[3]) {
-#pragma unroll
-    for (int p = 0; p < 3; p++) {
-        const int u = threadIdx.x + kPfThreads * p, row = u >> 4, c = u & 15;
-        if (row < 16 * MB) *reinterpret_cast<uint4 *>(dst + row * kPfLda + 8 * c) = r[p];
-    }
+// MFMA A operand (32 rows x 16 K): rows 32i + (lane & 31), chunk 8 (lane >> 5) + t
+template <int R>
+BM_DEV f16x8 frag32(const uint8_t *buf, int i, int lane, int t) {
+    return *reinterpret_cast<const f16x8 *>(buf + ((8 * (lane >> 5) + t) * R + 32 * i + (lane & 31)) * 16);
 }
+BM_DEV f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+// row of accumulator register r of a 32x32 block in lane half kh
+BM_DEV int acc_row(int r, int kh) { return 8 * (r >> 2) + 4 * kh + (r & 3); }
 
+// ---------------------------------------------------------------------------
+// gate/up.  512 threads; wave w owns h columns hc0 + 32w .. +31: block 0 the
+// gate rows, block 1 the up rows of those columns (lane & 31 = column).  In a
+// stage (half superblock, 4 groups) lane half kh takes groups 2kh, 2kh+1 -
+// one 16-byte piece of the tiled slab - k-step t being run t & 3 of group
+// 2kh + (t >> 2), i.e. stage K offset 64 kh + 8 t.
+// ---------------------------------------------------------------------------
 template <int MB>
 BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
-    uint16_t *sa[2] = {reinterpret_cast<uint16_t *>(lds + kPfTabBytes),
-                       reinterpret_cast<uint16_t *>(lds + kPfTabBytes + kPfABytes)};
+    constexpr int R = 32 * MB;
+    uint8_t *const sa = lds + kPfTabBytes;              // A buffer b at sa + b * kPfABytes
     int *stok = reinterpret_cast<int *>(lds + kPfTabBytes + 2 * kPfABytes);
     float *sxs = reinterpret_cast<float *>(stok + kPfRows);
     int *sexp = reinterpret_cast<int *>(sxs + kPfRows);
     float *smax = reinterpret_cast<float *>(sexp + kPfRows);
-    const int lane = lane_id(), n = lane & 15, kq = lane >> 4;
+    const int lane = lane_id(), col = lane & 31, kh = lane >> 5;
+    const uint32_t slot16 = (uint32_t)(lane & 15) << 4;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = a.H / kQK;
     const int64_t slab = (int64_t)a.I * nb * 66;
-    const uint8_t *src[2] = {a.gate + t.e * slab, a.up + t.e * slab};
-    // this lane's h column in blocks 0/2 and 1/3
-    const int hc = ntile * kPfGuCols + 32 * w + n;
-    // word and scale indices of block j at superblock 0, half 0
-    // (one expert's slab is below 4 GiB: 32-bit offsets)
-    uint32_t wbase[2], dbase[2];
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int col = hc + 16 * j, P = col >> 6, r = col & 63;
-        wbase[j] = ((uint32_t)(P * nb * 4 * 64 + (kq >> 1) * 64 + r) * 2 + (kq & 1)) * 8;
-        dbase[j] = (uint32_t)(P * nb * 64 + r) * 2 + (uint32_t)a.I * nb * 64;
-    }
-    auto load_w = [&](int kb, int hf, uint2 (&wv)[4]) {
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            wv[j] = *reinterpret_cast<const uint2 *>(src[j >> 1] + wbase[j & 1] + kb * 4096 + hf * 2048);
+    const uint8_t *G = a.gate + t.e * slab, *U = a.up + t.e * slab;
+    const int hc = ntile * kPfGuCols + 32 * w + col, P = hc >> 6, pr = hc & 63;
+    // byte offsets at superblock 0, half 0 (one expert's slab is below 4 GiB)
+    const uint32_t qoff = (uint32_t)((P * nb * 4 + kh) * 64 + pr) * 16;
+    const uint32_t doff = (uint32_t)a.I * nb * 64 + (uint32_t)(P * nb * 64 + pr) * 2;
+    struct Slot { uint4 g, u; uint32_t dg, du; };       // words of one stage + raw fp16 d
+    auto load_slot = [&](int st, Slot &sl) {
+        const uint32_t o = qoff + (st >> 1) * 4096 + (st & 1) * 2048, od = doff + (st >> 1) * 128;
+        sl.g = *reinterpret_cast<const uint4 *>(G + o);
+        sl.u = *reinterpret_cast<const uint4 *>(U + o);
+        sl.dg = *reinterpret_cast<const uint16_t *>(G + od);
+        sl.du = *reinterpret_cast<const uint16_t *>(U + od);
     };
-    auto load_d = [&](int kb, float (&dv)[4]) {
+    f32x16 acc[MB][2];
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            dv[j] = 0.125f * fp16_to_f32(*reinterpret_cast<const uint16_t *>(src[j >> 1] + dbase[j & 1] + kb * 128));
-    };
-    f32x4 acc[MB][4];
+    for (int i = 0; i < MB; i++) acc[i][0] = acc[i][1] = (f32x16)0.f;
+    // One stage: 8 k-steps.  K-step s reads its activation operands first,
+    // then issues the table lookups of k-step s+2 (LDS reads retire in issue
+    // order, so the MFMAs of s wait only for their own operands while the
+    // lookups stay in flight), then builds its weight operands from the
+    // lookups issued two k-steps earlier and runs its MFMAs.
+    auto compute = [&](const uint8_t *A, const Slot &sl) {
+        // c = d/8 (2s+1) per (block, group) as fp16 pairs
+        const float dg = 0.125f * fp16_to_f32(sl.dg), du = 0.125f * fp16_to_f32(sl.du);
+        const uint32_t c2[2][2] = {{f16_pair(dg * (float)(2u * iq2x_scale(sl.g.x, sl.g.y) + 1u)),
+                                    f16_pair(dg * (float)(2u * iq2x_scale(sl.g.z, sl.g.w) + 1u))},
+                                   {f16_pair(du * (float)(2u * iq2x_scale(sl.u.x, sl.u.y) + 1u)),
+                                    f16_pair(du * (float)(2u * iq2x_scale(sl.u.z, sl.u.w) + 1u))}};
+        auto word = [&](const uint4 &v, int s) {
+            const int q = s >> 2, rr = s & 3;
+            return rr < 2 ? (q ? v.z : v.x) : (q ? v.w : v.y);
+        };
+        RunLut lg[8], lu[8];
+        lg[0] = pf_iq2x_lookup(lds, word(sl.g, 0), 0, slot16);
+        lu[0] = pf_iq2x_lookup(lds, word(sl.u, 0), 0, slot16);
+        lg[1] = pf_iq2x_lookup(lds, word(sl.g, 1), 1, slot16);
+        lu[1] = pf_iq2x_lookup(lds, word(sl.u, 1), 1, slot16);
 #pragma unroll
-    for (int i = 0; i < MB; i++)
+        for (int s = 0; s < 8; s++) {
+            f16x8 av[MB];
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint2 wcur[4], wnxt[4];
-    float dcur[4], dnxt[4];
-    uint4 ar[3];
-    load_w(0, 0, wcur);
-    load_d(0, dcur);
-    gu_stage_load<MB>(a, stok, 0, 0, ar);
-    stage_store<MB>(sa[0], ar);
-    __syncthreads();
-    const int nsteps = 2 * nb;
-    for (int step = 0; step < nsteps; step++) {
-        const bool more = step + 1 < nsteps;
-        const int nkb = (step + 1) >> 1, nhf = (step + 1) & 1;
-        if (more) {
-            load_w(nkb, nhf, wnxt);
-            if (nhf == 0) load_d(nkb, dnxt);
-            gu_stage_load<MB>(a, stok, nkb, nhf, ar);
-        }
-        uint32_t c2[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) c2[j] = f16_pair(dcur[j] * (float)(2u * iq2x_scale(wcur[j].x, wcur[j].y) + 1u));
-        const uint16_t *A = sa[step & 1] + n * kPfLda + 32 * kq;
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            f16x8 b[4];
-#pragma unroll
-            for (int j = 0; j < 4; j++) b[j] = pf_iq2x_run(lds, r < 2 ? wcur[j].x : wcur[j].y, r & 1, c2[j]);
+            for (int i = 0; i < MB; i++) av[i] = frag32<R>(A, i, lane, s);
+            if (s + 2 < 8) {
+                lg[s + 2] = pf_iq2x_lookup(lds, word(sl.g, s + 2), (s + 2) & 1, slot16);
+                lu[s + 2] = pf_iq2x_lookup(lds, word(sl.u, s + 2), (s + 2) & 1, slot16);
+            }
+            const f16x8 bg = pf_iq2x_build(lg[s], c2[0][s >> 2]);
+            const f16x8 bu = pf_iq2x_build(lu[s], c2[1][s >> 2]);
 #pragma unroll
             for (int i = 0; i < MB; i++) {
-                const f16x8 av = *reinterpret_cast<const f16x8 *>(A + 16 * i * kPfLda + 8 * r);
-#pragma unroll
-                for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[j], acc[i][j], 0, 0, 0);
+                acc[i][0] = mfma32(av[i], bg, acc[i][0]);
+                acc[i][1] = mfma32(av[i], bu, acc[i][1]);
             }
-            __builtin_amdgcn_sched_barrier(0);   // keep each k-step's operands short-lived
         }
-        if (more) stage_store<MB>(sa[(step + 1) & 1], ar);
+    };
+    // Pipeline over half-stages st = 2 kb + hf: the slot (words + scales) of
+    // stage st+2 is loaded at the start of stage st, the activations of st+1
+    // too (issued first, so the wait before their LDS store leaves the slot
+    // loads in flight: memory counters retire in issue order).  The three
+    // slots rotate by call, never by copy (a copy would wait for the loads).
+    const int nsteps = 2 * nb;
+    u32x4 ar[R / 32];
+    auto stage = [&](int st, Slot &cur, Slot &pre) {
+        const int s1 = st + 1, s2 = st + 2;
+        // issue order pinned (compiler memory barriers): activations, then the slot
+        asm volatile("" ::: "memory");
+        if (s1 < nsteps) gu_stage_load<R>(a, stok, s1 >> 1, s1 & 1, ar);
+        asm volatile("" ::: "memory");
+        if (s2 < nsteps) load_slot(s2, pre);
+        asm volatile("" ::: "memory");
+        compute(sa + (st & 1) * kPfABytes, cur);
+        if (s1 < nsteps) stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 4; j++) wcur[j] = wnxt[j];
-        if (more && nhf == 0)
-#pragma unroll
-            for (int j = 0; j < 4; j++) dcur[j] = dnxt[j];
+    };
+    Slot q0, q1, q2;
+    gu_stage_load<R>(a, stok, 0, 0, ar);
+    load_slot(0, q0);
+    if (nsteps > 1) load_slot(1, q1);
+    stage_store<R>(sa, ar);
+    // drain the prologue loads: otherwise the compiler merges their pending
+    // state into the loop header and waits on the current slot every pass
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int st = 0;
+    for (; st + 3 <= nsteps; st += 3) {
+        stage(st, q0, q2);
+        stage(st + 1, q1, q0);
+        stage(st + 2, q2, q1);
     }
-    // epilogue: lane holds rows 16i + 4kq + q, columns hc (j=0) and hc+16 (j=1);
-    // h is computed twice (row maxima first, then the scaled stores)
+    if (st < nsteps) stage(st, q0, q2);
+    if (st + 1 < nsteps) stage(st + 1, q1, q0);
+    // epilogue: lane holds rows 32i + acc_row(r, kh), column hc; h is computed
+    // twice (row maxima over the workgroup's 256 columns first, then the
+    // stores scaled by the row's power of two)
 #pragma unroll
     for (int i = 0; i < MB; i++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const int m = 16 * i + 4 * kq + q;
+        for (int r = 0; r < 16; r++) {
+            const int m = 32 * i + acc_row(r, kh);
             const float xs = sxs[m];
-            float mx = 0.f;
+            float mx = fabsf(silu(acc[i][0][r] * xs) * (acc[i][1][r] * xs));
 #pragma unroll
-            for (int j = 0; j < 2; j++)
-                mx = fmaxf(mx, fabsf(silu(acc[i][j][q] * xs) * (acc[i][j + 2][q] * xs)));
-            mx = fmaxf(mx, __shfl_xor(mx, 1, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 2, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 4, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 8, kWave));
-            if (n == 0) smax[w * kPfRows + m] = mx;
+            for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+            if (col == 0) smax[w * kPfRows + m] = mx;
         }
     __syncthreads();
-    if (threadIdx.x < 16 * MB) {
+    if (threadIdx.x < R) {
         float mx = 0.f;
 #pragma unroll
         for (int v = 0; v < kPfWaves; v++) mx = fmaxf(mx, smax[v * kPfRows + threadIdx.x]);
@@ -326,15 +401,12 @@ BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
 #pragma unroll
     for (int i = 0; i < MB; i++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const int m = 16 * i + 4 * kq + q;
+        for (int r = 0; r < 16; r++) {
+            const int m = 32 * i + acc_row(r, kh);
             if (m < t.rows) {
-                const int e = sexp[m];
                 const float xs = sxs[m];
-                uint16_t *hp = a.h + (int64_t)(t.off + t.r0 + m) * a.I + hc;
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-                    hp[16 * j] = (uint16_t)f16_bits(ldexpf(silu(acc[i][j][q] * xs) * (acc[i][j + 2][q] * xs), -e));
+                a.h[(int64_t)(t.off + t.r0 + m) * a.I + hc] =
+                    (uint16_t)f16_bits(ldexpf(silu(acc[i][0][r] * xs) * (acc[i][1][r] * xs), -sexp[m]));
             }
         }
 }
@@ -342,6 +414,10 @@ BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
 __global__ void __launch_bounds__(kPfThreads)
 k_pf_gateup(GuArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    // Mentioning an accumulation register makes the compiler pick the MFMA
+    // form that keeps C/D in AGPRs (otherwise every MFMA reads and writes 16
+    // arch VGPRs, competing with the dequantisation VALU work for them).
+    asm volatile("" ::: "a0");
     const PfSlot sl = pf_slot(a.I / kPfGuCols);
     if (sl.tile >= *a.n_tiles) return;
     const PfTile t = pf_tile(sl.tile, a.tiles, a.counts, a.offsets);
@@ -352,21 +428,20 @@ k_pf_gateup(GuArgs a) {
         stok[threadIdx.x] = tok;
         sxs[threadIdx.x] = a.xsc[tok];
     }
-    pf_build_tables(a.grid, reinterpret_cast<uint2 *>(lds), reinterpret_cast<uint2 *>(lds + 32768));
+    pf_build_tables(a.grid, lds);
     __syncthreads();
-    switch ((t.rows + 15) >> 4) {
+    switch ((t.rows + 31) >> 5) {
         case 1: gu_tile<1>(a, lds, t, sl.ntile); break;
         case 2: gu_tile<2>(a, lds, t, sl.ntile); break;
-        case 3: gu_tile<3>(a, lds, t, sl.ntile); break;
-        case 4: gu_tile<4>(a, lds, t, sl.ntile); break;
-        case 5: gu_tile<5>(a, lds, t, sl.ntile); break;
-        default: gu_tile<6>(a, lds, t, sl.ntile); break;
+        default: gu_tile<3>(a, lds, t, sl.ntile); break;
     }
 }
 
 // ---------------------------------------------------------------------------
-// down.  512 threads; wave w owns output columns n0 + 64w .. +63 (4 blocks).
-// Lane kq of a half-superblock stage takes sub-blocks 8hf + 2kq, +1.
+// down.  512 threads; wave w owns output columns n0 + 64w .. +63 (blocks 0,1
+// of 32).  In a stage (half superblock, 8 sub-blocks) lane half kh takes
+// sub-blocks 4kh..4kh+3 - one 16-byte piece - k-step t being half t & 1 of
+// sub-block 4kh + (t >> 1): stage K offset 64 kh + 8 t again.
 // ---------------------------------------------------------------------------
 struct DnArgs {
     int H, I;
@@ -377,57 +452,53 @@ struct DnArgs {
     float *o;
 };
 
-template <int MB>
-BM_DEV void dn_stage_load(const DnArgs &a, const PfTile &t, const int *semax, int kb, int hf,
-                          uint4 (&r)[3]) {
+template <int R>
+BM_DEV void dn_stage_load(const DnArgs &a, const PfTile &t, const int *semax, int kb, int hf, u32x4 (&r)[R / 32]) {
     const int k0 = kb * kQK + hf * kPfHalf, nI = a.I / kPfGuCols;
 #pragma unroll
-    for (int p = 0; p < 3; p++) {
-        const int u = threadIdx.x + kPfThreads * p, row = u >> 4, c = u & 15;
-        if (row < 16 * MB) {
-            const int64_t gr = t.off + t.r0 + min(row, t.rows - 1);
-            uint4 v = *reinterpret_cast<const uint4 *>(a.h + gr * a.I + k0 + 8 * c);
-            const int d = a.hexp[gr * nI + kb] - semax[row];
-            if (d != 0) {
-                const uint32_t f = f16_pow2(d) * 0x10001u;
-                v = make_uint4(pk_mul(v.x, f), pk_mul(v.y, f), pk_mul(v.z, f), pk_mul(v.w, f));
-            }
-            r[p] = v;
+    for (int p = 0; p < R / 32; p++) {
+        const StageIdx x = stage_idx(p);
+        const int64_t gr = t.off + t.r0 + min(x.row, t.rows - 1);
+        u32x4 v = *reinterpret_cast<const u32x4 *>(a.h + gr * a.I + k0 + 8 * x.c);
+        const int d = a.hexp[gr * nI + kb] - semax[x.row];
+        if (d != 0) {
+            const uint32_t f = f16_pow2(d) * 0x10001u;
+            v = u32x4{pk_mul(v.x, f), pk_mul(v.y, f), pk_mul(v.z, f), pk_mul(v.w, f)};
         }
+        r[p] = v;
     }
 }
 
 template <int MB>
 BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
-    uint16_t *sa[2] = {reinterpret_cast<uint16_t *>(lds), reinterpret_cast<uint16_t *>(lds + kPfABytes)};
+    constexpr int R = 32 * MB;
+    uint8_t *const sa = lds;                             // A buffer b at sa + b * kPfABytes
     int *semax = reinterpret_cast<int *>(lds + 2 * kPfABytes);
-    const int lane = lane_id(), n = lane & 15, kq = lane >> 4;
+    const int lane = lane_id(), col = lane & 31, kh = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = a.I / kQK;
     const int64_t S = (int64_t)a.H * nb;
     const uint8_t *D = a.down + (int64_t)t.e * S * 84;
-    const int c0 = ntile * kPfDnCols + 64 * w + n;
+    const int c0 = ntile * kPfDnCols + 64 * w + col;
     const bool active = ntile * kPfDnCols + 64 * w < a.H;     // wave-uniform
-    // byte offsets at superblock 0 (one expert's slab is below 4 GiB)
-    uint32_t qoff[4], soff[4], doff[4];
+    uint32_t qoff[2], soff[2], doff[2];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int col = min(c0 + 16 * j, a.H - 1), P = col >> 6, r = col & 63;
-        const uint32_t pk64 = (uint32_t)(P * nb * 64 + r);           // (P nb + kb) 64 + r at kb = 0
-        qoff[j] = ((uint32_t)(P * nb * 256 + (kq >> 1) * 64 + r) * 2 + (kq & 1)) * 8;
-        soff[j] = (uint32_t)(S * 64) + pk64 * 16 + 2 * kq;
+    for (int j = 0; j < 2; j++) {
+        const int cc = min(c0 + 32 * j, a.H - 1), P = cc >> 6, pr = cc & 63;
+        const uint32_t pk64 = (uint32_t)(P * nb * 64 + pr);          // (P nb + kb) 64 + r at kb = 0
+        qoff[j] = (uint32_t)((P * nb * 4 + kh) * 64 + pr) * 16;
+        soff[j] = (uint32_t)(S * 64) + pk64 * 16 + 4 * kh;
         doff[j] = (uint32_t)(S * 80) + pk64 * 4;
     }
-    auto load_w = [&](int kb, int hf, uint2 (&wv)[4], uint32_t (&sv)[4]) {
+    struct Slot { uint4 w[2]; uint32_t sc[2], dd[2]; };     // words, 4 scale bytes, d|dmin per block
+    auto load_slot = [&](int st, Slot &sl) {
+        const int kb = st >> 1, hf = st & 1;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            wv[j] = *reinterpret_cast<const uint2 *>(D + qoff[j] + kb * 4096 + hf * 2048);
-            sv[j] = *reinterpret_cast<const uint16_t *>(D + soff[j] + kb * 1024 + 8 * hf);
+        for (int j = 0; j < 2; j++) {
+            sl.w[j] = *reinterpret_cast<const uint4 *>(D + qoff[j] + kb * 4096 + hf * 2048);
+            sl.sc[j] = *reinterpret_cast<const uint32_t *>(D + soff[j] + kb * 1024 + 8 * hf);
+            sl.dd[j] = *reinterpret_cast<const uint32_t *>(D + doff[j] + kb * 256);
         }
-    };
-    auto load_d = [&](int kb, uint32_t (&dv)[4]) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) dv[j] = *reinterpret_cast<const uint32_t *>(D + doff[j] + kb * 256);
     };
     const Q2kPairConsts pc;
     uint32_t nbias[5];
@@ -437,88 +508,85 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
         asm volatile("" : "+s"(v));
         nbias[s] = v;
     }
-    f32x4 acc[MB][4];
+    f32x16 acc[MB][2];
 #pragma unroll
-    for (int i = 0; i < MB; i++)
+    for (int i = 0; i < MB; i++) acc[i][0] = acc[i][1] = (f32x16)0.f;
+    auto compute = [&](const uint8_t *A, const Slot &sl) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint2 wcur[4], wnxt[4];
-    uint32_t scur[4], snxt[4], dcur[4], dnxt[4];
-    uint4 ar[3];
-    load_w(0, 0, wcur, scur);
-    load_d(0, dcur);
-    dn_stage_load<MB>(a, t, semax, 0, 0, ar);
-    stage_store<MB>(sa[0], ar);
-    __syncthreads();
-    const int nsteps = 2 * nb;
-    for (int step = 0; step < nsteps; step++) {
-        const bool more = step + 1 < nsteps;
-        const int nkb = (step + 1) >> 1, nhf = (step + 1) & 1;
-        if (more) {
-            load_w(nkb, nhf, wnxt, snxt);
-            if (nhf == 0) load_d(nkb, dnxt);
-            dn_stage_load<MB>(a, t, semax, nkb, nhf, ar);
-        }
-        if (active) {
-            const uint16_t *A = sa[step & 1] + n * kPfLda + 32 * kq;
+        for (int s = 0; s < 8; s++) {
+            f16x8 b[2];
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                f16x8 b[4];
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const uint32_t W = r < 2 ? wcur[j].x : wcur[j].y, W10 = W >> 10;
-                    // (a, -b) of this sub-block: a = d sc, b = dmin m
-                    const uint32_t sb = (scur[j] >> (8 * (r >> 1))) & 0xFFu;
-                    const f16x2 av = u2h(f16_pair(fp16_to_f32(dcur[j] & 0xFFFFu) * (float)(sb & 15u)));
-                    const f16x2 bv = u2h(f16_pair(-fp16_to_f32(dcur[j] >> 16) * (float)(sb >> 4)));
-                    uint32_t qb[4];
-                    if ((r & 1) == 0) {
-                        qb[0] = pc.pair<0>(W, W10); qb[1] = pc.pair<1>(W, W10);
-                        qb[2] = pc.pair<2>(W, W10); qb[3] = pc.pair<3>(W, W10);
-                    } else {
-                        qb[0] = pc.pair<4>(W, W10); qb[1] = pc.pair<5>(W, W10);
-                        qb[2] = pc.pair<6>(W, W10); qb[3] = pc.pair<7>(W, W10);
-                    }
-                    uint4 v;
-                    uint32_t *vv = reinterpret_cast<uint32_t *>(&v);
-#pragma unroll
-                    for (int p = 0; p < 4; p++) {
-                        const int pr = ((r & 1) ? 4 : 0) + p, s = pr < 5 ? pr : pr - 5;
-                        const f16x2 q = u2h(qb[p]) + u2h(nbias[s]);          // exact quant
-                        vv[p] = h2u(__builtin_elementwise_fma(q, av, bv));   // a q - b
-                    }
-                    b[j] = __builtin_bit_cast(f16x8, v);
+            for (int j = 0; j < 2; j++) {
+                const uint32_t wsel[4] = {sl.w[j].x, sl.w[j].y, sl.w[j].z, sl.w[j].w};
+                const uint32_t W = wsel[s >> 1], W10 = W >> 10;
+                // (a, -b) of this sub-block: a = d sc, b = dmin m
+                const uint32_t sb = (sl.sc[j] >> (8 * (s >> 1))) & 0xFFu;
+                const f16x2 av = u2h(f16_pair(fp16_to_f32(sl.dd[j] & 0xFFFFu) * (float)(sb & 15u)));
+                const f16x2 bv = u2h(f16_pair(-fp16_to_f32(sl.dd[j] >> 16) * (float)(sb >> 4)));
+                uint32_t qb[4];
+                if ((s & 1) == 0) {
+                    qb[0] = pc.pair<0>(W, W10); qb[1] = pc.pair<1>(W, W10);
+                    qb[2] = pc.pair<2>(W, W10); qb[3] = pc.pair<3>(W, W10);
+                } else {
+                    qb[0] = pc.pair<4>(W, W10); qb[1] = pc.pair<5>(W, W10);
+                    qb[2] = pc.pair<6>(W, W10); qb[3] = pc.pair<7>(W, W10);
                 }
+                uint4 v;
+                uint32_t *vv = reinterpret_cast<uint32_t *>(&v);
 #pragma unroll
-                for (int i = 0; i < MB; i++) {
-                    const f16x8 av = *reinterpret_cast<const f16x8 *>(A + 16 * i * kPfLda + 8 * r);
-#pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[j], acc[i][j], 0, 0, 0);
+                for (int p = 0; p < 4; p++) {
+                    const int pp = ((s & 1) ? 4 : 0) + p, sh = pp < 5 ? pp : pp - 5;
+                    const f16x2 q = u2h(qb[p]) + u2h(nbias[sh]);          // exact quant
+                    vv[p] = h2u(__builtin_elementwise_fma(q, av, bv));    // a q - b
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                b[j] = __builtin_bit_cast(f16x8, v);
             }
+#pragma unroll
+            for (int i = 0; i < MB; i++) {
+                const f16x8 av = frag32<R>(A, i, lane, s);
+                acc[i][0] = mfma32(av, b[0], acc[i][0]);
+                acc[i][1] = mfma32(av, b[1], acc[i][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) stage_store<MB>(sa[(step + 1) & 1], ar);
+    };
+    const int nsteps = 2 * nb;
+    u32x4 ar[R / 32];
+    auto stage = [&](int st, Slot &cur, Slot &pre) {
+        const int s1 = st + 1, s2 = st + 2;
+        if (s1 < nsteps) dn_stage_load<R>(a, t, semax, s1 >> 1, s1 & 1, ar);
+        if (s2 < nsteps) load_slot(s2, pre);
+        __builtin_amdgcn_sched_barrier(0);
+        if (active) compute(sa + (st & 1) * kPfABytes, cur);
+        if (s1 < nsteps) stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 4; j++) { wcur[j] = wnxt[j]; scur[j] = snxt[j]; }
-        if (more && nhf == 0)
-#pragma unroll
-            for (int j = 0; j < 4; j++) dcur[j] = dnxt[j];
+    };
+    Slot q0, q1, q2;
+    dn_stage_load<R>(a, t, semax, 0, 0, ar);
+    load_slot(0, q0);
+    if (nsteps > 1) load_slot(1, q1);
+    stage_store<R>(sa, ar);
+    __builtin_amdgcn_s_waitcnt(0);       // see gu_tile
+    __syncthreads();
+    int st = 0;
+    for (; st + 3 <= nsteps; st += 3) {
+        stage(st, q0, q2);
+        stage(st + 1, q1, q0);
+        stage(st + 2, q2, q1);
     }
+    if (st < nsteps) stage(st, q0, q2);
+    if (st + 1 < nsteps) stage(st + 1, q1, q0);
     if (!active) return;
 #pragma unroll
     for (int i = 0; i < MB; i++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const int m = 16 * i + 4 * kq + q;
+        for (int r = 0; r < 16; r++) {
+            const int m = 32 * i + acc_row(r, kh);
             if (m < t.rows) {
                 const int e = semax[m];
                 float *op = a.o + (int64_t)a.perm[t.off + t.r0 + m] * a.H;
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    if (c0 + 16 * j < a.H) op[c0 + 16 * j] = ldexpf(acc[i][j][q], e);
+                op[c0] = ldexpf(acc[i][0][r], e);
+                op[c0 + 32] = ldexpf(acc[i][1][r], e);
             }
         }
 }
@@ -526,6 +594,7 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
 __global__ void __launch_bounds__(kPfThreads)
 k_pf_down(DnArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    asm volatile("" ::: "a0");           // accumulators in AGPRs (see k_pf_gateup)
     const PfSlot sl = pf_slot((a.H + kPfDnCols - 1) / kPfDnCols);
     if (sl.tile >= *a.n_tiles) return;
     const PfTile t = pf_tile(sl.tile, a.tiles, a.counts, a.offsets);
@@ -538,13 +607,10 @@ k_pf_down(DnArgs a) {
         semax[threadIdx.x] = e;
     }
     __syncthreads();
-    switch ((t.rows + 15) >> 4) {
+    switch ((t.rows + 31) >> 5) {
         case 1: dn_tile<1>(a, lds, t, sl.ntile); break;
         case 2: dn_tile<2>(a, lds, t, sl.ntile); break;
-        case 3: dn_tile<3>(a, lds, t, sl.ntile); break;
-        case 4: dn_tile<4>(a, lds, t, sl.ntile); break;
-        case 5: dn_tile<5>(a, lds, t, sl.ntile); break;
-        default: dn_tile<6>(a, lds, t, sl.ntile); break;
+        default: dn_tile<3>(a, lds, t, sl.ntile); break;
     }
 }
 
