@@ -113,7 +113,7 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
 }
 
 size_t route_ws_bytes(const bitmoe_layer *L, int T, int x_dtype) {
-    if (T >= kMfmaRouterMinT && x_dtype == BITMOE_BF16) return up256((size_t)T * L->E * 4);
+    if (T >= kMfmaRouterMinT && x_dtype == BITMOE_BF16) return up256(bm_host::router_mfma_part_floats(T, L->E) * 4);
     return up256((size_t)std::min(T, bm_host::router_tokens_per_launch()) * L->E * 4);
 }
 
@@ -190,11 +190,8 @@ int moe_route(const bitmoe_layer *L, const void *x, int x_dtype, int T, float *l
     if (rc) return rc;
     hipStream_t s = as_stream(stream);
     float *part = static_cast<float *>(ws);
-    if (T >= kMfmaRouterMinT && x_dtype == BITMOE_BF16) {
-        float *lg = logits ? logits : part;
-        if ((rc = bm_host::launch_router_mfma(L, x, T, lg, s))) return rc;
-        return bm_host::launch_topk(lg, T, L->E, L->k, ids, w, s);
-    }
+    if (T >= kMfmaRouterMinT && x_dtype == BITMOE_BF16)
+        return bm_host::launch_router_mfma(L, x, T, logits, ids, w, part, s);
     // one wave per expert row, token batches of router_tokens_per_launch()
     const int NT = bm_host::router_tokens_per_launch();
     const size_t xs = x_dtype == BITMOE_BF16 ? 2 : 4;

@@ -257,8 +257,9 @@ int launch_pack_bf16(const void *src, void *dst, int N, int K, hipStream_t s);
 int router_tokens_per_launch();
 int launch_router_gemv(const bitmoe_layer *L, const void *x, int x_dtype, int T,
                        float *logits, hipStream_t s);
-int launch_router_mfma(const bitmoe_layer *L, const void *x, int T, float *logits,
-                       hipStream_t s);
+size_t router_mfma_part_floats(int T, int E);
+int launch_router_mfma(const bitmoe_layer *L, const void *x, int T, float *logits, int32_t *ids, float *w,
+                       float *part, hipStream_t s);
 int launch_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w, hipStream_t s);
 
 // bucketing

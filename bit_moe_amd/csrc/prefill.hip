@@ -39,7 +39,9 @@
 //           routing weights.
 #include <hip/hip_ext.h>
 
-#include "common.h"
+#include <type_traits>
+
+#include "device_util.h"
 
 namespace {
 
@@ -344,18 +346,25 @@ BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
     // slots rotate by call, never by copy (a copy would wait for the loads).
     const int nsteps = 2 * nb;
     u32x4 ar[R / 32];
-    auto stage = [&](int st, Slot &cur, Slot &pre) {
+    // FULL: stages whose prefetches (st+1, st+2) are both in range, so the
+    // main loop carries no conditionals (a conditional load path there breaks
+    // the issue order and the compiler then drains every load).
+    auto stage = [&](auto full, int st, Slot &cur, Slot &pre) {
         const int s1 = st + 1, s2 = st + 2;
-        // issue order pinned (compiler memory barriers): activations, then the slot
+        // issue order pinned (compiler memory barriers): activations, then the
+        // slot, so the wait before the activation store leaves the slot in flight
         asm volatile("" ::: "memory");
-        if (s1 < nsteps) gu_stage_load<R>(a, stok, s1 >> 1, s1 & 1, ar);
+        if (full || s1 < nsteps) gu_stage_load<R>(a, stok, s1 >> 1, s1 & 1, ar);
         asm volatile("" ::: "memory");
-        if (s2 < nsteps) load_slot(s2, pre);
+        if (full || s2 < nsteps) load_slot(s2, pre);
         asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         compute(sa + (st & 1) * kPfABytes, cur);
-        if (s1 < nsteps) stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
+        if (full || s1 < nsteps) stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
         __syncthreads();
     };
+    using Full = std::integral_constant<bool, true>;
+    using Part = std::integral_constant<bool, false>;
     Slot q0, q1, q2;
     gu_stage_load<R>(a, stok, 0, 0, ar);
     load_slot(0, q0);
@@ -366,26 +375,40 @@ BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int st = 0;
-    for (; st + 3 <= nsteps; st += 3) {
-        stage(st, q0, q2);
-        stage(st + 1, q1, q0);
-        stage(st + 2, q2, q1);
+    for (; st + 5 <= nsteps; st += 3) {
+        stage(Full{}, st, q0, q2);
+        stage(Full{}, st + 1, q1, q0);
+        stage(Full{}, st + 2, q2, q1);
     }
-    if (st < nsteps) stage(st, q0, q2);
-    if (st + 1 < nsteps) stage(st + 1, q1, q0);
-    // epilogue: lane holds rows 32i + acc_row(r, kh), column hc; h is computed
-    // twice (row maxima over the workgroup's 256 columns first, then the
-    // stores scaled by the row's power of two)
+    // at most 4 stages remain; the slot rotation continues from q0
+    if (st < nsteps) stage(Part{}, st, q0, q2);
+    if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0);
+    if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1);
+    if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2);
+    // epilogue: lane holds rows 32i + acc_row(r, kh), column hc.  h in
+    // registers; row maxima over the workgroup's 256 columns (32 lanes of a
+    // half-wave, then the 8 waves through LDS) give each row's power of two.
+    float hv[MB][16];
 #pragma unroll
     for (int i = 0; i < MB; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-            const int m = 32 * i + acc_row(r, kh);
-            const float xs = sxs[m];
-            float mx = fabsf(silu(acc[i][0][r] * xs) * (acc[i][1][r] * xs));
+            const float xs = sxs[32 * i + acc_row(r, kh)];
+            hv[i][r] = silu(acc[i][0][r] * xs) * (acc[i][1][r] * xs);
+        }
 #pragma unroll
-            for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-            if (col == 0) smax[w * kPfRows + m] = mx;
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            // max over the half-wave (DPP row shifts, then row 0 -> 1 and 2 -> 3):
+            // complete in lanes 31 and 63
+            float mx = fabsf(hv[i][r]);
+            mx = dpp_max<0x111, 0xF>(mx);
+            mx = dpp_max<0x112, 0xF>(mx);
+            mx = dpp_max<0x114, 0xF>(mx);
+            mx = dpp_max<0x118, 0xF>(mx);
+            mx = dpp_max<0x142, 0xA>(mx);
+            if (col == 31) smax[w * kPfRows + 32 * i + acc_row(r, kh)] = mx;
         }
     __syncthreads();
     if (threadIdx.x < R) {
@@ -403,11 +426,7 @@ BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int m = 32 * i + acc_row(r, kh);
-            if (m < t.rows) {
-                const float xs = sxs[m];
-                a.h[(int64_t)(t.off + t.r0 + m) * a.I + hc] =
-                    (uint16_t)f16_bits(ldexpf(silu(acc[i][0][r] * xs) * (acc[i][1][r] * xs), -sexp[m]));
-            }
+            if (m < t.rows) a.h[(int64_t)(t.off + t.r0 + m) * a.I + hc] = (uint16_t)f16_bits(ldexpf(hv[i][r], -sexp[m]));
         }
 }
 
@@ -552,15 +571,20 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
     };
     const int nsteps = 2 * nb;
     u32x4 ar[R / 32];
-    auto stage = [&](int st, Slot &cur, Slot &pre) {
+    auto stage = [&](auto full, int st, Slot &cur, Slot &pre) {      // as in gu_tile
         const int s1 = st + 1, s2 = st + 2;
-        if (s1 < nsteps) dn_stage_load<R>(a, t, semax, s1 >> 1, s1 & 1, ar);
-        if (s2 < nsteps) load_slot(s2, pre);
+        asm volatile("" ::: "memory");
+        if (full || s1 < nsteps) dn_stage_load<R>(a, t, semax, s1 >> 1, s1 & 1, ar);
+        asm volatile("" ::: "memory");
+        if (full || s2 < nsteps) load_slot(s2, pre);
+        asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         if (active) compute(sa + (st & 1) * kPfABytes, cur);
-        if (s1 < nsteps) stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
+        if (full || s1 < nsteps) stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
         __syncthreads();
     };
+    using Full = std::integral_constant<bool, true>;
+    using Part = std::integral_constant<bool, false>;
     Slot q0, q1, q2;
     dn_stage_load<R>(a, t, semax, 0, 0, ar);
     load_slot(0, q0);
@@ -569,13 +593,15 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
     __builtin_amdgcn_s_waitcnt(0);       // see gu_tile
     __syncthreads();
     int st = 0;
-    for (; st + 3 <= nsteps; st += 3) {
-        stage(st, q0, q2);
-        stage(st + 1, q1, q0);
-        stage(st + 2, q2, q1);
+    for (; st + 5 <= nsteps; st += 3) {
+        stage(Full{}, st, q0, q2);
+        stage(Full{}, st + 1, q1, q0);
+        stage(Full{}, st + 2, q2, q1);
     }
-    if (st < nsteps) stage(st, q0, q2);
-    if (st + 1 < nsteps) stage(st + 1, q1, q0);
+    if (st < nsteps) stage(Part{}, st, q0, q2);
+    if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0);
+    if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1);
+    if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2);
     if (!active) return;
 #pragma unroll
     for (int i = 0; i < MB; i++)

@@ -43,60 +43,86 @@ k_router_gemv(const uint16_t *__restrict__ wr, const void *__restrict__ x, int T
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Split-K: workgroup (token tile of 64, expert tile of 256, K slice s)
+// writes its partial sums to part[s][t][e]; k_topk_sum adds the slices in a
+// fixed order (deterministic).  Four waves, each 64 tokens x 64 experts.
+constexpr int kRouterSplit = 8;
 __global__ void __launch_bounds__(256)
-k_router_mfma(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, int T, int H, int E,
-              float *__restrict__ C) {
+k_router_splitk(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, int T, int H, int E, int kslice,
+                float *__restrict__ part) {
     constexpr int BK = 64, LD = BK + 8;   // padded row stride (bf16 elements)
     __shared__ __attribute__((aligned(16))) uint16_t sa[64 * LD];
-    __shared__ __attribute__((aligned(16))) uint16_t sb[64 * LD];
-    int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
-    int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-    f32x4 acc[2][2];
+    __shared__ __attribute__((aligned(16))) uint16_t sb[256 * LD];
+    const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 256, sl = blockIdx.z;
+    const int kbeg = sl * kslice, kend = min(H, kbeg + kslice);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    f32x4 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < H; k0 += BK) {
-        // 64 rows x 64 cols = 512 pieces of 8 bf16 per operand; 2 per thread
+        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = kbeg; k0 < kend; k0 += BK) {
+        // A: 64 rows x 64 = 512 pieces of 8 bf16 (2 per thread); B: 256 rows (8 per thread)
 #pragma unroll
         for (int p = 0; p < 2; p++) {
-            int piece = tid + 256 * p, r = piece >> 3, c = (piece & 7) * 8;
-            int ra = min(m0 + r, T - 1), rb = min(n0 + r, E - 1);
-            uint4 va = *reinterpret_cast<const uint4 *>(X + (int64_t)ra * H + k0 + c);
-            uint4 vb = *reinterpret_cast<const uint4 *>(W + (int64_t)rb * H + k0 + c);
-            *reinterpret_cast<uint4 *>(sa + r * LD + c) = va;
-            *reinterpret_cast<uint4 *>(sb + r * LD + c) = vb;
+            const int piece = tid + 256 * p, r = piece >> 3, c = (piece & 7) * 8;
+            const int ra = min(m0 + r, T - 1);
+            *reinterpret_cast<uint4 *>(sa + r * LD + c) = *reinterpret_cast<const uint4 *>(X + (int64_t)ra * H + k0 + c);
+        }
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            const int piece = tid + 256 * p, r = piece >> 3, c = (piece & 7) * 8;
+            const int rb = min(n0 + r, E - 1);
+            *reinterpret_cast<uint4 *>(sb + r * LD + c) = *reinterpret_cast<const uint4 *>(W + (int64_t)rb * H + k0 + c);
         }
         __syncthreads();
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8 fa[2], fb[2];
-            int kof = kk + 8 * (lane >> 4);
+            const int kof = kk + 8 * (lane >> 4);
+            bf16x8 fa[4], fb[4];
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                fa[i] = *reinterpret_cast<const bf16x8 *>(sa + (wm + 16 * i + (lane & 15)) * LD + kof);
-                fb[i] = *reinterpret_cast<const bf16x8 *>(sb + (wn + 16 * i + (lane & 15)) * LD + kof);
-            }
+            for (int i = 0; i < 4; i++) fa[i] = *reinterpret_cast<const bf16x8 *>(sa + (16 * i + (lane & 15)) * LD + kof);
 #pragma unroll
-            for (int i = 0; i < 2; i++)
+            for (int j = 0; j < 4; j++)
+                fb[j] = *reinterpret_cast<const bf16x8 *>(sb + (64 * wave + 16 * j + (lane & 15)) * LD + kof);
 #pragma unroll
-                for (int j = 0; j < 2; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
         __syncthreads();
     }
+    float *P = part + (int64_t)sl * T * E;
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            int n = n0 + wn + 16 * j + (lane & 15);
+        for (int j = 0; j < 4; j++) {
+            const int n = n0 + 64 * wave + 16 * j + (lane & 15);
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                int m = m0 + wm + 16 * i + 4 * (lane >> 4) + q;
-                if (m < T && n < E) C[(int64_t)m * E + n] = acc[i][j][q];
+                const int m = m0 + 16 * i + 4 * (lane >> 4) + q;
+                if (m < T && n < E) P[(int64_t)m * E + n] = acc[i][j][q];
             }
         }
+}
+
+// Logits of one token = sum over the K slices (fixed order), kept in LDS for
+// the top-k and written to `logits` when given; one wave per token.
+__global__ void __launch_bounds__(256)
+k_topk_sum(const float *__restrict__ part, int S, int T, int E, int k, float *__restrict__ logits,
+           int32_t *__restrict__ ids, float *__restrict__ wout) {
+    __shared__ float srow[4][1024];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wv;
+    if (t < T)
+        for (int e = lane; e < E; e += 64) {
+            float v = 0.f;
+            for (int sl = 0; sl < S; sl++) v += part[((int64_t)sl * T + t) * E + e];
+            srow[wv][e] = v;
+            if (logits) logits[(int64_t)t * E + e] = v;
+        }
+    __syncthreads();
+    if (t < T) topk_wave(srow[wv], E, k, ids + (int64_t)t * k, wout + (int64_t)t * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -127,10 +153,17 @@ int launch_router_gemv(const bitmoe_layer *L, const void *x, int x_dtype, int T,
     return BITMOE_OK;
 }
 
-int launch_router_mfma(const bitmoe_layer *L, const void *x, int T, float *logits, hipStream_t s) {
-    dim3 g((T + 63) / 64, (L->E + 63) / 64);
-    k_router_mfma<<<g, 256, 0, s>>>((const uint16_t *)x, (const uint16_t *)L->router_w, T, L->H,
-                                    L->E, logits);
+size_t router_mfma_part_floats(int T, int E) { return (size_t)kRouterSplit * T * E; }
+
+int launch_router_mfma(const bitmoe_layer *L, const void *x, int T, float *logits, int32_t *ids, float *w,
+                       float *part, hipStream_t s) {
+    const int kslice = (L->H / 64 + kRouterSplit - 1) / kRouterSplit * 64;
+    const int S = (L->H + kslice - 1) / kslice;
+    dim3 g((T + 63) / 64, (L->E + 255) / 256, S);
+    k_router_splitk<<<g, 256, 0, s>>>((const uint16_t *)x, (const uint16_t *)L->router_w, T, L->H, L->E, kslice,
+                                      part);
+    BM_LAUNCH_CHECK();
+    k_topk_sum<<<(T + 3) / 4, 256, 0, s>>>(part, S, T, L->E, L->k, logits, ids, w);
     BM_LAUNCH_CHECK();
     return BITMOE_OK;
 }
