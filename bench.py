@@ -11,7 +11,8 @@ shapes (H 7168, I 2048, 256 routed experts, top-8, one bf16 shared expert),
 seeded synthetic weights.  To keep timed calls out of the 256 MB MALL, the
 steps rotate over --copies independent device copies of the layer and over
 16 different token rows.  Extra objects report the 16-token Zipf decode
-batch and the 2048-token prefill chunk (grouped bf16-MFMA GEMMs).
+batch and the 2048-token prefill chunk (grouped GEMMs on the fp16 matrix
+cores, whose dense peak equals bf16's).
 
 Prints ONE JSON line.
 """
@@ -25,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
-BF16_PEAK = 2.5e15         # FLOP/s, dense bf16 MFMA
+BF16_PEAK = 2.5e15         # FLOP/s, dense bf16 (and fp16) MFMA
 
 
 def parse():
@@ -42,6 +43,11 @@ def parse():
                     help="print per-kernel durations of a rocprofv3 --kernel-trace run")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="print the per-kernel HBM traffic summary of four rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="print per-kernel MFMA TFLOP/s of a rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F16 "
+                         "--kernel-trace run")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only run the 2048-token prefill step (--prefill-steps times; for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the b16 and prefill lines")
     return ap.parse_args()
@@ -294,6 +300,34 @@ def summarize_kernels(trace_dir):
     return "\n".join(out)
 
 
+def summarize_mfma(pmc_dir):
+    """Per-kernel fp16/bf16 MFMA work from SQ_INSTS_VALU_MFMA_MOPS_F16/_BF16
+    (multiply-accumulates in units of 512, i.e. 1024 flops) over the kernel's
+    duration in the same run; the work includes any padding of partial tiles."""
+    import glob
+    import sqlite3
+    db = glob.glob(os.path.join(pmc_dir, "*.db"))[0]
+    c = sqlite3.connect(db)
+    mops = {}
+    for kn, cn, v in c.execute("select kernel_name, counter_name, sum(value) from counters_collection "
+                               "group by dispatch_id, counter_name"):
+        if "MFMA_MOPS" in cn:
+            mops.setdefault(kn, []).append(v)
+    dur = {}
+    for kn, d in c.execute("select name, end - start from kernels"):
+        dur.setdefault(kn, []).append(d)
+    lines = [f"{'kernel':40s} {'calls':>5s} {'avg_us':>9s} {'mfma_TFLOP':>11s} {'TFLOP/s':>9s} {'frac_2.5PF':>10s}"]
+    for kn, v in sorted(mops.items()):
+        if not any(x > 0 for x in v) or kn not in dur:
+            continue
+        fl = sum(v) / len(v) * 1024.0
+        us = sum(dur[kn]) / len(dur[kn]) / 1e3
+        name = kn.replace("(anonymous namespace)::", "").split("(")[0][:40]
+        lines.append(f"{name:40s} {len(v):5d} {us:9.1f} {fl / 1e12:11.3f} {fl / (us * 1e-6) / 1e12:9.1f} "
+                     f"{fl / (us * 1e-6) / BF16_PEAK:10.3f}")
+    return "\n".join(lines)
+
+
 def traffic_from_profile(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary,
     or None when the decode sources have changed since it was taken."""
@@ -319,6 +353,9 @@ def main():
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic, copy_bytes=1 << 30))
         return
+    if args.summarize_mfma:
+        print(summarize_mfma(args.summarize_mfma))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               f"multi-GPU path. Run with --gpus 1.", file=sys.stderr)
@@ -330,6 +367,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.prefill_only:
+        _, lays = build_layer(synth.WORKLOADS["decode_b1"], 1)
+        pf = prefill_2k(args, lays)
+        log(f"[bench] prefill_2k {pf['ms']:.2f} ms/step, gate/up {pf['gu_ms'] * 1e3:.1f} us")
         return
     w = synth.WORKLOADS["decode_b1"]
     L, lays = build_layer(w, args.copies)
