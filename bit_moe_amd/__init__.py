@@ -23,9 +23,6 @@ def layer_from_canonical(H, I, E, k, router_bits, gate, up, down, grid, shared=N
             t = t.view(dtype)
         return t.to(device).contiguous()
 
-    gmax = int(np.asarray(grid).max()) if isinstance(grid, np.ndarray) else int(grid.max().item())
-    if gmax > 7:
-        raise ValueError(f"codebook magnitudes must be 0..7 for the FFN kernels (found {gmax})")
     router = dev(router_bits, torch.bfloat16) if router_bits is not None else \
         torch.zeros((E, H), dtype=torch.bfloat16, device=device)
     gq = pack_iq2x(dev(gate).reshape(-1), E, I, H)

@@ -99,8 +99,6 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
         d.hscale = c.take<float>(n * (L->I / 64));
         d.o = c.take<float>(n * L->H);
         d.ycount = c.take<int32_t>(L->H / 64);
-        d.tab = c.take<uint4>(2 * 4096 / 4);
-        d.xs = c.take<float>((int64_t)T * (L->H / 32));
         if (shared) {
             d.sgp = c.take<float>((int64_t)p.kc_sg * 2 * T * L->I);
             d.hs = c.take<uint16_t>(2 * (int64_t)T * L->I);

@@ -87,64 +87,101 @@ BM_DEV void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---- tiled IQ2X group words ----------------------------------------------
 // A tiled IQ2X group (32 weights, four runs of 8) is two little-endian
-// 32-bit words, W0 for runs 0,1 and W1 for runs 2,3.  Bits 0-1 of W0 are
-// bits 0-1 of the 4-bit group scale, bits 0-1 of W1 its bits 2-3.  The
-// first run of a word is the 15-bit field R at bits 2-16, the second at
-// bits 17-31; within R: bits 0-2 the signs of weights 0,1,2, bit 3 the
-// parity of the signs of weights 0..3, bits 4-11 the codebook index and
-// bits 12-14 the signs of weights 4,5,6.  The sign of weight 3 is
-// bit 3 ^ bits 0..2, that of weight 7 (even parity over the 8) is
-// bit 3 ^ bits 12..14.  It is a bijective re-encoding of the canonical
-// 8 bytes of the group.
-//
-// Decode tables (LDS, 2 x 4096 dwords): table 1 at index R & 0xFFF holds
-// weights 0..3 of the run, table 2 at index R >> 3 weights 4..7, each
-// weight as one byte: the low byte of bf16(24 + w), w = +-magnitude (the
-// high byte of every such bf16 is 0x41 for magnitudes 0..7).  The
-// byte offsets of both lookups are a shift and a mask of the word.
-constexpr int kIq2xTabDwords = 4096;              // per table
-constexpr int kIq2xBias = 24;
-constexpr uint32_t kIq2xHiBytes = 0x41414141u;
-BM_DEV uint32_t iq2x_run(uint32_t W, int second) { return second ? W >> 17 : (W >> 2) & 0x7FFFu; }
-BM_DEV uint32_t iq2x_scale(uint32_t W0, uint32_t W1) { return (W0 & 3u) | ((W1 & 3u) << 2); }
-BM_DEV uint32_t iq2x_run_idx(uint32_t R) { return (R >> 4) & 0xFFu; }
-// signs of the 8 weights of a run (bit i = weight i negative)
-BM_DEV uint32_t iq2x_run_signs(uint32_t R) {
-    const uint32_t lo3 = R & 7u, hi3 = (R >> 12) & 7u, p = (R >> 3) & 1u;
-    const uint32_t s3 = p ^ (__popc(lo3) & 1u), s7 = p ^ (__popc(hi3) & 1u);
-    return lo3 | (s3 << 3) | (hi3 << 4) | (s7 << 7);
+// 32-bit words, W0 for runs 0,1 and W1 for runs 2,3.  A run takes two
+// bytes of its word, the first run bytes 0-1, the second bytes 2-3: the
+// codebook index, then the stored signs of weights 0..6 (bit i set: weight
+// i negative) in bits 0-6 and one bit of the 4-bit group scale in bit 7
+// (scale bit 0 in byte 1 of W0, bit 1 in byte 3 of W0, bit 2 in byte 1 of
+// W1, bit 3 in byte 3 of W1).  The sign of weight 7 makes the number of
+// negative weights of the run even.  It is a bijective regrouping of the
+// canonical 8 bytes of the group.
+BM_DEV uint32_t iq2x_scale(uint32_t W0, uint32_t W1) {
+    return ((W0 >> 15) & 1u) | ((W0 >> 30) & 2u) | ((W1 >> 13) & 4u) | ((W1 >> 28) & 8u);
 }
-// byte offsets into the tables of the two runs of word W
-BM_DEV uint32_t iq2x_off1(uint32_t W, int second) { return second ? (W >> 15) & 0x3FFCu : W & 0x3FFCu; }
-BM_DEV uint32_t iq2x_off2(uint32_t W, int second) {
-    return 4u * kIq2xTabDwords + (second ? (W >> 18) & 0x3FFCu : (W >> 3) & 0x3FFCu);
+// 2 s + 1 of the group scale s: the four scale bits spread to 0x00/0xFF
+// bytes by one byte permute, weighted 2, 4, 8, 16 and summed
+BM_DEV uint32_t iq2x_scale_odd(uint32_t W0, uint32_t W1) {
+    const uint32_t m = __builtin_amdgcn_perm(W1, W0, 0x0B0A0908u);
+    return __builtin_amdgcn_sad_u8(m & 0x10080402u, 0u, 1u);
 }
-// low byte of bf16(24 + (neg ? -m : m)), m in 0..7: 24 +- m lies in [16, 32)
-BM_DEV uint32_t iq2x_biased_byte(uint32_t m, uint32_t neg) {
-    const uint32_t v = neg ? 8u - m : 8u + m;      // (24 +- m) - 16, in 1..15
-    return 0x80u | (v << 3);
+
+// Run lookup tables in LDS.  Each 16-byte entry is kept in 16 copies, one
+// per 16-byte slot of a 256-byte line (copy c of entry i at 256 i + 16 c),
+// and lane l reads copy l & 15: a 16-lane group whose slots are distinct is
+// served without bank conflicts whichever lines it touches, so random
+// lookups run at the full LDS rate.
+//  magnitudes (at 0, 256 entries): the 8 codebook magnitudes of row i as
+//    16-bit floats (bf16 or fp16, both exact for bytes);
+//  signs (at 64 KiB): for the sign byte i of a run (bit 7, the scale bit,
+//    ignored), four XOR masks, bit 15 / bit 31 of mask p set when weight
+//    2p / 2p+1 is negative.  Either all 256 byte values are present (64 KiB)
+//    or the 128 without bit 7 (32 KiB; the offset is masked).
+// XOR-ing mask p into magnitude word p gives the signed pair (w_2p, w_2p+1).
+// The tables sit at LDS address 0 of kernels whose LDS is all dynamic (the
+// host checks that they have no static LDS), and lookups read them through
+// lds_ld16 at the computed offset as it is: reading through the extern
+// array would add its base, a symbol resolved only at link time, with one
+// more instruction per lookup.
+BM_DEV uint4 lds_ld16(uint32_t a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t *)a;
+    return make_uint4(v.x, v.y, v.z, v.w);
+#else
+    (void)a;               // device code only; the host pass sees this body
+    return uint4{};
+#endif
 }
-// table entry i of table `which` (0: weights 0..3, 1: weights 4..7)
-BM_DEV uint32_t iq2x_tab_entry(const uint8_t *__restrict__ grid, int which, uint32_t i) {
-    uint32_t idx, sg;
-    if (which == 0) {             // i = idx << 4 | parity03 << 3 | signs 0..2
-        idx = i >> 4;
-        const uint32_t lo3 = i & 7u, p = (i >> 3) & 1u;
-        sg = lo3 | ((p ^ (__popc(lo3) & 1u)) << 3);
-    } else {                      // i = signs 4..6 << 9 | idx << 1 | parity03
-        idx = (i >> 1) & 0xFFu;
-        const uint32_t hi3 = (i >> 9) & 7u, p = i & 1u;
-        sg = hi3 | ((p ^ (__popc(hi3) & 1u)) << 3);
-    }
-    const uint32_t m4 = *reinterpret_cast<const uint32_t *>(grid + 8 * idx + 4 * which);
-    uint32_t e = 0;
+constexpr int kLutMagBytes = 65536;
+constexpr int kLutSgnFull = 65536, kLutSgnHalf = 32768;
+// per-lane constant of the offset permutes: the lane's slot, and byte 2 = 1
+// for the sign table's base
+BM_DEV uint32_t lut_lane_const(int lane) { return (uint32_t)(lane & 15) << 4 | 1u << 16; }
+// byte offsets of the two lookups of run `second` of word W (one permute
+// each: [slot, index byte, 0, 0] and [slot, sign byte, 1, 0])
+BM_DEV uint32_t lut_mag_off(uint32_t W, uint32_t lc, int second) {
+    return __builtin_amdgcn_perm(W, lc, second ? 0x0C0C0600u : 0x0C0C0400u);
+}
+BM_DEV uint32_t lut_sgn_off(uint32_t W, uint32_t lc, int second) {
+    return __builtin_amdgcn_perm(W, lc, second ? 0x0C020700u : 0x0C020500u);
+}
+// entry `e` of the sign table: the 8 signs of the stored 7, as XOR masks
+BM_DEV uint4 lut_sign_entry(uint32_t e) {
+    const uint32_t s7 = e & 0x7Fu, sg = s7 | ((__popc(s7) & 1u) << 7);
+    uint32_t m[4];
 #pragma unroll
-    for (int b = 0; b < 4; b++) e |= iq2x_biased_byte((m4 >> (8 * b)) & 0xFFu, (sg >> b) & 1u) << (8 * b);
-    return e;
+    for (int p = 0; p < 4; p++) m[p] = (((sg >> (2 * p)) & 1u) << 15) | (((sg >> (2 * p + 1)) & 1u) << 31);
+    return make_uint4(m[0], m[1], m[2], m[3]);
 }
-// the two bf16 pairs (24 + w0, 24 + w1), (24 + w2, 24 + w3) of a table entry
-BM_DEV uint32_t iq2x_pair_lo(uint32_t e) { return __builtin_amdgcn_perm(kIq2xHiBytes, e, 0x04010400u); }
-BM_DEV uint32_t iq2x_pair_hi(uint32_t e) { return __builtin_amdgcn_perm(kIq2xHiBytes, e, 0x04030402u); }
+// entry `e` of the magnitude table from the codebook row (8 bytes), as
+// bf16 (BF = 1) or fp16 pairs
+template <int BF>
+BM_DEV uint4 lut_mag_entry(const uint8_t *__restrict__ grid, uint32_t e) {
+    const uint2 g = *reinterpret_cast<const uint2 *>(grid + 8 * e);
+    const uint32_t b[2] = {g.x, g.y};
+    uint32_t m[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const uint32_t w = b[p >> 1] >> (16 * (p & 1));
+        const float lo = (float)(w & 0xFFu), hi = (float)((w >> 8) & 0xFFu);
+        if (BF) {
+            m[p] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+        } else {
+            m[p] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+        }
+    }
+    return make_uint4(m[0], m[1], m[2], m[3]);
+}
+// both tables (SGN = kLutSgnFull or kLutSgnHalf bytes of signs), by the
+// threads of the workgroup
+template <int BF, int SGN>
+BM_DEV void lut_build(const uint8_t *__restrict__ grid, uint8_t *lut) {
+    for (int i = threadIdx.x; i < 256 * 16; i += blockDim.x)
+        *reinterpret_cast<uint4 *>(lut + 16 * i) = lut_mag_entry<BF>(grid, (uint32_t)i >> 4);
+    for (int i = threadIdx.x; i < SGN / 16; i += blockDim.x)
+        *reinterpret_cast<uint4 *>(lut + kLutMagBytes + 16 * i) = lut_sign_entry((uint32_t)i >> 4);
+}
 
 // ---- tiled Q2K quant words -------------------------------------------------
 // A tiled Q2K sub-block (16 weights) is one little-endian word: the 2-bit
@@ -299,8 +336,6 @@ struct DecodeBufs {
     float *o;               // [T*k][H] routed down outputs, pair order
     float *osp;             // [kc_sd][T][H] shared down partial sums
     int32_t *ycount;        // [H/64] finished down workgroups per panel
-    uint4 *tab;             // IQ2X decode tables (2 x 16 KiB)
-    float *xs;              // [T][H/32] activation sums over groups of 32
     float *y;               // [T][H]
 };
 DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router);

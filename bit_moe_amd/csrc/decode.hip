@@ -11,11 +11,11 @@
 //
 // Launches (T <= 128/k: three; larger batches add a routing/bucketing
 // launch, experts chosen by several tokens a second gate/up and down):
-//   front  : decode tables, activation sums, router rows; the workgroup
-//            that finds every router workgroup done tops-k and buckets the
-//            batch (or buckets the given ids); clears the combine counters
+//   front  : router rows; clears the combine counters
 //            || shared-expert gate/up partial sums per (panel, K chunk)
-//   gateup : routed gate/up + SwiGLU per (active expert, 64-row panel)
+//   gateup : routing of the batch (top-k and bucketing, in every
+//            workgroup), then routed gate/up + SwiGLU per (active expert,
+//            64-row panel) through run lookup tables built in LDS
 //   down   : routed down per (active expert, 64-row panel) || shared down
 //            per (panel, K chunk), its h built from the gate/up partials;
 //            the last workgroup to finish a panel combines it,
@@ -44,8 +44,6 @@ constexpr int kNT = 4;             // tokens per pass over the weights
 constexpr int kMaxChunks = 8;      // K chunks of the shared expert, at most
 constexpr int kMaxExperts = 1024;
 constexpr int kSharedChunkCols = 512;   // I columns of one shared-down K chunk, at most
-constexpr int kTabDw = 2 * kIq2xTabDwords;                     // decode tables, dwords (32 KiB)
-constexpr int kTabWG = kTabDw / (kW * 64);                       // front workgroups that build them
 // 16-byte pieces per load batch of a gate/up wave (fewer when several
 // tokens share the pass, to bound register use)
 template <int NT>
@@ -79,21 +77,17 @@ BM_DEV const void *xrow(const void *x, int t, int H, int k) {
                  : (const void *)(static_cast<const float *>(x) + (int64_t)t * H + k);
 }
 
-// One group's activations (32 values per token) and their sums, held in
-// scalar registers when the activations are bf16.
+// One group's activations (32 values per token), held in scalar registers
+// when the activations are bf16.
 template <int XBF16, int NT>
 struct XGroup {
     uint4 v[XBF16 ? NT : 1][4];
-    float s[NT];
 };
 
 template <int XBF16, int NT>
-BM_DEV void load_xgroup(XGroup<XBF16, NT> &g, const void *__restrict__ x, const float *__restrict__ xs,
-                        const int (&tok)[NT], int H, int gg) {
-    const int G = H / 32;
+BM_DEV void load_xgroup(XGroup<XBF16, NT> &g, const void *__restrict__ x, const int (&tok)[NT], int H, int gg) {
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-        g.s[t] = xs[(int64_t)tok[t] * G + gg];
         if (XBF16) {
             const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)tok[t] * H + 32 * gg);
 #pragma unroll
@@ -103,27 +97,32 @@ BM_DEV void load_xgroup(XGroup<XBF16, NT> &g, const void *__restrict__ x, const 
 }
 
 // One IQ2X group (32 weights, words W0, W1) of this lane's row dotted with
-// NT activation rows.  Each run of 8 weights is two 4-byte table reads and
-// four byte permutes giving bf16 pairs of 24 + w; the bias is removed per
-// group with the activation sums (24 * sum of the group's activations).
-template <int XBF16, int NT>
-BM_DEV void iq2x_group(uint32_t W0, uint32_t W1, float dq8, const char *tab, const XGroup<XBF16, NT> &xg,
-                       const void *x, const int (&tok)[NT], int H, int gg, float (&acc)[NT]) {
-    const float scale = dq8 * (float)(2u * iq2x_scale(W0, W1) + 1u);   // d*(0.5+s)/4
-    uint32_t e1[4], e2[4];
+// NT activation rows.  Each run of 8 weights is two 16-byte lookups (the
+// codebook row's magnitudes as bf16 pairs, the sign masks of its sign
+// byte), four XORs giving the signed bf16 pairs, and four bf16 dot
+// products per token; the group scale d/8 (2s+1) is applied to the group's
+// fp32 sum.  SGN: bytes of the sign table (the half table drops the scale
+// bit from the offset).
+template <int XBF16, int NT, int SGN>
+BM_DEV void iq2x_group(uint32_t W0, uint32_t W1, float dq8, const uint8_t *lut, uint32_t lc,
+                       const XGroup<XBF16, NT> &xg, const void *x, const int (&tok)[NT], int H, int gg,
+                       float (&acc)[NT]) {
+    const float scale = dq8 * (float)iq2x_scale_odd(W0, W1);
+    uint4 m[4], g[4];
 #pragma unroll
     for (int r = 0; r < 4; r++) {
         const uint32_t W = r < 2 ? W0 : W1;
-        e1[r] = *reinterpret_cast<const uint32_t *>(tab + iq2x_off1(W, r & 1));
-        e2[r] = *reinterpret_cast<const uint32_t *>(tab + iq2x_off2(W, r & 1));
+        const uint32_t so = lut_sgn_off(W, lc, r & 1);
+        m[r] = lds_ld16(lut_mag_off(W, lc, r & 1));
+        g[r] = lds_ld16(SGN == kLutSgnFull ? so : so & ~0x8000u);
     }
     float part[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) part[t] = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-        const uint2 lo = make_uint2(iq2x_pair_lo(e1[r]), iq2x_pair_hi(e1[r]));
-        const uint2 hi = make_uint2(iq2x_pair_lo(e2[r]), iq2x_pair_hi(e2[r]));
+        const uint2 lo = make_uint2(m[r].x ^ g[r].x, m[r].y ^ g[r].y);
+        const uint2 hi = make_uint2(m[r].z ^ g[r].z, m[r].w ^ g[r].w);
 #pragma unroll
         for (int t = 0; t < NT; t++) {
             if (XBF16) {
@@ -138,7 +137,7 @@ BM_DEV void iq2x_group(uint32_t W0, uint32_t W1, float dq8, const char *tab, con
         }
     }
 #pragma unroll
-    for (int t = 0; t < NT; t++) acc[t] = fmaf(scale, fmaf(-(float)kIq2xBias, xg.s[t], part[t]), acc[t]);
+    for (int t = 0; t < NT; t++) acc[t] = fmaf(scale, part[t], acc[t]);
 }
 
 // Even split of [0, n) over `parts`; returns [lo, hi) of part `i`.
@@ -194,53 +193,19 @@ BM_DEV void shared_gateup_pass(int H, int I, int T, int t0, int P, int c0, int c
     __syncthreads();
 }
 
-// Workgroup roles, in blockIdx order: decode tables | activation sums |
-// router rows (n_rwg) | shared-expert gate/up partial sums per (panel,
-// K chunk).
+// Workgroup roles, in blockIdx order: router rows (n_rwg) | shared-expert
+// gate/up partial sums per (panel, K chunk).  Workgroup 0 also clears the
+// down launch's per-panel combine counters.
 template <int XBF16>
 __global__ void __launch_bounds__(kW * 64)
-k_dec_front(int H, int I, int E, int T, int n_xwg, int n_rwg, int kc_sg, const uint16_t *__restrict__ wr,
-            const void *__restrict__ x, const uint8_t *__restrict__ grid, uint32_t *__restrict__ gtab,
-            float *__restrict__ xs, float *__restrict__ logits, int32_t *__restrict__ ycount,
+k_dec_front(int H, int I, int E, int T, int n_rwg, int kc_sg, const uint16_t *__restrict__ wr,
+            const void *__restrict__ x, float *__restrict__ logits, int32_t *__restrict__ ycount,
             const uint4 *__restrict__ sg, const uint4 *__restrict__ su, float *__restrict__ sgp) {
     __shared__ float red[kW * kNT * 2 * 64];
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int b = blockIdx.x;
-    if (b < kTabWG) {          // the decode tables, once per call
-        const int i = b * kW * 64 + threadIdx.x;
-        gtab[i] = iq2x_tab_entry(grid, i >= kIq2xTabDwords, i & (kIq2xTabDwords - 1));
-        if (b == 0)            // the down launch's per-panel combine counters
-            for (int p = threadIdx.x; p < H / 64; p += kW * 64) ycount[p] = 0;
-        return;
-    }
-    b -= kTabWG;
-    if (b < n_xwg) {           // activation sums over groups of 32, fixed order
-        const int G = H / 32;
-        const int64_t i = (int64_t)b * kW * 64 + threadIdx.x;
-        if (i >= (int64_t)T * G) return;
-        const int t = (int)(i / G), g = (int)(i - (int64_t)t * G);
-        float sum = 0.f;
-        if (XBF16) {
-            const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + (int64_t)t * H + 32 * g);
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const uint4 v = p[q];
-                const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int j = 0; j < 4; j++) sum += bf16_lo(wd[j]) + bf16_hi(wd[j]);
-            }
-        } else {
-            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (int64_t)t * H + 32 * g);
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                const float4 v = p[q];
-                sum += v.x + v.y + v.z + v.w;
-            }
-        }
-        xs[i] = sum;
-        return;
-    }
-    b -= n_xwg;
+    if (b == 0)
+        for (int p = threadIdx.x; p < H / 64; p += kW * 64) ycount[p] = 0;
     if (b < n_rwg) {
         const int e = b * kW + wv;
         if (e >= E) return;
@@ -254,7 +219,9 @@ k_dec_front(int H, int I, int E, int T, int n_xwg, int n_rwg, int kc_sg, const u
         return;
     }
     b -= n_rwg;
-    // shared gate/up: panel P of the I rows, K chunk c
+    // shared gate/up: panel P of the I rows, K chunk c (none without a
+    // shared expert: the grid then holds one workgroup for the counters)
+    if (kc_sg == 0 || b >= (I / 64) * kc_sg) return;
     const int P = b / kc_sg, c = b % kc_sg;
     int c0, c1;
     split_range(H / 8, kc_sg, c, c0, c1);
@@ -304,12 +271,10 @@ struct Tok {
     int cnt, off, e;
 };
 
-template <int XBF16, int NT>
-BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P, uint4 *tabl,
-                               const uint4 *__restrict__ gtab, bool copy_tab,
+template <int XBF16, int NT, int SGN>
+BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P, const uint8_t *lut,
                                const uint8_t *__restrict__ gate, const uint8_t *__restrict__ up,
-                               const void *__restrict__ x, const float *__restrict__ xs,
-                               const int32_t *perm,
+                               const void *__restrict__ x, const int32_t *perm,
                                uint16_t *__restrict__ h, float2 *__restrict__ hsum2,
                                float *__restrict__ hscale, float *red) {
     const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -345,14 +310,10 @@ BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P
         }
     };
     if (p0 < p1) load(p0, g4, u4, gdw, udw);
-    if (copy_tab) {            // the decode tables, while the first batch is in flight
-        for (int i = threadIdx.x; i < kTabDw / 4; i += blockDim.x) tabl[i] = gtab[i];
-        __syncthreads();
-    }
-    const char *tab = reinterpret_cast<const char *>(tabl);
+    const uint32_t lc = lut_lane_const(lane);
     // activations of the current group, the next one in flight
     XGroup<XBF16, NT> xa, xb;
-    if (p0 < p1) load_xgroup<XBF16, NT>(xa, x, xs, tok, H, 2 * p0);
+    if (p0 < p1) load_xgroup<XBF16, NT>(xa, x, tok, H, 2 * p0);
     for (int pb = p0; pb < p1; pb += kPB) {
         if (pb + kPB < p1) load(pb + kPB, ng, nu, ngd, nud);
         const int n = min(kPB, p1 - pb);
@@ -361,12 +322,12 @@ BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P
             if (i < n) {
                 const int gg = 2 * (pb + i);
                 const float dg = 0.125f * fp16_to_f32(gdw[i]), du = 0.125f * fp16_to_f32(udw[i]);
-                load_xgroup<XBF16, NT>(xb, x, xs, tok, H, gg + 1);
-                iq2x_group<XBF16, NT>(g4[i].x, g4[i].y, dg, tab, xa, x, tok, H, gg, ag);
-                iq2x_group<XBF16, NT>(u4[i].x, u4[i].y, du, tab, xa, x, tok, H, gg, au);
-                load_xgroup<XBF16, NT>(xa, x, xs, tok, H, pb + i + 1 < p1 ? gg + 2 : gg);
-                iq2x_group<XBF16, NT>(g4[i].z, g4[i].w, dg, tab, xb, x, tok, H, gg + 1, ag);
-                iq2x_group<XBF16, NT>(u4[i].z, u4[i].w, du, tab, xb, x, tok, H, gg + 1, au);
+                load_xgroup<XBF16, NT>(xb, x, tok, H, gg + 1);
+                iq2x_group<XBF16, NT, SGN>(g4[i].x, g4[i].y, dg, lut, lc, xa, x, tok, H, gg, ag);
+                iq2x_group<XBF16, NT, SGN>(u4[i].x, u4[i].y, du, lut, lc, xa, x, tok, H, gg, au);
+                load_xgroup<XBF16, NT>(xa, x, tok, H, pb + i + 1 < p1 ? gg + 2 : gg);
+                iq2x_group<XBF16, NT, SGN>(g4[i].z, g4[i].w, dg, lut, lc, xb, x, tok, H, gg + 1, ag);
+                iq2x_group<XBF16, NT, SGN>(u4[i].z, u4[i].w, du, lut, lc, xb, x, tok, H, gg + 1, au);
             }
         }
 #pragma unroll
@@ -463,46 +424,37 @@ BM_DEV void route_in_wg(int mode, int E, int k, int T, const float *__restrict__
 // MULTI = 0 takes the experts chosen by exactly one token, MULTI = 1 the
 // experts with several tokens (passes of kNT tokens); keeping the two apart
 // keeps each kernel's register use low.  route_mode: 0 the bucketing is in
-// bk already, 1/2 route_in_wg (MULTI = 0 only).
+// bk already, 1/2 route_in_wg (MULTI = 0 only).  The run lookup tables
+// (dynamic LDS, dec_lut_bytes) are built from the codebook while the batch
+// is routed.
+template <int MULTI>
+constexpr int dec_sgn_bytes() { return MULTI ? kLutSgnHalf : kLutSgnFull; }
+template <int MULTI>
+constexpr int dec_lut_bytes() { return kLutMagBytes + dec_sgn_bytes<MULTI>(); }
+// all LDS of a gate/up workgroup, dynamic so that the tables start at
+// address 0 (their lookup offsets are then the permutes' results as they
+// are): tables | cross-wave sums | routing
+template <int MULTI>
+constexpr int dec_red_floats() { return kWG * (MULTI ? kNT : 1) * 2 * 64; }
+template <int MULTI>
+constexpr int dec_gateup_lds() { return dec_lut_bytes<MULTI>() + dec_red_floats<MULTI>() * 4 + (int)sizeof(SmallRoute); }
+
 template <int XBF16, int MULTI>
 __global__ void __launch_bounds__(kWG * 64)
 k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const uint8_t *__restrict__ gate,
-             const uint8_t *__restrict__ up, const uint4 *__restrict__ gtab,
-             const void *__restrict__ x, const float *__restrict__ xs, const float *__restrict__ logits,
+             const uint8_t *__restrict__ up, const uint8_t *__restrict__ grid,
+             const void *__restrict__ x, const float *__restrict__ logits,
              int32_t *ids, float *w, bm_host::Buckets bk, uint16_t *__restrict__ h, float2 *__restrict__ hsum2,
              float *__restrict__ hscale, int kc_sg, const float *__restrict__ sgp, uint16_t *__restrict__ hs) {
-    if (!MULTI && (int)blockIdx.x >= n_gwg) {
-        // shared h = silu(sum of the gate partials) * (sum of the up
-        // partials), in a fixed order, as bf16 hi + lo for the down launch
-        const int64_t n = (int64_t)T * I;
-        const int64_t i = (int64_t)(blockIdx.x - n_gwg) * blockDim.x + threadIdx.x;
-        if (i >= n) return;
-        float g = 0.f, u = 0.f;
-        for (int c = 0; c < kc_sg; c++) {
-            g += sgp[(int64_t)(2 * c) * n + i];
-            u += sgp[(int64_t)(2 * c + 1) * n + i];
-        }
-        const float hv = silu(g) * u;
-        const uint32_t hi = f32_to_bf16_rne(hv);
-        hs[i] = (uint16_t)hi;
-        hs[n + i] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
-        return;
-    }
-    __shared__ uint4 tab[kTabDw / 4];
-    __shared__ float red[kWG * (MULTI ? kNT : 1) * 2 * 64];
-    __shared__ SmallRoute sr;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lut[];
+    float *red = reinterpret_cast<float *>(lut + dec_lut_bytes<MULTI>());
+    SmallRoute &sr = *reinterpret_cast<SmallRoute *>(red + dec_red_floats<MULTI>());
+    constexpr int SGN = dec_sgn_bytes<MULTI>();
     const int32_t *counts = bk.counts, *offsets = bk.offsets, *perm = bk.perm, *active = bk.active;
     int na;
-    bool copy_tab = true;
     if (!MULTI && route_mode) {
-        // the decode tables are fetched while the batch is routed
-        static_assert(kTabDw / 4 == 2 * kWG * 64, "two table pieces per thread");
-        const uint4 ta = gtab[threadIdx.x], tb = gtab[threadIdx.x + kWG * 64];
-        route_in_wg(route_mode, E, k, T, logits, ids, w, bk, sr);
-        tab[threadIdx.x] = ta;
-        tab[threadIdx.x + kWG * 64] = tb;
-        __syncthreads();
-        copy_tab = false;
+        lut_build<1, SGN>(grid, lut);
+        route_in_wg(route_mode, E, k, T, logits, ids, w, bk, sr);     // ends with a barrier
         counts = sr.counts;
         offsets = sr.offsets;
         perm = sr.perm;
@@ -514,24 +466,45 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
     const int b = blockIdx.x;
     if (b < n_gwg) {
         const int panels = I / 64, slot = b / panels, P = b % panels;
+        if (!MULTI && kc_sg && slot == 0) {
+            // shared h = silu(sum of the gate partials) * (sum of the up
+            // partials), in a fixed order, as bf16 hi + lo for the down
+            // launch; chunks of blockDim elements over the first panels'
+            // workgroups
+            const int64_t n = (int64_t)T * I;
+            for (int64_t i = (int64_t)P * blockDim.x + threadIdx.x; i < n; i += (int64_t)panels * blockDim.x) {
+                float g = 0.f, u = 0.f;
+                for (int c = 0; c < kc_sg; c++) {
+                    g += sgp[(int64_t)(2 * c) * n + i];
+                    u += sgp[(int64_t)(2 * c + 1) * n + i];
+                }
+                const float hv = silu(g) * u;
+                const uint32_t hi = f32_to_bf16_rne(hv);
+                hs[i] = (uint16_t)hi;
+                hs[n + i] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
+            }
+        }
         if (slot >= na) return;
         Tok tk;
         tk.e = active[slot];
         tk.off = offsets[tk.e];
         tk.cnt = counts[tk.e];
         if ((tk.cnt > 1) != (MULTI != 0)) return;
+        if (MULTI || !route_mode) {
+            lut_build<1, SGN>(grid, lut);
+            __syncthreads();
+        }
         if (!MULTI) {
-            routed_gateup_pass<XBF16, 1>(H, I, k, tk, 0, P, tab, gtab, copy_tab, gate, up, x, xs, perm, h, hsum2,
-                                         hscale, red);
+            routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, 0, P, lut, gate, up, x, perm, h, hsum2, hscale, red);
             return;
         }
         for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
             if (tk.cnt - t0 == 1)
-                routed_gateup_pass<XBF16, 1>(H, I, k, tk, t0, P, tab, gtab, t0 == 0, gate, up, x, xs, perm, h,
-                                             hsum2, hscale, red);
+                routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, P, lut, gate, up, x, perm, h, hsum2, hscale,
+                                                  red);
             else
-                routed_gateup_pass<XBF16, kNT>(H, I, k, tk, t0, P, tab, gtab, t0 == 0, gate, up, x, xs, perm,
-                                               h, hsum2, hscale, red);
+                routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, P, lut, gate, up, x, perm, h, hsum2, hscale,
+                                                    red);
         }
         return;
     }
@@ -802,15 +775,14 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     const bool shared = L->shared_gate != nullptr;
     const bool bf = x_dtype == BITMOE_BF16;
     if (p.kc_sd > kMaxChunks || p.kc_sg > kMaxChunks) return BITMOE_EUNSUPPORTED;
-    // front: tables, activation sums, router rows, shared gate/up
-    const int n_xwg = (int)(((int64_t)T * (H / 32) + kW * 64 - 1) / (kW * 64));
-    const int n_front = kTabWG + n_xwg + p.n_rwg + (shared ? (I / 64) * p.kc_sg : 0);
+    // front: router rows, shared gate/up (at least one workgroup: it clears
+    // the combine counters)
+    const int n_front = std::max(1, p.n_rwg + (shared ? (I / 64) * p.kc_sg : 0));
     {
         auto kf = bf ? k_dec_front<1> : k_dec_front<0>;
-        kf<<<n_front, kW * 64, 0, s>>>(H, I, E, T, n_xwg, p.n_rwg, p.kc_sg, (const uint16_t *)L->router_w, x,
-                                       (const uint8_t *)L->grid, reinterpret_cast<uint32_t *>(b.tab), b.xs,
-                                       b.logits, b.ycount, (const uint4 *)L->shared_gate,
-                                       (const uint4 *)L->shared_up, b.sgp);
+        kf<<<n_front, kW * 64, 0, s>>>(H, I, E, T, p.n_rwg, p.kc_sg, (const uint16_t *)L->router_w, x, b.logits,
+                                       b.ycount, (const uint4 *)L->shared_gate, (const uint4 *)L->shared_up,
+                                       b.sgp);
         BM_LAUNCH_CHECK();
     }
     // mid: top-k and bucketing of batches above 128 pairs
@@ -831,19 +803,33 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     }
     // routed gate/up; experts chosen by several tokens in a second launch
     const int n_gwg = p.slots * (I / 64);
-    const int n_fin = shared ? (int)(((int64_t)T * I + kWG * 64 - 1) / (kWG * 64)) : 0;
     const int route_mode = p.small ? (p.n_rwg ? 1 : 2) : 0;
+    static const bool lds_set = [] {
+        bool ok = true;
+        for (auto f : {k_dec_gateup<1, 0>, k_dec_gateup<0, 0>, k_dec_gateup<1, 1>, k_dec_gateup<0, 1>}) {
+            hipFuncAttributes fa;      // the tables must start at LDS address 0
+            ok &= hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(f)) == hipSuccess && fa.sharedSizeBytes == 0;
+        }
+        for (auto f : {k_dec_gateup<1, 0>, k_dec_gateup<0, 0>})
+            ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      dec_gateup_lds<0>()) == hipSuccess;
+        for (auto f : {k_dec_gateup<1, 1>, k_dec_gateup<0, 1>})
+            ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      dec_gateup_lds<1>()) == hipSuccess;
+        return ok;
+    }();
+    if (!lds_set) return BITMOE_EHIP;
     for (int multi = 0; multi < (T > 1 ? 2 : 1); multi++) {
         auto kg = multi ? (bf ? k_dec_gateup<1, 1> : k_dec_gateup<0, 1>)
                         : (bf ? k_dec_gateup<1, 0> : k_dec_gateup<0, 0>);
         // the timing events, when set, are taken by the dispatch itself
         // around the first gate/up launch
         const TimingEvents ev = multi ? TimingEvents{} : timing_events();
-        hipExtLaunchKernelGGL(kg, dim3(n_gwg + (multi ? 0 : n_fin)), dim3(kWG * 64), 0, s, ev.start, ev.stop, 0,
-                              H, I, E, k, T, n_gwg, multi ? 0 : route_mode, (const uint8_t *)L->gate_q,
-                              (const uint8_t *)L->up_q, (const uint4 *)b.tab, x, (const float *)b.xs,
-                              (const float *)b.logits, b.ids, b.w, b.bk, b.h, b.hsum2, b.hscale, p.kc_sg,
-                              (const float *)b.sgp, b.hs);
+        hipExtLaunchKernelGGL(kg, dim3(n_gwg), dim3(kWG * 64),
+                              multi ? dec_gateup_lds<1>() : dec_gateup_lds<0>(), s, ev.start, ev.stop, 0, H, I, E, k,
+                              T, n_gwg, multi ? 0 : route_mode, (const uint8_t *)L->gate_q,
+                              (const uint8_t *)L->up_q, (const uint8_t *)L->grid, x, (const float *)b.logits, b.ids,
+                              b.w, b.bk, b.h, b.hsum2, b.hscale, p.kc_sg, (const float *)b.sgp, b.hs);
         BM_LAUNCH_CHECK();
     }
     // down || shared down; the last workgroup to finish a panel combines it

@@ -107,18 +107,15 @@ k_dequant_q2k(const uint8_t *__restrict__ blocks, int64_t nblocks, void *__restr
     }
 }
 
-// One canonical IQ2X group (4 index bytes, u32 signs/scale) -> the two
-// words of the tiled layout (see common.h).
-BM_DEV uint32_t iq2x_run_field(uint32_t idx, uint32_t s7) {
-    const uint32_t p03 = __popc(s7 & 15u) & 1u;
-    return (s7 & 7u) | (p03 << 3) | (idx << 4) | (((s7 >> 4) & 7u) << 12);
-}
+// One canonical IQ2X group (4 index bytes, u32 of 4 x 7 sign bits and the
+// 4-bit scale) -> the two words of the tiled layout: per run its index
+// byte, then its 7 sign bits with one scale bit on top (see common.h).
 BM_DEV uint2 iq2x_group_fields(uint32_t idxw, uint32_t a) {
-    const uint32_t s = a >> 28;
-    uint32_t R[4];
+    uint32_t r[4];
 #pragma unroll
-    for (int j = 0; j < 4; j++) R[j] = iq2x_run_field((idxw >> (8 * j)) & 0xFFu, (a >> (7 * j)) & 0x7Fu);
-    return make_uint2((s & 3u) | (R[0] << 2) | (R[1] << 17), (s >> 2) | (R[2] << 2) | (R[3] << 17));
+    for (int j = 0; j < 4; j++)
+        r[j] = ((idxw >> (8 * j)) & 0xFFu) | (((a >> (7 * j)) & 0x7Fu) << 8) | (((a >> (28 + j)) & 1u) << 15);
+    return make_uint2(r[0] | (r[1] << 16), r[2] | (r[3] << 16));
 }
 
 // canonical IQ2X -> tiled; one thread per block

@@ -64,12 +64,18 @@ constexpr int kPfHalf = 128;                  // K per LDS stage
 constexpr int kPfGuCols = 256;                // h columns per gate/up workgroup
 constexpr int kPfDnCols = 512;                // output columns per down workgroup
 constexpr int kPfXcds = 8;
-constexpr int kPfMagBytes = 256 * 256;          // 256 codebook rows x 16 copies x 16 bytes
-constexpr int kPfSgnBytes = 128 * 256;          // 128 sign patterns x 16 copies x 16 bytes
+constexpr int kPfMagBytes = kLutMagBytes;       // 256 codebook rows x 16 copies x 16 bytes
+constexpr int kPfSgnBytes = kLutSgnHalf;        // 128 sign patterns x 16 copies x 16 bytes
 constexpr int kPfTabBytes = kPfMagBytes + kPfSgnBytes;
 constexpr int kPfABytes = kPfRows * kPfHalf * 2;
 constexpr int kPfGuLds = kPfTabBytes + 2 * kPfABytes + kPfRows * (4 + 4 + 4) + kPfWaves * kPfRows * 4;
 constexpr int kPfDnLds = 2 * kPfABytes + kPfRows * (4 + 4);
+// fp16 weight operands carry a factor 2^kPfWShift, removed in the fp32
+// epilogues: with it a superblock scale d in [2^-19, 8] keeps every nonzero
+// weight in fp16's normal range (smallest IQ2X weight d/8, largest 27 d; Q2K
+// at most 45 d + 15 dmin), where quantised layers' scales sit.
+constexpr int kPfWShift = 8;
+constexpr float kPfWScale = 256.f;
 
 BM_DEV uint32_t h2u(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 BM_DEV f16x2 u2h(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
@@ -156,47 +162,34 @@ k_pf_xprep(int H, const void *__restrict__ x, uint16_t *__restrict__ x16, float 
 // are the gate rows of those columns, blocks 2,3 the up rows.
 // ---------------------------------------------------------------------------
 
-// The LDS decode tables.  Magnitudes: line i holds, 16 times, the fp16
-// pairs (m0, m1), (m2, m3), (m4, m5), (m6, m7) of codebook row i.  Signs: line
-// i (i = the run field's bits 0-3 | bits 12-14 << 4, i.e. signs 0..2, the
-// parity of signs 0..3, signs 4..6) holds, 16 times, the XOR masks that
-// negate weight 2p in the low and weight 2p+1 in the high half of pair p;
-// sign 3 = parity ^ signs 0..2, sign 7 = parity ^ signs 4..6 (even parity).
+// The LDS decode tables (layout in common.h): magnitudes as fp16 pairs, and
+// the 128 sign entries without the scale bit (32 KiB).  Threads 0..255 each
+// write the 16 copies of one magnitude line, threads 256..383 those of one
+// sign line.
 BM_DEV void pf_build_tables(const uint8_t *__restrict__ grid, uint8_t *lds) {
     const int t = threadIdx.x;
-    u32x4 v;
+    uint4 v;
     uint8_t *line;
     if (t < 256) {
-        const uint2 g = *reinterpret_cast<const uint2 *>(grid + 8 * t);
-        const uint32_t m[2] = {g.x, g.y};
-        uint32_t h[8];
-#pragma unroll
-        for (int b = 0; b < 8; b++) h[b] = f16_bits((float)((m[b >> 2] >> (8 * (b & 3))) & 0xFFu));
-        v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        v = lut_mag_entry<0>(grid, t);
         line = lds + 256 * t;
     } else if (t < 384) {
-        const uint32_t i = t - 256, lo3 = i & 7u, p = (i >> 3) & 1u, hi3 = (i >> 4) & 7u;
-        const uint32_t sg = lo3 | ((p ^ (__popc(lo3) & 1u)) << 3) | (hi3 << 4) | ((p ^ (__popc(hi3) & 1u)) << 7);
-        uint32_t mk[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) mk[q] = (((sg >> (2 * q)) & 1u) << 15) | (((sg >> (2 * q + 1)) & 1u) << 31);
-        v = u32x4{mk[0], mk[1], mk[2], mk[3]};
-        line = lds + kPfMagBytes + 256 * i;
+        v = lut_sign_entry(t - 256);
+        line = lds + kPfMagBytes + 256 * (t - 256);
     } else {
         return;
     }
 #pragma unroll
-    for (int c = 0; c < 16; c++) *reinterpret_cast<u32x4 *>(line + 16 * c) = v;
+    for (int c = 0; c < 16; c++) *reinterpret_cast<uint4 *>(line + 16 * c) = v;
 }
 
-// Table lookups of run `second` of word W (magnitudes, sign masks); slot16 =
-// 16 (lane & 15)
+// Table lookups of run `second` of word W (magnitudes, sign masks); lc =
+// lut_lane_const(lane).  The sign offset drops the scale bit (bit 15).
 struct RunLut { u32x4 m, g; };
-BM_DEV RunLut pf_iq2x_lookup(const uint8_t *lds, uint32_t W, int second, uint32_t slot16) {
-    const uint32_t idx = second ? (W >> 21) & 0xFFu : (W >> 6) & 0xFFu;
-    const uint32_t sig = second ? ((W >> 17) & 0xFu) | ((W >> 25) & 0x70u) : ((W >> 2) & 0xFu) | ((W >> 10) & 0x70u);
-    return {*reinterpret_cast<const u32x4 *>(lds + (idx << 8) + slot16),
-            *reinterpret_cast<const u32x4 *>(lds + kPfMagBytes + (sig << 8) + slot16)};
+BM_DEV RunLut pf_iq2x_lookup(const uint8_t *lds, uint32_t W, int second, uint32_t lc) {
+    (void)lds;
+    const uint4 m = lds_ld16(lut_mag_off(W, lc, second)), g = lds_ld16(lut_sgn_off(W, lc, second) & ~0x8000u);
+    return {u32x4{m.x, m.y, m.z, m.w}, u32x4{g.x, g.y, g.z, g.w}};
 }
 // fp16 operand (8 weights, K order) of a looked-up run, times the group's c2
 BM_DEV f16x8 pf_iq2x_build(const RunLut &l, uint32_t c2) {
@@ -280,7 +273,7 @@ BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
     int *sexp = reinterpret_cast<int *>(sxs + kPfRows);
     float *smax = reinterpret_cast<float *>(sexp + kPfRows);
     const int lane = lane_id(), col = lane & 31, kh = lane >> 5;
-    const uint32_t slot16 = (uint32_t)(lane & 15) << 4;
+    const uint32_t lc = lut_lane_const(lane);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = a.H / kQK;
     const int64_t slab = (int64_t)a.I * nb * 66;
@@ -307,28 +300,28 @@ BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
     // lookups issued two k-steps earlier and runs its MFMAs.
     auto compute = [&](const uint8_t *A, const Slot &sl) {
         // c = d/8 (2s+1) per (block, group) as fp16 pairs
-        const float dg = 0.125f * fp16_to_f32(sl.dg), du = 0.125f * fp16_to_f32(sl.du);
-        const uint32_t c2[2][2] = {{f16_pair(dg * (float)(2u * iq2x_scale(sl.g.x, sl.g.y) + 1u)),
-                                    f16_pair(dg * (float)(2u * iq2x_scale(sl.g.z, sl.g.w) + 1u))},
-                                   {f16_pair(du * (float)(2u * iq2x_scale(sl.u.x, sl.u.y) + 1u)),
-                                    f16_pair(du * (float)(2u * iq2x_scale(sl.u.z, sl.u.w) + 1u))}};
+        const float dg = 0.125f * kPfWScale * fp16_to_f32(sl.dg), du = 0.125f * kPfWScale * fp16_to_f32(sl.du);
+        const uint32_t c2[2][2] = {{f16_pair(dg * (float)iq2x_scale_odd(sl.g.x, sl.g.y)),
+                                    f16_pair(dg * (float)iq2x_scale_odd(sl.g.z, sl.g.w))},
+                                   {f16_pair(du * (float)iq2x_scale_odd(sl.u.x, sl.u.y)),
+                                    f16_pair(du * (float)iq2x_scale_odd(sl.u.z, sl.u.w))}};
         auto word = [&](const uint4 &v, int s) {
             const int q = s >> 2, rr = s & 3;
             return rr < 2 ? (q ? v.z : v.x) : (q ? v.w : v.y);
         };
         RunLut lg[8], lu[8];
-        lg[0] = pf_iq2x_lookup(lds, word(sl.g, 0), 0, slot16);
-        lu[0] = pf_iq2x_lookup(lds, word(sl.u, 0), 0, slot16);
-        lg[1] = pf_iq2x_lookup(lds, word(sl.g, 1), 1, slot16);
-        lu[1] = pf_iq2x_lookup(lds, word(sl.u, 1), 1, slot16);
+        lg[0] = pf_iq2x_lookup(lds, word(sl.g, 0), 0, lc);
+        lu[0] = pf_iq2x_lookup(lds, word(sl.u, 0), 0, lc);
+        lg[1] = pf_iq2x_lookup(lds, word(sl.g, 1), 1, lc);
+        lu[1] = pf_iq2x_lookup(lds, word(sl.u, 1), 1, lc);
 #pragma unroll
         for (int s = 0; s < 8; s++) {
             f16x8 av[MB];
 #pragma unroll
             for (int i = 0; i < MB; i++) av[i] = frag32<R>(A, i, lane, s);
             if (s + 2 < 8) {
-                lg[s + 2] = pf_iq2x_lookup(lds, word(sl.g, s + 2), (s + 2) & 1, slot16);
-                lu[s + 2] = pf_iq2x_lookup(lds, word(sl.u, s + 2), (s + 2) & 1, slot16);
+                lg[s + 2] = pf_iq2x_lookup(lds, word(sl.g, s + 2), (s + 2) & 1, lc);
+                lu[s + 2] = pf_iq2x_lookup(lds, word(sl.u, s + 2), (s + 2) & 1, lc);
             }
             const f16x8 bg = pf_iq2x_build(lg[s], c2[0][s >> 2]);
             const f16x8 bu = pf_iq2x_build(lu[s], c2[1][s >> 2]);
@@ -445,7 +438,7 @@ k_pf_gateup(GuArgs a) {
     if (threadIdx.x < kPfRows) {
         const int tok = a.perm[t.off + t.r0 + min((int)threadIdx.x, t.rows - 1)] / a.k;
         stok[threadIdx.x] = tok;
-        sxs[threadIdx.x] = a.xsc[tok];
+        sxs[threadIdx.x] = a.xsc[tok] * (1.f / kPfWScale);
     }
     pf_build_tables(a.grid, lds);
     __syncthreads();
@@ -540,8 +533,8 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
                 const uint32_t W = wsel[s >> 1], W10 = W >> 10;
                 // (a, -b) of this sub-block: a = d sc, b = dmin m
                 const uint32_t sb = (sl.sc[j] >> (8 * (s >> 1))) & 0xFFu;
-                const f16x2 av = u2h(f16_pair(fp16_to_f32(sl.dd[j] & 0xFFFFu) * (float)(sb & 15u)));
-                const f16x2 bv = u2h(f16_pair(-fp16_to_f32(sl.dd[j] >> 16) * (float)(sb >> 4)));
+                const f16x2 av = u2h(f16_pair(kPfWScale * fp16_to_f32(sl.dd[j] & 0xFFFFu) * (float)(sb & 15u)));
+                const f16x2 bv = u2h(f16_pair(-kPfWScale * fp16_to_f32(sl.dd[j] >> 16) * (float)(sb >> 4)));
                 uint32_t qb[4];
                 if ((s & 1) == 0) {
                     qb[0] = pc.pair<0>(W, W10); qb[1] = pc.pair<1>(W, W10);
@@ -609,7 +602,7 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
         for (int r = 0; r < 16; r++) {
             const int m = 32 * i + acc_row(r, kh);
             if (m < t.rows) {
-                const int e = semax[m];
+                const int e = semax[m] - kPfWShift;
                 float *op = a.o + (int64_t)a.perm[t.off + t.r0 + m] * a.H;
                 op[c0] = ldexpf(acc[i][0][r], e);
                 op[c0 + 32] = ldexpf(acc[i][1][r], e);
@@ -710,14 +703,16 @@ int prefill_tile_rows() { return kPfRows; }
 int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T, const float *w, float *y,
                        const Buckets &b, int max_tiles, const PrefillBufs &pb, hipStream_t s) {
     const int H = L->H, I = L->I, k = L->k;
-    static bool attr = false;
-    if (!attr) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_gateup),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kPfGuLds);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_down),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kPfDnLds);
-        attr = true;
-    }
+    static const bool attr = [] {
+        hipFuncAttributes fa;           // the gate/up tables must start at LDS address 0
+        return hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(k_pf_gateup)) == hipSuccess &&
+               fa.sharedSizeBytes == 0 &&
+               hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_gateup),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, kPfGuLds) == hipSuccess &&
+               hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_down),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, kPfDnLds) == hipSuccess;
+    }();
+    if (!attr) return BITMOE_EHIP;
     if (x_dtype == BITMOE_BF16) k_pf_xprep<1><<<T, 256, 0, s>>>(H, x, pb.x16, pb.xsc);
     else k_pf_xprep<0><<<T, 256, 0, s>>>(H, x, pb.x16, pb.xsc);
     BM_LAUNCH_CHECK();

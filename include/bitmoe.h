@@ -59,16 +59,13 @@
  *   IQ2X slab (N*nb*66 bytes):
  *     [0, 64*N*nb):           piece c (groups 2c, 2c+1 of block (n,kb)) at
  *                             ((P*nb + kb)*4 + c)*64 + r, 16 bytes each; each
- *                             group re-encoded (bijectively, same 8 bytes) as
+ *                             group regrouped (bijectively, same 8 bytes) as
  *                             two little-endian words, W0 for runs 0,1 and W1
- *                             for runs 2,3 (a run is 8 weights): bits 0-1 of
- *                             W0 / W1 are bits 0-1 / 2-3 of the group scale s;
- *                             the first run of a word is the 15-bit field R
- *                             at bits 2-16, the second at bits 17-31.  In R:
- *                             bits 0-2 the signs of weights 0,1,2, bit 3 the
- *                             parity of the signs of weights 0..3, bits 4-11
- *                             the codebook index, bits 12-14 the signs of
- *                             weights 4,5,6 (weight 7: even parity of the 8)
+ *                             for runs 2,3 (a run is 8 weights); the first
+ *                             run of a word in bytes 0-1, the second in
+ *                             bytes 2-3: the run's codebook index idx[j],
+ *                             then its sign field (bits 0-6) with bit j of
+ *                             the group scale s in bit 7
  *     [64*N*nb, 66*N*nb):     d of block (n,kb) at (P*nb + kb)*64 + r, 2 bytes
  *   Q2K slab (N*nb*84 bytes):
  *     [0, 64*N*nb):           piece c at ((P*nb + kb)*4 + c)*64 + r, 16 bytes:
@@ -113,10 +110,9 @@ typedef struct bitmoe_layer {
     const void *gate_q;        /* TILED IQ2X, E slabs of I*(H/256)*66 bytes */
     const void *up_q;          /* TILED IQ2X, same shape as gate_q */
     const void *down_q;        /* TILED Q2K, E slabs of H*(I/256)*84 bytes */
-    const void *grid;          /* uint8 [256][8] codebook magnitudes; the FFN
-                                  entry points require values 0..7 (the
-                                  format's codebook is {1,3,5,7}); the
-                                  dequant entry point takes any byte */
+    const void *grid;          /* uint8 [256][8] codebook magnitudes (the
+                                  format's codebook holds 1, 3, 5, 7; any
+                                  byte is accepted) */
     const void *shared_gate;   /* TILED bf16 [I][H], or NULL: no shared expert */
     const void *shared_up;     /* TILED bf16 [I][H] (NULL iff shared_gate is) */
     const void *shared_down;   /* TILED bf16 [H][I] (NULL iff shared_gate is) */
@@ -168,8 +164,14 @@ size_t moe_workspace_bytes(const bitmoe_layer *L, int T, int mode);
  * moe_workspace_bytes(L, T, mode) bytes, 256-byte aligned.
  * moe_ffn_decode streams each active expert's packed blocks once and decodes
  * them in registers (fp32 accumulation); it is tuned for T <= 16 and correct
- * for any T.  moe_ffn_prefill runs grouped bf16 MFMA GEMMs over weight tiles
- * dequantised on chip; it is tuned for large T and correct for any T.
+ * for any T.  moe_ffn_prefill runs grouped fp16 MFMA GEMMs (fp32
+ * accumulation) over weights dequantised into matrix-core operands on chip;
+ * it is tuned for large T and correct for any T.  Its operands are fp16:
+ * each token's x and each row of h scaled by powers of two, and weights
+ * rounded to fp16 after folding the scales (d/8 (2s+1) for IQ2X, d sc and
+ * dmin m for Q2K) with a fixed factor 2^8, so full fp16 precision holds for
+ * superblock scales d, dmin in [2^-19, 8] (codebook magnitudes up to 7);
+ * larger scales can overflow.
  */
 int moe_ffn_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T,
                    const int32_t *ids, const float *w, float *y, void *ws,

@@ -16,16 +16,13 @@ def _tiled_iq2x_numpy(canon, N, K):
     grp = b[:, :, 2:].reshape(N, nb, 8, 8)
     idx = grp[:, :, :, :4].astype(np.uint32)
     a = grp[:, :, :, 4:8].copy().view("<u4")[..., 0]
-    s = a >> 28
     runs = np.zeros((N, nb, 8, 4), dtype=np.uint32)
     for j in range(4):
-        s7 = (a >> (7 * j)) & 0x7F
-        lo4 = s7 & 15
-        par = (np.unpackbits(lo4.astype(np.uint8)[..., None], axis=-1).sum(-1) & 1).astype(np.uint32)
-        runs[..., j] = (s7 & 7) | (par << 3) | (idx[..., j] << 4) | (((s7 >> 4) & 7) << 12)
+        # index byte, then 7 sign bits with scale bit j on top
+        runs[..., j] = idx[..., j] | (((a >> (7 * j)) & 0x7F) << 8) | (((a >> (28 + j)) & 1) << 15)
     words = np.zeros((N, nb, 8, 2), dtype=np.uint32)
-    words[..., 0] = (s & 3) | (runs[..., 0] << 2) | (runs[..., 1] << 17)
-    words[..., 1] = (s >> 2) | (runs[..., 2] << 2) | (runs[..., 3] << 17)
+    words[..., 0] = runs[..., 0] | (runs[..., 1] << 16)
+    words[..., 1] = runs[..., 2] | (runs[..., 3] << 16)
     qs = words.astype("<u4").view(np.uint8).reshape(N, nb, 4, 16)       # 4 pieces of 16 bytes
     qs = qs.reshape(N // 64, 64, nb, 4, 16).transpose(0, 2, 3, 1, 4)     # [P][kb][c][r][16]
     dd = d.reshape(N // 64, 64, nb, 2).transpose(0, 2, 1, 3)             # [P][kb][r][2]
