@@ -156,8 +156,7 @@ BM_DEV uint4 lut_sign_entry(uint32_t e) {
 // entry `e` of the magnitude table from the codebook row (8 bytes), as
 // bf16 (BF = 1) or fp16 pairs
 template <int BF>
-BM_DEV uint4 lut_mag_entry(const uint8_t *__restrict__ grid, uint32_t e) {
-    const uint2 g = *reinterpret_cast<const uint2 *>(grid + 8 * e);
+BM_DEV uint4 lut_mag_from_row(uint2 g) {
     const uint32_t b[2] = {g.x, g.y};
     uint32_t m[4];
 #pragma unroll
@@ -173,14 +172,26 @@ BM_DEV uint4 lut_mag_entry(const uint8_t *__restrict__ grid, uint32_t e) {
     }
     return make_uint4(m[0], m[1], m[2], m[3]);
 }
+template <int BF>
+BM_DEV uint4 lut_mag_entry(const uint8_t *__restrict__ grid, uint32_t e) {
+    return lut_mag_from_row<BF>(*reinterpret_cast<const uint2 *>(grid + 8 * e));
+}
+// The 16 copies of one line (entry `e` of the table at byte `base`), the
+// c-th write to slot (c + e) & 15 so that the lanes of a write instruction
+// (consecutive entries) hit distinct slots.
+BM_DEV void lut_write_line(uint8_t *lut, int base, int e, uint4 v) {
+    uint4 *line = reinterpret_cast<uint4 *>(lut + base + 256 * e);
+#pragma unroll
+    for (int c = 0; c < 16; c++) line[(c + e) & 15] = v;
+}
 // both tables (SGN = kLutSgnFull or kLutSgnHalf bytes of signs), by the
-// threads of the workgroup
+// threads of the workgroup: one line (16 copies of an entry) per thread
 template <int BF, int SGN>
 BM_DEV void lut_build(const uint8_t *__restrict__ grid, uint8_t *lut) {
-    for (int i = threadIdx.x; i < 256 * 16; i += blockDim.x)
-        *reinterpret_cast<uint4 *>(lut + 16 * i) = lut_mag_entry<BF>(grid, (uint32_t)i >> 4);
-    for (int i = threadIdx.x; i < SGN / 16; i += blockDim.x)
-        *reinterpret_cast<uint4 *>(lut + kLutMagBytes + 16 * i) = lut_sign_entry((uint32_t)i >> 4);
+    for (int e = threadIdx.x; e < 256 + SGN / 256; e += blockDim.x) {
+        if (e < 256) lut_write_line(lut, 0, e, lut_mag_entry<BF>(grid, e));
+        else lut_write_line(lut, kLutMagBytes, e - 256, lut_sign_entry(e - 256));
+    }
 }
 
 // ---- tiled Q2K quant words -------------------------------------------------

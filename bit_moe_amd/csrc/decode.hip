@@ -104,7 +104,7 @@ BM_DEV void load_xgroup(XGroup<XBF16, NT> &g, const void *__restrict__ x, const 
 // fp32 sum.  SGN: bytes of the sign table (the half table drops the scale
 // bit from the offset).
 template <int XBF16, int NT, int SGN>
-BM_DEV void iq2x_group(uint32_t W0, uint32_t W1, float dq8, const uint8_t *lut, uint32_t lc,
+BM_DEV void iq2x_group(uint32_t W0, uint32_t W1, float dq8, uint32_t lc,
                        const XGroup<XBF16, NT> &xg, const void *x, const int (&tok)[NT], int H, int gg,
                        float (&acc)[NT]) {
     const float scale = dq8 * (float)iq2x_scale_odd(W0, W1);
@@ -271,6 +271,48 @@ struct Tok {
     int cnt, off, e;
 };
 
+// Cross-wave sums of the gate/up partials of NT tokens, then for token
+// t0 + t (wave t): h = silu(g) u as fp16 scaled by 2^-e so that the panel's
+// largest |h| lies in [2^14, 2^15) (no overflow, full fp16 precision; 2^e is
+// kept), with per-16-column sums for the down launch.
+template <int NT>
+BM_DEV void gateup_epilogue(int I, const Tok &tk, int t0, int P, const float (&ag)[NT], const float (&au)[NT],
+                            uint16_t *__restrict__ h, float2 *__restrict__ hsum2, float *__restrict__ hscale,
+                            float *red) {
+    const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        red[((wv * NT + t) * 2 + 0) * 64 + lane] = ag[t];
+        red[((wv * NT + t) * 2 + 1) * 64 + lane] = au[t];
+    }
+    __syncthreads();
+    if (wv < NT && t0 + wv < tk.cnt) {
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWG; v++) {
+            g += red[((v * NT + wv) * 2 + 0) * 64 + lane];
+            u += red[((v * NT + wv) * 2 + 1) * 64 + lane];
+        }
+        const float hv = silu(g) * u;
+        const int n = P * 64 + lane;
+        const int64_t row = tk.off + t0 + wv;
+        const float amax = wave_max_f32(fabsf(hv));
+        int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 14 : 0;
+        e = max(-100, min(100, e));
+        const float inv = __uint_as_float((uint32_t)(127 - e) << 23), scl = __uint_as_float((uint32_t)(127 + e) << 23);
+        const _Float16 hf = (_Float16)(hv * inv);
+        h[row * I + n] = __builtin_bit_cast(uint16_t, hf);
+        // per 16 columns: sum of h and sum of B_p h, B_p the bias of the
+        // pair that column n % 16 falls in
+        const float v = (float)hf;
+        const int pp = (n & 15) >> 1;
+        const float hs = row16_sum(v), hb = row16_sum(q2k_pair_bias(pp) * v);
+        if ((lane & 15) == 15) hsum2[row * (I / 16) + (n >> 4)] = make_float2(hs, hb);
+        if (lane == 0) hscale[row * (I / 64) + P] = scl;
+    }
+    __syncthreads();
+}
+
 template <int XBF16, int NT, int SGN>
 BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P, const uint8_t *lut,
                                const uint8_t *__restrict__ gate, const uint8_t *__restrict__ up,
@@ -323,11 +365,11 @@ BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P
                 const int gg = 2 * (pb + i);
                 const float dg = 0.125f * fp16_to_f32(gdw[i]), du = 0.125f * fp16_to_f32(udw[i]);
                 load_xgroup<XBF16, NT>(xb, x, tok, H, gg + 1);
-                iq2x_group<XBF16, NT, SGN>(g4[i].x, g4[i].y, dg, lut, lc, xa, x, tok, H, gg, ag);
-                iq2x_group<XBF16, NT, SGN>(u4[i].x, u4[i].y, du, lut, lc, xa, x, tok, H, gg, au);
+                iq2x_group<XBF16, NT, SGN>(g4[i].x, g4[i].y, dg, lc, xa, x, tok, H, gg, ag);
+                iq2x_group<XBF16, NT, SGN>(u4[i].x, u4[i].y, du, lc, xa, x, tok, H, gg, au);
                 load_xgroup<XBF16, NT>(xa, x, tok, H, pb + i + 1 < p1 ? gg + 2 : gg);
-                iq2x_group<XBF16, NT, SGN>(g4[i].z, g4[i].w, dg, lut, lc, xb, x, tok, H, gg + 1, ag);
-                iq2x_group<XBF16, NT, SGN>(u4[i].z, u4[i].w, du, lut, lc, xb, x, tok, H, gg + 1, au);
+                iq2x_group<XBF16, NT, SGN>(g4[i].z, g4[i].w, dg, lc, xb, x, tok, H, gg + 1, ag);
+                iq2x_group<XBF16, NT, SGN>(u4[i].z, u4[i].w, du, lc, xb, x, tok, H, gg + 1, au);
             }
         }
 #pragma unroll
@@ -338,39 +380,78 @@ BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P
             udw[i] = nud[i];
         }
     }
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
-        red[((wv * NT + t) * 2 + 0) * 64 + lane] = ag[t];
-        red[((wv * NT + t) * 2 + 1) * 64 + lane] = au[t];
-    }
-    __syncthreads();
-    if (wv < NT && t0 + wv < tk.cnt) {
-        float g = 0.f, u = 0.f;
-#pragma unroll
-        for (int v = 0; v < kWG; v++) {
-            g += red[((v * NT + wv) * 2 + 0) * 64 + lane];
-            u += red[((v * NT + wv) * 2 + 1) * 64 + lane];
+    gateup_epilogue<NT>(I, tk, t0, P, ag, au, h, hsum2, hscale, red);
+}
+
+// The same for an expert chosen by one token: the wave's pieces stream
+// through a ring of kRing register slots, each refilled with the piece
+// kRing places ahead as soon as it is decoded (no copies between slots, so
+// the loads stay in flight while earlier pieces are decoded).
+template <int XBF16, int SGN>
+BM_DEV void routed_gateup_1(int H, int I, int k, const Tok &tk, int P, const uint8_t *__restrict__ gate,
+                            const uint8_t *__restrict__ up, const void *__restrict__ x, const int32_t *perm,
+                            uint16_t *__restrict__ h, float2 *__restrict__ hsum2, float *__restrict__ hscale,
+                            float *red) {
+    constexpr int kRing = 4;
+    const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tok[1] = {__builtin_amdgcn_readfirstlane(perm[tk.off] / k)};
+    const int nb = H / kQK;
+    const int64_t slab = (int64_t)I * nb * 66;
+    const uint8_t *G = gate + tk.e * slab, *U = up + tk.e * slab;
+    const uint4 *gq = reinterpret_cast<const uint4 *>(G) + (int64_t)P * nb * 4 * 64 + lane;
+    const uint4 *uq = reinterpret_cast<const uint4 *>(U) + (int64_t)P * nb * 4 * 64 + lane;
+    const uint16_t *gd = reinterpret_cast<const uint16_t *>(G + (int64_t)I * nb * 64) + (int64_t)P * nb * 64 + lane;
+    const uint16_t *ud = reinterpret_cast<const uint16_t *>(U + (int64_t)I * nb * 64) + (int64_t)P * nb * 64 + lane;
+    int p0, p1;
+    split_range(4 * nb, kWG, wv, p0, p1);
+    struct Piece { uint4 g, u; uint32_t dg, du; };
+    // pieces past the wave's last re-read it (cached) and are not decoded
+    auto load = [&](int pc, Piece &q) {
+        pc = min(pc, p1 - 1);
+        q.g = gq[(int64_t)pc * 64];
+        q.u = uq[(int64_t)pc * 64];
+        q.dg = gd[(int64_t)(pc >> 2) * 64];
+        q.du = ud[(int64_t)(pc >> 2) * 64];
+    };
+    float ag[1] = {0.f}, au[1] = {0.f};
+    const uint32_t lc = lut_lane_const(lane);
+    auto decode = [&](int pc, const Piece &q) {
+        XGroup<XBF16, 1> x0, x1;
+        load_xgroup<XBF16, 1>(x0, x, tok, H, 2 * pc);
+        load_xgroup<XBF16, 1>(x1, x, tok, H, 2 * pc + 1);
+        const float dg = 0.125f * fp16_to_f32(q.dg), du = 0.125f * fp16_to_f32(q.du);
+        iq2x_group<XBF16, 1, SGN>(q.g.x, q.g.y, dg, lc, x0, x, tok, H, 2 * pc, ag);
+        iq2x_group<XBF16, 1, SGN>(q.u.x, q.u.y, du, lc, x0, x, tok, H, 2 * pc, au);
+        iq2x_group<XBF16, 1, SGN>(q.g.z, q.g.w, dg, lc, x1, x, tok, H, 2 * pc + 1, ag);
+        iq2x_group<XBF16, 1, SGN>(q.u.z, q.u.w, du, lc, x1, x, tok, H, 2 * pc + 1, au);
+    };
+    // decode a slot, then refill it (the refill stays after the decode of
+    // the registers it overwrites)
+    auto step = [&](int pc, Piece &q) {
+        decode(pc, q);
+        __builtin_amdgcn_sched_barrier(0);
+        load(pc + kRing, q);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    static_assert(kRing == 4, "four slots below");
+    if (p0 < p1) {
+        Piece q0, q1, q2, q3;
+        load(p0, q0);
+        load(p0 + 1, q1);
+        load(p0 + 2, q2);
+        load(p0 + 3, q3);
+        int pc = p0;
+        for (; pc + kRing <= p1; pc += kRing) {
+            step(pc, q0);
+            step(pc + 1, q1);
+            step(pc + 2, q2);
+            step(pc + 3, q3);
         }
-        const float hv = silu(g) * u;
-        const int n = P * 64 + lane;
-        const int64_t row = tk.off + t0 + wv;
-        // fp16 h scaled by 2^-e so that the panel's largest |h| lies in
-        // [2^14, 2^15): no overflow, full fp16 precision; 2^e is kept
-        const float amax = wave_max_f32(fabsf(hv));
-        int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 14 : 0;
-        e = max(-100, min(100, e));
-        const float inv = __uint_as_float((uint32_t)(127 - e) << 23), scl = __uint_as_float((uint32_t)(127 + e) << 23);
-        const _Float16 hf = (_Float16)(hv * inv);
-        h[row * I + n] = __builtin_bit_cast(uint16_t, hf);
-        // per 16 columns: sum of h and sum of B_p h, B_p the bias of the
-        // pair that column n % 16 falls in
-        const float v = (float)hf;
-        const int pp = (n & 15) >> 1;
-        const float hs = row16_sum(v), hb = row16_sum(q2k_pair_bias(pp) * v);
-        if ((lane & 15) == 15) hsum2[row * (I / 16) + (n >> 4)] = make_float2(hs, hb);
-        if (lane == 0) hscale[row * (I / 64) + P] = scl;
+        if (pc < p1) decode(pc, q0);
+        if (pc + 1 < p1) decode(pc + 1, q1);
+        if (pc + 2 < p1) decode(pc + 2, q2);
     }
-    __syncthreads();
+    gateup_epilogue<1>(I, tk, 0, P, ag, au, h, hsum2, hscale, red);
 }
 
 // sum of 8 products of bf16 weight pairs with h given as bf16 hi + lo
@@ -393,14 +474,29 @@ struct SmallRoute {
     int n_active;
 };
 
+// Lane l of the wave: the logits of experts l, l+64, l+128, l+192 of token t
+// (E <= 256; indices past E re-read the last one and are ignored).
+BM_DEV void route_logits_load(const float *__restrict__ logits, int E, int t, float (&lv)[4]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < 4; i++) lv[i] = logits[(int64_t)t * E + min(lane + 64 * i, E - 1)];
+}
+
 BM_DEV void route_in_wg(int mode, int E, int k, int T, const float *__restrict__ logits, int32_t *ids,
-                        float *w, const bm_host::Buckets &bk, SmallRoute &r) {
-    const int wv = threadIdx.x >> 6, n = T * k;
+                        float *w, const bm_host::Buckets &bk, SmallRoute &r, float (&lv)[4], bool lv_loaded) {
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), n = T * k, nw = blockDim.x >> 6;
     const bool out = blockIdx.x == 0;
     if (mode == 1) {
-        for (int t = wv; t < T; t += kWG)
-            topk_wave(logits + (int64_t)t * E, E, k, out ? ids + (int64_t)t * k : nullptr,
-                      out ? w + (int64_t)t * k : nullptr, r.ids + t * k);
+        for (int t = wv; t < T; t += nw) {
+            int32_t *oi = out ? ids + (int64_t)t * k : nullptr;
+            float *ow = out ? w + (int64_t)t * k : nullptr;
+            if (E <= 256) {
+                if (!(lv_loaded && t == wv)) route_logits_load(logits, E, t, lv);
+                topk_wave4(lv, E, k, oi, ow, r.ids + t * k);
+            } else {
+                topk_wave(logits + (int64_t)t * E, E, k, oi, ow, r.ids + t * k);
+            }
+        }
     } else {
         for (int p = threadIdx.x; p < n; p += blockDim.x) r.ids[p] = ids[p];
     }
@@ -418,6 +514,32 @@ BM_DEV void route_in_wg(int mode, int E, int k, int T, const float *__restrict__
             bk.offsets[e] = r.offsets[e];
         }
         if (threadIdx.x == 0) *bk.n_active = r.n_active;
+    }
+}
+
+// Shared-expert h of elements [f0, f1) by this workgroup: h = silu(sum of
+// the gate partials) * (sum of the up partials), in a fixed order, as bf16
+// hi + lo for the down launch.  The first element's partials may have been
+// loaded already (fg, fu).
+BM_DEV void shared_h_store(int64_t n, int kc_sg, const float *__restrict__ sgp, uint16_t *__restrict__ hs, int64_t i,
+                           const float (&fg)[kMaxChunks], const float (&fu)[kMaxChunks]) {
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; c++)
+        if (c < kc_sg) { g += fg[c]; u += fu[c]; }
+    (void)sgp;
+    const float hv = silu(g) * u;
+    const uint32_t hi = f32_to_bf16_rne(hv);
+    hs[i] = (uint16_t)hi;
+    hs[n + i] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
+}
+BM_DEV void shared_h_load(int64_t n, int kc_sg, const float *__restrict__ sgp, int64_t i, float (&fg)[kMaxChunks],
+                          float (&fu)[kMaxChunks]) {
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; c++) {
+        const int cc = min(c, kc_sg - 1);
+        fg[c] = sgp[(int64_t)(2 * cc) * n + i];
+        fu[c] = sgp[(int64_t)(2 * cc + 1) * n + i];
     }
 }
 
@@ -450,63 +572,63 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
     float *red = reinterpret_cast<float *>(lut + dec_lut_bytes<MULTI>());
     SmallRoute &sr = *reinterpret_cast<SmallRoute *>(red + dec_red_floats<MULTI>());
     constexpr int SGN = dec_sgn_bytes<MULTI>();
+    const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b = blockIdx.x, panels = I / 64, slot = b / panels, P = b % panels;
     const int32_t *counts = bk.counts, *offsets = bk.offsets, *perm = bk.perm, *active = bk.active;
+    // shared-expert h, spread over all workgroups of the single-token launch
+    const int64_t nfin = (!MULTI && kc_sg) ? (int64_t)T * I : 0;
+    const int64_t fchunk = (nfin + n_gwg - 1) / n_gwg, f0 = b * fchunk, f1 = min(nfin, f0 + fchunk);
+    float fg[kMaxChunks], fu[kMaxChunks];
     int na;
     if (!MULTI && route_mode) {
-        lut_build<1, SGN>(grid, lut);
-        route_in_wg(route_mode, E, k, T, logits, ids, w, bk, sr);     // ends with a barrier
+        // routing in every workgroup.  Loads that do not depend on each
+        // other go out first: the codebook rows, the logits, the first
+        // shared-h partials; the tables are written while they arrive.
+        uint2 grow = make_uint2(0u, 0u);
+        if (tid < 256) grow = *reinterpret_cast<const uint2 *>(grid + 8 * tid);
+        float lv[4];
+        const bool pre = route_mode == 1 && E <= 256 && wv < T;
+        if (pre) route_logits_load(logits, E, wv, lv);
+        if (f0 + tid < f1) shared_h_load(nfin, kc_sg, sgp, f0 + tid, fg, fu);
+        if (tid < 256) lut_write_line(lut, 0, tid, lut_mag_from_row<1>(grow));
+        else if (tid < 256 + SGN / 256) lut_write_line(lut, kLutMagBytes, tid - 256, lut_sign_entry(tid - 256));
+        route_in_wg(route_mode, E, k, T, logits, ids, w, bk, sr, lv, pre);     // ends with a barrier
         counts = sr.counts;
         offsets = sr.offsets;
         perm = sr.perm;
         active = sr.active;
         na = sr.n_active;
     } else {
+        if constexpr (!MULTI)
+            if (f0 + tid < f1) shared_h_load(nfin, kc_sg, sgp, f0 + tid, fg, fu);
         na = *bk.n_active;
     }
-    const int b = blockIdx.x;
-    if (b < n_gwg) {
-        const int panels = I / 64, slot = b / panels, P = b % panels;
-        if (!MULTI && kc_sg && slot == 0) {
-            // shared h = silu(sum of the gate partials) * (sum of the up
-            // partials), in a fixed order, as bf16 hi + lo for the down
-            // launch; chunks of blockDim elements over the first panels'
-            // workgroups
-            const int64_t n = (int64_t)T * I;
-            for (int64_t i = (int64_t)P * blockDim.x + threadIdx.x; i < n; i += (int64_t)panels * blockDim.x) {
-                float g = 0.f, u = 0.f;
-                for (int c = 0; c < kc_sg; c++) {
-                    g += sgp[(int64_t)(2 * c) * n + i];
-                    u += sgp[(int64_t)(2 * c + 1) * n + i];
-                }
-                const float hv = silu(g) * u;
-                const uint32_t hi = f32_to_bf16_rne(hv);
-                hs[i] = (uint16_t)hi;
-                hs[n + i] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
-            }
+    if constexpr (!MULTI) {
+        if (f0 + tid < f1) shared_h_store(nfin, kc_sg, sgp, hs, f0 + tid, fg, fu);
+        for (int64_t i = f0 + tid + blockDim.x; i < f1; i += blockDim.x) {
+            shared_h_load(nfin, kc_sg, sgp, i, fg, fu);
+            shared_h_store(nfin, kc_sg, sgp, hs, i, fg, fu);
         }
-        if (slot >= na) return;
-        Tok tk;
-        tk.e = active[slot];
-        tk.off = offsets[tk.e];
-        tk.cnt = counts[tk.e];
-        if ((tk.cnt > 1) != (MULTI != 0)) return;
-        if (MULTI || !route_mode) {
-            lut_build<1, SGN>(grid, lut);
-            __syncthreads();
-        }
-        if (!MULTI) {
-            routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, 0, P, lut, gate, up, x, perm, h, hsum2, hscale, red);
-            return;
-        }
-        for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
-            if (tk.cnt - t0 == 1)
-                routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, P, lut, gate, up, x, perm, h, hsum2, hscale,
-                                                  red);
-            else
-                routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, P, lut, gate, up, x, perm, h, hsum2, hscale,
-                                                    red);
-        }
+    }
+    if (slot >= na) return;
+    Tok tk;
+    tk.e = active[slot];
+    tk.off = offsets[tk.e];
+    tk.cnt = counts[tk.e];
+    if ((tk.cnt > 1) != (MULTI != 0)) return;
+    if (MULTI || !route_mode) {
+        lut_build<1, SGN>(grid, lut);
+        __syncthreads();
+    }
+    if (!MULTI) {
+        routed_gateup_1<XBF16, SGN>(H, I, k, tk, P, gate, up, x, perm, h, hsum2, hscale, red);
         return;
+    }
+    for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
+        if (tk.cnt - t0 == 1)
+            routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, P, lut, gate, up, x, perm, h, hsum2, hscale, red);
+        else
+            routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, P, lut, gate, up, x, perm, h, hsum2, hscale, red);
     }
 }
 

@@ -76,6 +76,77 @@ BM_DEV void topk_wave(const float *__restrict__ lrow, int E, int k, int32_t *__r
     }
 }
 
+// Wave-wide minimum of an int (DPP as wave_max_f32).
+template <int CTRL, int ROWS>
+BM_DEV int dpp_min_i32(int v) {
+    return min(v, __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xF, false));
+}
+BM_DEV int wave_min_i32(int v) {
+    v = dpp_min_i32<0x111, 0xF>(v);
+    v = dpp_min_i32<0x112, 0xF>(v);
+    v = dpp_min_i32<0x114, 0xF>(v);
+    v = dpp_min_i32<0x118, 0xF>(v);
+    v = dpp_min_i32<0x142, 0xA>(v);
+    v = dpp_min_i32<0x143, 0xC>(v);
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Top-k of one token's logits for E <= 256, by one wavefront, from values
+// the caller loaded beforehand: lane l holds the logits of experts l, l+64,
+// l+128, l+192 in v[] (anything beyond E is ignored).  Order: logit
+// descending, expert index ascending; NaN counts as -inf.  Each lane sorts
+// its four; every round takes the wave max of the lane heads, the lowest
+// expert index among heads equal to it wins and its lane drops its head.
+// Lane j < k keeps the j-th pick, so the softmax over the k picks is one
+// row sum.  Lanes j < k write ids[j], w[j] and sids[j] (any may be null).
+BM_DEV void topk_wave4(float (&v)[4], int E, int k, int32_t *__restrict__ ids, float *__restrict__ wout,
+                       int *sids) {
+    const int lane = lane_id();
+    constexpr int kNone = 0x7FFFFFFF;
+    int ix[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int e = lane + 64 * i;
+        ix[i] = e < E ? e : kNone;
+        if (e >= E || !(v[i] == v[i])) v[i] = -__builtin_inff();
+    }
+    auto cx = [&](int a, int b) {          // order slots a < b
+        const bool sw = v[b] > v[a] || (v[b] == v[a] && ix[b] < ix[a]);
+        const float tv = sw ? v[b] : v[a], tb = sw ? v[a] : v[b];
+        const int ti = sw ? ix[b] : ix[a], tj = sw ? ix[a] : ix[b];
+        v[a] = tv; v[b] = tb; ix[a] = ti; ix[b] = tj;
+    };
+    cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+    float pv = 0.f, m0 = 0.f;
+    int pi = 0;
+    for (int j = 0; j < k; j++) {
+        const float m = wave_max_f32(v[0]);
+        const bool at = v[0] == m;
+        int win;
+        const uint64_t b = __ballot(at);
+        if (__popcll(b) == 1) {
+            win = (int)__builtin_ctzll(b);
+        } else {                            // equal heads: lowest expert index
+            const int mn = wave_min_i32(at ? ix[0] : kNone);
+            win = (int)__builtin_ctzll(__ballot(at && ix[0] == mn));
+        }
+        const int id = __builtin_amdgcn_readlane(ix[0], win);
+        if (j == 0) m0 = m;
+        if (lane == j) { pv = m; pi = id; }
+        if (lane == win) {
+            v[0] = v[1]; v[1] = v[2]; v[2] = v[3]; v[3] = -__builtin_inff();
+            ix[0] = ix[1]; ix[1] = ix[2]; ix[2] = ix[3]; ix[3] = kNone;
+        }
+    }
+    const float ex = lane < k ? __expf(pv - m0) : 0.f;
+    const float z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row16_sum(ex)), 15));
+    if (lane < k) {
+        if (ids) ids[lane] = pi;
+        if (wout) wout[lane] = ex * (1.0f / z);
+        if (sids) sids[lane] = pi;
+    }
+}
+
 constexpr int kBT = 1024;           // threads per bucketing block = pairs per chunk
 constexpr int kBW = kBT / 64;       // waves per block
 

@@ -168,19 +168,8 @@ k_pf_xprep(int H, const void *__restrict__ x, uint16_t *__restrict__ x16, float 
 // sign line.
 BM_DEV void pf_build_tables(const uint8_t *__restrict__ grid, uint8_t *lds) {
     const int t = threadIdx.x;
-    uint4 v;
-    uint8_t *line;
-    if (t < 256) {
-        v = lut_mag_entry<0>(grid, t);
-        line = lds + 256 * t;
-    } else if (t < 384) {
-        v = lut_sign_entry(t - 256);
-        line = lds + kPfMagBytes + 256 * (t - 256);
-    } else {
-        return;
-    }
-#pragma unroll
-    for (int c = 0; c < 16; c++) *reinterpret_cast<uint4 *>(line + 16 * c) = v;
+    if (t < 256) lut_write_line(lds, 0, t, lut_mag_entry<0>(grid, t));
+    else if (t < 384) lut_write_line(lds, kPfMagBytes, t - 256, lut_sign_entry(t - 256));
 }
 
 // Table lookups of run `second` of word W (magnitudes, sign masks); lc =
@@ -621,7 +610,7 @@ k_pf_down(DnArgs a) {
     if (threadIdx.x < kPfRows) {
         const int nI = a.I / kPfGuCols;
         const int64_t gr = t.off + t.r0 + min((int)threadIdx.x, t.rows - 1);
-        int e = -1 << 30;
+        int e = -(1 << 30);
         for (int c = 0; c < nI; c++) e = max(e, a.hexp[gr * nI + c]);
         semax[threadIdx.x] = e;
     }
