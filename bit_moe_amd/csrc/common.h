@@ -272,12 +272,20 @@ BM_DEV void router_row(const uint4 *__restrict__ wrow, const void *__restrict__ 
             const int s = s0 + i, k = 512 * s + 8 * lane;
             wv[i] = wrow[(s < steps && k < H) ? 64 * s + lane : lane];
         }
+        // every loaded piece is used (a branch around the extra ones would
+        // let the compiler sink their loads next to the use); the extra
+        // ones' sums are dropped
 #pragma unroll
         for (int i = 0; i < CH; i++) {
             const int s = s0 + i, k = 512 * s + 8 * lane;
-            if (s >= steps || k >= H) continue;
+            const bool keep = s < steps && k < H;
+            if (NT > 1 && !keep) continue;      // (more tokens: registers are short)
+            const int kc = keep ? k : 8 * lane;
 #pragma unroll
-            for (int t = 0; t < NT; t++) acc[t] = router_dot8<XBF16, NT>(wv[i], x, H, t < T ? t : 0, k, acc[t]);
+            for (int t = 0; t < NT; t++) {
+                const float a = router_dot8<XBF16, NT>(wv[i], x, H, t < T ? t : 0, kc, acc[t]);
+                acc[t] = keep ? a : acc[t];
+            }
         }
     }
 #pragma unroll

@@ -163,15 +163,33 @@ BM_DEV void shared_gateup_pass(int H, int I, int T, int t0, int P, int c0, int c
     for (int t = 0; t < NT; t++) ag[t] = au[t] = 0.f;
     int w0, w1;
     split_range(c1 - c0, NW, wv, w0, w1);
-#pragma unroll 4
-    for (int c = c0 + w0; c < c0 + w1; c++) {
-        const int64_t pc = ((int64_t)P * K8 + c) * 64 + lane;
-        const uint4 gw = sg[pc], uw = su[pc];
+    // the loads of up to kB pieces of both matrices at once (past the
+    // wave's range: its last piece again, unused)
+    constexpr int kB = NT == 1 ? 8 : 4;
+    for (int cb = c0 + w0; cb < c0 + w1; cb += kB) {
+        uint4 gw[kB], uw[kB];
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
-            const void *xp = xrow<XBF16>(x, tok[t], H, 8 * c);
-            ag[t] = dot8<XBF16>(make_uint2(gw.x, gw.y), make_uint2(gw.z, gw.w), xp, ag[t]);
-            au[t] = dot8<XBF16>(make_uint2(uw.x, uw.y), make_uint2(uw.z, uw.w), xp, au[t]);
+        for (int i = 0; i < kB; i++) {
+            const int64_t pc = ((int64_t)P * K8 + min(cb + i, c0 + w1 - 1)) * 64 + lane;
+            gw[i] = sg[pc];
+            uw[i] = su[pc];
+        }
+        __builtin_amdgcn_sched_barrier(0);      // keep the batch's loads together, ahead of their use
+        // every loaded piece is used (a branch around the extra ones would
+        // let the compiler sink their loads next to the use); the extra
+        // ones' sums are dropped
+#pragma unroll
+        for (int i = 0; i < kB; i++) {
+            const int c = min(cb + i, c0 + w1 - 1);
+            const bool keep = cb + i < c0 + w1;
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                const void *xp = xrow<XBF16>(x, tok[t], H, 8 * c);
+                const float g = dot8<XBF16>(make_uint2(gw[i].x, gw[i].y), make_uint2(gw[i].z, gw[i].w), xp, ag[t]);
+                const float u = dot8<XBF16>(make_uint2(uw[i].x, uw[i].y), make_uint2(uw[i].z, uw[i].w), xp, au[t]);
+                ag[t] = keep ? g : ag[t];
+                au[t] = keep ? u : au[t];
+            }
         }
     }
 #pragma unroll
@@ -197,7 +215,7 @@ BM_DEV void shared_gateup_pass(int H, int I, int T, int t0, int P, int c0, int c
 // gate/up partial sums per (panel, K chunk).  Workgroup 0 also clears the
 // down launch's per-panel combine counters.
 template <int XBF16>
-__global__ void __launch_bounds__(kW * 64)
+__global__ void __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4)))
 k_dec_front(int H, int I, int E, int T, int n_rwg, int kc_sg, const uint16_t *__restrict__ wr,
             const void *__restrict__ x, float *__restrict__ logits, int32_t *__restrict__ ycount,
             const uint4 *__restrict__ sg, const uint4 *__restrict__ su, float *__restrict__ sgp) {
