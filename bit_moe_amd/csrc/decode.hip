@@ -679,24 +679,23 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
     const Q2kPairConsts qc;
     int kb0, kb1;
     split_range(nb, kWD, wv, kb0, kb1);
-    // the next superblock is in flight while one is decoded
-    uint4 q4[4], nq4[4], sc4 = make_uint4(0, 0, 0, 0), nsc4 = sc4;
-    uint32_t dm = 0, ndm = 0;
-    auto load = [&](int kb, uint4 (&q)[4], uint4 &sc, uint32_t &dmv) {
+    // superblocks two at a time, both loaded before either is decoded (the
+    // second of an odd tail is the first again, decoded and dropped: a
+    // branch around it would let the compiler sink its loads to the use)
+    struct Sb { uint4 q[4], sc; uint32_t dm; };
+    auto load = [&](int kb, Sb &v) {
         const int64_t pk = (int64_t)P * nb + kb;
 #pragma unroll
-        for (int c = 0; c < 4; c++) q[c] = dq[(pk * 4 + c) * 64 + lane];
-        sc = ds[pk * 64 + lane];
-        dmv = dd[pk * 64 + lane];
+        for (int c = 0; c < 4; c++) v.q[c] = dq[(pk * 4 + c) * 64 + lane];
+        v.sc = ds[pk * 64 + lane];
+        v.dm = dd[pk * 64 + lane];
     };
-    if (kb0 < kb1) load(kb0, q4, sc4, dm);
-    for (int kb = kb0; kb < kb1; kb++) {
-        if (kb + 1 < kb1) load(kb + 1, nq4, nsc4, ndm);
-        const float d = fp16_to_f32(dm & 0xFFFFu), dmin = fp16_to_f32(dm >> 16);
+    auto decode = [&](int kb, const Sb &v, bool keep) {
+        const float d = fp16_to_f32(v.dm & 0xFFFFu), dmin = fp16_to_f32(v.dm >> 16);
 #pragma unroll
         for (int c = 0; c < 4; c++) {                 // 64 columns: sub-blocks 4c..4c+3
-            const uint32_t qw[4] = {q4[c].x, q4[c].y, q4[c].z, q4[c].w};
-            const uint32_t scw = c == 0 ? sc4.x : c == 1 ? sc4.y : c == 2 ? sc4.z : sc4.w;
+            const uint32_t qw[4] = {v.q[c].x, v.q[c].y, v.q[c].z, v.q[c].w};
+            const uint32_t scw = c == 0 ? v.sc.x : c == 1 ? v.sc.y : c == 2 ? v.sc.z : v.sc.w;
             const uint32_t scl = scw & 0x0F0F0F0Fu, mnb = (scw >> 4) & 0x0F0F0F0Fu;
             const int col = kb * kQK + 64 * c;
             float a1[NT], a2[NT];
@@ -729,13 +728,19 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
 #pragma unroll
             for (int t = 0; t < NT; t++) {
                 const float hsc = hscale[(int64_t)rows[t] * (I / 64) + (col >> 6)];
-                acc[t] = fmaf(hsc, fmaf(d, a1[t], -dmin * a2[t]), acc[t]);
+                const float v2 = fmaf(hsc, fmaf(d, a1[t], -dmin * a2[t]), acc[t]);
+                acc[t] = keep ? v2 : acc[t];
             }
         }
-#pragma unroll
-        for (int c = 0; c < 4; c++) q4[c] = nq4[c];
-        sc4 = nsc4;
-        dm = ndm;
+    };
+    for (int kb = kb0; kb < kb1; kb += 2) {
+        const int kb2 = kb + 1 < kb1 ? kb + 1 : kb;
+        Sb va, vb;
+        load(kb, va);
+        load(kb2, vb);
+        __builtin_amdgcn_sched_barrier(0);
+        decode(kb, va, true);
+        decode(kb2, vb, kb + 1 < kb1);
     }
 #pragma unroll
     for (int t = 0; t < NT; t++) red[(wv * NT + t) * 64 + lane] = acc[t];
@@ -763,31 +768,27 @@ BM_DEV void shared_down_pass(int H, int I, int T, int t0, int P, int c0, int c1,
     for (int t = 0; t < NT; t++) acc[t] = 0.f;
     int w0, w1;
     split_range(c1 - c0, kWD, wv, w0, w1);
-    // batches of 8 pieces, the next batch in flight while one is used
+    // batches of B pieces loaded at once (past the wave's range: its last
+    // piece again, used and dropped, so that the loads stay together)
     constexpr int B = 8;
-    uint4 cur[B], nxt[B];
     const uint4 *base = sd + (int64_t)P * K8 * 64 + lane;
-    auto load = [&](int cb, uint4 (&v)[B]) {
-#pragma unroll
-        for (int i = 0; i < B; i++) v[i] = base[(int64_t)min(cb + i, c0 + w1 - 1) * 64];
-    };
-    if (w0 < w1) load(c0 + w0, cur);
     for (int cb = c0 + w0; cb < c0 + w1; cb += B) {
-        if (cb + B < c0 + w1) load(cb + B, nxt);
+        uint4 cur[B];
+#pragma unroll
+        for (int i = 0; i < B; i++) cur[i] = base[(int64_t)min(cb + i, c0 + w1 - 1) * 64];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < B; i++) {
-            const int c = cb + i;
-            if (c < c0 + w1) {
+            const int c = min(cb + i, c0 + w1 - 1);
+            const bool keep = cb + i < c0 + w1;
 #pragma unroll
-                for (int t = 0; t < NT; t++) {
-                    const uint16_t *hp = hs + (int64_t)min(t0 + t, T - 1) * I + 8 * c;
-                    acc[t] = dot8_hilo(cur[i], *reinterpret_cast<const uint4 *>(hp),
-                                       *reinterpret_cast<const uint4 *>(hp + lo_off), acc[t]);
-                }
+            for (int t = 0; t < NT; t++) {
+                const uint16_t *hp = hs + (int64_t)min(t0 + t, T - 1) * I + 8 * c;
+                const float v = dot8_hilo(cur[i], *reinterpret_cast<const uint4 *>(hp),
+                                          *reinterpret_cast<const uint4 *>(hp + lo_off), acc[t]);
+                acc[t] = keep ? v : acc[t];
             }
         }
-#pragma unroll
-        for (int i = 0; i < B; i++) cur[i] = nxt[i];
     }
 #pragma unroll
     for (int t = 0; t < NT; t++) red[(wv * NT + t) * 64 + lane] = acc[t];
