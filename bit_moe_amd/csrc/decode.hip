@@ -265,8 +265,16 @@ k_dec_mid(int E, int k, int T, const float *__restrict__ logits, int32_t *__rest
     __shared__ int swave[kBW + 1];
     const int tid = threadIdx.x, wv = tid >> 6;
     if (logits) {
-        for (int t = wv; t < T; t += kBW)
-            topk_wave(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k);
+        for (int t = wv; t < T; t += kBW) {
+            if (E <= 256) {
+                float lv[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) lv[i] = logits[(int64_t)t * E + min(lane_id() + 64 * i, E - 1)];
+                topk_wave4(lv, E, k, ids + (int64_t)t * k, w + (int64_t)t * k, nullptr);
+            } else {
+                topk_wave(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k);
+            }
+        }
         __threadfence_block();
         __syncthreads();
     }
@@ -593,9 +601,9 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
     const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x, panels = I / 64, slot = b / panels, P = b % panels;
     const int32_t *counts = bk.counts, *offsets = bk.offsets, *perm = bk.perm, *active = bk.active;
-    // shared-expert h, spread over all workgroups of the single-token launch
+    // shared-expert h, spread over all workgroups of the MULTI = 0 launch
     const int64_t nfin = (!MULTI && kc_sg) ? (int64_t)T * I : 0;
-    const int64_t fchunk = (nfin + n_gwg - 1) / n_gwg, f0 = b * fchunk, f1 = min(nfin, f0 + fchunk);
+    const int64_t fchunk = (nfin + gridDim.x - 1) / gridDim.x, f0 = b * fchunk, f1 = min(nfin, f0 + fchunk);
     float fg[kMaxChunks], fu[kMaxChunks];
     int na;
     if (!MULTI && route_mode) {
@@ -628,25 +636,44 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
             shared_h_store(nfin, kc_sg, sgp, hs, i, fg, fu);
         }
     }
-    if (slot >= na) return;
-    Tok tk;
-    tk.e = active[slot];
-    tk.off = offsets[tk.e];
-    tk.cnt = counts[tk.e];
-    if ((tk.cnt > 1) != (MULTI != 0)) return;
-    if (MULTI || !route_mode) {
-        lut_build<1, SGN>(grid, lut);
-        __syncthreads();
-    }
-    if (!MULTI) {
+    if (!MULTI && route_mode) {
+        // one (slot, panel) item per workgroup, the tables already built
+        if (slot >= na) return;
+        Tok tk;
+        tk.e = active[slot];
+        tk.off = offsets[tk.e];
+        tk.cnt = counts[tk.e];
+        if (tk.cnt != 1) return;
         routed_gateup_1<XBF16, SGN>(H, I, k, tk, P, gate, up, x, perm, h, hsum2, hscale, red);
         return;
     }
-    for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
-        if (tk.cnt - t0 == 1)
-            routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, P, lut, gate, up, x, perm, h, hsum2, hscale, red);
-        else
-            routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, P, lut, gate, up, x, perm, h, hsum2, hscale, red);
+    // routing done by an earlier launch: the workgroups loop over the
+    // (slot, panel) items, the tables built once by each
+    bool built = false;
+    for (int it = b; it < n_gwg; it += gridDim.x) {
+        const int si = it / panels, Pi = it - si * panels;
+        if (si >= na) break;
+        Tok tk;
+        tk.e = active[si];
+        tk.off = offsets[tk.e];
+        tk.cnt = counts[tk.e];
+        if ((tk.cnt > 1) != (MULTI != 0)) continue;
+        if (!built) {
+            lut_build<1, SGN>(grid, lut);
+            __syncthreads();
+            built = true;
+        }
+        if (!MULTI) {
+            routed_gateup_1<XBF16, SGN>(H, I, k, tk, Pi, gate, up, x, perm, h, hsum2, hscale, red);
+            continue;
+        }
+        for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
+            if (tk.cnt - t0 == 1)
+                routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, Pi, lut, gate, up, x, perm, h, hsum2, hscale, red);
+            else
+                routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, lut, gate, up, x, perm, h, hsum2, hscale,
+                                                    red);
+        }
     }
 }
 
@@ -894,6 +921,14 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const uint8_t *__re
 
 namespace bm_host {
 
+// compute units of the current device (one gate/up workgroup fits per CU)
+static int cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
 DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     DecodePlan p;
     const bool shared = L->shared_gate != nullptr;
@@ -902,7 +937,10 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     p.kc_sg = shared ? 8 : 0;
     p.kc_sd = shared ? std::max(1, (L->I + kSharedChunkCols - 1) / kSharedChunkCols) : 0;
     p.small = (int64_t)T * L->k <= kWaveBucketMax;
-    p.need_mid = !p.small;
+    // one token: every gate/up workgroup routes it itself; more tokens: one
+    // routing launch, so that the gate/up workgroups can each take several
+    // (expert, panel) items
+    p.need_mid = !p.small || T > 1;
     return p;
 }
 
@@ -926,7 +964,7 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
                                        b.sgp);
         BM_LAUNCH_CHECK();
     }
-    // mid: top-k and bucketing of batches above 128 pairs
+    // mid: top-k and bucketing of batches of more than one token
     if (p.need_mid) {
         const int64_t n = (int64_t)T * k;
         const bool in_mid = n <= 4096;
@@ -944,7 +982,7 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     }
     // routed gate/up; experts chosen by several tokens in a second launch
     const int n_gwg = p.slots * (I / 64);
-    const int route_mode = p.small ? (p.n_rwg ? 1 : 2) : 0;
+    const int route_mode = T == 1 ? (p.n_rwg ? 1 : 2) : 0;
     static const bool lds_set = [] {
         bool ok = true;
         for (auto f : {k_dec_gateup<1, 0>, k_dec_gateup<0, 0>, k_dec_gateup<1, 1>, k_dec_gateup<0, 1>}) {
@@ -966,7 +1004,8 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
         // the timing events, when set, are taken by the dispatch itself
         // around the first gate/up launch
         const TimingEvents ev = multi ? TimingEvents{} : timing_events();
-        hipExtLaunchKernelGGL(kg, dim3(n_gwg), dim3(kWG * 64),
+        const int grid = route_mode ? n_gwg : std::min(n_gwg, cu_count());
+        hipExtLaunchKernelGGL(kg, dim3(grid), dim3(kWG * 64),
                               multi ? dec_gateup_lds<1>() : dec_gateup_lds<0>(), s, ev.start, ev.stop, 0, H, I, E, k,
                               T, n_gwg, multi ? 0 : route_mode, (const uint8_t *)L->gate_q,
                               (const uint8_t *)L->up_q, (const uint8_t *)L->grid, x, (const float *)b.logits, b.ids,
