@@ -210,3 +210,37 @@ def test_forward_decode_routes_and_matches_oracle(T):
     np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=1e-5)
     ref = oracle.layer_ffn(L, x, rid, gw.cpu().numpy().astype(np.float64))
     assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_forward_decode_small_expert_count(T):
+    """E = 8 experts (fewer than a wave's lanes: the in-launch top-k sees
+    missing entries), shared expert, bf16: GPU routing + FFN against the
+    oracle's."""
+    require_gpu()
+    import bit_moe_amd as bm
+    w = synth.WORKLOADS["tiny"].with_(name=f"tiny_fwd{T}", T=T, shared=True, x_dtype="bf16", seed=31)
+    L = synth_layer(w)
+    x, _ = synth.make_tokens(w, accept=lambda t, r: oracle.margin_ok(r, L.router(), w.k, 1e-4))
+    y, gid, gw = bm.forward_decode(device_layer(w), x_to_device(x))
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(x, L.router(), w.k)
+    np.testing.assert_array_equal(gid.cpu().numpy(), rid)
+    np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=1e-5)
+    ref = oracle.layer_ffn(L, x, rid, gw.cpu().numpy().astype(np.float64))
+    assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode E=8 T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_forward_decode_zero_input_ties(T):
+    """x = 0: every logit ties, so the top-k is experts 0..k-1 with weight
+    1/k each (lowest index first), and y = 0 exactly."""
+    require_gpu()
+    import bit_moe_amd as bm
+    w = synth.WORKLOADS["decode_b1"]
+    x = np.zeros((T, w.H), dtype=np.uint16)
+    y, gid, gw = bm.forward_decode(device_layer(w), x_to_device(x))
+    torch.cuda.synchronize()
+    assert gid.cpu().numpy().tolist() == [list(range(w.k))] * T
+    np.testing.assert_allclose(gw.cpu().numpy(), 1.0 / w.k, atol=1e-7)
+    assert not np.any(y.cpu().numpy())
