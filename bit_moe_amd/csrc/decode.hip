@@ -29,6 +29,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "device_util.h"
 
@@ -36,7 +37,7 @@ namespace {
 
 using namespace bm;
 
-constexpr int kW = 8;              // waves per workgroup
+constexpr int kW = 16;             // waves per front workgroup
 constexpr int kWG = 16;            // waves per routed gate/up workgroup
 constexpr int kWD = 4;             // waves per down workgroup: every down workgroup of a decode
                                    // batch is resident at once
@@ -922,10 +923,15 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const uint8_t *__re
 namespace bm_host {
 
 // compute units of the current device (one gate/up workgroup fits per CU)
+// (cached per device; 256 if the query fails)
 static int cu_count() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-        return 256;
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
@@ -934,7 +940,9 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     const bool shared = L->shared_gate != nullptr;
     p.slots = (int)std::min<int64_t>(L->E, (int64_t)T * L->k);
     p.n_rwg = with_router ? (L->E + kW - 1) / kW : 0;
-    p.kc_sg = shared ? 8 : 0;
+    // the shared gate/up's K chunks: as many as fit the compute units
+    // beside the router workgroups (one front workgroup per CU), at most 8
+    p.kc_sg = shared ? std::max(1, std::min(kMaxChunks, (cu_count() - p.n_rwg) / (L->I / 64))) : 0;
     p.kc_sd = shared ? std::max(1, (L->I + kSharedChunkCols - 1) / kSharedChunkCols) : 0;
     p.small = (int64_t)T * L->k <= kWaveBucketMax;
     // one token: every gate/up workgroup routes it itself; more tokens: one
