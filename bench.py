@@ -283,20 +283,35 @@ def summarize_traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes):
 
 def summarize_kernels(trace_dir):
     """Per-kernel launch count and average / min / max duration (us) from a
-    rocprofv3 --kernel-trace output directory, grouped by name and grid."""
+    rocprofv3 --kernel-trace output directory of a default bench run, grouped
+    by bench phase, name and grid.  Phases follow the run's order: layer set-up
+    (packing) until the first decode launch, decode_b1 until the batch-16 step's
+    first top-k, decode_b16 until the prefill step's first launch, then
+    prefill_2k."""
     import glob
     import sqlite3
     rows = {}
     for db in glob.glob(os.path.join(trace_dir, "**", "*.db"), recursive=True):
         c = sqlite3.connect(db)
-        for name, gx, n, avg, mn, mx in c.execute(
-                "select name, grid_x, count(*), avg(end - start), min(end - start), max(end - start) "
-                "from kernels group by name, grid_x"):
-            rows[(name, gx)] = (n, avg / 1e3, mn / 1e3, mx / 1e3)
-    out = [f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'grid':>10}  kernel"]
-    for (name, gx), (n, avg, mn, mx) in sorted(rows.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        phase = "setup"
+        for name, gx, t0, t1 in c.execute("select name, grid_x, start, end from kernels order by start"):
+            if phase == "setup" and "k_dec_front" in name:
+                phase = "decode_b1"
+            elif phase == "decode_b1" and ("k_topk" in name or "k_dec_mid" in name):
+                phase = "decode_b16"
+            elif phase == "decode_b16" and ("k_router_splitk" in name or "k_pf_" in name or "k_bucket" in name):
+                phase = "prefill_2k"
+            r = rows.setdefault((phase, name, gx), [0, 0.0, float("inf"), 0.0])
+            d = (t1 - t0) / 1e3
+            r[0] += 1
+            r[1] += d
+            r[2] = min(r[2], d)
+            r[3] = max(r[3], d)
+    out = [f"{'phase':<11} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'grid':>10}  kernel"]
+    order = {"setup": 0, "decode_b1": 1, "decode_b16": 2, "prefill_2k": 3}
+    for (phase, name, gx), (n, tot, mn, mx) in sorted(rows.items(), key=lambda kv: (order[kv[0][0]], -kv[1][1])):
         short = name[name.index("k_"):].split("(")[0] if "k_" in name else name.split("(")[0]
-        out.append(f"{n:6d} {avg:10.2f} {mn:10.2f} {mx:10.2f} {gx:10d}  {short}")
+        out.append(f"{phase:<11} {n:6d} {tot / n:10.2f} {mn:10.2f} {mx:10.2f} {gx:10d}  {short}")
     return "\n".join(out)
 
 
