@@ -99,6 +99,15 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
         d.hscale = c.take<float>(n * (L->I / 64));
         d.o = c.take<float>(n * L->H);
         d.ycount = c.take<int32_t>(L->H / 64);
+        if (p.pf_tiles) {
+            f.b.tiles = c.take<int32_t>(2 * p.pf_tiles);
+            f.b.n_tiles = c.take<int32_t>(1);
+            d.pf.x16 = c.take<uint16_t>((int64_t)T * L->H);
+            d.pf.xsc = c.take<float>(T);
+            d.pf.h = c.take<uint16_t>(n * L->I);
+            d.pf.hexp = c.take<int32_t>(n * (L->I / 256));
+            d.pf.o = d.o;
+        }
         if (shared) {
             d.sgp = c.take<float>((int64_t)p.kc_sg * 2 * T * L->I);
             d.hs = c.take<uint16_t>(2 * (int64_t)T * L->I);

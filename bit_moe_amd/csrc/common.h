@@ -339,9 +339,21 @@ struct DecodePlan {
     int n_rwg = 0;          // router workgroups in the front launch (0: ids given)
     int kc_sg = 0;          // K chunks of the shared gate/up
     int kc_sd = 0;          // K chunks of the shared down
-    bool small = false;     // T*k <= 128: routing / bucketing inside the gate/up workgroups
+    bool small = false;     // T*k <= 128: one-wave bucketing
     bool need_mid = true;   // top-k and/or bucketing in a launch of their own
+    int pf_tiles = 0;       // > 0: experts chosen by several tokens take the prefill
+                            // kernels, one row tile each (at most pf_tiles tiles)
 };
+// Prefill working buffers (all device memory, carved from the workspace).
+struct PrefillBufs {
+    uint16_t *x16;      // [T][H] fp16 activations, scaled per token by 1/xsc
+    float *xsc;         // [T] power-of-two token scales
+    uint16_t *h;        // [T*k][I] fp16 h rows in bucket order, scaled per 256 columns
+    int32_t *hexp;      // [T*k][I/256] exponents of those scales
+    float *o;           // [T*k][H] per-pair expert outputs
+    float *hs, *os;     // shared expert h [T][I] and output [T][H] (or null)
+};
+
 struct DecodeBufs {
     float *logits;          // [T][E] (router in the front launch)
     int32_t *ids;           // [T][k]
@@ -355,6 +367,8 @@ struct DecodeBufs {
     float *o;               // [T*k][H] routed down outputs, pair order
     float *osp;             // [kc_sd][T][H] shared down partial sums
     int32_t *ycount;        // [H/64] finished down workgroups per panel
+    PrefillBufs pf;         // batches: experts chosen by several tokens take the prefill kernels
+                            // (x16, xsc, h, hexp; their o is this o)
     float *y;               // [T][H]
 };
 DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router);
@@ -363,15 +377,9 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
 
 // prefill FFN
 int prefill_tile_rows();
-// Prefill working buffers (all device memory, carved from the workspace).
-struct PrefillBufs {
-    uint16_t *x16;      // [T][H] fp16 activations, scaled per token by 1/xsc
-    float *xsc;         // [T] power-of-two token scales
-    uint16_t *h;        // [T*k][I] fp16 h rows in bucket order, scaled per 256 columns
-    int32_t *hexp;      // [T*k][I/256] exponents of those scales
-    float *o;           // [T*k][H] per-pair expert outputs
-    float *hs, *os;     // shared expert h [T][I] and output [T][H] (or null)
-};
+// xprep + routed gate/up + routed down over b's row tiles; o written per pair
+int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int T, const Buckets &b,
+                          int max_tiles, const PrefillBufs &pb, hipStream_t s);
 int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T, const float *w, float *y,
                        const Buckets &b, int max_tiles, const PrefillBufs &pb, hipStream_t s);
 

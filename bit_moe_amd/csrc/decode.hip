@@ -261,7 +261,7 @@ __global__ void __launch_bounds__(kBT)
 k_dec_mid(int E, int k, int T, const float *__restrict__ logits, int32_t *__restrict__ ids,
           float *__restrict__ w, int do_bucket, int32_t *__restrict__ counts,
           int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ active,
-          int32_t *__restrict__ n_active) {
+          int32_t *__restrict__ n_active, int32_t *__restrict__ tiles, int32_t *__restrict__ n_tiles) {
     extern __shared__ int smem[];
     __shared__ int swave[kBW + 1];
     const int tid = threadIdx.x, wv = tid >> 6;
@@ -285,6 +285,7 @@ k_dec_mid(int E, int k, int T, const float *__restrict__ logits, int32_t *__rest
         if (wv == 0) bucket_wave_rank(ids, n, E, perm, smem);
         __syncthreads();
         if (wv == 0) bucket_wave_lists(n, smem, counts, offsets, active, n_active);
+        if (wv == 0 && tiles) bucket_wave_multi_tiles(n, smem, tiles, n_tiles);
         return;
     }
     bucket_block(ids, n, E, counts, offsets, perm, active, n_active, nullptr, nullptr, 1, smem, swave);
@@ -873,7 +874,7 @@ BM_DEV void count_and_combine(int H, int k, int T, int kc_sd, int P, int n_contr
 // experts chosen by several tokens (launched only when T > 1).
 template <int MULTI>
 __global__ void __launch_bounds__(kWD * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 6)))
-k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const uint8_t *__restrict__ down,
+k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, int multi_done, const uint8_t *__restrict__ down,
            const uint4 *__restrict__ sd, const int32_t *__restrict__ counts,
            const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
            const int32_t *__restrict__ active, const int32_t *__restrict__ n_active,
@@ -891,6 +892,11 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const uint8_t *__re
         tk.e = active[slot];
         tk.off = offsets[tk.e];
         tk.cnt = counts[tk.e];
+        if (!MULTI && tk.cnt > 1 && multi_done) {
+            // this expert's outputs came from an earlier launch: only count
+            count_and_combine(H, k, T, kc_sd, P, na + kc_sd, ycount, o, w, osp, y, &sdo);
+            return;
+        }
         if ((tk.cnt > 1) != (MULTI != 0)) return;
         if (!MULTI) {
             routed_down_pass<1>(H, I, tk, 0, P, down, perm, h, hsum2, hscale, o, red);
@@ -949,6 +955,10 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     // routing launch, so that the gate/up workgroups can each take several
     // (expert, panel) items
     p.need_mid = !p.small || T > 1;
+    // several tokens (one row tile per expert): experts chosen by more than
+    // one token go through the prefill kernels, which decode each weight once
+    // for all of its tokens on the matrix cores
+    p.pf_tiles = (p.small && T > 1 && T <= prefill_tile_rows()) ? (int)std::min<int64_t>(L->E, (int64_t)T * L->k / 2) : 0;
     return p;
 }
 
@@ -981,7 +991,8 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
             (void)hipFuncSetAttribute(reinterpret_cast<const void *>(k_dec_mid),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
         k_dec_mid<<<1, kBT, sh, s>>>(E, k, T, p.n_rwg ? b.logits : nullptr, b.ids, b.w, in_mid ? 1 : 0,
-                                     b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active, b.bk.n_active);
+                                     b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active, b.bk.n_active,
+                                     p.pf_tiles ? b.bk.tiles : nullptr, b.bk.n_tiles);
         BM_LAUNCH_CHECK();
         if (!in_mid) {
             int rc = launch_bucket(b.ids, T, k, E, b.bk, s);
@@ -1006,7 +1017,13 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
         return ok;
     }();
     if (!lds_set) return BITMOE_EHIP;
-    for (int multi = 0; multi < (T > 1 ? 2 : 1); multi++) {
+    // experts chosen by several tokens: the prefill kernels (their o rows
+    // are ready before the down launch's combine reads them)
+    if (p.pf_tiles) {
+        const int rc = launch_prefill_routed(L, x, x_dtype, T, b.bk, p.pf_tiles, b.pf, s);
+        if (rc) return rc;
+    }
+    for (int multi = 0; multi < (T > 1 && !p.pf_tiles ? 2 : 1); multi++) {
         auto kg = multi ? (bf ? k_dec_gateup<1, 1> : k_dec_gateup<0, 1>)
                         : (bf ? k_dec_gateup<1, 0> : k_dec_gateup<0, 0>);
         // the timing events, when set, are taken by the dispatch itself
@@ -1023,14 +1040,14 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     // down || shared down; the last workgroup to finish a panel combines it
     const int n_dwg = p.slots * (H / 64);
     const int n_sd = shared ? (H / 64) * p.kc_sd : 0;
-    k_dec_down<0><<<n_dwg + n_sd, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd,
+    k_dec_down<0><<<n_dwg + n_sd, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, p.pf_tiles ? 1 : 0,
                                                    (const uint8_t *)L->down_q, (const uint4 *)L->shared_down,
                                                    b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active,
                                                    b.bk.n_active, b.h, b.hsum2, b.hscale, b.hs, b.w, b.ycount,
                                                    shared ? b.osp : nullptr, b.o, b.y);
     BM_LAUNCH_CHECK();
-    if (T > 1) {
-        k_dec_down<1><<<n_dwg, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, (const uint8_t *)L->down_q,
+    if (T > 1 && !p.pf_tiles) {
+        k_dec_down<1><<<n_dwg, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, 0, (const uint8_t *)L->down_q,
                                                 (const uint4 *)L->shared_down, b.bk.counts, b.bk.offsets,
                                                 b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum2, b.hscale, b.hs,
                                                 b.w, b.ycount, shared ? b.osp : nullptr, b.o, b.y);

@@ -326,6 +326,34 @@ BM_DEV void bucket_wave_lists(int n, const int *sk, int32_t *__restrict__ counts
     if (lane == 0) *n_active = na;
 }
 
+// After bucket_wave_rank (sk[] = the n sorted keys): one row tile (e, 0) for
+// every expert holding more than one pair, in ascending expert order, and
+// their count.  One wavefront; every such expert must hold at most one
+// tile's rows.
+BM_DEV void bucket_wave_multi_tiles(int n, const int *sk, int32_t *__restrict__ tiles,
+                                    int32_t *__restrict__ n_tiles) {
+    const int lane = lane_id();
+    const uint64_t below = (1ull << lane) - 1ull;
+    bool lead[2], multi[2];
+    int key[2];
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        const int r = lane + 64 * m;
+        key[m] = r < n ? sk[r] : -1;
+        lead[m] = r < n && (r == 0 || sk[r - 1] != key[m]);
+        multi[m] = lead[m] && r + 1 < n && sk[r + 1] == key[m];
+    }
+    const uint64_t M0 = __ballot(multi[0]), M1 = __ballot(multi[1]);
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        if (!multi[m]) continue;
+        const int pos = m == 0 ? __popcll(M0 & below) : __popcll(M0) + __popcll(M1 & below);
+        tiles[2 * pos] = key[m];
+        tiles[2 * pos + 1] = 0;
+    }
+    if (lane == 0) *n_tiles = __popcll(M0) + __popcll(M1);
+}
+
 // Single-workgroup bucketing of n <= a few thousand pairs (kBT threads):
 // counts, offsets, stable perm, active list [, row tiles].  smem must hold
 // (2 + kBW) * E ints; swave kBW + 1 ints.

@@ -689,8 +689,8 @@ namespace bm_host {
 
 int prefill_tile_rows() { return kPfRows; }
 
-int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T, const float *w, float *y,
-                       const Buckets &b, int max_tiles, const PrefillBufs &pb, hipStream_t s) {
+int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int T, const Buckets &b,
+                          int max_tiles, const PrefillBufs &pb, hipStream_t s) {
     const int H = L->H, I = L->I, k = L->k;
     static const bool attr = [] {
         hipFuncAttributes fa;           // the gate/up tables must start at LDS address 0
@@ -720,6 +720,14 @@ int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T,
         k_pf_down<<<pf_grid(max_tiles, (H + kPfDnCols - 1) / kPfDnCols), kPfThreads, kPfDnLds, s>>>(a);
         BM_LAUNCH_CHECK();
     }
+    return BITMOE_OK;
+}
+
+int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T, const float *w, float *y,
+                       const Buckets &b, int max_tiles, const PrefillBufs &pb, hipStream_t s) {
+    const int H = L->H, I = L->I, k = L->k;
+    const int rc = launch_prefill_routed(L, x, x_dtype, T, b, max_tiles, pb, s);
+    if (rc) return rc;
     const bool shared = L->shared_gate != nullptr;
     if (shared) {
         dim3 gs1(I / 64, T), gs2(H / 64, T);

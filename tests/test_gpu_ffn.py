@@ -123,9 +123,12 @@ def test_decode_and_prefill_agree_and_batch_rows_match_single_tokens():
     yd = _gpu_ffn(w, x, ids, wt, "decode")
     yp = _gpu_ffn(w, x, ids, wt, "prefill")
     assert_close_rms(yp, yd.astype(np.float64), what="prefill vs decode")
+    # a token alone runs every expert on the single-token kernels; in the
+    # batch, experts chosen by several tokens take the matrix-core kernels,
+    # so rows agree to the FFN tolerance, not bit for bit
     for t in (0, 7, 15):
         y1 = _gpu_ffn(w, x[t:t + 1], ids[t:t + 1], wt[t:t + 1], "decode")
-        np.testing.assert_array_equal(y1[0], yd[t])
+        assert_close_rms(yd[t:t + 1], y1.astype(np.float64), what=f"batch row {t} vs alone")
 
 
 def test_deterministic_repeat():
