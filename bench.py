@@ -286,7 +286,8 @@ def summarize_kernels(trace_dir):
     rocprofv3 --kernel-trace output directory of a default bench run, grouped
     by bench phase, name and grid.  Phases follow the run's order: layer set-up
     (packing) until the first decode launch, decode_b1 until the batch-16 step's
-    first top-k, decode_b16 until the prefill step's first launch, then
+    first top-k, decode_b16 until the prefill step's router GEMM (the decode
+    batch also runs prefill kernels, for its multi-token experts), then
     prefill_2k."""
     import glob
     import sqlite3
@@ -299,7 +300,7 @@ def summarize_kernels(trace_dir):
                 phase = "decode_b1"
             elif phase == "decode_b1" and ("k_topk" in name or "k_dec_mid" in name):
                 phase = "decode_b16"
-            elif phase == "decode_b16" and ("k_router_splitk" in name or "k_pf_" in name or "k_bucket" in name):
+            elif phase == "decode_b16" and "k_router_splitk" in name:
                 phase = "prefill_2k"
             r = rows.setdefault((phase, name, gx), [0, 0.0, float("inf"), 0.0])
             d = (t1 - t0) / 1e3

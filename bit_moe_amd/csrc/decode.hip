@@ -45,6 +45,9 @@ constexpr int kNT = 4;             // tokens per pass over the weights
 constexpr int kMaxChunks = 8;      // K chunks of the shared expert, at most
 constexpr int kMaxExperts = 1024;
 constexpr int kSharedChunkCols = 512;   // I columns of one shared-down K chunk, at most
+// per token, the LDS staging of a routed down wave's two superblocks of h:
+// 64 pieces of 8 fp16, 16 pieces of two {hs, hb}, two pieces of 4 scales
+constexpr int kHst = 64 + 16 + 2;
 // 16-byte pieces per load batch of a gate/up wave (fewer when several
 // tokens share the pass, to bound register use)
 template <int NT>
@@ -691,7 +694,8 @@ template <int NT>
 BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
                              const uint8_t *__restrict__ down, const int32_t *__restrict__ perm,
                              const uint16_t *__restrict__ h, const float2 *__restrict__ hsum2,
-                             const float *__restrict__ hscale, float *__restrict__ o, float *red) {
+                             const float *__restrict__ hscale, float *__restrict__ o, float *red,
+                             uint4 *hst) {
     const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int rows[NT];
 #pragma unroll
@@ -719,14 +723,38 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
         v.sc = ds[pk * 64 + lane];
         v.dm = dd[pk * 64 + lane];
     };
-    auto decode = [&](int kb, const Sb &v, bool keep) {
+    // The h the two superblocks need (per token: 512 fp16, their 32 sums
+    // {hs, hb}, their 8 scales) is staged in this wave's slice of LDS by
+    // three vector loads per token, issued before the weights: as scalar
+    // loads, the first touch of each line came back one round trip at a time.
+    auto stage = [&](int kb, int kb2) {
+        uint4 hv[NT], sv[NT], cv[NT];
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            const int sb = lane < 32 ? kb : kb2;
+            hv[t] = *reinterpret_cast<const uint4 *>(h + (int64_t)rows[t] * I + sb * kQK + 8 * (lane & 31));
+            const int sb2 = (lane & 15) < 8 ? kb : kb2;
+            sv[t] = *reinterpret_cast<const uint4 *>(hsum2 + (int64_t)rows[t] * (I / 16) + sb2 * 16 + 2 * (lane & 7));
+            const int sb3 = (lane & 1) ? kb2 : kb;
+            cv[t] = *reinterpret_cast<const uint4 *>(hscale + (int64_t)rows[t] * (I / 64) + sb3 * 4);
+        }
+        return [=](void) {
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                hst[t * kHst + lane] = hv[t];
+                if (lane < 16) hst[t * kHst + 64 + lane] = sv[t];
+                if (lane < 2) hst[t * kHst + 80 + lane] = cv[t];
+            }
+        };
+    };
+    // superblock s (0, 1) of the staged pair
+    auto decode = [&](int s, const Sb &v, bool keep) {
         const float d = fp16_to_f32(v.dm & 0xFFFFu), dmin = fp16_to_f32(v.dm >> 16);
 #pragma unroll
         for (int c = 0; c < 4; c++) {                 // 64 columns: sub-blocks 4c..4c+3
             const uint32_t qw[4] = {v.q[c].x, v.q[c].y, v.q[c].z, v.q[c].w};
             const uint32_t scw = c == 0 ? v.sc.x : c == 1 ? v.sc.y : c == 2 ? v.sc.z : v.sc.w;
             const uint32_t scl = scw & 0x0F0F0F0Fu, mnb = (scw >> 4) & 0x0F0F0F0Fu;
-            const int col = kb * kQK + 64 * c;
             float a1[NT], a2[NT];
 #pragma unroll
             for (int t = 0; t < NT; t++) a1[t] = a2[t] = 0.f;
@@ -739,7 +767,7 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
                 const float scf = (float)((scl >> (8 * i)) & 0xFFu), mf = (float)((mnb >> (8 * i)) & 0xFFu);
 #pragma unroll
                 for (int t = 0; t < NT; t++) {
-                    const uint4 *hp = reinterpret_cast<const uint4 *>(h + (int64_t)rows[t] * I + col + 16 * i);
+                    const uint4 *hp = hst + t * kHst + s * 32 + 8 * c + 2 * i;
                     const uint4 x0 = hp[0], x1 = hp[1];
                     float sacc = dot2_f16(pr[0], x0.x, 0.f);
                     sacc = dot2_f16(pr[1], x0.y, sacc);
@@ -749,14 +777,14 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
                     sacc = dot2_f16(pr[5], x1.y, sacc);
                     sacc = dot2_f16(pr[6], x1.z, sacc);
                     sacc = dot2_f16(pr[7], x1.w, sacc);
-                    const float2 sb = hsum2[(int64_t)rows[t] * (I / 16) + (col >> 4) + i];   // {hs, hb}
+                    const float2 sb = reinterpret_cast<const float2 *>(hst + t * kHst + 64)[s * 16 + 4 * c + i];   // {hs, hb}
                     a1[t] = fmaf(scf, sacc - sb.y, a1[t]);
                     a2[t] = fmaf(mf, sb.x, a2[t]);
                 }
             }
 #pragma unroll
             for (int t = 0; t < NT; t++) {
-                const float hsc = hscale[(int64_t)rows[t] * (I / 64) + (col >> 6)];
+                const float hsc = reinterpret_cast<const float *>(hst + t * kHst + 80)[s * 4 + c];
                 const float v2 = fmaf(hsc, fmaf(d, a1[t], -dmin * a2[t]), acc[t]);
                 acc[t] = keep ? v2 : acc[t];
             }
@@ -764,12 +792,14 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
     };
     for (int kb = kb0; kb < kb1; kb += 2) {
         const int kb2 = kb + 1 < kb1 ? kb + 1 : kb;
+        auto put = stage(kb, kb2);
         Sb va, vb;
         load(kb, va);
         load(kb2, vb);
         __builtin_amdgcn_sched_barrier(0);
-        decode(kb, va, true);
-        decode(kb2, vb, kb + 1 < kb1);
+        put();
+        decode(0, va, true);
+        decode(1, vb, kb + 1 < kb1);
     }
 #pragma unroll
     for (int t = 0; t < NT; t++) red[(wv * NT + t) * 64 + lane] = acc[t];
@@ -788,7 +818,7 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
 template <int NT>
 BM_DEV void shared_down_pass(int H, int I, int T, int t0, int P, int c0, int c1,
                              const uint4 *__restrict__ sd, const uint16_t *__restrict__ hs,
-                             float *__restrict__ osp, float *red) {
+                             float *__restrict__ osp, float *red, uint4 *hst) {
     const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int K8 = I / 8;
     const int64_t lo_off = (int64_t)T * I;
@@ -801,20 +831,31 @@ BM_DEV void shared_down_pass(int H, int I, int T, int t0, int P, int c0, int c1,
     // piece again, used and dropped, so that the loads stay together)
     constexpr int B = 8;
     const uint4 *base = sd + (int64_t)P * K8 * 64 + lane;
+    static_assert(NT * 2 * B <= kHst, "staging slice");
     for (int cb = c0 + w0; cb < c0 + w1; cb += B) {
+        // the batch's h (hi pieces in lanes 0-7, lo pieces in lanes 8-15, per
+        // token) is staged in this wave's LDS slice by one vector load per
+        // token, issued before the weights
+        uint4 hv[NT];
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            const int c = min(cb + (lane & 7), c0 + w1 - 1);
+            hv[t] = *reinterpret_cast<const uint4 *>(hs + ((lane & 8) ? lo_off : 0) +
+                                                     (int64_t)min(t0 + t, T - 1) * I + 8 * c);
+        }
         uint4 cur[B];
 #pragma unroll
         for (int i = 0; i < B; i++) cur[i] = base[(int64_t)min(cb + i, c0 + w1 - 1) * 64];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
+        for (int t = 0; t < NT; t++)
+            if (lane < 2 * B) hst[t * 2 * B + lane] = hv[t];
+#pragma unroll
         for (int i = 0; i < B; i++) {
-            const int c = min(cb + i, c0 + w1 - 1);
             const bool keep = cb + i < c0 + w1;
 #pragma unroll
             for (int t = 0; t < NT; t++) {
-                const uint16_t *hp = hs + (int64_t)min(t0 + t, T - 1) * I + 8 * c;
-                const float v = dot8_hilo(cur[i], *reinterpret_cast<const uint4 *>(hp),
-                                          *reinterpret_cast<const uint4 *>(hp + lo_off), acc[t]);
+                const float v = dot8_hilo(cur[i], hst[t * 2 * B + i], hst[t * 2 * B + B + i], acc[t]);
                 acc[t] = keep ? v : acc[t];
             }
         }
@@ -873,7 +914,7 @@ BM_DEV void count_and_combine(int H, int k, int T, int kc_sd, int P, int n_contr
 // MULTI = 0: experts chosen by one token, and the shared down; MULTI = 1:
 // experts chosen by several tokens (launched only when T > 1).
 template <int MULTI>
-__global__ void __launch_bounds__(kWD * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 6)))
+__global__ void __launch_bounds__(kWD * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 5)))
 k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, int multi_done, const uint8_t *__restrict__ down,
            const uint4 *__restrict__ sd, const int32_t *__restrict__ counts,
            const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
@@ -882,7 +923,9 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, int multi_done, con
            const uint16_t *__restrict__ hs, const float *__restrict__ w, int32_t *__restrict__ ycount,
            float *__restrict__ osp, float *__restrict__ o, float *__restrict__ y) {
     __shared__ float red[kWD * kNT * 64];
+    __shared__ uint4 hstage[kWD][MULTI ? kNT : 1][kHst];
     __shared__ int sdo;
+    uint4 *hst = &hstage[threadIdx.x >> 6][0][0];
     const int panels = H / 64;
     const int na = *n_active;
     if ((int)blockIdx.x < n_dwg) {
@@ -899,13 +942,13 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, int multi_done, con
         }
         if ((tk.cnt > 1) != (MULTI != 0)) return;
         if (!MULTI) {
-            routed_down_pass<1>(H, I, tk, 0, P, down, perm, h, hsum2, hscale, o, red);
+            routed_down_pass<1>(H, I, tk, 0, P, down, perm, h, hsum2, hscale, o, red, hst);
         } else {
             for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
                 if (tk.cnt - t0 == 1)
-                    routed_down_pass<1>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red);
+                    routed_down_pass<1>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
                 else
-                    routed_down_pass<kNT>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red);
+                    routed_down_pass<kNT>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
             }
         }
         count_and_combine(H, k, T, kc_sd, P, na + kc_sd, ycount, o, w, osp, y, &sdo);
@@ -916,9 +959,9 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, int multi_done, con
         float *op = osp + (int64_t)c * T * H;
         for (int t0 = 0; t0 < T; t0 += kNT) {
             if (T - t0 == 1)
-                shared_down_pass<1>(H, I, T, t0, P, c0, c1, sd, hs, op, red);
+                shared_down_pass<1>(H, I, T, t0, P, c0, c1, sd, hs, op, red, hst);
             else
-                shared_down_pass<kNT>(H, I, T, t0, P, c0, c1, sd, hs, op, red);
+                shared_down_pass<kNT>(H, I, T, t0, P, c0, c1, sd, hs, op, red, hst);
         }
         count_and_combine(H, k, T, kc_sd, P, na + kc_sd, ycount, o, w, osp, y, &sdo);
     }
