@@ -425,7 +425,7 @@ BM_DEV void routed_gateup_1(int H, int I, int k, const Tok &tk, int P, const uin
                             float *red) {
     constexpr int kRing = 4;
     const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tok[1] = {__builtin_amdgcn_readfirstlane(perm[tk.off] / k)};
+    const int tok[1] = {perm ? __builtin_amdgcn_readfirstlane(perm[tk.off] / k) : 0};
     const int nb = H / kQK;
     const int64_t slab = (int64_t)I * nb * 66;
     const uint8_t *G = gate + tk.e * slab, *U = up + tk.e * slab;
@@ -494,14 +494,11 @@ BM_DEV float dot8_hilo(uint4 wq, uint4 hh, uint4 hl, float acc) {
     return acc;
 }
 
-// Routing of a small batch (T*k <= 128) inside a workgroup: top-k of the
-// router logits (mode 1) or the given ids (mode 2), then the one-wave
-// bucketing, all in LDS; workgroup 0 also writes the results out for the
-// launches that follow.  Counts and offsets are kept for the active experts
-// only.
+// One token's routing inside a gate/up workgroup (LDS): the experts by slot
+// (slot = rank of the expert index), the picks of the general top-k.
+constexpr int kMaxK = 16;
 struct SmallRoute {
-    int counts[kMaxExperts], offsets[kMaxExperts];
-    int perm[kWaveBucketMax], active[kWaveBucketMax], ids[kWaveBucketMax], sk[kWaveBucketMax];
+    int active[kMaxK], ids[kMaxK];
     int n_active;
 };
 
@@ -513,39 +510,43 @@ BM_DEV void route_logits_load(const float *__restrict__ logits, int E, int t, fl
     for (int i = 0; i < 4; i++) lv[i] = logits[(int64_t)t * E + min(lane + 64 * i, E - 1)];
 }
 
-BM_DEV void route_in_wg(int mode, int E, int k, int T, const float *__restrict__ logits, int32_t *ids,
-                        float *w, const bm_host::Buckets &bk, SmallRoute &r, float (&lv)[4], bool lv_loaded) {
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), n = T * k, nw = blockDim.x >> 6;
-    const bool out = blockIdx.x == 0;
-    if (mode == 1) {
-        for (int t = wv; t < T; t += nw) {
-            int32_t *oi = out ? ids + (int64_t)t * k : nullptr;
-            float *ow = out ? w + (int64_t)t * k : nullptr;
+// One token (k distinct experts, as a top-k gives): wave 0 takes the top-k
+// of the logits (mode 1) or loads the given ids (mode 2), and ranks the k
+// experts by index with k lane reads; slot = rank, each expert one pair, in
+// LDS (r.active) and, by the workgroup that writes out, in bk.
+BM_DEV void route_one_token(int mode, int E, int k, const float *__restrict__ logits, int32_t *ids, float *w,
+                            const bm_host::Buckets &bk, SmallRoute &r, float (&lv)[4], bool lv_loaded, bool out) {
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
+    if (wv == 0) {
+        int id;
+        if (mode == 1) {
             if (E <= 256) {
-                if (!(lv_loaded && t == wv)) route_logits_load(logits, E, t, lv);
-                topk_wave4(lv, E, k, oi, ow, r.ids + t * k);
+                if (!lv_loaded) route_logits_load(logits, E, 0, lv);
+                id = topk_wave4(lv, E, k, out ? ids : nullptr, out ? w : nullptr, nullptr);
             } else {
-                topk_wave(logits + (int64_t)t * E, E, k, oi, ow, r.ids + t * k);
+                topk_wave(logits, E, k, out ? ids : nullptr, out ? w : nullptr, r.ids);
+                id = lane < k ? r.ids[lane] : 0;
+            }
+        } else {
+            id = lane < k ? ids[lane] : 0;
+        }
+        int rank = 0;
+        for (int i = 0; i < k; i++) rank += __builtin_amdgcn_readlane(id, i) < id ? 1 : 0;
+        if (lane < k) {
+            r.active[rank] = id;
+            if (out) {
+                bk.perm[rank] = lane;
+                bk.active[rank] = id;
+                bk.counts[id] = 1;
+                bk.offsets[id] = rank;
             }
         }
-    } else {
-        for (int p = threadIdx.x; p < n; p += blockDim.x) r.ids[p] = ids[p];
-    }
-    __syncthreads();
-    if (wv == 0) bucket_wave_rank(r.ids, n, E, r.perm, r.sk);
-    __syncthreads();
-    if (wv == 0) bucket_wave_lists(n, r.sk, r.counts, r.offsets, r.active, &r.n_active);
-    __syncthreads();
-    if (out) {
-        for (int p = threadIdx.x; p < n; p += blockDim.x) bk.perm[p] = r.perm[p];
-        for (int a = threadIdx.x; a < r.n_active; a += blockDim.x) {
-            const int e = r.active[a];
-            bk.active[a] = e;
-            bk.counts[e] = r.counts[e];
-            bk.offsets[e] = r.offsets[e];
+        if (lane == 0) {
+            r.n_active = k;
+            if (out) *bk.n_active = k;
         }
-        if (threadIdx.x == 0) *bk.n_active = r.n_active;
     }
+    __syncthreads();
 }
 
 // Shared-expert h of elements [f0, f1) by this workgroup: h = silu(sum of
@@ -577,7 +578,8 @@ BM_DEV void shared_h_load(int64_t n, int kc_sg, const float *__restrict__ sgp, i
 // MULTI = 0 takes the experts chosen by exactly one token, MULTI = 1 the
 // experts with several tokens (passes of kNT tokens); keeping the two apart
 // keeps each kernel's register use low.  route_mode: 0 the bucketing is in
-// bk already, 1/2 route_in_wg (MULTI = 0 only).  The run lookup tables
+// bk already; one token (MULTI = 0 only): route_one_token from the logits
+// (1) or the given ids (2).  The run lookup tables
 // (dynamic LDS, dec_lut_bytes) are built from the codebook while the batch
 // is routed.
 template <int MULTI>
@@ -610,48 +612,43 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
     const int64_t nfin = (!MULTI && kc_sg) ? (int64_t)T * I : 0;
     const int64_t fchunk = (nfin + gridDim.x - 1) / gridDim.x, f0 = b * fchunk, f1 = min(nfin, f0 + fchunk);
     float fg[kMaxChunks], fu[kMaxChunks];
-    int na;
     if (!MULTI && route_mode) {
-        // routing in every workgroup.  Loads that do not depend on each
-        // other go out first: the codebook rows, the logits, the first
-        // shared-h partials; the tables are written while they arrive.
+        // one token, routed in every workgroup, one (slot, panel) item each.
+        // Loads that do not depend on each other go out first: the codebook
+        // rows, the logits, this workgroup's shared-h partials (on wave 1:
+        // wave 0 routes); the tables are written while they arrive.
         uint2 grow = make_uint2(0u, 0u);
         if (tid < 256) grow = *reinterpret_cast<const uint2 *>(grid + 8 * tid);
         float lv[4];
-        const bool pre = route_mode == 1 && E <= 256 && wv < T;
-        if (pre) route_logits_load(logits, E, wv, lv);
-        if (f0 + tid < f1) shared_h_load(nfin, kc_sg, sgp, f0 + tid, fg, fu);
+        const bool pre = route_mode == 1 && E <= 256 && wv == 0;
+        if (pre) route_logits_load(logits, E, 0, lv);
+        const int64_t fi = f0 + tid - 64;
+        if (tid >= 64 && fi < f1) shared_h_load(nfin, kc_sg, sgp, fi, fg, fu);
         if (tid < 256) lut_write_line(lut, 0, tid, lut_mag_from_row<1>(grow));
         else if (tid < 256 + SGN / 256) lut_write_line(lut, kLutMagBytes, tid - 256, lut_sign_entry(tid - 256));
-        route_in_wg(route_mode, E, k, T, logits, ids, w, bk, sr, lv, pre);     // ends with a barrier
-        counts = sr.counts;
-        offsets = sr.offsets;
-        perm = sr.perm;
-        active = sr.active;
-        na = sr.n_active;
-    } else {
-        if constexpr (!MULTI)
-            if (f0 + tid < f1) shared_h_load(nfin, kc_sg, sgp, f0 + tid, fg, fu);
-        na = *bk.n_active;
+        if (tid >= 64 && fi < f1) shared_h_store(nfin, kc_sg, sgp, hs, fi, fg, fu);
+        for (int64_t i = fi + blockDim.x - 64; tid >= 64 && i < f1; i += blockDim.x - 64) {
+            shared_h_load(nfin, kc_sg, sgp, i, fg, fu);
+            shared_h_store(nfin, kc_sg, sgp, hs, i, fg, fu);
+        }
+        route_one_token(route_mode, E, k, logits, ids, w, bk, sr, lv, pre, b == 0);   // ends with a barrier
+        // slot = rank: one pair each, pair row = slot, token 0
+        if (slot >= k) return;
+        Tok tk;
+        tk.e = sr.active[slot];
+        tk.off = slot;
+        tk.cnt = 1;
+        routed_gateup_1<XBF16, SGN>(H, I, k, tk, P, gate, up, x, nullptr, h, hsum2, hscale, red);
+        return;
     }
+    int na = 0;
     if constexpr (!MULTI) {
-        if (f0 + tid < f1) shared_h_store(nfin, kc_sg, sgp, hs, f0 + tid, fg, fu);
-        for (int64_t i = f0 + tid + blockDim.x; i < f1; i += blockDim.x) {
+        for (int64_t i = f0 + tid; i < f1; i += blockDim.x) {
             shared_h_load(nfin, kc_sg, sgp, i, fg, fu);
             shared_h_store(nfin, kc_sg, sgp, hs, i, fg, fu);
         }
     }
-    if (!MULTI && route_mode) {
-        // one (slot, panel) item per workgroup, the tables already built
-        if (slot >= na) return;
-        Tok tk;
-        tk.e = active[slot];
-        tk.off = offsets[tk.e];
-        tk.cnt = counts[tk.e];
-        if (tk.cnt != 1) return;
-        routed_gateup_1<XBF16, SGN>(H, I, k, tk, P, gate, up, x, perm, h, hsum2, hscale, red);
-        return;
-    }
+    na = *bk.n_active;
     // routing done by an earlier launch: the workgroups loop over the
     // (slot, panel) items, the tables built once by each
     bool built = false;

@@ -98,9 +98,10 @@ BM_DEV int wave_min_i32(int v) {
 // its four; every round takes the wave max of the lane heads, the lowest
 // expert index among heads equal to it wins and its lane drops its head.
 // Lane j < k keeps the j-th pick, so the softmax over the k picks is one
-// row sum.  Lanes j < k write ids[j], w[j] and sids[j] (any may be null).
-BM_DEV void topk_wave4(float (&v)[4], int E, int k, int32_t *__restrict__ ids, float *__restrict__ wout,
-                       int *sids) {
+// row sum.  Lanes j < k write ids[j], w[j] and sids[j] (any may be null)
+// and return their pick.
+BM_DEV int topk_wave4(float (&v)[4], int E, int k, int32_t *__restrict__ ids, float *__restrict__ wout,
+                      int *sids) {
     const int lane = lane_id();
     constexpr int kNone = 0x7FFFFFFF;
     int ix[4];
@@ -145,6 +146,7 @@ BM_DEV void topk_wave4(float (&v)[4], int E, int k, int32_t *__restrict__ ids, f
         if (wout) wout[lane] = ex * (1.0f / z);
         if (sids) sids[lane] = pi;
     }
+    return pi;
 }
 
 constexpr int kBT = 1024;           // threads per bucketing block = pairs per chunk
