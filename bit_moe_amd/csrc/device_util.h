@@ -91,54 +91,79 @@ BM_DEV int wave_min_i32(int v) {
     return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Key of (logit, expert) for the top-k below, a double in [1, 2) whose
+// mantissa is the logit's order-preserving 32-bit pattern (-0 as +0, NaN as
+// -inf, experts past E below everything) followed by 255 - expert: the
+// largest key is the largest logit, the lowest expert among equal logits.
+BM_DEV double topk_key(float v, int e, int E) {
+    uint32_t u = 0u;
+    if (e < E) {
+        const uint32_t b = v == v ? __float_as_uint(v + 0.0f) : 0xFF800000u;
+        u = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    }
+    const uint64_t m = ((uint64_t)u << 20) | ((uint64_t)(255 - (e & 255)) << 12);
+    return __longlong_as_double((long long)(0x3FF0000000000000ull | m));
+}
+BM_DEV void topk_key_decode(double key, float &v, int &e) {
+    const uint64_t m = (uint64_t)__double_as_longlong(key);
+    e = 255 - (int)((m >> 12) & 0xFFu);
+    const uint32_t u = (uint32_t)(m >> 20);
+    v = __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+template <int CTRL, int ROWS>
+BM_DEV double dpp_max_f64(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp((int)b, (int)b, CTRL, ROWS, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(b >> 32), (int)(b >> 32), CTRL, ROWS, 0xF, false);
+    return fmax(v, __longlong_as_double((long long)(uint32_t)lo | ((long long)hi << 32)));
+}
+BM_DEV double wave_max_f64(double v) {
+    v = dpp_max_f64<0x111, 0xF>(v);
+    v = dpp_max_f64<0x112, 0xF>(v);
+    v = dpp_max_f64<0x114, 0xF>(v);
+    v = dpp_max_f64<0x118, 0xF>(v);
+    v = dpp_max_f64<0x142, 0xA>(v);
+    v = dpp_max_f64<0x143, 0xC>(v);
+    const long long b = __double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)b, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(b >> 32), 63);
+    return __longlong_as_double((long long)lo | ((long long)hi << 32));
+}
+
 // Top-k of one token's logits for E <= 256, by one wavefront, from values
 // the caller loaded beforehand: lane l holds the logits of experts l, l+64,
 // l+128, l+192 in v[] (anything beyond E is ignored).  Order: logit
-// descending, expert index ascending; NaN counts as -inf.  Each lane sorts
-// its four; every round takes the wave max of the lane heads, the lowest
-// expert index among heads equal to it wins and its lane drops its head.
-// Lane j < k keeps the j-th pick, so the softmax over the k picks is one
-// row sum.  Lanes j < k write ids[j], w[j] and sids[j] (any may be null)
+// descending, expert index ascending; NaN counts as -inf.  Each (logit,
+// expert) becomes one unique key (topk_key); each lane sorts its four keys,
+// and every round takes the wave max of the lane heads, whose lane drops its
+// head.  Lane j < k keeps the j-th pick, so the softmax over the k picks is
+// one row sum.  Lanes j < k write ids[j], w[j] and sids[j] (any may be null)
 // and return their pick.
 BM_DEV int topk_wave4(float (&v)[4], int E, int k, int32_t *__restrict__ ids, float *__restrict__ wout,
                       int *sids) {
     const int lane = lane_id();
-    constexpr int kNone = 0x7FFFFFFF;
-    int ix[4];
+    double key[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int e = lane + 64 * i;
-        ix[i] = e < E ? e : kNone;
-        if (e >= E || !(v[i] == v[i])) v[i] = -__builtin_inff();
-    }
-    auto cx = [&](int a, int b) {          // order slots a < b
-        const bool sw = v[b] > v[a] || (v[b] == v[a] && ix[b] < ix[a]);
-        const float tv = sw ? v[b] : v[a], tb = sw ? v[a] : v[b];
-        const int ti = sw ? ix[b] : ix[a], tj = sw ? ix[a] : ix[b];
-        v[a] = tv; v[b] = tb; ix[a] = ti; ix[b] = tj;
+    for (int i = 0; i < 4; i++) key[i] = topk_key(v[i], lane + 64 * i, E);
+    auto cx = [&](int a, int b) {          // order slots a > b
+        const double hi = fmax(key[a], key[b]), lo = fmin(key[a], key[b]);
+        key[a] = hi;
+        key[b] = lo;
     };
     cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
-    float pv = 0.f, m0 = 0.f;
-    int pi = 0;
+    double pk = 1.0, k0 = 1.0;
     for (int j = 0; j < k; j++) {
-        const float m = wave_max_f32(v[0]);
-        const bool at = v[0] == m;
-        int win;
-        const uint64_t b = __ballot(at);
-        if (__popcll(b) == 1) {
-            win = (int)__builtin_ctzll(b);
-        } else {                            // equal heads: lowest expert index
-            const int mn = wave_min_i32(at ? ix[0] : kNone);
-            win = (int)__builtin_ctzll(__ballot(at && ix[0] == mn));
-        }
-        const int id = __builtin_amdgcn_readlane(ix[0], win);
-        if (j == 0) m0 = m;
-        if (lane == j) { pv = m; pi = id; }
-        if (lane == win) {
-            v[0] = v[1]; v[1] = v[2]; v[2] = v[3]; v[3] = -__builtin_inff();
-            ix[0] = ix[1]; ix[1] = ix[2]; ix[2] = ix[3]; ix[3] = kNone;
+        const double m = wave_max_f64(key[0]);
+        if (j == 0) k0 = m;
+        if (lane == j) pk = m;
+        if (key[0] == m) {
+            key[0] = key[1]; key[1] = key[2]; key[2] = key[3]; key[3] = 0.0;
         }
     }
+    float pv, m0;
+    int pi, e0;
+    topk_key_decode(pk, pv, pi);
+    topk_key_decode(k0, m0, e0);
     const float ex = lane < k ? __expf(pv - m0) : 0.f;
     const float z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row16_sum(ex)), 15));
     if (lane < k) {
