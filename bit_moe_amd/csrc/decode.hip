@@ -215,6 +215,96 @@ BM_DEV void shared_gateup_pass(int H, int I, int T, int t0, int P, int c0, int c
     __syncthreads();
 }
 
+// Shared-expert gate/up partial sums of panel P over K pieces [c0, c1) for
+// the tokens t0 .. t0+15 on the matrix cores (bf16 activations; a dense
+// contraction once there are several tokens), so that the bf16 weights
+// stream once for 16 tokens.  v_mfma_f32_16x16x32_bf16 takes the weights as
+// they are stored as operand B: lane l's 8 values (panel row l) are column
+// l % 16 of K block l / 16 of the instruction's 32.  Operand A carries the
+// activations of 4 tokens per instruction, block-diagonally: A row m = 4 j +
+// t (token t of the four) is nonzero only on K block j, so D row m, column n
+// is token t against panel row 16 j + n, and lane l's four results are panel
+// row l for the four tokens.  Lanes off the diagonal read a zero row.  The chunk's
+// activations are staged in LDS (xs), rows padded by 16 bytes so that the
+// four token rows fall on different banks; the 16 waves' sums meet in red,
+// one group of four tokens at a time.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kSgMfmaPieces = 160;          // K pieces of a chunk the LDS staging holds
+constexpr int kSgXsBytes = 16 * (kSgMfmaPieces * 16 + 16) + 16;
+BM_DEV void shared_gateup_mfma(int H, int I, int T, int t0, int P, int c0, int c1,
+                               const uint4 *__restrict__ sg, const uint4 *__restrict__ su,
+                               const uint16_t *__restrict__ x, float *__restrict__ gp, float *__restrict__ up_,
+                               float *red, uint8_t *xs) {
+    const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int K8 = H / 8, nc = c1 - c0, nt = min(16, T - t0);
+    const int stride = nc * 16 + 16, zero = 16 * stride;
+    __syncthreads();                     // the previous group's readers of xs and red are done
+    for (int i = threadIdx.x; i < 16 * nc; i += blockDim.x) {
+        const int tt = i / nc, cl = i - tt * nc;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (tt < nt) v = *reinterpret_cast<const uint4 *>(x + (int64_t)(t0 + tt) * H + 8 * (c0 + cl));
+        *reinterpret_cast<uint4 *>(xs + tt * stride + cl * 16) = v;
+    }
+    if (threadIdx.x == 0) *reinterpret_cast<uint4 *>(xs + zero) = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    const int j = lane >> 4, m = lane & 15;
+    const bool act = (m >> 2) == j;
+    f32x4_t ag[4], au[4];
+#pragma unroll
+    for (int g = 0; g < 4; g++) ag[g] = au[g] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    int w0, w1;
+    split_range(nc, kW, wv, w0, w1);
+    constexpr int kB = 4;
+    const uint4 *gbase = sg + (int64_t)P * K8 * 64 + lane, *ubase = su + (int64_t)P * K8 * 64 + lane;
+    for (int cb = w0; cb < w1; cb += kB) {
+        uint4 gw[kB], uw[kB];
+#pragma unroll
+        for (int i = 0; i < kB; i++) {
+            const int pc = c0 + min(cb + i, w1 - 1);
+            gw[i] = gbase[(int64_t)pc * 64];
+            uw[i] = ubase[(int64_t)pc * 64];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kB; i++) {
+            // past the wave's share: the zero row (the piece is its last one again)
+            const int cl = min(cb + i, w1 - 1);
+            const bool use = act && cb + i < w1;
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int addr = use ? (4 * g + (m & 3)) * stride + cl * 16 : zero;
+                const uint4 a = *reinterpret_cast<const uint4 *>(xs + addr);
+                ag[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                __builtin_bit_cast(bf16x8_t, gw[i]), ag[g], 0, 0, 0);
+                au[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                                __builtin_bit_cast(bf16x8_t, uw[i]), au[g], 0, 0, 0);
+            }
+        }
+    }
+    // lane l, result i of group g: panel row l, token 4 g + i
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            red[((wv * 4 + i) * 2 + 0) * 64 + lane] = ag[g][i];
+            red[((wv * 4 + i) * 2 + 1) * 64 + lane] = au[g][i];
+        }
+        __syncthreads();
+        if (wv < 4 && 4 * g + wv < nt) {
+            float gs = 0.f, us = 0.f;
+#pragma unroll
+            for (int v = 0; v < kW; v++) {
+                gs += red[((v * 4 + wv) * 2 + 0) * 64 + lane];
+                us += red[((v * 4 + wv) * 2 + 1) * 64 + lane];
+            }
+            gp[(int64_t)(t0 + 4 * g + wv) * I + P * 64 + lane] = gs;
+            up_[(int64_t)(t0 + 4 * g + wv) * I + P * 64 + lane] = us;
+        }
+        __syncthreads();
+    }
+}
+
 // Workgroup roles, in blockIdx order: router rows (n_rwg) | shared-expert
 // gate/up partial sums per (panel, K chunk).  Workgroup 0 also clears the
 // down launch's per-panel combine counters.
@@ -249,6 +339,13 @@ k_dec_front(int H, int I, int E, int T, int n_rwg, int kc_sg, const uint16_t *__
     split_range(H / 8, kc_sg, c, c0, c1);
     float *gp = sgp + (int64_t)(c * 2 + 0) * T * I;
     float *up_ = sgp + (int64_t)(c * 2 + 1) * T * I;
+    // several bf16 tokens: the matrix cores, 16 tokens per pass over the weights
+    if (XBF16 && T > 1 && c1 - c0 <= kSgMfmaPieces) {
+        __shared__ __attribute__((aligned(16))) uint8_t xs[kSgXsBytes];
+        for (int t0 = 0; t0 < T; t0 += 16)
+            shared_gateup_mfma(H, I, T, t0, P, c0, c1, sg, su, static_cast<const uint16_t *>(x), gp, up_, red, xs);
+        return;
+    }
     for (int t0 = 0; t0 < T; t0 += kNT) {
         if (T - t0 == 1)
             shared_gateup_pass<XBF16, 1, kW>(H, I, T, t0, P, c0, c1, sg, su, x, gp, up_, red);
