@@ -519,10 +519,10 @@ template <int XBF16, int SGN>
 BM_DEV void routed_gateup_1(int H, int I, int k, const Tok &tk, int P, const uint8_t *__restrict__ gate,
                             const uint8_t *__restrict__ up, const void *__restrict__ x, const int32_t *perm,
                             uint16_t *__restrict__ h, float2 *__restrict__ hsum2, float *__restrict__ hscale,
-                            float *red) {
+                            float *red, int tok0 = -1) {
     constexpr int kRing = 4;
     const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tok[1] = {perm ? __builtin_amdgcn_readfirstlane(perm[tk.off] / k) : 0};
+    const int tok[1] = {__builtin_amdgcn_readfirstlane(tok0 >= 0 ? tok0 : perm ? perm[tk.off] / k : 0)};
     const int nb = H / kQK;
     const int64_t slab = (int64_t)I * nb * 66;
     const uint8_t *G = gate + tk.e * slab, *U = up + tk.e * slab;
@@ -594,9 +594,11 @@ BM_DEV float dot8_hilo(uint4 wq, uint4 hh, uint4 hl, float acc) {
 // One token's routing inside a gate/up workgroup (LDS): the experts by slot
 // (slot = rank of the expert index), the picks of the general top-k.
 constexpr int kMaxK = 16;
+constexpr int kMaxWgItems = 32;     // (expert, panel) items of one gate/up workgroup, routing held in LDS
 struct SmallRoute {
     int active[kMaxK], ids[kMaxK];
     int n_active;
+    int4 items[kMaxWgItems];        // batches: {expert (-1: none), first pair row, pairs, first token}
 };
 
 // Lane l of the wave: the logits of experts l, l+64, l+128, l+192 of token t
@@ -745,8 +747,48 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
             shared_h_store(nfin, kc_sg, sgp, hs, i, fg, fu);
         }
     }
+    // routing done by an earlier launch.  The routing of this workgroup's
+    // items (it = b + j G) is loaded at once, one thread per item, instead of
+    // one chain of dependent loads per item (the active slot, its expert's
+    // row and count, its first token); indices past the active slots are
+    // clamped into range and their items marked empty.
+    const int G = gridDim.x, n_it = b < n_gwg ? (n_gwg - b + G - 1) / G : 0;
+    if (n_it <= kMaxWgItems) {
+        if (tid < n_it) {
+            const int si = (b + tid * G) / panels, nact = *bk.n_active;
+            const int e = min(max(active[si], 0), E - 1);
+            const int off = offsets[e], cnt = counts[e];
+            const int tok = perm[min(max(off, 0), T * k - 1)] / k;
+            sr.items[tid] = si < nact ? make_int4(e, off, cnt, tok) : make_int4(-1, 0, 0, 0);
+        }
+        lut_build<1, SGN>(grid, lut);
+        __syncthreads();
+        for (int j = 0; j < n_it; j++) {
+            const int4 in = sr.items[j];
+            if (in.x < 0) break;
+            Tok tk;
+            tk.e = in.x;
+            tk.off = in.y;
+            tk.cnt = in.z;
+            if ((tk.cnt > 1) != (MULTI != 0)) continue;
+            const int Pi = (b + j * G) % panels;
+            if (!MULTI) {
+                routed_gateup_1<XBF16, SGN>(H, I, k, tk, Pi, gate, up, x, perm, h, hsum2, hscale, red, in.w);
+                continue;
+            }
+            for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
+                if (tk.cnt - t0 == 1)
+                    routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, Pi, lut, gate, up, x, perm, h, hsum2, hscale,
+                                                      red);
+                else
+                    routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, lut, gate, up, x, perm, h, hsum2,
+                                                        hscale, red);
+            }
+        }
+        return;
+    }
     na = *bk.n_active;
-    // routing done by an earlier launch: the workgroups loop over the
+    // (more items than the table holds) the workgroups loop over the
     // (slot, panel) items, the tables built once by each
     bool built = false;
     for (int it = b; it < n_gwg; it += gridDim.x) {
