@@ -1051,7 +1051,8 @@ BM_DEV void count_and_combine(int H, int k, int T, int kc_sd, int P, int n_contr
 // experts chosen by several tokens (launched only when T > 1).
 template <int MULTI>
 __global__ void __launch_bounds__(kWD * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 5)))
-k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, int multi_done, const uint8_t *__restrict__ down,
+k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__restrict__ n_multi,
+           const uint8_t *__restrict__ down,
            const uint4 *__restrict__ sd, const int32_t *__restrict__ counts,
            const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
            const int32_t *__restrict__ active, const int32_t *__restrict__ n_active,
@@ -1064,6 +1065,12 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, int multi_done, con
     uint4 *hst = &hstage[threadIdx.x >> 6][0][0];
     const int panels = H / 64;
     const int na = *n_active;
+    // n_multi (batches): the experts chosen by several tokens wrote their
+    // outputs in an earlier launch (as many as there are row tiles) and are
+    // not counted, unless no other contributor would combine the panel
+    const int nm = n_multi ? *n_multi : 0;
+    const bool count_multi = na - nm + kc_sd == 0;
+    const int n_contrib = count_multi ? na + kc_sd : na - nm + kc_sd;
     if ((int)blockIdx.x < n_dwg) {
         const int slot = blockIdx.x / panels, P = blockIdx.x % panels;
         if (slot >= na) return;
@@ -1071,9 +1078,8 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, int multi_done, con
         tk.e = active[slot];
         tk.off = offsets[tk.e];
         tk.cnt = counts[tk.e];
-        if (!MULTI && tk.cnt > 1 && multi_done) {
-            // this expert's outputs came from an earlier launch: only count
-            count_and_combine(H, k, T, kc_sd, P, na + kc_sd, ycount, o, w, osp, y, &sdo);
+        if (!MULTI && tk.cnt > 1 && n_multi) {
+            if (count_multi) count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
             return;
         }
         if ((tk.cnt > 1) != (MULTI != 0)) return;
@@ -1087,7 +1093,7 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, int multi_done, con
                     routed_down_pass<kNT>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
             }
         }
-        count_and_combine(H, k, T, kc_sd, P, na + kc_sd, ycount, o, w, osp, y, &sdo);
+        count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
     } else if (!MULTI) {
         const int bs = blockIdx.x - n_dwg, c = bs % kc_sd, P = bs / kc_sd;
         int c0, c1;
@@ -1099,7 +1105,7 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, int multi_done, con
             else
                 shared_down_pass<kNT>(H, I, T, t0, P, c0, c1, sd, hs, op, red, hst);
         }
-        count_and_combine(H, k, T, kc_sd, P, na + kc_sd, ycount, o, w, osp, y, &sdo);
+        count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
     }
 }
 
@@ -1219,14 +1225,14 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     // down || shared down; the last workgroup to finish a panel combines it
     const int n_dwg = p.slots * (H / 64);
     const int n_sd = shared ? (H / 64) * p.kc_sd : 0;
-    k_dec_down<0><<<n_dwg + n_sd, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, p.pf_tiles ? 1 : 0,
+    k_dec_down<0><<<n_dwg + n_sd, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, p.pf_tiles ? b.bk.n_tiles : nullptr,
                                                    (const uint8_t *)L->down_q, (const uint4 *)L->shared_down,
                                                    b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active,
                                                    b.bk.n_active, b.h, b.hsum2, b.hscale, b.hs, b.w, b.ycount,
                                                    shared ? b.osp : nullptr, b.o, b.y);
     BM_LAUNCH_CHECK();
     if (T > 1 && !p.pf_tiles) {
-        k_dec_down<1><<<n_dwg, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, 0, (const uint8_t *)L->down_q,
+        k_dec_down<1><<<n_dwg, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, nullptr, (const uint8_t *)L->down_q,
                                                 (const uint4 *)L->shared_down, b.bk.counts, b.bk.offsets,
                                                 b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum2, b.hscale, b.hs,
                                                 b.w, b.ycount, shared ? b.osp : nullptr, b.o, b.y);

@@ -234,6 +234,25 @@ def test_forward_decode_small_expert_count(T):
     assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode E=8 T={T}")
 
 
+@pytest.mark.parametrize("shared", [False, True])
+def test_forward_decode_all_experts_shared_by_tokens(shared):
+    """Four copies of one token: every chosen expert has four pairs, so the
+    batch's experts all go through the matrix-core kernels and, without a
+    shared expert, no single-token expert is left to combine the outputs."""
+    require_gpu()
+    import bit_moe_amd as bm
+    w = synth.WORKLOADS["tiny"].with_(name=f"tiny_rep_{int(shared)}", T=1, shared=shared, x_dtype="bf16", seed=41)
+    L = synth_layer(w)
+    x1, _ = synth.make_tokens(w, accept=lambda t, r: oracle.margin_ok(r, L.router(), w.k, 1e-4))
+    x = np.repeat(x1, 4, axis=0)
+    y, gid, gw = bm.forward_decode(device_layer(w), x_to_device(x))
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(x, L.router(), w.k)
+    np.testing.assert_array_equal(gid.cpu().numpy(), rid)
+    ref = oracle.layer_ffn(L, x, rid, gw.cpu().numpy().astype(np.float64))
+    assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode 4 equal tokens shared={shared}")
+
+
 @pytest.mark.parametrize("T", [1, 4])
 def test_forward_decode_zero_input_ties(T):
     """x = 0: every logit ties, so the top-k is experts 0..k-1 with weight
