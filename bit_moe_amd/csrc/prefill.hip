@@ -671,16 +671,35 @@ k_shared_down_rows(int H, int I, const uint4 *__restrict__ sd, const float *__re
     os[(int64_t)t * H + P * 64 + lane] = acc;
 }
 
+// y[t][n] = sum_j w[t][j] o[t k + j][n] (+ os[t][n]): four consecutive
+// outputs per thread, the k rows' 16-byte loads issued together (k <= KMAX).
+template <int KMAX>
 __global__ void __launch_bounds__(256)
 k_combine_p(const float *__restrict__ o, const float *__restrict__ w, const float *__restrict__ os,
             float *__restrict__ y, int T, int H, int k) {
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)T * H) return;
-    int t = (int)(i / H), n = (int)(i % H);
-    float s = 0.f;
-    for (int j = 0; j < k; j++) s = fmaf(w[t * k + j], o[((int64_t)t * k + j) * H + n], s);
-    if (os) s += os[i];
-    y[i] = s;
+    const int H4 = H / 4;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (int64_t)T * H4) return;
+    const int t = (int)(q / H4), n4 = (int)(q - (int64_t)t * H4);
+    const float4 *o4 = reinterpret_cast<const float4 *>(o) + (int64_t)t * k * H4 + n4;
+    float4 v[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; j++) v[j] = o4[(int64_t)min(j, k - 1) * H4];
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < KMAX; j++)
+        if (j < k) {
+            const float wj = w[t * k + j];
+            s.x = fmaf(wj, v[j].x, s.x);
+            s.y = fmaf(wj, v[j].y, s.y);
+            s.z = fmaf(wj, v[j].z, s.z);
+            s.w = fmaf(wj, v[j].w, s.w);
+        }
+    if (os) {
+        const float4 a = reinterpret_cast<const float4 *>(os)[q];
+        s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+    }
+    reinterpret_cast<float4 *>(y)[q] = s;
 }
 
 }  // namespace
@@ -741,8 +760,10 @@ int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T,
         k_shared_down_rows<<<gs2, 64, 0, s>>>(H, I, (const uint4 *)L->shared_down, pb.hs, pb.os);
         BM_LAUNCH_CHECK();
     }
-    int64_t n = (int64_t)T * H;
-    k_combine_p<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(pb.o, w, shared ? pb.os : nullptr, y, T, H, k);
+    if (reinterpret_cast<uintptr_t>(y) % 16) return BITMOE_EINVAL;
+    const int64_t n4 = (int64_t)T * H / 4;
+    auto kc = k <= 8 ? k_combine_p<8> : k_combine_p<16>;
+    kc<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(pb.o, w, shared ? pb.os : nullptr, y, T, H, k);
     BM_LAUNCH_CHECK();
     return BITMOE_OK;
 }
