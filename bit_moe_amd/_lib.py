@@ -229,6 +229,8 @@ def _ffn(fn, name, mode, layer: Layer, x, ids, w, y=None, ws=None, stream=None):
 
 
 def ffn_decode(layer, x, ids, w, y=None, ws=None, stream=None):
+    """Decode FFN (moe_ffn_decode); each row of ids must hold k distinct
+    experts, as a top-k gives."""
     return _ffn(lib().moe_ffn_decode, "moe_ffn_decode", DECODE, layer, x, ids, w, y, ws, stream)
 
 

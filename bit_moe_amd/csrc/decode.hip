@@ -629,8 +629,13 @@ BM_DEV void route_one_token(int mode, int E, int k, const float *__restrict__ lo
         } else {
             id = lane < k ? ids[lane] : 0;
         }
+        // rank by (expert, position): a permutation of 0..k-1 even if a row
+        // repeats an expert (which a top-k never does), so every slot is set
         int rank = 0;
-        for (int i = 0; i < k; i++) rank += __builtin_amdgcn_readlane(id, i) < id ? 1 : 0;
+        for (int i = 0; i < k; i++) {
+            const int o = __builtin_amdgcn_readlane(id, i);
+            rank += (o < id || (o == id && i < lane)) ? 1 : 0;
+        }
         if (lane < k) {
             r.active[rank] = id;
             if (out) {

@@ -159,8 +159,10 @@ size_t moe_workspace_bytes(const bitmoe_layer *L, int T, int mode);
  * The MoE FFN: y[t] = sum_j w[t][j] * D_e(silu(G_e x_t) * U_e x_t)
  *                     (+ D_s(silu(G_s x_t) * U_s x_t) when the layer has a
  *                     shared expert), e = ids[t][j], silu(z) = z/(1+e^-z).
- * x [T][H] (x_dtype), ids int32 [T][k] (values in [0,E), trusted), w float32
- * [T][k], y float32 [T][H] (overwritten).  ws: device workspace of at least
+ * x [T][H] (x_dtype), ids int32 [T][k] (values in [0,E), trusted; each row
+ * k distinct experts, as a top-k gives: moe_ffn_decode does not support a
+ * row that repeats an expert), w float32 [T][k], y float32 [T][H]
+ * (overwritten).  ws: device workspace of at least
  * moe_workspace_bytes(L, T, mode) bytes, 256-byte aligned.
  * moe_ffn_decode streams each active expert's packed blocks once and decodes
  * them in registers (fp32 accumulation); it is tuned for T <= 16 and correct
