@@ -100,6 +100,9 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
         d.o = c.take<float>(n * L->H);
         d.ycount = c.take<int32_t>(L->H / 64);
         if (p.pf_tiles) {
+            d.single = c.take<int4>(p.slots);
+            d.n_single = c.take<int32_t>(1);
+            d.gctr = c.take<int32_t>(1);
             f.b.tiles = c.take<int32_t>(2 * p.pf_tiles);
             f.b.n_tiles = c.take<int32_t>(1);
             d.pf.x16 = c.take<uint16_t>((int64_t)T * L->H);

@@ -367,6 +367,9 @@ struct DecodeBufs {
     float *o;               // [T*k][H] routed down outputs, pair order
     float *osp;             // [kc_sd][T][H] shared down partial sums
     int32_t *ycount;        // [H/64] finished down workgroups per panel
+    int4 *single;           // [slots] batches with the prefill kernels: the single-token experts, compacted
+    int32_t *n_single;      // [1] their number
+    int32_t *gctr;          // [1] their gate/up items claimed so far
     PrefillBufs pf;         // batches: experts chosen by several tokens take the prefill kernels
                             // (x16, xsc, h, hexp; their o is this o)
     float *y;               // [T][H]

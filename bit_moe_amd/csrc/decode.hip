@@ -30,6 +30,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "device_util.h"
 
@@ -312,12 +313,15 @@ template <int XBF16>
 __global__ void __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4)))
 k_dec_front(int H, int I, int E, int T, int n_rwg, int kc_sg, const uint16_t *__restrict__ wr,
             const void *__restrict__ x, float *__restrict__ logits, int32_t *__restrict__ ycount,
-            const uint4 *__restrict__ sg, const uint4 *__restrict__ su, float *__restrict__ sgp) {
+            int32_t *__restrict__ gctr, const uint4 *__restrict__ sg, const uint4 *__restrict__ su,
+            float *__restrict__ sgp) {
     __shared__ float red[kW * kNT * 2 * 64];
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int b = blockIdx.x;
-    if (b == 0)
+    if (b == 0) {
         for (int p = threadIdx.x; p < H / 64; p += kW * 64) ycount[p] = 0;
+        if (gctr && threadIdx.x == 0) *gctr = 0;
+    }
     if (b < n_rwg) {
         const int e = b * kW + wv;
         if (e >= E) return;
@@ -361,7 +365,8 @@ __global__ void __launch_bounds__(kBT)
 k_dec_mid(int E, int k, int T, const float *__restrict__ logits, int32_t *__restrict__ ids,
           float *__restrict__ w, int do_bucket, int32_t *__restrict__ counts,
           int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ active,
-          int32_t *__restrict__ n_active, int32_t *__restrict__ tiles, int32_t *__restrict__ n_tiles) {
+          int32_t *__restrict__ n_active, int32_t *__restrict__ tiles, int32_t *__restrict__ n_tiles,
+          int4 *__restrict__ single, int32_t *__restrict__ n_single) {
     extern __shared__ int smem[];
     __shared__ int swave[kBW + 1];
     const int tid = threadIdx.x, wv = tid >> 6;
@@ -386,6 +391,30 @@ k_dec_mid(int E, int k, int T, const float *__restrict__ logits, int32_t *__rest
         __syncthreads();
         if (wv == 0) bucket_wave_lists(n, smem, counts, offsets, active, n_active);
         if (wv == 0 && tiles) bucket_wave_multi_tiles(n, smem, tiles, n_tiles);
+        if (!single) return;
+        // the experts chosen by one token, compacted: {expert, pair row, 1,
+        // token} (their gate/up items are claimed one at a time)
+        __syncthreads();
+        if (wv == 0) {
+            const int lane = lane_id(), na = *n_active;
+            const uint64_t below = (1ull << lane) - 1ull;
+            int4 v[2];
+            bool one[2];
+#pragma unroll
+            for (int m = 0; m < 2; m++) {
+                const int sl = lane + 64 * m;
+                one[m] = false;
+                if (sl < na) {
+                    const int e = active[sl], off = offsets[e];
+                    one[m] = counts[e] == 1;
+                    v[m] = make_int4(e, off, 1, perm[off] / k);
+                }
+            }
+            const uint64_t B0 = __ballot(one[0]), B1 = __ballot(one[1]);
+            if (one[0]) single[__popcll(B0 & below)] = v[0];
+            if (one[1]) single[__popcll(B0) + __popcll(B1 & below)] = v[1];
+            if (lane == 0) *n_single = __popcll(B0) + __popcll(B1);
+        }
         return;
     }
     bucket_block(ids, n, E, counts, offsets, perm, active, n_active, nullptr, nullptr, 1, smem, swave);
@@ -597,7 +626,7 @@ constexpr int kMaxK = 16;
 constexpr int kMaxWgItems = 32;     // (expert, panel) items of one gate/up workgroup, routing held in LDS
 struct SmallRoute {
     int active[kMaxK], ids[kMaxK];
-    int n_active;
+    int n_active, claim;
     int4 items[kMaxWgItems];        // batches: {expert (-1: none), first pair row, pairs, first token}
 };
 
@@ -704,7 +733,8 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
              const uint8_t *__restrict__ up, const uint8_t *__restrict__ grid,
              const void *__restrict__ x, const float *__restrict__ logits,
              int32_t *ids, float *w, bm_host::Buckets bk, uint16_t *__restrict__ h, float2 *__restrict__ hsum2,
-             float *__restrict__ hscale, int kc_sg, const float *__restrict__ sgp, uint16_t *__restrict__ hs) {
+             float *__restrict__ hscale, int kc_sg, const float *__restrict__ sgp, uint16_t *__restrict__ hs,
+             const int4 *__restrict__ single, const int32_t *__restrict__ n_single, int32_t *__restrict__ gctr) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lut[];
     float *red = reinterpret_cast<float *>(lut + dec_lut_bytes<MULTI>());
     SmallRoute &sr = *reinterpret_cast<SmallRoute *>(red + dec_red_floats<MULTI>());
@@ -751,6 +781,32 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
             shared_h_load(nfin, kc_sg, sgp, i, fg, fu);
             shared_h_store(nfin, kc_sg, sgp, hs, i, fg, fu);
         }
+    }
+    if (!MULTI && gctr) {
+        // a batch whose experts with several tokens run at the same time on
+        // the prefill kernels (another stream): the single-token experts'
+        // (expert, panel) items are claimed one at a time from a counter the
+        // front launch cleared, each next claim in flight while an item is
+        // decoded, so that workgroups that start late take fewer items
+        lut_build<1, SGN>(grid, lut);
+        if (tid == 0) sr.claim = __hip_atomic_fetch_add(gctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int n_items = *n_single * panels;
+        __syncthreads();
+        int it = sr.claim;
+        while (it < n_items) {
+            const int4 in = single[it / panels];
+            int nxt = 0;
+            if (tid == 0) nxt = __hip_atomic_fetch_add(gctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            Tok tk;
+            tk.e = in.x;
+            tk.off = in.y;
+            tk.cnt = 1;
+            routed_gateup_1<XBF16, SGN>(H, I, k, tk, it % panels, gate, up, x, nullptr, h, hsum2, hscale, red, in.w);
+            if (tid == 0) sr.claim = nxt;      // every thread read the last claim before the item's barriers
+            __syncthreads();
+            it = sr.claim;
+        }
+        return;
     }
     // routing done by an earlier launch.  The routing of this workgroup's
     // items (it = b + j G) is loaded at once, one thread per item, instead of
@@ -1118,6 +1174,34 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__re
 
 namespace bm_host {
 
+// The library's own stream on the current device (default priority) and the
+// events of a fork/join onto it, created on first use.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex mu;
+};
+static SideStream *side_stream() {
+    static SideStream ss[64];
+    static std::mutex create;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lk(create);
+    SideStream &d = ss[dev];
+    if (!d.s) {
+        hipStream_t st = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess)
+            return nullptr;
+        d.fork = f;
+        d.join = j;
+        d.s = st;
+    }
+    return &d;
+}
+
 // compute units of the current device (one gate/up workgroup fits per CU)
 // (cached per device; 256 if the query fails)
 static int cu_count() {
@@ -1168,8 +1252,8 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     {
         auto kf = bf ? k_dec_front<1> : k_dec_front<0>;
         kf<<<n_front, kW * 64, 0, s>>>(H, I, E, T, p.n_rwg, p.kc_sg, (const uint16_t *)L->router_w, x, b.logits,
-                                       b.ycount, (const uint4 *)L->shared_gate, (const uint4 *)L->shared_up,
-                                       b.sgp);
+                                       b.ycount, p.pf_tiles ? b.gctr : nullptr, (const uint4 *)L->shared_gate,
+                                       (const uint4 *)L->shared_up, b.sgp);
         BM_LAUNCH_CHECK();
     }
     // mid: top-k and bucketing of batches of more than one token
@@ -1182,7 +1266,8 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
         k_dec_mid<<<1, kBT, sh, s>>>(E, k, T, p.n_rwg ? b.logits : nullptr, b.ids, b.w, in_mid ? 1 : 0,
                                      b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active, b.bk.n_active,
-                                     p.pf_tiles ? b.bk.tiles : nullptr, b.bk.n_tiles);
+                                     p.pf_tiles ? b.bk.tiles : nullptr, b.bk.n_tiles,
+                                     p.pf_tiles ? b.single : nullptr, b.n_single);
         BM_LAUNCH_CHECK();
         if (!in_mid) {
             int rc = launch_bucket(b.ids, T, k, E, b.bk, s);
@@ -1207,11 +1292,24 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
         return ok;
     }();
     if (!lds_set) return BITMOE_EHIP;
-    // experts chosen by several tokens: the prefill kernels (their o rows
-    // are ready before the down launch's combine reads them)
+    // experts chosen by several tokens: the prefill kernels on the caller's
+    // stream, and the single-token experts' gate/up beside them on a stream
+    // of the library's own that forks after the routing and joins before the
+    // down launch.  The prefill kernels take their compute units first (the
+    // other stream starts some microseconds later); the gate/up workgroups
+    // claim their items one at a time, so those that start late take fewer.
+    // The lock keeps the fork/join sequence of one call whole when several
+    // host threads share the stream.
+    SideStream *ss = nullptr;
+    std::unique_lock<std::mutex> side_lock;
+    hipStream_t sg_stream = s;
     if (p.pf_tiles) {
-        const int rc = launch_prefill_routed(L, x, x_dtype, T, b.bk, p.pf_tiles, b.pf, s);
-        if (rc) return rc;
+        ss = side_stream();
+        if (!ss) return BITMOE_EHIP;
+        side_lock = std::unique_lock<std::mutex>(ss->mu);
+        if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
+            return BITMOE_EHIP;
+        sg_stream = ss->s;
     }
     for (int multi = 0; multi < (T > 1 && !p.pf_tiles ? 2 : 1); multi++) {
         auto kg = multi ? (bf ? k_dec_gateup<1, 1> : k_dec_gateup<0, 1>)
@@ -1221,11 +1319,20 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
         const TimingEvents ev = multi ? TimingEvents{} : timing_events();
         const int grid = route_mode ? n_gwg : std::min(n_gwg, cu_count());
         hipExtLaunchKernelGGL(kg, dim3(grid), dim3(kWG * 64),
-                              multi ? dec_gateup_lds<1>() : dec_gateup_lds<0>(), s, ev.start, ev.stop, 0, H, I, E, k,
+                              multi ? dec_gateup_lds<1>() : dec_gateup_lds<0>(), sg_stream, ev.start, ev.stop, 0, H, I,
+                              E, k,
                               T, n_gwg, multi ? 0 : route_mode, (const uint8_t *)L->gate_q,
                               (const uint8_t *)L->up_q, (const uint8_t *)L->grid, x, (const float *)b.logits, b.ids,
-                              b.w, b.bk, b.h, b.hsum2, b.hscale, p.kc_sg, (const float *)b.sgp, b.hs);
+                              b.w, b.bk, b.h, b.hsum2, b.hscale, p.kc_sg, (const float *)b.sgp, b.hs,
+                              (const int4 *)b.single, (const int32_t *)b.n_single,
+                              (!multi && p.pf_tiles) ? b.gctr : nullptr);
         BM_LAUNCH_CHECK();
+    }
+    if (ss) {
+        if (hipEventRecord(ss->join, ss->s) != hipSuccess) return BITMOE_EHIP;
+        const int rc = launch_prefill_routed(L, x, x_dtype, T, b.bk, p.pf_tiles, b.pf, s);
+        if (rc) return rc;
+        if (hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return BITMOE_EHIP;
     }
     // down || shared down; the last workgroup to finish a panel combines it
     const int n_dwg = p.slots * (H / 64);
