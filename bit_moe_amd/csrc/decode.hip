@@ -1108,11 +1108,36 @@ BM_DEV void count_and_combine(int H, int k, int T, int kc_sd, int P, int n_contr
     if (*sdo) combine_panel(H, k, T, kc_sd, P, o, w, osp, y);
 }
 
+// The panel combine as a launch of its own, one thread per output, in the
+// same fixed order (batches whose down launch runs beside the prefill
+// kernels' down: the combine waits for both).
+__global__ void __launch_bounds__(256)
+k_dec_combine(int H, int k, int T, int kc_sd, const float *__restrict__ o, const float *__restrict__ w,
+              const float *__restrict__ osp, float *__restrict__ y) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)T * H) return;
+    const int t = (int)(i / H), n = (int)(i - (int64_t)t * H);
+    float ov[16], sv[kMaxChunks];
+#pragma unroll
+    for (int j = 0; j < 16; j++) ov[j] = o[((int64_t)t * k + min(j, k - 1)) * H + n];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; c++) sv[c] = kc_sd ? osp[((int64_t)min(c, kc_sd - 1) * T + t) * H + n] : 0.f;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; j++)
+        if (j < k) s = fmaf(w[t * k + j], ov[j], s);
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; c++)
+        if (c < kc_sd) s += sv[c];
+    y[i] = s;
+}
+
 // MULTI = 0: experts chosen by one token, and the shared down; MULTI = 1:
-// experts chosen by several tokens (launched only when T > 1).
+// experts chosen by several tokens (launched only when T > 1).  combine = 0:
+// the outputs are only stored (k_dec_combine sums them).
 template <int MULTI>
 __global__ void __launch_bounds__(kWD * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 5)))
-k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__restrict__ n_multi,
+k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__restrict__ n_multi, int combine,
            const uint8_t *__restrict__ down,
            const uint4 *__restrict__ sd, const int32_t *__restrict__ counts,
            const int32_t *__restrict__ offsets, const int32_t *__restrict__ perm,
@@ -1140,7 +1165,7 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__re
         tk.off = offsets[tk.e];
         tk.cnt = counts[tk.e];
         if (!MULTI && tk.cnt > 1 && n_multi) {
-            if (count_multi) count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
+            if (combine && count_multi) count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
             return;
         }
         if ((tk.cnt > 1) != (MULTI != 0)) return;
@@ -1154,7 +1179,7 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__re
                     routed_down_pass<kNT>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
             }
         }
-        count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
+        if (combine) count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
     } else if (!MULTI) {
         const int bs = blockIdx.x - n_dwg, c = bs % kc_sd, P = bs / kc_sd;
         int c0, c1;
@@ -1166,7 +1191,7 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__re
             else
                 shared_down_pass<kNT>(H, I, T, t0, P, c0, c1, sd, hs, op, red, hst);
         }
-        count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
+        if (combine) count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
     }
 }
 
@@ -1328,23 +1353,28 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
                               (!multi && p.pf_tiles) ? b.gctr : nullptr);
         BM_LAUNCH_CHECK();
     }
+    // down || shared down; the last workgroup to finish a panel combines it
+    // (with the prefill kernels: the down runs on the library stream too,
+    // beside the prefill down, and a combine launch follows the join)
+    const int n_dwg = p.slots * (H / 64);
+    const int n_sd = shared ? (H / 64) * p.kc_sd : 0;
+    k_dec_down<0><<<n_dwg + n_sd, kWD * 64, 0, sg_stream>>>(
+        H, I, k, T, n_dwg, p.kc_sd, p.pf_tiles ? b.bk.n_tiles : nullptr, ss ? 0 : 1, (const uint8_t *)L->down_q,
+        (const uint4 *)L->shared_down, b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum2,
+        b.hscale, b.hs, b.w, b.ycount, shared ? b.osp : nullptr, b.o, b.y);
+    BM_LAUNCH_CHECK();
     if (ss) {
         if (hipEventRecord(ss->join, ss->s) != hipSuccess) return BITMOE_EHIP;
         const int rc = launch_prefill_routed(L, x, x_dtype, T, b.bk, p.pf_tiles, b.pf, s);
         if (rc) return rc;
         if (hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return BITMOE_EHIP;
+        const int64_t n = (int64_t)T * H;
+        k_dec_combine<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(H, k, T, shared ? p.kc_sd : 0, b.o, b.w,
+                                                                  shared ? b.osp : nullptr, b.y);
+        BM_LAUNCH_CHECK();
     }
-    // down || shared down; the last workgroup to finish a panel combines it
-    const int n_dwg = p.slots * (H / 64);
-    const int n_sd = shared ? (H / 64) * p.kc_sd : 0;
-    k_dec_down<0><<<n_dwg + n_sd, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, p.pf_tiles ? b.bk.n_tiles : nullptr,
-                                                   (const uint8_t *)L->down_q, (const uint4 *)L->shared_down,
-                                                   b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active,
-                                                   b.bk.n_active, b.h, b.hsum2, b.hscale, b.hs, b.w, b.ycount,
-                                                   shared ? b.osp : nullptr, b.o, b.y);
-    BM_LAUNCH_CHECK();
     if (T > 1 && !p.pf_tiles) {
-        k_dec_down<1><<<n_dwg, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, nullptr, (const uint8_t *)L->down_q,
+        k_dec_down<1><<<n_dwg, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, nullptr, 1, (const uint8_t *)L->down_q,
                                                 (const uint4 *)L->shared_down, b.bk.counts, b.bk.offsets,
                                                 b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum2, b.hscale, b.hs,
                                                 b.w, b.ycount, shared ? b.osp : nullptr, b.o, b.y);
