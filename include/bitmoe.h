@@ -31,6 +31,11 @@
  *  - Shapes: H (hidden) and I (expert intermediate) must be multiples of
  *    256; 1 <= k <= 16; k <= E <= 1024; T >= 0 (T = 0 is a no-op).
  *  - Calls are thread-safe; calls on different streams may overlap.
+ *  - moe_ffn_decode / moe_forward_decode on a batch in which some expert is
+ *    chosen by several tokens (2 <= T, T*k <= 128, T <= 96) fork part of the
+ *    work onto a stream the library keeps per device (created on the first
+ *    such call, default priority) and join it back into `stream` before the
+ *    call's last kernel: the call is still ordered on `stream` as a whole.
  *
  * Weight formats
  *  CANONICAL blocks (the interchange format, GGML order):
