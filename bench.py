@@ -191,6 +191,33 @@ def prefill_2k(args, lays):
     return dict(ms=ms, flops=flops, gu_ms=gu_ms, gu_flops=gu_flops)
 
 
+def prefill_8k_zipf(args, lays):
+    """8192 tokens with drawn Zipf(1.2) logits (the hottest experts get over a
+    thousand rows, the coldest a few): top-k of the logits + the prefill FFN."""
+    import numpy as np
+    import torch
+    import bit_moe_amd as bm
+    import synth
+    w = synth.WORKLOADS["prefill_8k_zipf"]
+    x, _ = synth.make_tokens(w)
+    xd = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
+    lg = torch.from_numpy(synth.zipf_logits(w)).cuda()
+    lay = bm.Layer(w.H, w.I, w.E, w.k, *lays[0].tensors[:5])
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+    y = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(bm.workspace_bytes(lay, w.T, bm.PREFILL), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        bm.topk(lg, w.k, ids=ids, w=wt)
+        bm.ffn_prefill(lay, xd, ids, wt, y=y, ws=ws)
+
+    ms = time_steps(step, 1, max(2, args.prefill_steps // 4))
+    rows = np.bincount(ids.cpu().numpy().ravel(), minlength=w.E)
+    flops = w.T * w.k * 3 * 2 * w.H * w.I
+    return dict(ms=ms, flops=flops, rows_max=int(rows.max()), rows_min=int(rows.min()))
+
+
 def cpu_baseline(target_s=15.0, max_tokens=400):
     """The oracle (plain fp64 C, all host threads) on the decode workload,
     one token at a time until about target_s seconds of oracle time: routing
@@ -287,8 +314,8 @@ def summarize_kernels(trace_dir):
     by bench phase, name and grid.  Phases follow the run's order: layer set-up
     (packing) until the first decode launch, decode_b1 until the batch-16 step's
     first top-k, decode_b16 until the prefill step's router GEMM (the decode
-    batch also runs prefill kernels, for its multi-token experts), then
-    prefill_2k."""
+    batch also runs prefill kernels, for its multi-token experts), prefill_2k
+    until the 8192-token step's top-k, then prefill_8k."""
     import glob
     import sqlite3
     rows = {}
@@ -302,6 +329,8 @@ def summarize_kernels(trace_dir):
                 phase = "decode_b16"
             elif phase == "decode_b16" and "k_router_splitk" in name:
                 phase = "prefill_2k"
+            elif phase == "prefill_2k" and "k_topk" in name and "k_topk_sum" not in name:
+                phase = "prefill_8k"
             r = rows.setdefault((phase, name, gx), [0, 0.0, float("inf"), 0.0])
             d = (t1 - t0) / 1e3
             r[0] += 1
@@ -309,7 +338,7 @@ def summarize_kernels(trace_dir):
             r[2] = min(r[2], d)
             r[3] = max(r[3], d)
     out = [f"{'phase':<11} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'grid':>10}  kernel"]
-    order = {"setup": 0, "decode_b1": 1, "decode_b16": 2, "prefill_2k": 3}
+    order = {"setup": 0, "decode_b1": 1, "decode_b16": 2, "prefill_2k": 3, "prefill_8k": 4}
     for (phase, name, gx), (n, tot, mn, mx) in sorted(rows.items(), key=lambda kv: (order[kv[0][0]], -kv[1][1])):
         short = name[name.index("k_"):].split("(")[0] if "k_" in name else name.split("(")[0]
         out.append(f"{phase:<11} {n:6d} {tot / n:10.2f} {mn:10.2f} {mx:10.2f} {gx:10d}  {short}")
@@ -435,6 +464,13 @@ def main():
                              "gateup_TFLOPs": pf["gu_flops"] / (pf["gu_ms"] * 1e-3) / 1e12,
                              "gateup_mfma_frac": pf["gu_flops"] / (pf["gu_ms"] * 1e-3) / BF16_PEAK}
         log(f"[bench] prefill_2k {pf['ms']:.2f} ms/step")
+        p8 = prefill_8k_zipf(args, lays)
+        out["prefill_8k_zipf"] = {"tokens_per_s": 8192 / (p8["ms"] * 1e-3), "ms_per_step": p8["ms"],
+                                  "routed_TFLOPs": p8["flops"] / (p8["ms"] * 1e-3) / 1e12,
+                                  "mfma_frac": p8["flops"] / (p8["ms"] * 1e-3) / BF16_PEAK,
+                                  "rows_per_expert_max": p8["rows_max"], "rows_per_expert_min": p8["rows_min"],
+                                  "note": "step = top-k of drawn Zipf(1.2) logits + prefill FFN"}
+        log(f"[bench] prefill_8k_zipf {p8['ms']:.2f} ms/step")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
         log(f"[bench] cpu baseline {out['cpu_baseline']['value']:.3f} tokens/s")
