@@ -44,7 +44,6 @@ constexpr int kWD = 4;             // waves per down workgroup: every down workg
                                    // batch is resident at once
 constexpr int kNT = 4;             // tokens per pass over the weights
 constexpr int kMaxChunks = 8;      // K chunks of the shared expert, at most
-constexpr int kMaxExperts = 1024;
 constexpr int kSharedChunkCols = 512;   // I columns of one shared-down K chunk, at most
 // per token, the LDS staging of a routed down wave's two superblocks of h:
 // 64 pieces of 8 fp16, 16 pieces of two {hs, hb}, two pieces of 4 scales
@@ -471,7 +470,7 @@ BM_DEV void gateup_epilogue(int I, const Tok &tk, int t0, int P, const float (&a
 }
 
 template <int XBF16, int NT, int SGN>
-BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P, const uint8_t *lut,
+BM_DEV void routed_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P,
                                const uint8_t *__restrict__ gate, const uint8_t *__restrict__ up,
                                const void *__restrict__ x, const int32_t *perm,
                                uint16_t *__restrict__ h, float2 *__restrict__ hsum2,
@@ -839,10 +838,10 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
             }
             for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
                 if (tk.cnt - t0 == 1)
-                    routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, Pi, lut, gate, up, x, perm, h, hsum2, hscale,
+                    routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale,
                                                       red);
                 else
-                    routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, lut, gate, up, x, perm, h, hsum2,
+                    routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2,
                                                         hscale, red);
             }
         }
@@ -871,9 +870,9 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
         }
         for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
             if (tk.cnt - t0 == 1)
-                routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, Pi, lut, gate, up, x, perm, h, hsum2, hscale, red);
+                routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale, red);
             else
-                routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, lut, gate, up, x, perm, h, hsum2, hscale,
+                routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale,
                                                     red);
         }
     }
