@@ -1107,6 +1107,86 @@ BM_DEV void count_and_combine(int H, int k, int T, int kc_sd, int P, int n_contr
     if (*sdo) combine_panel(H, k, T, kc_sd, P, o, w, osp, y);
 }
 
+// Shared down of a decode batch on the matrix cores (batches that run the
+// prefill kernels): panel P of the H output rows, K chunk c of the I columns
+// (kc chunks), 16 tokens per pass over the bf16 weights, with the operand
+// scheme of shared_gateup_mfma.  h arrives as bf16 hi + lo; the two parts
+// are two instructions into the same accumulators.  Four waves split the
+// chunk's pieces and meet in LDS; outputs go to osp[c][T][H] as in the
+// other shared down.
+constexpr int kSdmW = 4;
+constexpr int kSdmPieces = 64;              // K pieces of a chunk the staging holds
+constexpr int kSdmXsBytes = 2 * 16 * (kSdmPieces * 16 + 16) + 16;
+__global__ void __launch_bounds__(kSdmW * 64)
+k_shared_down_mfma(int H, int I, int T, int kc, const uint4 *__restrict__ sd, const uint16_t *__restrict__ hs,
+                   float *__restrict__ osp) {
+    __shared__ float red[kSdmW * 4 * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t xs[kSdmXsBytes];
+    const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int P = blockIdx.x / kc, c = blockIdx.x % kc, K8 = I / 8;
+    int c0, c1;
+    split_range(K8, kc, c, c0, c1);
+    const int nc = c1 - c0, stride = nc * 16 + 16, half = 16 * stride, zero = 2 * half;
+    const int j = lane >> 4, m = lane & 15;
+    const bool act = (m >> 2) == j;
+    const int64_t lo_off = (int64_t)T * I;
+    const uint4 *wbase = sd + (int64_t)P * K8 * 64 + lane;
+    int w0, w1;
+    split_range(nc, kSdmW, wv, w0, w1);
+    for (int t0 = 0; t0 < T; t0 += 16) {
+        const int nt = min(16, T - t0);
+        __syncthreads();                 // the previous pass's readers of xs and red are done
+        for (int i = threadIdx.x; i < 2 * 16 * nc; i += blockDim.x) {
+            const int part = i / (16 * nc), r = i - part * 16 * nc, tt = r / nc, cl = r - tt * nc;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (tt < nt)
+                v = *reinterpret_cast<const uint4 *>(hs + (part ? lo_off : 0) + (int64_t)(t0 + tt) * I + 8 * (c0 + cl));
+            *reinterpret_cast<uint4 *>(xs + part * half + tt * stride + cl * 16) = v;
+        }
+        if (threadIdx.x == 0) *reinterpret_cast<uint4 *>(xs + zero) = make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();
+        f32x4_t acc[4];
+#pragma unroll
+        for (int g = 0; g < 4; g++) acc[g] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        constexpr int kB = 4;
+        for (int cb = w0; cb < w1; cb += kB) {
+            uint4 wq[kB];
+#pragma unroll
+            for (int i = 0; i < kB; i++) wq[i] = wbase[(int64_t)(c0 + min(cb + i, w1 - 1)) * 64];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < kB; i++) {
+                const int cl = min(cb + i, w1 - 1);
+                const bool use = act && cb + i < w1;
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const int a = use ? (4 * g + (m & 3)) * stride + cl * 16 : zero;
+                    const uint4 ah = *reinterpret_cast<const uint4 *>(xs + (use ? a : zero));
+                    const uint4 al = *reinterpret_cast<const uint4 *>(xs + (use ? half + a : zero));
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah),
+                                                                     __builtin_bit_cast(bf16x8_t, wq[i]), acc[g], 0, 0, 0);
+                    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al),
+                                                                     __builtin_bit_cast(bf16x8_t, wq[i]), acc[g], 0, 0, 0);
+                }
+            }
+        }
+        // lane l, result i of group g: panel row l, token 4 g + i
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) red[(wv * 4 + i) * 64 + lane] = acc[g][i];
+            __syncthreads();
+            if (wv < 4 && 4 * g + wv < nt) {
+                float sum = 0.f;
+#pragma unroll
+                for (int v = 0; v < kSdmW; v++) sum += red[(v * 4 + wv) * 64 + lane];
+                osp[((int64_t)c * T + t0 + 4 * g + wv) * H + P * 64 + lane] = sum;
+            }
+            __syncthreads();
+        }
+    }
+}
+
 // The panel combine as a launch of its own, one thread per output, in the
 // same fixed order (batches whose down launch runs beside the prefill
 // kernels' down: the combine waits for both).
@@ -1356,7 +1436,15 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     // (with the prefill kernels: the down runs on the library stream too,
     // beside the prefill down, and a combine launch follows the join)
     const int n_dwg = p.slots * (H / 64);
-    const int n_sd = shared ? (H / 64) * p.kc_sd : 0;
+    // (beside the prefill kernels the shared down runs on the matrix cores,
+    // in a launch of its own on the library stream)
+    const bool sd_mfma = ss && shared && (I / 8 + p.kc_sd - 1) / p.kc_sd <= kSdmPieces;
+    if (sd_mfma) {
+        k_shared_down_mfma<<<(H / 64) * p.kc_sd, kSdmW * 64, 0, sg_stream>>>(H, I, T, p.kc_sd,
+                                                                           (const uint4 *)L->shared_down, b.hs, b.osp);
+        BM_LAUNCH_CHECK();
+    }
+    const int n_sd = shared && !sd_mfma ? (H / 64) * p.kc_sd : 0;
     k_dec_down<0><<<n_dwg + n_sd, kWD * 64, 0, sg_stream>>>(
         H, I, k, T, n_dwg, p.kc_sd, p.pf_tiles ? b.bk.n_tiles : nullptr, ss ? 0 : 1, (const uint8_t *)L->down_q,
         (const uint4 *)L->shared_down, b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum2,
