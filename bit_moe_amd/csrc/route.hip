@@ -133,6 +133,13 @@ k_topk(const float *__restrict__ logits, int T, int E, int k, int32_t *__restric
        float *__restrict__ wout) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
+    if (E <= 256) {         // four logits per lane, one key round per pick
+        float lv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) lv[i] = logits[(int64_t)t * E + min(lane_id() + 64 * i, E - 1)];
+        topk_wave4(lv, E, k, ids + (int64_t)t * k, wout + (int64_t)t * k, nullptr);
+        return;
+    }
     topk_wave(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, wout + (int64_t)t * k);
 }
 

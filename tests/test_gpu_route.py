@@ -110,6 +110,28 @@ def test_topk_on_drawn_logits(name):
     np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=1e-6)
 
 
+@pytest.mark.parametrize("E,k", [(200, 8), (256, 16), (1000, 6)])
+def test_topk_signed_zero_ties_and_expert_counts(E, k):
+    """Random logits with planted exact ties, including -0.0 against +0.0
+    (equal values: the lower expert index wins), for expert counts below,
+    at and above one wave's four logits per lane."""
+    require_gpu()
+    import bit_moe_amd as bm
+    rng = np.random.default_rng(E + k)
+    lg = rng.standard_normal((24, E)).astype(np.float32)
+    lg[:, 5] = lg[:, 3]                       # exact ties
+    lg[0, :] = 0.0
+    lg[0, 1::2] = -0.0                       # signed zeros only: experts 0..k-1
+    lg[1, : E // 2] = -0.0
+    lg[1, E // 2:] = -1.0                    # -0.0 wins, lowest indices first
+    rid, rw = oracle.topk(lg.astype(np.float64), k)
+    gid, gw = bm.topk(torch.from_numpy(lg).cuda(), k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gid.cpu().numpy(), rid)
+    np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=1e-6)
+    assert gid.cpu().numpy()[0].tolist() == list(range(k))
+
+
 def _bucket_case(ids, E):
     import bit_moe_amd as bm
     counts, offsets, perm = oracle.bucket(ids, E)
