@@ -453,20 +453,30 @@ struct DnArgs {
     float *o;
 };
 
+// Raw loads only (h piece and its chunk exponent): a rescale here would make
+// the wave wait for these loads before the current stage's MFMAs.
 template <int R>
-BM_DEV void dn_stage_load(const DnArgs &a, const PfTile &t, const int *semax, int kb, int hf, u32x4 (&r)[R / 32]) {
+BM_DEV void dn_stage_load(const DnArgs &a, const PfTile &t, int kb, int hf, u32x4 (&r)[R / 32], int (&ex)[R / 32]) {
     const int k0 = kb * kQK + hf * kPfHalf, nI = a.I / kPfGuCols;
 #pragma unroll
     for (int p = 0; p < R / 32; p++) {
         const StageIdx x = stage_idx(p);
         const int64_t gr = t.off + t.r0 + min(x.row, t.rows - 1);
-        u32x4 v = *reinterpret_cast<const u32x4 *>(a.h + gr * a.I + k0 + 8 * x.c);
-        const int d = a.hexp[gr * nI + kb] - semax[x.row];
+        r[p] = *reinterpret_cast<const u32x4 *>(a.h + gr * a.I + k0 + 8 * x.c);
+        ex[p] = a.hexp[gr * nI + kb];
+    }
+}
+
+// Rescale the loaded pieces to the row's largest exponent (exact: powers of two).
+template <int R>
+BM_DEV void dn_stage_scale(const int *semax, const int (&ex)[R / 32], u32x4 (&r)[R / 32]) {
+#pragma unroll
+    for (int p = 0; p < R / 32; p++) {
+        const int d = ex[p] - semax[stage_idx(p).row];
         if (d != 0) {
             const uint32_t f = f16_pow2(d) * 0x10001u;
-            v = u32x4{pk_mul(v.x, f), pk_mul(v.y, f), pk_mul(v.z, f), pk_mul(v.w, f)};
+            r[p] = u32x4{pk_mul(r[p].x, f), pk_mul(r[p].y, f), pk_mul(r[p].z, f), pk_mul(r[p].w, f)};
         }
-        r[p] = v;
     }
 }
 
@@ -553,24 +563,29 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
     };
     const int nsteps = 2 * nb;
     u32x4 ar[R / 32];
+    int aex[R / 32];
     auto stage = [&](auto full, int st, Slot &cur, Slot &pre) {      // as in gu_tile
         const int s1 = st + 1, s2 = st + 2;
         asm volatile("" ::: "memory");
-        if (full || s1 < nsteps) dn_stage_load<R>(a, t, semax, s1 >> 1, s1 & 1, ar);
+        if (full || s1 < nsteps) dn_stage_load<R>(a, t, s1 >> 1, s1 & 1, ar, aex);
         asm volatile("" ::: "memory");
         if (full || s2 < nsteps) load_slot(s2, pre);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         if (active) compute(sa + (st & 1) * kPfABytes, cur);
-        if (full || s1 < nsteps) stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
+        if (full || s1 < nsteps) {
+            dn_stage_scale<R>(semax, aex, ar);
+            stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
+        }
         __syncthreads();
     };
     using Full = std::integral_constant<bool, true>;
     using Part = std::integral_constant<bool, false>;
     Slot q0, q1, q2;
-    dn_stage_load<R>(a, t, semax, 0, 0, ar);
+    dn_stage_load<R>(a, t, 0, 0, ar, aex);
     load_slot(0, q0);
     if (nsteps > 1) load_slot(1, q1);
+    dn_stage_scale<R>(semax, aex, ar);
     stage_store<R>(sa, ar);
     __builtin_amdgcn_s_waitcnt(0);       // see gu_tile
     __syncthreads();
