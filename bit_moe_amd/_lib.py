@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(HERE, "libbitmoe.so")
 
 F32, BF16 = 0, 1
 DECODE, PREFILL = 0, 1
+LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
+TIME_GATEUP, TIME_DOWN = 0, 1
 EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = -1, -2, -3, -4
 
 # every symbol declared in include/bitmoe.h
@@ -31,7 +33,7 @@ class LayerStruct(C.Structure):
     _fields_ = [("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
                 ("router_w", C.c_void_p), ("gate_q", C.c_void_p), ("up_q", C.c_void_p),
                 ("down_q", C.c_void_p), ("grid", C.c_void_p), ("shared_gate", C.c_void_p),
-                ("shared_up", C.c_void_p), ("shared_down", C.c_void_p)]
+                ("shared_up", C.c_void_p), ("shared_down", C.c_void_p), ("layout", C.c_int32)]
 
 
 _lib = None
@@ -68,7 +70,7 @@ def lib() -> C.CDLL:
         "moe_pack_iq2x": ([P, P, I, I, I, P], I),
         "moe_pack_q2k": ([P, P, I, I, I, P], I),
         "moe_pack_bf16": ([P, P, I, I, P], I),
-        "moe_set_timing_events": ([P, P], I),
+        "moe_set_timing_events": ([P, P, I], I),
         "moe_strerror": ([I], C.c_char_p),
         "moe_version": ([], C.c_char_p),
     }
@@ -79,12 +81,13 @@ def lib() -> C.CDLL:
     return L
 
 
-def set_timing_events(start=None, stop=None) -> None:
-    """Record torch.cuda.Event objects around the gate/up kernel of the
+def set_timing_events(start=None, stop=None, which=TIME_GATEUP) -> None:
+    """Record torch.cuda.Event objects around one kernel (TIME_GATEUP: the
+    routed gate/up kernel, TIME_DOWN: the routed down kernel) of the
     following FFN calls from this thread (None, None turns it off)."""
     sp = start.cuda_event if start is not None else None
     tp = stop.cuda_event if stop is not None else None
-    _check(lib().moe_set_timing_events(sp, tp), "moe_set_timing_events")
+    _check(lib().moe_set_timing_events(sp, tp, which), "moe_set_timing_events")
 
 
 def strerror(code: int) -> str:
@@ -140,7 +143,8 @@ def _workspace(nbytes: int, device):
 
 
 class Layer:
-    """A routed-MoE layer whose weights live in torch device tensors (tiled)."""
+    """A routed-MoE layer whose weights live in torch device tensors, in the
+    tiled layout (moe_pack_* output)."""
 
     def __init__(self, H, I, E, k, router_w, gate_q, up_q, down_q, grid, shared=None):
         _dev_check(router_w, gate_q, up_q, down_q, grid)
@@ -153,7 +157,7 @@ class Layer:
             self.tensors += [sg, su, sd]
         self.has_shared = shared is not None
         self.s = LayerStruct(H, I, E, k, _ptr(router_w), _ptr(gate_q), _ptr(up_q), _ptr(down_q),
-                             _ptr(grid), _ptr(sg), _ptr(su), _ptr(sd))
+                             _ptr(grid), _ptr(sg), _ptr(su), _ptr(sd), LAYOUT_TILED)
 
     @property
     def ref(self):

@@ -2,20 +2,17 @@
 // orchestration.  Every check runs before the first launch, so a call that
 // returns an error has queued nothing; the checks never touch the GPU and
 // can be exercised without one.
-#include <hip/hip_runtime.h>
-
 #include <algorithm>
 #include <cstdint>
 
-#include "../../include/bitmoe.h"
-#include "common.h"
+#include "host.h"
 
 namespace {
 
+using bm_cfg::kFusedRouterMaxT;
+
 constexpr size_t kAlign = 256;
 constexpr int kMaxT = 1 << 20;           // tokens per call
-constexpr int kMfmaRouterMinT = 64;      // bf16 activations: MFMA router from here on
-constexpr int kFusedRouterMaxT = 16;     // decode: router rows fused into the first launch
 
 inline size_t up256(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
@@ -32,6 +29,9 @@ int check_layer_shape(const bitmoe_layer *L) {
 int check_ffn_layer(const bitmoe_layer *L) {
     int rc = check_layer_shape(L);
     if (rc) return rc;
+    // the FFN kernels read the tiled layout only
+    if (L->layout == BITMOE_LAYOUT_CANONICAL) return BITMOE_EUNSUPPORTED;
+    if (L->layout != BITMOE_LAYOUT_TILED) return BITMOE_EINVAL;
     if (!L->gate_q || !L->up_q || !L->down_q || !L->grid) return BITMOE_EINVAL;
     const bool a = L->shared_gate, b = L->shared_up, c = L->shared_down;
     if (a != b || b != c) return BITMOE_EINVAL;
@@ -61,6 +61,8 @@ struct FfnWs {
     bm_host::PrefillBufs p{};
     // decode
     bm_host::DecodeBufs d{};
+    void *route_ws = nullptr;      // moe_forward_decode, batches routed by moe_route
+    size_t route_ws_bytes = 0;
     size_t bytes = 0;
 };
 
@@ -76,7 +78,7 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
     f.b.n_active = c.take<int32_t>(1);
     f.b.scratch = reinterpret_cast<int32_t *>(c.take<char>(bm_host::bucket_scratch_bytes(T, L->k, L->E)));
     if (mode == BITMOE_PREFILL) {
-        f.b.tile_rows = bm_host::prefill_tile_rows();
+        f.b.tile_rows = bm_cfg::kPfRows;
         f.max_tiles = (int)((n + f.b.tile_rows - 1) / f.b.tile_rows + std::min<int64_t>(L->E, n));
         f.b.tiles = c.take<int32_t>(2 * std::max(f.max_tiles, 1));
         f.b.n_tiles = c.take<int32_t>(1);
@@ -117,14 +119,15 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
             d.osp = c.take<float>((int64_t)p.kc_sd * T * L->H);
         }
         d.bk = f.b;
+        if (T > kFusedRouterMaxT) {
+            // the router's scratch for moe_forward_decode (the larger of
+            // the two dtypes' needs)
+            f.route_ws_bytes = bm_host::route_ws_bytes(L, T, BITMOE_BF16);
+            f.route_ws = c.take<char>(f.route_ws_bytes);
+        }
     }
     f.bytes = c.off;
     return f;
-}
-
-size_t route_ws_bytes(const bitmoe_layer *L, int T, int x_dtype) {
-    if (T >= kMfmaRouterMinT && x_dtype == BITMOE_BF16) return up256(bm_host::router_mfma_part_floats(T, L->E) * 4);
-    return up256((size_t)std::min(T, bm_host::router_tokens_per_launch()) * L->E * 4);
 }
 
 int check_ws(void *ws, size_t have, size_t need) {
@@ -152,19 +155,15 @@ int ffn_common(const bitmoe_layer *L, const void *x, int x_dtype, int T, const i
 
 }  // namespace
 
-namespace bm_host {
-TimingEvents &timing_events() {
-    thread_local TimingEvents ev;
-    return ev;
-}
-}  // namespace bm_host
-
 extern "C" {
 
-int moe_set_timing_events(void *start, void *stop) {
+int moe_set_timing_events(void *start, void *stop, int which) {
     if ((start == nullptr) != (stop == nullptr)) return BITMOE_EINVAL;
-    bm_host::timing_events().start = static_cast<hipEvent_t>(start);
-    bm_host::timing_events().stop = static_cast<hipEvent_t>(stop);
+    if (which != BITMOE_TIME_GATEUP && which != BITMOE_TIME_DOWN) return BITMOE_EINVAL;
+    bm_host::TimingEvents &ev = bm_host::timing_events();
+    ev.start = static_cast<hipEvent_t>(start);
+    ev.stop = static_cast<hipEvent_t>(stop);
+    ev.which = which;
     return BITMOE_OK;
 }
 
@@ -172,7 +171,9 @@ const char *moe_strerror(int code) {
     switch (code) {
         case BITMOE_OK: return "ok";
         case BITMOE_EINVAL: return "invalid argument (null pointer, bad dtype or mode, bad size or alignment)";
-        case BITMOE_EUNSUPPORTED: return "unsupported shape (H and I must be multiples of 256, 1<=k<=16, k<=E<=1024)";
+        case BITMOE_EUNSUPPORTED:
+            return "unsupported shape or layout (H and I must be multiples of 256, 1<=k<=16, k<=E<=1024; "
+                   "the FFN calls read TILED blocks)";
         case BITMOE_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
         case BITMOE_EHIP: return "a HIP kernel launch failed";
         default: return "unknown error code";
@@ -183,7 +184,7 @@ const char *moe_version(void) { return "bitmoe 0.1.0 (gfx950)"; }
 
 size_t moe_route_workspace_bytes(const bitmoe_layer *L, int T, int x_dtype) {
     if (check_layer_shape(L) || T <= 0) return 0;
-    return route_ws_bytes(L, T, x_dtype);
+    return bm_host::route_ws_bytes(L, T, x_dtype);
 }
 
 int moe_route(const bitmoe_layer *L, const void *x, int x_dtype, int T, float *logits, int32_t *ids,
@@ -196,14 +197,14 @@ int moe_route(const bitmoe_layer *L, const void *x, int x_dtype, int T, float *l
     if (x_dtype != BITMOE_F32 && x_dtype != BITMOE_BF16) return BITMOE_EINVAL;
     if (T == 0) return BITMOE_OK;
     if (!x || !ids || !w || !aligned(x, 16)) return BITMOE_EINVAL;
-    rc = check_ws(ws, ws_bytes, route_ws_bytes(L, T, x_dtype));
+    rc = check_ws(ws, ws_bytes, bm_host::route_ws_bytes(L, T, x_dtype));
     if (rc) return rc;
     hipStream_t s = as_stream(stream);
     float *part = static_cast<float *>(ws);
-    if (T >= kMfmaRouterMinT && x_dtype == BITMOE_BF16)
+    if (bm_host::route_uses_mfma(T, x_dtype))
         return bm_host::launch_router_mfma(L, x, T, logits, ids, w, part, s);
-    // one wave per expert row, token batches of router_tokens_per_launch()
-    const int NT = bm_host::router_tokens_per_launch();
+    // one wave per expert row, token batches of kRouterNT
+    const int NT = bm_cfg::kRouterNT;
     const size_t xs = x_dtype == BITMOE_BF16 ? 2 : 4;
     for (int t0 = 0; t0 < T; t0 += NT) {
         int nt = std::min(NT, T - t0);
@@ -279,8 +280,8 @@ int moe_forward_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T,
     b.y = y;
     const bool fused = T <= kFusedRouterMaxT;
     if (!fused) {
-        // the decode workspace's logits area is large enough for the router
-        rc = moe_route(L, x, x_dtype, T, nullptr, ids, w, b.logits, up256((size_t)T * L->E * 4), stream);
+        // the router's scratch is carved from the decode workspace
+        rc = moe_route(L, x, x_dtype, T, nullptr, ids, w, f.route_ws, f.route_ws_bytes, stream);
         if (rc) return rc;
     }
     return bm_host::launch_decode(L, x, x_dtype, T, bm_host::decode_plan(L, T, fused), b, s);

@@ -85,14 +85,7 @@ k_bucket_scatter(const int32_t *__restrict__ ids, int n, int E, const int32_t *_
 
 namespace bm_host {
 
-constexpr int kSmallPairs = 4096;
-
-size_t bucket_scratch_bytes(int T, int k, int E) {
-    int64_t n = (int64_t)T * k;
-    if (n <= kSmallPairs) return 256;
-    int64_t nblk = (n + kBT - 1) / kBT;
-    return (size_t)(nblk * E * 4 + 255) / 256 * 256;
-}
+using bm_cfg::kSmallPairs;
 
 // Dynamic LDS above 64 KiB (E close to 1024) must be opted into per kernel.
 template <class K>

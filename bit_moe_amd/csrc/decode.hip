@@ -29,7 +29,6 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
-#include <atomic>
 #include <mutex>
 
 #include "device_util.h"
@@ -38,13 +37,12 @@ namespace {
 
 using namespace bm;
 
-constexpr int kW = 16;             // waves per front workgroup
+constexpr int kW = bm_cfg::kFrontWaves;   // waves per front workgroup
 constexpr int kWG = 16;            // waves per routed gate/up workgroup
 constexpr int kWD = 4;             // waves per down workgroup: every down workgroup of a decode
                                    // batch is resident at once
 constexpr int kNT = 4;             // tokens per pass over the weights
-constexpr int kMaxChunks = 8;      // K chunks of the shared expert, at most
-constexpr int kSharedChunkCols = 512;   // I columns of one shared-down K chunk, at most
+using bm_cfg::kMaxChunks;           // K chunks of the shared expert, at most
 // per token, the LDS staging of a routed down wave's two superblocks of h:
 // 64 pieces of 8 fp16, 16 pieces of two {hs, hb}, two pieces of 4 scales
 constexpr int kHst = 64 + 16 + 2;
@@ -1306,40 +1304,6 @@ static SideStream *side_stream() {
     return &d;
 }
 
-// compute units of the current device (one gate/up workgroup fits per CU)
-// (cached per device; 256 if the query fails)
-static int cu_count() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n > 0) return n;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
-
-DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
-    DecodePlan p;
-    const bool shared = L->shared_gate != nullptr;
-    p.slots = (int)std::min<int64_t>(L->E, (int64_t)T * L->k);
-    p.n_rwg = with_router ? (L->E + kW - 1) / kW : 0;
-    // the shared gate/up's K chunks: as many as fit the compute units
-    // beside the router workgroups (one front workgroup per CU), at most 8
-    p.kc_sg = shared ? std::max(1, std::min(kMaxChunks, (cu_count() - p.n_rwg) / (L->I / 64))) : 0;
-    p.kc_sd = shared ? std::max(1, (L->I + kSharedChunkCols - 1) / kSharedChunkCols) : 0;
-    p.small = (int64_t)T * L->k <= kWaveBucketMax;
-    // one token: every gate/up workgroup routes it itself; more tokens: one
-    // routing launch, so that the gate/up workgroups can each take several
-    // (expert, panel) items
-    p.need_mid = !p.small || T > 1;
-    // several tokens (one row tile per expert): experts chosen by more than
-    // one token go through the prefill kernels, which decode each weight once
-    // for all of its tokens on the matrix cores
-    p.pf_tiles = (p.small && T > 1 && T <= prefill_tile_rows()) ? (int)std::min<int64_t>(L->E, (int64_t)T * L->k / 2) : 0;
-    return p;
-}
-
 size_t decode_mid_lds(int E) {
     return (size_t)std::max<int64_t>((int64_t)(2 + kBW) * E, kWaveBucketMax) * sizeof(int);
 }
@@ -1403,24 +1367,40 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     // other stream starts some microseconds later); the gate/up workgroups
     // claim their items one at a time, so those that start late take fewer.
     // The lock keeps the fork/join sequence of one call whole when several
-    // host threads share the stream.
+    // host threads share the stream.  Without the fork (p.fork false) the
+    // same launches run one after the other on the caller's stream.
+    const bool split = p.pf_tiles > 0;
     SideStream *ss = nullptr;
     std::unique_lock<std::mutex> side_lock;
     hipStream_t sg_stream = s;
-    if (p.pf_tiles) {
+    if (split && p.fork) {
         ss = side_stream();
         if (!ss) return BITMOE_EHIP;
         side_lock = std::unique_lock<std::mutex>(ss->mu);
-        if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess)
-            return BITMOE_EHIP;
+        if (hipEventRecord(ss->fork, s) != hipSuccess) return BITMOE_EHIP;
+        if (hipStreamWaitEvent(ss->s, ss->fork, 0) != hipSuccess) return BITMOE_EHIP;
         sg_stream = ss->s;
     }
-    for (int multi = 0; multi < (T > 1 && !p.pf_tiles ? 2 : 1); multi++) {
+    // After the fork every return joins the side stream back into the
+    // caller's first, so that no kernel of this call that writes the
+    // workspace can still be running once the caller's stream moves on.
+    auto fail = [&](int rc) {
+        if (ss) {
+            (void)hipEventRecord(ss->join, ss->s);
+            (void)hipStreamWaitEvent(s, ss->join, 0);
+        }
+        return rc;
+    };
+#define BM_CHECK_JOIN()                                                   \
+    do {                                                                  \
+        if (hipGetLastError() != hipSuccess) return fail(BITMOE_EHIP);   \
+    } while (0)
+    for (int multi = 0; multi < (T > 1 && !split ? 2 : 1); multi++) {
         auto kg = multi ? (bf ? k_dec_gateup<1, 1> : k_dec_gateup<0, 1>)
                         : (bf ? k_dec_gateup<1, 0> : k_dec_gateup<0, 0>);
         // the timing events, when set, are taken by the dispatch itself
         // around the first gate/up launch
-        const TimingEvents ev = multi ? TimingEvents{} : timing_events();
+        const TimingEvents ev = multi ? TimingEvents{} : timing_for(BITMOE_TIME_GATEUP);
         const int grid = route_mode ? n_gwg : std::min(n_gwg, cu_count());
         hipExtLaunchKernelGGL(kg, dim3(grid), dim3(kWG * 64),
                               multi ? dec_gateup_lds<1>() : dec_gateup_lds<0>(), sg_stream, ev.start, ev.stop, 0, H, I,
@@ -1429,8 +1409,8 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
                               (const uint8_t *)L->up_q, (const uint8_t *)L->grid, x, (const float *)b.logits, b.ids,
                               b.w, b.bk, b.h, b.hsum2, b.hscale, p.kc_sg, (const float *)b.sgp, b.hs,
                               (const int4 *)b.single, (const int32_t *)b.n_single,
-                              (!multi && p.pf_tiles) ? b.gctr : nullptr);
-        BM_LAUNCH_CHECK();
+                              (!multi && split) ? b.gctr : nullptr);
+        BM_CHECK_JOIN();
     }
     // down || shared down; the last workgroup to finish a panel combines it
     // (with the prefill kernels: the down runs on the library stream too,
@@ -1438,29 +1418,37 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     const int n_dwg = p.slots * (H / 64);
     // (beside the prefill kernels the shared down runs on the matrix cores,
     // in a launch of its own on the library stream)
-    const bool sd_mfma = ss && shared && (I / 8 + p.kc_sd - 1) / p.kc_sd <= kSdmPieces;
+    const bool sd_mfma = split && shared && (I / 8 + p.kc_sd - 1) / p.kc_sd <= kSdmPieces;
     if (sd_mfma) {
         k_shared_down_mfma<<<(H / 64) * p.kc_sd, kSdmW * 64, 0, sg_stream>>>(H, I, T, p.kc_sd,
                                                                            (const uint4 *)L->shared_down, b.hs, b.osp);
-        BM_LAUNCH_CHECK();
+        BM_CHECK_JOIN();
     }
     const int n_sd = shared && !sd_mfma ? (H / 64) * p.kc_sd : 0;
-    k_dec_down<0><<<n_dwg + n_sd, kWD * 64, 0, sg_stream>>>(
-        H, I, k, T, n_dwg, p.kc_sd, p.pf_tiles ? b.bk.n_tiles : nullptr, ss ? 0 : 1, (const uint8_t *)L->down_q,
-        (const uint4 *)L->shared_down, b.bk.counts, b.bk.offsets, b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum2,
-        b.hscale, b.hs, b.w, b.ycount, shared ? b.osp : nullptr, b.o, b.y);
-    BM_LAUNCH_CHECK();
-    if (ss) {
-        if (hipEventRecord(ss->join, ss->s) != hipSuccess) return BITMOE_EHIP;
+    {
+        const TimingEvents ev = timing_for(BITMOE_TIME_DOWN);
+        hipExtLaunchKernelGGL(k_dec_down<0>, dim3(n_dwg + n_sd), dim3(kWD * 64), 0, sg_stream, ev.start, ev.stop, 0,
+                              H, I, k, T, n_dwg, p.kc_sd, (const int32_t *)(split ? b.bk.n_tiles : nullptr),
+                              split ? 0 : 1, (const uint8_t *)L->down_q, (const uint4 *)L->shared_down,
+                              (const int32_t *)b.bk.counts, (const int32_t *)b.bk.offsets, (const int32_t *)b.bk.perm,
+                              (const int32_t *)b.bk.active, (const int32_t *)b.bk.n_active, (const uint16_t *)b.h,
+                              (const float2 *)b.hsum2, (const float *)b.hscale, (const uint16_t *)b.hs,
+                              (const float *)b.w, b.ycount, shared ? b.osp : nullptr, b.o, b.y);
+        BM_CHECK_JOIN();
+    }
+    if (split) {
+        if (ss && hipEventRecord(ss->join, ss->s) != hipSuccess) return fail(BITMOE_EHIP);
         const int rc = launch_prefill_routed(L, x, x_dtype, T, b.bk, p.pf_tiles, b.pf, s);
-        if (rc) return rc;
-        if (hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return BITMOE_EHIP;
+        if (rc) return fail(rc);
+        if (ss && hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return fail(BITMOE_EHIP);
+        ss = nullptr;                                    // joined
         const int64_t n = (int64_t)T * H;
         k_dec_combine<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(H, k, T, shared ? p.kc_sd : 0, b.o, b.w,
                                                                   shared ? b.osp : nullptr, b.y);
         BM_LAUNCH_CHECK();
     }
-    if (T > 1 && !p.pf_tiles) {
+#undef BM_CHECK_JOIN
+    if (T > 1 && !split) {
         k_dec_down<1><<<n_dwg, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, nullptr, 1, (const uint8_t *)L->down_q,
                                                 (const uint4 *)L->shared_down, b.bk.counts, b.bk.offsets,
                                                 b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum2, b.hscale, b.hs,

@@ -174,8 +174,8 @@ BM_DEV int topk_wave4(float (&v)[4], int E, int k, int32_t *__restrict__ ids, fl
     return pi;
 }
 
-constexpr int kBT = 1024;           // threads per bucketing block = pairs per chunk
-constexpr int kBW = kBT / 64;       // waves per block
+using bm_cfg::kBT;                  // threads per bucketing block = pairs per chunk
+using bm_cfg::kBW;                  // waves per block
 
 BM_DEV int key_bits(int E) {        // bits needed for keys 0..E (E = "no pair")
     int b = 1;
@@ -282,7 +282,7 @@ BM_DEV void active_and_tiles(const int *scount, int E, int32_t *__restrict__ act
 // first; perm[rank] = pair, and the keys in sorted order into LDS sk[].
 // Stage 2 (after a block barrier): the ascending active list, and counts
 // and offsets of the active experts only (other entries are not written).
-constexpr int kWaveBucketMax = 128;
+using bm_cfg::kWaveBucketMax;
 
 BM_DEV void bucket_wave_rank(const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ perm,
                              int *sk) {

@@ -1,0 +1,72 @@
+// Launch planning: how a call is split into launches and how much scratch it
+// needs.  Host code only (no kernels), shared by the C ABI's validation and
+// workspace sizing and by the launchers.
+#include <algorithm>
+#include <atomic>
+
+#include "host.h"
+
+namespace bm_host {
+
+using namespace bm_cfg;
+
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+size_t bucket_scratch_bytes(int T, int k, int E) {
+    const int64_t n = (int64_t)T * k;
+    if (n <= kSmallPairs) return 256;
+    const int64_t nblk = (n + kBT - 1) / kBT;
+    return (size_t)(nblk * E * 4 + 255) / 256 * 256;
+}
+
+size_t router_mfma_part_floats(int T, int E) { return (size_t)kRouterSplit * T * E; }
+
+bool route_uses_mfma(int T, int x_dtype) { return T >= kMfmaRouterMinT && x_dtype == BITMOE_BF16; }
+
+size_t route_ws_bytes(const bitmoe_layer *L, int T, int x_dtype) {
+    const size_t floats = route_uses_mfma(T, x_dtype) ? router_mfma_part_floats(T, L->E)
+                                                     : (size_t)std::min(T, kRouterNT) * L->E;
+    return (floats * 4 + 255) / 256 * 256;
+}
+
+DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
+    DecodePlan p;
+    const bool shared = L->shared_gate != nullptr;
+    p.slots = (int)std::min<int64_t>(L->E, (int64_t)T * L->k);
+    p.n_rwg = with_router ? (L->E + kFrontWaves - 1) / kFrontWaves : 0;
+    // the shared gate/up's K chunks: as many as fit the compute units
+    // beside the router workgroups (one front workgroup per CU), at most 8
+    p.kc_sg = shared ? std::max(1, std::min(kMaxChunks, (cu_count() - p.n_rwg) / (L->I / 64))) : 0;
+    p.kc_sd = shared ? std::max(1, (L->I + kSharedChunkCols - 1) / kSharedChunkCols) : 0;
+    p.small = (int64_t)T * L->k <= kWaveBucketMax;
+    // one token: every gate/up workgroup routes it itself; more tokens: one
+    // routing launch, so that the gate/up workgroups can each take several
+    // (expert, panel) items
+    p.need_mid = !p.small || T > 1;
+    // several tokens (one row tile per expert): experts chosen by more than
+    // one token go through the prefill kernels, which decode each weight once
+    // for all of its tokens on the matrix cores
+    p.pf_tiles = (p.small && T > 1 && T <= kPfRows) ? (int)std::min<int64_t>(L->E, (int64_t)T * L->k / 2) : 0;
+    return p;
+}
+
+TimingEvents &timing_events() {
+    thread_local TimingEvents ev;
+    return ev;
+}
+
+TimingEvents timing_for(int which) {
+    const TimingEvents &ev = timing_events();
+    return ev.which == which ? ev : TimingEvents{};
+}
+
+}  // namespace bm_host

@@ -54,7 +54,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfRows = 96;                   // rows per tile (3 blocks of 32)
+using bm_cfg::kPfRows;                        // rows per tile (3 blocks of 32)
 constexpr int kPfHalf = 128;                  // K per LDS stage
 // Activation stage in LDS, chunk-major: 16-byte chunk c (8 K values) of row m
 // at (c * kPfRows + m) * 16.  An MFMA operand read (16 lanes = 16 rows of one
@@ -70,12 +70,19 @@ constexpr int kPfTabBytes = kPfMagBytes + kPfSgnBytes;
 constexpr int kPfABytes = kPfRows * kPfHalf * 2;
 constexpr int kPfGuLds = kPfTabBytes + 2 * kPfABytes + kPfRows * (4 + 4 + 4) + kPfWaves * kPfRows * 4;
 constexpr int kPfDnLds = 2 * kPfABytes + kPfRows * (4 + 4);
-// fp16 weight operands carry a factor 2^kPfWShift, removed in the fp32
-// epilogues: with it a superblock scale d in [2^-19, 8] keeps every nonzero
-// weight in fp16's normal range (smallest IQ2X weight d/8, largest 27 d; Q2K
-// at most 45 d + 15 dmin), where quantised layers' scales sit.
+// fp16 weight operands carry a factor 2^kPfWShift (IQ2X) or 2^kPfDnWShift
+// (Q2K), removed in the fp32 epilogues: with it a superblock scale d (and
+// dmin) in [2^-19, 8] keeps every nonzero weight in fp16's normal range and
+// below its largest finite value.  IQ2X weights lie in [d/8, 217 d/8] (group
+// scale (0.5+s)/4 <= 31/8, magnitude <= 7): times 2^8, [2^-14, 55552] at the
+// ends of the range.  Q2K terms d sc q <= 45 d and dmin m <= 15 dmin: times
+// 2^7, at most 46080, and the smallest nonzero term d sc (or dmin m) is
+// 2^-12; a q - b is formed in one fused fp16 operation, so its only
+// rounding is that of the result.
 constexpr int kPfWShift = 8;
 constexpr float kPfWScale = 256.f;
+constexpr int kPfDnWShift = 7;
+constexpr float kPfDnWScale = 128.f;
 
 BM_DEV uint32_t h2u(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 BM_DEV f16x2 u2h(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
@@ -532,8 +539,8 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
                 const uint32_t W = wsel[s >> 1], W10 = W >> 10;
                 // (a, -b) of this sub-block: a = d sc, b = dmin m
                 const uint32_t sb = (sl.sc[j] >> (8 * (s >> 1))) & 0xFFu;
-                const f16x2 av = u2h(f16_pair(kPfWScale * fp16_to_f32(sl.dd[j] & 0xFFFFu) * (float)(sb & 15u)));
-                const f16x2 bv = u2h(f16_pair(-kPfWScale * fp16_to_f32(sl.dd[j] >> 16) * (float)(sb >> 4)));
+                const f16x2 av = u2h(f16_pair(kPfDnWScale * fp16_to_f32(sl.dd[j] & 0xFFFFu) * (float)(sb & 15u)));
+                const f16x2 bv = u2h(f16_pair(-kPfDnWScale * fp16_to_f32(sl.dd[j] >> 16) * (float)(sb >> 4)));
                 uint32_t qb[4];
                 if ((s & 1) == 0) {
                     qb[0] = pc.pair<0>(W, W10); qb[1] = pc.pair<1>(W, W10);
@@ -606,7 +613,7 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
         for (int r = 0; r < 16; r++) {
             const int m = 32 * i + acc_row(r, kh);
             if (m < t.rows) {
-                const int e = semax[m] - kPfWShift;
+                const int e = semax[m] - kPfDnWShift;
                 float *op = a.o + (int64_t)a.perm[t.off + t.r0 + m] * a.H;
                 op[c0] = ldexpf(acc[i][0][r], e);
                 op[c0 + 32] = ldexpf(acc[i][1][r], e);
@@ -721,8 +728,6 @@ k_combine_p(const float *__restrict__ o, const float *__restrict__ w, const floa
 
 namespace bm_host {
 
-int prefill_tile_rows() { return kPfRows; }
-
 int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int T, const Buckets &b,
                           int max_tiles, const PrefillBufs &pb, hipStream_t s) {
     const int H = L->H, I = L->I, k = L->k;
@@ -743,7 +748,7 @@ int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int
         GuArgs a{H, I, k, (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q, (const uint8_t *)L->grid,
                  pb.x16, pb.xsc, b.counts, b.offsets, b.perm, b.tiles, b.n_tiles, pb.h, pb.hexp};
         // the timing events, when set, are taken by the dispatch itself
-        const TimingEvents ev = timing_events();
+        const TimingEvents ev = timing_for(BITMOE_TIME_GATEUP);
         hipExtLaunchKernelGGL(k_pf_gateup, dim3(pf_grid(max_tiles, I / kPfGuCols)), dim3(kPfThreads), kPfGuLds, s,
                               ev.start, ev.stop, 0, a);
         BM_LAUNCH_CHECK();
@@ -751,7 +756,9 @@ int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int
     {
         DnArgs a{H, I, (const uint8_t *)L->down_q, pb.h, pb.hexp, b.counts, b.offsets, b.perm, b.tiles,
                  b.n_tiles, pb.o};
-        k_pf_down<<<pf_grid(max_tiles, (H + kPfDnCols - 1) / kPfDnCols), kPfThreads, kPfDnLds, s>>>(a);
+        const TimingEvents ev = timing_for(BITMOE_TIME_DOWN);
+        hipExtLaunchKernelGGL(k_pf_down, dim3(pf_grid(max_tiles, (H + kPfDnCols - 1) / kPfDnCols)), dim3(kPfThreads),
+                              kPfDnLds, s, ev.start, ev.stop, 0, a);
         BM_LAUNCH_CHECK();
     }
     return BITMOE_OK;

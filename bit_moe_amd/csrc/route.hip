@@ -12,7 +12,7 @@ namespace {
 
 using namespace bm;
 
-constexpr int kRouterNT = 16;   // tokens per launch of the small-T router
+using bm_cfg::kRouterNT;       // tokens per launch of the small-T router
 
 // ---------------------------------------------------------------------------
 // Small-T router: one wave per expert row, lanes across K (16-byte pieces,
@@ -46,7 +46,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // Split-K: workgroup (token tile of 64, expert tile of 256, K slice s)
 // writes its partial sums to part[s][t][e]; k_topk_sum adds the slices in a
 // fixed order (deterministic).  Four waves, each 64 tokens x 64 experts.
-constexpr int kRouterSplit = 8;
+using bm_cfg::kRouterSplit;
 __global__ void __launch_bounds__(256)
 k_router_splitk(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, int T, int H, int E, int kslice,
                 float *__restrict__ part) {
@@ -147,8 +147,6 @@ k_topk(const float *__restrict__ logits, int T, int E, int k, int32_t *__restric
 
 namespace bm_host {
 
-int router_tokens_per_launch() { return kRouterNT; }
-
 int launch_router_gemv(const bitmoe_layer *L, const void *x, int x_dtype, int T, float *logits,
                        hipStream_t s) {
     dim3 g((L->E + 3) / 4);
@@ -159,8 +157,6 @@ int launch_router_gemv(const bitmoe_layer *L, const void *x, int x_dtype, int T,
     BM_LAUNCH_CHECK();
     return BITMOE_OK;
 }
-
-size_t router_mfma_part_floats(int T, int E) { return (size_t)kRouterSplit * T * E; }
 
 int launch_router_mfma(const bitmoe_layer *L, const void *x, int T, float *logits, int32_t *ids, float *w,
                        float *part, hipStream_t s) {

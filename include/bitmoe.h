@@ -31,11 +31,15 @@
  *  - Shapes: H (hidden) and I (expert intermediate) must be multiples of
  *    256; 1 <= k <= 16; k <= E <= 1024; T >= 0 (T = 0 is a no-op).
  *  - Calls are thread-safe; calls on different streams may overlap.
- *  - moe_ffn_decode / moe_forward_decode on a batch in which some expert is
- *    chosen by several tokens (2 <= T, T*k <= 128, T <= 96) fork part of the
- *    work onto a stream the library keeps per device (created on the first
- *    such call, default priority) and join it back into `stream` before the
- *    call's last kernel: the call is still ordered on `stream` as a whole.
+ *  - The one piece of library state: moe_ffn_decode / moe_forward_decode on
+ *    a batch in which some expert is chosen by several tokens (2 <= T,
+ *    T*k <= 128, T <= 96) fork part of the work onto a stream the library
+ *    keeps per device (created on the first such call, default priority,
+ *    with two events) and join it back into `stream` before the call's last
+ *    kernel, also when a launch fails after the fork: the call is ordered
+ *    on `stream` as a whole.  Such calls from several host threads take
+ *    turns at that stream (a lock held while the call queues its work), so
+ *    their side-stream halves run one after another.
  *
  * Weight formats
  *  CANONICAL blocks (the interchange format, GGML order):
@@ -55,7 +59,8 @@
  *   A projection with N outputs and K inputs stores block (n, kb) at index
  *   n*(K/256) + kb; experts are stacked on a leading axis [E].
  *
- *  TILED layout (what the FFN entry points read; moe_pack_* produces it).
+ *  TILED layout (what the FFN entry points read; moe_pack_* produces it;
+ *  bitmoe_layer.layout says which of the two a descriptor's blocks are in).
  *   The same information in the same number of bytes, regrouped into 64-row
  *   panels so that 64 lanes reading one 16-byte piece of 64 consecutive rows
  *   issue one contiguous 1 KiB access.
@@ -105,7 +110,18 @@ extern "C" {
 #define BITMOE_DECODE  0
 #define BITMOE_PREFILL 1
 
-/* One routed-MoE layer.  All pointers are device pointers. */
+#define BITMOE_LAYOUT_CANONICAL 0   /* GGML block order (the interchange format) */
+#define BITMOE_LAYOUT_TILED     1   /* 64-row panels (moe_pack_*), read by the FFN calls */
+
+#define BITMOE_TIME_GATEUP 0        /* moe_set_timing_events: the routed gate/up kernel */
+#define BITMOE_TIME_DOWN   1        /* moe_set_timing_events: the routed down kernel */
+
+/*
+ * One routed-MoE layer.  All pointers are device pointers.  The FFN entry
+ * points read TILED blocks and return BITMOE_EUNSUPPORTED for a descriptor
+ * whose layout is BITMOE_LAYOUT_CANONICAL (convert with moe_pack_* first);
+ * moe_route and moe_topk read only the router, in either case.
+ */
 typedef struct bitmoe_layer {
     int32_t H;                 /* hidden size (multiple of 256) */
     int32_t I;                 /* expert intermediate size (multiple of 256) */
@@ -121,10 +137,18 @@ typedef struct bitmoe_layer {
     const void *shared_gate;   /* TILED bf16 [I][H], or NULL: no shared expert */
     const void *shared_up;     /* TILED bf16 [I][H] (NULL iff shared_gate is) */
     const void *shared_down;   /* TILED bf16 [H][I] (NULL iff shared_gate is) */
+    int32_t layout;            /* BITMOE_LAYOUT_TILED or BITMOE_LAYOUT_CANONICAL:
+                                  the layout of gate_q, up_q, down_q and the
+                                  shared matrices */
 } bitmoe_layer;
 
 /*
- * Routing (router logits, top-k, renormalised softmax).
+ * Routing (router logits, top-k, renormalised softmax).  The router picks a
+ * few experts for every token ("Un modele de 284 milliards de parametres
+ * tourne desormais sur un Mac de 128 Go. Qui y perd ?", section "Comment un
+ * modele de 284 milliards de parametres tient sur une seule machine"); it
+ * stays unquantised ("antirez/ds4 - Moteur local d'inference DeepSeek V4
+ * Flash pour Metal", section "Poids du modele").
  * x: [T][H] of x_dtype (BITMOE_F32 or BITMOE_BF16).
  * logits (may be NULL): float32 [T][E], logits[t][e] = sum_h x[t][h]*W[e][h]
  *   accumulated in fp32.
@@ -134,18 +158,29 @@ typedef struct bitmoe_layer {
  * ws: device scratch of at least moe_route_workspace_bytes(L, T, x_dtype)
  *   bytes, 256-byte aligned (partial sums of the split-K router; results do
  *   not depend on scheduling: the splits are added in a fixed order).
+ * Errors: EINVAL (null x/ids/w or router, bad dtype, T < 0, x not 16-byte
+ * aligned), EUNSUPPORTED (shape), EWORKSPACE, EHIP.
  */
 size_t moe_route_workspace_bytes(const bitmoe_layer *L, int T, int x_dtype);
 int moe_route(const bitmoe_layer *L, const void *x, int x_dtype, int T,
               float *logits, int32_t *ids, float *w, void *ws, size_t ws_bytes,
               void *stream);
 
-/* Top-k + renormalised softmax of given float32 logits [T][E]. */
+/*
+ * Top-k + renormalised softmax of given float32 logits [T][E] (the second
+ * half of moe_route, same passage): ids int32 [T][k], w float32 [T][k] as
+ * in moe_route.  Errors: EINVAL (null pointer, T < 0, E or k < 1),
+ * EUNSUPPORTED (k > 16, k > E, E > 1024), EHIP.
+ */
 int moe_topk(const float *logits, int T, int E, int k, int32_t *ids,
              float *w, void *stream);
 
 /*
- * Token->expert bucketing.  ids int32 [T][k] with values in [0,E) (trusted).
+ * Token->expert bucketing, so that each chosen expert's weights are streamed
+ * once per call: decode is bound by memory bandwidth ("Faire tenir un MoE de
+ * 284B dans un portable de 128 Go", section "Un pre-remplissage a 790 t/s
+ * revele le veritable goulot d'etranglement").
+ * ids int32 [T][k] with values in [0,E) (trusted).
  * counts int32 [E]; offsets int32 [E+1] exclusive prefix sum of counts;
  * perm int32 [T*k]: pair indices p = t*k + j grouped by expert, ascending p
  * within each expert; active int32 [E]: experts with counts > 0 ascending,
@@ -157,11 +192,22 @@ int moe_bucket(const int32_t *ids, int T, int k, int E, int32_t *counts,
                int32_t *offsets, int32_t *perm, int32_t *active,
                int32_t *n_active, void *ws, size_t ws_bytes, void *stream);
 
-/* Bytes of workspace moe_ffn_decode / moe_ffn_prefill need for T tokens. */
+/*
+ * Bytes of workspace moe_ffn_decode / moe_forward_decode (mode
+ * BITMOE_DECODE) or moe_ffn_prefill (BITMOE_PREFILL) need for T tokens; 0
+ * for an invalid layer, T or mode.
+ */
 size_t moe_workspace_bytes(const bitmoe_layer *L, int T, int mode);
 
 /*
- * The MoE FFN: y[t] = sum_j w[t][j] * D_e(silu(G_e x_t) * U_e x_t)
+ * The MoE FFN, with the routed experts' up/gate in IQ2_XXS and down in Q2_K
+ * and the shared expert unquantised ("ds4 : analyse pratique pour un usage
+ * documente", section "Support de modeles et choix de quantification";
+ * "antirez/ds4 ...", section "Poids du modele"); decode is bound by memory
+ * bandwidth, prefill by compute ("Faire tenir un MoE de 284B ...", section
+ * "Un pre-remplissage a 790 t/s revele le veritable goulot
+ * d'etranglement"):
+ *         y[t] = sum_j w[t][j] * D_e(silu(G_e x_t) * U_e x_t)
  *                     (+ D_s(silu(G_s x_t) * U_s x_t) when the layer has a
  *                     shared expert), e = ids[t][j], silu(z) = z/(1+e^-z).
  * x [T][H] (x_dtype), ids int32 [T][k] (values in [0,E), trusted; each row
@@ -179,6 +225,9 @@ size_t moe_workspace_bytes(const bitmoe_layer *L, int T, int mode);
  * dmin m for Q2K) with a fixed factor 2^8, so full fp16 precision holds for
  * superblock scales d, dmin in [2^-19, 8] (codebook magnitudes up to 7);
  * larger scales can overflow.
+ * Errors: EINVAL (null x/ids/w/y or quantised weights, a shared matrix
+ * without the other two, bad dtype, T < 0, x or y not 16-byte aligned),
+ * EUNSUPPORTED (shape, or a CANONICAL layout), EWORKSPACE, EHIP.
  */
 int moe_ffn_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T,
                    const int32_t *ids, const float *w, float *y, void *ws,
@@ -188,23 +237,31 @@ int moe_ffn_prefill(const bitmoe_layer *L, const void *x, int x_dtype, int T,
                     size_t ws_bytes, void *stream);
 
 /*
- * The whole layer for a decode batch: moe_route followed by moe_ffn_decode
- * in one call.  For T <= 16 and T*k <= 128 the router rows, the shared expert
+ * The whole layer for a decode batch (the passages of moe_route and
+ * moe_ffn_decode): moe_route followed by moe_ffn_decode in one call.  For T <= 16 and T*k <= 128 the router rows, the shared expert
  * and the bookkeeping share launches with the expert GEMVs (three launches
  * in all; more for larger batches).
  * ids int32 [T][k] and w float32 [T][k] receive the routing (same values as
  * moe_route); y float32 [T][H] as moe_ffn_decode.  Needs L->router_w.
- * ws: at least moe_workspace_bytes(L, T, BITMOE_DECODE) bytes.
+ * ws: at least moe_workspace_bytes(L, T, BITMOE_DECODE) bytes (which
+ * includes the router's scratch for batches routed in a launch of their
+ * own).  Errors: those of moe_ffn_decode, and EINVAL without a router.
  */
 int moe_forward_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T,
                        int32_t *ids, float *w, float *y, void *ws,
                        size_t ws_bytes, void *stream);
 
 /*
- * Standalone dequantisation of CANONICAL blocks: nblocks blocks ->
+ * Standalone dequantisation of CANONICAL blocks (GGML's GGUF block layouts:
+ * "antirez/ds4 ...", section "Remerciements a llama.cpp et GGML"; the two
+ * formats: "ds4 : analyse pratique ...", section "Support de modeles et
+ * choix de quantification"): nblocks blocks ->
  * out [nblocks*256] of out_dtype.  BITMOE_F32 output is the exact value
  * (IQ2X) or the single fp32 rounding of d*scale*q - dmin*min (Q2K);
  * BITMOE_BF16 output is that fp32 value rounded to nearest-even.
+ * Errors: EINVAL (null or misaligned pointer: blocks 2-byte (IQ2X) or
+ * 4-byte (Q2K), grid 8-byte, out 16-byte aligned; nblocks < 0; bad dtype),
+ * EHIP.
  */
 int moe_dequant_iq2x(const void *blocks, const void *grid, int64_t nblocks,
                      void *out, int out_dtype, void *stream);
@@ -214,7 +271,10 @@ int moe_dequant_q2k(const void *blocks, int64_t nblocks, void *out,
 /*
  * Load-time layout transforms (canonical -> TILED, see above), E experts of
  * an [N][K] projection; N multiple of 64, K multiple of 256 (bf16: of 8).
- * src and dst must not overlap.
+ * The canonical order is GGML's ("antirez/ds4 ...", section "Remerciements
+ * a llama.cpp et GGML"); the tiled one is this library's, with the same
+ * bytes.  src and dst must not overlap.  Errors: EINVAL (null or misaligned
+ * pointer, negative size), EUNSUPPORTED (N or K not a multiple), EHIP.
  */
 int moe_pack_iq2x(const void *src, void *dst, int E, int N, int K, void *stream);
 int moe_pack_q2k(const void *src, void *dst, int E, int N, int K, void *stream);
@@ -223,14 +283,16 @@ int moe_pack_bf16(const void *src, void *dst, int N, int K, void *stream);
 /*
  * Measurement hook.  When start and stop are both hipEvent_t handles (passed
  * as void*), every later decode or prefill FFN call made from the calling
- * thread launches its routed gate/up projection kernel with hipExtLaunchKernel
- * and these events, which the dispatch itself takes when the kernel starts
- * and when it ends, so hipEventElapsedTime gives that kernel's duration
- * (for a decode batch with experts chosen by several tokens, the first of
- * its two gate/up launches).  Pass NULL, NULL to turn it off.  The setting
- * is per host thread.
+ * thread launches one kernel with hipExtLaunchKernel and these events, which
+ * the dispatch itself takes when the kernel starts and when it ends, so
+ * hipEventElapsedTime gives that kernel's duration.  which: BITMOE_TIME_GATEUP
+ * (the routed gate/up kernel; for a decode batch with experts chosen by
+ * several tokens, the single-token experts' one) or BITMOE_TIME_DOWN (the
+ * routed down kernel; for decode, the one that also runs the shared down).
+ * Pass NULL, NULL to turn it off.  The setting is per host thread.
+ * Errors: EINVAL (one event without the other, unknown which).
  */
-int moe_set_timing_events(void *start, void *stop);
+int moe_set_timing_events(void *start, void *stop, int which);
 
 const char *moe_strerror(int code);
 const char *moe_version(void);

@@ -40,10 +40,11 @@ def test_strerror_names_every_code():
 def _layer(H=256, I=512, E=8, k=2, shared=False, **kw):
     d = dict(H=H, I=I, E=E, k=k, router_w=16, gate_q=16, up_q=16, down_q=16, grid=16,
              shared_gate=16 if shared else None, shared_up=16 if shared else None,
-             shared_down=16 if shared else None)
+             shared_down=16 if shared else None, layout=_lib.LAYOUT_TILED)
     d.update(kw)
     return _lib.LayerStruct(d["H"], d["I"], d["E"], d["k"], d["router_w"], d["gate_q"], d["up_q"],
-                            d["down_q"], d["grid"], d["shared_gate"], d["shared_up"], d["shared_down"])
+                            d["down_q"], d["grid"], d["shared_gate"], d["shared_up"], d["shared_down"],
+                            d["layout"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -104,6 +105,48 @@ def test_ffn_argument_checks(fn):
     assert f(C.byref(half), 16, 1, 4, 16, 16, 16, 256, need, None) == _lib.EINVAL
     nog = _layer(gate_q=None)
     assert f(C.byref(nog), 16, 1, 4, 16, 16, 16, 256, need, None) == _lib.EINVAL
+    # the FFN kernels read tiled blocks: a canonical descriptor is refused,
+    # an unknown layout tag is invalid
+    canon = _layer(layout=_lib.LAYOUT_CANONICAL)
+    assert f(C.byref(canon), 16, 1, 4, 16, 16, 16, 256, need, None) == _lib.EUNSUPPORTED
+    assert L.moe_workspace_bytes(C.byref(canon), 4, mode) == 0
+    bad = _layer(layout=7)
+    assert f(C.byref(bad), 16, 1, 4, 16, 16, 16, 256, need, None) == _lib.EINVAL
+
+
+def test_forward_decode_checks_layout_and_router():
+    L = bm.lib()
+    need = L.moe_workspace_bytes(C.byref(_layer()), 4, 0)
+    canon = _layer(layout=_lib.LAYOUT_CANONICAL)
+    assert L.moe_forward_decode(C.byref(canon), 16, 1, 4, 16, 16, 16, 256, need, None) == _lib.EUNSUPPORTED
+    norouter = _layer(router_w=None)
+    assert L.moe_forward_decode(C.byref(norouter), 16, 1, 4, 16, 16, 16, 256, need, None) == _lib.EINVAL
+    # routing reads only the router: a canonical descriptor routes
+    rneed = L.moe_route_workspace_bytes(C.byref(canon), 4, 0)
+    assert L.moe_route(C.byref(canon), 16, 0, 0, None, 16, 16, 256, rneed, None) == 0
+
+
+@pytest.mark.parametrize("T", [17, 64, 200])
+@pytest.mark.parametrize("x_dtype", [0, 1])
+def test_forward_decode_workspace_covers_its_router(T, x_dtype):
+    """Batches above the fused-router size are routed by moe_route inside
+    moe_forward_decode; the decode workspace must hold that router's scratch
+    for either activation dtype (bf16 from 64 tokens takes the split-K
+    matrix-core router, eight partial sums per logit)."""
+    L = bm.lib()
+    lay = _layer(H=7168, I=2048, E=256, k=8, shared=True)
+    ws = L.moe_workspace_bytes(C.byref(lay), T, 0)
+    assert ws >= L.moe_route_workspace_bytes(C.byref(lay), T, x_dtype)
+    if x_dtype == 1 and T >= 64:
+        assert ws >= 8 * T * 256 * 4
+
+
+def test_timing_event_selector_checks():
+    L = bm.lib()
+    assert L.moe_set_timing_events(None, None, _lib.TIME_GATEUP) == 0
+    assert L.moe_set_timing_events(None, None, _lib.TIME_DOWN) == 0
+    assert L.moe_set_timing_events(None, None, 2) == _lib.EINVAL
+    assert L.moe_set_timing_events(16, None, 0) == _lib.EINVAL
 
 
 def test_workspace_sizes_grow_with_tokens_and_shared():

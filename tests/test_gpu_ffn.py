@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from _gpu import (assert_close_rms, device_layer, near_tie_tokens, require_gpu, say, synth_layer,
+from _gpu import (W_TOL, assert_close_rms, device_layer, near_tie_tokens, require_gpu, say, synth_layer,
                   torch, x_to_device)
 
 pytestmark = pytest.mark.gpu
@@ -87,21 +87,49 @@ def test_decode_b16_zipf_full():
     assert_close_rms(y, ref, what="decode_b16_zipf")
 
 
-def _sample_rows(ids, n_random, seed):
-    """Random tokens plus tokens routed to the hottest and coldest experts."""
+PF_TILE_ROWS = 96      # rows per prefill row tile (blocks of 32 rows)
+
+
+def _sample_rows(ids, E, n_random, seed):
+    """Tokens whose rows cover the prefill tile classes: one row from every
+    row tile of the hottest and the coldest expert (first rows, and the last
+    row of the expert), the last row of partial tails holding 1-32, 33-64
+    and 65-96 rows (one, two and three 32-row blocks) for two experts each,
+    plus n_random random tokens.  Row r of expert e is bucket slot
+    offsets[e] + r (the oracle's bucketing), pair perm[slot], token pair // k."""
     rng = np.random.default_rng(seed)
-    T = ids.shape[0]
-    c = np.bincount(ids.ravel())
-    hot, cold = int(np.argmax(c)), int(np.argmin(np.where(c > 0, c, c.max() + 1)))
-    t_hot = np.nonzero((ids == hot).any(axis=1))[0]
-    t_cold = np.nonzero((ids == cold).any(axis=1))[0]
-    rows = set(rng.choice(T, size=n_random, replace=False).tolist())
-    rows |= {int(t_hot[0]), int(t_hot[-1]), int(t_cold[0]), 0, T - 1}
+    T, k = ids.shape
+    counts, offsets, perm = oracle.bucket(ids, E)
+    tok_of = lambda e, r: int(perm[offsets[e] + r]) // k
+    used = np.nonzero(counts)[0]
+    hot = int(used[np.argmax(counts[used])])
+    cold = int(used[np.argmin(counts[used])])
+    rows = set()
+    for e in (hot, cold):
+        c = int(counts[e])
+        rows |= {tok_of(e, r0) for r0 in range(0, c, PF_TILE_ROWS)}
+        rows.add(tok_of(e, c - 1))
+    classes = {1: [], 2: [], 3: []}
+    for e in used:
+        tail = int(counts[e]) % PF_TILE_ROWS or PF_TILE_ROWS
+        classes[(tail + 31) // 32].append(int(e))
+    for mb, es in classes.items():
+        for e in es[:2]:
+            c = int(counts[e])
+            rows |= {tok_of(e, c - 1), tok_of(e, (c - 1) // PF_TILE_ROWS * PF_TILE_ROWS)}
+    rows |= set(rng.choice(T, size=n_random, replace=False).tolist()) | {0, T - 1}
+    say(f"[sample] hot e{hot} ({counts[hot]} rows, {(counts[hot] + PF_TILE_ROWS - 1) // PF_TILE_ROWS} tiles), "
+        f"cold e{cold} ({counts[cold]} rows), tail classes "
+        f"{ {mb: len(es) for mb, es in classes.items()} }, {len(rows)} tokens")
     return np.array(sorted(rows))
 
 
 @pytest.mark.parametrize("name", ["prefill_2k", "prefill_8k_zipf"])
 def test_prefill_full_size_sampled(name):
+    """Full-size prefill chunks at the launch configuration the bench times,
+    compared on at least 64 tokens the oracle computes one by one, chosen
+    to reach every row tile of the hottest and coldest expert and every
+    tile size class."""
     require_gpu()
     w = synth.WORKLOADS[name]
     x, _ = synth.make_tokens(w)
@@ -109,9 +137,10 @@ def test_prefill_full_size_sampled(name):
     c = np.bincount(ids.ravel(), minlength=w.E)
     say(f"[ffn] {name} rows/expert max={c.max()} min={c.min()} active={np.count_nonzero(c)}")
     y = _gpu_ffn(w, x, ids, wt, "prefill")
-    rows = _sample_rows(ids, 6, 1)
+    rows = _sample_rows(ids, w.E, 56, 1)
+    assert len(rows) >= 64
     ref = _oracle_rows(w, x, ids, wt, rows)
-    assert_close_rms(y[rows], ref, what=f"{name} rows {rows.tolist()}")
+    assert_close_rms(y[rows], ref, what=f"{name} {len(rows)} sampled tokens")
     assert np.all(np.isfinite(y))
 
 
@@ -195,10 +224,12 @@ def test_end_to_end_route_then_ffn():
     assert_close_rms(y.cpu().numpy(), ref, what="route+decode")
 
 
-@pytest.mark.parametrize("T", [1, 4, 16, 20])
+@pytest.mark.parametrize("T", [1, 4, 16, 20, 64, 200])
 def test_forward_decode_routes_and_matches_oracle(T):
     """moe_forward_decode (router fused into the first launch for T <= 16,
-    separate routing above) against oracle routing + FFN."""
+    separate routing above: the one-wave-per-row router below 64 bf16
+    tokens, the split-K matrix-core router from 64) against oracle routing
+    + FFN."""
     require_gpu()
     import bit_moe_amd as bm
     w0 = synth.WORKLOADS["decode_b1"]
@@ -210,8 +241,8 @@ def test_forward_decode_routes_and_matches_oracle(T):
     torch.cuda.synchronize()
     rid, rw = oracle.route(x, L.router(), w.k)
     np.testing.assert_array_equal(gid.cpu().numpy(), rid)
-    np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=1e-5)
-    ref = oracle.layer_ffn(L, x, rid, gw.cpu().numpy().astype(np.float64))
+    np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=W_TOL)
+    ref = oracle.layer_ffn(L, x, rid, rw)
     assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode T={T}")
 
 
@@ -229,8 +260,8 @@ def test_forward_decode_small_expert_count(T):
     torch.cuda.synchronize()
     rid, rw = oracle.route(x, L.router(), w.k)
     np.testing.assert_array_equal(gid.cpu().numpy(), rid)
-    np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=1e-5)
-    ref = oracle.layer_ffn(L, x, rid, gw.cpu().numpy().astype(np.float64))
+    np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=W_TOL)
+    ref = oracle.layer_ffn(L, x, rid, rw)
     assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode E=8 T={T}")
 
 
@@ -249,7 +280,8 @@ def test_forward_decode_all_experts_shared_by_tokens(shared):
     torch.cuda.synchronize()
     rid, rw = oracle.route(x, L.router(), w.k)
     np.testing.assert_array_equal(gid.cpu().numpy(), rid)
-    ref = oracle.layer_ffn(L, x, rid, gw.cpu().numpy().astype(np.float64))
+    np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=W_TOL)
+    ref = oracle.layer_ffn(L, x, rid, rw)
     assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode 4 equal tokens shared={shared}")
 
 
@@ -266,3 +298,45 @@ def test_forward_decode_zero_input_ties(T):
     assert gid.cpu().numpy().tolist() == [list(range(w.k))] * T
     np.testing.assert_allclose(gw.cpu().numpy(), 1.0 / w.k, atol=1e-7)
     assert not np.any(y.cpu().numpy())
+
+
+def _scaled_layer_case(w, d_of_block):
+    """The tiny layer's canonical blocks with every superblock scale (IQ2X d;
+    Q2K d and dmin) replaced by d_of_block(n) (fp16 values), uploaded and
+    packed; returns (device layer, gate, up, down per expert)."""
+    import bit_moe_amd as bm
+    L = synth_layer(w)
+    gate, up, down = L.gate_all().copy(), L.up_all().copy(), L.down_all().copy()
+    for arr, cols in ((gate, [(0, 2)]), (up, [(0, 2)]), (down, [(80, 82), (82, 84)])):
+        for a, b in cols:
+            d = d_of_block(arr.shape[0]).astype(np.float16)
+            arr[:, a:b] = d.view(np.uint8).reshape(-1, 2)
+    lay = bm.layer_from_canonical(w.H, w.I, w.E, w.k, L.router(), gate, up, down, L.grid(), None)
+    ng, nd = w.I * (w.H // 256), w.H * (w.I // 256)
+    per = lambda a, n: {e: a[e * n:(e + 1) * n] for e in range(w.E)}
+    return lay, per(gate, ng), per(up, ng), per(down, nd)
+
+
+@pytest.mark.parametrize("case", ["d=8", "d=2^-19", "log-uniform"])
+def test_scale_envelope_both_paths(case):
+    """Superblock scales at both ends of the range the prefill fp16 operands
+    hold exactly in their normal range (d, dmin in [2^-19, 8]: largest IQ2X
+    weight 27.1 d, largest Q2K term 45 d), and log-uniform over it; decode and
+    prefill against the oracle on the same blocks."""
+    require_gpu()
+    w = synth.WORKLOADS["tiny"].with_(name=f"tiny_env", T=37, x_dtype="bf16", seed=51)
+    rng = np.random.default_rng(5)
+    pick = {"d=8": lambda n: np.full(n, 8.0),
+            "d=2^-19": lambda n: np.full(n, 2.0 ** -19),
+            "log-uniform": lambda n: np.exp2(rng.uniform(-19, 3, n))}[case]
+    lay, gate, up, down = _scaled_layer_case(w, pick)
+    x, _ = synth.make_tokens(w)
+    ids, wt = _routing(w, x)
+    L = synth_layer(w)
+    ref = oracle.moe_ffn(w.H, w.I, w.E, w.k, L.grid(), gate, up, down, None, x, ids, wt.astype(np.float64))
+    assert np.all(np.isfinite(ref))
+    import bit_moe_amd as bm
+    for mode, fn in (("decode", bm.ffn_decode), ("prefill", bm.ffn_prefill)):
+        y = fn(lay, x_to_device(x), torch.from_numpy(ids).cuda(), torch.from_numpy(wt).cuda())
+        torch.cuda.synchronize()
+        assert_close_rms(y.cpu().numpy(), ref, what=f"scale envelope {case}/{mode}")

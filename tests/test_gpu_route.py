@@ -34,7 +34,8 @@ def _check_route(w, x, router_bits=None):
     np.testing.assert_allclose(glog, ref_logits, rtol=0, atol=2e-5 * max(scale, 1.0))
     ties = set(near_tie_tokens(ref_logits, w.k).tolist())
     ok = np.array([t not in ties for t in range(x.shape[0])])
-    say(f"[route] {w.name} T={x.shape[0]} near-ties={len(ties)}")
+    say(f"[route] {w.name} T={x.shape[0]} near-ties={len(ties)} "
+        f"max|dlogit|={float(np.abs(glog - ref_logits).max()):.2e}")
     np.testing.assert_array_equal(gid[ok], rid[ok])
     # w_j = exp(l_j - l_1) / sum_i exp(l_i - l_1): a logit error d moves each
     # weight by at most w_j * 2 max|d| <= 2 max|d| (+ fp32 exp/divide rounding)

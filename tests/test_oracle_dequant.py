@@ -2,8 +2,10 @@
 
 The pages print no worked example of either block format, so the oracle's
 decoders are pinned by: hand-decoded golden blocks (tests/golden/), the fp16
-decoding against numpy's IEEE half type for all 65536 patterns, and
-invariants that hold for any correct decoder on random blocks.
+decoding against numpy's IEEE half type for all 65536 patterns, invariants
+that hold for any correct decoder on random blocks, and an independent numpy
+decoder (below) that must agree bit for bit on every tiny-config tensor and
+on 2^20 random superblocks of each format.
 """
 import json
 import os
@@ -194,3 +196,94 @@ def test_slab_equals_slice_of_full_tensor():
     full = L.down_all()
     per = w.H * (w.I // 256)
     np.testing.assert_array_equal(full[3 * per:4 * per], L.down(3))
+
+
+# ---- an independent decoder, written in numpy from the byte description ----
+# (the format text of include/bitmoe.h: GGML's IQ2_XXS and Q2_K block orders,
+# as "antirez/ds4 - Moteur local d'inference DeepSeek V4 Flash pour Metal",
+# section "Remerciements a llama.cpp et GGML" has ds4 keep them, with the
+# synthetic codebook).  It shares no code with the oracle: whole-array bit
+# slicing instead of per-value loops, fp16 fields through numpy's half type.
+
+_POP7 = np.array([bin(v).count("1") & 1 for v in range(128)], dtype=np.uint8)
+
+
+def _np_iq2x(blocks, grid):
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1, 66)
+    n = b.shape[0]
+    d = b[:, 0:2].copy().view(np.float16).astype(np.float64).reshape(n)
+    groups = b[:, 2:66].reshape(n, 8, 8)                       # [block, group, byte]
+    idx = groups[:, :, 0:4]                                    # [block, group, run]
+    a = groups[:, :, 4:8].copy().view("<u4").reshape(n, 8).astype(np.uint64)
+    scale = (a >> 28).astype(np.float64)                       # [block, group]
+    s7 = np.stack([(a >> (7 * j)) & 0x7F for j in range(4)], axis=2).astype(np.uint8)
+    sign_byte = s7 | (_POP7[s7] << 7)                          # even parity in bit 7
+    neg = np.unpackbits(sign_byte[..., None], axis=-1, bitorder="little")   # [block, group, run, i]
+    mag = grid.astype(np.float64)[idx]                         # [block, group, run, i]
+    db = d[:, None] * (0.5 + scale) * 0.25                     # [block, group]
+    with np.errstate(invalid="ignore"):
+        v = db[:, :, None, None] * mag * np.where(neg == 1, -1.0, 1.0)
+    return v.reshape(n * 256)                                  # position 32 g + 8 run + i
+
+
+def _np_q2k(blocks):
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1, 84)
+    n = b.shape[0]
+    sc = (b[:, 0:16] & 15).astype(np.float64)                  # [block, sub-block]
+    mn = (b[:, 0:16] >> 4).astype(np.float64)
+    qs = b[:, 16:80].reshape(n, 2, 1, 32)                      # [block, half, -, l]
+    shifts = (2 * np.arange(4, dtype=np.uint8)).reshape(1, 1, 4, 1)
+    q = ((qs >> shifts) & 3).astype(np.float64).reshape(n, 16, 16)   # value 128 h + 32 j + l
+    d = b[:, 80:82].copy().view(np.float16).astype(np.float64).reshape(n, 1, 1)
+    dmin = b[:, 82:84].copy().view(np.float16).astype(np.float64).reshape(n, 1, 1)
+    with np.errstate(invalid="ignore"):                        # Inf * 0 patterns give NaN
+        v = d * sc[:, :, None] * q - dmin * mn[:, :, None]
+    return v.reshape(n * 256)
+
+
+def _same(a, b):
+    """Equal as IEEE values (NaN matches NaN whatever its payload), and
+    bit-identical wherever finite."""
+    np.testing.assert_array_equal(a, b)
+    f = np.isfinite(a)
+    np.testing.assert_array_equal(a[f].view(np.uint64), b[f].view(np.uint64))
+
+
+def test_numpy_decoder_agrees_on_every_tiny_tensor():
+    """Both decoders on every block of the tiny config's gate, up and down
+    tensors (all 8 experts)."""
+    L = synth.make_layer(synth.WORKLOADS["tiny"])
+    grid = L.grid()
+    for name, arr in (("gate", L.gate_all()), ("up", L.up_all())):
+        _same(_np_iq2x(arr, grid), oracle.dequant_iq2x(arr, grid))
+    down = L.down_all()
+    _same(_np_q2k(down), oracle.dequant_q2k(down))
+
+
+@pytest.mark.parametrize("fmt", ["iq2x", "q2k"])
+def test_numpy_decoder_agrees_on_a_million_random_superblocks(fmt):
+    """2^20 superblocks of uniformly random bytes per format: every fp16
+    scale pattern occurs (zero, subnormal, negative, Inf, NaN), with random
+    codebooks."""
+    rng = np.random.default_rng(1234 if fmt == "iq2x" else 4321)
+    nbytes = 66 if fmt == "iq2x" else 84
+    total, chunk = 1 << 20, 1 << 16
+    for c in range(total // chunk):
+        blocks = rng.integers(0, 256, size=(chunk, nbytes), dtype=np.uint8)
+        if fmt == "iq2x":
+            grid = rng.integers(0, 256, size=(256, 8), dtype=np.uint8)
+            _same(_np_iq2x(blocks, grid), oracle.dequant_iq2x(blocks, grid))
+        else:
+            _same(_np_q2k(blocks), oracle.dequant_q2k(blocks))
+
+
+def test_numpy_decoder_matches_hand_goldens():
+    """The numpy decoder also reproduces the hand-decoded golden blocks, so
+    the three (hand values, oracle, numpy) agree."""
+    g = _golden("iq2x_hand.json")
+    for c in g["cases"]:
+        blk = np.frombuffer(bytes.fromhex(c["hex"].replace(" ", "")), dtype=np.uint8)
+        np.testing.assert_array_equal(_np_iq2x(blk, _hand_grid(g)), np.array(_expand(c["expect"])))
+    for c in _golden("q2k_hand.json")["cases"]:
+        blk = np.frombuffer(bytes.fromhex(c["hex"].replace(" ", "")), dtype=np.uint8)
+        np.testing.assert_array_equal(_np_q2k(blk), np.array(_expand(c["expect"])))
