@@ -18,12 +18,14 @@ F32, BF16 = 0, 1
 DECODE, PREFILL = 0, 1
 LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
 TIME_GATEUP, TIME_DOWN = 0, 1
-EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = -1, -2, -3, -4
+EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ESCRATCH = -1, -2, -3, -4, -5
+STATIC_SCRATCH_BYTES = 16 << 20
 
 # every symbol declared in include/bitmoe.h
 SYMBOLS = [
     "moe_route_workspace_bytes", "moe_route", "moe_topk", "moe_bucket_workspace_bytes",
-    "moe_bucket", "moe_workspace_bytes", "moe_ffn_decode", "moe_forward_decode", "moe_ffn_prefill",
+    "moe_bucket", "moe_workspace_bytes", "moe_ffn_decode", "moe_forward_decode", "moe_forward_decode_noalloc",
+    "moe_ffn_prefill",
     "moe_dequant_iq2x", "moe_dequant_q2k", "moe_pack_iq2x", "moe_pack_q2k", "moe_pack_bf16",
     "moe_set_timing_events", "moe_strerror", "moe_version",
 ]
@@ -65,6 +67,7 @@ def lib() -> C.CDLL:
         "moe_ffn_decode": ([LP, P, I, I, P, P, P, P, SZ, P], I),
         "moe_ffn_prefill": ([LP, P, I, I, P, P, P, P, SZ, P], I),
         "moe_forward_decode": ([LP, P, I, I, P, P, P, P, SZ, P], I),
+        "moe_forward_decode_noalloc": ([LP, P, I, I, P, P, P, P], I),
         "moe_dequant_iq2x": ([P, P, I64, P, I, P], I),
         "moe_dequant_q2k": ([P, I64, P, I, P], I),
         "moe_pack_iq2x": ([P, P, I, I, I, P], I),
@@ -254,6 +257,24 @@ def forward_decode(layer, x, ids=None, w=None, y=None, ws=None, stream=None):
     _dev_check(x, ids, w, y, ws)
     _check(lib().moe_forward_decode(layer.ref, _ptr(x), _x_dtype(x), T, _ptr(ids), _ptr(w), _ptr(y),
                                     _ptr(ws), ws.numel(), _stream(stream)), "moe_forward_decode")
+    return y, ids, w
+
+
+def forward_decode_noalloc(layer, x, ids=None, w=None, y=None, stream=None):
+    """moe_forward_decode_noalloc: routing + decode FFN with the library's
+    static scratch (no workspace). Returns (y, ids, w)."""
+    torch = _torch()
+    T = x.shape[0]
+    dev = x.device
+    if ids is None:
+        ids = torch.empty((T, layer.k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((T, layer.k), dtype=torch.float32, device=dev)
+    if y is None:
+        y = torch.empty((T, layer.H), dtype=torch.float32, device=dev)
+    _dev_check(x, ids, w, y)
+    _check(lib().moe_forward_decode_noalloc(layer.ref, _ptr(x), _x_dtype(x), T, _ptr(ids), _ptr(w), _ptr(y),
+                                            _stream(stream)), "moe_forward_decode_noalloc")
     return y, ids, w
 
 

@@ -136,8 +136,9 @@ int check_ws(void *ws, size_t have, size_t need) {
     return BITMOE_OK;
 }
 
-int ffn_common(const bitmoe_layer *L, const void *x, int x_dtype, int T, const int32_t *ids,
-               const float *w, float *y, void *ws, size_t ws_bytes, int mode, FfnWs *out) {
+// Every argument but the workspace.
+int ffn_args(const bitmoe_layer *L, const void *x, int x_dtype, int T, const int32_t *ids, const float *w,
+             const float *y) {
     int rc = check_ffn_layer(L);
     if (rc) return rc;
     if (T < 0) return BITMOE_EINVAL;
@@ -146,6 +147,13 @@ int ffn_common(const bitmoe_layer *L, const void *x, int x_dtype, int T, const i
     if (T == 0) return BITMOE_OK;
     if (!x || !ids || !w || !y) return BITMOE_EINVAL;
     if (!aligned(x, 16) || !aligned(y, 16)) return BITMOE_EINVAL;
+    return BITMOE_OK;
+}
+
+int ffn_common(const bitmoe_layer *L, const void *x, int x_dtype, int T, const int32_t *ids,
+               const float *w, float *y, void *ws, size_t ws_bytes, int mode, FfnWs *out) {
+    int rc = ffn_args(L, x, x_dtype, T, ids, w, y);
+    if (rc || T == 0) return rc;
     FfnWs need = carve_ffn(L, T, mode, nullptr);
     rc = check_ws(ws, ws_bytes, need.bytes);
     if (rc) return rc;
@@ -176,6 +184,9 @@ const char *moe_strerror(int code) {
                    "the FFN calls read TILED blocks)";
         case BITMOE_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
         case BITMOE_EHIP: return "a HIP kernel launch failed";
+        case BITMOE_ESCRATCH:
+            return "the call needs more scratch than the library's static array holds "
+                   "(BITMOE_STATIC_SCRATCH_BYTES; use the entry point that takes a workspace)";
         default: return "unknown error code";
     }
 }
@@ -269,22 +280,7 @@ int moe_ffn_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, con
 
 int moe_forward_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, int32_t *ids,
                        float *w, float *y, void *ws, size_t ws_bytes, void *stream) {
-    if (L && !L->router_w) return BITMOE_EINVAL;
-    FfnWs f;
-    int rc = ffn_common(L, x, x_dtype, T, ids, w, y, ws, ws_bytes, BITMOE_DECODE, &f);
-    if (rc || T == 0) return rc;
-    hipStream_t s = as_stream(stream);
-    bm_host::DecodeBufs b = f.d;
-    b.ids = ids;
-    b.w = w;
-    b.y = y;
-    const bool fused = T <= kFusedRouterMaxT;
-    if (!fused) {
-        // the router's scratch is carved from the decode workspace
-        rc = moe_route(L, x, x_dtype, T, nullptr, ids, w, f.route_ws, f.route_ws_bytes, stream);
-        if (rc) return rc;
-    }
-    return bm_host::launch_decode(L, x, x_dtype, T, bm_host::decode_plan(L, T, fused), b, s);
+    return bm_host::forward_decode(L, x, x_dtype, T, ids, w, y, ws, ws_bytes, stream, true);
 }
 
 int moe_ffn_prefill(const bitmoe_layer *L, const void *x, int x_dtype, int T, const int32_t *ids,
@@ -340,3 +336,38 @@ int moe_pack_bf16(const void *src, void *dst, int N, int K, void *stream) {
 }
 
 }  // extern "C"
+
+namespace bm_host {
+
+int forward_decode_check(const bitmoe_layer *L, const void *x, int x_dtype, int T, const int32_t *ids,
+                         const float *w, const float *y, size_t *ws_need) {
+    if (L && !L->router_w) return BITMOE_EINVAL;
+    const int rc = ffn_args(L, x, x_dtype, T, ids, w, y);
+    if (rc || T == 0) return rc;
+    *ws_need = carve_ffn(L, T, BITMOE_DECODE, nullptr).bytes;
+    return BITMOE_OK;
+}
+
+int forward_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, int32_t *ids, float *w, float *y,
+                   void *ws, size_t ws_bytes, void *stream, bool fork) {
+    if (L && !L->router_w) return BITMOE_EINVAL;
+    FfnWs f;
+    int rc = ffn_common(L, x, x_dtype, T, ids, w, y, ws, ws_bytes, BITMOE_DECODE, &f);
+    if (rc || T == 0) return rc;
+    hipStream_t s = as_stream(stream);
+    DecodeBufs b = f.d;
+    b.ids = ids;
+    b.w = w;
+    b.y = y;
+    const bool fused = T <= kFusedRouterMaxT;
+    if (!fused) {
+        // the router's scratch is carved from the decode workspace
+        rc = moe_route(L, x, x_dtype, T, nullptr, ids, w, f.route_ws, f.route_ws_bytes, stream);
+        if (rc) return rc;
+    }
+    DecodePlan p = decode_plan(L, T, fused);
+    p.fork = fork;
+    return launch_decode(L, x, x_dtype, T, p, b, s);
+}
+
+}  // namespace bm_host

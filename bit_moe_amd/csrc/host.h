@@ -117,6 +117,15 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router);
 int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, const DecodePlan &p,
                   const DecodeBufs &b, hipStream_t s);
 
+// moe_forward_decode on a given workspace; fork = false keeps every launch
+// on the caller's stream (no library stream is created or used).
+// forward_decode_check validates every argument but the workspace and
+// gives the workspace bytes the call needs.
+int forward_decode_check(const bitmoe_layer *L, const void *x, int x_dtype, int T, const int32_t *ids,
+                         const float *w, const float *y, size_t *ws_need);
+int forward_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, int32_t *ids, float *w, float *y,
+                   void *ws, size_t ws_bytes, void *stream, bool fork);
+
 // prefill FFN
 // xprep + routed gate/up + routed down over b's row tiles; o written per pair
 int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int T, const Buckets &b,

@@ -83,6 +83,7 @@ constexpr int kPfWShift = 8;
 constexpr float kPfWScale = 256.f;
 constexpr int kPfDnWShift = 7;
 constexpr float kPfDnWScale = 128.f;
+static_assert(kPfWScale == (float)(1 << kPfWShift) && kPfDnWScale == (float)(1 << kPfDnWShift), "scale factors");
 
 BM_DEV uint32_t h2u(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 BM_DEV f16x2 u2h(uint32_t v) { return __builtin_bit_cast(f16x2, v); }

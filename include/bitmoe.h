@@ -103,6 +103,7 @@ extern "C" {
 #define BITMOE_EUNSUPPORTED (-2)  /* H or I not a multiple of 256, k > 16, k > E, E > 1024, T too large */
 #define BITMOE_EWORKSPACE   (-3)  /* workspace missing, too small or misaligned */
 #define BITMOE_EHIP         (-4)  /* a HIP launch failed */
+#define BITMOE_ESCRATCH     (-5)  /* more scratch than BITMOE_STATIC_SCRATCH_BYTES (noalloc call) */
 
 #define BITMOE_F32  0   /* float32 activations / outputs */
 #define BITMOE_BF16 1   /* bfloat16 activations / outputs */
@@ -250,6 +251,25 @@ int moe_ffn_prefill(const bitmoe_layer *L, const void *x, int x_dtype, int T,
 int moe_forward_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T,
                        int32_t *ids, float *w, float *y, void *ws,
                        size_t ws_bytes, void *stream);
+
+/*
+ * moe_forward_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same routing and decode FFN, with the same outputs, but
+ * its scratch lives in a device array of the library
+ * (BITMOE_STATIC_SCRATCH_BYTES per device, held from load until the process
+ * ends) instead of a caller workspace, and every launch stays on `stream`
+ * (no side stream).  The call allocates nothing.  Calls whose scratch would
+ * exceed the array return BITMOE_ESCRATCH before any launch (at H 7168,
+ * I 2048, E 256, k 8 with a shared expert: up to 16 tokens fit).  Every
+ * call on one device shares that device's array: calls that overlap on one
+ * device race and must be serialised by the caller.
+ * Errors: those of moe_forward_decode (no EWORKSPACE), ESCRATCH, and EHIP if
+ * the array's device address cannot be looked up.
+ */
+#define BITMOE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int moe_forward_decode_noalloc(const bitmoe_layer *L, const void *x, int x_dtype, int T,
+                               int32_t *ids, float *w, float *y, void *stream);
 
 /*
  * Standalone dequantisation of CANONICAL blocks (GGML's GGUF block layouts:

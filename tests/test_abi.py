@@ -182,3 +182,19 @@ def test_dequant_pack_topk_bucket_argument_checks():
     big = L.moe_bucket_workspace_bytes(8192, 8, 256)
     assert big >= 64 * 256 * 4
     assert L.moe_bucket(16, 8192, 8, 256, 16, 16, 16, 16, 16, 256, big - 1, None) == _lib.EWORKSPACE
+
+
+def test_noalloc_refuses_calls_beyond_its_static_scratch():
+    """The allocation-free decode call checks its scratch need on the host,
+    before any device work: 64 tokens at full shape with a shared expert
+    need more than the static array, 16 tokens fit."""
+    L = bm.lib()
+    lay = _layer(H=7168, I=2048, E=256, k=8, shared=True)
+    assert L.moe_workspace_bytes(C.byref(lay), 16, 0) <= _lib.STATIC_SCRATCH_BYTES
+    assert L.moe_workspace_bytes(C.byref(lay), 64, 0) > _lib.STATIC_SCRATCH_BYTES
+    assert L.moe_forward_decode_noalloc(C.byref(lay), 16, 1, 64, 16, 16, 16, None) == _lib.ESCRATCH
+    assert L.moe_forward_decode_noalloc(C.byref(lay), 16, 1, 0, 16, 16, 16, None) == 0
+    assert L.moe_forward_decode_noalloc(C.byref(lay), None, 1, 4, 16, 16, 16, None) == _lib.EINVAL
+    canon = _layer(layout=_lib.LAYOUT_CANONICAL)
+    assert L.moe_forward_decode_noalloc(C.byref(canon), 16, 1, 4, 16, 16, 16, None) == _lib.EUNSUPPORTED
+    assert "static" in bm.strerror(_lib.ESCRATCH)
