@@ -77,22 +77,30 @@ def build_layer(w, copies):
 
 
 def time_steps(step, warmup, steps):
+    """Run `warmup` untimed steps, then time exactly `steps` steps between a
+    synchronize on both sides.  An event is recorded on the stream between
+    consecutive steps, so besides the average (first to last event / steps)
+    every step's own duration is known.  Returns (ms per step, stats)."""
     import torch
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
     for i in range(steps):
         step(warmup + i)
-    b.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / steps      # ms per step
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    q = lambda f: per[min(len(per) - 1, int(f * (len(per) - 1) + 0.5))]
+    stats = {"median_ms": q(0.5), "p10_ms": q(0.1), "p90_ms": q(0.9), "n": steps}
+    return ev[0].elapsed_time(ev[steps]) / steps, stats
 
 
-def time_dominant(step, n):
-    """Average duration of the gate/up kernel, from the HIP events that its
-    dispatch takes at kernel start and end (moe_set_timing_events)."""
+def time_kernel(step, n, which):
+    """Average duration (ms) of one kernel of the step, from the HIP events
+    its dispatch takes at kernel start and end (moe_set_timing_events),
+    with the median, p10 and p90 over the n calls."""
     import torch
     import bit_moe_amd as bm
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
@@ -101,11 +109,13 @@ def time_dominant(step, n):
         e.record()
     torch.cuda.synchronize()
     for i, (s, e) in enumerate(evs):
-        bm.set_timing_events(s, e)
+        bm.set_timing_events(s, e, which)
         step(i)
     bm.set_timing_events(None, None)
     torch.cuda.synchronize()
-    return sum(s.elapsed_time(e) for s, e in evs) / n
+    d = sorted(s.elapsed_time(e) for s, e in evs)
+    q = lambda f: d[min(len(d) - 1, int(f * (len(d) - 1) + 0.5))]
+    return sum(d) / n, {"median_ms": q(0.5), "p10_ms": q(0.1), "p90_ms": q(0.9), "n": n}
 
 
 def decode_b1(args, L, lays):
@@ -125,12 +135,17 @@ def decode_b1(args, L, lays):
         lay, x = lays[i % len(lays)], xs[i % R]
         bm.forward_decode(lay, x, ids=ids, w=wt, y=y, ws=ws)
 
-    ms = time_steps(step, args.warmup, args.steps)
-    gu_ms = time_dominant(step, min(args.steps, 100))
-    # the timed launch streams the routed gate/up blocks of the k experts
+    ms, stats = time_steps(step, args.warmup, args.steps)
+    n = min(args.steps, 100)
+    gu_ms, gu_stats = time_kernel(step, n, bm.TIME_GATEUP)
+    dn_ms, dn_stats = time_kernel(step, n, bm.TIME_DOWN)
+    # the gate/up launch streams the routed gate/up blocks of the k experts;
+    # the down launch the k experts' down blocks and the shared down
     gu_bytes = w.k * (2 * w.I * (w.H // 256) * 66)
+    dn_bytes = w.k * (w.H * (w.I // 256) * 84) + w.I * w.H * 2
     step_bytes = w.k * (2 * w.I * (w.H // 256) * 66 + w.H * (w.I // 256) * 84) + 3 * w.I * w.H * 2 + w.E * w.H * 2
-    return dict(ms=ms, gu_ms=gu_ms, gu_bytes=gu_bytes, step_bytes=step_bytes)
+    return dict(ms=ms, stats=stats, gu_ms=gu_ms, gu_stats=gu_stats, gu_bytes=gu_bytes, dn_ms=dn_ms,
+                dn_stats=dn_stats, dn_bytes=dn_bytes, step_bytes=step_bytes)
 
 
 def decode_b16(args, lays):
@@ -156,14 +171,27 @@ def decode_b16(args, lays):
         bm.topk(lgs[r], w.k, ids=ids, w=wt)
         bm.ffn_decode(lay, xs[r], ids, wt, y=y, ws=ws)
 
-    ms = time_steps(step, args.warmup, args.steps)
+    ms, stats = time_steps(step, args.warmup, args.steps)
     # distinct experts per draw decide the bytes streamed
     d = np.mean([len(np.unique(bm.topk(l, w.k)[0].cpu().numpy())) for l in lgs])
     byts = d * w.I * (w.H // 256) * 66 * 2 + d * w.H * (w.I // 256) * 84 + 3 * w.I * w.H * 2
-    return dict(ms=ms, distinct=float(d), bytes=float(byts))
+    return dict(ms=ms, stats=stats, distinct=float(d), bytes=float(byts))
+
+
+def issued_rows(counts, tile_rows=96):
+    """Rows the prefill matrix-core kernels run per expert: each row tile of
+    up to 96 rows runs in blocks of 32, so a tile of r rows issues
+    32 ceil(r / 32)."""
+    tot = 0
+    for c in counts:
+        c = int(c)
+        full, tail = divmod(c, tile_rows)
+        tot += full * tile_rows + (-(-tail // 32)) * 32
+    return tot
 
 
 def prefill_2k(args, lays):
+    import numpy as np
     import torch
     import bit_moe_amd as bm
     import synth
@@ -183,12 +211,17 @@ def prefill_2k(args, lays):
         bm.route(lay, xd, ids=ids, w=wt, ws=rws)
         bm.ffn_prefill(lay, xd, ids, wt, y=y, ws=ws)
 
-    ms = time_steps(step, 2, args.prefill_steps)
-    gu_ms = time_dominant(step, 3)
+    ms, stats = time_steps(step, 2, args.prefill_steps)
+    gu_ms, gu_stats = time_kernel(step, 5, bm.TIME_GATEUP)
+    dn_ms, dn_stats = time_kernel(step, 5, bm.TIME_DOWN)
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=w.E)
     pairs = w.T * w.k
-    flops = pairs * 3 * 2 * w.H * w.I
-    gu_flops = pairs * 2 * 2 * w.H * w.I
-    return dict(ms=ms, flops=flops, gu_ms=gu_ms, gu_flops=gu_flops)
+    rows_issued = issued_rows(counts)
+    return dict(ms=ms, stats=stats, flops=pairs * 3 * 2 * w.H * w.I,
+                gu_ms=gu_ms, gu_stats=gu_stats, gu_flops=pairs * 2 * 2 * w.H * w.I,
+                gu_flops_issued=rows_issued * 2 * 2 * w.H * w.I,
+                dn_ms=dn_ms, dn_stats=dn_stats, dn_flops=pairs * 2 * w.H * w.I,
+                dn_flops_issued=rows_issued * 2 * w.H * w.I)
 
 
 def prefill_8k_zipf(args, lays):
@@ -212,30 +245,43 @@ def prefill_8k_zipf(args, lays):
         bm.topk(lg, w.k, ids=ids, w=wt)
         bm.ffn_prefill(lay, xd, ids, wt, y=y, ws=ws)
 
-    ms = time_steps(step, 1, max(2, args.prefill_steps // 4))
+    ms, stats = time_steps(step, 1, max(3, args.prefill_steps // 2))
     rows = np.bincount(ids.cpu().numpy().ravel(), minlength=w.E)
     flops = w.T * w.k * 3 * 2 * w.H * w.I
-    return dict(ms=ms, flops=flops, rows_max=int(rows.max()), rows_min=int(rows.min()))
+    return dict(ms=ms, stats=stats, flops=flops, rows_max=int(rows.max()), rows_min=int(rows.min()))
 
 
-def cpu_baseline(target_s=15.0, max_tokens=400):
-    """The oracle (plain fp64 C, all host threads) on the decode workload,
-    one token at a time until about target_s seconds of oracle time: routing
-    and the layer per token.  Expert slabs are generated (untimed) before the
-    token that first uses them."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(name, target_s, max_tokens=400):
+    """The oracle as it stands (plain fp64 C, all host threads) on a bounded
+    sample of one workload's tokens, one token at a time until about target_s
+    seconds of oracle time: routing (computed or drawn logits) and the layer
+    per token.  Expert slabs are generated (untimed) before the token that
+    first uses them."""
     import numpy as np
     import oracle
     import synth
-    w = synth.WORKLOADS["decode_b1"]
+    w = synth.WORKLOADS[name]
     L = synth.make_layer(w)
-    x, _ = synth.make_tokens(w.with_(T=max_tokens))
+    T = min(max_tokens, w.T) if w.routing == "zipf" else max_tokens
+    x, _ = synth.make_tokens(w.with_(T=T))
+    zl = synth.zipf_logits(w, T=T).astype(np.float64) if w.routing == "zipf" else None
     grid, router, shared = L.grid(), L.router(), L.shared()
     gate, up, down = {}, {}, {}
     spent, n = 0.0, 0
-    while n < max_tokens and (spent < target_s or n < 4):
+    while n < T and (spent < target_s or n < 4):
         xt = x[n:n + 1]
         t0 = time.perf_counter()
-        ids, wt = oracle.route(xt, router, w.k)
+        ids, wt = oracle.topk(zl[n:n + 1], w.k) if zl is not None else oracle.route(xt, router, w.k)
         spent += time.perf_counter() - t0
         for e in (int(v) for v in np.unique(ids)):
             if e not in gate:
@@ -244,9 +290,12 @@ def cpu_baseline(target_s=15.0, max_tokens=400):
         oracle.moe_ffn(w.H, w.I, w.E, w.k, grid, gate, up, down, shared, xt, ids, wt)
         spent += time.perf_counter() - t0
         n += 1
-    return dict(value=n / spent, unit="tokens/s", cores=oracle.max_threads(), kind="oracle",
-                sample=f"{n} decode tokens of the batch-1 workload (routing + 8 routed experts + "
-                       f"shared expert each, fp64), {spent:.1f} s of oracle time")
+    what = {"decode_b1": "the batch-1 decode workload (routing + 8 routed experts + shared expert each)",
+            "decode_b16_zipf": "the 16-token Zipf(1.1) decode batch (top-k of the drawn logits + 8 routed "
+                               "experts + shared expert each)",
+            "prefill_2k": "the 2048-token prefill chunk (routing + 8 routed experts each)"}[name]
+    return dict(value=n / spent, unit="tokens/s", cores=oracle.max_threads(), cpu=cpu_model(), kind="oracle",
+                sample=f"{n} tokens of {what}, fp64, {spent:.1f} s of oracle time")
 
 
 def copy_calibration(nbytes=1 << 30, reps=5):
@@ -416,13 +465,18 @@ def main():
     if args.prefill_only:
         _, lays = build_layer(synth.WORKLOADS["decode_b1"], 1)
         pf = prefill_2k(args, lays)
-        log(f"[bench] prefill_2k {pf['ms']:.2f} ms/step, gate/up {pf['gu_ms'] * 1e3:.1f} us")
+        log(f"[bench] prefill_2k {pf['ms']:.2f} ms/step, gate/up {pf['gu_ms'] * 1e3:.1f} us, "
+            f"down {pf['dn_ms'] * 1e3:.1f} us")
         return
     w = synth.WORKLOADS["decode_b1"]
     L, lays = build_layer(w, args.copies)
     r = decode_b1(args, L, lays)
-    log(f"[bench] decode_b1 {r['ms'] * 1e3:.1f} us/step, gate/up {r['gu_ms'] * 1e3:.1f} us")
+    log(f"[bench] decode_b1 {r['ms'] * 1e3:.1f} us/step (median {r['stats']['median_ms'] * 1e3:.1f}), "
+        f"gate/up {r['gu_ms'] * 1e3:.1f} us, down {r['dn_ms'] * 1e3:.1f} us")
     gu_bw = r["gu_bytes"] / (r["gu_ms"] * 1e-3)
+    dn_bw = r["dn_bytes"] / (r["dn_ms"] * 1e-3)
+    us = lambda st: {k: (v * 1e3 if k.endswith("_ms") else v) for k, v in st.items()}
+    usd = lambda st: {k.replace("_ms", "_us"): v for k, v in us(st).items()}
     out = {
         "metric": "MoE-layer tokens/s: decode HBM GB/s (%peak) + prefill MFMA TFLOP/s (%peak)",
         "value": 1.0 / (r["ms"] * 1e-3),
@@ -440,15 +494,21 @@ def main():
                                "IQ2X up/gate + Q2K down, bf16 router and shared expert",
                    "tokens_per_step": 1, "layer_copies_rotated": args.copies,
                    "step_hbm_bytes": r["step_bytes"],
-                   "step_hbm_GBps": r["step_bytes"] / (r["ms"] * 1e-3) / 1e9},
+                   "step_hbm_GBps": r["step_bytes"] / (r["ms"] * 1e-3) / 1e9,
+                   "step_us": usd(r["stats"])},
         "roofline": {"bound": "hbm", "kernel": "k_dec_gateup",
                      "achieved": gu_bw / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": gu_bw / HBM_PEAK, "traffic": traffic_from_profile("k_dec_gateup<1,0>"),
-                     "kernel_us": r["gu_ms"] * 1e3, "algorithmic_bytes": r["gu_bytes"]},
+                     "kernel_us": r["gu_ms"] * 1e3, "kernel_us_dist": usd(r["gu_stats"]),
+                     "algorithmic_bytes": r["gu_bytes"],
+                     "down_kernel": {"kernel": "k_dec_down", "achieved": dn_bw / 1e9, "frac": dn_bw / HBM_PEAK,
+                                     "kernel_us": r["dn_ms"] * 1e3, "algorithmic_bytes": r["dn_bytes"],
+                                     "traffic": traffic_from_profile("k_dec_down<0>")}},
     }
     if not args.no_extra:
         b16 = decode_b16(args, lays)
         out["decode_b16_zipf"] = {"tokens_per_s": 16 / (b16["ms"] * 1e-3), "ms_per_step": b16["ms"],
+                                  "step_us": usd(b16["stats"]),
                                   "distinct_experts": b16["distinct"],
                                   "hbm_GBps": b16["bytes"] / (b16["ms"] * 1e-3) / 1e9,
                                   "hbm_frac": b16["bytes"] / (b16["ms"] * 1e-3) / HBM_PEAK,
@@ -457,23 +517,39 @@ def main():
         del lays[1:]
         torch.cuda.empty_cache()
         pf = prefill_2k(args, lays)
-        out["prefill_2k"] = {"tokens_per_s": 2048 / (pf["ms"] * 1e-3), "ms_per_step": pf["ms"],
-                             "routed_TFLOPs": pf["flops"] / (pf["ms"] * 1e-3) / 1e12,
-                             "mfma_frac": pf["flops"] / (pf["ms"] * 1e-3) / BF16_PEAK,
-                             "gateup_kernel_us": pf["gu_ms"] * 1e3,
-                             "gateup_TFLOPs": pf["gu_flops"] / (pf["gu_ms"] * 1e-3) / 1e12,
-                             "gateup_mfma_frac": pf["gu_flops"] / (pf["gu_ms"] * 1e-3) / BF16_PEAK}
-        log(f"[bench] prefill_2k {pf['ms']:.2f} ms/step")
+        tfs = lambda f, ms: f / (ms * 1e-3) / 1e12
+        out["prefill_2k"] = {
+            "tokens_per_s": 2048 / (pf["ms"] * 1e-3), "ms_per_step": pf["ms"], "step_ms": pf["stats"],
+            "routed_TFLOPs": tfs(pf["flops"], pf["ms"]),
+            "mfma_frac": pf["flops"] / (pf["ms"] * 1e-3) / BF16_PEAK,
+            "roofline": [
+                {"bound": "mfma", "kernel": "k_pf_gateup", "unit": "TFLOP/s", "peak": BF16_PEAK / 1e12,
+                 "achieved": tfs(pf["gu_flops"], pf["gu_ms"]), "frac": tfs(pf["gu_flops"], pf["gu_ms"]) * 1e12 / BF16_PEAK,
+                 "issued_frac": tfs(pf["gu_flops_issued"], pf["gu_ms"]) * 1e12 / BF16_PEAK,
+                 "kernel_us": pf["gu_ms"] * 1e3, "kernel_us_dist": usd(pf["gu_stats"]),
+                 "algorithmic_flops": pf["gu_flops"], "issued_flops": pf["gu_flops_issued"], "traffic": None},
+                {"bound": "mfma", "kernel": "k_pf_down", "unit": "TFLOP/s", "peak": BF16_PEAK / 1e12,
+                 "achieved": tfs(pf["dn_flops"], pf["dn_ms"]), "frac": tfs(pf["dn_flops"], pf["dn_ms"]) * 1e12 / BF16_PEAK,
+                 "issued_frac": tfs(pf["dn_flops_issued"], pf["dn_ms"]) * 1e12 / BF16_PEAK,
+                 "kernel_us": pf["dn_ms"] * 1e3, "kernel_us_dist": usd(pf["dn_stats"]),
+                 "algorithmic_flops": pf["dn_flops"], "issued_flops": pf["dn_flops_issued"], "traffic": None}]}
+        log(f"[bench] prefill_2k {pf['ms']:.2f} ms/step, gate/up {pf['gu_ms'] * 1e3:.0f} us, "
+            f"down {pf['dn_ms'] * 1e3:.0f} us")
         p8 = prefill_8k_zipf(args, lays)
         out["prefill_8k_zipf"] = {"tokens_per_s": 8192 / (p8["ms"] * 1e-3), "ms_per_step": p8["ms"],
+                                  "step_ms": p8["stats"],
                                   "routed_TFLOPs": p8["flops"] / (p8["ms"] * 1e-3) / 1e12,
                                   "mfma_frac": p8["flops"] / (p8["ms"] * 1e-3) / BF16_PEAK,
                                   "rows_per_expert_max": p8["rows_max"], "rows_per_expert_min": p8["rows_min"],
                                   "note": "step = top-k of drawn Zipf(1.2) logits + prefill FFN"}
         log(f"[bench] prefill_8k_zipf {p8['ms']:.2f} ms/step")
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline("decode_b1", args.cpu_seconds)
         log(f"[bench] cpu baseline {out['cpu_baseline']['value']:.3f} tokens/s")
+        if not args.no_extra:
+            for name in ("decode_b16_zipf", "prefill_2k"):
+                out[name]["cpu_baseline"] = cb = cpu_baseline(name, args.cpu_seconds / 2)
+                log(f"[bench] cpu baseline {name} {cb['value']:.3f} tokens/s")
     print(json.dumps(out), flush=True)
 
 
