@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
                     help="print per-kernel MFMA TFLOP/s of a rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F16 "
                          "--kernel-trace run")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="print per-kernel averages of every counter of rocprofv3 --pmc runs")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the 2048-token prefill step (--prefill-steps times; for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -76,25 +78,36 @@ def build_layer(w, copies):
     return L, lays
 
 
-def time_steps(step, warmup, steps):
+def time_steps(step, warmup, steps, dist_steps=None):
     """Run `warmup` untimed steps, then time exactly `steps` steps between a
-    synchronize on both sides.  An event is recorded on the stream between
-    consecutive steps, so besides the average (first to last event / steps)
-    every step's own duration is known.  Returns (ms per step, stats)."""
+    synchronize on both sides (one event pair around them: ms per step).
+    Then a separate pass of `dist_steps` steps with an event between
+    consecutive steps gives the per-step distribution (median, p10, p90;
+    each includes one event record, so it reads slightly above the mean of
+    the clean pass).  Returns (ms per step, stats)."""
     import torch
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    ev[0].record()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
     for i in range(steps):
         step(warmup + i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    n = steps if dist_steps is None else dist_steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record()
+    for i in range(n):
+        step(warmup + steps + i)
         ev[i + 1].record()
     torch.cuda.synchronize()
-    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n))
     q = lambda f: per[min(len(per) - 1, int(f * (len(per) - 1) + 0.5))]
-    stats = {"median_ms": q(0.5), "p10_ms": q(0.1), "p90_ms": q(0.9), "n": steps}
-    return ev[0].elapsed_time(ev[steps]) / steps, stats
+    stats = {"median_ms": q(0.5), "p10_ms": q(0.1), "p90_ms": q(0.9), "n": n,
+             "note": "separate pass, one event record between steps"}
+    return ms, stats
 
 
 def time_kernel(step, n, which):
@@ -422,6 +435,40 @@ def summarize_mfma(pmc_dir):
     return "\n".join(lines)
 
 
+def summarize_counters(dirs, only=("k_pf_", "k_dec_", "k_combine", "k_shared")):
+    """Per-kernel average per dispatch of every counter collected in one or
+    more rocprofv3 --pmc output directories (one pass each), one row per
+    kernel with the counters as columns, plus the kernels' average
+    durations from the same runs."""
+    import glob
+    import sqlite3
+    vals, durs = {}, {}
+    for d in dirs:
+        for db in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+            c = sqlite3.connect(db)
+            per = {}
+            for kn, disp, cn, v in c.execute("select kernel_name, dispatch_id, counter_name, sum(value) "
+                                             "from counters_collection group by dispatch_id, counter_name"):
+                per.setdefault((kn, cn), []).append(v)
+            for (kn, cn), v in per.items():
+                vals.setdefault(kn, {})[cn] = sum(v) / len(v)
+            try:
+                for kn, t in c.execute("select name, end - start from kernels"):
+                    durs.setdefault(kn, []).append(t)
+            except sqlite3.Error:
+                pass
+    out = []
+    for kn in sorted(vals):
+        short = kn.replace("(anonymous namespace)::", "").split("(")[0]
+        if only and not any(o in short for o in only):
+            continue
+        us = sum(durs.get(kn, [0])) / max(1, len(durs.get(kn, []))) / 1e3
+        out.append(f"kernel {short} avg_us {us:.1f}")
+        for cn in sorted(vals[kn]):
+            out.append(f"  {cn} {vals[kn][cn]:.6g}")
+    return "\n".join(out)
+
+
 def traffic_from_profile(kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary,
     or None when the decode sources have changed since it was taken."""
@@ -449,6 +496,9 @@ def main():
         return
     if args.summarize_mfma:
         print(summarize_mfma(args.summarize_mfma))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "

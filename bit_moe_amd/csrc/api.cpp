@@ -86,7 +86,8 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
         f.p.xsc = c.take<float>(T);
         f.p.h = c.take<uint16_t>(n * L->I);
         f.p.hexp = c.take<int32_t>(n * (L->I / 256));
-        f.p.o = c.take<float>(n * L->H);
+        f.p.o16 = c.take<uint16_t>(n * L->H);
+        f.p.oexp = c.take<int32_t>(n * ((L->H + 511) / 512));
         if (shared) {
             f.p.hs = c.take<float>((int64_t)T * L->I);
             f.p.os = c.take<float>((int64_t)T * L->H);

@@ -87,7 +87,9 @@ struct PrefillBufs {
     float *xsc;         // [T] power-of-two token scales
     uint16_t *h;        // [T*k][I] fp16 h rows in bucket order, scaled per 256 columns
     int32_t *hexp;      // [T*k][I/256] exponents of those scales
-    float *o;           // [T*k][H] per-pair expert outputs
+    float *o;           // [T*k][H] per-pair expert outputs in fp32 (decode batches), or
+    uint16_t *o16;      // [T*k][H] in fp16 (prefill) with
+    int32_t *oexp;      // [T*k][ceil(H/512)] their power-of-two exponents
     float *hs, *os;     // shared expert h [T][I] and output [T][H] (or null)
 };
 

@@ -62,14 +62,13 @@ constexpr int kPfHalf = 128;                  // K per LDS stage
 // contiguous 128-byte runs, which gfx950's LDS serves without bank conflicts
 // (row-strided layouts, padded or XOR-swizzled, cost 4 extra cycles per read).
 constexpr int kPfGuCols = 256;                // h columns per gate/up workgroup
-constexpr int kPfDnCols = 512;                // output columns per down workgroup
+constexpr int kPfDnCols = 512;                // output columns per down workgroup (16 waves x 32)
 constexpr int kPfXcds = 8;
 constexpr int kPfMagBytes = kLutMagBytes;       // 256 codebook rows x 16 copies x 16 bytes
 constexpr int kPfSgnBytes = kLutSgnHalf;        // 128 sign patterns x 16 copies x 16 bytes
 constexpr int kPfTabBytes = kPfMagBytes + kPfSgnBytes;
 constexpr int kPfABytes = kPfRows * kPfHalf * 2;
 constexpr int kPfGuLds = kPfTabBytes + 2 * kPfABytes + kPfRows * (4 + 4 + 4) + kPfWaves * kPfRows * 4;
-constexpr int kPfDnLds = 2 * kPfABytes + kPfRows * (4 + 4);
 // fp16 weight operands carry a factor 2^kPfWShift (IQ2X) or 2^kPfDnWShift
 // (Q2K), removed in the fp32 epilogues: with it a superblock scale d (and
 // dmin) in [2^-19, 8] keeps every nonzero weight in fp16's normal range and
@@ -447,103 +446,135 @@ k_pf_gateup(GuArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// down.  512 threads; wave w owns output columns n0 + 64w .. +63 (blocks 0,1
-// of 32).  In a stage (half superblock, 8 sub-blocks) lane half kh takes
-// sub-blocks 4kh..4kh+3 - one 16-byte piece - k-step t being half t & 1 of
-// sub-block 4kh + (t >> 1): stage K offset 64 kh + 8 t again.
+// down.  1024 threads (16 waves); wave w owns output columns n0 + 32w ..
+// +31, one 32-column block, so a wave holds at most 3 x 16 accumulators and
+// four waves run on each SIMD: the Q2K decode (VALU) of some waves then runs
+// under the MFMAs of others.  (Measured against two 8-wave workgroups of
+// 256 columns per compute unit, which stage every activation tile twice:
+// slower.)  In a stage (half superblock, 8 sub-blocks) lane
+// half kh takes sub-blocks 4kh..4kh+3 - one 16-byte piece - k-step t being
+// half t & 1 of sub-block 4kh + (t >> 1): stage K offset 64 kh + 8 t again.
+// Outputs: fp16 per pair with one power-of-two exponent per (pair, 512
+// columns) (prefill), or fp32 per pair (decode batches).
 // ---------------------------------------------------------------------------
+constexpr int kDnWaves = 16;
+constexpr int kDnThreads = kDnWaves * kWave;
+static_assert(kPfDnCols == kDnWaves * 32, "one 32-column block per down wave");
+// LDS: two A stages | semax [rows] | output exponents [rows] | pair of each
+// row [rows] | row maxima [waves][rows]
+constexpr int kPfDnLdsAll = 2 * kPfABytes + kPfRows * (4 + 4 + 4) + kDnWaves * kPfRows * 4;
+
 struct DnArgs {
     int H, I;
     const uint8_t *down;
     const uint16_t *h;
     const int32_t *hexp;
     const int32_t *counts, *offsets, *perm, *tiles, *n_tiles;
-    float *o;
+    float *o;           // fp32 outputs [pairs][H] (decode batches), or
+    uint16_t *o16;      // fp16 outputs [pairs][H] and their
+    int32_t *oexp;      // exponents [pairs][H / kPfDnCols, rounded up]
 };
 
-// Raw loads only (h piece and its chunk exponent): a rescale here would make
-// the wave wait for these loads before the current stage's MFMAs.
+// Stage pieces of a down workgroup: R rows x 16 chunks, thread
+// threadIdx.x + kDnThreads p taking piece p; the row test is wave-uniform.
 template <int R>
-BM_DEV void dn_stage_load(const DnArgs &a, const PfTile &t, int kb, int hf, u32x4 (&r)[R / 32], int (&ex)[R / 32]) {
+constexpr int dn_pieces() { return (16 * R + kDnThreads - 1) / kDnThreads; }
+BM_DEV StageIdx dn_stage_idx(int p) {
+    const int u = threadIdx.x + kDnThreads * p, q = u >> 6, l = u & 63;
+    return {8 * (q >> 1) + (l & 7), 8 * (q & 1) + (l >> 3)};
+}
+
+// Raw loads only (h piece and its chunk exponent): a rescale here would make
+// the wave wait for these loads before the current stage's MFMAs.  Pieces
+// past the tile's R rows re-read a valid row and are never stored.
+template <int R>
+BM_DEV void dn_stage_load(const DnArgs &a, const PfTile &t, int kb, int hf, u32x4 (&r)[dn_pieces<R>()],
+                          int (&ex)[dn_pieces<R>()]) {
     const int k0 = kb * kQK + hf * kPfHalf, nI = a.I / kPfGuCols;
 #pragma unroll
-    for (int p = 0; p < R / 32; p++) {
-        const StageIdx x = stage_idx(p);
-        const int64_t gr = t.off + t.r0 + min(x.row, t.rows - 1);
+    for (int p = 0; p < dn_pieces<R>(); p++) {
+        const StageIdx x = dn_stage_idx(p);
+        const int64_t gr = t.off + t.r0 + min(min(x.row, R - 1), t.rows - 1);
         r[p] = *reinterpret_cast<const u32x4 *>(a.h + gr * a.I + k0 + 8 * x.c);
         ex[p] = a.hexp[gr * nI + kb];
     }
 }
 
-// Rescale the loaded pieces to the row's largest exponent (exact: powers of two).
+// Rescale the loaded pieces to the row's largest exponent (exact: powers of
+// two) and store them into the stage buffer.
 template <int R>
-BM_DEV void dn_stage_scale(const int *semax, const int (&ex)[R / 32], u32x4 (&r)[R / 32]) {
+BM_DEV void dn_stage_put(uint8_t *dst, const int *semax, const int (&ex)[dn_pieces<R>()],
+                         u32x4 (&r)[dn_pieces<R>()]) {
 #pragma unroll
-    for (int p = 0; p < R / 32; p++) {
-        const int d = ex[p] - semax[stage_idx(p).row];
-        if (d != 0) {
-            const uint32_t f = f16_pow2(d) * 0x10001u;
-            r[p] = u32x4{pk_mul(r[p].x, f), pk_mul(r[p].y, f), pk_mul(r[p].z, f), pk_mul(r[p].w, f)};
+    for (int p = 0; p < dn_pieces<R>(); p++) {
+        const StageIdx x = dn_stage_idx(p);
+        if (x.row < R) {
+            const int d = ex[p] - semax[x.row];
+            if (d != 0) {
+                const uint32_t f = f16_pow2(d) * 0x10001u;
+                r[p] = u32x4{pk_mul(r[p].x, f), pk_mul(r[p].y, f), pk_mul(r[p].z, f), pk_mul(r[p].w, f)};
+            }
+            *reinterpret_cast<u32x4 *>(dst + (x.c * R + x.row) * 16) = r[p];
         }
     }
 }
 
-template <int MB>
+template <int MB, int OUT32>
 BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
-    constexpr int R = 32 * MB;
+    constexpr int R = 32 * MB, DP = dn_pieces<R>();
     uint8_t *const sa = lds;                             // A buffer b at sa + b * kPfABytes
     int *semax = reinterpret_cast<int *>(lds + 2 * kPfABytes);
+    int *soex = semax + kPfRows;
+    const int *spair = soex + kPfRows;
+    float *smax = reinterpret_cast<float *>(soex + 2 * kPfRows);
     const int lane = lane_id(), col = lane & 31, kh = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = a.I / kQK;
     const int64_t S = (int64_t)a.H * nb;
     const uint8_t *D = a.down + (int64_t)t.e * S * 84;
-    const int c0 = ntile * kPfDnCols + 64 * w + col;
-    const bool active = ntile * kPfDnCols + 64 * w < a.H;     // wave-uniform
-    uint32_t qoff[2], soff[2], doff[2];
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int cc = min(c0 + 32 * j, a.H - 1), P = cc >> 6, pr = cc & 63;
-        const uint32_t pk64 = (uint32_t)(P * nb * 64 + pr);          // (P nb + kb) 64 + r at kb = 0
-        qoff[j] = (uint32_t)((P * nb * 4 + kh) * 64 + pr) * 16;
-        soff[j] = (uint32_t)(S * 64) + pk64 * 16 + 4 * kh;
-        doff[j] = (uint32_t)(S * 80) + pk64 * 4;
-    }
-    struct Slot { uint4 w[2]; uint32_t sc[2], dd[2]; };     // words, 4 scale bytes, d|dmin per block
+    const int c0 = ntile * kPfDnCols + 32 * w + col;
+    const bool active = ntile * kPfDnCols + 32 * w < a.H;     // wave-uniform (H is a multiple of 256)
+    const int cc = min(c0, a.H - 1), P = cc >> 6, pr = cc & 63;
+    const uint32_t pk64 = (uint32_t)(P * nb * 64 + pr);          // (P nb + kb) 64 + r at kb = 0
+    const uint32_t qoff = (uint32_t)((P * nb * 4 + kh) * 64 + pr) * 16;
+    const uint32_t soff = (uint32_t)(S * 64) + pk64 * 16 + 4 * kh;
+    const uint32_t doff = (uint32_t)(S * 80) + pk64 * 4;
+    struct Slot { uint4 w; uint32_t sc, dd; };           // words, 4 scale bytes, d|dmin
     auto load_slot = [&](int st, Slot &sl) {
         const int kb = st >> 1, hf = st & 1;
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            sl.w[j] = *reinterpret_cast<const uint4 *>(D + qoff[j] + kb * 4096 + hf * 2048);
-            sl.sc[j] = *reinterpret_cast<const uint32_t *>(D + soff[j] + kb * 1024 + 8 * hf);
-            sl.dd[j] = *reinterpret_cast<const uint32_t *>(D + doff[j] + kb * 256);
-        }
+        sl.w = *reinterpret_cast<const uint4 *>(D + qoff + kb * 4096 + hf * 2048);
+        sl.sc = *reinterpret_cast<const uint32_t *>(D + soff + kb * 1024 + 8 * hf);
+        sl.dd = *reinterpret_cast<const uint32_t *>(D + doff + kb * 256);
     };
     const Q2kPairConsts pc;
     uint32_t nbias[5];
 #pragma unroll
-    for (int s = 0; s < 5; s++) {
-        uint32_t v = f16_pair(-(float)(1 << (10 - 2 * s)));
+    for (int q = 0; q < 5; q++) {
+        uint32_t v = f16_pair(-(float)(1 << (10 - 2 * q)));
         asm volatile("" : "+s"(v));
-        nbias[s] = v;
+        nbias[q] = v;
     }
-    f32x16 acc[MB][2];
+    f32x16 acc[MB];
 #pragma unroll
-    for (int i = 0; i < MB; i++) acc[i][0] = acc[i][1] = (f32x16)0.f;
+    for (int i = 0; i < MB; i++) acc[i] = (f32x16)0.f;
     auto compute = [&](const uint8_t *A, const Slot &sl) {
+        const float ds = kPfDnWScale * fp16_to_f32(sl.dd & 0xFFFFu);
+        const float ms = -kPfDnWScale * fp16_to_f32(sl.dd >> 16);
+        const uint32_t wsel[4] = {sl.w.x, sl.w.y, sl.w.z, sl.w.w};
 #pragma unroll
-        for (int s = 0; s < 8; s++) {
-            f16x8 b[2];
+        for (int sbk = 0; sbk < 4; sbk++) {                 // sub-block 4kh + sbk: k-steps 2 sbk, 2 sbk + 1
+            const uint32_t W = wsel[sbk], W10 = W >> 10;
+            // (a, -b) of this sub-block: a = d sc, b = dmin m
+            const uint32_t sb = (sl.sc >> (8 * sbk)) & 0xFFu;
+            const f16x2 av = u2h(f16_pair(ds * (float)(sb & 15u)));
+            const f16x2 bv = u2h(f16_pair(ms * (float)(sb >> 4)));
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const uint32_t wsel[4] = {sl.w[j].x, sl.w[j].y, sl.w[j].z, sl.w[j].w};
-                const uint32_t W = wsel[s >> 1], W10 = W >> 10;
-                // (a, -b) of this sub-block: a = d sc, b = dmin m
-                const uint32_t sb = (sl.sc[j] >> (8 * (s >> 1))) & 0xFFu;
-                const f16x2 av = u2h(f16_pair(kPfDnWScale * fp16_to_f32(sl.dd[j] & 0xFFFFu) * (float)(sb & 15u)));
-                const f16x2 bv = u2h(f16_pair(-kPfDnWScale * fp16_to_f32(sl.dd[j] >> 16) * (float)(sb >> 4)));
+            for (int half = 0; half < 2; half++) {
+                f16x8 af[MB];
+#pragma unroll
+                for (int i = 0; i < MB; i++) af[i] = frag32<R>(A, i, lane, 2 * sbk + half);
                 uint32_t qb[4];
-                if ((s & 1) == 0) {
+                if (half == 0) {
                     qb[0] = pc.pair<0>(W, W10); qb[1] = pc.pair<1>(W, W10);
                     qb[2] = pc.pair<2>(W, W10); qb[3] = pc.pair<3>(W, W10);
                 } else {
@@ -553,26 +584,24 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
                 uint4 v;
                 uint32_t *vv = reinterpret_cast<uint32_t *>(&v);
 #pragma unroll
-                for (int p = 0; p < 4; p++) {
-                    const int pp = ((s & 1) ? 4 : 0) + p, sh = pp < 5 ? pp : pp - 5;
-                    const f16x2 q = u2h(qb[p]) + u2h(nbias[sh]);          // exact quant
-                    vv[p] = h2u(__builtin_elementwise_fma(q, av, bv));    // a q - b
+                for (int q = 0; q < 4; q++) {
+                    const int pp = 4 * half + q, sh = pp < 5 ? pp : pp - 5;
+                    const f16x2 qv = u2h(qb[q]) + u2h(nbias[sh]);          // exact quant
+                    vv[q] = h2u(__builtin_elementwise_fma(qv, av, bv));    // a q - b
                 }
-                b[j] = __builtin_bit_cast(f16x8, v);
-            }
+                const f16x8 b = __builtin_bit_cast(f16x8, v);
 #pragma unroll
-            for (int i = 0; i < MB; i++) {
-                const f16x8 av = frag32<R>(A, i, lane, s);
-                acc[i][0] = mfma32(av, b[0], acc[i][0]);
-                acc[i][1] = mfma32(av, b[1], acc[i][1]);
+                for (int i = 0; i < MB; i++) acc[i] = mfma32(af[i], b, acc[i]);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
     };
     const int nsteps = 2 * nb;
-    u32x4 ar[R / 32];
-    int aex[R / 32];
-    auto stage = [&](auto full, int st, Slot &cur, Slot &pre) {      // as in gu_tile
+    u32x4 ar[DP];
+    int aex[DP];
+    // as in gu_tile: the slot of stage st+2 and the activations of st+1 are
+    // loaded at the start of stage st (activations first), three slots
+    // rotating by call
+    auto stage = [&](auto full, int st, Slot &cur, Slot &pre) {
         const int s1 = st + 1, s2 = st + 2;
         asm volatile("" ::: "memory");
         if (full || s1 < nsteps) dn_stage_load<R>(a, t, s1 >> 1, s1 & 1, ar, aex);
@@ -581,10 +610,7 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         if (active) compute(sa + (st & 1) * kPfABytes, cur);
-        if (full || s1 < nsteps) {
-            dn_stage_scale<R>(semax, aex, ar);
-            stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
-        }
+        if (full || s1 < nsteps) dn_stage_put<R>(sa + (s1 & 1) * kPfABytes, semax, aex, ar);
         __syncthreads();
     };
     using Full = std::integral_constant<bool, true>;
@@ -593,8 +619,7 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
     dn_stage_load<R>(a, t, 0, 0, ar, aex);
     load_slot(0, q0);
     if (nsteps > 1) load_slot(1, q1);
-    dn_stage_scale<R>(semax, aex, ar);
-    stage_store<R>(sa, ar);
+    dn_stage_put<R>(sa, semax, aex, ar);
     __builtin_amdgcn_s_waitcnt(0);       // see gu_tile
     __syncthreads();
     int st = 0;
@@ -607,41 +632,83 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
     if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0);
     if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1);
     if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2);
+    // epilogue: lane holds rows 32i + acc_row(r, kh), column c0
+    if (OUT32) {
+        if (!active) return;
+#pragma unroll
+        for (int i = 0; i < MB; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = 32 * i + acc_row(r, kh);
+                if (m < t.rows) a.o[(int64_t)spair[m] * a.H + c0] = ldexpf(acc[i][r], semax[m] - kPfDnWShift);
+            }
+        return;
+    }
+    // fp16 outputs: each row's largest |value| over the workgroup's 512
+    // columns (32 lanes of a half-wave by DPP, then the 16 waves through LDS)
+    // sets its power of two
+#pragma unroll
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            float mx = active ? fabsf(acc[i][r]) : 0.f;
+            mx = dpp_max<0x111, 0xF>(mx);
+            mx = dpp_max<0x112, 0xF>(mx);
+            mx = dpp_max<0x114, 0xF>(mx);
+            mx = dpp_max<0x118, 0xF>(mx);
+            mx = dpp_max<0x142, 0xA>(mx);
+            if (col == 31) smax[w * kPfRows + 32 * i + acc_row(r, kh)] = mx;
+        }
+    __syncthreads();
+    if (threadIdx.x < R) {
+        float mx = 0.f;
+#pragma unroll
+        for (int v = 0; v < kDnWaves; v++) mx = fmaxf(mx, smax[v * kPfRows + threadIdx.x]);
+        const int e = pf_exponent(mx);
+        soex[threadIdx.x] = e;
+        if ((int)threadIdx.x < t.rows)
+            a.oexp[(int64_t)spair[threadIdx.x] * ((a.H + kPfDnCols - 1) / kPfDnCols) + ntile] =
+                e + semax[threadIdx.x] - kPfDnWShift;
+    }
+    __syncthreads();
     if (!active) return;
 #pragma unroll
     for (int i = 0; i < MB; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int m = 32 * i + acc_row(r, kh);
-            if (m < t.rows) {
-                const int e = semax[m] - kPfDnWShift;
-                float *op = a.o + (int64_t)a.perm[t.off + t.r0 + m] * a.H;
-                op[c0] = ldexpf(acc[i][0][r], e);
-                op[c0 + 32] = ldexpf(acc[i][1][r], e);
-            }
+            if (m < t.rows) a.o16[(int64_t)spair[m] * a.H + c0] = (uint16_t)f16_bits(ldexpf(acc[i][r], -soex[m]));
         }
 }
 
-__global__ void __launch_bounds__(kPfThreads)
+template <int OUT32>
+__global__ void __launch_bounds__(kDnThreads)
 k_pf_down(DnArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    asm volatile("" ::: "a0");           // accumulators in AGPRs (see k_pf_gateup)
+    // (no AGPR hint: at most 48 accumulators, which fit beside the decode
+    // state in the 128 registers a wave may hold at four waves per SIMD)
     const PfSlot sl = pf_slot((a.H + kPfDnCols - 1) / kPfDnCols);
     if (sl.tile >= *a.n_tiles) return;
     const PfTile t = pf_tile(sl.tile, a.tiles, a.counts, a.offsets);
+    // each row's largest h exponent and its pair: every (row, 256-column
+    // chunk) exponent loaded at once, maxima by LDS atomics
     int *semax = reinterpret_cast<int *>(lds + 2 * kPfABytes);
+    const int nI = a.I / kPfGuCols;
     if (threadIdx.x < kPfRows) {
-        const int nI = a.I / kPfGuCols;
-        const int64_t gr = t.off + t.r0 + min((int)threadIdx.x, t.rows - 1);
-        int e = -(1 << 30);
-        for (int c = 0; c < nI; c++) e = max(e, a.hexp[gr * nI + c]);
-        semax[threadIdx.x] = e;
+        semax[threadIdx.x] = -(1 << 30);
+        semax[2 * kPfRows + threadIdx.x] = a.perm[t.off + t.r0 + min((int)threadIdx.x, t.rows - 1)];
+    }
+    __syncthreads();
+    for (int u = threadIdx.x; u < kPfRows * nI; u += kDnThreads) {
+        const int m = u / nI, c = u - m * nI;
+        const int64_t gr = t.off + t.r0 + min(m, t.rows - 1);
+        atomicMax(&semax[m], a.hexp[gr * nI + c]);
     }
     __syncthreads();
     switch ((t.rows + 31) >> 5) {
-        case 1: dn_tile<1>(a, lds, t, sl.ntile); break;
-        case 2: dn_tile<2>(a, lds, t, sl.ntile); break;
-        default: dn_tile<3>(a, lds, t, sl.ntile); break;
+        case 1: dn_tile<1, OUT32>(a, lds, t, sl.ntile); break;
+        case 2: dn_tile<2, OUT32>(a, lds, t, sl.ntile); break;
+        default: dn_tile<3, OUT32>(a, lds, t, sl.ntile); break;
     }
 }
 
@@ -694,35 +761,50 @@ k_shared_down_rows(int H, int I, const uint4 *__restrict__ sd, const float *__re
     os[(int64_t)t * H + P * 64 + lane] = acc;
 }
 
-// y[t][n] = sum_j w[t][j] o[t k + j][n] (+ os[t][n]): four consecutive
-// outputs per thread, the k rows' 16-byte loads issued together (k <= KMAX).
+// y[t][n] = sum_j w[t][j] o[t k + j][n] (+ os[t][n]) with o in fp16 and one
+// power-of-two exponent per (pair, 512 columns): eight consecutive outputs
+// per thread, the k rows' 16-byte loads issued together (k <= KMAX), slots
+// summed in order.
 template <int KMAX>
 __global__ void __launch_bounds__(256)
-k_combine_p(const float *__restrict__ o, const float *__restrict__ w, const float *__restrict__ os,
-            float *__restrict__ y, int T, int H, int k) {
-    const int H4 = H / 4;
+k_combine_p(const uint16_t *__restrict__ o16, const int32_t *__restrict__ oexp, const float *__restrict__ w,
+            const float *__restrict__ os, float *__restrict__ y, int T, int H, int k) {
+    const int H8 = H / 8, nN = (H + kPfDnCols - 1) / kPfDnCols;
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q >= (int64_t)T * H4) return;
-    const int t = (int)(q / H4), n4 = (int)(q - (int64_t)t * H4);
-    const float4 *o4 = reinterpret_cast<const float4 *>(o) + (int64_t)t * k * H4 + n4;
-    float4 v[KMAX];
+    if (q >= (int64_t)T * H8) return;
+    const int t = (int)(q / H8), n8 = (int)(q - (int64_t)t * H8), tile = 8 * n8 / kPfDnCols;
+    const uint4 *o4 = reinterpret_cast<const uint4 *>(o16) + (int64_t)t * k * H8 + n8;
+    uint4 v[KMAX];
+    int e[KMAX];
 #pragma unroll
-    for (int j = 0; j < KMAX; j++) v[j] = o4[(int64_t)min(j, k - 1) * H4];
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < KMAX; j++) {
+        const int jj = min(j, k - 1);
+        v[j] = o4[(int64_t)jj * H8];
+        e[j] = oexp[((int64_t)t * k + jj) * nN + tile];
+    }
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) s[i] = 0.f;
 #pragma unroll
     for (int j = 0; j < KMAX; j++)
         if (j < k) {
-            const float wj = w[t * k + j];
-            s.x = fmaf(wj, v[j].x, s.x);
-            s.y = fmaf(wj, v[j].y, s.y);
-            s.z = fmaf(wj, v[j].z, s.z);
-            s.w = fmaf(wj, v[j].w, s.w);
+            const float wj = ldexpf(w[t * k + j], e[j]);
+            const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                s[2 * i] = fmaf(wj, fp16_to_f32(u[i] & 0xFFFFu), s[2 * i]);
+                s[2 * i + 1] = fmaf(wj, fp16_to_f32(u[i] >> 16), s[2 * i + 1]);
+            }
         }
     if (os) {
-        const float4 a = reinterpret_cast<const float4 *>(os)[q];
-        s.x += a.x; s.y += a.y; s.z += a.z; s.w += a.w;
+        const float4 *a4 = reinterpret_cast<const float4 *>(os + (int64_t)t * H + 8 * n8);
+        const float4 a = a4[0], b = a4[1];
+        s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+        s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
     }
-    reinterpret_cast<float4 *>(y)[q] = s;
+    float4 *y4 = reinterpret_cast<float4 *>(y + (int64_t)t * H + 8 * n8);
+    y4[0] = make_float4(s[0], s[1], s[2], s[3]);
+    y4[1] = make_float4(s[4], s[5], s[6], s[7]);
 }
 
 }  // namespace
@@ -738,8 +820,10 @@ int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int
                fa.sharedSizeBytes == 0 &&
                hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_gateup),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, kPfGuLds) == hipSuccess &&
-               hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_down),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, kPfDnLds) == hipSuccess;
+               hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_down<0>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, kPfDnLdsAll) == hipSuccess &&
+               hipFuncSetAttribute(reinterpret_cast<const void *>(k_pf_down<1>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, kPfDnLdsAll) == hipSuccess;
     }();
     if (!attr) return BITMOE_EHIP;
     if (x_dtype == BITMOE_BF16) k_pf_xprep<1><<<T, 256, 0, s>>>(H, x, pb.x16, pb.xsc);
@@ -755,11 +839,14 @@ int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int
         BM_LAUNCH_CHECK();
     }
     {
+        // fp16 outputs with exponents when the buffers are given (prefill),
+        // fp32 otherwise (decode batches)
         DnArgs a{H, I, (const uint8_t *)L->down_q, pb.h, pb.hexp, b.counts, b.offsets, b.perm, b.tiles,
-                 b.n_tiles, pb.o};
+                 b.n_tiles, pb.o, pb.o16, pb.oexp};
         const TimingEvents ev = timing_for(BITMOE_TIME_DOWN);
-        hipExtLaunchKernelGGL(k_pf_down, dim3(pf_grid(max_tiles, (H + kPfDnCols - 1) / kPfDnCols)), dim3(kPfThreads),
-                              kPfDnLds, s, ev.start, ev.stop, 0, a);
+        hipExtLaunchKernelGGL(pb.o16 ? k_pf_down<0> : k_pf_down<1>,
+                              dim3(pf_grid(max_tiles, (H + kPfDnCols - 1) / kPfDnCols)), dim3(kDnThreads),
+                              kPfDnLdsAll, s, ev.start, ev.stop, 0, a);
         BM_LAUNCH_CHECK();
     }
     return BITMOE_OK;
@@ -784,9 +871,9 @@ int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T,
         BM_LAUNCH_CHECK();
     }
     if (reinterpret_cast<uintptr_t>(y) % 16) return BITMOE_EINVAL;
-    const int64_t n4 = (int64_t)T * H / 4;
+    const int64_t n8 = (int64_t)T * H / 8;
     auto kc = k <= 8 ? k_combine_p<8> : k_combine_p<16>;
-    kc<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(pb.o, w, shared ? pb.os : nullptr, y, T, H, k);
+    kc<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(pb.o16, pb.oexp, w, shared ? pb.os : nullptr, y, T, H, k);
     BM_LAUNCH_CHECK();
     return BITMOE_OK;
 }

@@ -317,18 +317,23 @@ def _scaled_layer_case(w, d_of_block):
     return lay, per(gate, ng), per(up, ng), per(down, nd)
 
 
-@pytest.mark.parametrize("case", ["d=8", "d=2^-19", "log-uniform"])
+@pytest.mark.parametrize("case", ["d=8", "d=2^-19", "per-expert log-uniform"])
 def test_scale_envelope_both_paths(case):
     """Superblock scales at both ends of the range the prefill fp16 operands
     hold exactly in their normal range (d, dmin in [2^-19, 8]: largest IQ2X
-    weight 27.1 d, largest Q2K term 45 d), and log-uniform over it; decode and
-    prefill against the oracle on the same blocks."""
+    weight 27.1 d, largest Q2K term 45 d), and one scale per expert tensor
+    drawn log-uniformly over it (experts 2^22 apart in one token's sum);
+    decode and prefill against the oracle on the same blocks."""
     require_gpu()
     w = synth.WORKLOADS["tiny"].with_(name=f"tiny_env", T=37, x_dtype="bf16", seed=51)
     rng = np.random.default_rng(5)
+
+    def per_expert(n):
+        per = n // w.E
+        return np.repeat(np.exp2(rng.uniform(-19, 3, w.E)), per)
     pick = {"d=8": lambda n: np.full(n, 8.0),
             "d=2^-19": lambda n: np.full(n, 2.0 ** -19),
-            "log-uniform": lambda n: np.exp2(rng.uniform(-19, 3, n))}[case]
+            "per-expert log-uniform": per_expert}[case]
     lay, gate, up, down = _scaled_layer_case(w, pick)
     x, _ = synth.make_tokens(w)
     ids, wt = _routing(w, x)
