@@ -7,7 +7,9 @@ sources and readings).
 
 Parity status: dequantisation, routing, bucketing and the FFN are pinned by
 tests that do not re-use this code (hand-decoded golden blocks, closed forms,
-invariants, and dense float64 matrix products on small shapes).
+invariants, and dense float64 matrix products on small shapes); the
+quantizer (quant.c) by exact round trips of representable blocks, brute-force
+optimality of every run and sub-block choice, and never-worse-than-start.
 """
 from __future__ import annotations
 
@@ -39,6 +41,8 @@ def lib():
         L.oracle_bucket.argtypes = [P, I32, I32, I32, P, P, P]
         L.oracle_moe_ffn.argtypes = [I32, I32, I32, I32, P, P, P, P, P, P, P,
                                      P, I32, I32, P, P, P]
+        L.oracle_quantize_iq2x.argtypes = [P, P, I64, P]
+        L.oracle_quantize_q2k.argtypes = [P, I64, P]
         L.oracle_max_threads.restype = I32
         L.oracle_set_threads.argtypes = [I32]
         _lib = L
@@ -75,6 +79,26 @@ def dequant_q2k(blocks: np.ndarray) -> np.ndarray:
     b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1, 84)
     out = np.empty(b.shape[0] * 256, dtype=np.float64)
     lib().oracle_dequant_q2k(_p(b), b.shape[0], _p(out))
+    return out
+
+
+def quantize_iq2x(w: np.ndarray, grid: np.ndarray) -> np.ndarray:
+    """float32 weights [n * 256] -> canonical IQ2X blocks uint8 [n, 66]
+    (error-minimising search of quant.c)."""
+    wf = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+    assert wf.size % 256 == 0
+    g = np.ascontiguousarray(grid, dtype=np.uint8).reshape(256, 8)
+    out = np.empty((wf.size // 256, 66), dtype=np.uint8)
+    lib().oracle_quantize_iq2x(_p(wf), _p(g), out.shape[0], _p(out))
+    return out
+
+
+def quantize_q2k(w: np.ndarray) -> np.ndarray:
+    """float32 weights [n * 256] -> canonical Q2K blocks uint8 [n, 84]."""
+    wf = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+    assert wf.size % 256 == 0
+    out = np.empty((wf.size // 256, 84), dtype=np.uint8)
+    lib().oracle_quantize_q2k(_p(wf), out.shape[0], _p(out))
     return out
 
 

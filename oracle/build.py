@@ -6,13 +6,13 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "oracle.c")
+SRC = [os.path.join(HERE, "oracle.c"), os.path.join(HERE, "quant.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC",
-           "-shared", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+           "-shared", "-Wall", "-Wextra", "-o", LIB + ".tmp", *SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
