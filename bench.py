@@ -264,6 +264,58 @@ def prefill_8k_zipf(args, lays):
     return dict(ms=ms, stats=stats, flops=flops, rows_max=int(rows.max()), rows_min=int(rows.min()))
 
 
+FP64_OPS_PEAK = 256 * 64 * 2.4e9   # unfused fp64 operations/s: 256 CUs x 64 lanes x 2.4 GHz
+
+# fp64 operations of the IQ2X search per superblock, error terms only:
+# 8 groups x 16 scales x 4 runs x 256 codebook rows x 8 weights x 4
+# (db*g, difference, square, accumulate)
+IQ2X_OPS_PER_SB = 8 * 16 * 4 * 256 * 8 * 4
+
+
+def quantize_bench(args):
+    """The quantizer on one full expert tensor per format (2048 x 7168 gate/up
+    weights to IQ2X, 7168 x 2048 down weights to Q2K: 57344 superblocks
+    each), synthetic N(0, 1/(10.6 sqrt(K))) weights resident in HBM."""
+    import numpy as np
+    import torch
+    import bit_moe_amd as bm
+    import synth
+    n = 2048 * 7168 // 256
+    rng = np.random.default_rng(7)
+    w = torch.from_numpy((rng.standard_normal(n * 256) / (10.6 * np.sqrt(7168))).astype(np.float32)).cuda()
+    grid = torch.from_numpy(synth.make_layer(synth.WORKLOADS["decode_b1"]).grid()).cuda()
+    oi = torch.empty((n, 66), dtype=torch.uint8, device="cuda")
+    oq = torch.empty((n, 84), dtype=torch.uint8, device="cuda")
+    ms_i, st_i = time_steps(lambda i: bm.quantize_iq2x(w, grid, out=oi), 1, 5)
+    ms_q, st_q = time_steps(lambda i: bm.quantize_q2k(w, out=oq), 2, 20)
+    return dict(n=n, ms_iq2x=ms_i, ms_q2k=ms_q, st_iq2x=st_i, st_q2k=st_q, w=w.cpu().numpy(),
+                grid=grid.cpu().numpy())
+
+
+def quantize_cpu_baseline(w, grid, target_s):
+    """The oracle's encoder (all host threads) on a bounded sample of the
+    same tensor's superblocks, IQ2X then Q2K."""
+    import numpy as np
+    import oracle
+    out = {}
+    for fmt, first in (("iq2x", 64), ("q2k", 4096)):
+        nb, spent = first, 0.0
+        while True:
+            x = np.ascontiguousarray(w[:nb * 256])
+            t0 = time.perf_counter()
+            if fmt == "iq2x":
+                oracle.quantize_iq2x(x, grid)
+            else:
+                oracle.quantize_q2k(x)
+            spent = time.perf_counter() - t0
+            if spent >= target_s / 4 or nb * 256 * 2 > w.size:
+                break
+            nb *= 2
+        out[fmt] = dict(value=nb * 256 / spent, unit="weights/s", cores=oracle.max_threads(), cpu=cpu_model(),
+                        kind="oracle", sample=f"the first {nb} superblocks of the tensor, {spent:.2f} s")
+    return out
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -593,7 +645,27 @@ def main():
                                   "rows_per_expert_max": p8["rows_max"], "rows_per_expert_min": p8["rows_min"],
                                   "note": "step = top-k of drawn Zipf(1.2) logits + prefill FFN"}
         log(f"[bench] prefill_8k_zipf {p8['ms']:.2f} ms/step")
+        qb = quantize_bench(args)
+        iq_ops = qb["n"] * IQ2X_OPS_PER_SB / (qb["ms_iq2x"] * 1e-3)
+        q_bytes = qb["n"] * (256 * 4 + 84) / (qb["ms_q2k"] * 1e-3)
+        out["quantize"] = {
+            "workload": "one 2048 x 7168 expert tensor of fp32 weights (57344 superblocks) per format",
+            "iq2x": {"weights_per_s": qb["n"] * 256 / (qb["ms_iq2x"] * 1e-3), "ms": qb["ms_iq2x"],
+                     "ms_dist": qb["st_iq2x"],
+                     "roofline": {"bound": "alu", "unit": "Gop/s (fp64, unfused)", "achieved": iq_ops / 1e9,
+                                  "peak": FP64_OPS_PEAK / 1e9, "frac": iq_ops / FP64_OPS_PEAK,
+                                  "ops_per_superblock": IQ2X_OPS_PER_SB, "traffic": None}},
+            "q2k": {"weights_per_s": qb["n"] * 256 / (qb["ms_q2k"] * 1e-3), "ms": qb["ms_q2k"],
+                    "ms_dist": qb["st_q2k"],
+                    "roofline": {"bound": "hbm", "unit": "GB/s", "achieved": q_bytes / 1e9, "peak": HBM_PEAK / 1e9,
+                                 "frac": q_bytes / HBM_PEAK, "bytes_per_superblock": 256 * 4 + 84,
+                                 "traffic": None}}}
+        log(f"[bench] quantize iq2x {qb['ms_iq2x']:.2f} ms, q2k {qb['ms_q2k']:.3f} ms per tensor")
     if not args.no_cpu_baseline:
+        if not args.no_extra:
+            for fmt, cb in quantize_cpu_baseline(qb["w"], qb["grid"], args.cpu_seconds / 2).items():
+                out["quantize"][fmt]["cpu_baseline"] = cb
+                log(f"[bench] cpu baseline quantize {fmt} {cb['value']:.3g} weights/s")
         out["cpu_baseline"] = cpu_baseline("decode_b1", args.cpu_seconds)
         log(f"[bench] cpu baseline {out['cpu_baseline']['value']:.3f} tokens/s")
         if not args.no_extra:

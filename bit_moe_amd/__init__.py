@@ -6,7 +6,7 @@ library's HIP kernels.
 """
 from ._lib import (BF16, BitMoEError, DECODE, F32, Layer, PREFILL, SYMBOLS, TIME_DOWN, TIME_GATEUP, bucket,
                    dequant_iq2x,
-                   dequant_q2k, ffn_decode, ffn_prefill, forward_decode, forward_decode_noalloc, lib, pack_bf16, pack_iq2x, pack_q2k, route,
+                   dequant_q2k, ffn_decode, ffn_prefill, forward_decode, forward_decode_noalloc, lib, quantize_iq2x, quantize_q2k, pack_bf16, pack_iq2x, pack_q2k, route,
                    route_workspace_bytes, set_timing_events, strerror, topk, version,
                    workspace_bytes)
 
@@ -39,6 +39,6 @@ def layer_from_canonical(H, I, E, k, router_bits, gate, up, down, grid, shared=N
 
 __all__ = ["BF16", "BitMoEError", "DECODE", "F32", "Layer", "PREFILL", "SYMBOLS", "TIME_DOWN", "TIME_GATEUP", "bucket",
            "dequant_iq2x", "dequant_q2k", "ffn_decode", "ffn_prefill", "forward_decode", "forward_decode_noalloc",
-           "layer_from_canonical", "lib",
+           "layer_from_canonical", "quantize_iq2x", "quantize_q2k", "lib",
            "pack_bf16", "pack_iq2x", "pack_q2k", "route", "route_workspace_bytes", "set_timing_events", "strerror", "topk",
            "version", "workspace_bytes"]

@@ -26,7 +26,7 @@ SYMBOLS = [
     "moe_route_workspace_bytes", "moe_route", "moe_topk", "moe_bucket_workspace_bytes",
     "moe_bucket", "moe_workspace_bytes", "moe_ffn_decode", "moe_forward_decode", "moe_forward_decode_noalloc",
     "moe_ffn_prefill",
-    "moe_dequant_iq2x", "moe_dequant_q2k", "moe_pack_iq2x", "moe_pack_q2k", "moe_pack_bf16",
+    "moe_dequant_iq2x", "moe_dequant_q2k", "moe_quantize_iq2x", "moe_quantize_q2k", "moe_pack_iq2x", "moe_pack_q2k", "moe_pack_bf16",
     "moe_set_timing_events", "moe_strerror", "moe_version",
 ]
 
@@ -70,6 +70,8 @@ def lib() -> C.CDLL:
         "moe_forward_decode_noalloc": ([LP, P, I, I, P, P, P, P], I),
         "moe_dequant_iq2x": ([P, P, I64, P, I, P], I),
         "moe_dequant_q2k": ([P, I64, P, I, P], I),
+        "moe_quantize_iq2x": ([P, P, I64, P, P], I),
+        "moe_quantize_q2k": ([P, I64, P, P], I),
         "moe_pack_iq2x": ([P, P, I, I, I, P], I),
         "moe_pack_q2k": ([P, P, I, I, I, P], I),
         "moe_pack_bf16": ([P, P, I, I, P], I),
@@ -301,6 +303,30 @@ def dequant_q2k(blocks, out_dtype=F32, stream=None):
     _dev_check(blocks)
     _check(lib().moe_dequant_q2k(_ptr(blocks), nb, _ptr(out), out_dtype, _stream(stream)),
            "moe_dequant_q2k")
+    return out
+
+
+def quantize_iq2x(w, grid, out=None, stream=None):
+    """float32 weights (numel a multiple of 256) -> canonical IQ2X blocks
+    uint8 [n, 66] (moe_quantize_iq2x)."""
+    torch = _torch()
+    nb = w.numel() // 256
+    if out is None:
+        out = torch.empty((nb, 66), dtype=torch.uint8, device=w.device)
+    _dev_check(w, grid, out)
+    _check(lib().moe_quantize_iq2x(_ptr(w), _ptr(grid), nb, _ptr(out), _stream(stream)), "moe_quantize_iq2x")
+    return out
+
+
+def quantize_q2k(w, out=None, stream=None):
+    """float32 weights (numel a multiple of 256) -> canonical Q2K blocks
+    uint8 [n, 84] (moe_quantize_q2k)."""
+    torch = _torch()
+    nb = w.numel() // 256
+    if out is None:
+        out = torch.empty((nb, 84), dtype=torch.uint8, device=w.device)
+    _dev_check(w, out)
+    _check(lib().moe_quantize_q2k(_ptr(w), nb, _ptr(out), _stream(stream)), "moe_quantize_q2k")
     return out
 
 

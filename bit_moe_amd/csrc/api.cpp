@@ -312,6 +312,20 @@ int moe_dequant_q2k(const void *blocks, int64_t nblocks, void *out, int out_dtyp
     return bm_host::launch_dequant_q2k(blocks, nblocks, out, out_dtype, as_stream(stream));
 }
 
+int moe_quantize_iq2x(const float *w, const void *grid, int64_t nblocks, void *blocks, void *stream) {
+    if (nblocks < 0) return BITMOE_EINVAL;
+    if (nblocks == 0) return BITMOE_OK;
+    if (!w || !grid || !blocks || !aligned(w, 16) || !aligned(grid, 8)) return BITMOE_EINVAL;
+    return bm_host::launch_quant_iq2x(w, grid, nblocks, blocks, as_stream(stream));
+}
+
+int moe_quantize_q2k(const float *w, int64_t nblocks, void *blocks, void *stream) {
+    if (nblocks < 0) return BITMOE_EINVAL;
+    if (nblocks == 0) return BITMOE_OK;
+    if (!w || !blocks || !aligned(w, 16)) return BITMOE_EINVAL;
+    return bm_host::launch_quant_q2k(w, nblocks, blocks, as_stream(stream));
+}
+
 int moe_pack_iq2x(const void *src, void *dst, int E, int N, int K, void *stream) {
     if (E < 0 || N < 0 || K < 0) return BITMOE_EINVAL;
     if (N % 64 || K % 256) return BITMOE_EUNSUPPORTED;

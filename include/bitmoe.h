@@ -289,6 +289,32 @@ int moe_dequant_q2k(const void *blocks, int64_t nblocks, void *out,
                     int out_dtype, void *stream);
 
 /*
+ * Quantizer (the step before the layer): fp32 weights -> CANONICAL blocks,
+ * nblocks superblocks of 256 consecutive weights of one row each.  The
+ * routed experts are quantised asymmetrically to 2 bits, up/gate in IQ2_XXS
+ * and down in Q2_K ("antirez/ds4 ...", section "Poids du modele"), with an
+ * importance matrix ("ds4 : un MoE de 284 milliards sur un Mac de 128 Go",
+ * section "Comment un 284B tient en memoire"); with no calibration data the
+ * search minimises the plain squared error:
+ *  IQ2X: d = fp16(max|w| / 27.125); per group of 32 the group scale 0..15
+ *   and per run of 8 the codebook row (of grid, uint8 [256][8]) and signs
+ *   (those of w, with the cheapest single flip when the parity rule needs
+ *   one) of least squared error; ties to the lower row, scale, element.
+ *  Q2K: per sub-block of 16, m = max(0, -min w), a = (max w + m) / 3;
+ *   d = fp16(max a / 15), dmin = fp16(max m / 15); per sub-block the best
+ *   (scale, min) codes within +-1 of rint(a / d), rint(m / dmin), quants
+ *   clamp(rint((w + M) / A), 0, 3).
+ * Every decision is taken in double precision with unfused operations in a
+ * fixed order, so the bytes depend on the input alone.  fp16(x) is the
+ * nearest binary16 (ties to even), at most 65504.
+ * w: float32 [nblocks * 256], 16-byte aligned; blocks: uint8 [nblocks][66]
+ * or [nblocks][84].  Errors: EINVAL (null or misaligned pointer, nblocks <
+ * 0), EHIP.
+ */
+int moe_quantize_iq2x(const float *w, const void *grid, int64_t nblocks, void *blocks, void *stream);
+int moe_quantize_q2k(const float *w, int64_t nblocks, void *blocks, void *stream);
+
+/*
  * Load-time layout transforms (canonical -> TILED, see above), E experts of
  * an [N][K] projection; N multiple of 64, K multiple of 256 (bf16: of 8).
  * The canonical order is GGML's ("antirez/ds4 ...", section "Remerciements

@@ -198,3 +198,15 @@ def test_noalloc_refuses_calls_beyond_its_static_scratch():
     canon = _layer(layout=_lib.LAYOUT_CANONICAL)
     assert L.moe_forward_decode_noalloc(C.byref(canon), 16, 1, 4, 16, 16, 16, None) == _lib.EUNSUPPORTED
     assert "static" in bm.strerror(_lib.ESCRATCH)
+
+
+def test_quantize_argument_checks():
+    L = bm.lib()
+    assert L.moe_quantize_iq2x(16, 16, 0, 16, None) == 0
+    assert L.moe_quantize_iq2x(16, 16, -1, 16, None) == _lib.EINVAL
+    assert L.moe_quantize_iq2x(None, 16, 4, 16, None) == _lib.EINVAL
+    assert L.moe_quantize_iq2x(16, None, 4, 16, None) == _lib.EINVAL
+    assert L.moe_quantize_iq2x(8, 16, 4, 16, None) == _lib.EINVAL       # misaligned weights
+    assert L.moe_quantize_q2k(16, 4, None, None) == _lib.EINVAL
+    assert L.moe_quantize_q2k(16, -2, 16, None) == _lib.EINVAL
+    assert L.moe_quantize_q2k(16, 0, None, None) == 0
