@@ -272,6 +272,78 @@ FP64_OPS_PEAK = 256 * 64 * 2.4e9   # unfused fp64 operations/s: 256 CUs x 64 lan
 IQ2X_OPS_PER_SB = 8 * 16 * 4 * 256 * 8 * 4
 
 
+def cache_bench(args, lays, slots=96, steps=48, warm=8):
+    """Decode batch 16 with Zipf(1.1) routing drawn anew each step, routed
+    experts served from a pool of `slots` HBM slots (of 256) over pinned host
+    slabs: top-k on the GPU, ids to the host, the cache's map (copies of the
+    missing experts on the stream), the decode FFN on the pool.  The step
+    includes the device-to-host sync the host-side policy needs.  Returns
+    tokens/s, hit rate, host-to-device bytes, and the bandwidth of a plain
+    pinned copy of one expert's slabs (the roofline's peak)."""
+    import numpy as np
+    import torch
+    import bit_moe_amd as bm
+    import synth
+    w = synth.WORKLOADS["decode_b16_zipf"]
+    lay = lays[0]
+    host = tuple(t.cpu().pin_memory() for t in lay.tensors[1:4])
+    cache = bm.ExpertCache(lay, host, slots)
+    R = steps + warm
+    xs, lgs = [], []
+    for r in range(R):
+        wr = w.with_(seed=w.seed + 7000 + r)
+        x, _ = synth.make_tokens(wr)
+        xs.append(torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda())
+        lgs.append(torch.from_numpy(synth.zipf_logits(wr)).cuda())
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+    y = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+    ids_h = torch.empty((w.T, w.k), dtype=torch.int32).pin_memory()
+    slot_d = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(bm.workspace_bytes(cache.layer, w.T, bm.DECODE), dtype=torch.uint8, device="cuda")
+    copied = [0]
+
+    def step(i):
+        bm.topk(lgs[i], w.k, ids=ids, w=wt)
+        ids_h.copy_(ids)                               # synchronous: the policy runs on the host
+        sl, n = cache.map(ids_h)
+        copied[0] += n
+        slot_d.copy_(sl, non_blocking=True)
+        bm.ffn_decode(cache.layer, xs[i], slot_d, wt, y=y, ws=ws)
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    h0, m0, _ = cache.stats()
+    copied[0] = 0
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(warm, R):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    h1, m1, _ = cache.stats()
+    cache.close()
+    eb = 2 * w.I * (w.H // 256) * 66 + w.H * (w.I // 256) * 84          # one expert's slabs
+    # a plain pinned host-to-device copy of the same size as one expert's slabs
+    src = torch.empty(eb, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(eb, dtype=torch.uint8, device="cuda")
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    c0.record()
+    for _ in range(20):
+        dst.copy_(src, non_blocking=True)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_bw = 20 * eb / (c0.elapsed_time(c1) * 1e-3)
+    hits, misses = h1 - h0, m1 - m0
+    return dict(ms=ms, slots=slots, steps=steps, hits=hits, misses=misses, copied=copied[0], expert_bytes=eb,
+                h2d_bytes_per_step=copied[0] * eb / steps, copy_bw=copy_bw)
+
+
 def quantize_bench(args):
     """The quantizer on one full expert tensor per format (2048 x 7168 gate/up
     weights to IQ2X, 7168 x 2048 down weights to Q2K: 57344 superblocks
@@ -645,6 +717,19 @@ def main():
                                   "rows_per_expert_max": p8["rows_max"], "rows_per_expert_min": p8["rows_min"],
                                   "note": "step = top-k of drawn Zipf(1.2) logits + prefill FFN"}
         log(f"[bench] prefill_8k_zipf {p8['ms']:.2f} ms/step")
+        cb = cache_bench(args, lays)
+        h2d = cb["h2d_bytes_per_step"] / (cb["ms"] * 1e-3)
+        out["expert_cache"] = {
+            "workload": f"decode batch 16, Zipf(1.1) routing drawn per step, {cb['slots']} HBM slots of 256 experts "
+                        "over pinned host slabs; step = top-k, ids to host, cache map (copies of misses), decode FFN",
+            "tokens_per_s": 16 / (cb["ms"] * 1e-3), "ms_per_step": cb["ms"], "steps": cb["steps"],
+            "hit_rate": cb["hits"] / max(1, cb["hits"] + cb["misses"]), "experts_copied_per_step": cb["copied"] / cb["steps"],
+            "roofline": {"bound": "pcie", "unit": "GB/s", "achieved": h2d / 1e9, "peak": cb["copy_bw"] / 1e9,
+                         "frac": h2d / cb["copy_bw"], "peak_note": "a plain pinned host-to-device copy of one "
+                         "expert's slabs, measured in the same run", "traffic": None}}
+        log(f"[bench] expert_cache {cb['ms']:.3f} ms/step, hit rate {out['expert_cache']['hit_rate']:.3f}, "
+            f"{cb['copied'] / cb['steps']:.1f} experts copied per step, H2D {h2d / 1e9:.1f} GB/s "
+            f"(plain copy {cb['copy_bw'] / 1e9:.1f} GB/s)")
         qb = quantize_bench(args)
         iq_ops = qb["n"] * IQ2X_OPS_PER_SB / (qb["ms_iq2x"] * 1e-3)
         q_bytes = qb["n"] * (256 * 4 + 84) / (qb["ms_q2k"] * 1e-3)

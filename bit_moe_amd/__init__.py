@@ -4,7 +4,7 @@ Python binding over libbitmoe.so (see include/bitmoe.h).  PyTorch provides
 device memory and streams only; every step of the layer runs in the
 library's HIP kernels.
 """
-from ._lib import (BF16, BitMoEError, DECODE, F32, Layer, PREFILL, SYMBOLS, TIME_DOWN, TIME_GATEUP, bucket,
+from ._lib import (BF16, BitMoEError, DECODE, ExpertCache, F32, Layer, PREFILL, SYMBOLS, TIME_DOWN, TIME_GATEUP, bucket,
                    dequant_iq2x,
                    dequant_q2k, ffn_decode, ffn_prefill, forward_decode, forward_decode_noalloc, lib, quantize_iq2x, quantize_q2k, pack_bf16, pack_iq2x, pack_q2k, route,
                    route_workspace_bytes, set_timing_events, strerror, topk, version,
@@ -37,7 +37,7 @@ def layer_from_canonical(H, I, E, k, router_bits, gate, up, down, grid, shared=N
     return Layer(H, I, E, k, router, gq, uq, dq, g, sh)
 
 
-__all__ = ["BF16", "BitMoEError", "DECODE", "F32", "Layer", "PREFILL", "SYMBOLS", "TIME_DOWN", "TIME_GATEUP", "bucket",
+__all__ = ["BF16", "BitMoEError", "DECODE", "ExpertCache", "F32", "Layer", "PREFILL", "SYMBOLS", "TIME_DOWN", "TIME_GATEUP", "bucket",
            "dequant_iq2x", "dequant_q2k", "ffn_decode", "ffn_prefill", "forward_decode", "forward_decode_noalloc",
            "layer_from_canonical", "quantize_iq2x", "quantize_q2k", "lib",
            "pack_bf16", "pack_iq2x", "pack_q2k", "route", "route_workspace_bytes", "set_timing_events", "strerror", "topk",

@@ -28,6 +28,8 @@ SYMBOLS = [
     "moe_ffn_prefill",
     "moe_dequant_iq2x", "moe_dequant_q2k", "moe_quantize_iq2x", "moe_quantize_q2k", "moe_pack_iq2x", "moe_pack_q2k", "moe_pack_bf16",
     "moe_set_timing_events", "moe_strerror", "moe_version",
+    "moe_cache_pool_bytes", "moe_cache_create", "moe_cache_layer", "moe_cache_map", "moe_cache_stats",
+    "moe_cache_destroy",
 ]
 
 
@@ -77,6 +79,12 @@ def lib() -> C.CDLL:
         "moe_pack_bf16": ([P, P, I, I, P], I),
         "moe_set_timing_events": ([P, P, I], I),
         "moe_strerror": ([I], C.c_char_p),
+        "moe_cache_pool_bytes": ([LP, I], SZ),
+        "moe_cache_create": ([LP, P, P, P, I, P, SZ, C.POINTER(C.c_void_p)], I),
+        "moe_cache_layer": ([P, LP], I),
+        "moe_cache_map": ([P, P, I, P, P, P], I),
+        "moe_cache_stats": ([P, C.POINTER(C.c_int64), C.POINTER(C.c_int64), P], I),
+        "moe_cache_destroy": ([P], I),
         "moe_version": ([], C.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -304,6 +312,71 @@ def dequant_q2k(blocks, out_dtype=F32, stream=None):
     _check(lib().moe_dequant_q2k(_ptr(blocks), nb, _ptr(out), out_dtype, _stream(stream)),
            "moe_dequant_q2k")
     return out
+
+
+class ExpertCache:
+    """moe_cache_*: the routed experts of `host_layer` (tiled slabs in pinned
+    host tensors) served from a pool of `slots` HBM slots.
+
+    host: (gate, up, down) uint8 tensors in pinned host memory, the tiled
+    slabs of all E experts; dev_layer: a Layer whose router, grid and shared
+    expert are on the device (its routed tensors are not used)."""
+
+    def __init__(self, dev_layer: "Layer", host, slots: int):
+        torch = _torch()
+        self.host = host
+        gate, up, down = host
+        for t in host:
+            if t.is_cuda or not t.is_pinned():
+                raise ValueError("host slabs must be pinned host tensors")
+        L = lib()
+        nbytes = int(L.moe_cache_pool_bytes(dev_layer.ref, slots))
+        if nbytes == 0:
+            raise BitMoEError(EINVAL, "moe_cache_pool_bytes")
+        self.pool = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.dev_layer = dev_layer
+        h = C.c_void_p()
+        _check(L.moe_cache_create(dev_layer.ref, _ptr(gate), _ptr(up), _ptr(down), slots, _ptr(self.pool), nbytes,
+                                  C.byref(h)), "moe_cache_create")
+        self.h = h
+        self.slots = slots
+        s = LayerStruct()
+        _check(L.moe_cache_layer(self.h, C.byref(s)), "moe_cache_layer")
+        self.layer = Layer.__new__(Layer)
+        self.layer.H, self.layer.I, self.layer.E, self.layer.k = s.H, s.I, s.E, s.k
+        self.layer.tensors = [self.pool] + list(dev_layer.tensors)
+        self.layer.has_shared = dev_layer.has_shared
+        self.layer.s = s
+
+    def map(self, ids_host, stream=None):
+        """ids_host: int32 host tensor [T, k] -> (slot ids int32 host tensor,
+        experts copied)."""
+        torch = _torch()
+        ids = ids_host.contiguous()
+        slot_ids = torch.empty_like(ids)
+        loaded = C.c_int(0)
+        _check(lib().moe_cache_map(self.h, _ptr(ids), ids.numel(), _ptr(slot_ids), C.byref(loaded),
+                                   _stream(stream)), "moe_cache_map")
+        return slot_ids, loaded.value
+
+    def stats(self):
+        import numpy as np
+        hits, misses = C.c_int64(0), C.c_int64(0)
+        slots = np.empty(self.slots, dtype=np.int32)
+        _check(lib().moe_cache_stats(self.h, C.byref(hits), C.byref(misses), slots.ctypes.data_as(C.c_void_p)),
+               "moe_cache_stats")
+        return hits.value, misses.value, slots
+
+    def close(self):
+        if self.h:
+            lib().moe_cache_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def quantize_iq2x(w, grid, out=None, stream=None):

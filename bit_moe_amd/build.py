@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libbitmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.cpp", "plan.cpp", "dequant.hip", "route.hip", "bucket.hip", "decode.hip", "prefill.hip", "noalloc.hip", "quant.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "cache.cpp", "dequant.hip", "route.hip", "bucket.hip", "decode.hip", "prefill.hip", "noalloc.hip", "quant.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -181,8 +181,8 @@ const char *moe_strerror(int code) {
         case BITMOE_OK: return "ok";
         case BITMOE_EINVAL: return "invalid argument (null pointer, bad dtype or mode, bad size or alignment)";
         case BITMOE_EUNSUPPORTED:
-            return "unsupported shape or layout (H and I must be multiples of 256, 1<=k<=16, k<=E<=1024; "
-                   "the FFN calls read TILED blocks)";
+            return "unsupported shape, layout or size (H and I must be multiples of 256, 1<=k<=16, k<=E<=1024; "
+                   "the FFN calls read TILED blocks; a cache map needs no more distinct experts than slots)";
         case BITMOE_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
         case BITMOE_EHIP: return "a HIP kernel launch failed";
         case BITMOE_ESCRATCH:

@@ -289,6 +289,49 @@ int moe_dequant_q2k(const void *blocks, int64_t nblocks, void *out,
                     int out_dtype, void *stream);
 
 /*
+ * Routed-expert residency cache, for layers whose routed experts do not all
+ * fit in HBM: the experts' TILED slabs stay in host memory (pinned, for
+ * asynchronous copies) and a pool of `slots` HBM slots holds the ones in
+ * use.  This is the pages' streaming of routed experts from SSD through an
+ * in-memory expert cache, non-routed weights staying resident ("Faire tenir
+ * un MoE de 284B dans un portable de 128 Go", section "Streaming depuis le
+ * SSD quand la memoire fait defaut"), with host memory in the SSD's place.
+ *  moe_cache_pool_bytes: device bytes of the pool for `slots` slots
+ *   (k <= slots <= E; 0 if invalid).
+ *  moe_cache_create: L gives H, I, E, k and the DEVICE router, grid and
+ *   shared expert (its gate_q/up_q/down_q are ignored); host_gate, host_up,
+ *   host_down are the E experts' TILED slabs in host memory (owned by the
+ *   caller, valid until destroy); pool is caller-owned device memory of at
+ *   least moe_cache_pool_bytes(L, slots).  *cache receives a handle owned by
+ *   the caller (moe_cache_destroy frees it); the library keeps no other
+ *   state.
+ *  moe_cache_layer: a descriptor over the pool (E = slots, routed slabs in
+ *   the pool, the rest as given) for moe_ffn_decode / moe_ffn_prefill.
+ *  moe_cache_map: routing ids (HOST int32 [n], values in [0, E)) -> slot ids
+ *   (HOST int32 [n]) for the pool descriptor; experts not resident are copied
+ *   into slots with hipMemcpyAsync on `stream` (so FFN calls queued after it
+ *   on that stream see them, and earlier calls on it finish reading a slot
+ *   before it is overwritten).  Policy: the call's distinct experts, in
+ *   order of first appearance, keep their slots; a missing one takes the
+ *   lowest-numbered empty slot, else the least recently used slot not used
+ *   by this call (ties to the lower slot).  *loaded (may be NULL) receives
+ *   the number of experts copied.  Errors: EINVAL (null pointer, an id out
+ *   of range), EUNSUPPORTED (more distinct experts than slots), EHIP.
+ *  moe_cache_stats: cumulative hits and misses (experts), and the expert
+ *   in each slot (-1: empty) into expert_in_slot [slots] (any may be NULL).
+ * A handle is not thread-safe: calls on one handle must be serialised.
+ */
+size_t moe_cache_pool_bytes(const bitmoe_layer *L, int slots);
+int moe_cache_create(const bitmoe_layer *L, const void *host_gate, const void *host_up,
+                     const void *host_down, int slots, void *pool, size_t pool_bytes,
+                     void **cache);
+int moe_cache_layer(const void *cache, bitmoe_layer *out);
+int moe_cache_map(void *cache, const int32_t *ids, int n, int32_t *slot_ids, int *loaded,
+                  void *stream);
+int moe_cache_stats(const void *cache, int64_t *hits, int64_t *misses, int32_t *expert_in_slot);
+int moe_cache_destroy(void *cache);
+
+/*
  * Quantizer (the step before the layer): fp32 weights -> CANONICAL blocks,
  * nblocks superblocks of 256 consecutive weights of one row each.  The
  * routed experts are quantised asymmetrically to 2 bits, up/gate in IQ2_XXS
