@@ -41,6 +41,9 @@ def lib():
         L.oracle_bucket.argtypes = [P, I32, I32, I32, P, P, P]
         L.oracle_moe_ffn.argtypes = [I32, I32, I32, I32, P, P, P, P, P, P, P,
                                      P, I32, I32, P, P, P]
+        L.oracle_moe_ffn_mxfp4.argtypes = [I32, I32, I32, I32, P, P, P, P, P, P,
+                                           P, I32, I32, P, P, P]
+        L.oracle_dequant_mxfp4.argtypes = [P, I64, P]
         L.oracle_quantize_iq2x.argtypes = [P, P, I64, P]
         L.oracle_quantize_q2k.argtypes = [P, I64, P]
         L.oracle_max_threads.restype = I32
@@ -102,6 +105,14 @@ def quantize_q2k(w: np.ndarray) -> np.ndarray:
     return out
 
 
+def dequant_mxfp4(blocks: np.ndarray) -> np.ndarray:
+    """Canonical MXFP4 blocks uint8 [n, 17] -> float64 [n * 32] (exact)."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1, 17)
+    out = np.empty(b.shape[0] * 32, dtype=np.float64)
+    lib().oracle_dequant_mxfp4(_p(b), b.shape[0], _p(out))
+    return out
+
+
 def _x_args(x: np.ndarray):
     if x.dtype == np.float32:
         return np.ascontiguousarray(x), 0
@@ -146,8 +157,11 @@ def bucket(ids: np.ndarray, E: int):
     return counts, offsets, perm
 
 
-def moe_ffn(H, I, E, k, grid, gate, up, down, shared, x, ids, w) -> np.ndarray:
+def moe_ffn(H, I, E, k, grid, gate, up, down, shared, x, ids, w, fmt: str = "2bit") -> np.ndarray:
     """Routed (+ shared) SwiGLU FFN in float64.
+
+    fmt "2bit": gate/up IQ2X, down Q2K (grid: the codebook); "mxfp4": all
+    three MXFP4 (grid unused).
 
     gate/up/down: mappings expert -> canonical block array of that expert
     (any expert referenced by ``ids`` must be present).  shared: None or
@@ -178,9 +192,14 @@ def moe_ffn(H, I, E, k, grid, gate, up, down, shared, x, ids, w) -> np.ndarray:
             has = (e in src) if isinstance(src, dict) else (e < len(src))
             if not has:
                 raise KeyError(f"expert {e} missing")
-    g_p = ptrs(gate, I * (H // 256) * 66)
-    u_p = ptrs(up, I * (H // 256) * 66)
-    d_p = ptrs(down, H * (I // 256) * 84)
+    if fmt == "mxfp4":
+        g_p = ptrs(gate, I * (H // 32) * 17)
+        u_p = ptrs(up, I * (H // 32) * 17)
+        d_p = ptrs(down, H * (I // 32) * 17)
+    else:
+        g_p = ptrs(gate, I * (H // 256) * 66)
+        u_p = ptrs(up, I * (H // 256) * 66)
+        d_p = ptrs(down, H * (I // 256) * 84)
     if shared is not None:
         sg, su, sd = (np.ascontiguousarray(a, dtype=np.uint16) for a in shared)
         assert sg.shape == (I, H) and su.shape == (I, H) and sd.shape == (H, I)
@@ -188,8 +207,12 @@ def moe_ffn(H, I, E, k, grid, gate, up, down, shared, x, ids, w) -> np.ndarray:
         sgp, sup, sdp = _p(sg), _p(su), _p(sd)
     else:
         sgp = sup = sdp = None
-    gr = np.ascontiguousarray(grid, dtype=np.uint8).reshape(256, 8)
     y = np.empty((T, H), dtype=np.float64)
+    if fmt == "mxfp4":
+        lib().oracle_moe_ffn_mxfp4(H, I, E, k, g_p, u_p, d_p, sgp, sup, sdp,
+                                   _p(xc), dt, T, _p(ids_c), _p(w_c), _p(y))
+        return y
+    gr = np.ascontiguousarray(grid, dtype=np.uint8).reshape(256, 8)
     lib().oracle_moe_ffn(H, I, E, k, _p(gr), g_p, u_p, d_p, sgp, sup, sdp,
                          _p(xc), dt, T, _p(ids_c), _p(w_c), _p(y))
     return y
@@ -203,7 +226,7 @@ def layer_ffn(layer, x, ids, w, experts=None) -> np.ndarray:
     up = {e: layer.up(e) for e in used}
     down = {e: layer.down(e) for e in used}
     return moe_ffn(wl.H, wl.I, wl.E, wl.k, layer.grid(), gate, up, down,
-                   layer.shared(), x, ids, w)
+                   layer.shared(), x, ids, w, fmt=getattr(wl, "fmt", "2bit"))
 
 
 def margin_ok(x_row: np.ndarray, wr_bits: np.ndarray, k: int, margin: float) -> bool:

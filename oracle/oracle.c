@@ -113,6 +113,40 @@ static void q2k_block(const uint8_t *blk, double *out)
     }
 }
 
+/*
+ * MXFP4 (OCP Microscaling format, FP4 E2M1 elements with one E8M0 scale per
+ * 32): the format of the pages' MXFP4 variant, which keeps DeepSeek's
+ * released FP4 expert weights ("ds4 : analyse pratique pour un usage
+ * documente", section "Support de modeles et choix de quantification").
+ * Block of 17 bytes per 32 consecutive weights of one row, GGML's order:
+ * byte 0 the scale X (value 2^(X-127); X = 255 is NaN), bytes 1-16 qs:
+ * weight j (0..15) in the low nibble of qs[j], weight j+16 in its high
+ * nibble.  Element code c: sign c >> 3, exponent field (c >> 1) & 3,
+ * mantissa bit c & 1; exponent field 0 gives m * 0.5, otherwise
+ * 2^(e-1) * (1 + m/2): 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ */
+static double e2m1(unsigned c)
+{
+    unsigned e = (c >> 1) & 3, m = c & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, (int)e - 1);
+    return (c >> 3) ? -v : v;
+}
+
+static void mxfp4_block(const uint8_t *blk, double *out)
+{
+    double scale = blk[0] == 255 ? NAN : ldexp(1.0, (int)blk[0] - 127);
+    for (int j = 0; j < 16; j++) {
+        out[j] = e2m1(blk[1 + j] & 0xF) * scale;
+        out[j + 16] = e2m1(blk[1 + j] >> 4) * scale;
+    }
+}
+
+void oracle_dequant_mxfp4(const uint8_t *blocks, int64_t nblocks, double *out)
+{
+    for (int64_t b = 0; b < nblocks; b++)
+        mxfp4_block(blocks + 17 * b, out + 32 * b);
+}
+
 void oracle_dequant_iq2x(const uint8_t *blocks, const uint8_t *grid,
                          int64_t nblocks, double *out)
 {
@@ -230,6 +264,22 @@ static void matvec_q2k(const uint8_t *m, int N, int K, const double *v,
     }
 }
 
+static void matvec_mxfp4(const uint8_t *m, int N, int K, const double *v,
+                         double *out)
+{
+    int nb = K / 32;
+    #pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; n++) {
+        double row[32], acc = 0.0;
+        for (int kb = 0; kb < nb; kb++) {
+            mxfp4_block(m + 17 * ((int64_t)n * nb + kb), row);
+            for (int i = 0; i < 32; i++)
+                acc += row[i] * v[32 * kb + i];
+        }
+        out[n] = acc;
+    }
+}
+
 static void matvec_bf16(const uint16_t *m, int N, int K, const double *v,
                         double *out)
 {
@@ -250,7 +300,7 @@ static void matvec_bf16(const uint16_t *m, int N, int K, const double *v,
  * an expert no token uses may be NULL.  shared_*: bf16 bits [I][H], [I][H],
  * [H][I], or NULL for none.  y: double [T][H], overwritten.
  */
-void oracle_moe_ffn(int H, int I, int E, int k, const uint8_t *grid,
+static void moe_ffn(int mx, int H, int I, int E, int k, const uint8_t *grid,
                     const uint8_t *const *gate, const uint8_t *const *up,
                     const uint8_t *const *down,
                     const uint16_t *shared_gate, const uint16_t *shared_up,
@@ -271,11 +321,19 @@ void oracle_moe_ffn(int H, int I, int E, int k, const uint8_t *grid,
         }
         for (int j = 0; j < k; j++) {
             int e = ids[t * k + j];
-            matvec_iq2x(gate[e], grid, I, H, xv, g);
-            matvec_iq2x(up[e], grid, I, H, xv, u);
+            if (mx) {
+                matvec_mxfp4(gate[e], I, H, xv, g);
+                matvec_mxfp4(up[e], I, H, xv, u);
+            } else {
+                matvec_iq2x(gate[e], grid, I, H, xv, g);
+                matvec_iq2x(up[e], grid, I, H, xv, u);
+            }
             for (int n = 0; n < I; n++)
                 g[n] = silu(g[n]) * u[n];
-            matvec_q2k(down[e], H, I, g, o);
+            if (mx)
+                matvec_mxfp4(down[e], H, I, g, o);
+            else
+                matvec_q2k(down[e], H, I, g, o);
             for (int n = 0; n < H; n++)
                 yt[n] += w[t * k + j] * o[n];
         }
@@ -290,6 +348,32 @@ void oracle_moe_ffn(int H, int I, int E, int k, const uint8_t *grid,
         }
     }
     free(xv); free(g); free(u); free(o);
+}
+
+/* Routed experts in IQ2X (gate, up) and Q2K (down). */
+void oracle_moe_ffn(int H, int I, int E, int k, const uint8_t *grid,
+                    const uint8_t *const *gate, const uint8_t *const *up,
+                    const uint8_t *const *down,
+                    const uint16_t *shared_gate, const uint16_t *shared_up,
+                    const uint16_t *shared_down,
+                    const void *x, int x_dtype, int T,
+                    const int32_t *ids, const double *w, double *y)
+{
+    moe_ffn(0, H, I, E, k, grid, gate, up, down, shared_gate, shared_up,
+            shared_down, x, x_dtype, T, ids, w, y);
+}
+
+/* Routed experts in MXFP4 (gate, up and down; grid unused). */
+void oracle_moe_ffn_mxfp4(int H, int I, int E, int k,
+                          const uint8_t *const *gate, const uint8_t *const *up,
+                          const uint8_t *const *down,
+                          const uint16_t *shared_gate, const uint16_t *shared_up,
+                          const uint16_t *shared_down,
+                          const void *x, int x_dtype, int T,
+                          const int32_t *ids, const double *w, double *y)
+{
+    moe_ffn(1, H, I, E, k, NULL, gate, up, down, shared_gate, shared_up,
+            shared_down, x, x_dtype, T, ids, w, y);
 }
 
 #ifdef _OPENMP

@@ -39,6 +39,7 @@ import numpy as np
 QK = 256                 # weights per superblock
 IQ2X_BLOCK_BYTES = 66    # fp16 d + 8 groups x (4 index bytes + u32 signs/scale)
 Q2K_BLOCK_BYTES = 84     # 16 scale/min bytes + 64 quant bytes + fp16 d + fp16 dmin
+MXFP4_BLOCK_BYTES = 17   # E8M0 scale byte + 16 bytes of 32 E2M1 codes (32 weights)
 
 # stream identifiers (second element of every SeedSequence entropy list)
 _GRID, _ROUTER, _GATE, _UP, _DOWN, _SGATE, _SUP, _SDOWN, _X, _ZIPF = range(10)
@@ -64,6 +65,7 @@ class Workload:
     shared: bool          # a bf16 shared expert is present
     seed: int
     mode: str             # "decode" or "prefill": the entry point it exercises
+    fmt: str = "2bit"     # routed experts: "2bit" (IQ2X gate/up, Q2K down) or "mxfp4"
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -127,6 +129,20 @@ def iq2x_slab(seed: int, tensor: int, e: int, N: int, K: int) -> np.ndarray:
     return raw
 
 
+def mxfp4_slab(seed: int, tensor: int, e: int, N: int, K: int) -> np.ndarray:
+    """Canonical MXFP4 blocks of one expert's [N, K] projection: uint8
+    [N * K/32, 17], block (n, kb) at row n*(K/32)+kb.  The 16 element bytes
+    are uniform random; the E8M0 scale byte X is drawn around
+    127 + log2(1 / (2.93 sqrt(K))), +-1 (the rms of a uniform random E2M1
+    code is 2.93), so that one output row has rms close to rms(x)."""
+    nb = N * (K // 32)
+    rng = _rng(seed, tensor, e)
+    raw = _random_bytes(rng, nb * MXFP4_BLOCK_BYTES).reshape(nb, MXFP4_BLOCK_BYTES)
+    centre = 127 + int(round(math.log2(1.0 / (2.93 * math.sqrt(K)))))
+    raw[:, 0] = centre + rng.integers(-1, 2, nb)
+    return raw
+
+
 def q2k_slab(seed: int, tensor: int, e: int, N: int, K: int) -> np.ndarray:
     """Canonical Q2K blocks of one expert's [N, K] projection:
     uint8 [N * K/256, 84]."""
@@ -173,12 +189,18 @@ class Layer:
             self.w.seed, _ROUTER, (self.w.E, self.w.H), 0.02))
 
     def gate(self, e: int) -> np.ndarray:
+        if self.w.fmt == "mxfp4":
+            return mxfp4_slab(self.w.seed, _GATE, e, self.w.I, self.w.H)
         return iq2x_slab(self.w.seed, _GATE, e, self.w.I, self.w.H)
 
     def up(self, e: int) -> np.ndarray:
+        if self.w.fmt == "mxfp4":
+            return mxfp4_slab(self.w.seed, _UP, e, self.w.I, self.w.H)
         return iq2x_slab(self.w.seed, _UP, e, self.w.I, self.w.H)
 
     def down(self, e: int) -> np.ndarray:
+        if self.w.fmt == "mxfp4":
+            return mxfp4_slab(self.w.seed, _DOWN, e, self.w.H, self.w.I)
         return q2k_slab(self.w.seed, _DOWN, e, self.w.H, self.w.I)
 
     def _all(self, fn) -> np.ndarray:
