@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libbitmoe.so")
 F32, BF16 = 0, 1
 DECODE, PREFILL = 0, 1
 LAYOUT_CANONICAL, LAYOUT_TILED = 0, 1
+FORMAT_2BIT, FORMAT_MXFP4 = 0, 1
 TIME_GATEUP, TIME_DOWN = 0, 1
 EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, ESCRATCH = -1, -2, -3, -4, -5
 STATIC_SCRATCH_BYTES = 16 << 20
@@ -26,7 +27,8 @@ SYMBOLS = [
     "moe_route_workspace_bytes", "moe_route", "moe_topk", "moe_bucket_workspace_bytes",
     "moe_bucket", "moe_workspace_bytes", "moe_ffn_decode", "moe_forward_decode", "moe_forward_decode_noalloc",
     "moe_ffn_prefill",
-    "moe_dequant_iq2x", "moe_dequant_q2k", "moe_quantize_iq2x", "moe_quantize_q2k", "moe_pack_iq2x", "moe_pack_q2k", "moe_pack_bf16",
+    "moe_dequant_iq2x", "moe_dequant_q2k", "moe_dequant_mxfp4", "moe_quantize_iq2x", "moe_quantize_q2k",
+    "moe_pack_iq2x", "moe_pack_q2k", "moe_pack_bf16", "moe_pack_mxfp4",
     "moe_set_timing_events", "moe_strerror", "moe_version",
     "moe_cache_pool_bytes", "moe_cache_create", "moe_cache_layer", "moe_cache_map", "moe_cache_stats",
     "moe_cache_destroy",
@@ -37,7 +39,8 @@ class LayerStruct(C.Structure):
     _fields_ = [("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
                 ("router_w", C.c_void_p), ("gate_q", C.c_void_p), ("up_q", C.c_void_p),
                 ("down_q", C.c_void_p), ("grid", C.c_void_p), ("shared_gate", C.c_void_p),
-                ("shared_up", C.c_void_p), ("shared_down", C.c_void_p), ("layout", C.c_int32)]
+                ("shared_up", C.c_void_p), ("shared_down", C.c_void_p), ("layout", C.c_int32),
+                ("format", C.c_int32)]
 
 
 _lib = None
@@ -72,11 +75,13 @@ def lib() -> C.CDLL:
         "moe_forward_decode_noalloc": ([LP, P, I, I, P, P, P, P], I),
         "moe_dequant_iq2x": ([P, P, I64, P, I, P], I),
         "moe_dequant_q2k": ([P, I64, P, I, P], I),
+        "moe_dequant_mxfp4": ([P, I64, P, I, P], I),
         "moe_quantize_iq2x": ([P, P, I64, P, P], I),
         "moe_quantize_q2k": ([P, I64, P, P], I),
         "moe_pack_iq2x": ([P, P, I, I, I, P], I),
         "moe_pack_q2k": ([P, P, I, I, I, P], I),
         "moe_pack_bf16": ([P, P, I, I, P], I),
+        "moe_pack_mxfp4": ([P, P, I, I, I, P], I),
         "moe_set_timing_events": ([P, P, I], I),
         "moe_strerror": ([I], C.c_char_p),
         "moe_cache_pool_bytes": ([LP, I], SZ),
@@ -157,12 +162,14 @@ def _workspace(nbytes: int, device):
 
 class Layer:
     """A routed-MoE layer whose weights live in torch device tensors, in the
-    tiled layout (moe_pack_* output)."""
+    tiled layout (moe_pack_* output).  fmt: FORMAT_2BIT (IQ2X gate/up, Q2K
+    down, grid required) or FORMAT_MXFP4 (grid may be None)."""
 
-    def __init__(self, H, I, E, k, router_w, gate_q, up_q, down_q, grid, shared=None):
+    def __init__(self, H, I, E, k, router_w, gate_q, up_q, down_q, grid, shared=None, fmt=FORMAT_2BIT):
         _dev_check(router_w, gate_q, up_q, down_q, grid)
         self.H, self.I, self.E, self.k = H, I, E, k
-        self.tensors = [router_w, gate_q, up_q, down_q, grid]
+        self.fmt = fmt
+        self.tensors = [t for t in (router_w, gate_q, up_q, down_q, grid) if t is not None]
         sg = su = sd = None
         if shared is not None:
             sg, su, sd = shared
@@ -170,7 +177,7 @@ class Layer:
             self.tensors += [sg, su, sd]
         self.has_shared = shared is not None
         self.s = LayerStruct(H, I, E, k, _ptr(router_w), _ptr(gate_q), _ptr(up_q), _ptr(down_q),
-                             _ptr(grid), _ptr(sg), _ptr(su), _ptr(sd), LAYOUT_TILED)
+                             _ptr(grid), _ptr(sg), _ptr(su), _ptr(sd), LAYOUT_TILED, fmt)
 
     @property
     def ref(self):
@@ -314,6 +321,17 @@ def dequant_q2k(blocks, out_dtype=F32, stream=None):
     return out
 
 
+def dequant_mxfp4(blocks, out_dtype=F32, stream=None):
+    """Canonical MXFP4 blocks (uint8, 17 bytes each) -> values [n*32]."""
+    torch = _torch()
+    nb = blocks.numel() // 17
+    dt = torch.float32 if out_dtype == F32 else torch.bfloat16
+    out = torch.empty(nb * 32, dtype=dt, device=blocks.device)
+    _dev_check(blocks)
+    _check(lib().moe_dequant_mxfp4(_ptr(blocks), nb, _ptr(out), out_dtype, _stream(stream)), "moe_dequant_mxfp4")
+    return out
+
+
 class ExpertCache:
     """moe_cache_*: the routed experts of `host_layer` (tiled slabs in pinned
     host tensors) served from a pool of `slots` HBM slots.
@@ -344,6 +362,7 @@ class ExpertCache:
         _check(L.moe_cache_layer(self.h, C.byref(s)), "moe_cache_layer")
         self.layer = Layer.__new__(Layer)
         self.layer.H, self.layer.I, self.layer.E, self.layer.k = s.H, s.I, s.E, s.k
+        self.layer.fmt = s.format
         self.layer.tensors = [self.pool] + list(dev_layer.tensors)
         self.layer.has_shared = dev_layer.has_shared
         self.layer.s = s
@@ -416,6 +435,14 @@ def pack_q2k(src, E, N, K, stream=None):
     dst = torch.empty_like(src)
     _dev_check(src)
     _check(lib().moe_pack_q2k(_ptr(src), _ptr(dst), E, N, K, _stream(stream)), "moe_pack_q2k")
+    return dst
+
+
+def pack_mxfp4(src, E, N, K, stream=None):
+    torch = _torch()
+    dst = torch.empty_like(src)
+    _dev_check(src)
+    _check(lib().moe_pack_mxfp4(_ptr(src), _ptr(dst), E, N, K, _stream(stream)), "moe_pack_mxfp4")
     return dst
 
 

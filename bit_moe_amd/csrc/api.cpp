@@ -32,7 +32,9 @@ int check_ffn_layer(const bitmoe_layer *L) {
     // the FFN kernels read the tiled layout only
     if (L->layout == BITMOE_LAYOUT_CANONICAL) return BITMOE_EUNSUPPORTED;
     if (L->layout != BITMOE_LAYOUT_TILED) return BITMOE_EINVAL;
-    if (!L->gate_q || !L->up_q || !L->down_q || !L->grid) return BITMOE_EINVAL;
+    if (L->format != BITMOE_FORMAT_2BIT && L->format != BITMOE_FORMAT_MXFP4) return BITMOE_EINVAL;
+    if (!L->gate_q || !L->up_q || !L->down_q) return BITMOE_EINVAL;
+    if (L->format == BITMOE_FORMAT_2BIT && !L->grid) return BITMOE_EINVAL;
     const bool a = L->shared_gate, b = L->shared_up, c = L->shared_down;
     if (a != b || b != c) return BITMOE_EINVAL;
     return BITMOE_OK;
@@ -312,6 +314,14 @@ int moe_dequant_q2k(const void *blocks, int64_t nblocks, void *out, int out_dtyp
     return bm_host::launch_dequant_q2k(blocks, nblocks, out, out_dtype, as_stream(stream));
 }
 
+int moe_dequant_mxfp4(const void *blocks, int64_t nblocks, void *out, int out_dtype, void *stream) {
+    if (nblocks < 0) return BITMOE_EINVAL;
+    if (out_dtype != BITMOE_F32 && out_dtype != BITMOE_BF16) return BITMOE_EINVAL;
+    if (nblocks == 0) return BITMOE_OK;
+    if (!blocks || !out || !aligned(out, 16)) return BITMOE_EINVAL;
+    return bm_host::launch_dequant_mxfp4(blocks, nblocks, out, out_dtype, as_stream(stream));
+}
+
 int moe_quantize_iq2x(const float *w, const void *grid, int64_t nblocks, void *blocks, void *stream) {
     if (nblocks < 0) return BITMOE_EINVAL;
     if (nblocks == 0) return BITMOE_OK;
@@ -340,6 +350,14 @@ int moe_pack_q2k(const void *src, void *dst, int E, int N, int K, void *stream) 
     if ((int64_t)E * N * K == 0) return BITMOE_OK;
     if (!src || !dst || !aligned(src, 4) || !aligned(dst, 16)) return BITMOE_EINVAL;
     return bm_host::launch_pack_q2k(src, dst, E, N, K, as_stream(stream));
+}
+
+int moe_pack_mxfp4(const void *src, void *dst, int E, int N, int K, void *stream) {
+    if (E < 0 || N < 0 || K < 0) return BITMOE_EINVAL;
+    if (N % 64 || K % 256) return BITMOE_EUNSUPPORTED;
+    if ((int64_t)E * N * K == 0) return BITMOE_OK;
+    if (!src || !dst || !aligned(dst, 16)) return BITMOE_EINVAL;
+    return bm_host::launch_pack_mxfp4(src, dst, E, N, K, as_stream(stream));
 }
 
 int moe_pack_bf16(const void *src, void *dst, int N, int K, void *stream) {

@@ -37,6 +37,11 @@ struct Cache {
 };
 
 void slabs(const bitmoe_layer *L, size_t (&s)[3]) {
+    if (L->format == BITMOE_FORMAT_MXFP4) {
+        s[0] = s[1] = (size_t)L->I * (L->H / 32) * 17;
+        s[2] = (size_t)L->H * (L->I / 32) * 17;
+        return;
+    }
     s[0] = s[1] = (size_t)L->I * (L->H / 256) * 66;
     s[2] = (size_t)L->H * (L->I / 256) * 84;
 }
@@ -44,6 +49,7 @@ void slabs(const bitmoe_layer *L, size_t (&s)[3]) {
 int check_cache_layer(const bitmoe_layer *L) {
     if (!L) return BITMOE_EINVAL;
     if (L->H <= 0 || L->I <= 0 || L->E <= 0 || L->k <= 0) return BITMOE_EINVAL;
+    if (L->format != BITMOE_FORMAT_2BIT && L->format != BITMOE_FORMAT_MXFP4) return BITMOE_EINVAL;
     if (L->H % 256 || L->I % 256 || L->k > 16 || L->k > L->E || L->E > 1024) return BITMOE_EUNSUPPORTED;
     return BITMOE_OK;
 }
@@ -63,7 +69,8 @@ int moe_cache_create(const bitmoe_layer *L, const void *host_gate, const void *h
                      int slots, void *pool, size_t pool_bytes, void **cache) {
     int rc = check_cache_layer(L);
     if (rc) return rc;
-    if (!cache || !host_gate || !host_up || !host_down || !pool || !L->grid) return BITMOE_EINVAL;
+    if (!cache || !host_gate || !host_up || !host_down || !pool) return BITMOE_EINVAL;
+    if (L->format == BITMOE_FORMAT_2BIT && !L->grid) return BITMOE_EINVAL;
     if (slots < L->k || slots > L->E) return BITMOE_EINVAL;
     if ((L->shared_gate != nullptr) != (L->shared_up != nullptr) ||
         (L->shared_up != nullptr) != (L->shared_down != nullptr))

@@ -44,6 +44,38 @@ BM_DEV float dot2_f16(uint32_t a, uint32_t b, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
 }
 
+// ---- MXFP4 (OCP Microscaling: E2M1 elements, one E8M0 scale per 32) -----
+// v_cvt_scalef32_pk_{bf16,f16,f32}_fp4: byte SEL of w holds two E2M1
+// elements, the first in its low nibble; the result holds element * scale
+// for both, the first in the low half, rounded to nearest-even (exact in
+// fp32, and in bf16 / fp16 within range).  The instruction reads the scale
+// operand's exponent field as an E8M0 value, so the fp32 bit pattern X << 23
+// stands for 2^(X-127) for every X, 0 and 255 (NaN) included.
+BM_DEV float mx_cvt_scale(uint32_t X) { return __uint_as_float(X << 23); }
+template <int SEL>
+BM_DEV uint32_t fp4x2_bf16s(uint32_t w, float scale) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL));
+}
+template <int SEL>
+BM_DEV uint32_t fp4x2_f16s(uint32_t w, float scale) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, SEL));
+}
+template <int SEL>
+BM_DEV float2 fp4x2_f32s(uint32_t w, float scale) {
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
+    return make_float2(v[0], v[1]);
+}
+// the two elements themselves (scale 1)
+template <int SEL>
+BM_DEV uint32_t fp4x2_bf16(uint32_t w) { return fp4x2_bf16s<SEL>(w, 1.f); }
+template <int SEL>
+BM_DEV uint32_t fp4x2_f16(uint32_t w) { return fp4x2_f16s<SEL>(w, 1.f); }
+// The block scale 2^(X-127) as fp32: X << 23 for X = 1..254, the subnormal
+// 2^-127 for X = 0 and NaN for X = 255 (both take mantissa bit 22).
+BM_DEV float mx_scale(uint32_t X) {
+    return __uint_as_float((X << 23) | ((((X + 1u) & 0xFEu) == 0u) ? 0x400000u : 0u));
+}
+
 // ---- wave helpers -------------------------------------------------------
 
 BM_DEV int lane_id() { return __lane_id(); }

@@ -429,7 +429,7 @@ struct Tok {
 // t0 + t (wave t): h = silu(g) u as fp16 scaled by 2^-e so that the panel's
 // largest |h| lies in [2^14, 2^15) (no overflow, full fp16 precision; 2^e is
 // kept), with per-16-column sums for the down launch.
-template <int NT>
+template <int NT, int SUMS = 1>
 BM_DEV void gateup_epilogue(int I, const Tok &tk, int t0, int P, const float (&ag)[NT], const float (&au)[NT],
                             uint16_t *__restrict__ h, float2 *__restrict__ hsum2, float *__restrict__ hscale,
                             float *red) {
@@ -456,12 +456,14 @@ BM_DEV void gateup_epilogue(int I, const Tok &tk, int t0, int P, const float (&a
         const float inv = __uint_as_float((uint32_t)(127 - e) << 23), scl = __uint_as_float((uint32_t)(127 + e) << 23);
         const _Float16 hf = (_Float16)(hv * inv);
         h[row * I + n] = __builtin_bit_cast(uint16_t, hf);
-        // per 16 columns: sum of h and sum of B_p h, B_p the bias of the
-        // pair that column n % 16 falls in
-        const float v = (float)hf;
-        const int pp = (n & 15) >> 1;
-        const float hs = row16_sum(v), hb = row16_sum(q2k_pair_bias(pp) * v);
-        if ((lane & 15) == 15) hsum2[row * (I / 16) + (n >> 4)] = make_float2(hs, hb);
+        if (SUMS) {
+            // per 16 columns: sum of h and sum of B_p h, B_p the bias of the
+            // pair that column n % 16 falls in (the Q2K down's terms)
+            const float v = (float)hf;
+            const int pp = (n & 15) >> 1;
+            const float hs = row16_sum(v), hb = row16_sum(q2k_pair_bias(pp) * v);
+            if ((lane & 15) == 15) hsum2[row * (I / 16) + (n >> 4)] = make_float2(hs, hb);
+        }
         if (lane == 0) hscale[row * (I / 64) + P] = scl;
     }
     __syncthreads();
@@ -608,6 +610,183 @@ BM_DEV void routed_gateup_1(int H, int I, int k, const Tok &tk, int P, const uin
     gateup_epilogue<1>(I, tk, 0, P, ag, au, h, hsum2, hscale, red);
 }
 
+// ---- MXFP4 routed experts ---------------------------------------------------
+// A piece is one 32-weight block of a row (16 bytes, byte i holding weights
+// 2i and 2i+1) with its scale byte X.  The hardware conversion turns each
+// byte into two exact bf16 (gate/up: dotted with the bf16 activations) or
+// fp16 (down: dotted with the fp16 h) values; the block's fp32 sum is then
+// multiplied by 2^(X-127).  Piece pc of row P*64 + r (pc = 8 kb + c) sits at
+// ((P nb 8 + pc) 64 + r) * 16, its scale at N K/2 + (P nb 64 + (pc >> 3) 64
+// + r) 8 + (pc & 7), nb = K/256.
+template <int XBF16, int NT>
+BM_DEV void mx_piece(uint4 q, float scale, const XGroup<XBF16, NT> &xg, const void *x, const int (&tok)[NT],
+                     int H, int pc, float (&acc)[NT]) {
+    float part[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) part[t] = 0.f;
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const uint32_t W = qw[r];
+        const uint2 lo = make_uint2(fp4x2_bf16<0>(W), fp4x2_bf16<1>(W));
+        const uint2 hi = make_uint2(fp4x2_bf16<2>(W), fp4x2_bf16<3>(W));
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            if (XBF16) {
+                const uint4 xv = xg.v[t][r];
+                part[t] = dot2_bf16(lo.x, xv.x, part[t]);
+                part[t] = dot2_bf16(lo.y, xv.y, part[t]);
+                part[t] = dot2_bf16(hi.x, xv.z, part[t]);
+                part[t] = dot2_bf16(hi.y, xv.w, part[t]);
+            } else {
+                part[t] = dot8<0>(lo, hi, xrow<0>(x, tok[t], H, 32 * pc + 8 * r), part[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = fmaf(scale, part[t], acc[t]);
+}
+
+struct MxRows {
+    const uint4 *q;          // piece 0 of this lane's row
+    const uint8_t *sc;       // scale byte of piece 0
+    BM_DEV uint4 piece(int pc) const { return q[(int64_t)pc * 64]; }
+    BM_DEV uint32_t scale(int pc) const { return sc[(int64_t)(pc >> 3) * 512 + (pc & 7)]; }
+};
+// rows of 64-row panel P of an expert's [N][K] slab at `slab`, this lane's row
+BM_DEV MxRows mx_rows(const uint8_t *slab, int N, int K, int P) {
+    const int nb = K / kQK, lane = lane_id();
+    MxRows m;
+    m.q = reinterpret_cast<const uint4 *>(slab) + (int64_t)P * nb * 8 * 64 + lane;
+    m.sc = slab + (int64_t)N * K / 2 + ((int64_t)P * nb * 64 + lane) * 8;
+    return m;
+}
+
+// Gate/up of panel P for tokens t0..t0+NT-1 of expert tk (MXFP4); the
+// wave's pieces in batches of two, the next batch in flight.
+template <int XBF16, int NT>
+BM_DEV void mx_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P, const uint8_t *__restrict__ gate,
+                           const uint8_t *__restrict__ up, const void *__restrict__ x, const int32_t *perm,
+                           uint16_t *__restrict__ h, float *__restrict__ hscale, float *red) {
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int tok[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+        tok[t] = __builtin_amdgcn_readfirstlane(perm[tk.off + min(t0 + t, tk.cnt - 1)] / k);
+    float ag[NT], au[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) ag[t] = au[t] = 0.f;
+    const int64_t slab = (int64_t)I * H / 32 * 17;
+    const MxRows G = mx_rows(gate + tk.e * slab, I, H, P), U = mx_rows(up + tk.e * slab, I, H, P);
+    int p0, p1;
+    split_range(8 * (H / kQK), kWG, wv, p0, p1);
+    constexpr int kPB = 2;
+    struct Batch { uint4 g[kPB], u[kPB]; uint32_t sg[kPB], su[kPB]; };
+    auto load = [&](int pb, Batch &b) {
+#pragma unroll
+        for (int i = 0; i < kPB; i++) {
+            const int pc = min(pb + i, p1 - 1);      // a short last batch re-reads its last piece
+            b.g[i] = G.piece(pc);
+            b.u[i] = U.piece(pc);
+            b.sg[i] = G.scale(pc);
+            b.su[i] = U.scale(pc);
+        }
+    };
+    Batch cur{}, nxt{};
+    if (p0 < p1) load(p0, cur);
+    for (int pb = p0; pb < p1; pb += kPB) {
+        if (pb + kPB < p1) load(pb + kPB, nxt);
+#pragma unroll
+        for (int i = 0; i < kPB; i++) {
+            if (pb + i < p1) {
+                XGroup<XBF16, NT> xg;
+                load_xgroup<XBF16, NT>(xg, x, tok, H, pb + i);
+                mx_piece<XBF16, NT>(cur.g[i], mx_scale(cur.sg[i]), xg, x, tok, H, pb + i, ag);
+                mx_piece<XBF16, NT>(cur.u[i], mx_scale(cur.su[i]), xg, x, tok, H, pb + i, au);
+            }
+        }
+        cur = nxt;
+    }
+    gateup_epilogue<NT, 0>(I, tk, t0, P, ag, au, h, nullptr, hscale, red);
+}
+
+// The same for an expert chosen by one token: the pieces stream through a
+// ring of four register slots, each refilled as soon as it is decoded.
+template <int XBF16>
+BM_DEV void mx_gateup_1(int H, int I, int k, const Tok &tk, int P, const uint8_t *__restrict__ gate,
+                        const uint8_t *__restrict__ up, const void *__restrict__ x, const int32_t *perm,
+                        uint16_t *__restrict__ h, float *__restrict__ hscale, float *red, int tok0 = -1) {
+    constexpr int kRing = 4;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tok[1] = {__builtin_amdgcn_readfirstlane(tok0 >= 0 ? tok0 : perm ? perm[tk.off] / k : 0)};
+    const int64_t slab = (int64_t)I * H / 32 * 17;
+    const MxRows G = mx_rows(gate + tk.e * slab, I, H, P), U = mx_rows(up + tk.e * slab, I, H, P);
+    int p0, p1;
+    split_range(8 * (H / kQK), kWG, wv, p0, p1);
+    struct Piece { uint4 g, u; uint32_t sg, su; };
+    auto load = [&](int pc, Piece &q) {
+        pc = min(pc, p1 - 1);                          // past the wave's last: re-read, not decoded
+        q.g = G.piece(pc);
+        q.u = U.piece(pc);
+        q.sg = G.scale(pc);
+        q.su = U.scale(pc);
+    };
+    float ag[1] = {0.f}, au[1] = {0.f};
+    auto decode = [&](int pc, const Piece &q) {
+        XGroup<XBF16, 1> xg;
+        load_xgroup<XBF16, 1>(xg, x, tok, H, pc);
+        mx_piece<XBF16, 1>(q.g, mx_scale(q.sg), xg, x, tok, H, pc, ag);
+        mx_piece<XBF16, 1>(q.u, mx_scale(q.su), xg, x, tok, H, pc, au);
+    };
+    auto step = [&](int pc, Piece &q) {
+        decode(pc, q);
+        __builtin_amdgcn_sched_barrier(0);
+        load(pc + kRing, q);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    static_assert(kRing == 4, "four slots below");
+    if (p0 < p1) {
+        Piece q0, q1, q2, q3;
+        load(p0, q0);
+        load(p0 + 1, q1);
+        load(p0 + 2, q2);
+        load(p0 + 3, q3);
+        int pc = p0;
+        for (; pc + kRing <= p1; pc += kRing) {
+            step(pc, q0);
+            step(pc + 1, q1);
+            step(pc + 2, q2);
+            step(pc + 3, q3);
+        }
+        if (pc < p1) decode(pc, q0);
+        if (pc + 1 < p1) decode(pc + 1, q1);
+        if (pc + 2 < p1) decode(pc + 2, q2);
+    }
+    gateup_epilogue<1, 0>(I, tk, 0, P, ag, au, h, nullptr, hscale, red);
+}
+
+// Format dispatch of the routed gate/up passes.
+template <int FMT, int XBF16, int SGN>
+BM_DEV void gateup_1(int H, int I, int k, const Tok &tk, int P, const uint8_t *__restrict__ gate,
+                     const uint8_t *__restrict__ up, const void *__restrict__ x, const int32_t *perm,
+                     uint16_t *__restrict__ h, float2 *__restrict__ hsum2, float *__restrict__ hscale, float *red,
+                     int tok0 = -1) {
+    if constexpr (FMT == BITMOE_FORMAT_MXFP4)
+        mx_gateup_1<XBF16>(H, I, k, tk, P, gate, up, x, perm, h, hscale, red, tok0);
+    else
+        routed_gateup_1<XBF16, SGN>(H, I, k, tk, P, gate, up, x, perm, h, hsum2, hscale, red, tok0);
+}
+template <int FMT, int XBF16, int NT, int SGN>
+BM_DEV void gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P, const uint8_t *__restrict__ gate,
+                        const uint8_t *__restrict__ up, const void *__restrict__ x, const int32_t *perm,
+                        uint16_t *__restrict__ h, float2 *__restrict__ hsum2, float *__restrict__ hscale,
+                        float *red) {
+    if constexpr (FMT == BITMOE_FORMAT_MXFP4)
+        mx_gateup_pass<XBF16, NT>(H, I, k, tk, t0, P, gate, up, x, perm, h, hscale, red);
+    else
+        routed_gateup_pass<XBF16, NT, SGN>(H, I, k, tk, t0, P, gate, up, x, perm, h, hsum2, hscale, red);
+}
+
 // sum of 8 products of bf16 weight pairs with h given as bf16 hi + lo
 BM_DEV float dot8_hilo(uint4 wq, uint4 hh, uint4 hl, float acc) {
     acc = dot2_bf16(wq.x, hh.x, acc); acc = dot2_bf16(wq.x, hl.x, acc);
@@ -714,17 +893,19 @@ BM_DEV void shared_h_load(int64_t n, int kc_sg, const float *__restrict__ sgp, i
 // is routed.
 template <int MULTI>
 constexpr int dec_sgn_bytes() { return MULTI ? kLutSgnHalf : kLutSgnFull; }
-template <int MULTI>
-constexpr int dec_lut_bytes() { return kLutMagBytes + dec_sgn_bytes<MULTI>(); }
+template <int FMT, int MULTI>
+constexpr int dec_lut_bytes() { return FMT == BITMOE_FORMAT_MXFP4 ? 0 : kLutMagBytes + dec_sgn_bytes<MULTI>(); }
 // all LDS of a gate/up workgroup, dynamic so that the tables start at
 // address 0 (their lookup offsets are then the permutes' results as they
 // are): tables | cross-wave sums | routing
 template <int MULTI>
 constexpr int dec_red_floats() { return kWG * (MULTI ? kNT : 1) * 2 * 64; }
-template <int MULTI>
-constexpr int dec_gateup_lds() { return dec_lut_bytes<MULTI>() + dec_red_floats<MULTI>() * 4 + (int)sizeof(SmallRoute); }
+template <int FMT, int MULTI>
+constexpr int dec_gateup_lds() {
+    return dec_lut_bytes<FMT, MULTI>() + dec_red_floats<MULTI>() * 4 + (int)sizeof(SmallRoute);
+}
 
-template <int XBF16, int MULTI>
+template <int FMT, int XBF16, int MULTI>
 __global__ void __launch_bounds__(kWG * 64)
 k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const uint8_t *__restrict__ gate,
              const uint8_t *__restrict__ up, const uint8_t *__restrict__ grid,
@@ -733,7 +914,7 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
              float *__restrict__ hscale, int kc_sg, const float *__restrict__ sgp, uint16_t *__restrict__ hs,
              const int4 *__restrict__ single, const int32_t *__restrict__ n_single, int32_t *__restrict__ gctr) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lut[];
-    float *red = reinterpret_cast<float *>(lut + dec_lut_bytes<MULTI>());
+    float *red = reinterpret_cast<float *>(lut + dec_lut_bytes<FMT, MULTI>());
     SmallRoute &sr = *reinterpret_cast<SmallRoute *>(red + dec_red_floats<MULTI>());
     constexpr int SGN = dec_sgn_bytes<MULTI>();
     const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -748,15 +929,18 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
         // Loads that do not depend on each other go out first: the codebook
         // rows, the logits, this workgroup's shared-h partials (on wave 1:
         // wave 0 routes); the tables are written while they arrive.
+        constexpr bool kTab = FMT != BITMOE_FORMAT_MXFP4;
         uint2 grow = make_uint2(0u, 0u);
-        if (tid < 256) grow = *reinterpret_cast<const uint2 *>(grid + 8 * tid);
+        if (kTab && tid < 256) grow = *reinterpret_cast<const uint2 *>(grid + 8 * tid);
         float lv[4];
         const bool pre = route_mode == 1 && E <= 256 && wv == 0;
         if (pre) route_logits_load(logits, E, 0, lv);
         const int64_t fi = f0 + tid - 64;
         if (tid >= 64 && fi < f1) shared_h_load(nfin, kc_sg, sgp, fi, fg, fu);
-        if (tid < 256) lut_write_line(lut, 0, tid, lut_mag_from_row<1>(grow));
-        else if (tid < 256 + SGN / 256) lut_write_line(lut, kLutMagBytes, tid - 256, lut_sign_entry(tid - 256));
+        if constexpr (kTab) {
+            if (tid < 256) lut_write_line(lut, 0, tid, lut_mag_from_row<1>(grow));
+            else if (tid < 256 + SGN / 256) lut_write_line(lut, kLutMagBytes, tid - 256, lut_sign_entry(tid - 256));
+        }
         if (tid >= 64 && fi < f1) shared_h_store(nfin, kc_sg, sgp, hs, fi, fg, fu);
         for (int64_t i = fi + blockDim.x - 64; tid >= 64 && i < f1; i += blockDim.x - 64) {
             shared_h_load(nfin, kc_sg, sgp, i, fg, fu);
@@ -769,7 +953,7 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
         tk.e = sr.active[slot];
         tk.off = slot;
         tk.cnt = 1;
-        routed_gateup_1<XBF16, SGN>(H, I, k, tk, P, gate, up, x, nullptr, h, hsum2, hscale, red);
+        gateup_1<FMT, XBF16, SGN>(H, I, k, tk, P, gate, up, x, nullptr, h, hsum2, hscale, red);
         return;
     }
     int na = 0;
@@ -785,7 +969,7 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
         // (expert, panel) items are claimed one at a time from a counter the
         // front launch cleared, each next claim in flight while an item is
         // decoded, so that workgroups that start late take fewer items
-        lut_build<1, SGN>(grid, lut);
+        if constexpr (FMT != BITMOE_FORMAT_MXFP4) lut_build<1, SGN>(grid, lut);
         if (tid == 0) sr.claim = __hip_atomic_fetch_add(gctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int n_items = *n_single * panels;
         __syncthreads();
@@ -798,7 +982,7 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
             tk.e = in.x;
             tk.off = in.y;
             tk.cnt = 1;
-            routed_gateup_1<XBF16, SGN>(H, I, k, tk, it % panels, gate, up, x, nullptr, h, hsum2, hscale, red, in.w);
+            gateup_1<FMT, XBF16, SGN>(H, I, k, tk, it % panels, gate, up, x, nullptr, h, hsum2, hscale, red, in.w);
             if (tid == 0) sr.claim = nxt;      // every thread read the last claim before the item's barriers
             __syncthreads();
             it = sr.claim;
@@ -819,7 +1003,7 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
             const int tok = perm[min(max(off, 0), T * k - 1)] / k;
             sr.items[tid] = si < nact ? make_int4(e, off, cnt, tok) : make_int4(-1, 0, 0, 0);
         }
-        lut_build<1, SGN>(grid, lut);
+        if constexpr (FMT != BITMOE_FORMAT_MXFP4) lut_build<1, SGN>(grid, lut);
         __syncthreads();
         for (int j = 0; j < n_it; j++) {
             const int4 in = sr.items[j];
@@ -831,15 +1015,15 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
             if ((tk.cnt > 1) != (MULTI != 0)) continue;
             const int Pi = (b + j * G) % panels;
             if (!MULTI) {
-                routed_gateup_1<XBF16, SGN>(H, I, k, tk, Pi, gate, up, x, perm, h, hsum2, hscale, red, in.w);
+                gateup_1<FMT, XBF16, SGN>(H, I, k, tk, Pi, gate, up, x, perm, h, hsum2, hscale, red, in.w);
                 continue;
             }
             for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
                 if (tk.cnt - t0 == 1)
-                    routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale,
+                    gateup_pass<FMT, XBF16, 1, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale,
                                                       red);
                 else
-                    routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2,
+                    gateup_pass<FMT, XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2,
                                                         hscale, red);
             }
         }
@@ -858,19 +1042,19 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
         tk.cnt = counts[tk.e];
         if ((tk.cnt > 1) != (MULTI != 0)) continue;
         if (!built) {
-            lut_build<1, SGN>(grid, lut);
+            if constexpr (FMT != BITMOE_FORMAT_MXFP4) lut_build<1, SGN>(grid, lut);
             __syncthreads();
             built = true;
         }
         if (!MULTI) {
-            routed_gateup_1<XBF16, SGN>(H, I, k, tk, Pi, gate, up, x, perm, h, hsum2, hscale, red);
+            gateup_1<FMT, XBF16, SGN>(H, I, k, tk, Pi, gate, up, x, perm, h, hsum2, hscale, red);
             continue;
         }
         for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
             if (tk.cnt - t0 == 1)
-                routed_gateup_pass<XBF16, 1, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale, red);
+                gateup_pass<FMT, XBF16, 1, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale, red);
             else
-                routed_gateup_pass<XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale,
+                gateup_pass<FMT, XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale,
                                                     red);
         }
     }
@@ -1005,6 +1189,107 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
         st_dev(&o[(int64_t)perm[tk.off + t0 + wv] * H + P * 64 + lane], s);
     }
     __syncthreads();
+}
+
+// Routed MXFP4 down of panel P for the pair rows of tokens t0..t0+NT-1 of
+// expert tk.  h arrives as fp16 scaled per 64 columns (hscale); each piece
+// (32 columns of h) is 16 fp16 dot products, times its block scale and the
+// h scale.  The wave's share of h (16 pieces at a time, with their scales)
+// is staged in its slice of LDS by one vector load per token.
+template <int NT>
+BM_DEV void mx_down_pass(int H, int I, const Tok &tk, int t0, int P, const uint8_t *__restrict__ down,
+                         const int32_t *__restrict__ perm, const uint16_t *__restrict__ h,
+                         const float *__restrict__ hscale, float *__restrict__ o, float *red, uint4 *hst) {
+    constexpr int kChunk = 16;                       // pieces per staging (64 uint4 of h per token)
+    static_assert(4 * kChunk + 4 <= kHst, "staging slice");
+    const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int rows[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) rows[t] = tk.off + min(t0 + t, tk.cnt - 1);
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = 0.f;
+    const int64_t slab = (int64_t)H * I / 32 * 17;
+    const MxRows D = mx_rows(down + tk.e * slab, H, I, P);
+    const int nsc = I / 64;
+    int p0, p1;
+    split_range(8 * (I / kQK), kWD, wv, p0, p1);
+    struct B4 { uint4 q[4]; uint32_t s[4]; };
+    auto load = [&](int pb, B4 &b) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int pc = min(pb + i, p1 - 1);
+            b.q[i] = D.piece(pc);
+            b.s[i] = D.scale(pc);
+        }
+    };
+    for (int c0 = p0; c0 < p1; c0 += kChunk) {
+        const int c1 = min(c0 + kChunk, p1), g0 = c0 >> 1;
+        uint4 hv[NT];
+        float sv[NT];
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            hv[t] = make_uint4(0u, 0u, 0u, 0u);
+            if (lane < 4 * (c1 - c0))
+                hv[t] = *reinterpret_cast<const uint4 *>(h + (int64_t)rows[t] * I + 32 * c0 + 8 * lane);
+            sv[t] = hscale[(int64_t)rows[t] * nsc + min(g0 + (lane & 15), nsc - 1)];
+        }
+        B4 cur{}, nxt{};
+        load(c0, cur);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            hst[t * kHst + lane] = hv[t];
+            if (lane < 16) reinterpret_cast<float *>(hst + t * kHst + 4 * kChunk)[lane] = sv[t];
+        }
+        for (int pb = c0; pb < c1; pb += 4) {
+            if (pb + 4 < c1) load(pb + 4, nxt);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int pc = pb + i;
+                if (pc < c1) {
+                    const uint32_t qw[4] = {cur.q[i].x, cur.q[i].y, cur.q[i].z, cur.q[i].w};
+                    const float bs = mx_scale(cur.s[i]);
+#pragma unroll
+                    for (int t = 0; t < NT; t++) {
+                        float part = 0.f;
+#pragma unroll
+                        for (int r = 0; r < 4; r++) {
+                            const uint4 hp = hst[t * kHst + 4 * (pc - c0) + r];
+                            part = dot2_f16(fp4x2_f16<0>(qw[r]), hp.x, part);
+                            part = dot2_f16(fp4x2_f16<1>(qw[r]), hp.y, part);
+                            part = dot2_f16(fp4x2_f16<2>(qw[r]), hp.z, part);
+                            part = dot2_f16(fp4x2_f16<3>(qw[r]), hp.w, part);
+                        }
+                        const float hsc = reinterpret_cast<const float *>(hst + t * kHst + 4 * kChunk)[(pc >> 1) - g0];
+                        acc[t] = fmaf(bs, part * hsc, acc[t]);
+                    }
+                }
+            }
+            cur = nxt;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++) red[(wv * NT + t) * 64 + lane] = acc[t];
+    __syncthreads();
+    if (wv < NT && t0 + wv < tk.cnt) {
+        float sum = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWD; v++) sum += red[(v * NT + wv) * 64 + lane];
+        st_dev(&o[(int64_t)perm[tk.off + t0 + wv] * H + P * 64 + lane], sum);
+    }
+    __syncthreads();
+}
+
+template <int FMT, int NT>
+BM_DEV void down_pass(int H, int I, const Tok &tk, int t0, int P, const uint8_t *__restrict__ down,
+                      const int32_t *__restrict__ perm, const uint16_t *__restrict__ h,
+                      const float2 *__restrict__ hsum2, const float *__restrict__ hscale, float *__restrict__ o,
+                      float *red, uint4 *hst) {
+    if constexpr (FMT == BITMOE_FORMAT_MXFP4)
+        mx_down_pass<NT>(H, I, tk, t0, P, down, perm, h, hscale, o, red, hst);
+    else
+        routed_down_pass<NT>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
 }
 
 // Shared down of panel P over the K pieces [c0, c1); h as bf16 hi + lo
@@ -1212,7 +1497,7 @@ k_dec_combine(int H, int k, int T, int kc_sd, const float *__restrict__ o, const
 // MULTI = 0: experts chosen by one token, and the shared down; MULTI = 1:
 // experts chosen by several tokens (launched only when T > 1).  combine = 0:
 // the outputs are only stored (k_dec_combine sums them).
-template <int MULTI>
+template <int FMT, int MULTI>
 __global__ void __launch_bounds__(kWD * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 5)))
 k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__restrict__ n_multi, int combine,
            const uint8_t *__restrict__ down,
@@ -1247,13 +1532,13 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__re
         }
         if ((tk.cnt > 1) != (MULTI != 0)) return;
         if (!MULTI) {
-            routed_down_pass<1>(H, I, tk, 0, P, down, perm, h, hsum2, hscale, o, red, hst);
+            down_pass<FMT, 1>(H, I, tk, 0, P, down, perm, h, hsum2, hscale, o, red, hst);
         } else {
             for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
                 if (tk.cnt - t0 == 1)
-                    routed_down_pass<1>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
+                    down_pass<FMT, 1>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
                 else
-                    routed_down_pass<kNT>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
+                    down_pass<FMT, kNT>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
             }
         }
         if (combine) count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
@@ -1308,8 +1593,9 @@ size_t decode_mid_lds(int E) {
     return (size_t)std::max<int64_t>((int64_t)(2 + kBW) * E, kWaveBucketMax) * sizeof(int);
 }
 
-int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, const DecodePlan &p,
-                  const DecodeBufs &b, hipStream_t s) {
+template <int FMT>
+static int launch_decode_fmt(const bitmoe_layer *L, const void *x, int x_dtype, int T, const DecodePlan &p,
+                             const DecodeBufs &b, hipStream_t s) {
     const int H = L->H, I = L->I, E = L->E, k = L->k;
     const bool shared = L->shared_gate != nullptr;
     const bool bf = x_dtype == BITMOE_BF16;
@@ -1347,16 +1633,17 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     const int route_mode = T == 1 ? (p.n_rwg ? 1 : 2) : 0;
     static const bool lds_set = [] {
         bool ok = true;
-        for (auto f : {k_dec_gateup<1, 0>, k_dec_gateup<0, 0>, k_dec_gateup<1, 1>, k_dec_gateup<0, 1>}) {
+        for (auto f : {k_dec_gateup<FMT, 1, 0>, k_dec_gateup<FMT, 0, 0>, k_dec_gateup<FMT, 1, 1>,
+                       k_dec_gateup<FMT, 0, 1>}) {
             hipFuncAttributes fa;      // the tables must start at LDS address 0
             ok &= hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(f)) == hipSuccess && fa.sharedSizeBytes == 0;
         }
-        for (auto f : {k_dec_gateup<1, 0>, k_dec_gateup<0, 0>})
+        for (auto f : {k_dec_gateup<FMT, 1, 0>, k_dec_gateup<FMT, 0, 0>})
             ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      dec_gateup_lds<0>()) == hipSuccess;
-        for (auto f : {k_dec_gateup<1, 1>, k_dec_gateup<0, 1>})
+                                      dec_gateup_lds<FMT, 0>()) == hipSuccess;
+        for (auto f : {k_dec_gateup<FMT, 1, 1>, k_dec_gateup<FMT, 0, 1>})
             ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      dec_gateup_lds<1>()) == hipSuccess;
+                                      dec_gateup_lds<FMT, 1>()) == hipSuccess;
         return ok;
     }();
     if (!lds_set) return BITMOE_EHIP;
@@ -1396,14 +1683,14 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
         if (hipGetLastError() != hipSuccess) return fail(BITMOE_EHIP);   \
     } while (0)
     for (int multi = 0; multi < (T > 1 && !split ? 2 : 1); multi++) {
-        auto kg = multi ? (bf ? k_dec_gateup<1, 1> : k_dec_gateup<0, 1>)
-                        : (bf ? k_dec_gateup<1, 0> : k_dec_gateup<0, 0>);
+        auto kg = multi ? (bf ? k_dec_gateup<FMT, 1, 1> : k_dec_gateup<FMT, 0, 1>)
+                        : (bf ? k_dec_gateup<FMT, 1, 0> : k_dec_gateup<FMT, 0, 0>);
         // the timing events, when set, are taken by the dispatch itself
         // around the first gate/up launch
         const TimingEvents ev = multi ? TimingEvents{} : timing_for(BITMOE_TIME_GATEUP);
         const int grid = route_mode ? n_gwg : std::min(n_gwg, cu_count());
         hipExtLaunchKernelGGL(kg, dim3(grid), dim3(kWG * 64),
-                              multi ? dec_gateup_lds<1>() : dec_gateup_lds<0>(), sg_stream, ev.start, ev.stop, 0, H, I,
+                              multi ? dec_gateup_lds<FMT, 1>() : dec_gateup_lds<FMT, 0>(), sg_stream, ev.start, ev.stop, 0, H, I,
                               E, k,
                               T, n_gwg, multi ? 0 : route_mode, (const uint8_t *)L->gate_q,
                               (const uint8_t *)L->up_q, (const uint8_t *)L->grid, x, (const float *)b.logits, b.ids,
@@ -1427,7 +1714,7 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     const int n_sd = shared && !sd_mfma ? (H / 64) * p.kc_sd : 0;
     {
         const TimingEvents ev = timing_for(BITMOE_TIME_DOWN);
-        hipExtLaunchKernelGGL(k_dec_down<0>, dim3(n_dwg + n_sd), dim3(kWD * 64), 0, sg_stream, ev.start, ev.stop, 0,
+        hipExtLaunchKernelGGL(k_dec_down<FMT, 0>, dim3(n_dwg + n_sd), dim3(kWD * 64), 0, sg_stream, ev.start, ev.stop, 0,
                               H, I, k, T, n_dwg, p.kc_sd, (const int32_t *)(split ? b.bk.n_tiles : nullptr),
                               split ? 0 : 1, (const uint8_t *)L->down_q, (const uint4 *)L->shared_down,
                               (const int32_t *)b.bk.counts, (const int32_t *)b.bk.offsets, (const int32_t *)b.bk.perm,
@@ -1449,13 +1736,19 @@ int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, cons
     }
 #undef BM_CHECK_JOIN
     if (T > 1 && !split) {
-        k_dec_down<1><<<n_dwg, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, nullptr, 1, (const uint8_t *)L->down_q,
+        k_dec_down<FMT, 1><<<n_dwg, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, nullptr, 1, (const uint8_t *)L->down_q,
                                                 (const uint4 *)L->shared_down, b.bk.counts, b.bk.offsets,
                                                 b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum2, b.hscale, b.hs,
                                                 b.w, b.ycount, shared ? b.osp : nullptr, b.o, b.y);
         BM_LAUNCH_CHECK();
     }
     return BITMOE_OK;
+}
+
+int launch_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, const DecodePlan &p,
+                  const DecodeBufs &b, hipStream_t s) {
+    return L->format == BITMOE_FORMAT_MXFP4 ? launch_decode_fmt<BITMOE_FORMAT_MXFP4>(L, x, x_dtype, T, p, b, s)
+                                            : launch_decode_fmt<BITMOE_FORMAT_2BIT>(L, x, x_dtype, T, p, b, s);
 }
 
 }  // namespace bm_host

@@ -1,5 +1,5 @@
-// Standalone dequantisation of canonical IQ2X / Q2K blocks, and the load-time
-// canonical -> tiled layout transforms.
+// Standalone dequantisation of canonical IQ2X / Q2K / MXFP4 blocks, and the
+// load-time canonical -> tiled layout transforms.
 //
 // Formats: the routed experts' IQ2_XXS-style up/gate blocks and Q2_K down
 // blocks (page "ds4 : analyse pratique pour un usage documente", section
@@ -180,6 +180,84 @@ k_pack_q2k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int E, in
     reinterpret_cast<uint32_t *>(slab + 80 * per_e)[pk * 64 + r] = s[20];
 }
 
+// One thread per canonical MXFP4 block (17 bytes, no alignment).  The
+// gfx950 scaled conversion turns each byte's two elements (weights j and
+// j+16 of the block) into element * 2^(X-127), exactly (fp32), or rounded
+// to nearest-even (bf16), from the E8M0 scale in the exponent field of its
+// scale operand; the FFN kernels use the same conversion.
+template <int OUT_BF16>
+__global__ void __launch_bounds__(256)
+k_dequant_mxfp4(const uint8_t *__restrict__ blocks, int64_t nblocks, void *__restrict__ out) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nblocks) return;
+    const uint8_t *blk = blocks + 17 * b;
+    const float sc = mx_cvt_scale(blk[0]);
+    uint32_t q[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        q[i] = (uint32_t)blk[1 + 4 * i] | ((uint32_t)blk[2 + 4 * i] << 8) | ((uint32_t)blk[3 + 4 * i] << 16) |
+               ((uint32_t)blk[4 + 4 * i] << 24);
+    if (OUT_BF16) {
+        uint32_t lo[8], hi[8];          // bf16 bits of weights 0..15 and 16..31
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t p[4] = {fp4x2_bf16s<0>(q[i], sc), fp4x2_bf16s<1>(q[i], sc), fp4x2_bf16s<2>(q[i], sc),
+                                   fp4x2_bf16s<3>(q[i], sc)};
+            lo[2 * i] = (p[0] & 0xFFFFu) | (p[1] << 16);
+            lo[2 * i + 1] = (p[2] & 0xFFFFu) | (p[3] << 16);
+            hi[2 * i] = (p[0] >> 16) | (p[1] & 0xFFFF0000u);
+            hi[2 * i + 1] = (p[2] >> 16) | (p[3] & 0xFFFF0000u);
+        }
+        uint4 *o = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + 32 * b);
+        o[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        o[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+        o[2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        o[3] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+    } else {
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float2 p[4] = {fp4x2_f32s<0>(q[i], sc), fp4x2_f32s<1>(q[i], sc), fp4x2_f32s<2>(q[i], sc),
+                                 fp4x2_f32s<3>(q[i], sc)};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                v[4 * i + j] = p[j].x;
+                v[16 + 4 * i + j] = p[j].y;
+            }
+        }
+        float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(out) + 32 * b);
+#pragma unroll
+        for (int q4 = 0; q4 < 8; q4++) o[q4] = make_float4(v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]);
+    }
+}
+
+// canonical MXFP4 -> tiled; one thread per block (n, 32-weight block kc):
+// its 16 element bytes re-paired so that byte i holds weights 2i, 2i+1,
+// its scale byte into the row's 8 scales of the 256-weight chunk
+__global__ void __launch_bounds__(256)
+k_pack_mxfp4(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int E, int N, int nb) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_e = (int64_t)N * nb * 8;
+    if (gid >= per_e * E) return;
+    const int64_t e = gid / per_e, rem = gid % per_e;
+    const int n = (int)(rem / (8 * nb)), kc = (int)(rem % (8 * nb)), kb = kc >> 3, c = kc & 7;
+    const int P = n >> 6, r = n & 63;
+    const uint8_t *s = src + 17 * gid;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        // weights 2i and 2i+1: element j sits in qs[j % 16], high nibble if j >= 16
+        const int j0 = 2 * i, j1 = 2 * i + 1;
+        const uint32_t e0 = j0 < 16 ? (s[1 + j0] & 15u) : (s[1 + j0 - 16] >> 4);
+        const uint32_t e1 = j1 < 16 ? (s[1 + j1] & 15u) : (s[1 + j1 - 16] >> 4);
+        w[i >> 2] |= (e0 | (e1 << 4)) << (8 * (i & 3));
+    }
+    uint8_t *slab = dst + e * per_e * 17;
+    const int64_t pk = (int64_t)P * nb + kb;
+    reinterpret_cast<uint4 *>(slab)[(pk * 8 + c) * 64 + r] = make_uint4(w[0], w[1], w[2], w[3]);
+    slab[per_e * 16 + (pk * 64 + r) * 8 + c] = s[0];
+}
+
 // row-major bf16 [N][K] -> tiled; one thread per 8-value piece
 __global__ void __launch_bounds__(256)
 k_pack_bf16(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int N, int K8) {
@@ -226,6 +304,23 @@ int launch_pack_iq2x(const void *src, void *dst, int E, int N, int K, hipStream_
 int launch_pack_q2k(const void *src, void *dst, int E, int N, int K, hipStream_t s) {
     int64_t n = (int64_t)E * N * (K / 256);
     k_pack_q2k<<<grid_for(n, 256), 256, 0, s>>>((const uint8_t *)src, (uint8_t *)dst, E, N, K / 256);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
+
+int launch_dequant_mxfp4(const void *blocks, int64_t nblocks, void *out, int out_dtype, hipStream_t s) {
+    unsigned g = grid_for(nblocks, 256);
+    if (out_dtype == BITMOE_BF16)
+        k_dequant_mxfp4<1><<<g, 256, 0, s>>>((const uint8_t *)blocks, nblocks, out);
+    else
+        k_dequant_mxfp4<0><<<g, 256, 0, s>>>((const uint8_t *)blocks, nblocks, out);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
+
+int launch_pack_mxfp4(const void *src, void *dst, int E, int N, int K, hipStream_t s) {
+    int64_t n = (int64_t)E * N * (K / 32);
+    k_pack_mxfp4<<<grid_for(n, 256), 256, 0, s>>>((const uint8_t *)src, (uint8_t *)dst, E, N, K / 256);
     BM_LAUNCH_CHECK();
     return BITMOE_OK;
 }

@@ -41,6 +41,8 @@ int launch_dequant_q2k(const void *blocks, int64_t nblocks, void *out,
 int launch_pack_iq2x(const void *src, void *dst, int E, int N, int K, hipStream_t s);
 int launch_pack_q2k(const void *src, void *dst, int E, int N, int K, hipStream_t s);
 int launch_pack_bf16(const void *src, void *dst, int N, int K, hipStream_t s);
+int launch_dequant_mxfp4(const void *blocks, int64_t nblocks, void *out, int out_dtype, hipStream_t s);
+int launch_pack_mxfp4(const void *src, void *dst, int E, int N, int K, hipStream_t s);
 
 int launch_quant_iq2x(const float *w, const void *grid, int64_t nblocks, void *out, hipStream_t s);
 int launch_quant_q2k(const float *w, int64_t nblocks, void *out, hipStream_t s);

@@ -519,14 +519,70 @@ BM_DEV void dn_stage_put(uint8_t *dst, const int *semax, const int (&ex)[dn_piec
     }
 }
 
+// Down epilogue: lane holds rows 32i + acc_row(r, kh) of output column c0,
+// each row's value being acc * 2^(semax[m] - wshift).  fp32 outputs per pair
+// (OUT32), or fp16 with one power-of-two exponent per (pair, 512 columns):
+// each row's largest |value| over the workgroup's 512 columns (32 lanes of
+// a half-wave by DPP, then the 16 waves through LDS) sets its power of two.
+template <int MB, int OUT32>
+BM_DEV void dn_epilogue(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile, const f32x16 (&acc)[MB],
+                        int c0, bool active, int wshift) {
+    const int *semax = reinterpret_cast<const int *>(lds + 2 * kPfABytes);
+    int *soex = const_cast<int *>(semax) + kPfRows;
+    const int *spair = soex + kPfRows;
+    float *smax = reinterpret_cast<float *>(soex + 2 * kPfRows);
+    const int lane = lane_id(), col = lane & 31, kh = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (OUT32) {
+        if (!active) return;
+#pragma unroll
+        for (int i = 0; i < MB; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = 32 * i + acc_row(r, kh);
+                if (m < t.rows) a.o[(int64_t)spair[m] * a.H + c0] = ldexpf(acc[i][r], semax[m] - wshift);
+            }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            float mx = active ? fabsf(acc[i][r]) : 0.f;
+            mx = dpp_max<0x111, 0xF>(mx);
+            mx = dpp_max<0x112, 0xF>(mx);
+            mx = dpp_max<0x114, 0xF>(mx);
+            mx = dpp_max<0x118, 0xF>(mx);
+            mx = dpp_max<0x142, 0xA>(mx);
+            if (col == 31) smax[w * kPfRows + 32 * i + acc_row(r, kh)] = mx;
+        }
+    __syncthreads();
+    if (threadIdx.x < 32 * MB) {
+        float mx = 0.f;
+#pragma unroll
+        for (int v = 0; v < kDnWaves; v++) mx = fmaxf(mx, smax[v * kPfRows + threadIdx.x]);
+        const int e = pf_exponent(mx);
+        soex[threadIdx.x] = e;
+        if ((int)threadIdx.x < t.rows)
+            a.oexp[(int64_t)spair[threadIdx.x] * ((a.H + kPfDnCols - 1) / kPfDnCols) + ntile] =
+                e + semax[threadIdx.x] - wshift;
+    }
+    __syncthreads();
+    if (!active) return;
+#pragma unroll
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int m = 32 * i + acc_row(r, kh);
+            if (m < t.rows) a.o16[(int64_t)spair[m] * a.H + c0] = (uint16_t)f16_bits(ldexpf(acc[i][r], -soex[m]));
+        }
+}
+
 template <int MB, int OUT32>
 BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
     constexpr int R = 32 * MB, DP = dn_pieces<R>();
     uint8_t *const sa = lds;                             // A buffer b at sa + b * kPfABytes
     int *semax = reinterpret_cast<int *>(lds + 2 * kPfABytes);
-    int *soex = semax + kPfRows;
-    const int *spair = soex + kPfRows;
-    float *smax = reinterpret_cast<float *>(soex + 2 * kPfRows);
     const int lane = lane_id(), col = lane & 31, kh = lane >> 5;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = a.I / kQK;
@@ -632,53 +688,7 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
     if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0);
     if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1);
     if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2);
-    // epilogue: lane holds rows 32i + acc_row(r, kh), column c0
-    if (OUT32) {
-        if (!active) return;
-#pragma unroll
-        for (int i = 0; i < MB; i++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = 32 * i + acc_row(r, kh);
-                if (m < t.rows) a.o[(int64_t)spair[m] * a.H + c0] = ldexpf(acc[i][r], semax[m] - kPfDnWShift);
-            }
-        return;
-    }
-    // fp16 outputs: each row's largest |value| over the workgroup's 512
-    // columns (32 lanes of a half-wave by DPP, then the 16 waves through LDS)
-    // sets its power of two
-#pragma unroll
-    for (int i = 0; i < MB; i++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-            float mx = active ? fabsf(acc[i][r]) : 0.f;
-            mx = dpp_max<0x111, 0xF>(mx);
-            mx = dpp_max<0x112, 0xF>(mx);
-            mx = dpp_max<0x114, 0xF>(mx);
-            mx = dpp_max<0x118, 0xF>(mx);
-            mx = dpp_max<0x142, 0xA>(mx);
-            if (col == 31) smax[w * kPfRows + 32 * i + acc_row(r, kh)] = mx;
-        }
-    __syncthreads();
-    if (threadIdx.x < R) {
-        float mx = 0.f;
-#pragma unroll
-        for (int v = 0; v < kDnWaves; v++) mx = fmaxf(mx, smax[v * kPfRows + threadIdx.x]);
-        const int e = pf_exponent(mx);
-        soex[threadIdx.x] = e;
-        if ((int)threadIdx.x < t.rows)
-            a.oexp[(int64_t)spair[threadIdx.x] * ((a.H + kPfDnCols - 1) / kPfDnCols) + ntile] =
-                e + semax[threadIdx.x] - kPfDnWShift;
-    }
-    __syncthreads();
-    if (!active) return;
-#pragma unroll
-    for (int i = 0; i < MB; i++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int m = 32 * i + acc_row(r, kh);
-            if (m < t.rows) a.o16[(int64_t)spair[m] * a.H + c0] = (uint16_t)f16_bits(ldexpf(acc[i][r], -soex[m]));
-        }
+    dn_epilogue<MB, OUT32>(a, lds, t, ntile, acc, c0, active, kPfDnWShift);
 }
 
 template <int OUT32>
@@ -709,6 +719,273 @@ k_pf_down(DnArgs a) {
         case 1: dn_tile<1, OUT32>(a, lds, t, sl.ntile); break;
         case 2: dn_tile<2, OUT32>(a, lds, t, sl.ntile); break;
         default: dn_tile<3, OUT32>(a, lds, t, sl.ntile); break;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 routed experts.  The operands are bf16: the activations as they
+// are (fp32 activations rounded to bf16 first, k_mx_xprep), h rounded to
+// bf16, and the weights straight from the hardware conversion, one
+// instruction per weight pair with the block scale applied (element *
+// 2^(X-127) is exact in bf16 for every X up to 252), so there are no
+// tables and no exponent bookkeeping: the k-step's VALU work is eight
+// conversions (gate/up) or four (down) against 2 MB or MB MFMAs.
+// Tiled MXFP4 slab of an [N][K] matrix: piece c (32 weights) of 256-weight
+// chunk kb of row P*64 + r at ((P nb + kb) 8 + c) 64 + r, 16 bytes, byte i
+// holding weights 2i (low nibble) and 2i+1; the row's 8 scale bytes of the
+// chunk at N K/2 + ((P nb + kb) 64 + r) 8.  In a stage (half chunk: pieces
+// 4 hf .. 4 hf + 3) lane half kh takes pieces 4 hf + 2 kh and + 1, k-step t
+// reading dword t & 3 of piece 4 hf + 2 kh + (t >> 2): stage K offset
+// 64 kh + 8 t, as for the 2-bit formats.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int kMxGuLds = 2 * kPfABytes + kPfRows * 4;
+
+BM_DEV f32x16 mfma32b(bf16x8 a, bf16x8 b, f32x16 c) { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+template <int R>
+BM_DEV bf16x8 frag32b(const uint8_t *buf, int i, int lane, int t) {
+    return *reinterpret_cast<const bf16x8 *>(buf + ((8 * (lane >> 5) + t) * R + 32 * i + (lane & 31)) * 16);
+}
+// bf16 operand of 8 weights (one dword) at scale 2^(X-127)
+BM_DEV bf16x8 mx_operand(uint32_t W, uint32_t X) {
+    const float sc = mx_cvt_scale(X);
+    const uint4 v = make_uint4(fp4x2_bf16s<0>(W, sc), fp4x2_bf16s<1>(W, sc), fp4x2_bf16s<2>(W, sc),
+                               fp4x2_bf16s<3>(W, sc));
+    return __builtin_bit_cast(bf16x8, v);
+}
+BM_DEV uint32_t u4_word(const uint4 &v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+
+// fp32 activations -> bf16 (nearest-even), 8 per thread
+__global__ void __launch_bounds__(256)
+k_mx_xprep(int64_t n8, const float *__restrict__ x, uint16_t *__restrict__ xb) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const float4 *p = reinterpret_cast<const float4 *>(x) + 2 * i;
+    const float4 u = p[0], v = p[1];
+    reinterpret_cast<uint4 *>(xb)[i] =
+        make_uint4(f32_to_bf16_rne(u.x) | (f32_to_bf16_rne(u.y) << 16), f32_to_bf16_rne(u.z) | (f32_to_bf16_rne(u.w) << 16),
+                   f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16), f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16));
+}
+
+// gate/up: 8 waves x 32 h columns as in gu_tile; a.x16 holds the bf16
+// activation rows.  Epilogue: h = silu(g) u rounded to bf16.
+template <int MB>
+BM_DEV void mx_gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
+    constexpr int R = 32 * MB;
+    uint8_t *const sa = lds;                            // A buffer b at sa + b * kPfABytes
+    const int *stok = reinterpret_cast<const int *>(lds + 2 * kPfABytes);
+    const int lane = lane_id(), col = lane & 31, kh = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nb = a.H / kQK;
+    const int64_t slab = (int64_t)a.I * a.H / 32 * 17;
+    const uint8_t *G = a.gate + t.e * slab, *U = a.up + t.e * slab;
+    const int hc = ntile * kPfGuCols + 32 * w + col, P = hc >> 6, pr = hc & 63;
+    // byte offsets at chunk 0, half 0 (one expert's slab is below 4 GiB)
+    const uint32_t qoff = (uint32_t)((P * nb * 8 + 2 * kh) * 64 + pr) * 16;
+    const uint32_t soff = (uint32_t)(a.I * a.H / 2) + (uint32_t)(P * nb * 64 + pr) * 8 + 2 * kh;
+    struct Slot { uint4 g0, g1, u0, u1; uint32_t sg, su; };
+    auto load_slot = [&](int st, Slot &sl) {
+        const int kb = st >> 1, hf = st & 1;
+        const uint32_t o = qoff + kb * 8192 + hf * 4096, os = soff + kb * 512 + 4 * hf;
+        sl.g0 = *reinterpret_cast<const uint4 *>(G + o);
+        sl.g1 = *reinterpret_cast<const uint4 *>(G + o + 1024);
+        sl.u0 = *reinterpret_cast<const uint4 *>(U + o);
+        sl.u1 = *reinterpret_cast<const uint4 *>(U + o + 1024);
+        sl.sg = *reinterpret_cast<const uint16_t *>(G + os);
+        sl.su = *reinterpret_cast<const uint16_t *>(U + os);
+    };
+    f32x16 acc[MB][2];
+#pragma unroll
+    for (int i = 0; i < MB; i++) acc[i][0] = acc[i][1] = (f32x16)0.f;
+    auto compute = [&](const uint8_t *A, const Slot &sl) {
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            bf16x8 av[MB];
+#pragma unroll
+            for (int i = 0; i < MB; i++) av[i] = frag32b<R>(A, i, lane, s);
+            const bf16x8 bg = mx_operand(u4_word(s < 4 ? sl.g0 : sl.g1, s & 3), s < 4 ? sl.sg & 0xFFu : sl.sg >> 8);
+            const bf16x8 bu = mx_operand(u4_word(s < 4 ? sl.u0 : sl.u1, s & 3), s < 4 ? sl.su & 0xFFu : sl.su >> 8);
+#pragma unroll
+            for (int i = 0; i < MB; i++) {
+                acc[i][0] = mfma32b(av[i], bg, acc[i][0]);
+                acc[i][1] = mfma32b(av[i], bu, acc[i][1]);
+            }
+        }
+    };
+    // pipeline as in gu_tile: at the start of stage st the activations of
+    // st+1 and then the slot of st+2 are loaded; three slots rotate by call
+    const int nsteps = 2 * nb;
+    u32x4 ar[R / 32];
+    auto stage = [&](auto full, int st, Slot &cur, Slot &pre) {
+        const int s1 = st + 1, s2 = st + 2;
+        asm volatile("" ::: "memory");
+        if (full || s1 < nsteps) gu_stage_load<R>(a, stok, s1 >> 1, s1 & 1, ar);
+        asm volatile("" ::: "memory");
+        if (full || s2 < nsteps) load_slot(s2, pre);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sa + (st & 1) * kPfABytes, cur);
+        if (full || s1 < nsteps) stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
+        __syncthreads();
+    };
+    using Full = std::integral_constant<bool, true>;
+    using Part = std::integral_constant<bool, false>;
+    Slot q0, q1, q2;
+    gu_stage_load<R>(a, stok, 0, 0, ar);
+    load_slot(0, q0);
+    if (nsteps > 1) load_slot(1, q1);
+    stage_store<R>(sa, ar);
+    __builtin_amdgcn_s_waitcnt(0);       // see gu_tile
+    __syncthreads();
+    int st = 0;
+    for (; st + 5 <= nsteps; st += 3) {
+        stage(Full{}, st, q0, q2);
+        stage(Full{}, st + 1, q1, q0);
+        stage(Full{}, st + 2, q2, q1);
+    }
+    if (st < nsteps) stage(Part{}, st, q0, q2);
+    if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0);
+    if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1);
+    if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2);
+#pragma unroll
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int m = 32 * i + acc_row(r, kh);
+            if (m < t.rows)
+                a.h[(int64_t)(t.off + t.r0 + m) * a.I + hc] =
+                    (uint16_t)f32_to_bf16_rne(silu(acc[i][0][r]) * acc[i][1][r]);
+        }
+}
+
+__global__ void __launch_bounds__(kPfThreads)
+k_mx_gateup(GuArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    asm volatile("" ::: "a0");           // accumulators in AGPRs (see k_pf_gateup)
+    const PfSlot sl = pf_slot(a.I / kPfGuCols);
+    if (sl.tile >= *a.n_tiles) return;
+    const PfTile t = pf_tile(sl.tile, a.tiles, a.counts, a.offsets);
+    int *stok = reinterpret_cast<int *>(lds + 2 * kPfABytes);
+    if (threadIdx.x < kPfRows) stok[threadIdx.x] = a.perm[t.off + t.r0 + min((int)threadIdx.x, t.rows - 1)] / a.k;
+    __syncthreads();
+    switch ((t.rows + 31) >> 5) {
+        case 1: mx_gu_tile<1>(a, lds, t, sl.ntile); break;
+        case 2: mx_gu_tile<2>(a, lds, t, sl.ntile); break;
+        default: mx_gu_tile<3>(a, lds, t, sl.ntile); break;
+    }
+}
+
+// down: 16 waves x 32 output columns as in dn_tile; A = the bf16 h rows
+// copied into the stage as they are.
+template <int R>
+BM_DEV void mx_dn_stage_load(const DnArgs &a, const PfTile &t, int kb, int hf, u32x4 (&r)[dn_pieces<R>()]) {
+    const int k0 = kb * kQK + hf * kPfHalf;
+#pragma unroll
+    for (int p = 0; p < dn_pieces<R>(); p++) {
+        const StageIdx x = dn_stage_idx(p);
+        const int64_t gr = t.off + t.r0 + min(min(x.row, R - 1), t.rows - 1);
+        r[p] = *reinterpret_cast<const u32x4 *>(a.h + gr * a.I + k0 + 8 * x.c);
+    }
+}
+template <int R>
+BM_DEV void mx_dn_stage_put(uint8_t *dst, const u32x4 (&r)[dn_pieces<R>()]) {
+#pragma unroll
+    for (int p = 0; p < dn_pieces<R>(); p++) {
+        const StageIdx x = dn_stage_idx(p);
+        if (x.row < R) *reinterpret_cast<u32x4 *>(dst + (x.c * R + x.row) * 16) = r[p];
+    }
+}
+
+template <int MB, int OUT32>
+BM_DEV void mx_dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
+    constexpr int R = 32 * MB, DP = dn_pieces<R>();
+    uint8_t *const sa = lds;
+    const int lane = lane_id(), col = lane & 31, kh = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nb = a.I / kQK;
+    const int64_t slab = (int64_t)a.H * a.I / 32 * 17;
+    const uint8_t *D = a.down + (int64_t)t.e * slab;
+    const int c0 = ntile * kPfDnCols + 32 * w + col;
+    const bool active = ntile * kPfDnCols + 32 * w < a.H;     // wave-uniform
+    const int cc = min(c0, a.H - 1), P = cc >> 6, pr = cc & 63;
+    const uint32_t qoff = (uint32_t)((P * nb * 8 + 2 * kh) * 64 + pr) * 16;
+    const uint32_t soff = (uint32_t)(a.H * a.I / 2) + (uint32_t)(P * nb * 64 + pr) * 8 + 2 * kh;
+    struct Slot { uint4 w0, w1; uint32_t sc; };
+    auto load_slot = [&](int st, Slot &sl) {
+        const int kb = st >> 1, hf = st & 1;
+        const uint32_t o = qoff + kb * 8192 + hf * 4096;
+        sl.w0 = *reinterpret_cast<const uint4 *>(D + o);
+        sl.w1 = *reinterpret_cast<const uint4 *>(D + o + 1024);
+        sl.sc = *reinterpret_cast<const uint16_t *>(D + soff + kb * 512 + 4 * hf);
+    };
+    f32x16 acc[MB];
+#pragma unroll
+    for (int i = 0; i < MB; i++) acc[i] = (f32x16)0.f;
+    auto compute = [&](const uint8_t *A, const Slot &sl) {
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            bf16x8 af[MB];
+#pragma unroll
+            for (int i = 0; i < MB; i++) af[i] = frag32b<R>(A, i, lane, s);
+            const bf16x8 b = mx_operand(u4_word(s < 4 ? sl.w0 : sl.w1, s & 3), s < 4 ? sl.sc & 0xFFu : sl.sc >> 8);
+#pragma unroll
+            for (int i = 0; i < MB; i++) acc[i] = mfma32b(af[i], b, acc[i]);
+        }
+    };
+    const int nsteps = 2 * nb;
+    u32x4 ar[DP];
+    auto stage = [&](auto full, int st, Slot &cur, Slot &pre) {
+        const int s1 = st + 1, s2 = st + 2;
+        asm volatile("" ::: "memory");
+        if (full || s1 < nsteps) mx_dn_stage_load<R>(a, t, s1 >> 1, s1 & 1, ar);
+        asm volatile("" ::: "memory");
+        if (full || s2 < nsteps) load_slot(s2, pre);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if (active) compute(sa + (st & 1) * kPfABytes, cur);
+        if (full || s1 < nsteps) mx_dn_stage_put<R>(sa + (s1 & 1) * kPfABytes, ar);
+        __syncthreads();
+    };
+    using Full = std::integral_constant<bool, true>;
+    using Part = std::integral_constant<bool, false>;
+    Slot q0, q1, q2;
+    mx_dn_stage_load<R>(a, t, 0, 0, ar);
+    load_slot(0, q0);
+    if (nsteps > 1) load_slot(1, q1);
+    mx_dn_stage_put<R>(sa, ar);
+    __builtin_amdgcn_s_waitcnt(0);       // see gu_tile
+    __syncthreads();
+    int st = 0;
+    for (; st + 5 <= nsteps; st += 3) {
+        stage(Full{}, st, q0, q2);
+        stage(Full{}, st + 1, q1, q0);
+        stage(Full{}, st + 2, q2, q1);
+    }
+    if (st < nsteps) stage(Part{}, st, q0, q2);
+    if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0);
+    if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1);
+    if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2);
+    dn_epilogue<MB, OUT32>(a, lds, t, ntile, acc, c0, active, 0);
+}
+
+template <int OUT32>
+__global__ void __launch_bounds__(kDnThreads)
+k_mx_down(DnArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const PfSlot sl = pf_slot((a.H + kPfDnCols - 1) / kPfDnCols);
+    if (sl.tile >= *a.n_tiles) return;
+    const PfTile t = pf_tile(sl.tile, a.tiles, a.counts, a.offsets);
+    // the epilogue's row exponents (0: h is not rescaled) and pairs
+    int *semax = reinterpret_cast<int *>(lds + 2 * kPfABytes);
+    if (threadIdx.x < kPfRows) {
+        semax[threadIdx.x] = 0;
+        semax[2 * kPfRows + threadIdx.x] = a.perm[t.off + t.r0 + min((int)threadIdx.x, t.rows - 1)];
+    }
+    __syncthreads();
+    switch ((t.rows + 31) >> 5) {
+        case 1: mx_dn_tile<1, OUT32>(a, lds, t, sl.ntile); break;
+        case 2: mx_dn_tile<2, OUT32>(a, lds, t, sl.ntile); break;
+        default: mx_dn_tile<3, OUT32>(a, lds, t, sl.ntile); break;
     }
 }
 
@@ -811,8 +1088,46 @@ k_combine_p(const uint16_t *__restrict__ o16, const int32_t *__restrict__ oexp, 
 
 namespace bm_host {
 
+// MXFP4 routed experts: activation rounding (fp32 input only), gate/up, down
+static int launch_prefill_routed_mx(const bitmoe_layer *L, const void *x, int x_dtype, int T, const Buckets &b,
+                                    int max_tiles, const PrefillBufs &pb, hipStream_t s) {
+    const int H = L->H, I = L->I, k = L->k;
+    static const bool attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_down<0>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kPfDnLdsAll) == hipSuccess &&
+        hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_down<1>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kPfDnLdsAll) == hipSuccess;
+    if (!attr) return BITMOE_EHIP;
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    if (x_dtype != BITMOE_BF16) {
+        const int64_t n8 = (int64_t)T * H / 8;
+        k_mx_xprep<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(n8, static_cast<const float *>(x), pb.x16);
+        BM_LAUNCH_CHECK();
+        xb = pb.x16;
+    }
+    {
+        GuArgs a{H, I, k, (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q, nullptr, xb, nullptr,
+                 b.counts, b.offsets, b.perm, b.tiles, b.n_tiles, pb.h, nullptr};
+        const TimingEvents ev = timing_for(BITMOE_TIME_GATEUP);
+        hipExtLaunchKernelGGL(k_mx_gateup, dim3(pf_grid(max_tiles, I / kPfGuCols)), dim3(kPfThreads), kMxGuLds, s,
+                              ev.start, ev.stop, 0, a);
+        BM_LAUNCH_CHECK();
+    }
+    {
+        DnArgs a{H, I, (const uint8_t *)L->down_q, pb.h, nullptr, b.counts, b.offsets, b.perm, b.tiles,
+                 b.n_tiles, pb.o, pb.o16, pb.oexp};
+        const TimingEvents ev = timing_for(BITMOE_TIME_DOWN);
+        hipExtLaunchKernelGGL(pb.o16 ? k_mx_down<0> : k_mx_down<1>,
+                              dim3(pf_grid(max_tiles, (H + kPfDnCols - 1) / kPfDnCols)), dim3(kDnThreads),
+                              kPfDnLdsAll, s, ev.start, ev.stop, 0, a);
+        BM_LAUNCH_CHECK();
+    }
+    return BITMOE_OK;
+}
+
 int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int T, const Buckets &b,
                           int max_tiles, const PrefillBufs &pb, hipStream_t s) {
+    if (L->format == BITMOE_FORMAT_MXFP4) return launch_prefill_routed_mx(L, x, x_dtype, T, b, max_tiles, pb, s);
     const int H = L->H, I = L->I, k = L->k;
     static const bool attr = [] {
         hipFuncAttributes fa;           // the gate/up tables must start at LDS address 0

@@ -58,6 +58,16 @@
  *     weight i = d * scale * q - dmin * min
  *   A projection with N outputs and K inputs stores block (n, kb) at index
  *   n*(K/256) + kb; experts are stacked on a leading axis [E].
+ *   MXFP4 (OCP Microscaling: FP4 E2M1 elements, one E8M0 scale per 32; the
+ *   pages' MXFP4 variant keeps the released FP4 expert weights, "ds4 :
+ *   analyse pratique ...", section "Support de modeles et choix de
+ *   quantification"), 17 bytes per 32 consecutive weights of one row:
+ *     byte 0      scale exponent X: the block's scale is 2^(X-127) (X = 255: NaN)
+ *     bytes 1-16  qs: weight j (0..15) in the low nibble of qs[j], weight
+ *                 j+16 in its high nibble
+ *     element code c: sign c >> 3, then 0, 0.5, 1, 1.5, 2, 3, 4, 6 for c & 7
+ *     weight = element * 2^(X-127)
+ *   Block (n, kb) of an [N][K] projection at index n*(K/32) + kb.
  *
  *  TILED layout (what the FFN entry points read; moe_pack_* produces it;
  *  bitmoe_layer.layout says which of the two a descriptor's blocks are in).
@@ -85,6 +95,13 @@
  *                             that of weight 2p+1 at bits 16+2p
  *     [64*N*nb, 80*N*nb):     scales (bytes 0-15) at (P*nb + kb)*64 + r, 16 B
  *     [80*N*nb, 84*N*nb):     d, dmin (bytes 80-83) at (P*nb + kb)*64 + r, 4 B
+ *   MXFP4 slab (N*(K/32)*17 bytes), nb = K/256 again:
+ *     [0, N*K/2):             piece c (the block of weights 32c..32c+31 of
+ *                             the 256 at kb) at ((P*nb + kb)*8 + c)*64 + r,
+ *                             16 bytes: byte i holds weight 2i in its low
+ *                             nibble and weight 2i+1 in its high nibble
+ *     [N*K/2, N*K*17/32):     the 8 scale bytes X of (n, kb) at
+ *                             ((P*nb + kb)*64 + r)*8, piece c's at + c
  *   BF16 (shared expert) matrix [N][K] row-major -> tiled: the 8 values
  *   K = 8c..8c+7 of row n at ((P*(K/8) + c)*64 + r)*16 bytes.
  */
@@ -114,6 +131,9 @@ extern "C" {
 #define BITMOE_LAYOUT_CANONICAL 0   /* GGML block order (the interchange format) */
 #define BITMOE_LAYOUT_TILED     1   /* 64-row panels (moe_pack_*), read by the FFN calls */
 
+#define BITMOE_FORMAT_2BIT  0   /* routed gate/up IQ2X, down Q2K (grid required) */
+#define BITMOE_FORMAT_MXFP4 1   /* routed gate, up and down MXFP4 (grid unused) */
+
 #define BITMOE_TIME_GATEUP 0        /* moe_set_timing_events: the routed gate/up kernel */
 #define BITMOE_TIME_DOWN   1        /* moe_set_timing_events: the routed down kernel */
 
@@ -129,18 +149,22 @@ typedef struct bitmoe_layer {
     int32_t E;                 /* routed experts, k <= E <= 1024 */
     int32_t k;                 /* experts per token, 1..16 */
     const void *router_w;      /* bf16 [E][H] row-major */
-    const void *gate_q;        /* TILED IQ2X, E slabs of I*(H/256)*66 bytes */
-    const void *up_q;          /* TILED IQ2X, same shape as gate_q */
-    const void *down_q;        /* TILED Q2K, E slabs of H*(I/256)*84 bytes */
+    const void *gate_q;        /* TILED IQ2X, E slabs of I*(H/256)*66 bytes
+                                  (MXFP4: I*(H/32)*17 bytes) */
+    const void *up_q;          /* same shape as gate_q */
+    const void *down_q;        /* TILED Q2K, E slabs of H*(I/256)*84 bytes
+                                  (MXFP4: H*(I/32)*17 bytes) */
     const void *grid;          /* uint8 [256][8] codebook magnitudes (the
                                   format's codebook holds 1, 3, 5, 7; any
-                                  byte is accepted) */
+                                  byte is accepted); unused for MXFP4 */
     const void *shared_gate;   /* TILED bf16 [I][H], or NULL: no shared expert */
     const void *shared_up;     /* TILED bf16 [I][H] (NULL iff shared_gate is) */
     const void *shared_down;   /* TILED bf16 [H][I] (NULL iff shared_gate is) */
     int32_t layout;            /* BITMOE_LAYOUT_TILED or BITMOE_LAYOUT_CANONICAL:
                                   the layout of gate_q, up_q, down_q and the
                                   shared matrices */
+    int32_t format;            /* BITMOE_FORMAT_2BIT (0) or BITMOE_FORMAT_MXFP4:
+                                  the routed experts' block format */
 } bitmoe_layer;
 
 /*
@@ -287,6 +311,15 @@ int moe_dequant_iq2x(const void *blocks, const void *grid, int64_t nblocks,
                      void *out, int out_dtype, void *stream);
 int moe_dequant_q2k(const void *blocks, int64_t nblocks, void *out,
                     int out_dtype, void *stream);
+/*
+ * The same for CANONICAL MXFP4 blocks (17 bytes, see above): nblocks blocks
+ * -> out [nblocks*32].  BITMOE_F32 output is the fp32 rounding of
+ * element * 2^(X-127) (exact unless it overflows to +-inf; X = 255 gives
+ * NaN); BITMOE_BF16 output rounds that to nearest-even.  Errors: EINVAL
+ * (null pointer, out not 16-byte aligned, nblocks < 0, bad dtype), EHIP.
+ */
+int moe_dequant_mxfp4(const void *blocks, int64_t nblocks, void *out,
+                      int out_dtype, void *stream);
 
 /*
  * Routed-expert residency cache, for layers whose routed experts do not all
@@ -368,6 +401,7 @@ int moe_quantize_q2k(const float *w, int64_t nblocks, void *blocks, void *stream
 int moe_pack_iq2x(const void *src, void *dst, int E, int N, int K, void *stream);
 int moe_pack_q2k(const void *src, void *dst, int E, int N, int K, void *stream);
 int moe_pack_bf16(const void *src, void *dst, int N, int K, void *stream);
+int moe_pack_mxfp4(const void *src, void *dst, int E, int N, int K, void *stream);
 
 /*
  * Measurement hook.  When start and stop are both hipEvent_t handles (passed

@@ -43,9 +43,11 @@ def synth_layer(w: synth.Workload):
 def device_layer(w: synth.Workload):
     import bit_moe_amd as bm
     L = synth_layer(w)
-    say(f"[upload] {w.name} H={w.H} I={w.I} E={w.E} k={w.k} shared={w.shared}")
+    say(f"[upload] {w.name} H={w.H} I={w.I} E={w.E} k={w.k} shared={w.shared} fmt={w.fmt}")
+    mx = w.fmt == "mxfp4"
     lay = bm.layer_from_canonical(w.H, w.I, w.E, w.k, L.router(), L.gate_all(), L.up_all(),
-                                  L.down_all(), L.grid(), L.shared())
+                                  L.down_all(), None if mx else L.grid(), L.shared(),
+                                  fmt=bm.FORMAT_MXFP4 if mx else bm.FORMAT_2BIT)
     torch.cuda.synchronize()
     return lay
 

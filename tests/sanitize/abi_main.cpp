@@ -21,13 +21,16 @@ static int failures = 0;
 
 static void *fake(uintptr_t a) { return reinterpret_cast<void *>(a); }
 
-static bitmoe_layer layer(int H, int I, int E, int k, bool shared, int layout = BITMOE_LAYOUT_TILED) {
+static bitmoe_layer layer(int H, int I, int E, int k, bool shared, int layout = BITMOE_LAYOUT_TILED,
+                          int format = BITMOE_FORMAT_2BIT) {
     bitmoe_layer L;
     std::memset(&L, 0, sizeof(L));
     L.H = H; L.I = I; L.E = E; L.k = k;
     L.router_w = L.gate_q = L.up_q = L.down_q = L.grid = fake(1 << 20);
     if (shared) L.shared_gate = L.shared_up = L.shared_down = fake(2 << 20);
     L.layout = layout;
+    L.format = format;
+    if (format == BITMOE_FORMAT_MXFP4) L.grid = nullptr;       // not needed by MXFP4 layers
     return L;
 }
 
@@ -35,9 +38,10 @@ int main() {
     const int shapes[][4] = {{256, 512, 8, 2}, {7168, 2048, 256, 8}, {512, 256, 1024, 16}, {256, 256, 1, 1}};
     const int tokens[] = {1, 2, 3, 4, 16, 17, 63, 64, 96, 97, 200, 2048, 8192, 65536, 1 << 20};
     void *x = fake(1 << 24), *out = fake(2 << 24), *ws = fake(3 << 24);
+    for (int fmt = 0; fmt < 2; fmt++)
     for (const auto &s : shapes)
         for (int sh = 0; sh < 2; sh++) {
-            bitmoe_layer L = layer(s[0], s[1], s[2], s[3], sh);
+            bitmoe_layer L = layer(s[0], s[1], s[2], s[3], sh, BITMOE_LAYOUT_TILED, fmt);
             size_t prev[2] = {0, 0};
             for (int T : tokens) {
                 for (int mode = 0; mode < 2; mode++) {
@@ -94,6 +98,16 @@ int main() {
     EXPECT(moe_pack_iq2x(x, out, 2, 64, 256, nullptr) == BITMOE_EHIP);
     EXPECT(moe_pack_q2k(x, out, 2, 64, 100, nullptr) == BITMOE_EUNSUPPORTED);
     EXPECT(moe_pack_bf16(x, out, 64, 12, nullptr) == BITMOE_EUNSUPPORTED);
+    EXPECT(moe_dequant_mxfp4(fake(3), 10, out, 0, nullptr) == BITMOE_EHIP);      // blocks: no alignment
+    EXPECT(moe_dequant_mxfp4(x, 10, fake(8), 0, nullptr) == BITMOE_EINVAL);
+    EXPECT(moe_dequant_mxfp4(x, 10, out, 2, nullptr) == BITMOE_EINVAL);
+    EXPECT(moe_pack_mxfp4(fake(3), out, 2, 64, 256, nullptr) == BITMOE_EHIP);
+    EXPECT(moe_pack_mxfp4(x, out, 2, 64, 32, nullptr) == BITMOE_EUNSUPPORTED);
+    bitmoe_layer nog = layer(256, 512, 8, 2, false);
+    nog.grid = nullptr;                                                        // 2-bit layers need the codebook
+    EXPECT(moe_ffn_decode(&nog, x, 1, 4, o32, of, of, ws, 1 << 20, nullptr) == BITMOE_EINVAL);
+    nog.format = 7;
+    EXPECT(moe_ffn_decode(&nog, x, 1, 4, o32, of, of, ws, 1 << 20, nullptr) == BITMOE_EINVAL);
     EXPECT(moe_set_timing_events(nullptr, nullptr, 5) == BITMOE_EINVAL);
     for (int c = 1; c >= -5; c--) EXPECT(std::strlen(moe_strerror(c)) > 0);
     EXPECT(std::strlen(moe_version()) > 0);

@@ -13,6 +13,8 @@ int launch_quant_q2k(const float *, int64_t, void *, hipStream_t) { return BITMO
 int launch_pack_iq2x(const void *, void *, int, int, int, hipStream_t) { return BITMOE_EHIP; }
 int launch_pack_q2k(const void *, void *, int, int, int, hipStream_t) { return BITMOE_EHIP; }
 int launch_pack_bf16(const void *, void *, int, int, hipStream_t) { return BITMOE_EHIP; }
+int launch_dequant_mxfp4(const void *, int64_t, void *, int, hipStream_t) { return BITMOE_EHIP; }
+int launch_pack_mxfp4(const void *, void *, int, int, int, hipStream_t) { return BITMOE_EHIP; }
 int launch_router_gemv(const bitmoe_layer *, const void *, int, int, float *, hipStream_t) { return BITMOE_EHIP; }
 int launch_router_mfma(const bitmoe_layer *, const void *, int, float *, int32_t *, float *, float *, hipStream_t) {
     return BITMOE_EHIP;
