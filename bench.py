@@ -50,6 +50,8 @@ def parse():
                     help="print per-kernel averages of every counter of rocprofv3 --pmc runs")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the 2048-token prefill step (--prefill-steps times; for counter runs)")
+    ap.add_argument("--fmt", choices=("2bit", "mxfp4"), default="2bit",
+                    help="routed-expert format of the --prefill-only run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the b16 and prefill lines")
     return ap.parse_args()
@@ -59,21 +61,37 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def expert_bytes(w):
+    """Bytes of one routed expert's gate+up and down blocks."""
+    if w.fmt == "mxfp4":
+        return 2 * w.I * (w.H // 32) * 17, w.H * (w.I // 32) * 17
+    return 2 * w.I * (w.H // 256) * 66, w.H * (w.I // 256) * 84
+
+
+def routed_view(bm, w, lay):
+    """The layer without its shared expert (the prefill workloads have none)."""
+    g = None if lay.fmt == bm.FORMAT_MXFP4 else lay.tensors[4]
+    return bm.Layer(w.H, w.I, w.E, w.k, *lay.tensors[:4], g, fmt=lay.fmt)
+
+
 def build_layer(w, copies):
     import torch
     import bit_moe_amd as bm
     import synth
     L = synth.make_layer(w)
+    mx = w.fmt == "mxfp4"
+    fmt = bm.FORMAT_MXFP4 if mx else bm.FORMAT_2BIT
     t0 = time.time()
     lay = bm.layer_from_canonical(w.H, w.I, w.E, w.k, L.router(), L.gate_all(), L.up_all(),
-                                  L.down_all(), L.grid(), L.shared())
+                                  L.down_all(), None if mx else L.grid(), L.shared(), fmt=fmt)
     torch.cuda.synchronize()
-    log(f"[bench] layer generated+packed in {time.time() - t0:.1f}s")
+    log(f"[bench] {w.fmt} layer generated+packed in {time.time() - t0:.1f}s")
     lays = [lay]
+    nq = 4 if mx else 5                 # router, gate, up, down (+ grid)
     for _ in range(copies - 1):
         t = [x.clone() for x in lay.tensors]
-        sh = tuple(t[5:8]) if lay.has_shared else None
-        lays.append(bm.Layer(w.H, w.I, w.E, w.k, t[0], t[1], t[2], t[3], t[4], sh))
+        sh = tuple(t[nq:nq + 3]) if lay.has_shared else None
+        lays.append(bm.Layer(w.H, w.I, w.E, w.k, t[0], t[1], t[2], t[3], None if mx else t[4], sh, fmt=fmt))
     torch.cuda.synchronize()
     return L, lays
 
@@ -131,11 +149,11 @@ def time_kernel(step, n, which):
     return sum(d) / n, {"median_ms": q(0.5), "p10_ms": q(0.1), "p90_ms": q(0.9), "n": n}
 
 
-def decode_b1(args, L, lays):
+def decode_b1(args, L, lays, fmt="2bit"):
     import torch
     import bit_moe_amd as bm
     import synth
-    w = synth.WORKLOADS["decode_b1"]
+    w = synth.WORKLOADS["decode_b1"].with_(fmt=fmt)
     R = 16
     xs_np, _ = synth.make_tokens(w.with_(T=R))
     xs = [torch.from_numpy(xs_np[i:i + 1].view("int16")).view(torch.bfloat16).cuda() for i in range(R)]
@@ -154,9 +172,10 @@ def decode_b1(args, L, lays):
     dn_ms, dn_stats = time_kernel(step, n, bm.TIME_DOWN)
     # the gate/up launch streams the routed gate/up blocks of the k experts;
     # the down launch the k experts' down blocks and the shared down
-    gu_bytes = w.k * (2 * w.I * (w.H // 256) * 66)
-    dn_bytes = w.k * (w.H * (w.I // 256) * 84) + w.I * w.H * 2
-    step_bytes = w.k * (2 * w.I * (w.H // 256) * 66 + w.H * (w.I // 256) * 84) + 3 * w.I * w.H * 2 + w.E * w.H * 2
+    eg, ed = expert_bytes(w)
+    gu_bytes = w.k * eg
+    dn_bytes = w.k * ed + w.I * w.H * 2
+    step_bytes = w.k * (eg + ed) + 3 * w.I * w.H * 2 + w.E * w.H * 2
     return dict(ms=ms, stats=stats, gu_ms=gu_ms, gu_stats=gu_stats, gu_bytes=gu_bytes, dn_ms=dn_ms,
                 dn_stats=dn_stats, dn_bytes=dn_bytes, step_bytes=step_bytes)
 
@@ -203,17 +222,15 @@ def issued_rows(counts, tile_rows=96):
     return tot
 
 
-def prefill_2k(args, lays):
+def prefill_2k(args, lays, fmt="2bit"):
     import numpy as np
     import torch
     import bit_moe_amd as bm
     import synth
-    w = synth.WORKLOADS["prefill_2k"]
+    w = synth.WORKLOADS["prefill_2k"].with_(fmt=fmt)
     x, _ = synth.make_tokens(w)
     xd = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
-    lay0 = lays[0]
-    # prefill has no shared expert: a layer view without it
-    lay = bm.Layer(w.H, w.I, w.E, w.k, *lay0.tensors[:5])
+    lay = routed_view(bm, w, lays[0])
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
     wt = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
     y = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
@@ -230,7 +247,9 @@ def prefill_2k(args, lays):
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=w.E)
     pairs = w.T * w.k
     rows_issued = issued_rows(counts)
-    return dict(ms=ms, stats=stats, flops=pairs * 3 * 2 * w.H * w.I,
+    eg, ed = expert_bytes(w)
+    active = int(np.count_nonzero(counts))
+    return dict(ms=ms, stats=stats, flops=pairs * 3 * 2 * w.H * w.I, gu_bytes=active * eg, dn_bytes=active * ed,
                 gu_ms=gu_ms, gu_stats=gu_stats, gu_flops=pairs * 2 * 2 * w.H * w.I,
                 gu_flops_issued=rows_issued * 2 * 2 * w.H * w.I,
                 dn_ms=dn_ms, dn_stats=dn_stats, dn_flops=pairs * 2 * w.H * w.I,
@@ -248,7 +267,7 @@ def prefill_8k_zipf(args, lays):
     x, _ = synth.make_tokens(w)
     xd = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
     lg = torch.from_numpy(synth.zipf_logits(w)).cuda()
-    lay = bm.Layer(w.H, w.I, w.E, w.k, *lays[0].tensors[:5])
+    lay = routed_view(bm, w, lays[0])
     ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
     wt = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
     y = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
@@ -501,7 +520,10 @@ def summarize_kernels(trace_dir):
     (packing) until the first decode launch, decode_b1 until the batch-16 step's
     first top-k, decode_b16 until the prefill step's router GEMM (the decode
     batch also runs prefill kernels, for its multi-token experts), prefill_2k
-    until the 8192-token step's top-k, then prefill_8k."""
+    until the 8192-token step's top-k, prefill_8k until the expert cache's
+    first decode launch, expert_cache until the quantizer, quantize until the
+    MXFP4 layer's packing, then mxfp4_decode_b1 from its first decode launch
+    and mxfp4_prefill_2k from its router GEMM."""
     import glob
     import sqlite3
     rows = {}
@@ -517,17 +539,29 @@ def summarize_kernels(trace_dir):
                 phase = "prefill_2k"
             elif phase == "prefill_2k" and "k_topk" in name and "k_topk_sum" not in name:
                 phase = "prefill_8k"
+            elif phase == "prefill_8k" and "k_dec_front" in name:
+                phase = "expert_cache"
+            elif phase == "expert_cache" and "k_quant" in name:
+                phase = "quantize"
+            elif phase == "quantize" and "k_pack_mxfp4" in name:
+                phase = "mxfp4_setup"
+            elif phase == "mxfp4_setup" and "k_dec_front" in name:
+                phase = "mxfp4_decode_b1"
+            elif phase == "mxfp4_decode_b1" and "k_router_splitk" in name:
+                phase = "mxfp4_prefill_2k"
             r = rows.setdefault((phase, name, gx), [0, 0.0, float("inf"), 0.0])
             d = (t1 - t0) / 1e3
             r[0] += 1
             r[1] += d
             r[2] = min(r[2], d)
             r[3] = max(r[3], d)
-    out = [f"{'phase':<11} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'grid':>10}  kernel"]
-    order = {"setup": 0, "decode_b1": 1, "decode_b16": 2, "prefill_2k": 3, "prefill_8k": 4}
+    out = [f"{'phase':<16} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'grid':>10}  kernel"]
+    order = {p: i for i, p in enumerate(("setup", "decode_b1", "decode_b16", "prefill_2k", "prefill_8k",
+                                         "expert_cache", "quantize", "mxfp4_setup", "mxfp4_decode_b1",
+                                         "mxfp4_prefill_2k"))}
     for (phase, name, gx), (n, tot, mn, mx) in sorted(rows.items(), key=lambda kv: (order[kv[0][0]], -kv[1][1])):
         short = name[name.index("k_"):].split("(")[0] if "k_" in name else name.split("(")[0]
-        out.append(f"{phase:<11} {n:6d} {tot / n:10.2f} {mn:10.2f} {mx:10.2f} {gx:10d}  {short}")
+        out.append(f"{phase:<16} {n:6d} {tot / n:10.2f} {mn:10.2f} {mx:10.2f} {gx:10d}  {short}")
     return "\n".join(out)
 
 
@@ -559,7 +593,7 @@ def summarize_mfma(pmc_dir):
     return "\n".join(lines)
 
 
-def summarize_counters(dirs, only=("k_pf_", "k_dec_", "k_combine", "k_shared")):
+def summarize_counters(dirs, only=("k_pf_", "k_mx_", "k_dec_", "k_combine", "k_shared")):
     """Per-kernel average per dispatch of every counter collected in one or
     more rocprofv3 --pmc output directories (one pass each), one row per
     kernel with the counters as columns, plus the kernels' average
@@ -610,6 +644,58 @@ def traffic_from_profile(kernel):
     return None
 
 
+def mxfp4_bench(args):
+    """The MXFP4 routed-expert variant at the decode batch-1 and 2048-token
+    prefill shapes (same router, shared expert and routing as the 2-bit
+    lines)."""
+    import torch
+    import synth
+    w = synth.WORKLOADS["decode_b1"].with_(fmt="mxfp4")
+    L, lays = build_layer(w, args.copies)
+    r = decode_b1(args, L, lays, fmt="mxfp4")
+    usd = lambda st: {k.replace("_ms", "_us"): (v * 1e3 if k.endswith("_ms") else v) for k, v in st.items()}
+    gu_bw = r["gu_bytes"] / (r["gu_ms"] * 1e-3)
+    dn_bw = r["dn_bytes"] / (r["dn_ms"] * 1e-3)
+    log(f"[bench] mxfp4 decode_b1 {r['ms'] * 1e3:.1f} us/step, gate/up {r['gu_ms'] * 1e3:.1f} us "
+        f"({gu_bw / 1e9:.0f} GB/s), down {r['dn_ms'] * 1e3:.1f} us")
+    res = {"workload": "MXFP4 routed experts (OCP Microscaling: E2M1 elements, E8M0 scale per 32 weights) at "
+                       "H7168, I2048, 256 experts top-8; decode: moe_forward_decode of one bf16 token with the bf16 "
+                       "shared expert; prefill: route + moe_ffn_prefill of 2048 bf16 tokens",
+           "decode_b1": {"tokens_per_s": 1.0 / (r["ms"] * 1e-3), "us_per_step": r["ms"] * 1e3,
+                         "step_us": usd(r["stats"]), "step_hbm_bytes": r["step_bytes"],
+                         "step_hbm_GBps": r["step_bytes"] / (r["ms"] * 1e-3) / 1e9,
+                         "roofline": {"bound": "hbm", "kernel": "k_dec_gateup (MXFP4)", "unit": "GB/s",
+                                      "achieved": gu_bw / 1e9, "peak": HBM_PEAK / 1e9, "frac": gu_bw / HBM_PEAK,
+                                      "kernel_us": r["gu_ms"] * 1e3, "algorithmic_bytes": r["gu_bytes"],
+                                      "traffic": None,
+                                      "down_kernel": {"kernel": "k_dec_down (MXFP4)", "achieved": dn_bw / 1e9,
+                                                      "frac": dn_bw / HBM_PEAK, "kernel_us": r["dn_ms"] * 1e3,
+                                                      "algorithmic_bytes": r["dn_bytes"]}}}}
+    del lays[1:]
+    torch.cuda.empty_cache()
+    pf = prefill_2k(args, lays, fmt="mxfp4")
+    tfs = lambda f, ms: f / (ms * 1e-3) / 1e12
+    res["prefill_2k"] = {
+        "tokens_per_s": 2048 / (pf["ms"] * 1e-3), "ms_per_step": pf["ms"], "step_ms": pf["stats"],
+        "routed_TFLOPs": tfs(pf["flops"], pf["ms"]), "mfma_frac": pf["flops"] / (pf["ms"] * 1e-3) / BF16_PEAK,
+        "roofline": [
+            {"bound": "mfma", "kernel": kname, "unit": "TFLOP/s", "peak": BF16_PEAK / 1e12,
+             "achieved": tfs(pf[f + "_flops"], pf[f + "_ms"]),
+             "frac": tfs(pf[f + "_flops"], pf[f + "_ms"]) * 1e12 / BF16_PEAK,
+             "issued_frac": tfs(pf[f + "_flops_issued"], pf[f + "_ms"]) * 1e12 / BF16_PEAK,
+             "kernel_us": pf[f + "_ms"] * 1e3, "algorithmic_flops": pf[f + "_flops"], "traffic": None,
+             # at about 64 rows per expert the MXFP4 weights (17/32 B per weight) make this kernel's
+             # intensity 2 x 64 / (17/32) = 241 FLOP/B, below the 312 FLOP/B ridge: HBM binds first
+             "weight_bytes": pf[f + "_bytes"], "hbm_GBps": pf[f + "_bytes"] / (pf[f + "_ms"] * 1e-3) / 1e9,
+             "hbm_frac": pf[f + "_bytes"] / (pf[f + "_ms"] * 1e-3) / HBM_PEAK}
+            for kname, f in (("k_mx_gateup", "gu"), ("k_mx_down", "dn"))]}
+    log(f"[bench] mxfp4 prefill_2k {pf['ms']:.2f} ms/step, gate/up {pf['gu_ms'] * 1e3:.0f} us, "
+        f"down {pf['dn_ms'] * 1e3:.0f} us")
+    del lays
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_kernels:
@@ -637,9 +723,9 @@ def main():
         copy_calibration()
         return
     if args.prefill_only:
-        _, lays = build_layer(synth.WORKLOADS["decode_b1"], 1)
-        pf = prefill_2k(args, lays)
-        log(f"[bench] prefill_2k {pf['ms']:.2f} ms/step, gate/up {pf['gu_ms'] * 1e3:.1f} us, "
+        _, lays = build_layer(synth.WORKLOADS["decode_b1"].with_(fmt=args.fmt), 1)
+        pf = prefill_2k(args, lays, fmt=args.fmt)
+        log(f"[bench] {args.fmt} prefill_2k {pf['ms']:.2f} ms/step, gate/up {pf['gu_ms'] * 1e3:.1f} us, "
             f"down {pf['dn_ms'] * 1e3:.1f} us")
         return
     w = synth.WORKLOADS["decode_b1"]
@@ -672,12 +758,12 @@ def main():
                    "step_us": usd(r["stats"])},
         "roofline": {"bound": "hbm", "kernel": "k_dec_gateup",
                      "achieved": gu_bw / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": gu_bw / HBM_PEAK, "traffic": traffic_from_profile("k_dec_gateup<1,0>"),
+                     "frac": gu_bw / HBM_PEAK, "traffic": traffic_from_profile("k_dec_gateup<0,1,0>"),
                      "kernel_us": r["gu_ms"] * 1e3, "kernel_us_dist": usd(r["gu_stats"]),
                      "algorithmic_bytes": r["gu_bytes"],
                      "down_kernel": {"kernel": "k_dec_down", "achieved": dn_bw / 1e9, "frac": dn_bw / HBM_PEAK,
                                      "kernel_us": r["dn_ms"] * 1e3, "algorithmic_bytes": r["dn_bytes"],
-                                     "traffic": traffic_from_profile("k_dec_down<0>")}},
+                                     "traffic": traffic_from_profile("k_dec_down<0,0>")}},
     }
     if not args.no_extra:
         b16 = decode_b16(args, lays)
@@ -746,6 +832,10 @@ def main():
                                  "frac": q_bytes / HBM_PEAK, "bytes_per_superblock": 256 * 4 + 84,
                                  "traffic": None}}}
         log(f"[bench] quantize iq2x {qb['ms_iq2x']:.2f} ms, q2k {qb['ms_q2k']:.3f} ms per tensor")
+    if not args.no_extra:
+        del lays, L
+        torch.cuda.empty_cache()
+        out["mxfp4"] = mxfp4_bench(args)
     if not args.no_cpu_baseline:
         if not args.no_extra:
             for fmt, cb in quantize_cpu_baseline(qb["w"], qb["grid"], args.cpu_seconds / 2).items():
