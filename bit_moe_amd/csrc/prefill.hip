@@ -33,10 +33,13 @@
 //  gate/up: 8 waves x 32 h columns (gate and up blocks of the same columns
 //           in one lane), epilogue h = silu(g) u stored as fp16 with one
 //           power-of-two exponent per (row, 256 columns).
-//  down:    8 waves x 64 output columns, A = h rows rescaled per 256-column
+//  down:    16 waves x 32 output columns, A = h rows rescaled per 256-column
 //           chunk to the row's largest exponent while staged into LDS;
-//           epilogue writes o[pair][n] (fp32); k_combine_p applies the
-//           routing weights.
+//           epilogue writes o[pair][n] as fp16 with one power-of-two
+//           exponent per (pair, 512 columns) (fp32 for decode batches);
+//           k_combine_p applies the routing weights.
+// MXFP4 routed experts (k_mx_*) keep this tiling and pipeline on the bf16
+// matrix cores, with operands from the hardware E2M1 conversion (below).
 #include <hip/hip_ext.h>
 
 #include <type_traits>
