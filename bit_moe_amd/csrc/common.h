@@ -227,42 +227,20 @@ BM_DEV void lut_build(const uint8_t *__restrict__ grid, uint8_t *lut) {
 }
 
 // ---- tiled Q2K quant words -------------------------------------------------
-// A tiled Q2K sub-block (16 weights) is one little-endian word: the 2-bit
-// quants of the even-indexed weights 0,2,..,14 at bits 0-15 (weight 2p at
-// bits 2p), those of the odd-indexed ones at bits 16-31 (weight 2p+1 at
-// bits 16+2p).  Piece c (16 bytes) of a block holds sub-blocks 4c..4c+3.
-BM_DEV uint32_t q2k_word_quant(uint32_t W, int i) { return (W >> (16 * (i & 1) + (i & ~1))) & 3u; }
-// Weights 2p, 2p+1 of word W as the fp16 pair (B_p + q_2p, B_p + q_2p+1),
-// B_p = 2^(10 - 2s), s = p for p < 5, else p - 5 (taken from W >> 10): the
-// quants sit in the mantissa where one unit is 1, so only a mask and an OR
-// are needed.  W10 = W >> 10.
-template <int PAIR>
-BM_DEV uint32_t q2k_pair_f16(uint32_t W, uint32_t W10) {
-    constexpr int s = PAIR < 5 ? PAIR : PAIR - 5;
-    constexpr uint32_t base = (uint32_t)(25 - 2 * s) << 10;     // fp16 bits of 2^(10 - 2s)
-    return ((PAIR < 5 ? W : W10) & (0x00030003u << (2 * s))) | base | (base << 16);
-}
-// The 5 masks and 5 bases of q2k_pair_f16 held in registers, so that each
-// pair is one v_and_or_b32 (a three-operand op takes no two literals).
-struct Q2kPairConsts {
-    uint32_t mask[5], base[5];
-    BM_DEV Q2kPairConsts() {
-#pragma unroll
-        for (int s = 0; s < 5; s++) {
-            uint32_t m = 0x00030003u << (2 * s), b = ((uint32_t)(25 - 2 * s) << 10) * 0x10001u;
-            asm volatile("" : "+v"(m));
-            asm volatile("" : "+s"(b));
-            mask[s] = m;
-            base[s] = b;
-        }
-    }
-    template <int PAIR>
-    BM_DEV uint32_t pair(uint32_t W, uint32_t W10) const {
-        constexpr int s = PAIR < 5 ? PAIR : PAIR - 5;
-        return ((PAIR < 5 ? W : W10) & mask[s]) | base[s];
-    }
-};
-constexpr float q2k_pair_bias(int pair) { return (float)(1 << (10 - 2 * (pair < 5 ? pair : pair - 5))); }
+// A tiled Q2K sub-block (16 weights) is one little-endian word whose byte s
+// (0..3) holds the 2-bit quants of weights 2s and 2s+1 in bits 0-1 and 4-5,
+// and those of weights 8+2s and 9+2s in bits 2-3 and 6-7.  Masking the word
+// (q2k_lo: weights 0..7, q2k_hi: weights 8..15) leaves in each byte two
+// nibbles that are E2M1 codes 0..3, whose values are q/2; the hardware
+// conversion at scale 2 then gives each consecutive pair as exact fp16 quants.
+// Piece c (16 bytes) of a block holds sub-blocks 4c..4c+3.
+BM_DEV int q2k_word_shift(int i) { return 8 * ((i & 7) >> 1) + 4 * (i & 1) + 2 * (i >> 3); }
+BM_DEV uint32_t q2k_word_quant(uint32_t W, int i) { return (W >> q2k_word_shift(i)) & 3u; }
+BM_DEV uint32_t q2k_lo(uint32_t W) { return W & 0x33333333u; }
+BM_DEV uint32_t q2k_hi(uint32_t W) { return (W >> 2) & 0x33333333u; }
+// (q_{2S}, q_{2S+1}) of a masked word as an fp16 pair (E2M1 scale 2^1)
+template <int S>
+BM_DEV uint32_t q2k_pair_f16(uint32_t spread) { return fp4x2_f16s<S>(spread, 2.f); }
 
 // ---- small-T router row: one wave per expert row, lanes across K ---------
 // The row is read in chunks (up to 8 loads of 16 bytes per lane, all in

@@ -457,12 +457,9 @@ BM_DEV void gateup_epilogue(int I, const Tok &tk, int t0, int P, const float (&a
         const _Float16 hf = (_Float16)(hv * inv);
         h[row * I + n] = __builtin_bit_cast(uint16_t, hf);
         if (SUMS) {
-            // per 16 columns: sum of h and sum of B_p h, B_p the bias of the
-            // pair that column n % 16 falls in (the Q2K down's terms)
-            const float v = (float)hf;
-            const int pp = (n & 15) >> 1;
-            const float hs = row16_sum(v), hb = row16_sum(q2k_pair_bias(pp) * v);
-            if ((lane & 15) == 15) hsum2[row * (I / 16) + (n >> 4)] = make_float2(hs, hb);
+            // per 16 columns: the sum of h (the Q2K down's min term)
+            const float hs = row16_sum((float)hf);
+            if ((lane & 15) == 15) hsum2[row * (I / 16) + (n >> 4)] = make_float2(hs, 0.f);
         }
         if (lane == 0) hscale[row * (I / 64) + P] = scl;
     }
@@ -1066,8 +1063,9 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
 // ---------------------------------------------------------------------------
 // Routed Q2K down of panel P for the pair rows of tokens t0..t0+NT-1 of
 // expert tk.  h arrives as fp16 scaled per 64 columns (hscale), with per-16
-// sums hs and bias-weighted sums hb (hsum2 = {hs, hb}); each sub-block is 8
-// fp16 dot products of (B_p + q) pairs, then sc*(S - hb) and m*hs.
+// sums hs (hsum2 = {hs, 0}); each sub-block is 8 fp16 dot products of exact
+// quant pairs (the hardware E2M1 conversion of the masked word), then
+// d sc S - dmin m hs.
 template <int NT>
 BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
                              const uint8_t *__restrict__ down, const int32_t *__restrict__ perm,
@@ -1087,7 +1085,6 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
     const uint4 *dq = reinterpret_cast<const uint4 *>(D);
     const uint4 *ds = reinterpret_cast<const uint4 *>(D + S * 64);
     const uint32_t *dd = reinterpret_cast<const uint32_t *>(D + S * 80);
-    const Q2kPairConsts qc;
     int kb0, kb1;
     split_range(nb, kWD, wv, kb0, kb1);
     // superblocks two at a time, both loaded before either is decoded (the
@@ -1138,10 +1135,10 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
             for (int t = 0; t < NT; t++) a1[t] = a2[t] = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const uint32_t W = qw[i], W10 = W >> 10;
-                const uint32_t pr[8] = {qc.pair<0>(W, W10), qc.pair<1>(W, W10), qc.pair<2>(W, W10),
-                                        qc.pair<3>(W, W10), qc.pair<4>(W, W10), qc.pair<5>(W, W10),
-                                        qc.pair<6>(W, W10), qc.pair<7>(W, W10)};
+                const uint32_t lo = q2k_lo(qw[i]), hi = q2k_hi(qw[i]);
+                const uint32_t pr[8] = {q2k_pair_f16<0>(lo), q2k_pair_f16<1>(lo), q2k_pair_f16<2>(lo),
+                                        q2k_pair_f16<3>(lo), q2k_pair_f16<0>(hi), q2k_pair_f16<1>(hi),
+                                        q2k_pair_f16<2>(hi), q2k_pair_f16<3>(hi)};
                 const float scf = (float)((scl >> (8 * i)) & 0xFFu), mf = (float)((mnb >> (8 * i)) & 0xFFu);
 #pragma unroll
                 for (int t = 0; t < NT; t++) {
@@ -1155,8 +1152,8 @@ BM_DEV void routed_down_pass(int H, int I, const Tok &tk, int t0, int P,
                     sacc = dot2_f16(pr[5], x1.y, sacc);
                     sacc = dot2_f16(pr[6], x1.z, sacc);
                     sacc = dot2_f16(pr[7], x1.w, sacc);
-                    const float2 sb = reinterpret_cast<const float2 *>(hst + t * kHst + 64)[s * 16 + 4 * c + i];   // {hs, hb}
-                    a1[t] = fmaf(scf, sacc - sb.y, a1[t]);
+                    const float2 sb = reinterpret_cast<const float2 *>(hst + t * kHst + 64)[s * 16 + 4 * c + i];   // {hs, 0}
+                    a1[t] = fmaf(scf, sacc, a1[t]);
                     a2[t] = fmaf(mf, sb.x, a2[t]);
                 }
             }

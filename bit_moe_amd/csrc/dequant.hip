@@ -159,7 +159,8 @@ k_pack_q2k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int E, in
     uint8_t *slab = dst + e * per_e * 84;
     int64_t pk = (int64_t)P * nb + kb;
     // sub-block b = 8h + 2j + lh holds weights l = 16 lh .. 16 lh + 15 of
-    // plane j of half h: q = (qs[32h + l] >> 2j) & 3
+    // plane j of half h: q = (qs[32h + l] >> 2j) & 3; weight t of the
+    // sub-block goes to bits 8 ((t & 7) >> 1) + 4 (t & 1) + 2 (t >> 3)
     uint32_t W[16];
 #pragma unroll
     for (int b = 0; b < 16; b++) {
@@ -168,7 +169,7 @@ k_pack_q2k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int E, in
 #pragma unroll
         for (int t = 0; t < 16; t++) {
             const uint32_t q = (qs[32 * h + 16 * lh + t] >> (2 * j)) & 3u;
-            w |= q << (16 * (t & 1) + (t & ~1));
+            w |= q << q2k_word_shift(t);
         }
         W[b] = w;
     }

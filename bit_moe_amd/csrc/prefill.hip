@@ -605,49 +605,36 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
         sl.sc = *reinterpret_cast<const uint32_t *>(D + soff + kb * 1024 + 8 * hf);
         sl.dd = *reinterpret_cast<const uint32_t *>(D + doff + kb * 256);
     };
-    const Q2kPairConsts pc;
-    uint32_t nbias[5];
-#pragma unroll
-    for (int q = 0; q < 5; q++) {
-        uint32_t v = f16_pair(-(float)(1 << (10 - 2 * q)));
-        asm volatile("" : "+s"(v));
-        nbias[q] = v;
-    }
     f32x16 acc[MB];
 #pragma unroll
     for (int i = 0; i < MB; i++) acc[i] = (f32x16)0.f;
     auto compute = [&](const uint8_t *A, const Slot &sl) {
-        const float ds = kPfDnWScale * fp16_to_f32(sl.dd & 0xFFFFu);
-        const float ms = -kPfDnWScale * fp16_to_f32(sl.dd >> 16);
+        // (a, -b) of each sub-block from one packed fma: (16 + sc, 16 + m) times
+        // (d', -dmin') minus 16 (d', -dmin'), d' = 2^7 d and dmin' = 2^7 dmin
+        // (exact scalings), i.e. one fp16 rounding each of d' sc and -dmin' m
+        const f16x2 dm = u2h(sl.dd) * f16x2{kPfDnWScale, -kPfDnWScale};
+        const f16x2 c16 = dm * f16x2{-16.f, -16.f};
+        const uint32_t slo = sl.sc & 0x0F0F0F0Fu, shi = (sl.sc >> 4) & 0x0F0F0F0Fu;
         const uint32_t wsel[4] = {sl.w.x, sl.w.y, sl.w.z, sl.w.w};
 #pragma unroll
         for (int sbk = 0; sbk < 4; sbk++) {                 // sub-block 4kh + sbk: k-steps 2 sbk, 2 sbk + 1
-            const uint32_t W = wsel[sbk], W10 = W >> 10;
-            // (a, -b) of this sub-block: a = d sc, b = dmin m
-            const uint32_t sb = (sl.sc >> (8 * sbk)) & 0xFFu;
-            const f16x2 av = u2h(f16_pair(ds * (float)(sb & 15u)));
-            const f16x2 bv = u2h(f16_pair(ms * (float)(sb >> 4)));
+            // sc and m of byte sbk into the two halves, as the fp16 mantissas of 16 + sc, 16 + m
+            const uint32_t scm = __builtin_amdgcn_perm(shi, slo, 0x0C040C00u + 0x00010001u * sbk);
+            const f16x2 ab = __builtin_elementwise_fma(u2h((scm << 6) | 0x4C004C00u), dm, c16);
+            const f16x2 av = ab.xx, bv = ab.yy;
+            const uint32_t qlo = q2k_lo(wsel[sbk]), qhi = q2k_hi(wsel[sbk]);
 #pragma unroll
             for (int half = 0; half < 2; half++) {
                 f16x8 af[MB];
 #pragma unroll
                 for (int i = 0; i < MB; i++) af[i] = frag32<R>(A, i, lane, 2 * sbk + half);
-                uint32_t qb[4];
-                if (half == 0) {
-                    qb[0] = pc.pair<0>(W, W10); qb[1] = pc.pair<1>(W, W10);
-                    qb[2] = pc.pair<2>(W, W10); qb[3] = pc.pair<3>(W, W10);
-                } else {
-                    qb[0] = pc.pair<4>(W, W10); qb[1] = pc.pair<5>(W, W10);
-                    qb[2] = pc.pair<6>(W, W10); qb[3] = pc.pair<7>(W, W10);
-                }
+                const uint32_t src = half ? qhi : qlo;
+                const uint32_t qb[4] = {q2k_pair_f16<0>(src), q2k_pair_f16<1>(src), q2k_pair_f16<2>(src),
+                                        q2k_pair_f16<3>(src)};                  // exact quant pairs
                 uint4 v;
                 uint32_t *vv = reinterpret_cast<uint32_t *>(&v);
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const int pp = 4 * half + q, sh = pp < 5 ? pp : pp - 5;
-                    const f16x2 qv = u2h(qb[q]) + u2h(nbias[sh]);          // exact quant
-                    vv[q] = h2u(__builtin_elementwise_fma(qv, av, bv));    // a q - b
-                }
+                for (int q = 0; q < 4; q++) vv[q] = h2u(__builtin_elementwise_fma(u2h(qb[q]), av, bv));   // a q - b
                 const f16x8 b = __builtin_bit_cast(f16x8, v);
 #pragma unroll
                 for (int i = 0; i < MB; i++) acc[i] = mfma32(af[i], b, acc[i]);

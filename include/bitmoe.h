@@ -91,8 +91,10 @@
  *     [0, 64*N*nb):           piece c at ((P*nb + kb)*4 + c)*64 + r, 16 bytes:
  *                             the quants of sub-blocks 4c..4c+3 (weights
  *                             64c..64c+63), one little-endian word each: the
- *                             quant of weight 2p of the sub-block at bits 2p,
- *                             that of weight 2p+1 at bits 16+2p
+ *                             quant of weight t (0..15) of the sub-block at
+ *                             bits 8*((t & 7) >> 1) + 4*(t & 1) + 2*(t >> 3)
+ *                             (byte s: weights 2s, 2s+1 in bits 0-1, 4-5 and
+ *                             weights 8+2s, 9+2s in bits 2-3, 6-7)
  *     [64*N*nb, 80*N*nb):     scales (bytes 0-15) at (P*nb + kb)*64 + r, 16 B
  *     [80*N*nb, 84*N*nb):     d, dmin (bytes 80-83) at (P*nb + kb)*64 + r, 4 B
  *   MXFP4 slab (N*(K/32)*17 bytes), nb = K/256 again:

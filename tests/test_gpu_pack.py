@@ -38,7 +38,8 @@ def _tiled_q2k_numpy(canon, N, K):
     q = (qs[..., 32 * (i // 128) + i % 32] >> (2 * ((i % 128) // 32))) & 3  # [P][kb][r][256]
     q = q.reshape(q.shape[:-1] + (16, 16))                                # sub-block, weight t
     t = np.arange(16)
-    words = (q << (16 * (t & 1) + (t & ~1))).sum(axis=-1).astype(np.uint32)   # [P][kb][r][16]
+    # weight t of a sub-block at bits 8 ((t & 7) >> 1) + 4 (t & 1) + 2 (t >> 3)
+    words = (q << (8 * ((t & 7) >> 1) + 4 * (t & 1) + 2 * (t >> 3))).sum(axis=-1).astype(np.uint32)
     pieces = words.reshape(N // 64, nb, 64, 4, 4).transpose(0, 1, 3, 2, 4)    # [P][kb][c][r][4]
     qs_t = np.ascontiguousarray(pieces.astype("<u4")).view(np.uint8)
     return np.concatenate([qs_t.reshape(-1), b[..., 0:16].reshape(-1), b[..., 80:84].reshape(-1)])
