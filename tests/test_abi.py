@@ -40,11 +40,11 @@ def test_strerror_names_every_code():
 def _layer(H=256, I=512, E=8, k=2, shared=False, **kw):
     d = dict(H=H, I=I, E=E, k=k, router_w=16, gate_q=16, up_q=16, down_q=16, grid=16,
              shared_gate=16 if shared else None, shared_up=16 if shared else None,
-             shared_down=16 if shared else None, layout=_lib.LAYOUT_TILED)
+             shared_down=16 if shared else None, layout=_lib.LAYOUT_TILED, fmt=_lib.FORMAT_2BIT)
     d.update(kw)
     return _lib.LayerStruct(d["H"], d["I"], d["E"], d["k"], d["router_w"], d["gate_q"], d["up_q"],
                             d["down_q"], d["grid"], d["shared_gate"], d["shared_up"], d["shared_down"],
-                            d["layout"])
+                            d["layout"], d["fmt"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -210,3 +210,36 @@ def test_quantize_argument_checks():
     assert L.moe_quantize_q2k(16, 4, None, None) == _lib.EINVAL
     assert L.moe_quantize_q2k(16, -2, 16, None) == _lib.EINVAL
     assert L.moe_quantize_q2k(16, 0, None, None) == 0
+
+
+def test_format_tag_and_mxfp4_entry_points():
+    """The layer's format tag: an unknown tag is invalid; a 2-bit layer needs
+    the codebook, an MXFP4 layer does not (a T = 0 call passes every check
+    and queues nothing).  MXFP4 dequant / pack argument checks, and the cache
+    pool of an MXFP4 layer (17 bytes per 32 weights per slab)."""
+    L = bm.lib()
+    x = y = ids = w = 16
+    for f in (L.moe_ffn_decode, L.moe_ffn_prefill):
+        bad = _layer(fmt=7)
+        assert f(C.byref(bad), x, 1, 4, ids, w, y, 256, 1 << 20, None) == _lib.EINVAL
+        assert L.moe_workspace_bytes(C.byref(bad), 4, 0) == 0
+        nog = _layer(grid=None)
+        assert f(C.byref(nog), x, 1, 4, ids, w, y, 256, 1 << 20, None) == _lib.EINVAL
+        mx = _layer(grid=None, fmt=_lib.FORMAT_MXFP4)
+        assert f(C.byref(mx), x, 1, 0, ids, w, y, None, 0, None) == 0
+        assert L.moe_workspace_bytes(C.byref(mx), 4, 0) > 0
+        assert f(C.byref(mx), x, 1, 4, ids, w, y, None, 0, None) == _lib.EWORKSPACE
+    assert L.moe_dequant_mxfp4(16, -1, 16, 0, None) == _lib.EINVAL
+    assert L.moe_dequant_mxfp4(16, 4, 16, 2, None) == _lib.EINVAL
+    assert L.moe_dequant_mxfp4(16, 4, 8, 0, None) == _lib.EINVAL            # out not 16-byte aligned
+    assert L.moe_dequant_mxfp4(None, 4, 16, 0, None) == _lib.EINVAL
+    assert L.moe_dequant_mxfp4(None, 0, None, 0, None) == 0
+    assert L.moe_pack_mxfp4(16, 16, 2, 64, 32, None) == _lib.EUNSUPPORTED   # K not a multiple of 256
+    assert L.moe_pack_mxfp4(16, 16, 2, 100, 256, None) == _lib.EUNSUPPORTED
+    assert L.moe_pack_mxfp4(16, 8, 2, 64, 256, None) == _lib.EINVAL          # dst not 16-byte aligned
+    assert L.moe_pack_mxfp4(None, None, 0, 64, 256, None) == 0
+    mx = _layer(H=7168, I=2048, E=256, k=8, grid=None, fmt=_lib.FORMAT_MXFP4)
+    slab = 2 * 2048 * 7168 // 32 * 17 + 7168 * 2048 // 32 * 17
+    assert L.moe_cache_pool_bytes(C.byref(mx), 24) == 3 * 256 + 24 * slab
+    two = _layer(H=7168, I=2048, E=256, k=8)
+    assert L.moe_cache_pool_bytes(C.byref(two), 24) == 3 * 256 + 24 * (2 * 2048 * 28 * 66 + 7168 * 8 * 84)

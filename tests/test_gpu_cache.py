@@ -75,3 +75,21 @@ def test_full_shape_cache_steps_match_resident(name, slots, steps):
         say(f"[cache] {name} step {i}: {loaded} experts copied")
         np.testing.assert_array_equal(yc, yr)
     assert misses > 0 and hits + misses == sum(len(np.unique(o[2])) for o in out)
+
+
+def test_mxfp4_layer_cache_steps_match_resident():
+    """The cache over an MXFP4 layer (slabs of 17 bytes per 32 weights): every
+    step equals the resident layer bit for bit, the copies follow the LRU
+    model, and one step matches the oracle."""
+    require_gpu()
+    w = synth.WORKLOADS["tiny"].with_(name="tiny_cache_mx", T=3, shared=True, x_dtype="bf16", seed=73,
+                                      fmt="mxfp4")
+    out, hits, misses = _run(w, 6, 10, "computed")
+    model = _lru_model([list(o[2].ravel()) for o in out], w.E, 6)
+    for i, (yc, yr, ids, x, wt, loaded) in enumerate(out):
+        np.testing.assert_array_equal(yc, yr)
+        assert loaded == model[i][1], (i, loaded, model[i])
+    assert (hits, misses) == model[-1][3:]
+    yc, _, ids, x, wt, _ = out[-1]
+    ref = oracle.layer_ffn(synth_layer(w), x, ids, wt.astype(np.float64))
+    assert_close_rms(yc, ref, what="mxfp4 cache step vs oracle")
