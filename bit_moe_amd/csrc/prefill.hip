@@ -256,6 +256,79 @@ BM_DEV f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) { return __builtin_amdgcn_mfma_
 // row of accumulator register r of a 32x32 block in lane half kh
 BM_DEV int acc_row(int r, int kh) { return 8 * (r >> 2) + 4 * kh + (r & 3); }
 
+// ---- the stage pipeline of every grouped-GEMM tile ----------------------------
+// Stage st (128 K) runs its MFMAs from LDS activation buffer st & 1.  At its
+// start it loads the activation pieces of stage st + AHEAD into registers
+// (load_a) and the weight slot of stage st + 2 (load_slot); after its MFMAs
+// (compute) it writes the activations of stage st + 1 into the other buffer
+// (put_a), then a barrier.  AHEAD = 2 keeps two register sets, alternating by
+// stage, so that each activation load has two stages' compute to arrive.
+// The issue order is pinned (activations, then the slot), so that the wait
+// before put_a leaves the slot in flight (memory counters retire in issue
+// order).  Slots and register sets rotate by call, never by copy (a copy
+// would wait for the loads), and the stages whose prefetches are all in
+// range carry no conditionals (a conditional load path there breaks the
+// issue order and the compiler then drains every load).
+template <int AHEAD, class Regs, class Slot, class LoadA, class PutA, class LoadSlot, class Compute>
+BM_DEV void run_stages(int nsteps, LoadA &&load_a, PutA &&put_a, LoadSlot &&load_slot, Compute &&compute) {
+    static_assert(AHEAD == 1 || AHEAD == 2, "activation prefetch depth");
+    Regs ra, rb;
+    Slot q0, q1, q2;
+    auto stage = [&](auto full, int st, Slot &cur, Slot &pre, Regs &ld, Regs &sv) {
+        const int s1 = st + 1, s2 = st + 2, sa = st + AHEAD;
+        asm volatile("" ::: "memory");
+        if (full || sa < nsteps) load_a(sa, ld);
+        asm volatile("" ::: "memory");
+        if (full || s2 < nsteps) load_slot(s2, pre);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        compute(st & 1, cur);
+        if (full || s1 < nsteps) put_a(s1 & 1, sv);
+        __syncthreads();
+    };
+    using Full = std::integral_constant<bool, true>;
+    using Part = std::integral_constant<bool, false>;
+    load_a(0, ra);
+    if (AHEAD == 2) load_a(1, rb);
+    load_slot(0, q0);
+    load_slot(1, q1);                    // nsteps >= 2: K is a multiple of 256
+    put_a(0, ra);
+    // drain the prologue loads: otherwise the compiler merges their pending
+    // state into the loop header and waits on the current slot every pass
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int st = 0;
+    if constexpr (AHEAD == 1) {
+        for (; st + 5 <= nsteps; st += 3) {
+            stage(Full{}, st, q0, q2, ra, ra);
+            stage(Full{}, st + 1, q1, q0, ra, ra);
+            stage(Full{}, st + 2, q2, q1, ra, ra);
+        }
+        // at most 4 stages remain; the slot rotation continues from q0
+        if (st < nsteps) stage(Part{}, st, q0, q2, ra, ra);
+        if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0, ra, ra);
+        if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1, ra, ra);
+        if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2, ra, ra);
+    } else {
+        for (; st + 8 <= nsteps; st += 6) {
+            stage(Full{}, st, q0, q2, ra, rb);
+            stage(Full{}, st + 1, q1, q0, rb, ra);
+            stage(Full{}, st + 2, q2, q1, ra, rb);
+            stage(Full{}, st + 3, q0, q2, rb, ra);
+            stage(Full{}, st + 4, q1, q0, ra, rb);
+            stage(Full{}, st + 5, q2, q1, rb, ra);
+        }
+        // at most 7 stages remain
+        if (st < nsteps) stage(Part{}, st, q0, q2, ra, rb);
+        if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0, rb, ra);
+        if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1, ra, rb);
+        if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2, rb, ra);
+        if (st + 4 < nsteps) stage(Part{}, st + 4, q1, q0, ra, rb);
+        if (st + 5 < nsteps) stage(Part{}, st + 5, q2, q1, rb, ra);
+        if (st + 6 < nsteps) stage(Part{}, st + 6, q0, q2, ra, rb);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // gate/up.  512 threads; wave w owns h columns hc0 + 32w .. +31: block 0 the
 // gate rows, block 1 the up rows of those columns (lane & 31 = column).  In a
@@ -331,52 +404,11 @@ BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
             }
         }
     };
-    // Pipeline over half-stages st = 2 kb + hf: the slot (words + scales) of
-    // stage st+2 is loaded at the start of stage st, the activations of st+1
-    // too (issued first, so the wait before their LDS store leaves the slot
-    // loads in flight: memory counters retire in issue order).  The three
-    // slots rotate by call, never by copy (a copy would wait for the loads).
-    const int nsteps = 2 * nb;
-    u32x4 ar[R / 32];
-    // FULL: stages whose prefetches (st+1, st+2) are both in range, so the
-    // main loop carries no conditionals (a conditional load path there breaks
-    // the issue order and the compiler then drains every load).
-    auto stage = [&](auto full, int st, Slot &cur, Slot &pre) {
-        const int s1 = st + 1, s2 = st + 2;
-        // issue order pinned (compiler memory barriers): activations, then the
-        // slot, so the wait before the activation store leaves the slot in flight
-        asm volatile("" ::: "memory");
-        if (full || s1 < nsteps) gu_stage_load<R>(a, stok, s1 >> 1, s1 & 1, ar);
-        asm volatile("" ::: "memory");
-        if (full || s2 < nsteps) load_slot(s2, pre);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        compute(sa + (st & 1) * kPfABytes, cur);
-        if (full || s1 < nsteps) stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
-        __syncthreads();
-    };
-    using Full = std::integral_constant<bool, true>;
-    using Part = std::integral_constant<bool, false>;
-    Slot q0, q1, q2;
-    gu_stage_load<R>(a, stok, 0, 0, ar);
-    load_slot(0, q0);
-    if (nsteps > 1) load_slot(1, q1);
-    stage_store<R>(sa, ar);
-    // drain the prologue loads: otherwise the compiler merges their pending
-    // state into the loop header and waits on the current slot every pass
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int st = 0;
-    for (; st + 5 <= nsteps; st += 3) {
-        stage(Full{}, st, q0, q2);
-        stage(Full{}, st + 1, q1, q0);
-        stage(Full{}, st + 2, q2, q1);
-    }
-    // at most 4 stages remain; the slot rotation continues from q0
-    if (st < nsteps) stage(Part{}, st, q0, q2);
-    if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0);
-    if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1);
-    if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2);
+    struct ARegs { u32x4 r[R / 32]; };
+    run_stages<2, ARegs, Slot>(
+        2 * nb, [&](int st, ARegs &v) { gu_stage_load<R>(a, stok, st >> 1, st & 1, v.r); },
+        [&](int buf, ARegs &v) { stage_store<R>(sa + buf * kPfABytes, v.r); }, load_slot,
+        [&](int buf, const Slot &sl) { compute(sa + buf * kPfABytes, sl); });
     // epilogue: lane holds rows 32i + acc_row(r, kh), column hc.  h in
     // registers; row maxima over the workgroup's 256 columns (32 lanes of a
     // half-wave, then the 8 waves through LDS) give each row's power of two.
@@ -641,43 +673,13 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
             }
         }
     };
-    const int nsteps = 2 * nb;
-    u32x4 ar[DP];
-    int aex[DP];
-    // as in gu_tile: the slot of stage st+2 and the activations of st+1 are
-    // loaded at the start of stage st (activations first), three slots
-    // rotating by call
-    auto stage = [&](auto full, int st, Slot &cur, Slot &pre) {
-        const int s1 = st + 1, s2 = st + 2;
-        asm volatile("" ::: "memory");
-        if (full || s1 < nsteps) dn_stage_load<R>(a, t, s1 >> 1, s1 & 1, ar, aex);
-        asm volatile("" ::: "memory");
-        if (full || s2 < nsteps) load_slot(s2, pre);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        if (active) compute(sa + (st & 1) * kPfABytes, cur);
-        if (full || s1 < nsteps) dn_stage_put<R>(sa + (s1 & 1) * kPfABytes, semax, aex, ar);
-        __syncthreads();
-    };
-    using Full = std::integral_constant<bool, true>;
-    using Part = std::integral_constant<bool, false>;
-    Slot q0, q1, q2;
-    dn_stage_load<R>(a, t, 0, 0, ar, aex);
-    load_slot(0, q0);
-    if (nsteps > 1) load_slot(1, q1);
-    dn_stage_put<R>(sa, semax, aex, ar);
-    __builtin_amdgcn_s_waitcnt(0);       // see gu_tile
-    __syncthreads();
-    int st = 0;
-    for (; st + 5 <= nsteps; st += 3) {
-        stage(Full{}, st, q0, q2);
-        stage(Full{}, st + 1, q1, q0);
-        stage(Full{}, st + 2, q2, q1);
-    }
-    if (st < nsteps) stage(Part{}, st, q0, q2);
-    if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0);
-    if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1);
-    if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2);
+    struct ARegs { u32x4 r[DP]; int e[DP]; };
+    run_stages<1, ARegs, Slot>(
+        2 * nb, [&](int st, ARegs &v) { dn_stage_load<R>(a, t, st >> 1, st & 1, v.r, v.e); },
+        [&](int buf, ARegs &v) { dn_stage_put<R>(sa + buf * kPfABytes, semax, v.e, v.r); }, load_slot,
+        [&](int buf, const Slot &sl) {
+            if (active) compute(sa + buf * kPfABytes, sl);
+        });
     dn_epilogue<MB, OUT32>(a, lds, t, ntile, acc, c0, active, kPfDnWShift);
 }
 
@@ -802,41 +804,11 @@ BM_DEV void mx_gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile
             }
         }
     };
-    // pipeline as in gu_tile: at the start of stage st the activations of
-    // st+1 and then the slot of st+2 are loaded; three slots rotate by call
-    const int nsteps = 2 * nb;
-    u32x4 ar[R / 32];
-    auto stage = [&](auto full, int st, Slot &cur, Slot &pre) {
-        const int s1 = st + 1, s2 = st + 2;
-        asm volatile("" ::: "memory");
-        if (full || s1 < nsteps) gu_stage_load<R>(a, stok, s1 >> 1, s1 & 1, ar);
-        asm volatile("" ::: "memory");
-        if (full || s2 < nsteps) load_slot(s2, pre);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        compute(sa + (st & 1) * kPfABytes, cur);
-        if (full || s1 < nsteps) stage_store<R>(sa + (s1 & 1) * kPfABytes, ar);
-        __syncthreads();
-    };
-    using Full = std::integral_constant<bool, true>;
-    using Part = std::integral_constant<bool, false>;
-    Slot q0, q1, q2;
-    gu_stage_load<R>(a, stok, 0, 0, ar);
-    load_slot(0, q0);
-    if (nsteps > 1) load_slot(1, q1);
-    stage_store<R>(sa, ar);
-    __builtin_amdgcn_s_waitcnt(0);       // see gu_tile
-    __syncthreads();
-    int st = 0;
-    for (; st + 5 <= nsteps; st += 3) {
-        stage(Full{}, st, q0, q2);
-        stage(Full{}, st + 1, q1, q0);
-        stage(Full{}, st + 2, q2, q1);
-    }
-    if (st < nsteps) stage(Part{}, st, q0, q2);
-    if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0);
-    if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1);
-    if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2);
+    struct ARegs { u32x4 r[R / 32]; };
+    run_stages<2, ARegs, Slot>(
+        2 * nb, [&](int st, ARegs &v) { gu_stage_load<R>(a, stok, st >> 1, st & 1, v.r); },
+        [&](int buf, ARegs &v) { stage_store<R>(sa + buf * kPfABytes, v.r); }, load_slot,
+        [&](int buf, const Slot &sl) { compute(sa + buf * kPfABytes, sl); });
 #pragma unroll
     for (int i = 0; i < MB; i++)
 #pragma unroll
@@ -922,39 +894,13 @@ BM_DEV void mx_dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile
             for (int i = 0; i < MB; i++) acc[i] = mfma32b(af[i], b, acc[i]);
         }
     };
-    const int nsteps = 2 * nb;
-    u32x4 ar[DP];
-    auto stage = [&](auto full, int st, Slot &cur, Slot &pre) {
-        const int s1 = st + 1, s2 = st + 2;
-        asm volatile("" ::: "memory");
-        if (full || s1 < nsteps) mx_dn_stage_load<R>(a, t, s1 >> 1, s1 & 1, ar);
-        asm volatile("" ::: "memory");
-        if (full || s2 < nsteps) load_slot(s2, pre);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        if (active) compute(sa + (st & 1) * kPfABytes, cur);
-        if (full || s1 < nsteps) mx_dn_stage_put<R>(sa + (s1 & 1) * kPfABytes, ar);
-        __syncthreads();
-    };
-    using Full = std::integral_constant<bool, true>;
-    using Part = std::integral_constant<bool, false>;
-    Slot q0, q1, q2;
-    mx_dn_stage_load<R>(a, t, 0, 0, ar);
-    load_slot(0, q0);
-    if (nsteps > 1) load_slot(1, q1);
-    mx_dn_stage_put<R>(sa, ar);
-    __builtin_amdgcn_s_waitcnt(0);       // see gu_tile
-    __syncthreads();
-    int st = 0;
-    for (; st + 5 <= nsteps; st += 3) {
-        stage(Full{}, st, q0, q2);
-        stage(Full{}, st + 1, q1, q0);
-        stage(Full{}, st + 2, q2, q1);
-    }
-    if (st < nsteps) stage(Part{}, st, q0, q2);
-    if (st + 1 < nsteps) stage(Part{}, st + 1, q1, q0);
-    if (st + 2 < nsteps) stage(Part{}, st + 2, q2, q1);
-    if (st + 3 < nsteps) stage(Part{}, st + 3, q0, q2);
+    struct ARegs { u32x4 r[DP]; };
+    run_stages<1, ARegs, Slot>(
+        2 * nb, [&](int st, ARegs &v) { mx_dn_stage_load<R>(a, t, st >> 1, st & 1, v.r); },
+        [&](int buf, ARegs &v) { mx_dn_stage_put<R>(sa + buf * kPfABytes, v.r); }, load_slot,
+        [&](int buf, const Slot &sl) {
+            if (active) compute(sa + buf * kPfABytes, sl);
+        });
     dn_epilogue<MB, OUT32>(a, lds, t, ntile, acc, c0, active, 0);
 }
 
