@@ -46,6 +46,7 @@ def lib():
         L.oracle_dequant_mxfp4.argtypes = [P, I64, P]
         L.oracle_quantize_iq2x.argtypes = [P, P, I64, P]
         L.oracle_quantize_q2k.argtypes = [P, I64, P]
+        L.oracle_quantize_mxfp4.argtypes = [P, I64, P]
         L.oracle_max_threads.restype = I32
         L.oracle_set_threads.argtypes = [I32]
         _lib = L
@@ -93,6 +94,16 @@ def quantize_iq2x(w: np.ndarray, grid: np.ndarray) -> np.ndarray:
     g = np.ascontiguousarray(grid, dtype=np.uint8).reshape(256, 8)
     out = np.empty((wf.size // 256, 66), dtype=np.uint8)
     lib().oracle_quantize_iq2x(_p(wf), _p(g), out.shape[0], _p(out))
+    return out
+
+
+def quantize_mxfp4(w: np.ndarray) -> np.ndarray:
+    """float32 weights [n * 32] -> canonical MXFP4 blocks uint8 [n, 17]
+    (OCP shared exponent with the two-way scale search of quant.c)."""
+    wf = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+    assert wf.size % 32 == 0
+    out = np.empty((wf.size // 32, 17), dtype=np.uint8)
+    lib().oracle_quantize_mxfp4(_p(wf), out.shape[0], _p(out))
     return out
 
 

@@ -1,6 +1,6 @@
 /*
- * CPU oracle of the quantizer round trip: fp32 weights -> canonical IQ2X and
- * Q2K blocks by an error-minimising search.
+ * CPU oracle of the quantizer round trip: fp32 weights -> canonical IQ2X,
+ * Q2K and MXFP4 blocks by an error-minimising search.
  *
  * TEST INFRASTRUCTURE ONLY, like oracle.c: only the tests, the smoke check
  * and the CPU-baseline leg of the benchmark use it.  It shares no code with
@@ -50,6 +50,18 @@
  *                  q_j = A > 0 ? clamp(rint((w_j + M) / A), 0, 3) : 0,
  *                  E = sum_j (w_j - (A q_j - M))^2 (j in order);
  *                  the least E wins, ties to the earlier candidate.
+ *
+ * MXFP4 block (32 weights, OCP Microscaling conversion with a two-way scale
+ * search):
+ *   amax = max |w|; amax = 0 stores zero bytes (scale byte 0, codes 0).
+ *   e0 = floor(log2 amax) - 2 (2 = the largest E2M1 exponent, as the OCP
+ *   conversion sets the shared exponent); for e = e0, e0 + 1 (each clamped to
+ *   -127..127): t_j = |w_j| / 2^e, the E2M1 magnitude nearest t_j among 0,
+ *   0.5, 1, 1.5, 2, 3, 4, 6 (t_j > 6 saturates to 6; a tie goes to the one
+ *   with an even mantissa bit: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2,
+ *   2.5 -> 2, 3.5 -> 4, 5 -> 4), E = sum_j (w_j - sign(w_j) m_j 2^e)^2 (j in
+ *   order); the least E wins, ties to e0.  Code = magnitude code, plus 8 for a
+ *   negative weight with a nonzero magnitude; byte 0 = e + 127.
  */
 #include <math.h>
 #include <stdint.h>
@@ -232,6 +244,71 @@ static void q2k_encode_block(const float *w, uint8_t *blk)
             blk[16 + 32 * h + l] |= (uint8_t)(bq[j] << (2 * sh));
         }
     }
+}
+
+/* E2M1 magnitude code nearest t >= 0 (ties to the even mantissa bit) */
+static int e2m1_code(double t)
+{
+    if (t <= 0.25) return 0;
+    if (t < 0.75) return 1;
+    if (t <= 1.25) return 2;
+    if (t < 1.75) return 3;
+    if (t <= 2.5) return 4;
+    if (t < 3.5) return 5;
+    if (t <= 5.0) return 6;
+    return 7;
+}
+
+static const double e2m1_mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+static void mxfp4_encode_block(const float *w, uint8_t *blk)
+{
+    memset(blk, 0, 17);
+    double amax = 0.0;
+    for (int j = 0; j < 32; j++) {
+        double a = fabs((double)w[j]);
+        if (a > amax)
+            amax = a;
+    }
+    if (amax == 0.0)
+        return;
+    int fe;
+    frexp(amax, &fe);                              /* amax = f 2^fe, f in [0.5, 1) */
+    int e0 = fe - 1 - 2;
+    int best_e = 0, found = 0;
+    double best_err = 0.0;
+    for (int e = e0; e <= e0 + 1; e++) {
+        int ec = e < -127 ? -127 : e > 127 ? 127 : e;
+        double s = ldexp(1.0, ec), err = 0.0;
+        for (int j = 0; j < 32; j++) {
+            double m = e2m1_mag[e2m1_code(fabs((double)w[j]) / s)] * s;
+            double diff = fabs((double)w[j]) - m;
+            err = err + diff * diff;
+        }
+        if (!found || err < best_err) {
+            found = 1;
+            best_err = err;
+            best_e = ec;
+        }
+    }
+    double s = ldexp(1.0, best_e);
+    blk[0] = (uint8_t)(best_e + 127);
+    for (int j = 0; j < 32; j++) {
+        int c = e2m1_code(fabs((double)w[j]) / s);
+        if (c && w[j] < 0.0f)
+            c |= 8;
+        if (j < 16)
+            blk[1 + j] |= (uint8_t)c;
+        else
+            blk[1 + j - 16] |= (uint8_t)(c << 4);
+    }
+}
+
+void oracle_quantize_mxfp4(const float *w, int64_t nblocks, uint8_t *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblocks; b++)
+        mxfp4_encode_block(w + 32 * b, out + 17 * b);
 }
 
 /* nblocks superblocks of 256 fp32 weights -> canonical blocks (66 or 84

@@ -161,3 +161,63 @@ def test_error_on_gaussian_weights_is_that_of_two_bits():
     ei = np.sqrt(np.mean((oracle.dequant_iq2x(oracle.quantize_iq2x(w, GRID), GRID) - w) ** 2))
     eq = np.sqrt(np.mean((oracle.dequant_q2k(oracle.quantize_q2k(w)) - w) ** 2))
     assert 0.25 < ei < 0.45 and 0.2 < eq < 0.35, (ei, eq)
+
+
+# ---- MXFP4 (OCP Microscaling conversion with a two-way scale search) --------
+
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+
+
+def test_mxfp4_exact_round_trip_of_representable_blocks():
+    """Random codes at a random scale with one element at +-6: the shared
+    exponent floor(log2 6 s) - 2 is the block's own, so every value comes back."""
+    rng = np.random.default_rng(21)
+    n = 64
+    blk = rng.integers(0, 256, size=(n, 17), dtype=np.uint8)
+    blk[:, 0] = rng.integers(20, 235, n)
+    blk[:, 1] = (blk[:, 1] & 0xF0) | rng.choice([7, 15], n)          # element 0: +-6
+    w = oracle.dequant_mxfp4(blk)
+    assert np.all(w.astype(np.float32).astype(np.float64) == w)
+    re = oracle.quantize_mxfp4(w.astype(np.float32))
+    np.testing.assert_array_equal(oracle.dequant_mxfp4(re), w)       # (-0 and +0 compare equal)
+    np.testing.assert_array_equal(re[:, 0], blk[:, 0])
+
+
+def test_mxfp4_blocks_are_optimal_over_the_two_scales():
+    """For each block: the scale byte is e0 + 127 or e0 + 128 (e0 = floor(log2
+    max|w|) - 2), and the squared error equals the brute-force minimum over
+    those two scales and all 16 codes of every element."""
+    rng = np.random.default_rng(22)
+    w = (rng.standard_normal(32 * 200) * np.exp2(rng.integers(-20, 20, 32 * 200))).astype(np.float32)
+    blk = oracle.quantize_mxfp4(w)
+    got = oracle.dequant_mxfp4(blk).reshape(-1, 32)
+    wb = w.astype(np.float64).reshape(-1, 32)
+    for b in range(blk.shape[0]):
+        e0 = int(np.floor(np.log2(np.abs(wb[b]).max()))) - 2
+        assert int(blk[b, 0]) - 127 in (e0, e0 + 1)
+        best = min(((wb[b][:, None] - E2M1[None, :] * 2.0 ** e) ** 2).min(axis=1).sum() for e in (e0, e0 + 1))
+        mine = ((got[b] - wb[b]) ** 2).sum()
+        assert mine == pytest.approx(best, rel=1e-12, abs=1e-300), b
+
+
+def test_mxfp4_element_ties_round_to_even_mantissa():
+    """Midpoints between E2M1 values at scale 1 (kept by the exactly
+    representable 6, 0.5 and 1.5 elsewhere in the block): 0.25 -> 0,
+    0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4, and their
+    negatives."""
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    want = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+    w = np.array([6.0] + ties + [-t for t in ties] + [0.5, 1.5] * 8 + [0.5], dtype=np.float32)[:32]
+    blk = oracle.quantize_mxfp4(w)
+    assert blk[0, 0] == 127
+    got = oracle.dequant_mxfp4(blk)
+    np.testing.assert_array_equal(got[1:8], want)
+    np.testing.assert_array_equal(got[8:15], [-v for v in want])
+
+
+def test_mxfp4_zero_blocks_and_gaussian_error():
+    assert not oracle.quantize_mxfp4(np.zeros(64, np.float32)).any()
+    rng = np.random.default_rng(23)
+    w = rng.standard_normal(32 * 512).astype(np.float32)
+    e = np.sqrt(np.mean((oracle.dequant_mxfp4(oracle.quantize_mxfp4(w)) - w) ** 2))
+    assert 0.08 < e < 0.15, e
