@@ -377,10 +377,12 @@ def quantize_bench(args):
     grid = torch.from_numpy(synth.make_layer(synth.WORKLOADS["decode_b1"]).grid()).cuda()
     oi = torch.empty((n, 66), dtype=torch.uint8, device="cuda")
     oq = torch.empty((n, 84), dtype=torch.uint8, device="cuda")
+    om = torch.empty((n * 8, 17), dtype=torch.uint8, device="cuda")
     ms_i, st_i = time_steps(lambda i: bm.quantize_iq2x(w, grid, out=oi), 1, 5)
     ms_q, st_q = time_steps(lambda i: bm.quantize_q2k(w, out=oq), 2, 20)
-    return dict(n=n, ms_iq2x=ms_i, ms_q2k=ms_q, st_iq2x=st_i, st_q2k=st_q, w=w.cpu().numpy(),
-                grid=grid.cpu().numpy())
+    ms_m, st_m = time_steps(lambda i: bm.quantize_mxfp4(w, out=om), 2, 20)
+    return dict(n=n, ms_iq2x=ms_i, ms_q2k=ms_q, ms_mxfp4=ms_m, st_iq2x=st_i, st_q2k=st_q, st_mxfp4=st_m,
+                w=w.cpu().numpy(), grid=grid.cpu().numpy())
 
 
 def quantize_cpu_baseline(w, grid, target_s):
@@ -389,15 +391,17 @@ def quantize_cpu_baseline(w, grid, target_s):
     import numpy as np
     import oracle
     out = {}
-    for fmt, first in (("iq2x", 64), ("q2k", 4096)):
+    for fmt, first in (("iq2x", 64), ("q2k", 4096), ("mxfp4", 4096)):
         nb, spent = first, 0.0
         while True:
             x = np.ascontiguousarray(w[:nb * 256])
             t0 = time.perf_counter()
             if fmt == "iq2x":
                 oracle.quantize_iq2x(x, grid)
-            else:
+            elif fmt == "q2k":
                 oracle.quantize_q2k(x)
+            else:
+                oracle.quantize_mxfp4(x)
             spent = time.perf_counter() - t0
             if spent >= target_s / 4 or nb * 256 * 2 > w.size:
                 break
@@ -819,6 +823,7 @@ def main():
         qb = quantize_bench(args)
         iq_ops = qb["n"] * IQ2X_OPS_PER_SB / (qb["ms_iq2x"] * 1e-3)
         q_bytes = qb["n"] * (256 * 4 + 84) / (qb["ms_q2k"] * 1e-3)
+        m_bytes = qb["n"] * 8 * (32 * 4 + 17) / (qb["ms_mxfp4"] * 1e-3)
         out["quantize"] = {
             "workload": "one 2048 x 7168 expert tensor of fp32 weights (57344 superblocks) per format",
             "iq2x": {"weights_per_s": qb["n"] * 256 / (qb["ms_iq2x"] * 1e-3), "ms": qb["ms_iq2x"],
@@ -830,8 +835,14 @@ def main():
                     "ms_dist": qb["st_q2k"],
                     "roofline": {"bound": "hbm", "unit": "GB/s", "achieved": q_bytes / 1e9, "peak": HBM_PEAK / 1e9,
                                  "frac": q_bytes / HBM_PEAK, "bytes_per_superblock": 256 * 4 + 84,
-                                 "traffic": None}}}
-        log(f"[bench] quantize iq2x {qb['ms_iq2x']:.2f} ms, q2k {qb['ms_q2k']:.3f} ms per tensor")
+                                 "traffic": None}},
+            "mxfp4": {"weights_per_s": qb["n"] * 256 / (qb["ms_mxfp4"] * 1e-3), "ms": qb["ms_mxfp4"],
+                      "ms_dist": qb["st_mxfp4"],
+                      "roofline": {"bound": "hbm", "unit": "GB/s", "achieved": m_bytes / 1e9,
+                                   "peak": HBM_PEAK / 1e9, "frac": m_bytes / HBM_PEAK,
+                                   "bytes_per_block": 32 * 4 + 17, "traffic": None}}}
+        log(f"[bench] quantize iq2x {qb['ms_iq2x']:.2f} ms, q2k {qb['ms_q2k']:.3f} ms, "
+            f"mxfp4 {qb['ms_mxfp4']:.3f} ms per tensor")
     if not args.no_extra:
         del lays, L
         torch.cuda.empty_cache()

@@ -28,6 +28,7 @@ SYMBOLS = [
     "moe_bucket", "moe_workspace_bytes", "moe_ffn_decode", "moe_forward_decode", "moe_forward_decode_noalloc",
     "moe_ffn_prefill",
     "moe_dequant_iq2x", "moe_dequant_q2k", "moe_dequant_mxfp4", "moe_quantize_iq2x", "moe_quantize_q2k",
+    "moe_quantize_mxfp4",
     "moe_pack_iq2x", "moe_pack_q2k", "moe_pack_bf16", "moe_pack_mxfp4",
     "moe_set_timing_events", "moe_strerror", "moe_version",
     "moe_cache_pool_bytes", "moe_cache_create", "moe_cache_layer", "moe_cache_map", "moe_cache_stats",
@@ -78,6 +79,7 @@ def lib() -> C.CDLL:
         "moe_dequant_mxfp4": ([P, I64, P, I, P], I),
         "moe_quantize_iq2x": ([P, P, I64, P, P], I),
         "moe_quantize_q2k": ([P, I64, P, P], I),
+        "moe_quantize_mxfp4": ([P, I64, P, P], I),
         "moe_pack_iq2x": ([P, P, I, I, I, P], I),
         "moe_pack_q2k": ([P, P, I, I, I, P], I),
         "moe_pack_bf16": ([P, P, I, I, P], I),
@@ -419,6 +421,18 @@ def quantize_q2k(w, out=None, stream=None):
         out = torch.empty((nb, 84), dtype=torch.uint8, device=w.device)
     _dev_check(w, out)
     _check(lib().moe_quantize_q2k(_ptr(w), nb, _ptr(out), _stream(stream)), "moe_quantize_q2k")
+    return out
+
+
+def quantize_mxfp4(w, out=None, stream=None):
+    """float32 weights (numel a multiple of 32) -> canonical MXFP4 blocks
+    uint8 [n, 17] (moe_quantize_mxfp4)."""
+    torch = _torch()
+    nb = w.numel() // 32
+    if out is None:
+        out = torch.empty((nb, 17), dtype=torch.uint8, device=w.device)
+    _dev_check(w, out)
+    _check(lib().moe_quantize_mxfp4(_ptr(w), nb, _ptr(out), _stream(stream)), "moe_quantize_mxfp4")
     return out
 
 

@@ -336,6 +336,13 @@ int moe_quantize_q2k(const float *w, int64_t nblocks, void *blocks, void *stream
     return bm_host::launch_quant_q2k(w, nblocks, blocks, as_stream(stream));
 }
 
+int moe_quantize_mxfp4(const float *w, int64_t nblocks, void *blocks, void *stream) {
+    if (nblocks < 0) return BITMOE_EINVAL;
+    if (nblocks == 0) return BITMOE_OK;
+    if (!w || !blocks || !aligned(w, 16)) return BITMOE_EINVAL;
+    return bm_host::launch_quant_mxfp4(w, nblocks, blocks, as_stream(stream));
+}
+
 int moe_pack_iq2x(const void *src, void *dst, int E, int N, int K, void *stream) {
     if (E < 0 || N < 0 || K < 0) return BITMOE_EINVAL;
     if (N % 64 || K % 256) return BITMOE_EUNSUPPORTED;

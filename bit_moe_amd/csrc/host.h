@@ -46,6 +46,7 @@ int launch_pack_mxfp4(const void *src, void *dst, int E, int N, int K, hipStream
 
 int launch_quant_iq2x(const float *w, const void *grid, int64_t nblocks, void *out, hipStream_t s);
 int launch_quant_q2k(const float *w, int64_t nblocks, void *out, hipStream_t s);
+int launch_quant_mxfp4(const float *w, int64_t nblocks, void *out, hipStream_t s);
 
 // router logits [T][E] fp32 for at most bm_cfg::kRouterNT tokens
 int launch_router_gemv(const bitmoe_layer *L, const void *x, int x_dtype, int T,

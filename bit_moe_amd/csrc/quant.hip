@@ -1,4 +1,4 @@
-// Quantizer: fp32 weights -> canonical IQ2X and Q2K blocks by an
+// Quantizer: fp32 weights -> canonical IQ2X, Q2K and MXFP4 blocks by an
 // error-minimising search over each format's own choices.
 //
 // The pages say the routed experts are quantised asymmetrically to 2 bits,
@@ -258,9 +258,80 @@ k_quant_q2k(const float *__restrict__ w, int64_t nblocks, uint8_t *__restrict__ 
     }
 }
 
+// MXFP4: one thread per 32-weight block.  The OCP Microscaling conversion's
+// shared exponent e0 = floor(log2 max|w|) - 2 and the next one up are both
+// tried (each clamped to -127..127); elements go to the nearest E2M1
+// magnitude (ties to the even mantissa bit, saturating at 6), and the scale
+// with the smaller squared error is kept (ties to e0).  All-zero blocks are
+// zero bytes.
+BM_DEV int e2m1_code(double t) {
+    return t <= 0.25 ? 0 : t < 0.75 ? 1 : t <= 1.25 ? 2 : t < 1.75 ? 3 : t <= 2.5 ? 4 : t < 3.5 ? 5 : t <= 5.0 ? 6 : 7;
+}
+BM_DEV double e2m1_mag(int c) {
+    return c == 0 ? 0.0 : c == 1 ? 0.5 : c == 2 ? 1.0 : c == 3 ? 1.5 : c == 4 ? 2.0 : c == 5 ? 3.0 : c == 6 ? 4.0 : 6.0;
+}
+
+__global__ void __launch_bounds__(256)
+k_quant_mxfp4(const float *__restrict__ w, int64_t nblocks, uint8_t *__restrict__ out) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblocks) return;
+    float x[32];
+    const float4 *p = reinterpret_cast<const float4 *>(w + 32 * b);
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        const float4 v = p[q];
+        x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+    double amax = 0.0;
+#pragma unroll
+    for (int j = 0; j < 32; j++) amax = fmax(amax, fabs((double)x[j]));
+    uint8_t *ob = out + 17 * b;
+    if (amax == 0.0) {
+#pragma unroll
+        for (int j = 0; j < 17; j++) ob[j] = 0;
+        return;
+    }
+    const int e0 = ilogb(amax) - 2;
+    int best_e = 0;
+    double best = 0.0;
+    for (int e = e0; e <= e0 + 1; e++) {
+        const int ec = min(max(e, -127), 127);
+        const double s = ldexp(1.0, ec);
+        double err = 0.0;
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            const double a = fabs((double)x[j]);
+            const double diff = a - e2m1_mag(e2m1_code(a / s)) * s;
+            err = err + diff * diff;
+        }
+        if (e == e0 || err < best) {
+            best = err;
+            best_e = ec;
+        }
+    }
+    const double s = ldexp(1.0, best_e);
+    uint32_t q[4] = {0u, 0u, 0u, 0u};                   // qs bytes 0..15: weight j low, j + 16 high
+#pragma unroll
+    for (int j = 0; j < 32; j++) {
+        int c = e2m1_code(fabs((double)x[j]) / s);
+        if (c && x[j] < 0.f) c |= 8;
+        const int byte = j & 15;
+        q[byte >> 2] |= (uint32_t)c << (8 * (byte & 3) + (j < 16 ? 0 : 4));
+    }
+    ob[0] = (uint8_t)(best_e + 127);
+#pragma unroll
+    for (int j = 0; j < 16; j++) ob[1 + j] = (uint8_t)(q[j >> 2] >> (8 * (j & 3)));
+}
+
 }  // namespace
 
 namespace bm_host {
+
+int launch_quant_mxfp4(const float *w, int64_t nblocks, void *out, hipStream_t s) {
+    k_quant_mxfp4<<<(unsigned)((nblocks + 255) / 256), 256, 0, s>>>(w, nblocks, (uint8_t *)out);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
+}
 
 int launch_quant_iq2x(const float *w, const void *grid, int64_t nblocks, void *out, hipStream_t s) {
     const int64_t grid_n = (nblocks + 3) / 4;

@@ -391,6 +391,20 @@ int moe_cache_destroy(void *cache);
  */
 int moe_quantize_iq2x(const float *w, const void *grid, int64_t nblocks, void *blocks, void *stream);
 int moe_quantize_q2k(const float *w, int64_t nblocks, void *blocks, void *stream);
+/*
+ * The same for MXFP4 (OCP Microscaling conversion; the pages' MXFP4 variant,
+ * "ds4 : analyse pratique ...", section "Support de modeles et choix de
+ * quantification"): nblocks blocks of 32 consecutive weights -> canonical
+ * 17-byte blocks.  The shared exponent e0 = floor(log2 max|w|) - 2 of the
+ * OCP conversion and e0 + 1 are both tried (clamped to -127..127); each
+ * weight goes to the nearest E2M1 magnitude (ties to the even mantissa bit,
+ * saturating at 6), and the exponent with the smaller squared error is kept
+ * (ties to e0); a negative weight with a nonzero magnitude takes the sign
+ * bit.  All-zero blocks are zero bytes.  Decisions in double precision as
+ * above; inputs must be finite.  w: float32 [nblocks * 32], 16-byte
+ * aligned; blocks: uint8 [nblocks][17].  Errors: EINVAL, EHIP.
+ */
+int moe_quantize_mxfp4(const float *w, int64_t nblocks, void *blocks, void *stream);
 
 /*
  * Load-time layout transforms (canonical -> TILED, see above), E experts of

@@ -10,6 +10,7 @@ int launch_dequant_iq2x(const void *, const void *, int64_t, void *, int, hipStr
 int launch_dequant_q2k(const void *, int64_t, void *, int, hipStream_t) { return BITMOE_EHIP; }
 int launch_quant_iq2x(const float *, const void *, int64_t, void *, hipStream_t) { return BITMOE_EHIP; }
 int launch_quant_q2k(const float *, int64_t, void *, hipStream_t) { return BITMOE_EHIP; }
+int launch_quant_mxfp4(const float *, int64_t, void *, hipStream_t) { return BITMOE_EHIP; }
 int launch_pack_iq2x(const void *, void *, int, int, int, hipStream_t) { return BITMOE_EHIP; }
 int launch_pack_q2k(const void *, void *, int, int, int, hipStream_t) { return BITMOE_EHIP; }
 int launch_pack_bf16(const void *, void *, int, int, hipStream_t) { return BITMOE_EHIP; }

@@ -243,3 +243,11 @@ def test_format_tag_and_mxfp4_entry_points():
     assert L.moe_cache_pool_bytes(C.byref(mx), 24) == 3 * 256 + 24 * slab
     two = _layer(H=7168, I=2048, E=256, k=8)
     assert L.moe_cache_pool_bytes(C.byref(two), 24) == 3 * 256 + 24 * (2 * 2048 * 28 * 66 + 7168 * 8 * 84)
+
+
+def test_quantize_mxfp4_argument_checks():
+    L = bm.lib()
+    assert L.moe_quantize_mxfp4(16, -1, 16, None) == _lib.EINVAL
+    assert L.moe_quantize_mxfp4(None, 0, None, None) == 0
+    assert L.moe_quantize_mxfp4(None, 4, 16, None) == _lib.EINVAL
+    assert L.moe_quantize_mxfp4(8, 4, 16, None) == _lib.EINVAL                # w not 16-byte aligned

@@ -97,3 +97,31 @@ def test_full_size_expert_tensor_sampled(fmt):
     o = _oracle(fmt, w.reshape(n, 256)[rows].reshape(-1))
     say(f"[quant] {fmt} full tensor: {len(rows)} sampled superblocks")
     np.testing.assert_array_equal(g[rows], o)
+
+
+def test_mxfp4_quantizer_matches_oracle():
+    """moe_quantize_mxfp4 against the oracle's encoder, byte for byte:
+    Gaussian weights over many binades, fp32 subnormals and values near the
+    top of fp32's range, ties at every E2M1 midpoint, zero, negative zero and
+    constant blocks, and a full 2048 x 7168 expert tensor in one launch."""
+    require_gpu()
+    import bit_moe_amd as bm
+    rng = np.random.default_rng(31)
+    w = (rng.standard_normal(32 * 4096) * np.exp2(rng.integers(-60, 60, 32 * 4096))).astype(np.float32)
+    b = w.reshape(-1, 32)
+    b[0] = 0.0
+    b[1] = -0.0
+    b[2] = 0.37
+    b[3] = -1e-40                                               # fp32 subnormals
+    b[4] = rng.standard_normal(32).astype(np.float32) * np.float32(1e-42)
+    b[5] = rng.standard_normal(32).astype(np.float32) * np.float32(1e37)
+    b[6, :8] = [6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]     # ties at scale 1
+    b[6, 8:] = 0.5
+    full = (rng.standard_normal(2048 * 7168) * 0.02).astype(np.float32)
+    for what, x in (("edge blocks over many binades", w), ("one 2048 x 7168 tensor", full)):
+        g = bm.quantize_mxfp4(torch.from_numpy(x).cuda())
+        torch.cuda.synchronize()
+        g = g.cpu().numpy()
+        o = oracle.quantize_mxfp4(x)
+        say(f"[quant] mxfp4 {what}: {g.shape[0]} blocks, {int((g != o).any(axis=1).sum())} differ")
+        np.testing.assert_array_equal(g, o)
