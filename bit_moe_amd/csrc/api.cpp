@@ -89,7 +89,7 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
         f.p.h = c.take<uint16_t>(n * L->I);
         f.p.hexp = c.take<int32_t>(n * (L->I / 256));
         f.p.o16 = c.take<uint16_t>(n * L->H);
-        f.p.oexp = c.take<int32_t>(n * ((L->H + 511) / 512));
+        f.p.oexp = c.take<int32_t>(n * ((L->H + bm_cfg::kPfDnCols - 1) / bm_cfg::kPfDnCols));
         if (shared) {
             f.p.hs = c.take<float>((int64_t)T * L->I);
             f.p.os = c.take<float>((int64_t)T * L->H);

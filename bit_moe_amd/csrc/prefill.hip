@@ -65,7 +65,7 @@ constexpr int kPfHalf = 128;                  // K per LDS stage
 // contiguous 128-byte runs, which gfx950's LDS serves without bank conflicts
 // (row-strided layouts, padded or XOR-swizzled, cost 4 extra cycles per read).
 constexpr int kPfGuCols = 256;                // h columns per gate/up workgroup
-constexpr int kPfDnCols = 512;                // output columns per down workgroup (16 waves x 32)
+using bm_cfg::kPfDnCols;                      // output columns per down workgroup (one 32-column block per wave)
 constexpr int kPfXcds = 8;
 constexpr int kPfMagBytes = kLutMagBytes;       // 256 codebook rows x 16 copies x 16 bytes
 constexpr int kPfSgnBytes = kLutSgnHalf;        // 128 sign patterns x 16 copies x 16 bytes
