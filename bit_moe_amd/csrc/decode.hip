@@ -303,9 +303,11 @@ BM_DEV void shared_gateup_mfma(int H, int I, int T, int t0, int P, int c0, int c
     }
 }
 
-// Workgroup roles, in blockIdx order: router rows (n_rwg) | shared-expert
-// gate/up partial sums per (panel, K chunk).  Workgroup 0 also clears the
-// down launch's per-panel combine counters.
+// Workgroup roles, in blockIdx order: router rows (n_rwg, one per wave) |
+// shared-expert gate/up partial sums per (panel, K chunk).  Workgroup 0
+// also clears the down launch's per-panel combine counters.  Launched with
+// kW waves, or (no shared chunks) fewer, so that the router rows spread
+// over more compute units.
 template <int XBF16>
 __global__ void __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4)))
 k_dec_front(int H, int I, int E, int T, int n_rwg, int kc_sg, const uint16_t *__restrict__ wr,
@@ -313,14 +315,14 @@ k_dec_front(int H, int I, int E, int T, int n_rwg, int kc_sg, const uint16_t *__
             int32_t *__restrict__ gctr, const uint4 *__restrict__ sg, const uint4 *__restrict__ su,
             float *__restrict__ sgp) {
     __shared__ float red[kW * kNT * 2 * 64];
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
     int b = blockIdx.x;
     if (b == 0) {
-        for (int p = threadIdx.x; p < H / 64; p += kW * 64) ycount[p] = 0;
+        for (int p = threadIdx.x; p < H / 64; p += blockDim.x) ycount[p] = 0;
         if (gctr && threadIdx.x == 0) *gctr = 0;
     }
     if (b < n_rwg) {
-        const int e = b * kW + wv;
+        const int e = b * nw + wv;
         if (e >= E) return;
         const uint4 *wrow = reinterpret_cast<const uint4 *>(wr + (int64_t)e * H);
         if (T == 1)
@@ -544,7 +546,7 @@ template <int XBF16, int SGN>
 BM_DEV void routed_gateup_1(int H, int I, int k, const Tok &tk, int P, const uint8_t *__restrict__ gate,
                             const uint8_t *__restrict__ up, const void *__restrict__ x, const int32_t *perm,
                             uint16_t *__restrict__ h, float2 *__restrict__ hsum2, float *__restrict__ hscale,
-                            float *red, int tok0 = -1) {
+                            float *red, int tok0 = -1, int nrw = kWG) {
     constexpr int kRing = 4;
     const int lane = lane_id(), wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tok[1] = {__builtin_amdgcn_readfirstlane(tok0 >= 0 ? tok0 : perm ? perm[tk.off] / k : 0)};
@@ -555,8 +557,8 @@ BM_DEV void routed_gateup_1(int H, int I, int k, const Tok &tk, int P, const uin
     const uint4 *uq = reinterpret_cast<const uint4 *>(U) + (int64_t)P * nb * 4 * 64 + lane;
     const uint16_t *gd = reinterpret_cast<const uint16_t *>(G + (int64_t)I * nb * 64) + (int64_t)P * nb * 64 + lane;
     const uint16_t *ud = reinterpret_cast<const uint16_t *>(U + (int64_t)I * nb * 64) + (int64_t)P * nb * 64 + lane;
-    int p0, p1;
-    split_range(4 * nb, kWG, wv, p0, p1);
+    int p0 = 0, p1 = 0;                                // waves from nrw on take none
+    if (wv < nrw) split_range(4 * nb, nrw, wv, p0, p1);
     struct Piece { uint4 g, u; uint32_t dg, du; };
     // pieces past the wave's last re-read it (cached) and are not decoded
     auto load = [&](int pc, Piece &q) {
@@ -712,14 +714,15 @@ BM_DEV void mx_gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P, co
 template <int XBF16>
 BM_DEV void mx_gateup_1(int H, int I, int k, const Tok &tk, int P, const uint8_t *__restrict__ gate,
                         const uint8_t *__restrict__ up, const void *__restrict__ x, const int32_t *perm,
-                        uint16_t *__restrict__ h, float *__restrict__ hscale, float *red, int tok0 = -1) {
+                        uint16_t *__restrict__ h, float *__restrict__ hscale, float *red, int tok0 = -1,
+                        int nrw = kWG) {
     constexpr int kRing = 4;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tok[1] = {__builtin_amdgcn_readfirstlane(tok0 >= 0 ? tok0 : perm ? perm[tk.off] / k : 0)};
     const int64_t slab = (int64_t)I * H / 32 * 17;
     const MxRows G = mx_rows(gate + tk.e * slab, I, H, P), U = mx_rows(up + tk.e * slab, I, H, P);
-    int p0, p1;
-    split_range(8 * (H / kQK), kWG, wv, p0, p1);
+    int p0 = 0, p1 = 0;                                // waves from nrw on take none
+    if (wv < nrw) split_range(8 * (H / kQK), nrw, wv, p0, p1);
     struct Piece { uint4 g, u; uint32_t sg, su; };
     auto load = [&](int pc, Piece &q) {
         pc = min(pc, p1 - 1);                          // past the wave's last: re-read, not decoded
@@ -767,11 +770,11 @@ template <int FMT, int XBF16, int SGN>
 BM_DEV void gateup_1(int H, int I, int k, const Tok &tk, int P, const uint8_t *__restrict__ gate,
                      const uint8_t *__restrict__ up, const void *__restrict__ x, const int32_t *perm,
                      uint16_t *__restrict__ h, float2 *__restrict__ hsum2, float *__restrict__ hscale, float *red,
-                     int tok0 = -1) {
+                     int tok0 = -1, int nrw = kWG) {
     if constexpr (FMT == BITMOE_FORMAT_MXFP4)
-        mx_gateup_1<XBF16>(H, I, k, tk, P, gate, up, x, perm, h, hscale, red, tok0);
+        mx_gateup_1<XBF16>(H, I, k, tk, P, gate, up, x, perm, h, hscale, red, tok0, nrw);
     else
-        routed_gateup_1<XBF16, SGN>(H, I, k, tk, P, gate, up, x, perm, h, hsum2, hscale, red, tok0);
+        routed_gateup_1<XBF16, SGN>(H, I, k, tk, P, gate, up, x, perm, h, hsum2, hscale, red, tok0, nrw);
 }
 template <int FMT, int XBF16, int NT, int SGN>
 BM_DEV void gateup_pass(int H, int I, int k, const Tok &tk, int t0, int P, const uint8_t *__restrict__ gate,
@@ -811,48 +814,46 @@ BM_DEV void route_logits_load(const float *__restrict__ logits, int E, int t, fl
     for (int i = 0; i < 4; i++) lv[i] = logits[(int64_t)t * E + min(lane + 64 * i, E - 1)];
 }
 
-// One token (k distinct experts, as a top-k gives): wave 0 takes the top-k
-// of the logits (mode 1) or loads the given ids (mode 2), and ranks the k
-// experts by index with k lane reads; slot = rank, each expert one pair, in
-// LDS (r.active) and, by the workgroup that writes out, in bk.
-BM_DEV void route_one_token(int mode, int E, int k, const float *__restrict__ logits, int32_t *ids, float *w,
-                            const bm_host::Buckets &bk, SmallRoute &r, float (&lv)[4], bool lv_loaded, bool out) {
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
-    if (wv == 0) {
-        int id;
-        if (mode == 1) {
-            if (E <= 256) {
-                if (!lv_loaded) route_logits_load(logits, E, 0, lv);
-                id = topk_wave4(lv, E, k, out ? ids : nullptr, out ? w : nullptr, nullptr);
-            } else {
-                topk_wave(logits, E, k, out ? ids : nullptr, out ? w : nullptr, r.ids);
-                id = lane < k ? r.ids[lane] : 0;
-            }
+// One token (k distinct experts, as a top-k gives), by wave 0: the top-k of
+// the logits (mode 1) or the given ids (mode 2), the k experts ranked by
+// index with k lane reads; slot = rank, each expert one pair, in LDS
+// (r.active) and, by the workgroup that writes out, in bk.  The other waves
+// read r after the next workgroup barrier.
+BM_DEV void route_token_wave0(int mode, int E, int k, const float *__restrict__ logits, int32_t *ids, float *w,
+                              const bm_host::Buckets &bk, SmallRoute &r, float (&lv)[4], bool lv_loaded, bool out) {
+    const int lane = lane_id();
+    int id;
+    if (mode == 1) {
+        if (E <= 256) {
+            if (!lv_loaded) route_logits_load(logits, E, 0, lv);
+            id = topk_wave4(lv, E, k, out ? ids : nullptr, out ? w : nullptr, nullptr);
         } else {
-            id = lane < k ? ids[lane] : 0;
+            topk_wave(logits, E, k, out ? ids : nullptr, out ? w : nullptr, r.ids);
+            id = lane < k ? r.ids[lane] : 0;
         }
-        // rank by (expert, position): a permutation of 0..k-1 even if a row
-        // repeats an expert (which a top-k never does), so every slot is set
-        int rank = 0;
-        for (int i = 0; i < k; i++) {
-            const int o = __builtin_amdgcn_readlane(id, i);
-            rank += (o < id || (o == id && i < lane)) ? 1 : 0;
-        }
-        if (lane < k) {
-            r.active[rank] = id;
-            if (out) {
-                bk.perm[rank] = lane;
-                bk.active[rank] = id;
-                bk.counts[id] = 1;
-                bk.offsets[id] = rank;
-            }
-        }
-        if (lane == 0) {
-            r.n_active = k;
-            if (out) *bk.n_active = k;
+    } else {
+        id = lane < k ? ids[lane] : 0;
+    }
+    // rank by (expert, position): a permutation of 0..k-1 even if a row
+    // repeats an expert (which a top-k never does), so every slot is set
+    int rank = 0;
+    for (int i = 0; i < k; i++) {
+        const int o = __builtin_amdgcn_readlane(id, i);
+        rank += (o < id || (o == id && i < lane)) ? 1 : 0;
+    }
+    if (lane < k) {
+        r.active[rank] = id;
+        if (out) {
+            bk.perm[rank] = lane;
+            bk.active[rank] = id;
+            bk.counts[id] = 1;
+            bk.offsets[id] = rank;
         }
     }
-    __syncthreads();
+    if (lane == 0) {
+        r.n_active = k;
+        if (out) *bk.n_active = k;
+    }
 }
 
 // Shared-expert h of elements [f0, f1) by this workgroup: h = silu(sum of
@@ -881,6 +882,109 @@ BM_DEV void shared_h_load(int64_t n, int kc_sg, const float *__restrict__ sgp, i
     }
 }
 
+// The shared expert's gate/up for the one token of a single-token batch,
+// inside the routed gate/up launch, on kSgWaves waves of each workgroup
+// beside the routed ones: workgroup (slot s, panel P) takes rows r0 = s R ..
+// r0 + R - 1 of panel P (R = 64/k: the k workgroups of a panel share its 64
+// rows) over all of K, so that no sum crosses workgroups.  Lane l of
+// shared wave sw takes row r0 + l % R and the pieces c = q + j Q, q = sw
+// (64/R) + l / R, Q = kSgWaves (64/R), rounds j: one load of the wave
+// covers 64/R pieces of R consecutive rows (R adjacent 16-byte pieces each
+// in the tiled layout).  The routed waves decode (VALU-bound) while these
+// stream (memory-bound), and none of it depends on the routing, so the
+// first rounds run while the token is routed.  The rounds stream through a
+// ring of kRing register slots, each refilled as soon as it is summed.
+constexpr int kSgWaves = 4;
+constexpr int kSgPreRounds = 8;      // rounds before the routing barrier
+constexpr int kSredFloats = kSgWaves * 2 * 64;
+BM_DEV float dot8x(uint4 w, uint4 xv, float acc) {
+    acc = dot2_bf16(w.x, xv.x, acc);
+    acc = dot2_bf16(w.y, xv.y, acc);
+    acc = dot2_bf16(w.z, xv.z, acc);
+    return dot2_bf16(w.w, xv.w, acc);
+}
+BM_DEV int shared_rows_rounds(int H, int R) { return (H / 8 + kSgWaves * (64 / R) - 1) / (kSgWaves * (64 / R)); }
+template <int XBF16>
+BM_DEV void shared_rows_range(int H, int R, int r0, int P, int sw, int j0, int j1, const uint4 *__restrict__ sg,
+                              const uint4 *__restrict__ su, const void *__restrict__ x, float &ag, float &au) {
+    constexpr int kRing = 8;
+    if (j0 >= j1) return;
+    const int lane = lane_id();
+    const int K8 = H / 8, G = 64 / R, Q = kSgWaves * G, sh = __builtin_ctz(R);
+    const int q = sw * G + (lane >> sh);
+    const int64_t base = (int64_t)P * K8 * 64 + r0 + (lane & (R - 1));
+    struct Slot { uint4 g, u, xv; };
+    // rounds past j1 re-read the last one (cached) and are not summed;
+    // pieces past K8 (a ragged last round) likewise
+    auto load = [&](int j, Slot &sl) {
+        const int c = min(q + min(j, j1 - 1) * Q, K8 - 1);
+        sl.g = sg[base + (int64_t)c * 64];
+        sl.u = su[base + (int64_t)c * 64];
+        if (XBF16) sl.xv = reinterpret_cast<const uint4 *>(x)[c];
+    };
+    auto sum = [&](int j, const Slot &sl) {
+        const int c = q + j * Q;
+        float g, u;
+        if (XBF16) {
+            g = dot8x(sl.g, sl.xv, ag);
+            u = dot8x(sl.u, sl.xv, au);
+        } else {
+            const void *xp = static_cast<const float *>(x) + 8 * min(c, K8 - 1);
+            g = dot8<0>(make_uint2(sl.g.x, sl.g.y), make_uint2(sl.g.z, sl.g.w), xp, ag);
+            u = dot8<0>(make_uint2(sl.u.x, sl.u.y), make_uint2(sl.u.z, sl.u.w), xp, au);
+        }
+        ag = c < K8 ? g : ag;
+        au = c < K8 ? u : au;
+    };
+    Slot ring[kRing];
+#pragma unroll
+    for (int i = 0; i < kRing; i++) load(j0 + i, ring[i]);
+    int j = j0;
+    for (; j + kRing <= j1; j += kRing) {
+#pragma unroll
+        for (int i = 0; i < kRing; i++) {
+            sum(j + i, ring[i]);
+            __builtin_amdgcn_sched_barrier(0);
+            load(j + i + kRing, ring[i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kRing; i++)
+        if (j + i < j1) sum(j + i, ring[i]);
+}
+// the lanes of a row meet by lane exchanges (xor over l / R), the shared
+// waves in sred ([kSgWaves][2][64])
+BM_DEV void shared_rows_reduce(int R, int sw, float ag, float au, float *sred) {
+    const int lane = lane_id();
+    for (int m = R; m < 64; m <<= 1) {
+        ag += __shfl_xor(ag, m, 64);
+        au += __shfl_xor(au, m, 64);
+    }
+    if (lane < R) {
+        sred[(sw * 2 + 0) * 64 + lane] = ag;
+        sred[(sw * 2 + 1) * 64 + lane] = au;
+    }
+}
+// h of the R rows (after a workgroup barrier, by one wave): the shared
+// waves' sums in wave order, h = silu(g) u as bf16 hi + lo for the down
+// launch.
+BM_DEV void shared_rows_finish(int I, int R, int r0, int P, const float *sred, uint16_t *__restrict__ hs) {
+    const int lane = lane_id();
+    if (lane >= R) return;
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int v = 0; v < kSgWaves; v++) {
+        g += sred[(v * 2 + 0) * 64 + lane];
+        u += sred[(v * 2 + 1) * 64 + lane];
+    }
+    const float hv = silu(g) * u;
+    const int n = P * 64 + r0 + lane;
+    const uint32_t hi = f32_to_bf16_rne(hv);
+    hs[n] = (uint16_t)hi;
+    hs[I + n] = (uint16_t)f32_to_bf16_rne(hv - bf16_to_f32(hi));
+}
+
 // MULTI = 0 takes the experts chosen by exactly one token, MULTI = 1 the
 // experts with several tokens (passes of kNT tokens); keeping the two apart
 // keeps each kernel's register use low.  route_mode: 0 the bucketing is in
@@ -894,12 +998,13 @@ template <int FMT, int MULTI>
 constexpr int dec_lut_bytes() { return FMT == BITMOE_FORMAT_MXFP4 ? 0 : kLutMagBytes + dec_sgn_bytes<MULTI>(); }
 // all LDS of a gate/up workgroup, dynamic so that the tables start at
 // address 0 (their lookup offsets are then the permutes' results as they
-// are): tables | cross-wave sums | routing
+// are): tables | cross-wave sums | routing | (MULTI = 0) shared-row sums
 template <int MULTI>
 constexpr int dec_red_floats() { return kWG * (MULTI ? kNT : 1) * 2 * 64; }
 template <int FMT, int MULTI>
 constexpr int dec_gateup_lds() {
-    return dec_lut_bytes<FMT, MULTI>() + dec_red_floats<MULTI>() * 4 + (int)sizeof(SmallRoute);
+    return dec_lut_bytes<FMT, MULTI>() + dec_red_floats<MULTI>() * 4 + (int)sizeof(SmallRoute) +
+           (MULTI ? 0 : kSredFloats * 4);
 }
 
 template <int FMT, int XBF16, int MULTI>
@@ -909,10 +1014,12 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
              const void *__restrict__ x, const float *__restrict__ logits,
              int32_t *ids, float *w, bm_host::Buckets bk, uint16_t *__restrict__ h, float2 *__restrict__ hsum2,
              float *__restrict__ hscale, int kc_sg, const float *__restrict__ sgp, uint16_t *__restrict__ hs,
+             int sg_rows, const uint4 *__restrict__ sg, const uint4 *__restrict__ su,
              const int4 *__restrict__ single, const int32_t *__restrict__ n_single, int32_t *__restrict__ gctr) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lut[];
     float *red = reinterpret_cast<float *>(lut + dec_lut_bytes<FMT, MULTI>());
     SmallRoute &sr = *reinterpret_cast<SmallRoute *>(red + dec_red_floats<MULTI>());
+    float *sred = reinterpret_cast<float *>(&sr + 1);
     constexpr int SGN = dec_sgn_bytes<MULTI>();
     const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = blockIdx.x, panels = I / 64, slot = b / panels, P = b % panels;
@@ -943,14 +1050,30 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
             shared_h_load(nfin, kc_sg, sgp, i, fg, fu);
             shared_h_store(nfin, kc_sg, sgp, hs, i, fg, fu);
         }
-        route_one_token(route_mode, E, k, logits, ids, w, bk, sr, lv, pre, b == 0);   // ends with a barrier
+        if (wv == 0) route_token_wave0(route_mode, E, k, logits, ids, w, bk, sr, lv, pre, b == 0);
+        // sg_rows: the last kSgWaves waves take this workgroup's shared rows
+        // (the grid holds the k slots' workgroups, so slot < k), their
+        // first rounds while wave 0 routes
+        const int nrw = sg_rows ? kWG - kSgWaves : kWG, sw = wv - nrw;
+        float sa = 0.f, sb = 0.f;
+        const int sj = sg_rows ? shared_rows_rounds(H, sg_rows) : 0;
+        if (sw >= 0)
+            shared_rows_range<XBF16>(H, sg_rows, slot * sg_rows, P, sw, 0, min(sj, kSgPreRounds), sg, su, x, sa, sb);
+        __syncthreads();
         // slot = rank: one pair each, pair row = slot, token 0
         if (slot >= k) return;
+        if (sw >= 0) {
+            shared_rows_range<XBF16>(H, sg_rows, slot * sg_rows, P, sw, kSgPreRounds, sj, sg, su, x, sa, sb);
+            shared_rows_reduce(sg_rows, sw, sa, sb, sred);
+        }
         Tok tk;
         tk.e = sr.active[slot];
         tk.off = slot;
         tk.cnt = 1;
-        gateup_1<FMT, XBF16, SGN>(H, I, k, tk, P, gate, up, x, nullptr, h, hsum2, hscale, red);
+        // (the shared waves take no routed pieces; the pass's barriers make
+        // sred whole before it returns)
+        gateup_1<FMT, XBF16, SGN>(H, I, k, tk, P, gate, up, x, nullptr, h, hsum2, hscale, red, -1, nrw);
+        if (sw == 0) shared_rows_finish(I, sg_rows, slot * sg_rows, P, sred, hs);
         return;
     }
     int na = 0;
@@ -1600,9 +1723,11 @@ static int launch_decode_fmt(const bitmoe_layer *L, const void *x, int x_dtype, 
     // front: router rows, shared gate/up (at least one workgroup: it clears
     // the combine counters)
     const int n_front = std::max(1, p.n_rwg + (shared ? (I / 64) * p.kc_sg : 0));
+    if (p.front_waves < 1 || p.front_waves > kW || (p.kc_sg && p.front_waves != kW)) return BITMOE_EINVAL;
+    if (p.sg_rows && (T != 1 || p.sg_rows * k != 64 || p.slots != k || !shared)) return BITMOE_EINVAL;
     {
         auto kf = bf ? k_dec_front<1> : k_dec_front<0>;
-        kf<<<n_front, kW * 64, 0, s>>>(H, I, E, T, p.n_rwg, p.kc_sg, (const uint16_t *)L->router_w, x, b.logits,
+        kf<<<n_front, p.front_waves * 64, 0, s>>>(H, I, E, T, p.n_rwg, p.kc_sg, (const uint16_t *)L->router_w, x, b.logits,
                                        b.ycount, p.pf_tiles ? b.gctr : nullptr, (const uint4 *)L->shared_gate,
                                        (const uint4 *)L->shared_up, b.sgp);
         BM_LAUNCH_CHECK();
@@ -1692,6 +1817,7 @@ static int launch_decode_fmt(const bitmoe_layer *L, const void *x, int x_dtype, 
                               T, n_gwg, multi ? 0 : route_mode, (const uint8_t *)L->gate_q,
                               (const uint8_t *)L->up_q, (const uint8_t *)L->grid, x, (const float *)b.logits, b.ids,
                               b.w, b.bk, b.h, b.hsum2, b.hscale, p.kc_sg, (const float *)b.sgp, b.hs,
+                              multi ? 0 : p.sg_rows, (const uint4 *)L->shared_gate, (const uint4 *)L->shared_up,
                               (const int4 *)b.single, (const int32_t *)b.n_single,
                               (!multi && split) ? b.gctr : nullptr);
         BM_CHECK_JOIN();

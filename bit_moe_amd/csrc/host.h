@@ -25,6 +25,7 @@ constexpr int kMfmaRouterMinT = 64;       // bf16 tokens from which the matrix-c
 constexpr int kFusedRouterMaxT = 16;      // decode: router rows fused into the first launch
 // decode
 constexpr int kFrontWaves = 16;           // waves per front workgroup
+constexpr int kFrontRouterWaves = 4;      // the same when it only computes router rows
 constexpr int kMaxChunks = 8;             // K chunks of the shared expert, at most
 constexpr int kSharedChunkCols = 512;     // I columns of one shared-down K chunk, at most
 // prefill
@@ -80,7 +81,10 @@ int launch_bucket(const int32_t *ids, int T, int k, int E, const Buckets &b, hip
 struct DecodePlan {
     int slots = 0;          // workgroup rows reserved for active experts
     int n_rwg = 0;          // router workgroups in the front launch (0: ids given)
-    int kc_sg = 0;          // K chunks of the shared gate/up
+    int kc_sg = 0;          // K chunks of the shared gate/up in the front launch (0: none there)
+    int sg_rows = 0;        // > 0: one token, the shared gate/up inside the routed gate/up
+                            // launch, sg_rows = 64/k rows of a panel per workgroup
+    int front_waves = bm_cfg::kFrontWaves;   // waves per front workgroup (router rows: one per wave)
     int kc_sd = 0;          // K chunks of the shared down
     bool small = false;     // T*k <= kWaveBucketMax: one-wave bucketing
     bool need_mid = true;   // top-k and/or bucketing in a launch of their own

@@ -42,10 +42,15 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     DecodePlan p;
     const bool shared = L->shared_gate != nullptr;
     p.slots = (int)std::min<int64_t>(L->E, (int64_t)T * L->k);
-    p.n_rwg = with_router ? (L->E + kFrontWaves - 1) / kFrontWaves : 0;
-    // the shared gate/up's K chunks: as many as fit the compute units
-    // beside the router workgroups (one front workgroup per CU), at most 8
-    p.kc_sg = shared ? std::max(1, std::min(kMaxChunks, (cu_count() - p.n_rwg) / (L->I / 64))) : 0;
+    // one token: the k gate/up workgroups of a panel also take 64/k of its
+    // shared rows each (k a power of two), so the front launch only computes
+    // the router logits, with small workgroups spread over more CUs
+    p.sg_rows = (shared && T == 1 && L->k <= 16 && 64 % L->k == 0) ? 64 / L->k : 0;
+    p.front_waves = (T == 1 && (p.sg_rows || !shared)) ? kFrontRouterWaves : kFrontWaves;
+    p.n_rwg = with_router ? (L->E + p.front_waves - 1) / p.front_waves : 0;
+    // otherwise the shared gate/up's K chunks: as many as fit the compute
+    // units beside the router workgroups (one front workgroup per CU), at most 8
+    p.kc_sg = shared && !p.sg_rows ? std::max(1, std::min(kMaxChunks, (cu_count() - p.n_rwg) / (L->I / 64))) : 0;
     p.kc_sd = shared ? std::max(1, (L->I + kSharedChunkCols - 1) / kSharedChunkCols) : 0;
     p.small = (int64_t)T * L->k <= kWaveBucketMax;
     // one token: every gate/up workgroup routes it itself; more tokens: one

@@ -87,6 +87,32 @@ def test_decode_b16_zipf_full():
     assert_close_rms(y, ref, what="decode_b16_zipf")
 
 
+@pytest.mark.parametrize("k", [1, 3, 4, 16])
+def test_decode_one_token_shared_every_k(k):
+    """One token with a shared expert.  k a power of two: the k gate/up
+    workgroups of each panel also take 64/k of its shared rows each over all
+    of K (k = 1: all 64 rows; k = 16: four), on four waves that deal out the
+    160 (H 1280) or 96 (H 768) pieces of a row in rounds of 4 * k pieces:
+    a ragged last round at k = 16 (64 per round); at k = 4 (16 per round)
+    6 or 10 rounds, fewer and more than run before the routing barrier.
+    k = 3: the front launch's K chunks.  bf16 and fp32 activations, both
+    entry points that take one token (given ids, and routing on the GPU)."""
+    require_gpu()
+    import bit_moe_amd as bm
+    for xd, H in (("bf16", 1280), ("f32", 768)):
+        w = synth.WORKLOADS["tiny"].with_(name=f"tiny_sr{k}_{xd}", T=1, H=H, E=32, k=k, shared=True, x_dtype=xd,
+                                          seed=60 + k)
+        L = synth_layer(w)
+        x, _ = synth.make_tokens(w, accept=lambda t, r: oracle.margin_ok(r, L.router(), w.k, 1e-4))
+        ids, wt = _routing(w, x)
+        ref = _oracle_rows(w, x, ids, wt, np.arange(1))
+        assert_close_rms(_gpu_ffn(w, x, ids, wt, "decode"), ref, what=f"one token k={k} {xd} H={H}")
+        y, gid, gw = bm.forward_decode(device_layer(w), x_to_device(x))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gid.cpu().numpy(), ids)
+        assert_close_rms(y.cpu().numpy(), ref, what=f"one token routed on the GPU k={k} {xd} H={H}")
+
+
 PF_TILE_ROWS = 96      # rows per prefill row tile (blocks of 32 rows)
 
 
