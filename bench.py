@@ -170,10 +170,13 @@ def decode_b1(args, L, lays, fmt="2bit"):
     n = min(args.steps, 100)
     gu_ms, gu_stats = time_kernel(step, n, bm.TIME_GATEUP)
     dn_ms, dn_stats = time_kernel(step, n, bm.TIME_DOWN)
-    # the gate/up launch streams the routed gate/up blocks of the k experts;
-    # the down launch the k experts' down blocks and the shared down
+    # the gate/up launch streams the routed gate/up blocks of the k experts
+    # and, for 2-bit experts and k a power of two up to 16 (the shared
+    # expert's rows split over the k workgroups of each panel), the shared
+    # gate/up; the down launch the k experts' down blocks and the shared down
     eg, ed = expert_bytes(w)
-    gu_bytes = w.k * eg
+    shared_in_gu = w.shared and fmt == "2bit" and w.k <= 16 and 64 % w.k == 0
+    gu_bytes = w.k * eg + (2 * w.I * w.H * 2 if shared_in_gu else 0)
     dn_bytes = w.k * ed + w.I * w.H * 2
     step_bytes = w.k * (eg + ed) + 3 * w.I * w.H * 2 + w.E * w.H * 2
     return dict(ms=ms, stats=stats, gu_ms=gu_ms, gu_stats=gu_stats, gu_bytes=gu_bytes, dn_ms=dn_ms,

@@ -140,9 +140,12 @@ int forward_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, int
                    void *ws, size_t ws_bytes, void *stream, bool fork);
 
 // prefill FFN
-// xprep + routed gate/up + routed down over b's row tiles; o written per pair
+// xprep + routed gate/up + routed down over b's row tiles; o written per pair.
+// parts: kPfPrep the activations' preparation only (it needs no routing),
+// kPfRouted the rest, kPfAll both
+enum { kPfPrep = 1, kPfRouted = 2, kPfAll = 3 };
 int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int T, const Buckets &b,
-                          int max_tiles, const PrefillBufs &pb, hipStream_t s);
+                          int max_tiles, const PrefillBufs &pb, hipStream_t s, int parts = kPfAll);
 int launch_prefill_ffn(const bitmoe_layer *L, const void *x, int x_dtype, int T, const float *w, float *y,
                        const Buckets &b, int max_tiles, const PrefillBufs &pb, hipStream_t s);
 

@@ -42,10 +42,14 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     DecodePlan p;
     const bool shared = L->shared_gate != nullptr;
     p.slots = (int)std::min<int64_t>(L->E, (int64_t)T * L->k);
-    // one token: the k gate/up workgroups of a panel also take 64/k of its
-    // shared rows each (k a power of two), so the front launch only computes
-    // the router logits, with small workgroups spread over more CUs
-    p.sg_rows = (shared && T == 1 && L->k <= 16 && 64 % L->k == 0) ? 64 / L->k : 0;
+    // one token, 2-bit experts: the k gate/up workgroups of a panel also take
+    // 64/k of its shared rows each (k a power of two), streaming beside the
+    // routed experts' decode, which is bound by its lookups and arithmetic;
+    // the front launch then only computes the router logits, with small
+    // workgroups spread over more CUs.  (The MXFP4 gate/up streams at the
+    // memory's pace already: its shared gate/up stays in the front launch.)
+    p.sg_rows = (shared && T == 1 && L->format == BITMOE_FORMAT_2BIT && L->k <= 16 && 64 % L->k == 0)
+                    ? 64 / L->k : 0;
     p.front_waves = (T == 1 && (p.sg_rows || !shared)) ? kFrontRouterWaves : kFrontWaves;
     p.n_rwg = with_router ? (L->E + p.front_waves - 1) / p.front_waves : 0;
     // otherwise the shared gate/up's K chunks: as many as fit the compute

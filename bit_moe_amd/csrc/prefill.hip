@@ -1026,7 +1026,7 @@ namespace bm_host {
 
 // MXFP4 routed experts: activation rounding (fp32 input only), gate/up, down
 static int launch_prefill_routed_mx(const bitmoe_layer *L, const void *x, int x_dtype, int T, const Buckets &b,
-                                    int max_tiles, const PrefillBufs &pb, hipStream_t s) {
+                                    int max_tiles, const PrefillBufs &pb, hipStream_t s, int parts) {
     const int H = L->H, I = L->I, k = L->k;
     static const bool attr =
         hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_down<0>), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1034,13 +1034,13 @@ static int launch_prefill_routed_mx(const bitmoe_layer *L, const void *x, int x_
         hipFuncSetAttribute(reinterpret_cast<const void *>(k_mx_down<1>), hipFuncAttributeMaxDynamicSharedMemorySize,
                             kPfDnLdsAll) == hipSuccess;
     if (!attr) return BITMOE_EHIP;
-    const uint16_t *xb = static_cast<const uint16_t *>(x);
-    if (x_dtype != BITMOE_BF16) {
+    const uint16_t *xb = x_dtype == BITMOE_BF16 ? static_cast<const uint16_t *>(x) : pb.x16;
+    if (x_dtype != BITMOE_BF16 && (parts & kPfPrep)) {
         const int64_t n8 = (int64_t)T * H / 8;
         k_mx_xprep<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(n8, static_cast<const float *>(x), pb.x16);
         BM_LAUNCH_CHECK();
-        xb = pb.x16;
     }
+    if (!(parts & kPfRouted)) return BITMOE_OK;
     {
         GuArgs a{H, I, k, (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q, nullptr, xb, nullptr,
                  b.counts, b.offsets, b.perm, b.tiles, b.n_tiles, pb.h, nullptr};
@@ -1062,8 +1062,9 @@ static int launch_prefill_routed_mx(const bitmoe_layer *L, const void *x, int x_
 }
 
 int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int T, const Buckets &b,
-                          int max_tiles, const PrefillBufs &pb, hipStream_t s) {
-    if (L->format == BITMOE_FORMAT_MXFP4) return launch_prefill_routed_mx(L, x, x_dtype, T, b, max_tiles, pb, s);
+                          int max_tiles, const PrefillBufs &pb, hipStream_t s, int parts) {
+    if (L->format == BITMOE_FORMAT_MXFP4)
+        return launch_prefill_routed_mx(L, x, x_dtype, T, b, max_tiles, pb, s, parts);
     const int H = L->H, I = L->I, k = L->k;
     static const bool attr = [] {
         hipFuncAttributes fa;           // the gate/up tables must start at LDS address 0
@@ -1077,9 +1078,12 @@ int launch_prefill_routed(const bitmoe_layer *L, const void *x, int x_dtype, int
                                    hipFuncAttributeMaxDynamicSharedMemorySize, kPfDnLdsAll) == hipSuccess;
     }();
     if (!attr) return BITMOE_EHIP;
-    if (x_dtype == BITMOE_BF16) k_pf_xprep<1><<<T, 256, 0, s>>>(H, x, pb.x16, pb.xsc);
-    else k_pf_xprep<0><<<T, 256, 0, s>>>(H, x, pb.x16, pb.xsc);
-    BM_LAUNCH_CHECK();
+    if (parts & kPfPrep) {
+        if (x_dtype == BITMOE_BF16) k_pf_xprep<1><<<T, 256, 0, s>>>(H, x, pb.x16, pb.xsc);
+        else k_pf_xprep<0><<<T, 256, 0, s>>>(H, x, pb.x16, pb.xsc);
+        BM_LAUNCH_CHECK();
+    }
+    if (!(parts & kPfRouted)) return BITMOE_OK;
     {
         GuArgs a{H, I, k, (const uint8_t *)L->gate_q, (const uint8_t *)L->up_q, (const uint8_t *)L->grid,
                  pb.x16, pb.xsc, b.counts, b.offsets, b.perm, b.tiles, b.n_tiles, pb.h, pb.hexp};
