@@ -273,14 +273,15 @@ BM_DEV void router_row(const uint4 *__restrict__ wrow, const void *__restrict__ 
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] = 0.f;
     const int steps = (H + 511) / 512;          // H is a multiple of 256
+    const int spare = lane < H / 8 ? lane : 0;
     for (int s0 = 0; s0 < steps; s0 += CH) {
         uint4 wv[CH];
 #pragma unroll
         for (int i = 0; i < CH; i++) {
             // steps past the row, and the idle half-wave of a half-width
-            // last step, re-read the row's first piece and are not used
+            // last step, re-read a piece of the row's first step and are not used
             const int s = s0 + i, k = 512 * s + 8 * lane;
-            wv[i] = wrow[(s < steps && k < H) ? 64 * s + lane : lane];
+            wv[i] = wrow[(s < steps && k < H) ? 64 * s + lane : spare];
         }
         // every loaded piece is used (a branch around the extra ones would
         // let the compiler sink their loads next to the use); the extra
@@ -290,7 +291,7 @@ BM_DEV void router_row(const uint4 *__restrict__ wrow, const void *__restrict__ 
             const int s = s0 + i, k = 512 * s + 8 * lane;
             const bool keep = s < steps && k < H;
             if (NT > 1 && !keep) continue;      // (more tokens: registers are short)
-            const int kc = keep ? k : 8 * lane;
+            const int kc = keep ? k : 8 * spare;
 #pragma unroll
             for (int t = 0; t < NT; t++) {
                 const float a = router_dot8<XBF16, NT>(wv[i], x, H, t < T ? t : 0, kc, acc[t]);
