@@ -213,6 +213,48 @@ def decode_b16(args, lays):
     return dict(ms=ms, stats=stats, distinct=float(d), bytes=float(byts))
 
 
+def decode_small(args, lays, sizes=(2, 3, 4, 8)):
+    """Tiny decode batches (speculative verification of 2-3 tokens, a few
+    batched sessions): moe_forward_decode of T bf16 tokens with the routing
+    computed on the GPU, the layer rotated as at batch 1."""
+    import numpy as np
+    import torch
+    import bit_moe_amd as bm
+    import synth
+    w0 = synth.WORKLOADS["decode_b1"]
+    eg, ed = expert_bytes(w0)
+    out = {}
+    for T in sizes:
+        R = 4
+        xs = []
+        for r in range(R):
+            x, _ = synth.make_tokens(w0.with_(T=T, seed=w0.seed + 1000 * T + r))
+            xs.append(torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda())
+        ids = torch.empty((T, w0.k), dtype=torch.int32, device="cuda")
+        wt = torch.empty((T, w0.k), dtype=torch.float32, device="cuda")
+        y = torch.empty((T, w0.H), dtype=torch.float32, device="cuda")
+        ws = torch.empty(bm.workspace_bytes(lays[0], T, bm.DECODE), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            bm.forward_decode(lays[i % len(lays)], xs[i % R], ids=ids, w=wt, y=y, ws=ws)
+
+        ms, stats = time_steps(step, args.warmup, args.steps)
+        d = []
+        for r in range(R):
+            bm.forward_decode(lays[0], xs[r], ids=ids, w=wt, y=y, ws=ws)
+            d.append(len(np.unique(ids.cpu().numpy())))
+        d = float(np.mean(d))
+        byts = d * (eg + ed) + 3 * w0.I * w0.H * 2 + w0.E * w0.H * 2
+        out[f"T{T}"] = {"tokens": T, "us_per_step": ms * 1e3, "step_us": {k.replace("_ms", "_us"): v * 1e3 if
+                                                                          k.endswith("_ms") else v
+                                                                          for k, v in stats.items()},
+                        "tokens_per_s": T / (ms * 1e-3), "distinct_experts": d, "hbm_bytes": byts,
+                        "hbm_GBps": byts / (ms * 1e-3) / 1e9, "hbm_frac": byts / (ms * 1e-3) / HBM_PEAK}
+        log(f"[bench] decode T={T} {ms * 1e3:.1f} us/step ({d:.1f} distinct experts, "
+            f"{byts / (ms * 1e-3) / 1e9:.0f} GB/s)")
+    return out
+
+
 def issued_rows(counts, tile_rows=96):
     """Rows the prefill matrix-core kernels run per expert: each row tile of
     up to 96 rows runs in blocks of 32, so a tile of r rows issues
@@ -781,6 +823,9 @@ def main():
                                   "hbm_frac": b16["bytes"] / (b16["ms"] * 1e-3) / HBM_PEAK,
                                   "note": "step = top-k of drawn Zipf(1.1) logits + decode FFN"}
         log(f"[bench] decode_b16 {b16['ms'] * 1e3:.1f} us/step")
+        out["decode_small"] = dict(decode_small(args, lays),
+                                   note="moe_forward_decode of T bf16 tokens, routing on the GPU; HBM bytes over the "
+                                        "realised distinct experts + shared expert + router")
         del lays[1:]
         torch.cuda.empty_cache()
         pf = prefill_2k(args, lays)

@@ -987,7 +987,9 @@ BM_DEV void shared_rows_finish(int I, int R, int r0, int P, const float *sred, u
 
 // MULTI = 0 takes the experts chosen by exactly one token, MULTI = 1 the
 // experts with several tokens (passes of kNT tokens); keeping the two apart
-// keeps each kernel's register use low.  route_mode: 0 the bucketing is in
+// keeps each kernel's register use low.  MULTI = 2 takes both in one launch
+// (batches of 2 to 8 tokens, whose few experts with several tokens would
+// otherwise leave most of the GPU idle in a launch of their own).  route_mode: 0 the bucketing is in
 // bk already; one token (MULTI = 0 only): route_one_token from the logits
 // (1) or the given ids (2).  The run lookup tables
 // (dynamic LDS, dec_lut_bytes) are built from the codebook while the batch
@@ -1025,7 +1027,7 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
     const int b = blockIdx.x, panels = I / 64, slot = b / panels, P = b % panels;
     const int32_t *counts = bk.counts, *offsets = bk.offsets, *perm = bk.perm, *active = bk.active;
     // shared-expert h, spread over all workgroups of the MULTI = 0 launch
-    const int64_t nfin = (!MULTI && kc_sg) ? (int64_t)T * I : 0;
+    const int64_t nfin = (MULTI != 1 && kc_sg) ? (int64_t)T * I : 0;
     const int64_t fchunk = (nfin + gridDim.x - 1) / gridDim.x, f0 = b * fchunk, f1 = min(nfin, f0 + fchunk);
     float fg[kMaxChunks], fu[kMaxChunks];
     if (!MULTI && route_mode) {
@@ -1077,7 +1079,7 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
         return;
     }
     int na = 0;
-    if constexpr (!MULTI) {
+    if constexpr (MULTI != 1) {
         for (int64_t i = f0 + tid; i < f1; i += blockDim.x) {
             shared_h_load(nfin, kc_sg, sgp, i, fg, fu);
             shared_h_store(nfin, kc_sg, sgp, hs, i, fg, fu);
@@ -1109,6 +1111,26 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
         }
         return;
     }
+    // one (expert, panel) item: an expert chosen by one token through the
+    // one-token ring, one with several in passes of up to kNT tokens
+    auto run_item = [&](const Tok &tk, int Pi, int tok0) {
+        if (MULTI != 1 && tk.cnt == 1) {
+            gateup_1<FMT, XBF16, SGN>(H, I, k, tk, Pi, gate, up, x, perm, h, hsum2, hscale, red, tok0);
+            return;
+        }
+        if constexpr (MULTI != 0) {
+            for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
+                const int n = tk.cnt - t0;
+                if (n == 1)
+                    gateup_pass<FMT, XBF16, 1, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale, red);
+                else if (n == 2)
+                    gateup_pass<FMT, XBF16, 2, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale, red);
+                else
+                    gateup_pass<FMT, XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale,
+                                                        red);
+            }
+        }
+    };
     // routing done by an earlier launch.  The routing of this workgroup's
     // items (it = b + j G) is loaded at once, one thread per item, instead of
     // one chain of dependent loads per item (the active slot, its expert's
@@ -1132,20 +1154,8 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
             tk.e = in.x;
             tk.off = in.y;
             tk.cnt = in.z;
-            if ((tk.cnt > 1) != (MULTI != 0)) continue;
-            const int Pi = (b + j * G) % panels;
-            if (!MULTI) {
-                gateup_1<FMT, XBF16, SGN>(H, I, k, tk, Pi, gate, up, x, perm, h, hsum2, hscale, red, in.w);
-                continue;
-            }
-            for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
-                if (tk.cnt - t0 == 1)
-                    gateup_pass<FMT, XBF16, 1, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale,
-                                                      red);
-                else
-                    gateup_pass<FMT, XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2,
-                                                        hscale, red);
-            }
+            if (MULTI != 2 && (tk.cnt > 1) != (MULTI != 0)) continue;
+            run_item(tk, (b + j * G) % panels, in.w);
         }
         return;
     }
@@ -1160,23 +1170,13 @@ k_dec_gateup(int H, int I, int E, int k, int T, int n_gwg, int route_mode, const
         tk.e = active[si];
         tk.off = offsets[tk.e];
         tk.cnt = counts[tk.e];
-        if ((tk.cnt > 1) != (MULTI != 0)) continue;
+        if (MULTI != 2 && (tk.cnt > 1) != (MULTI != 0)) continue;
         if (!built) {
             if constexpr (FMT != BITMOE_FORMAT_MXFP4) lut_build<1, SGN>(grid, lut);
             __syncthreads();
             built = true;
         }
-        if (!MULTI) {
-            gateup_1<FMT, XBF16, SGN>(H, I, k, tk, Pi, gate, up, x, perm, h, hsum2, hscale, red);
-            continue;
-        }
-        for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
-            if (tk.cnt - t0 == 1)
-                gateup_pass<FMT, XBF16, 1, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale, red);
-            else
-                gateup_pass<FMT, XBF16, kNT, SGN>(H, I, k, tk, t0, Pi, gate, up, x, perm, h, hsum2, hscale,
-                                                    red);
-        }
+        run_item(tk, Pi, -1);
     }
 }
 
@@ -1615,8 +1615,9 @@ k_dec_combine(int H, int k, int T, int kc_sd, const float *__restrict__ o, const
 }
 
 // MULTI = 0: experts chosen by one token, and the shared down; MULTI = 1:
-// experts chosen by several tokens (launched only when T > 1).  combine = 0:
-// the outputs are only stored (k_dec_combine sums them).
+// experts chosen by several tokens (launched only when T > 1); MULTI = 2:
+// all of them and the shared down, in one launch (batches of 2 to 8 tokens).
+// combine = 0: the outputs are only stored (k_dec_combine sums them).
 template <int FMT, int MULTI>
 __global__ void __launch_bounds__(kWD * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 5)))
 k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__restrict__ n_multi, int combine,
@@ -1650,19 +1651,22 @@ k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__re
             if (combine && count_multi) count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
             return;
         }
-        if ((tk.cnt > 1) != (MULTI != 0)) return;
-        if (!MULTI) {
+        if (MULTI != 2 && (tk.cnt > 1) != (MULTI != 0)) return;
+        if (MULTI == 0 || tk.cnt == 1) {
             down_pass<FMT, 1>(H, I, tk, 0, P, down, perm, h, hsum2, hscale, o, red, hst);
-        } else {
+        } else if constexpr (MULTI != 0) {
             for (int t0 = 0; t0 < tk.cnt; t0 += kNT) {
-                if (tk.cnt - t0 == 1)
+                const int n = tk.cnt - t0;
+                if (n == 1)
                     down_pass<FMT, 1>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
+                else if (n == 2)
+                    down_pass<FMT, 2>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
                 else
                     down_pass<FMT, kNT>(H, I, tk, t0, P, down, perm, h, hsum2, hscale, o, red, hst);
             }
         }
         if (combine) count_and_combine(H, k, T, kc_sd, P, n_contrib, ycount, o, w, osp, y, &sdo);
-    } else if (!MULTI) {
+    } else if (MULTI != 1) {
         const int bs = blockIdx.x - n_dwg, c = bs % kc_sd, P = bs / kc_sd;
         int c0, c1;
         split_range(I / 8, kc_sd, c, c0, c1);
@@ -1768,6 +1772,12 @@ static int launch_decode_fmt(const bitmoe_layer *L, const void *x, int x_dtype, 
         for (auto f : {k_dec_gateup<FMT, 1, 1>, k_dec_gateup<FMT, 0, 1>})
             ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
                                       dec_gateup_lds<FMT, 1>()) == hipSuccess;
+        for (auto f : {k_dec_gateup<FMT, 1, 2>, k_dec_gateup<FMT, 0, 2>}) {
+            hipFuncAttributes fa;
+            ok &= hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(f)) == hipSuccess && fa.sharedSizeBytes == 0;
+            ok &= hipFuncSetAttribute(reinterpret_cast<const void *>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      dec_gateup_lds<FMT, 2>()) == hipSuccess;
+        }
         return ok;
     }();
     if (!lds_set) return BITMOE_EHIP;
@@ -1816,15 +1826,24 @@ static int launch_decode_fmt(const bitmoe_layer *L, const void *x, int x_dtype, 
         const int rc = launch_prefill_routed(L, x, x_dtype, T, b.bk, p.pf_tiles, b.pf, s, kPfRouted);
         if (rc) return fail(rc);
     }
-    for (int multi = 0; multi < (T > 1 && !split ? 2 : 1); multi++) {
-        auto kg = multi ? (bf ? k_dec_gateup<FMT, 1, 1> : k_dec_gateup<FMT, 0, 1>)
-                        : (bf ? k_dec_gateup<FMT, 1, 0> : k_dec_gateup<FMT, 0, 0>);
+    // gate/up launches: experts chosen by one token (all experts of a batch
+    // of one), then, for larger batches without the prefill kernels, those
+    // chosen by several tokens; batches of 2 to 8 tokens take both kinds in
+    // one launch (MULTI = 2)
+    const bool mixed = T > 1 && !split && T < bm_cfg::kSplitMinT;
+    const int n_gu = T > 1 && !split && !mixed ? 2 : 1;
+    for (int li = 0; li < n_gu; li++) {
+        const int multi = li ? 1 : mixed ? 2 : 0;
+        auto kg = multi == 2 ? (bf ? k_dec_gateup<FMT, 1, 2> : k_dec_gateup<FMT, 0, 2>)
+                  : multi    ? (bf ? k_dec_gateup<FMT, 1, 1> : k_dec_gateup<FMT, 0, 1>)
+                             : (bf ? k_dec_gateup<FMT, 1, 0> : k_dec_gateup<FMT, 0, 0>);
+        const int lds = multi == 2 ? dec_gateup_lds<FMT, 2>() : multi ? dec_gateup_lds<FMT, 1>()
+                                                                       : dec_gateup_lds<FMT, 0>();
         // the timing events, when set, are taken by the dispatch itself
         // around the first gate/up launch
-        const TimingEvents ev = multi ? TimingEvents{} : timing_for(BITMOE_TIME_GATEUP);
+        const TimingEvents ev = li ? TimingEvents{} : timing_for(BITMOE_TIME_GATEUP);
         const int grid = route_mode ? n_gwg : std::min(n_gwg, cu_count());
-        hipExtLaunchKernelGGL(kg, dim3(grid), dim3(kWG * 64),
-                              multi ? dec_gateup_lds<FMT, 1>() : dec_gateup_lds<FMT, 0>(), sg_stream, ev.start, ev.stop, 0, H, I,
+        hipExtLaunchKernelGGL(kg, dim3(grid), dim3(kWG * 64), lds, sg_stream, ev.start, ev.stop, 0, H, I,
                               E, k,
                               T, n_gwg, multi ? 0 : route_mode, (const uint8_t *)L->gate_q,
                               (const uint8_t *)L->up_q, (const uint8_t *)L->grid, x, (const float *)b.logits, b.ids,
@@ -1849,7 +1868,8 @@ static int launch_decode_fmt(const bitmoe_layer *L, const void *x, int x_dtype, 
     const int n_sd = shared && !sd_mfma ? (H / 64) * p.kc_sd : 0;
     {
         const TimingEvents ev = timing_for(BITMOE_TIME_DOWN);
-        hipExtLaunchKernelGGL(k_dec_down<FMT, 0>, dim3(n_dwg + n_sd), dim3(kWD * 64), 0, sg_stream, ev.start, ev.stop, 0,
+        hipExtLaunchKernelGGL(mixed ? k_dec_down<FMT, 2> : k_dec_down<FMT, 0>, dim3(n_dwg + n_sd), dim3(kWD * 64), 0,
+                              sg_stream, ev.start, ev.stop, 0,
                               H, I, k, T, n_dwg, p.kc_sd, (const int32_t *)(split ? b.bk.n_tiles : nullptr),
                               split ? 0 : 1, (const uint8_t *)L->down_q, (const uint4 *)L->shared_down,
                               (const int32_t *)b.bk.counts, (const int32_t *)b.bk.offsets, (const int32_t *)b.bk.perm,
@@ -1868,7 +1888,7 @@ static int launch_decode_fmt(const bitmoe_layer *L, const void *x, int x_dtype, 
         BM_LAUNCH_CHECK();
     }
 #undef BM_CHECK_JOIN
-    if (T > 1 && !split) {
+    if (T > 1 && !split && !mixed) {
         k_dec_down<FMT, 1><<<n_dwg, kWD * 64, 0, s>>>(H, I, k, T, n_dwg, p.kc_sd, nullptr, 1, (const uint8_t *)L->down_q,
                                                 (const uint4 *)L->shared_down, b.bk.counts, b.bk.offsets,
                                                 b.bk.perm, b.bk.active, b.bk.n_active, b.h, b.hsum2, b.hscale, b.hs,

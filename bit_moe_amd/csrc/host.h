@@ -30,6 +30,8 @@ constexpr int kMaxChunks = 8;             // K chunks of the shared expert, at m
 constexpr int kSharedChunkCols = 512;     // I columns of one shared-down K chunk, at most
 // prefill
 constexpr int kPfRows = 96;               // rows per prefill row tile (three blocks of 32)
+constexpr int kSplitMinT = 9;             // decode batches from this many tokens run the prefill kernels
+                                          // for their experts chosen by several tokens
 constexpr int kPfDnCols = 512;            // output columns per prefill down workgroup (one exponent each per pair)
 
 }  // namespace bm_cfg

@@ -63,8 +63,12 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     p.need_mid = !p.small || T > 1;
     // several tokens (one row tile per expert): experts chosen by more than
     // one token go through the prefill kernels, which decode each weight once
-    // for all of its tokens on the matrix cores
-    p.pf_tiles = (p.small && T > 1 && T <= kPfRows) ? (int)std::min<int64_t>(L->E, (int64_t)T * L->k / 2) : 0;
+    // for all of its tokens on the matrix cores, beside the single-token
+    // experts on a second stream.  Below kSplitMinT tokens few experts are
+    // shared, and one decode launch for all experts (passes of up to four
+    // tokens) is faster than the fork, the join and the extra launches.
+    p.pf_tiles = (p.small && T >= kSplitMinT && T <= kPfRows) ? (int)std::min<int64_t>(L->E, (int64_t)T * L->k / 2)
+                                                              : 0;
     return p;
 }
 

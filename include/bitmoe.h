@@ -32,14 +32,15 @@
  *    256; 1 <= k <= 16; k <= E <= 1024; T >= 0 (T = 0 is a no-op).
  *  - Calls are thread-safe; calls on different streams may overlap.
  *  - The one piece of library state: moe_ffn_decode / moe_forward_decode on
- *    a batch in which some expert is chosen by several tokens (2 <= T,
- *    T*k <= 128, T <= 96) fork part of the work onto a stream the library
- *    keeps per device (created on the first such call, default priority,
- *    with two events) and join it back into `stream` before the call's last
- *    kernel, also when a launch fails after the fork: the call is ordered
- *    on `stream` as a whole.  Such calls from several host threads take
- *    turns at that stream (a lock held while the call queues its work), so
- *    their side-stream halves run one after another.
+ *    a batch of 9 <= T <= 96 tokens with T*k <= 128 (whose experts chosen
+ *    by several tokens take the prefill kernels) fork part of the work onto
+ *    a stream the library keeps per device (created on the first such call,
+ *    default priority, with two events) and join it back into `stream`
+ *    before the call's last kernel, also when a launch fails after the
+ *    fork: the call is ordered on `stream` as a whole.  Such calls from
+ *    several host threads take turns at that stream (a lock held while the
+ *    call queues its work), so their side-stream halves run one after
+ *    another.
  *
  * Weight formats
  *  CANONICAL blocks (the interchange format, GGML order):

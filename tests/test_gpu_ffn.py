@@ -250,12 +250,13 @@ def test_end_to_end_route_then_ffn():
     assert_close_rms(y.cpu().numpy(), ref, what="route+decode")
 
 
-@pytest.mark.parametrize("T", [1, 4, 16, 20, 64, 200])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 8, 9, 16, 20, 64, 200])
 def test_forward_decode_routes_and_matches_oracle(T):
     """moe_forward_decode (router fused into the first launch for T <= 16,
     separate routing above: the one-wave-per-row router below 64 bf16
     tokens, the split-K matrix-core router from 64) against oracle routing
-    + FFN."""
+    + FFN.  2 to 8 tokens take one decode launch for all experts, 9 to 96
+    the prefill kernels beside them for experts chosen by several tokens."""
     require_gpu()
     import bit_moe_amd as bm
     w0 = synth.WORKLOADS["decode_b1"]
@@ -291,24 +292,27 @@ def test_forward_decode_small_expert_count(T):
     assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode E=8 T={T}")
 
 
+@pytest.mark.parametrize("copies", [4, 12])
 @pytest.mark.parametrize("shared", [False, True])
-def test_forward_decode_all_experts_shared_by_tokens(shared):
-    """Four copies of one token: every chosen expert has four pairs, so the
-    batch's experts all go through the matrix-core kernels and, without a
-    shared expert, no single-token expert is left to combine the outputs."""
+def test_forward_decode_all_experts_shared_by_tokens(shared, copies):
+    """Copies of one token: every chosen expert has one pair per copy.  Twelve
+    copies: the batch's experts all go through the matrix-core kernels and,
+    without a shared expert, no single-token expert is left to combine the
+    outputs; four copies: the one decode launch for all experts, every item
+    a pass of four tokens."""
     require_gpu()
     import bit_moe_amd as bm
     w = synth.WORKLOADS["tiny"].with_(name=f"tiny_rep_{int(shared)}", T=1, shared=shared, x_dtype="bf16", seed=41)
     L = synth_layer(w)
     x1, _ = synth.make_tokens(w, accept=lambda t, r: oracle.margin_ok(r, L.router(), w.k, 1e-4))
-    x = np.repeat(x1, 4, axis=0)
+    x = np.repeat(x1, copies, axis=0)
     y, gid, gw = bm.forward_decode(device_layer(w), x_to_device(x))
     torch.cuda.synchronize()
     rid, rw = oracle.route(x, L.router(), w.k)
     np.testing.assert_array_equal(gid.cpu().numpy(), rid)
     np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=W_TOL)
     ref = oracle.layer_ffn(L, x, rid, rw)
-    assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode 4 equal tokens shared={shared}")
+    assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode {copies} equal tokens shared={shared}")
 
 
 @pytest.mark.parametrize("T", [1, 4])

@@ -125,11 +125,13 @@ def test_tiny_shared_ragged_both_dtypes(mode):
         assert_close_rms(_gpu_ffn(w, x, ids, wt, mode), ref, what=f"mxfp4 tiny-shared/{xd}/{mode}/T={T}")
 
 
-@pytest.mark.parametrize("T", [1, 16, 64, 200])
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 16, 64, 200])
 def test_tiny_decode_batch_paths(T):
-    """T = 1: one expert per workgroup item; 16 and 64: experts chosen by
-    several tokens on the prefill kernels beside the single-token ones;
-    200: the several-token decode passes (four tokens per pass)."""
+    """T = 1: one expert per workgroup item; 2 to 8: experts chosen by one
+    and by several tokens in the same launches (passes of up to 4 tokens);
+    16 and 64: experts chosen by several tokens on the prefill kernels
+    beside the single-token ones; 200: the several-token decode passes (four
+    tokens per pass)."""
     require_gpu()
     from test_gpu_ffn import _gpu_ffn
     w = _mx("tiny").with_(name=f"tiny_mx_b{T}", T=T, x_dtype="bf16", shared=True, seed=40 + T)
