@@ -14,6 +14,23 @@ BM_DEV float dpp_max(float v) {
     const int o = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF, false);
     return fmaxf(v, __int_as_float(o));
 }
+// Max of |v| over each half-wave (row shifts, then row 0 -> 1 and 2 -> 3),
+// complete in lanes 31 and 63.  Non-negative floats order as their bit
+// patterns (a NaN's above +inf), so the steps are integer maxima, each one
+// instruction with its DPP move folded in (lanes without a source read 0,
+// the maximum's identity; a float max adds canonicalising moves around
+// every step).
+BM_DEV float half_wave_max_abs(float v) {
+    uint32_t u = __float_as_uint(fabsf(v));
+#define BM_DPP_UMAX(CTRL, ROWS) u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, CTRL, ROWS, 0xF, false))
+    BM_DPP_UMAX(0x111, 0xF);   // row_shr:1
+    BM_DPP_UMAX(0x112, 0xF);   // row_shr:2
+    BM_DPP_UMAX(0x114, 0xF);   // row_shr:4
+    BM_DPP_UMAX(0x118, 0xF);   // row_shr:8: lane 15 of each row holds the row max
+    BM_DPP_UMAX(0x142, 0xA);   // row_bcast:15 into rows 1, 3
+#undef BM_DPP_UMAX
+    return __uint_as_float(u);
+}
 BM_DEV float wave_max_f32(float v) {
     v = dpp_max<0x111, 0xF>(v);   // row_shr:1
     v = dpp_max<0x112, 0xF>(v);   // row_shr:2

@@ -420,19 +420,19 @@ BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
             const float xs = sxs[32 * i + acc_row(r, kh)];
             hv[i][r] = silu(acc[i][0][r] * xs) * (acc[i][1][r] * xs);
         }
+    // per row, the max over the half-wave's 32 columns (complete in lanes 31
+    // and 63), eight independent reductions at a time so that they interleave
 #pragma unroll
     for (int i = 0; i < MB; i++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            // max over the half-wave (DPP row shifts, then row 0 -> 1 and 2 -> 3):
-            // complete in lanes 31 and 63
-            float mx = fabsf(hv[i][r]);
-            mx = dpp_max<0x111, 0xF>(mx);
-            mx = dpp_max<0x112, 0xF>(mx);
-            mx = dpp_max<0x114, 0xF>(mx);
-            mx = dpp_max<0x118, 0xF>(mx);
-            mx = dpp_max<0x142, 0xA>(mx);
-            if (col == 31) smax[w * kPfRows + 32 * i + acc_row(r, kh)] = mx;
+        for (int r0 = 0; r0 < 16; r0 += 8) {
+            float mx[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) mx[j] = half_wave_max_abs(hv[i][r0 + j]);
+            if (col == 31) {
+#pragma unroll
+                for (int j = 0; j < 8; j++) smax[w * kPfRows + 32 * i + acc_row(r0 + j, kh)] = mx[j];
+            }
         }
     __syncthreads();
     if (threadIdx.x < R) {
@@ -582,14 +582,14 @@ BM_DEV void dn_epilogue(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntil
 #pragma unroll
     for (int i = 0; i < MB; i++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            float mx = active ? fabsf(acc[i][r]) : 0.f;
-            mx = dpp_max<0x111, 0xF>(mx);
-            mx = dpp_max<0x112, 0xF>(mx);
-            mx = dpp_max<0x114, 0xF>(mx);
-            mx = dpp_max<0x118, 0xF>(mx);
-            mx = dpp_max<0x142, 0xA>(mx);
-            if (col == 31) smax[w * kPfRows + 32 * i + acc_row(r, kh)] = mx;
+        for (int r0 = 0; r0 < 16; r0 += 8) {
+            float mx[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) mx[j] = half_wave_max_abs(active ? acc[i][r0 + j] : 0.f);
+            if (col == 31) {
+#pragma unroll
+                for (int j = 0; j < 8; j++) smax[w * kPfRows + 32 * i + acc_row(r0 + j, kh)] = mx[j];
+            }
         }
     __syncthreads();
     if (threadIdx.x < 32 * MB) {
