@@ -445,13 +445,23 @@ BM_DEV void gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
             a.hexp[(int64_t)(t.off + t.r0 + threadIdx.x) * (a.I / kPfGuCols) + ntile] = e;
     }
     __syncthreads();
+    // (a block whose 32 rows are all in the tile stores without per-row tests)
+    uint16_t *hrow = a.h + (int64_t)(t.off + t.r0) * a.I + hc;
+    auto store = [&](int i, int r) {
+        const int m = 32 * i + acc_row(r, kh);
+        hrow[(int64_t)m * a.I] = (uint16_t)f16_bits(ldexpf(hv[i][r], -sexp[m]));
+    };
 #pragma unroll
-    for (int i = 0; i < MB; i++)
+    for (int i = 0; i < MB; i++) {
+        if (32 * (i + 1) <= t.rows) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int m = 32 * i + acc_row(r, kh);
-            if (m < t.rows) a.h[(int64_t)(t.off + t.r0 + m) * a.I + hc] = (uint16_t)f16_bits(ldexpf(hv[i][r], -sexp[m]));
+            for (int r = 0; r < 16; r++) store(i, r);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (32 * i + acc_row(r, kh) < t.rows) store(i, r);
         }
+    }
 }
 
 __global__ void __launch_bounds__(kPfThreads)
@@ -604,13 +614,22 @@ BM_DEV void dn_epilogue(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntil
     }
     __syncthreads();
     if (!active) return;
+    // (a block whose 32 rows are all in the tile stores without per-row tests)
+    auto store = [&](int i, int r) {
+        const int m = 32 * i + acc_row(r, kh);
+        a.o16[(int64_t)spair[m] * a.H + c0] = (uint16_t)f16_bits(ldexpf(acc[i][r], -soex[m]));
+    };
 #pragma unroll
-    for (int i = 0; i < MB; i++)
+    for (int i = 0; i < MB; i++) {
+        if (32 * (i + 1) <= t.rows) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int m = 32 * i + acc_row(r, kh);
-            if (m < t.rows) a.o16[(int64_t)spair[m] * a.H + c0] = (uint16_t)f16_bits(ldexpf(acc[i][r], -soex[m]));
+            for (int r = 0; r < 16; r++) store(i, r);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (32 * i + acc_row(r, kh) < t.rows) store(i, r);
         }
+    }
 }
 
 template <int MB, int OUT32>
@@ -809,15 +828,23 @@ BM_DEV void mx_gu_tile(const GuArgs &a, uint8_t *lds, const PfTile &t, int ntile
         2 * nb, [&](int st, ARegs &v) { gu_stage_load<R>(a, stok, st >> 1, st & 1, v.r); },
         [&](int buf, ARegs &v) { stage_store<R>(sa + buf * kPfABytes, v.r); }, load_slot,
         [&](int buf, const Slot &sl) { compute(sa + buf * kPfABytes, sl); });
+    // (a block whose 32 rows are all in the tile stores without per-row tests)
+    uint16_t *hrow = a.h + (int64_t)(t.off + t.r0) * a.I + hc;
+    auto store = [&](int i, int r) {
+        const int m = 32 * i + acc_row(r, kh);
+        hrow[(int64_t)m * a.I] = (uint16_t)f32_to_bf16_rne(silu(acc[i][0][r]) * acc[i][1][r]);
+    };
 #pragma unroll
-    for (int i = 0; i < MB; i++)
+    for (int i = 0; i < MB; i++) {
+        if (32 * (i + 1) <= t.rows) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int m = 32 * i + acc_row(r, kh);
-            if (m < t.rows)
-                a.h[(int64_t)(t.off + t.r0 + m) * a.I + hc] =
-                    (uint16_t)f32_to_bf16_rne(silu(acc[i][0][r]) * acc[i][1][r]);
+            for (int r = 0; r < 16; r++) store(i, r);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (32 * i + acc_row(r, kh) < t.rows) store(i, r);
         }
+    }
 }
 
 __global__ void __launch_bounds__(kPfThreads)
