@@ -567,8 +567,9 @@ def summarize_kernels(trace_dir):
     rocprofv3 --kernel-trace output directory of a default bench run, grouped
     by bench phase, name and grid.  Phases follow the run's order: layer set-up
     (packing) until the first decode launch, decode_b1 until the batch-16 step's
-    first top-k, decode_b16 until the prefill step's router GEMM (the decode
-    batch also runs prefill kernels, for its multi-token experts), prefill_2k
+    first top-k, decode_b16 (the decode batch also runs prefill kernels, for
+    its multi-token experts) until the first decode launch not preceded by a
+    top-k, decode_small (2 to 8 tokens) until the prefill step's router GEMM, prefill_2k
     until the 8192-token step's top-k, prefill_8k until the expert cache's
     first decode launch, expert_cache until the quantizer, quantize until the
     MXFP4 layer's packing, then mxfp4_decode_b1 from its first decode launch
@@ -578,13 +579,15 @@ def summarize_kernels(trace_dir):
     rows = {}
     for db in glob.glob(os.path.join(trace_dir, "**", "*.db"), recursive=True):
         c = sqlite3.connect(db)
-        phase = "setup"
+        phase, prev = "setup", ""
         for name, gx, t0, t1 in c.execute("select name, grid_x, start, end from kernels order by start"):
             if phase == "setup" and "k_dec_front" in name:
                 phase = "decode_b1"
             elif phase == "decode_b1" and ("k_topk" in name or "k_dec_mid" in name):
                 phase = "decode_b16"
-            elif phase == "decode_b16" and "k_router_splitk" in name:
+            elif phase == "decode_b16" and "k_dec_front" in name and "k_topk" not in prev:
+                phase = "decode_small"
+            elif phase in ("decode_b16", "decode_small") and "k_router_splitk" in name:
                 phase = "prefill_2k"
             elif phase == "prefill_2k" and "k_topk" in name and "k_topk_sum" not in name:
                 phase = "prefill_8k"
@@ -598,6 +601,7 @@ def summarize_kernels(trace_dir):
                 phase = "mxfp4_decode_b1"
             elif phase == "mxfp4_decode_b1" and "k_router_splitk" in name:
                 phase = "mxfp4_prefill_2k"
+            prev = name
             r = rows.setdefault((phase, name, gx), [0, 0.0, float("inf"), 0.0])
             d = (t1 - t0) / 1e3
             r[0] += 1
@@ -605,7 +609,7 @@ def summarize_kernels(trace_dir):
             r[2] = min(r[2], d)
             r[3] = max(r[3], d)
     out = [f"{'phase':<16} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'grid':>10}  kernel"]
-    order = {p: i for i, p in enumerate(("setup", "decode_b1", "decode_b16", "prefill_2k", "prefill_8k",
+    order = {p: i for i, p in enumerate(("setup", "decode_b1", "decode_b16", "decode_small", "prefill_2k", "prefill_8k",
                                          "expert_cache", "quantize", "mxfp4_setup", "mxfp4_decode_b1",
                                          "mxfp4_prefill_2k"))}
     for (phase, name, gx), (n, tot, mn, mx) in sorted(rows.items(), key=lambda kv: (order[kv[0][0]], -kv[1][1])):
