@@ -65,6 +65,20 @@ def test_tiny_shapes_with_shared_and_ragged_tokens(mode):
         assert_close_rms(y, ref, what=f"tiny-shared/{xd}/{mode}/T={T}")
 
 
+@pytest.mark.parametrize("T", [2, 3])
+def test_tiny_decode_few_tokens_shared_both_dtypes(T):
+    """2 or 3 tokens with a shared expert (one gate/up and one down launch
+    for every expert, the shared gate/up partial sums from the front launch),
+    bf16 and fp32 activations."""
+    require_gpu()
+    for xd in ("bf16", "f32"):
+        w = synth.WORKLOADS["tiny"].with_(name=f"tiny_few_{xd}", T=T, shared=True, x_dtype=xd, seed=70 + T)
+        x, _ = synth.make_tokens(w)
+        ids, wt = _routing(w, x)
+        ref = _oracle_rows(w, x, ids, wt, np.arange(T))
+        assert_close_rms(_gpu_ffn(w, x, ids, wt, "decode"), ref, what=f"tiny few tokens/{xd}/T={T}")
+
+
 def test_decode_b1_full():
     require_gpu()
     w = synth.WORKLOADS["decode_b1"]
