@@ -6,7 +6,7 @@ library's HIP kernels.
 """
 from ._lib import (BF16, BitMoEError, DECODE, ExpertCache, F32, FORMAT_2BIT, FORMAT_MXFP4, Layer, PREFILL, SYMBOLS,
                    TIME_DOWN, TIME_GATEUP, bucket, dequant_iq2x, dequant_mxfp4, dequant_q2k, ffn_decode, ffn_prefill,
-                   forward_decode, forward_decode_noalloc, lib, quantize_iq2x, quantize_mxfp4, quantize_q2k, pack_bf16, pack_iq2x,
+                   forward_decode, forward_decode_noalloc, lib, lib_checked, quantize_iq2x, quantize_mxfp4, quantize_q2k, pack_bf16, pack_iq2x,
                    pack_mxfp4, pack_q2k, route, route_workspace_bytes, set_timing_events, strerror, topk, version,
                    workspace_bytes)
 
@@ -46,6 +46,6 @@ def layer_from_canonical(H, I, E, k, router_bits, gate, up, down, grid, shared=N
 
 __all__ = ["BF16", "BitMoEError", "DECODE", "ExpertCache", "F32", "FORMAT_2BIT", "FORMAT_MXFP4", "Layer", "PREFILL",
            "SYMBOLS", "TIME_DOWN", "TIME_GATEUP", "bucket", "dequant_iq2x", "dequant_mxfp4", "dequant_q2k", "ffn_decode",
-           "ffn_prefill", "forward_decode", "forward_decode_noalloc", "layer_from_canonical", "quantize_iq2x",
+           "ffn_prefill", "forward_decode", "forward_decode_noalloc", "layer_from_canonical", "lib_checked", "quantize_iq2x",
            "quantize_mxfp4", "quantize_q2k", "lib", "pack_bf16", "pack_iq2x", "pack_mxfp4", "pack_q2k", "route", "route_workspace_bytes",
            "set_timing_events", "strerror", "topk", "version", "workspace_bytes"]

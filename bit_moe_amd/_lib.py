@@ -13,6 +13,7 @@ from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbitmoe.so")
+LIB_CHECKED_PATH = os.path.join(HERE, "libbitmoe_checked.so")    # built with BITMOE_CHECK_IDS = 1
 
 F32, BF16 = 0, 1
 DECODE, PREFILL = 0, 1
@@ -45,6 +46,7 @@ class LayerStruct(C.Structure):
 
 
 _lib = None
+_lib_checked = None
 
 
 class BitMoEError(RuntimeError):
@@ -56,11 +58,26 @@ class BitMoEError(RuntimeError):
 def lib() -> C.CDLL:
     """Load libbitmoe.so (built in-tree by bit_moe_amd.build)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_moe_amd.build`")
-    L = C.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def lib_checked() -> C.CDLL:
+    """Load libbitmoe_checked.so: the same library built with
+    BITMOE_CHECK_IDS = 1, whose FFN and bucketing calls write the count of
+    the caller's routing ids outside [0, E) into the first int32 of their
+    workspace."""
+    global _lib_checked
+    if _lib_checked is None:
+        _lib_checked = _load(LIB_CHECKED_PATH)
+    return _lib_checked
+
+
+def _load(path: str) -> C.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m bit_moe_amd.build`")
+    L = C.CDLL(path)
     P, I, I64, SZ = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
     LP = C.POINTER(LayerStruct)
     sig = {
@@ -97,7 +114,6 @@ def lib() -> C.CDLL:
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
         fn.argtypes, fn.restype = args, res
-    _lib = L
     return L
 
 
@@ -224,8 +240,10 @@ def topk(logits, k: int, ids=None, w=None, stream=None):
     return ids, w
 
 
-def bucket(ids, E: int, stream=None):
-    """Returns (counts, offsets, perm, active, n_active) int32 device tensors."""
+def bucket(ids, E: int, stream=None, library=None):
+    """Returns (counts, offsets, perm, active, n_active) int32 device tensors
+    (library: lib() by default, or lib_checked())."""
+    L = library or lib()
     torch = _torch()
     T, k = ids.shape
     dev = ids.device
@@ -234,10 +252,10 @@ def bucket(ids, E: int, stream=None):
     perm = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
     active = torch.empty(E, dtype=torch.int32, device=dev)
     n_active = torch.empty(1, dtype=torch.int32, device=dev)
-    ws = _workspace(lib().moe_bucket_workspace_bytes(T, k, E), dev)
+    ws = _workspace(L.moe_bucket_workspace_bytes(T, k, E), dev)
     _dev_check(ids)
-    _check(lib().moe_bucket(_ptr(ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(active),
-                            _ptr(n_active), _ptr(ws), ws.numel(), _stream(stream)), "moe_bucket")
+    _check(L.moe_bucket(_ptr(ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(active),
+                        _ptr(n_active), _ptr(ws), ws.numel(), _stream(stream)), "moe_bucket")
     return counts, offsets, perm[:T * k], active, n_active
 
 
@@ -254,10 +272,10 @@ def _ffn(fn, name, mode, layer: Layer, x, ids, w, y=None, ws=None, stream=None):
     return y
 
 
-def ffn_decode(layer, x, ids, w, y=None, ws=None, stream=None):
+def ffn_decode(layer, x, ids, w, y=None, ws=None, stream=None, library=None):
     """Decode FFN (moe_ffn_decode); each row of ids must hold k distinct
-    experts, as a top-k gives."""
-    return _ffn(lib().moe_ffn_decode, "moe_ffn_decode", DECODE, layer, x, ids, w, y, ws, stream)
+    experts, as a top-k gives (library: lib() by default, or lib_checked())."""
+    return _ffn((library or lib()).moe_ffn_decode, "moe_ffn_decode", DECODE, layer, x, ids, w, y, ws, stream)
 
 
 def forward_decode(layer, x, ids=None, w=None, y=None, ws=None, stream=None):
@@ -297,8 +315,8 @@ def forward_decode_noalloc(layer, x, ids=None, w=None, y=None, stream=None):
     return y, ids, w
 
 
-def ffn_prefill(layer, x, ids, w, y=None, ws=None, stream=None):
-    return _ffn(lib().moe_ffn_prefill, "moe_ffn_prefill", PREFILL, layer, x, ids, w, y, ws, stream)
+def ffn_prefill(layer, x, ids, w, y=None, ws=None, stream=None, library=None):
+    return _ffn((library or lib()).moe_ffn_prefill, "moe_ffn_prefill", PREFILL, layer, x, ids, w, y, ws, stream)
 
 
 def dequant_iq2x(blocks, grid, out_dtype=F32, stream=None):

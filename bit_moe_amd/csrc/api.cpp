@@ -65,6 +65,7 @@ struct FfnWs {
     bm_host::DecodeBufs d{};
     void *route_ws = nullptr;      // moe_forward_decode, batches routed by moe_route
     size_t route_ws_bytes = 0;
+    int32_t *ids_flag = nullptr;   // the checked build's count of caller ids outside [0, E)
     size_t bytes = 0;
 };
 
@@ -73,6 +74,7 @@ FfnWs carve_ffn(const bitmoe_layer *L, int T, int mode, void *ws) {
     Carve c(ws);
     const int64_t n = (int64_t)T * L->k;
     const bool shared = L->shared_gate != nullptr;
+    f.ids_flag = reinterpret_cast<int32_t *>(c.take<char>(bm_host::kIdsFlagBytes));
     f.b.counts = c.take<int32_t>(L->E);
     f.b.offsets = c.take<int32_t>(L->E + 1);
     f.b.perm = c.take<int32_t>(std::max<int64_t>(n, 1));
@@ -194,7 +196,9 @@ const char *moe_strerror(int code) {
     }
 }
 
-const char *moe_version(void) { return "bitmoe 0.1.0 (gfx950)"; }
+const char *moe_version(void) {
+    return BITMOE_CHECK_IDS ? "bitmoe 0.1.0 (gfx950, caller routing ids checked)" : "bitmoe 0.1.0 (gfx950)";
+}
 
 size_t moe_route_workspace_bytes(const bitmoe_layer *L, int T, int x_dtype) {
     if (check_layer_shape(L) || T <= 0) return 0;
@@ -243,7 +247,7 @@ int moe_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w, v
 
 size_t moe_bucket_workspace_bytes(int T, int k, int E) {
     if (T <= 0 || k <= 0 || E <= 0) return 0;
-    return bm_host::bucket_scratch_bytes(T, k, E);
+    return bm_host::kIdsFlagBytes + bm_host::bucket_scratch_bytes(T, k, E);
 }
 
 int moe_bucket(const int32_t *ids, int T, int k, int E, int32_t *counts, int32_t *offsets,
@@ -253,13 +257,15 @@ int moe_bucket(const int32_t *ids, int T, int k, int E, int32_t *counts, int32_t
     if (k > 16 || k > E || E > 1024 || T > kMaxT) return BITMOE_EUNSUPPORTED;
     if (T == 0) return BITMOE_OK;
     if (!ids || !counts || !offsets || !perm || !active || !n_active) return BITMOE_EINVAL;
-    int rc = check_ws(ws, ws_bytes, bm_host::bucket_scratch_bytes(T, k, E));
+    int rc = check_ws(ws, ws_bytes, bm_host::kIdsFlagBytes + bm_host::bucket_scratch_bytes(T, k, E));
     if (rc) return rc;
     bm_host::Buckets b{};
     b.counts = counts; b.offsets = offsets; b.perm = perm; b.active = active;
     b.n_active = n_active; b.tiles = nullptr; b.n_tiles = nullptr;
-    b.scratch = static_cast<int32_t *>(ws); b.tile_rows = 1;
-    return bm_host::launch_bucket(ids, T, k, E, b, as_stream(stream));
+    b.scratch = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + bm_host::kIdsFlagBytes); b.tile_rows = 1;
+    hipStream_t s = as_stream(stream);
+    if ((rc = bm_host::launch_check_ids(ids, (int64_t)T * k, E, static_cast<int32_t *>(ws), s))) return rc;
+    return bm_host::launch_bucket(ids, T, k, E, b, s);
 }
 
 size_t moe_workspace_bytes(const bitmoe_layer *L, int T, int mode) {
@@ -277,8 +283,9 @@ int moe_ffn_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, con
     b.ids = const_cast<int32_t *>(ids);
     b.w = const_cast<float *>(w);
     b.y = y;
-    return bm_host::launch_decode(L, x, x_dtype, T, bm_host::decode_plan(L, T, false), b,
-                                  as_stream(stream));
+    hipStream_t s = as_stream(stream);
+    if ((rc = bm_host::launch_check_ids(ids, (int64_t)T * L->k, L->E, f.ids_flag, s))) return rc;
+    return bm_host::launch_decode(L, x, x_dtype, T, bm_host::decode_plan(L, T, false), b, s);
 }
 
 int moe_forward_decode(const bitmoe_layer *L, const void *x, int x_dtype, int T, int32_t *ids,
@@ -292,6 +299,7 @@ int moe_ffn_prefill(const bitmoe_layer *L, const void *x, int x_dtype, int T, co
     int rc = ffn_common(L, x, x_dtype, T, ids, w, y, ws, ws_bytes, BITMOE_PREFILL, &f);
     if (rc || T == 0) return rc;
     hipStream_t s = as_stream(stream);
+    if ((rc = bm_host::launch_check_ids(ids, (int64_t)T * L->k, L->E, f.ids_flag, s))) return rc;
     if ((rc = bm_host::launch_bucket(ids, T, L->k, L->E, f.b, s))) return rc;
     return bm_host::launch_prefill_ffn(L, x, x_dtype, T, w, y, f.b, f.max_tiles, f.p, s);
 }

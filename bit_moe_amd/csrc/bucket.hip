@@ -26,6 +26,19 @@ k_bucket_small(const int32_t *__restrict__ ids, int n, int E, int32_t *__restric
                  swave);
 }
 
+// ---- the checked build's count of ids outside [0, E) ------------------------
+// One workgroup, a fixed order of partial sums: flag = the count (0: all in
+// range).
+__global__ void __launch_bounds__(kBT)
+k_check_ids(const int32_t *__restrict__ ids, int64_t n, int E, int32_t *__restrict__ flag) {
+    __shared__ int swave[kBW + 1];
+    int bad = 0;
+    for (int64_t p = threadIdx.x; p < n; p += kBT) bad += (ids[p] < 0 || ids[p] >= E) ? 1 : 0;
+    int tot;
+    (void)block_exscan(bad, swave, &tot);
+    if (threadIdx.x == 0) *flag = tot;
+}
+
 // ---- multi-block path -------------------------------------------------------
 __global__ void __launch_bounds__(kBT)
 k_bucket_hist(const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict__ bhist) {
@@ -34,7 +47,7 @@ k_bucket_hist(const int32_t *__restrict__ ids, int n, int E, int32_t *__restrict
     for (int e = tid; e < E; e += kBT) sh[e] = 0;
     __syncthreads();
     int p = blockIdx.x * kBT + tid;
-    if (p < n) atomicAdd(&sh[ids[p]], 1);
+    if (p < n) atomicAdd(&sh[user_id(ids[p], E)], 1);
     __syncthreads();
     for (int e = tid; e < E; e += kBT) bhist[(int64_t)blockIdx.x * E + e] = sh[e];
 }
@@ -93,6 +106,13 @@ static void allow_lds(K kernel, size_t bytes) {
     if (bytes > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+int launch_check_ids(const int32_t *ids, int64_t n, int E, int32_t *flag, hipStream_t s) {
+    if (!BITMOE_CHECK_IDS || n == 0) return BITMOE_OK;
+    k_check_ids<<<1, kBT, 0, s>>>(ids, n, E, flag);
+    BM_LAUNCH_CHECK();
+    return BITMOE_OK;
 }
 
 int launch_bucket(const int32_t *ids, int T, int k, int E, const Buckets &b, hipStream_t s) {

@@ -832,7 +832,7 @@ BM_DEV void route_token_wave0(int mode, int E, int k, const float *__restrict__ 
             id = lane < k ? r.ids[lane] : 0;
         }
     } else {
-        id = lane < k ? ids[lane] : 0;
+        id = lane < k ? user_id(ids[lane], E) : 0;
     }
     // rank by (expert, position): a permutation of 0..k-1 even if a row
     // repeats an expert (which a top-k never does), so every slot is set

@@ -14,6 +14,16 @@ BM_DEV float dpp_max(float v) {
     const int o = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF, false);
     return fmaxf(v, __int_as_float(o));
 }
+// Routing ids given by the caller are trusted: values in [0, E).  A build
+// with BITMOE_CHECK_IDS = 1 counts the others before the FFN (k_check_ids,
+// into the first int32 of the call's workspace) and reads every id clamped
+// into range, so that a bad id can only give a wrong result, never an access
+// out of bounds.
+#ifndef BITMOE_CHECK_IDS
+#define BITMOE_CHECK_IDS 0
+#endif
+BM_DEV int user_id(int v, int E) { return BITMOE_CHECK_IDS ? min(max(v, 0), E - 1) : v; }
+
 // Max of |v| over each half-wave (row shifts, then row 0 -> 1 and 2 -> 3),
 // complete in lanes 31 and 63.  Non-negative floats order as their bit
 // patterns (a NaN's above +inf), so the steps are integer maxima, each one
@@ -247,7 +257,7 @@ BM_DEV void scatter_chunk(const int32_t *__restrict__ ids, int n, int E, int p0,
                           int *wcnt, int32_t *__restrict__ perm, int kbits) {
     int tid = threadIdx.x, w = tid >> 6;
     int p = p0 + tid;
-    int key = p < n ? ids[p] : E;
+    int key = p < n ? user_id(ids[p], E) : E;
     uint64_t match;
     int rank;
     wave_match(key, kbits, match, rank);
@@ -311,7 +321,7 @@ BM_DEV void bucket_wave_rank(const int32_t *__restrict__ ids, int n, int E, int3
 #pragma unroll
     for (int m = 0; m < 2; m++) {
         const int p = lane + 64 * m;
-        key[m] = p < n ? ids[p] : E;
+        key[m] = p < n ? user_id(ids[p], E) : E;
     }
     for (int m = 0; m < M; m++) {
         int rank = 0;
@@ -413,7 +423,7 @@ BM_DEV void bucket_block(const int32_t *__restrict__ ids, int n, int E, int32_t 
     for (int e = tid; e < E; e += kBT) scount[e] = 0;
     for (int i = tid; i < kBW * E; i += kBT) wcnt[i] = 0;
     __syncthreads();
-    for (int p = tid; p < n; p += kBT) atomicAdd(&scount[ids[p]], 1);
+    for (int p = tid; p < n; p += kBT) atomicAdd(&scount[user_id(ids[p], E)], 1);
     __syncthreads();
     {
         const int c = tid < E ? scount[tid] : 0;

@@ -78,6 +78,13 @@ struct Buckets {
 };
 size_t bucket_scratch_bytes(int T, int k, int E);
 int launch_bucket(const int32_t *ids, int T, int k, int E, const Buckets &b, hipStream_t s);
+// the checked build (BITMOE_CHECK_IDS): *flag = the count of ids outside
+// [0, E); a no-op otherwise
+int launch_check_ids(const int32_t *ids, int64_t n, int E, int32_t *flag, hipStream_t s);
+constexpr size_t kIdsFlagBytes = 256;        // at the start of the workspaces that take caller ids
+#ifndef BITMOE_CHECK_IDS
+#define BITMOE_CHECK_IDS 0
+#endif
 
 // decode FFN (three launches for decode batches, see decode.hip)
 struct DecodePlan {

@@ -41,6 +41,15 @@
  *    several host threads take turns at that stream (a lock held while the
  *    call queues its work), so their side-stream halves run one after
  *    another.
+ *  - Routing ids given by the caller (moe_bucket, moe_ffn_decode,
+ *    moe_ffn_prefill) must lie in [0, E); this library trusts them.  The
+ *    same sources built with BITMOE_CHECK_IDS=1 (libbitmoe_checked.so,
+ *    built beside libbitmoe.so; its moe_version() says so) check them on
+ *    the device: those calls first write the count of ids outside [0, E)
+ *    into the int32 at the start of their workspace (0: all valid), and read
+ *    every id clamped into range, so that a bad id gives a wrong result but
+ *    no access out of bounds.  The first 256 bytes of those workspaces are
+ *    reserved for that count in both builds.
  *
  * Weight formats
  *  CANONICAL blocks (the interchange format, GGML order):
@@ -208,7 +217,7 @@ int moe_topk(const float *logits, int T, int E, int k, int32_t *ids,
  * once per call: decode is bound by memory bandwidth ("Faire tenir un MoE de
  * 284B dans un portable de 128 Go", section "Un pre-remplissage a 790 t/s
  * revele le veritable goulot d'etranglement").
- * ids int32 [T][k] with values in [0,E) (trusted).
+ * ids int32 [T][k] with values in [0,E) (trusted; checked builds: above).
  * counts int32 [E]; offsets int32 [E+1] exclusive prefix sum of counts;
  * perm int32 [T*k]: pair indices p = t*k + j grouped by expert, ascending p
  * within each expert; active int32 [E]: experts with counts > 0 ascending,
@@ -238,7 +247,8 @@ size_t moe_workspace_bytes(const bitmoe_layer *L, int T, int mode);
  *         y[t] = sum_j w[t][j] * D_e(silu(G_e x_t) * U_e x_t)
  *                     (+ D_s(silu(G_s x_t) * U_s x_t) when the layer has a
  *                     shared expert), e = ids[t][j], silu(z) = z/(1+e^-z).
- * x [T][H] (x_dtype), ids int32 [T][k] (values in [0,E), trusted; each row
+ * x [T][H] (x_dtype), ids int32 [T][k] (values in [0,E), trusted or
+ * checked as above; each row
  * k distinct experts, as a top-k gives: moe_ffn_decode does not support a
  * row that repeats an expert), w float32 [T][k], y float32 [T][H]
  * (overwritten).  ws: device workspace of at least

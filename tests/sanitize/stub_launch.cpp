@@ -22,11 +22,13 @@ int launch_router_mfma(const bitmoe_layer *, const void *, int, float *, int32_t
 }
 int launch_topk(const float *, int, int, int, int32_t *, float *, hipStream_t) { return BITMOE_EHIP; }
 int launch_bucket(const int32_t *, int, int, int, const Buckets &, hipStream_t) { return BITMOE_EHIP; }
+// (a release build queues nothing here)
+int launch_check_ids(const int32_t *, int64_t, int, int32_t *, hipStream_t) { return BITMOE_OK; }
 int launch_decode(const bitmoe_layer *, const void *, int, int, const DecodePlan &, const DecodeBufs &, hipStream_t) {
     return BITMOE_EHIP;
 }
 int launch_prefill_routed(const bitmoe_layer *, const void *, int, int, const Buckets &, int, const PrefillBufs &,
-                          hipStream_t) {
+                          hipStream_t, int) {
     return BITMOE_EHIP;
 }
 int launch_prefill_ffn(const bitmoe_layer *, const void *, int, int, const float *, float *, const Buckets &, int,

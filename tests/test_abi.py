@@ -31,6 +31,24 @@ def test_library_exports_every_declared_symbol():
     assert "gfx950" in bm.version()
 
 
+def test_checked_ids_build_exports_the_same_symbols_and_workspaces():
+    """libbitmoe_checked.so (BITMOE_CHECK_IDS=1): the same entry points and
+    workspace sizes, the first 256 bytes of the bucketing and FFN workspaces
+    holding the count of bad ids."""
+    C = bm.lib_checked()
+    for name in _header_functions():
+        assert hasattr(C, name), name
+    assert "checked" in C.moe_version().decode() and "checked" not in bm.version()
+    L = bm.lib()
+    for T, k, E in ((1, 8, 256), (16, 8, 256), (8192, 8, 256)):
+        assert C.moe_bucket_workspace_bytes(T, k, E) == L.moe_bucket_workspace_bytes(T, k, E)
+    # the count's 256 bytes come before the bucketing scratch
+    assert L.moe_bucket_workspace_bytes(8192, 8, 256) >= 256 + 8192 * 8 // 256
+    lay = _layer()
+    for mode in (bm.DECODE, bm.PREFILL):
+        assert C.moe_workspace_bytes(lay, 16, mode) == L.moe_workspace_bytes(lay, 16, mode) > 256
+
+
 def test_strerror_names_every_code():
     for code in (0, -1, -2, -3, -4):
         assert bm.strerror(code)
