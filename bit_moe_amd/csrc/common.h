@@ -44,6 +44,67 @@ BM_DEV float dot2_f16(uint32_t a, uint32_t b, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
 }
 
+BM_DEV uint32_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// ---- fp16 activations for the matrix-core kernels ------------------------
+// Each token row goes to fp16 times 2^-e, one power of two e per token, so
+// that the row's largest |x| lands in [2^14, 2^15): any bf16/fp32 range then
+// maps onto fp16's normal range (0, inf and NaN give e = 0).
+BM_DEV int pf_exponent(float m) {
+    const uint32_t u = __float_as_uint(m);
+    if (!(m > 0.f) || u >= 0x7F800000u) return 0;
+    const int ex = (int)(u >> 23) - 127;
+    return max(ex - 14, -100);
+}
+struct Xp8 { float v[8]; };
+// 8 consecutive activations at element offset i (bf16 or fp32), as fp32
+template <int XBF16>
+BM_DEV Xp8 xprep_load8(const void *x, int64_t i) {
+    Xp8 r;
+    if (XBF16) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + i);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) { r.v[2 * j] = bf16_lo(w[j]); r.v[2 * j + 1] = bf16_hi(w[j]); }
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + i);
+        const float4 a = p[0], b = p[1];
+        r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+        r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
+    }
+    return r;
+}
+BM_DEV float xprep_absmax8(const Xp8 &a) {
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; j++) m = fmaxf(m, fabsf(a.v[j]));
+    return m;
+}
+BM_DEV void xprep_store8(uint16_t *dst, const Xp8 &a, int e) {
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) o[j] = f16_bits(ldexpf(a.v[2 * j], -e)) | (f16_bits(ldexpf(a.v[2 * j + 1], -e)) << 16);
+    *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+// One token row on one workgroup (H a multiple of 8; sm holds a float per
+// wave).  Every thread calls it: it holds a block barrier.
+template <int XBF16>
+BM_DEV void xprep_token_block(int H, const void *x, int t, uint16_t *x16, float *xsc, float *sm) {
+    const int tid = threadIdx.x, nt = blockDim.x, nw = nt / kWave;
+    const int64_t row = (int64_t)t * H;
+    float m = 0.f;
+    for (int c = tid * 8; c < H; c += nt * 8) m = fmaxf(m, xprep_absmax8(xprep_load8<XBF16>(x, row + c)));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    if ((tid & (kWave - 1)) == 0) sm[tid / kWave] = m;
+    __syncthreads();
+    m = 0.f;
+    for (int w = 0; w < nw; w++) m = fmaxf(m, sm[w]);
+    const int e = pf_exponent(m);
+    if (tid == 0) xsc[t] = ldexpf(1.f, e);
+    for (int c = tid * 8; c < H; c += nt * 8) xprep_store8(x16 + row + c, xprep_load8<XBF16>(x, row + c), e);
+}
+
 // ---- MXFP4 (OCP Microscaling: E2M1 elements, one E8M0 scale per 32) -----
 // v_cvt_scalef32_pk_{bf16,f16,f32}_fp4: byte SEL of w holds two E2M1
 // elements, the first in its low nibble; the result holds element * scale

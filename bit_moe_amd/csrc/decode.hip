@@ -303,9 +303,74 @@ BM_DEV void shared_gateup_mfma(int H, int I, int T, int t0, int P, int c0, int c
     }
 }
 
-// Workgroup roles, in blockIdx order: router rows (n_rwg, one per wave) |
-// shared-expert gate/up partial sums per (panel, K chunk).  Workgroup 0
-// also clears the down launch's per-panel combine counters.  Launched with
+// ---------------------------------------------------------------------------
+// Bucketing of a decode batch's n <= kWaveBucketMax pairs on wave 0 of the
+// calling workgroup (every thread calls it: it holds block barriers; sk is
+// kWaveBucketMax ints of LDS): counts, offsets, perm, the active list, with
+// tiles the row tiles of the experts chosen by several tokens, with single
+// the experts chosen by one token, compacted as {expert, pair row, 1, token}
+// (their gate/up items are claimed one at a time).
+// ---------------------------------------------------------------------------
+BM_DEV void bucket_decode_wave(const int32_t *__restrict__ ids, int n, int k, int E, int32_t *__restrict__ counts,
+                               int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+                               int32_t *__restrict__ active, int32_t *__restrict__ n_active,
+                               int32_t *__restrict__ tiles, int32_t *__restrict__ n_tiles,
+                               int4 *__restrict__ single, int32_t *__restrict__ n_single, int *sk) {
+    const int wv = threadIdx.x >> 6;
+    if (wv == 0) bucket_wave_rank(ids, n, E, perm, sk);
+    __syncthreads();
+    if (wv == 0) bucket_wave_lists(n, sk, counts, offsets, active, n_active);
+    if (wv == 0 && tiles) bucket_wave_multi_tiles(n, sk, tiles, n_tiles);
+    if (!single) return;
+    __syncthreads();
+    if (wv == 0) {
+        const int lane = lane_id(), na = *n_active;
+        const uint64_t below = (1ull << lane) - 1ull;
+        int4 v[2];
+        bool one[2];
+#pragma unroll
+        for (int m = 0; m < 2; m++) {
+            const int sl = lane + 64 * m;
+            one[m] = false;
+            if (sl < na) {
+                const int e = active[sl], off = offsets[e];
+                one[m] = counts[e] == 1;
+                v[m] = make_int4(e, off, 1, perm[off] / k);
+            }
+        }
+        const uint64_t B0 = __ballot(one[0]), B1 = __ballot(one[1]);
+        if (one[0]) single[__popcll(B0 & below)] = v[0];
+        if (one[1]) single[__popcll(B0) + __popcll(B1 & below)] = v[1];
+        if (lane == 0) *n_single = __popcll(B0) + __popcll(B1);
+    }
+}
+
+// Decode batches: work that the front launch's first n_wg workgroups take
+// before its other roles.  With ids (given by the caller) the first one
+// buckets them on its wave 0 (no mid launch); with x16 workgroup t < T
+// prepares token t's fp16 activations for the prefill kernels.
+struct FrontPrep {
+    int n_wg, k;
+    const int32_t *ids;
+    bm_host::Buckets bk;        // tiles null unless the prefill kernels run
+    int4 *single;               // null unless the prefill kernels run
+    int32_t *n_single;
+    uint16_t *x16;
+    float *xsc;
+};
+template <int XBF16>
+BM_DEV void front_prep(int H, int T, int E, const void *x, const FrontPrep &pr, int b, float *lds) {
+    if (b == 0 && pr.ids)
+        bucket_decode_wave(pr.ids, T * pr.k, pr.k, E, pr.bk.counts, pr.bk.offsets, pr.bk.perm, pr.bk.active,
+                           pr.bk.n_active, pr.bk.tiles, pr.bk.n_tiles, pr.single, pr.n_single,
+                           reinterpret_cast<int *>(lds));
+    if (pr.x16 && b < T) xprep_token_block<XBF16>(H, x, b, pr.x16, pr.xsc, lds + kWaveBucketMax);
+}
+
+// Workgroup roles, in blockIdx order: preparation (pr.n_wg, above) | router
+// rows (n_rwg, one per wave) | shared-expert gate/up partial sums per
+// (panel, K chunk).  Workgroup 0 also clears the down launch's per-panel
+// combine counters.  Launched with
 // kW waves, or (no shared chunks) fewer, so that the router rows spread
 // over more compute units.
 template <int XBF16>
@@ -313,14 +378,20 @@ __global__ void __launch_bounds__(kW * 64) __attribute__((amdgpu_waves_per_eu(4)
 k_dec_front(int H, int I, int E, int T, int n_rwg, int kc_sg, const uint16_t *__restrict__ wr,
             const void *__restrict__ x, float *__restrict__ logits, int32_t *__restrict__ ycount,
             int32_t *__restrict__ gctr, const uint4 *__restrict__ sg, const uint4 *__restrict__ su,
-            float *__restrict__ sgp) {
+            float *__restrict__ sgp, FrontPrep pr) {
     __shared__ float red[kW * kNT * 2 * 64];
+    static_assert(kW * kNT * 2 * 64 >= kWaveBucketMax + kW, "front prep LDS");
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nw = blockDim.x >> 6;
     int b = blockIdx.x;
     if (b == 0) {
         for (int p = threadIdx.x; p < H / 64; p += blockDim.x) ycount[p] = 0;
         if (gctr && threadIdx.x == 0) *gctr = 0;
     }
+    if (b < pr.n_wg) {
+        front_prep<XBF16>(H, T, E, x, pr, b, red);
+        return;
+    }
+    b -= pr.n_wg;
     if (b < n_rwg) {
         const int e = b * nw + wv;
         if (e >= E) return;
@@ -386,34 +457,8 @@ k_dec_mid(int E, int k, int T, const float *__restrict__ logits, int32_t *__rest
     if (!do_bucket) return;
     const int n = T * k;
     if (n <= kWaveBucketMax) {        // decode batches: one wave, no block scans
-        if (wv == 0) bucket_wave_rank(ids, n, E, perm, smem);
-        __syncthreads();
-        if (wv == 0) bucket_wave_lists(n, smem, counts, offsets, active, n_active);
-        if (wv == 0 && tiles) bucket_wave_multi_tiles(n, smem, tiles, n_tiles);
-        if (!single) return;
-        // the experts chosen by one token, compacted: {expert, pair row, 1,
-        // token} (their gate/up items are claimed one at a time)
-        __syncthreads();
-        if (wv == 0) {
-            const int lane = lane_id(), na = *n_active;
-            const uint64_t below = (1ull << lane) - 1ull;
-            int4 v[2];
-            bool one[2];
-#pragma unroll
-            for (int m = 0; m < 2; m++) {
-                const int sl = lane + 64 * m;
-                one[m] = false;
-                if (sl < na) {
-                    const int e = active[sl], off = offsets[e];
-                    one[m] = counts[e] == 1;
-                    v[m] = make_int4(e, off, 1, perm[off] / k);
-                }
-            }
-            const uint64_t B0 = __ballot(one[0]), B1 = __ballot(one[1]);
-            if (one[0]) single[__popcll(B0 & below)] = v[0];
-            if (one[1]) single[__popcll(B0) + __popcll(B1 & below)] = v[1];
-            if (lane == 0) *n_single = __popcll(B0) + __popcll(B1);
-        }
+        bucket_decode_wave(ids, n, k, E, counts, offsets, perm, active, n_active, tiles, n_tiles, single, n_single,
+                           smem);
         return;
     }
     bucket_block(ids, n, E, counts, offsets, perm, active, n_active, nullptr, nullptr, 1, smem, swave);
@@ -1726,16 +1771,24 @@ static int launch_decode_fmt(const bitmoe_layer *L, const void *x, int x_dtype, 
     const bool shared = L->shared_gate != nullptr;
     const bool bf = x_dtype == BITMOE_BF16;
     if (p.kc_sd > kMaxChunks || p.kc_sg > kMaxChunks) return BITMOE_EUNSUPPORTED;
-    // front: router rows, shared gate/up (at least one workgroup: it clears
-    // the combine counters)
-    const int n_front = std::max(1, p.n_rwg + (shared ? (I / 64) * p.kc_sg : 0));
+    // front: preparation, router rows, shared gate/up (at least one
+    // workgroup: it clears the combine counters)
+    const int n_front = std::max(1, p.prep_wg + p.n_rwg + (shared ? (I / 64) * p.kc_sg : 0));
     if (p.front_waves < 1 || p.front_waves > kW || (p.kc_sg && p.front_waves != kW)) return BITMOE_EINVAL;
     if (p.sg_rows && (T != 1 || p.sg_rows * k != 64 || p.slots != k || !shared)) return BITMOE_EINVAL;
+    if ((p.bucket_in_front && (T * k > kWaveBucketMax || p.n_rwg)) ||
+        (p.xprep_in_front && (!p.pf_tiles || FMT != BITMOE_FORMAT_2BIT || p.prep_wg != T)) ||
+        p.prep_wg < (p.bucket_in_front ? 1 : 0))
+        return BITMOE_EINVAL;
     {
+        Buckets bk = b.bk;
+        if (!p.pf_tiles) bk.tiles = nullptr;
+        const FrontPrep pr{p.prep_wg, k, p.bucket_in_front ? b.ids : nullptr, bk, p.pf_tiles ? b.single : nullptr,
+                           b.n_single, p.xprep_in_front ? b.pf.x16 : nullptr, b.pf.xsc};
         auto kf = bf ? k_dec_front<1> : k_dec_front<0>;
         kf<<<n_front, p.front_waves * 64, 0, s>>>(H, I, E, T, p.n_rwg, p.kc_sg, (const uint16_t *)L->router_w, x, b.logits,
                                        b.ycount, p.pf_tiles ? b.gctr : nullptr, (const uint4 *)L->shared_gate,
-                                       (const uint4 *)L->shared_up, b.sgp);
+                                       (const uint4 *)L->shared_up, b.sgp, pr);
         BM_LAUNCH_CHECK();
     }
     // mid: top-k and bucketing of batches of more than one token
@@ -1785,7 +1838,8 @@ static int launch_decode_fmt(const bitmoe_layer *L, const void *x, int x_dtype, 
     // stream, and the single-token experts' gate/up and down beside them on
     // a stream of the library's own that forks after the routing and joins
     // before the combine launch.  The prefill kernels' activation preparation
-    // needs no routing and goes before the fork, and the prefill kernels are
+    // needs no routing and goes before the fork (in the front launch up to
+    // kFrontPrepMaxT tokens of 2-bit experts), and the prefill kernels are
     // enqueued before the other stream's, so that the device does not wait
     // for the host's fork.  They take their compute units first; the gate/up
     // workgroups claim their items one at a time, so those that start late
@@ -1793,7 +1847,7 @@ static int launch_decode_fmt(const bitmoe_layer *L, const void *x, int x_dtype, 
     // when several host threads share the stream.  Without the fork (p.fork
     // false) the same launches run one after the other on the caller's stream.
     const bool split = p.pf_tiles > 0;
-    if (split) {
+    if (split && !p.xprep_in_front) {
         const int rc = launch_prefill_routed(L, x, x_dtype, T, b.bk, p.pf_tiles, b.pf, s, kPfPrep);
         if (rc) return rc;
     }

@@ -26,6 +26,8 @@ constexpr int kFusedRouterMaxT = 16;      // decode: router rows fused into the 
 // decode
 constexpr int kFrontWaves = 16;           // waves per front workgroup
 constexpr int kFrontRouterWaves = 4;      // the same when it only computes router rows
+constexpr int kFrontPrepMaxT = 32;        // decode batches up to this size prepare the prefill
+                                          // kernels' activations in the front launch
 constexpr int kMaxChunks = 8;             // K chunks of the shared expert, at most
 constexpr int kSharedChunkCols = 512;     // I columns of one shared-down K chunk, at most
 // prefill
@@ -97,6 +99,9 @@ struct DecodePlan {
     int kc_sd = 0;          // K chunks of the shared down
     bool small = false;     // T*k <= kWaveBucketMax: one-wave bucketing
     bool need_mid = true;   // top-k and/or bucketing in a launch of their own
+    int prep_wg = 0;        // preparation workgroups at the head of the front launch:
+    bool bucket_in_front = false;   // the caller's ids bucketed there (no mid launch)
+    bool xprep_in_front = false;    // the prefill kernels' fp16 activations, one workgroup per token
     int pf_tiles = 0;       // > 0: experts chosen by several tokens take the prefill
                             // kernels, one row tile each (at most pf_tiles tiles)
     bool fork = true;       // with pf_tiles: may fork onto the library's side stream

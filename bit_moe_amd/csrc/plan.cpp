@@ -52,15 +52,8 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
                     ? 64 / L->k : 0;
     p.front_waves = (T == 1 && (p.sg_rows || !shared)) ? kFrontRouterWaves : kFrontWaves;
     p.n_rwg = with_router ? (L->E + p.front_waves - 1) / p.front_waves : 0;
-    // otherwise the shared gate/up's K chunks: as many as fit the compute
-    // units beside the router workgroups (one front workgroup per CU), at most 8
-    p.kc_sg = shared && !p.sg_rows ? std::max(1, std::min(kMaxChunks, (cu_count() - p.n_rwg) / (L->I / 64))) : 0;
     p.kc_sd = shared ? std::max(1, (L->I + kSharedChunkCols - 1) / kSharedChunkCols) : 0;
     p.small = (int64_t)T * L->k <= kWaveBucketMax;
-    // one token: every gate/up workgroup routes it itself; more tokens: one
-    // routing launch, so that the gate/up workgroups can each take several
-    // (expert, panel) items
-    p.need_mid = !p.small || T > 1;
     // several tokens (one row tile per expert): experts chosen by more than
     // one token go through the prefill kernels, which decode each weight once
     // for all of its tokens on the matrix cores, beside the single-token
@@ -69,6 +62,22 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     // tokens) is faster than the fork, the join and the extra launches.
     p.pf_tiles = (p.small && T >= kSplitMinT && T <= kPfRows) ? (int)std::min<int64_t>(L->E, (int64_t)T * L->k / 2)
                                                               : 0;
+    // one token: every gate/up workgroup routes it itself.  More tokens: the
+    // gate/up workgroups each take several (expert, panel) items from one
+    // bucketing, done by the front launch's first workgroup when the caller
+    // gives the ids, else (top-k of the router logits first) by a mid launch.
+    // The prefill kernels' fp16 activations (2-bit experts) are prepared by
+    // front workgroups too, one per token, up to kFrontPrepMaxT tokens.
+    p.bucket_in_front = !with_router && T > 1 && p.small;
+    p.xprep_in_front = p.pf_tiles > 0 && L->format == BITMOE_FORMAT_2BIT && T <= kFrontPrepMaxT;
+    p.prep_wg = p.xprep_in_front ? T : p.bucket_in_front ? 1 : 0;
+    p.need_mid = (!p.small || T > 1) && !p.bucket_in_front;
+    // otherwise the shared gate/up's K chunks: as many as fit the compute
+    // units beside the other front workgroups (one front workgroup per CU), at
+    // most 8
+    p.kc_sg = shared && !p.sg_rows
+                  ? std::max(1, std::min(kMaxChunks, (cu_count() - p.n_rwg - p.prep_wg) / (L->I / 64)))
+                  : 0;
     return p;
 }
 

@@ -89,17 +89,8 @@ static_assert(kPfWScale == (float)(1 << kPfWShift) && kPfDnWScale == (float)(1 <
 
 BM_DEV uint32_t h2u(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 BM_DEV f16x2 u2h(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
-BM_DEV uint32_t f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 BM_DEV uint32_t f16_pair(float f) { const uint32_t b = f16_bits(f); return b | (b << 16); }
 BM_DEV uint32_t pk_mul(uint32_t a, uint32_t b) { return h2u(u2h(a) * u2h(b)); }
-
-// Power-of-two exponent e with m * 2^-e in [2^14, 2^15) (0 for 0, inf, NaN).
-BM_DEV int pf_exponent(float m) {
-    const uint32_t u = __float_as_uint(m);
-    if (!(m > 0.f) || u >= 0x7F800000u) return 0;
-    const int ex = (int)(u >> 23) - 127;
-    return max(ex - 14, -100);
-}
 
 // fp16 bits of 2^d, d <= 0 (subnormal below 2^-14, zero below 2^-24)
 BM_DEV uint32_t f16_pow2(int d) {
@@ -118,53 +109,13 @@ int pf_grid(int max_tiles, int nN) { return (max_tiles + kPfXcds - 1) / kPfXcds 
 
 // ---------------------------------------------------------------------------
 // activations -> fp16, one power-of-two scale per token.  grid = T, 256 thr.
+// (decode batches that take these kernels do the same in their front launch)
 // ---------------------------------------------------------------------------
 template <int XBF16>
 __global__ void __launch_bounds__(256)
 k_pf_xprep(int H, const void *__restrict__ x, uint16_t *__restrict__ x16, float *__restrict__ xsc) {
     __shared__ float sm[4];
-    const int t = blockIdx.x, tid = threadIdx.x;
-    const int64_t row = (int64_t)t * H;
-    float m = 0.f;
-    for (int c = tid * 8; c < H; c += 256 * 8) {
-        float v[8];
-        if (XBF16) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + row + c);
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
-        } else {
-            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + row + c);
-            const float4 a = p[0], b = p[1];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-    if ((tid & 63) == 0) sm[tid >> 6] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-    const int e = pf_exponent(m);
-    if (tid == 0) xsc[t] = ldexpf(1.f, e);
-    for (int c = tid * 8; c < H; c += 256 * 8) {
-        float v[8];
-        if (XBF16) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + row + c);
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int i = 0; i < 4; i++) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
-        } else {
-            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + row + c);
-            const float4 a = p[0], b = p[1];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-        }
-        uint32_t o[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) o[i] = f16_bits(ldexpf(v[2 * i], -e)) | (f16_bits(ldexpf(v[2 * i + 1], -e)) << 16);
-        *reinterpret_cast<uint4 *>(x16 + row + c) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+    xprep_token_block<XBF16>(H, x, blockIdx.x, x16, xsc, sm);
 }
 
 // ---------------------------------------------------------------------------
