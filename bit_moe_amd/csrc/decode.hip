@@ -1664,7 +1664,7 @@ k_dec_combine(int H, int k, int T, int kc_sd, const float *__restrict__ o, const
 // all of them and the shared down, in one launch (batches of 2 to 8 tokens).
 // combine = 0: the outputs are only stored (k_dec_combine sums them).
 template <int FMT, int MULTI>
-__global__ void __launch_bounds__(kWD * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 5)))
+__global__ void __launch_bounds__(kWD * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : bm_cfg::kDownWavesPerSimd)))
 k_dec_down(int H, int I, int k, int T, int n_dwg, int kc_sd, const int32_t *__restrict__ n_multi, int combine,
            const uint8_t *__restrict__ down,
            const uint4 *__restrict__ sd, const int32_t *__restrict__ counts,

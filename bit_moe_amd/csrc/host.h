@@ -30,6 +30,8 @@ constexpr int kFrontPrepMaxT = 32;        // decode batches up to this size prep
                                           // kernels' activations in the front launch
 constexpr int kMaxChunks = 8;             // K chunks of the shared expert, at most
 constexpr int kSharedChunkCols = 512;     // I columns of one shared-down K chunk, at most
+constexpr int kDownWavesPerSimd = 5;      // waves per SIMD of the one-token decode down kernel: its
+                                          // 4-wave workgroups, 5 to a compute unit
 // prefill
 constexpr int kPfRows = 96;               // rows per prefill row tile (three blocks of 32)
 constexpr int kSplitMinT = 9;             // decode batches from this many tokens run the prefill kernels

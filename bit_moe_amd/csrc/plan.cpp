@@ -53,6 +53,13 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     p.front_waves = (T == 1 && (p.sg_rows || !shared)) ? kFrontRouterWaves : kFrontWaves;
     p.n_rwg = with_router ? (L->E + p.front_waves - 1) / p.front_waves : 0;
     p.kc_sd = shared ? std::max(1, (L->I + kSharedChunkCols - 1) / kSharedChunkCols) : 0;
+    // one token: no more shared-down chunks than leave every down workgroup
+    // (k routed + the shared chunks per 64 outputs) resident at once, so that
+    // none waits for a second round at the end of the launch
+    if (shared && T == 1) {
+        const int panels = L->H / 64, fit = cu_count() * kDownWavesPerSimd - p.slots * panels;
+        p.kc_sd = std::max(1, std::min(p.kc_sd, fit / panels));
+    }
     p.small = (int64_t)T * L->k <= kWaveBucketMax;
     // several tokens (one row tile per expert): experts chosen by more than
     // one token go through the prefill kernels, which decode each weight once
