@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=8, help="layer copies rotated to defeat MALL")
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=100, help="timed prefill steps (each workload)")
+    ap.add_argument("--prefill-warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample size (seconds)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
@@ -286,9 +287,10 @@ def prefill_2k(args, lays, fmt="2bit"):
         bm.route(lay, xd, ids=ids, w=wt, ws=rws)
         bm.ffn_prefill(lay, xd, ids, wt, y=y, ws=ws)
 
-    ms, stats = time_steps(step, 2, args.prefill_steps)
-    gu_ms, gu_stats = time_kernel(step, 5, bm.TIME_GATEUP)
-    dn_ms, dn_stats = time_kernel(step, 5, bm.TIME_DOWN)
+    ms, stats = time_steps(step, args.prefill_warmup, args.prefill_steps)
+    nk = max(5, min(20, args.prefill_steps))
+    gu_ms, gu_stats = time_kernel(step, nk, bm.TIME_GATEUP)
+    dn_ms, dn_stats = time_kernel(step, nk, bm.TIME_DOWN)
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=w.E)
     pairs = w.T * w.k
     rows_issued = issued_rows(counts)
@@ -322,7 +324,7 @@ def prefill_8k_zipf(args, lays):
         bm.topk(lg, w.k, ids=ids, w=wt)
         bm.ffn_prefill(lay, xd, ids, wt, y=y, ws=ws)
 
-    ms, stats = time_steps(step, 1, max(3, args.prefill_steps // 2))
+    ms, stats = time_steps(step, args.prefill_warmup, args.prefill_steps)
     rows = np.bincount(ids.cpu().numpy().ravel(), minlength=w.E)
     flops = w.T * w.k * 3 * 2 * w.H * w.I
     return dict(ms=ms, stats=stats, flops=flops, rows_max=int(rows.max()), rows_min=int(rows.min()))
