@@ -538,7 +538,7 @@ def _pmc_per_kernel(dirname, counter):
 def source_digest():
     import hashlib
     h = hashlib.sha256()
-    for f in ("decode.hip", "common.h", "device_util.h"):
+    for f in ("decode.hip", "common.h", "device_util.h", "plan.cpp", "host.h"):
         with open(os.path.join(ROOT, "bit_moe_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
