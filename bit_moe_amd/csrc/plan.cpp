@@ -55,10 +55,11 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     p.kc_sd = shared ? std::max(1, (L->I + kSharedChunkCols - 1) / kSharedChunkCols) : 0;
     // one token: no more shared-down chunks than leave every down workgroup
     // (k routed + the shared chunks per 64 outputs) resident at once, so that
-    // none waits for a second round at the end of the launch
+    // none waits for a second round at the end of the launch (when the routed
+    // workgroups alone do not fit, the chunks stay as they are)
     if (shared && T == 1) {
-        const int panels = L->H / 64, fit = cu_count() * kDownWavesPerSimd - p.slots * panels;
-        p.kc_sd = std::max(1, std::min(p.kc_sd, fit / panels));
+        const int panels = L->H / 64, room = (cu_count() * kDownWavesPerSimd - p.slots * panels) / panels;
+        if (room >= 1) p.kc_sd = std::min(p.kc_sd, room);
     }
     p.small = (int64_t)T * L->k <= kWaveBucketMax;
     // several tokens (one row tile per expert): experts chosen by more than

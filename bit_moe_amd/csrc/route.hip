@@ -61,21 +61,33 @@ k_router_splitk(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, 
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = kbeg; k0 < kend; k0 += BK) {
-        // A: 64 rows x 64 = 512 pieces of 8 bf16 (2 per thread); B: 256 rows (8 per thread)
+    // A: 64 rows x 64 = 512 pieces of 8 bf16 (2 per thread); B: 256 rows (8
+    // per thread).  Two register sets take the pieces of the next two stages
+    // while the current stage's MFMAs run (one workgroup per CU, one wave per
+    // SIMD: the loads' latency, not the MFMAs, sets the pace); loads past the
+    // slice re-read its last stage, unused.
+    const int pr = tid >> 3, pc = (tid & 7) * 8;          // piece p: row pr + 32 p, column pc
+    const uint16_t *xa0 = X + (int64_t)min(m0 + pr, T - 1) * H + pc;
+    const uint16_t *xa1 = X + (int64_t)min(m0 + pr + 32, T - 1) * H + pc;
+    const uint16_t *wrow[8];
 #pragma unroll
-        for (int p = 0; p < 2; p++) {
-            const int piece = tid + 256 * p, r = piece >> 3, c = (piece & 7) * 8;
-            const int ra = min(m0 + r, T - 1);
-            *reinterpret_cast<uint4 *>(sa + r * LD + c) = *reinterpret_cast<const uint4 *>(X + (int64_t)ra * H + k0 + c);
-        }
-#pragma unroll
-        for (int p = 0; p < 8; p++) {
-            const int piece = tid + 256 * p, r = piece >> 3, c = (piece & 7) * 8;
-            const int rb = min(n0 + r, E - 1);
-            *reinterpret_cast<uint4 *>(sb + r * LD + c) = *reinterpret_cast<const uint4 *>(W + (int64_t)rb * H + k0 + c);
-        }
-        __syncthreads();
+    for (int p = 0; p < 8; p++) wrow[p] = W + (int64_t)min(n0 + pr + 32 * p, E - 1) * H + pc;
+    auto ld = [](const uint16_t *q, int k) { return *reinterpret_cast<const uint4 *>(q + k); };
+    auto st = [&](int r, uint4 v) { *reinterpret_cast<uint4 *>((r < 64 ? sa + r * LD : sb + (r - 64) * LD) + pc) = v; };
+#define BM_RT_LOAD(S, k)                                                                                     \
+    do {                                                                                                     \
+        const int kk_ = min(k, kend - BK);                                                                   \
+        a0##S = ld(xa0, kk_); a1##S = ld(xa1, kk_);                                                          \
+        b0##S = ld(wrow[0], kk_); b1##S = ld(wrow[1], kk_); b2##S = ld(wrow[2], kk_); b3##S = ld(wrow[3], kk_); \
+        b4##S = ld(wrow[4], kk_); b5##S = ld(wrow[5], kk_); b6##S = ld(wrow[6], kk_); b7##S = ld(wrow[7], kk_); \
+    } while (0)
+#define BM_RT_STORE(S)                                                                                       \
+    do {                                                                                                     \
+        st(pr, a0##S); st(pr + 32, a1##S);                                                                   \
+        st(64 + pr, b0##S); st(96 + pr, b1##S); st(128 + pr, b2##S); st(160 + pr, b3##S);                   \
+        st(192 + pr, b4##S); st(224 + pr, b5##S); st(256 + pr, b6##S); st(288 + pr, b7##S);                 \
+    } while (0)
+    auto compute = [&]() {
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 32) {
             const int kof = kk + 8 * (lane >> 4);
@@ -90,8 +102,28 @@ k_router_splitk(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, 
 #pragma unroll
                 for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
+    };
+    uint4 a00, a10, b00, b10, b20, b30, b40, b50, b60, b70;
+    uint4 a01, a11, b01, b11, b21, b31, b41, b51, b61, b71;
+    if (kbeg < kend) {
+        BM_RT_LOAD(0, kbeg);
+        BM_RT_LOAD(1, kbeg + BK);
+    }
+    for (int k0 = kbeg; k0 < kend; k0 += 2 * BK) {
+        BM_RT_STORE(0);
+        __syncthreads();
+        BM_RT_LOAD(0, k0 + 2 * BK);
+        compute();
+        __syncthreads();
+        if (k0 + BK >= kend) break;
+        BM_RT_STORE(1);
+        __syncthreads();
+        BM_RT_LOAD(1, k0 + 3 * BK);
+        compute();
         __syncthreads();
     }
+#undef BM_RT_LOAD
+#undef BM_RT_STORE
     float *P = part + (int64_t)sl * T * E;
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -114,6 +146,20 @@ k_topk_sum(const float *__restrict__ part, int S, int T, int E, int k, float *__
     __shared__ float srow[4][1024];
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wv;
+    if (E <= 256) {         // four logits per lane, the keyed one-wave top-k
+        if (t >= T) return;
+        float lv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int e = min(lane + 64 * i, E - 1);
+            float v = 0.f;
+            for (int sl = 0; sl < S; sl++) v += part[((int64_t)sl * T + t) * E + e];
+            lv[i] = v;
+            if (logits && lane + 64 * i < E) logits[(int64_t)t * E + e] = v;
+        }
+        topk_wave4(lv, E, k, ids + (int64_t)t * k, wout + (int64_t)t * k, nullptr);
+        return;
+    }
     if (t < T)
         for (int e = lane; e < E; e += 64) {
             float v = 0.f;
