@@ -270,12 +270,43 @@ BM_DEV void scatter_chunk(const int32_t *__restrict__ ids, int n, int E, int p0,
     }
 }
 
-// Active list (ascending experts with pairs) and the row-tile list.
+// Active list (ascending experts with pairs) and the row-tile list.  The
+// tiles are listed by their count of 32-row blocks, largest first (full
+// tiles of every expert in expert order, then each expert's last tile by
+// its blocks), so that the grouped GEMMs dispatch the longest tiles first
+// and the shortest fill the last round.
+BM_DEV int tile_class(int c, int tile_rows, int &nt) {      // blocks of the last tile, at most 3 (0: none)
+    nt = (c + tile_rows - 1) / tile_rows;
+    return nt ? min((c - (nt - 1) * tile_rows + 31) / 32, 3) : 0;
+}
 BM_DEV void active_and_tiles(const int *scount, int E, int32_t *__restrict__ active,
                              int32_t *__restrict__ n_active, int32_t *__restrict__ tiles,
                              int32_t *__restrict__ n_tiles, int tile_rows, int *swave) {
     int tid = threadIdx.x;
-    for (int e0 = 0, abase = 0, tbase = 0; e0 < E; e0 += kBT) {
+    const int full_cls = min((tile_rows + 31) / 32, 3);
+    // tiles: first pass, the count of each class (full tiles are of class
+    // full_cls; the last tile of an expert of its own blocks)
+    int cls_base[4] = {0, 0, 0, 0};
+    if (tiles) {
+        int tot[4] = {0, 0, 0, 0};
+        for (int e0 = 0; e0 < E; e0 += kBT) {
+            const int e = e0 + tid, c = e < E ? scount[e] : 0;
+            int nt;
+            const int cl = tile_class(c, tile_rows, nt);
+#pragma unroll
+            for (int k = 1; k <= 3; k++) {
+                const int m = (k == cl ? 1 : 0) + (k == full_cls && nt > 1 ? nt - 1 : 0);
+                int t;
+                block_exscan(m, swave, &t);
+                tot[k] += t;
+            }
+        }
+        for (int k = 3, acc = 0; k >= 1; k--) {
+            cls_base[k] = acc;
+            acc += tot[k];
+        }
+    }
+    for (int e0 = 0, abase = 0; e0 < E; e0 += kBT) {
         int e = e0 + tid;
         int c = e < E ? scount[e] : 0;
         int tot;
@@ -287,17 +318,28 @@ BM_DEV void active_and_tiles(const int *scount, int E, int32_t *__restrict__ act
         if (e < E && c > 0) active[abase + a] = e;
         abase += tot;
         if (tiles) {
-            int nt = (c + tile_rows - 1) / tile_rows, ttot;
-            int t0 = block_exscan(nt, swave, &ttot);
-            for (int i = 0; i < nt; i++) {
-                tiles[2 * (tbase + t0 + i)] = e;
-                tiles[2 * (tbase + t0 + i) + 1] = i * tile_rows;
+            int nt;
+            const int cl = tile_class(c, tile_rows, nt);
+#pragma unroll
+            for (int k = 1; k <= 3; k++) {
+                const int nfull = k == full_cls && nt > 1 ? nt - 1 : 0;
+                const int m = (k == cl ? 1 : 0) + nfull;
+                int t;
+                const int t0 = cls_base[k] + block_exscan(m, swave, &t);
+                for (int i = 0; i < nfull; i++) {
+                    tiles[2 * (t0 + i)] = e;
+                    tiles[2 * (t0 + i) + 1] = i * tile_rows;
+                }
+                if (k == cl) {
+                    tiles[2 * (t0 + nfull)] = e;
+                    tiles[2 * (t0 + nfull) + 1] = (nt - 1) * tile_rows;
+                }
+                cls_base[k] += t;
             }
-            tbase += ttot;
         }
         if (e0 + kBT >= E && tid == 0) {
             *n_active = abase;
-            if (n_tiles) *n_tiles = tbase;
+            if (n_tiles) *n_tiles = cls_base[1];
         }
     }
 }
