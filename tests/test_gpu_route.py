@@ -88,6 +88,16 @@ def test_route_ragged_and_small_expert_counts():
         _check_route(w, x)
 
 
+def test_route_mfma_odd_stage_slices():
+    """The matrix-core router's K slices with an odd number of 64-wide stages
+    and a short last slice (H 2304: seven slices of 5 stages, one of 1),
+    tokens past the last 64-token tile and experts past the last full tile."""
+    require_gpu()
+    w = synth.Workload("r_odd", 130, 2304, 256, 200, 6, "bf16", "computed", None, False, 13, "decode")
+    x, _ = synth.make_tokens(w)
+    _check_route(w, x)
+
+
 def test_route_zero_input_ties_to_lowest_index():
     require_gpu()
     w = synth.WORKLOADS["decode_b1"].with_(T=3)
