@@ -284,6 +284,39 @@ BM_DEV void active_and_tiles(const int *scount, int E, int32_t *__restrict__ act
                              int32_t *__restrict__ n_tiles, int tile_rows, int *swave) {
     int tid = threadIdx.x;
     const int full_cls = min((tile_rows + 31) / 32, 3);
+    if (E <= kBT && full_cls == 3) {
+        // one chunk of experts, full tiles of class 3 (the prefill tiles):
+        // the class counts come with the positions, from one scan of the
+        // class-3 tiles and one of the class-2 and class-1 last tiles packed
+        // (at most one per expert each, E <= kBT < 2^16)
+        const int e = tid, c = e < E ? scount[e] : 0;
+        int tot;
+        const int a = block_exscan(c > 0 ? 1 : 0, swave, &tot);
+        if (e < E) active[e] = -1;
+        __syncthreads();
+        if (e < E && c > 0) active[a] = e;
+        if (tiles) {
+            int nt;
+            const int cl = tile_class(c, tile_rows, nt);
+            const int n3 = (nt > 1 ? nt - 1 : 0) + (cl == 3 ? 1 : 0);
+            int t3, t21;
+            const int p3 = block_exscan(n3, swave, &t3);
+            const int p21 = block_exscan((cl == 2 ? 1 : 0) | (cl == 1 ? 1 << 16 : 0), swave, &t21);
+            const int t2 = t21 & 0xFFFF, t1 = t21 >> 16;
+            for (int i = 0; i + 1 < nt; i++) {
+                tiles[2 * (p3 + i)] = e;
+                tiles[2 * (p3 + i) + 1] = i * tile_rows;
+            }
+            if (cl > 0) {
+                const int pos = cl == 3 ? p3 + nt - 1 : cl == 2 ? t3 + (p21 & 0xFFFF) : t3 + t2 + (p21 >> 16);
+                tiles[2 * pos] = e;
+                tiles[2 * pos + 1] = (nt - 1) * tile_rows;
+            }
+            if (tid == 0 && n_tiles) *n_tiles = t3 + t2 + t1;
+        }
+        if (tid == 0) *n_active = tot;
+        return;
+    }
     // tiles: first pass, the count of each class (full tiles are of class
     // full_cls; the last tile of an expert of its own blocks)
     int cls_base[4] = {0, 0, 0, 0};
