@@ -220,8 +220,15 @@ BM_DEV int acc_row(int r, int kh) { return 8 * (r >> 2) + 4 * kh + (r & 3); }
 // would wait for the loads), and the stages whose prefetches are all in
 // range carry no conditionals (a conditional load path there breaks the
 // issue order and the compiler then drains every load).
-template <int AHEAD, class Regs, class Slot, class LoadA, class PutA, class LoadSlot, class Compute>
-BM_DEV void run_stages(int nsteps, LoadA &&load_a, PutA &&put_a, LoadSlot &&load_slot, Compute &&compute) {
+// pre() runs after the prologue's loads are issued and before the first
+// put_a: set-up that the first put_a needs may overlap those loads.
+struct NoPre {
+    BM_DEV void operator()() const {}
+};
+template <int AHEAD, class Regs, class Slot, class LoadA, class PutA, class LoadSlot, class Compute,
+          class Pre = NoPre>
+BM_DEV void run_stages(int nsteps, LoadA &&load_a, PutA &&put_a, LoadSlot &&load_slot, Compute &&compute,
+                       Pre &&pre = Pre{}) {
     static_assert(AHEAD == 1 || AHEAD == 2, "activation prefetch depth");
     Regs ra, rb;
     Slot q0, q1, q2;
@@ -243,6 +250,7 @@ BM_DEV void run_stages(int nsteps, LoadA &&load_a, PutA &&put_a, LoadSlot &&load
     if (AHEAD == 2) load_a(1, rb);
     load_slot(0, q0);
     load_slot(1, q1);                    // nsteps >= 2: K is a multiple of 256
+    pre();
     put_a(0, ra);
     // drain the prologue loads: otherwise the compiler merges their pending
     // state into the loop header and waits on the current slot every pass
@@ -644,12 +652,27 @@ BM_DEV void dn_tile(const DnArgs &a, uint8_t *lds, const PfTile &t, int ntile) {
         }
     };
     struct ARegs { u32x4 r[DP]; int e[DP]; };
+    // each row's largest h exponent (the staged pieces are rescaled to it):
+    // every (row, 256-column chunk) exponent loaded at once, maxima by LDS
+    // atomics, while the first stages' loads are in flight
+    auto row_max_exponents = [&]() {
+        const int nI = a.I / kPfGuCols;
+        if (threadIdx.x < kPfRows) semax[threadIdx.x] = -(1 << 30);
+        __syncthreads();
+        for (int u = threadIdx.x; u < kPfRows * nI; u += kDnThreads) {
+            const int m = u / nI, c = u - m * nI;
+            const int64_t gr = t.off + t.r0 + min(m, t.rows - 1);
+            atomicMax(&semax[m], a.hexp[gr * nI + c]);
+        }
+        __syncthreads();
+    };
     run_stages<1, ARegs, Slot>(
         2 * nb, [&](int st, ARegs &v) { dn_stage_load<R>(a, t, st >> 1, st & 1, v.r, v.e); },
         [&](int buf, ARegs &v) { dn_stage_put<R>(sa + buf * kPfABytes, semax, v.e, v.r); }, load_slot,
         [&](int buf, const Slot &sl) {
             if (active) compute(sa + buf * kPfABytes, sl);
-        });
+        },
+        row_max_exponents);
     dn_epilogue<MB, OUT32>(a, lds, t, ntile, acc, c0, active, kPfDnWShift);
 }
 
@@ -662,21 +685,11 @@ k_pf_down(DnArgs a) {
     const PfSlot sl = pf_slot((a.H + kPfDnCols - 1) / kPfDnCols);
     if (sl.tile >= *a.n_tiles) return;
     const PfTile t = pf_tile(sl.tile, a.tiles, a.counts, a.offsets);
-    // each row's largest h exponent and its pair: every (row, 256-column
-    // chunk) exponent loaded at once, maxima by LDS atomics
+    // the pair of each row (the epilogue's output rows); the rows' largest h
+    // exponents are gathered inside the stage pipeline's prologue
     int *semax = reinterpret_cast<int *>(lds + 2 * kPfABytes);
-    const int nI = a.I / kPfGuCols;
-    if (threadIdx.x < kPfRows) {
-        semax[threadIdx.x] = -(1 << 30);
+    if (threadIdx.x < kPfRows)
         semax[2 * kPfRows + threadIdx.x] = a.perm[t.off + t.r0 + min((int)threadIdx.x, t.rows - 1)];
-    }
-    __syncthreads();
-    for (int u = threadIdx.x; u < kPfRows * nI; u += kDnThreads) {
-        const int m = u / nI, c = u - m * nI;
-        const int64_t gr = t.off + t.r0 + min(m, t.rows - 1);
-        atomicMax(&semax[m], a.hexp[gr * nI + c]);
-    }
-    __syncthreads();
     switch ((t.rows + 31) >> 5) {
         case 1: dn_tile<1, OUT32>(a, lds, t, sl.ntile); break;
         case 2: dn_tile<2, OUT32>(a, lds, t, sl.ntile); break;
