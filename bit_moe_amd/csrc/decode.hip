@@ -38,9 +38,10 @@ namespace {
 using namespace bm;
 
 constexpr int kW = bm_cfg::kFrontWaves;   // waves per front workgroup
+using bm_cfg::kRouterRowWaves;       // several tokens: waves per router row in the front launch
 constexpr int kWG = 16;            // waves per routed gate/up workgroup
-constexpr int kWD = 4;             // waves per down workgroup: every down workgroup of a decode
-                                   // batch is resident at once
+constexpr int kWD = 4;             // waves per down workgroup (at one token the plan sizes the
+                                   // shared-down chunks so that all of them are resident at once)
 constexpr int kNT = 4;             // tokens per pass over the weights
 using bm_cfg::kMaxChunks;           // K chunks of the shared expert, at most
 // per token, the LDS staging of a routed down wave's two superblocks of h:
@@ -345,6 +346,42 @@ BM_DEV void bucket_decode_wave(const int32_t *__restrict__ ids, int n, int k, in
     }
 }
 
+// Router partial logits of T <= NT tokens over the row's 512-wide K steps
+// [s0, s1), all of a lane's pieces loaded at once (at most 4 steps); wave
+// sums to out[0..NT) (LDS).  Tokens past T repeat token 0 and are not used.
+template <int XBF16, int NT>
+BM_DEV void router_row_part(const uint4 *__restrict__ wrow, const void *__restrict__ x, int H, int T, int s0,
+                            int s1, float *out) {
+    constexpr int CH = 4;
+    const int lane = lane_id();
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = 0.f;
+    const int spare = lane < H / 8 ? lane : 0;
+    for (int sb = s0; sb < s1; sb += CH) {
+        uint4 wv[CH];
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            // steps past the part, and the idle half-wave of a half-width
+            // last step, re-read a piece of the row's first step, unused
+            const int s = sb + i, k = 512 * s + 8 * lane;
+            wv[i] = wrow[(s < s1 && k < H) ? 64 * s + lane : spare];
+        }
+#pragma unroll
+        for (int i = 0; i < CH; i++) {
+            const int s = sb + i, k = 512 * s + 8 * lane;
+            if (!(s < s1 && k < H)) continue;
+#pragma unroll
+            for (int t = 0; t < NT; t++) acc[t] = router_dot8<XBF16, NT>(wv[i], x, H, t < T ? t : 0, k, acc[t]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        const float v = wave_sum(acc[t]);
+        if (lane == 0) out[t] = v;
+    }
+}
+
 // Decode batches: work that the front launch's first n_wg workgroups take
 // before its other roles.  With ids (given by the caller) the first one
 // buckets them on its wave 0 (no mid launch); with x16 workgroup t < T
@@ -368,7 +405,8 @@ BM_DEV void front_prep(int H, int T, int E, const void *x, const FrontPrep &pr, 
 }
 
 // Workgroup roles, in blockIdx order: preparation (pr.n_wg, above) | router
-// rows (n_rwg, one per wave) | shared-expert gate/up partial sums per
+// rows (n_rwg: one per wave for one token, one per kRouterRowWaves waves for
+// several) | shared-expert gate/up partial sums per
 // (panel, K chunk).  Workgroup 0 also clears the down launch's per-panel
 // combine counters.  Launched with
 // kW waves, or (no shared chunks) fewer, so that the router rows spread
@@ -392,6 +430,30 @@ k_dec_front(int H, int I, int E, int T, int n_rwg, int kc_sg, const uint16_t *__
         return;
     }
     b -= pr.n_wg;
+    if (b < n_rwg && T > 1) {
+        // several tokens: kRouterRowWaves waves per row, each over a quarter
+        // of the row's 512-wide K steps, the parts summed in a fixed order
+        static_assert(kW % kRouterRowWaves == 0 && kW * 16 <= kW * kNT * 2 * 64, "router row parts");
+        const int e = b * (nw / kRouterRowWaves) + wv / kRouterRowWaves, part = wv % kRouterRowWaves;
+        const bool live = e < E;
+        const uint4 *wrow = reinterpret_cast<const uint4 *>(wr + (int64_t)min(e, E - 1) * H);
+        int s0, s1;
+        split_range((H + 511) / 512, kRouterRowWaves, part, s0, s1);
+        if (T <= 4)
+            router_row_part<XBF16, 4>(wrow, x, H, T, s0, s1, red + wv * 16);
+        else if (T <= 8)
+            router_row_part<XBF16, 8>(wrow, x, H, T, s0, s1, red + wv * 16);
+        else
+            router_row_part<XBF16, 16>(wrow, x, H, T, s0, s1, red + wv * 16);
+        __syncthreads();
+        if (live && part == 0 && lane_id() < T) {
+            float v = 0.f;
+#pragma unroll
+            for (int j = 0; j < kRouterRowWaves; j++) v += red[(wv + j) * 16 + lane_id()];
+            logits[(int64_t)lane_id() * E + e] = v;
+        }
+        return;
+    }
     if (b < n_rwg) {
         const int e = b * nw + wv;
         if (e >= E) return;

@@ -26,6 +26,8 @@ constexpr int kFusedRouterMaxT = 16;      // decode: router rows fused into the 
 // decode
 constexpr int kFrontWaves = 16;           // waves per front workgroup
 constexpr int kFrontRouterWaves = 4;      // the same when it only computes router rows
+constexpr int kRouterRowWaves = 4;        // several tokens: waves per router row in the front launch
+                                          // (each a quarter of K)
 constexpr int kFrontPrepMaxT = 32;        // decode batches up to this size prepare the prefill
                                           // kernels' activations in the front launch
 constexpr int kMaxChunks = 8;             // K chunks of the shared expert, at most

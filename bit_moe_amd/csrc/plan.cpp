@@ -51,7 +51,11 @@ DecodePlan decode_plan(const bitmoe_layer *L, int T, bool with_router) {
     p.sg_rows = (shared && T == 1 && L->format == BITMOE_FORMAT_2BIT && L->k <= 16 && 64 % L->k == 0)
                     ? 64 / L->k : 0;
     p.front_waves = (T == 1 && (p.sg_rows || !shared)) ? kFrontRouterWaves : kFrontWaves;
-    p.n_rwg = with_router ? (L->E + p.front_waves - 1) / p.front_waves : 0;
+    // router rows per front workgroup: one per wave for one token; for
+    // several, kRouterRowWaves waves share a row (a quarter of K each), so
+    // that the rows spread over four times the compute units
+    const int rows_per_wg = T > 1 ? p.front_waves / kRouterRowWaves : p.front_waves;
+    p.n_rwg = with_router ? (L->E + rows_per_wg - 1) / rows_per_wg : 0;
     p.kc_sd = shared ? std::max(1, (L->I + kSharedChunkCols - 1) / kSharedChunkCols) : 0;
     // one token: no more shared-down chunks than leave every down workgroup
     // (k routed + the shared chunks per 64 outputs) resident at once, so that
