@@ -10,6 +10,8 @@
 namespace {
 
 using bm_cfg::kFusedRouterMaxT;
+// the decode front launch's router rows take at most 16 tokens per pass
+static_assert(kFusedRouterMaxT <= 16, "router rows fused into the decode front launch: at most 16 tokens");
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxT = 1 << 20;           // tokens per call
