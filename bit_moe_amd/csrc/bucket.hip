@@ -62,11 +62,21 @@ k_bucket_scan(int E, int nblk, int32_t *__restrict__ bhist, int32_t *__restrict_
     int tid = threadIdx.x;
     int e = tid;
     int run = 0;
+    // the blocks' counts in batches of kB loads issued together, then their
+    // prefix (a load after each store would wait for it: one round trip per
+    // block)
+    constexpr int kB = 16;
     if (e < E)
-        for (int b = 0; b < nblk; b++) {
-            int c = bhist[(int64_t)b * E + e];
-            bhist[(int64_t)b * E + e] = run;        // rows of e in earlier blocks
-            run += c;
+        for (int b0 = 0; b0 < nblk; b0 += kB) {
+            int c[kB];
+#pragma unroll
+            for (int i = 0; i < kB; i++) c[i] = b0 + i < nblk ? bhist[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kB; i++)
+                if (b0 + i < nblk) {
+                    bhist[(int64_t)(b0 + i) * E + e] = run;        // rows of e in earlier blocks
+                    run += c[i];
+                }
         }
     int tot;
     int o = block_exscan(e < E ? run : 0, swave, &tot);
@@ -74,7 +84,14 @@ k_bucket_scan(int E, int nblk, int32_t *__restrict__ bhist, int32_t *__restrict_
         counts[e] = run;
         offsets[e] = o;
         scount[e] = run;
-        for (int b = 0; b < nblk; b++) bhist[(int64_t)b * E + e] += o;
+        for (int b0 = 0; b0 < nblk; b0 += kB) {
+            int v[kB];
+#pragma unroll
+            for (int i = 0; i < kB; i++) v[i] = b0 + i < nblk ? bhist[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kB; i++)
+                if (b0 + i < nblk) bhist[(int64_t)(b0 + i) * E + e] = v[i] + o;
+        }
     }
     if (tid == 0) offsets[E] = tot;
     __syncthreads();
