@@ -306,6 +306,25 @@ def test_forward_decode_small_expert_count(T):
     assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode E=8 T={T}")
 
 
+@pytest.mark.parametrize("T", [2, 6, 13])
+def test_forward_decode_router_rows_past_expert_count(T):
+    """E = 30 experts: for several tokens the front launch's router rows take
+    four waves each, four rows per workgroup, so the last workgroup holds rows
+    past E (not written); token counts on the 4-, 8- and 16-token passes."""
+    require_gpu()
+    import bit_moe_amd as bm
+    w = synth.WORKLOADS["tiny"].with_(name=f"tiny_e30_{T}", T=T, E=30, k=6, shared=True, x_dtype="bf16", seed=37)
+    L = synth_layer(w)
+    x, _ = synth.make_tokens(w, accept=lambda t, r: oracle.margin_ok(r, L.router(), w.k, 1e-4))
+    y, gid, gw = bm.forward_decode(device_layer(w), x_to_device(x))
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(x, L.router(), w.k)
+    np.testing.assert_array_equal(gid.cpu().numpy(), rid)
+    np.testing.assert_allclose(gw.cpu().numpy(), rw, atol=W_TOL)
+    ref = oracle.layer_ffn(L, x, rid, rw)
+    assert_close_rms(y.cpu().numpy(), ref, what=f"forward_decode E=30 T={T}")
+
+
 @pytest.mark.parametrize("copies", [4, 12])
 @pytest.mark.parametrize("shared", [False, True])
 def test_forward_decode_all_experts_shared_by_tokens(shared, copies):
