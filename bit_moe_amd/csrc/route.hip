@@ -63,9 +63,10 @@ k_router_splitk(const uint16_t *__restrict__ X, const uint16_t *__restrict__ W, 
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // A: 64 rows x 64 = 512 pieces of 8 bf16 (2 per thread); B: 256 rows (8
     // per thread).  Two register sets take the pieces of the next two stages
-    // while the current stage's MFMAs run (one workgroup per CU, one wave per
-    // SIMD: the loads' latency, not the MFMAs, sets the pace); loads past the
-    // slice re-read its last stage, unused.
+    // while the current stage's MFMAs run (at 2048 tokens the grid is one
+    // workgroup per CU, one wave per SIMD, so the loads' latency, not the
+    // MFMAs, sets the pace); loads past the slice re-read its last stage,
+    // unused.
     const int pr = tid >> 3, pc = (tid & 7) * 8;          // piece p: row pr + 32 p, column pc
     const uint16_t *xa0 = X + (int64_t)min(m0 + pr, T - 1) * H + pc;
     const uint16_t *xa1 = X + (int64_t)min(m0 + pr + 32, T - 1) * H + pc;
