@@ -149,12 +149,24 @@ k_topk_sum(const float *__restrict__ part, int S, int T, int E, int k, float *__
     const int t = blockIdx.x * 4 + wv;
     if (E <= 256) {         // four logits per lane, the keyed one-wave top-k
         if (t >= T) return;
+        // every slice's partial loaded first (at most kRouterSplit), then
+        // summed in slice order: one round trip instead of one per slice
+        float pv[4][kRouterSplit];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int e = min(lane + 64 * i, E - 1);
+#pragma unroll
+            for (int sl = 0; sl < kRouterSplit; sl++)
+                pv[i][sl] = sl < S ? part[((int64_t)sl * T + t) * E + e] : 0.f;
+        }
         float lv[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int e = min(lane + 64 * i, E - 1);
             float v = 0.f;
-            for (int sl = 0; sl < S; sl++) v += part[((int64_t)sl * T + t) * E + e];
+#pragma unroll
+            for (int sl = 0; sl < kRouterSplit; sl++)
+                if (sl < S) v += pv[i][sl];
             lv[i] = v;
             if (logits && lane + 64 * i < E) logits[(int64_t)t * E + e] = v;
         }
