@@ -92,8 +92,20 @@ template <int XBF16>
 BM_DEV void xprep_token_block(int H, const void *x, int t, uint16_t *x16, float *xsc, float *sm) {
     const int tid = threadIdx.x, nt = blockDim.x, nw = nt / kWave;
     const int64_t row = (int64_t)t * H;
+    // the thread's first kHold pieces are loaded together and kept in
+    // registers for the second pass (H 7168 on 256 threads: all of them)
+    constexpr int kHold = 4;
+    Xp8 hv[kHold];
     float m = 0.f;
-    for (int c = tid * 8; c < H; c += nt * 8) m = fmaxf(m, xprep_absmax8(xprep_load8<XBF16>(x, row + c)));
+#pragma unroll
+    for (int i = 0; i < kHold; i++) {
+        const int c = (tid + i * nt) * 8;
+        if (c < H) {
+            hv[i] = xprep_load8<XBF16>(x, row + c);
+            m = fmaxf(m, xprep_absmax8(hv[i]));
+        }
+    }
+    for (int c = (tid + kHold * nt) * 8; c < H; c += nt * 8) m = fmaxf(m, xprep_absmax8(xprep_load8<XBF16>(x, row + c)));
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
     if ((tid & (kWave - 1)) == 0) sm[tid / kWave] = m;
@@ -102,7 +114,12 @@ BM_DEV void xprep_token_block(int H, const void *x, int t, uint16_t *x16, float 
     for (int w = 0; w < nw; w++) m = fmaxf(m, sm[w]);
     const int e = pf_exponent(m);
     if (tid == 0) xsc[t] = ldexpf(1.f, e);
-    for (int c = tid * 8; c < H; c += nt * 8) xprep_store8(x16 + row + c, xprep_load8<XBF16>(x, row + c), e);
+#pragma unroll
+    for (int i = 0; i < kHold; i++) {
+        const int c = (tid + i * nt) * 8;
+        if (c < H) xprep_store8(x16 + row + c, hv[i], e);
+    }
+    for (int c = (tid + kHold * nt) * 8; c < H; c += nt * 8) xprep_store8(x16 + row + c, xprep_load8<XBF16>(x, row + c), e);
 }
 
 // ---- MXFP4 (OCP Microscaling: E2M1 elements, one E8M0 scale per 32) -----
